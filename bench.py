@@ -1,0 +1,186 @@
+"""Frame-step benchmark: Moshi-7B-shaped RQ-Transformer, bfloat16 weights, B=1, on one MI355X.
+
+One step = one 80 ms frame through the whole hot path (ring, embedding sum, 32 temporal layers,
+text head + argmax, 8 depformer codebook steps, ring update), issued as one hipGraph replay per
+frame.  After W warm-up frames the session is reset and K frames are timed from offset 0 (the
+workload: 250 greedy frames, seed-1 random-init weights, uniform user tokens).
+
+Prints one JSON line with frames/s, the roofline of the dominant kernel (measured with HIP
+events on the session stream) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "frames/s (80 ms) at B=1, Moshi-7B shape bf16; % of HBM roofline"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stage_bytes(cfg, band: str, n_kv: float) -> dict:
+    """Algorithmic HBM bytes of one launch of each stage: the weights it must stream once, the
+    KV it must read, and its activation vectors (read once, written once)."""
+    D, F, Dd, Fd, Q = cfg.d_model, cfg.ffn_hidden, cfg.dep_d_model, cfg.dep_ffn_hidden, cfg.dep_q
+    Vt, Va, L = cfg.text_card, cfg.audio_card, cfg.n_layers
+    we = {"f32": 4, "bf16": 2, "i8": 1}[band]
+    kve = 4 if band == "f32" else 2
+    sc = 4 if band == "i8" else 0  # per-row scales
+
+    def lin(n, k):
+        return n * k * we + n * sc
+
+    f = 4  # float32 activations
+    return {
+        "embed": (2 * Q + 1) * D * (2 if band != "f32" else 4) + 2 * D * f,
+        "qkv": lin(3 * D, D) + 2 * D * f + D * f + 2 * D * kve,
+        "attn": 2 * n_kv * D * kve + 2 * D * f,
+        "out_proj": lin(D, D) + D * f + 2 * D * f,
+        "gate_in": lin(2 * F, D) + 2 * D * f + F * f,
+        "gate_out": lin(D, F) + F * f + 2 * D * f,
+        "text_head": lin(Vt, D) + 2 * D * f + Vt * f + D * f,
+        "dep_in": lin(Q * Dd, D) + D * f + Q * Dd * f,
+        "dep_qkv": lin(3 * Dd, Dd) + 2 * Dd * f + 3 * Dd * f,
+        "dep_out": lin(Dd, Dd) + 4 * Dd * f,
+        "dep_gate_in": lin(2 * Fd, Dd) + 2 * Dd * f + Fd * f,
+        "dep_gate_out": lin(Dd, Fd) + Fd * f + 2 * Dd * f,
+        "dep_head": lin(Va, Dd) + Dd * f + Va * f,
+        "frame_end": 0,
+    }
+
+
+def frame_bytes(weight_bytes: int, cfg, band: str, positions) -> float:
+    """Weights + KV read per frame (the frame-level roofline of the method), averaged over the
+    given positions."""
+    kve = 4 if band == "f32" else 2
+    n = np.minimum(np.asarray(positions) + 1, cfg.context)
+    return weight_bytes + float(np.mean(n)) * cfg.n_layers * 2 * cfg.d_model * kve
+
+
+def cpu_baseline(cfg, weights, users, budget_s: float, max_frames: int):
+    """The oracle as it stands, on the host cores, over the first frames of the same workload."""
+    from oracle import OracleLM
+    try:
+        import threadpoolctl
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    t = time.time()
+    lm = OracleLM(cfg, weights)
+    log(f"oracle weights widened to float32 in {time.time() - t:.1f}s")
+    st = lm.new_state()
+    done, t0 = 0, time.perf_counter()
+    while done < max_frames and (done < 2 or time.perf_counter() - t0 < budget_s):
+        lm.step(st, users[done])
+        done += 1
+    dt = time.perf_counter() - t0
+    del lm
+    return {"value": done / dt, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {done} frames (offset 0..{done - 1}) of the same 7B bf16 B=1 workload, "
+                      f"float32 numpy oracle with the bf16 weights widened, {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=250)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="moshi7b_bf16_b1")
+    ap.add_argument("--exec", default="graph", choices=["graph", "stream"])
+    ap.add_argument("--profile-frames", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the B=1 frame step does not shard; see DESIGN.md for how batched conversations would)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import rq_transformer_frame_amd as rq
+    import synth
+
+    cfg = synth.CONFIGS[args.config]
+    band = cfg.band
+    t = time.time()
+    weights = synth.gen_weights(cfg)
+    log(f"generated {cfg.name} weights (seed {cfg.seed}) in {time.time() - t:.1f}s")
+    K, W = args.steps, args.warmup
+    users = synth.user_tokens(cfg, max(K, W, args.profile_frames))
+
+    sess = rq.Session(cfg, exec=args.exec)
+    t = time.time()
+    sess.load_weights(weights)
+    log(f"loaded weights in {time.time() - t:.1f}s")
+    lin_bytes, all_bytes = sess.weight_bytes()
+
+    # per-stage HIP-event profile on the session stream (kernels launched one by one)
+    prof = sess.profile_frames(users[:args.profile_frames])
+    sess.reset()
+    sb = stage_bytes(cfg, band, n_kv=float(np.mean(np.arange(1, args.profile_frames + 1))))
+    stages = {}
+    for name, (n, us) in prof.items():
+        if n:
+            stages[name] = {"launches": n, "avg_us": us / n, "total_us_per_frame": us / args.profile_frames,
+                            "bytes_per_launch": sb[name],
+                            "gbs": sb[name] / (us / n) / 1e3 if us > 0 else None}
+    dom = max((k for k in stages if k != "frame_end"), key=lambda k: stages[k]["total_us_per_frame"])
+    prof_frame_us = sum(v["total_us_per_frame"] for v in stages.values())
+    log(f"profiled {args.profile_frames} frames; dominant stage {dom}: "
+        f"{stages[dom]['avg_us']:.1f} us/launch, {stages[dom]['gbs']:.0f} GB/s")
+
+    for f in range(W):
+        sess.step(users[f])
+    sess.reset()
+    t0 = time.perf_counter()
+    for f in range(K):
+        sess.step(users[f])
+    dt = time.perf_counter() - t0
+    fps = K / dt
+    fb = frame_bytes(lin_bytes, cfg, band, np.arange(K))
+    log(f"{K} frames in {dt:.3f}s: {fps:.1f} frames/s, {fb / (dt / K) / 1e9:.0f} GB/s frame-level")
+    sess.close()
+
+    d = stages[dom]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": d["bytes_per_launch"], "avg_us": round(d["avg_us"], 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, weights, users, args.cpu_seconds, max_frames=30)
+        log(f"cpu baseline: {cpu['value']:.3f} frames/s on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(1000 * dt / K, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if band == "bf16" else band, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: Moshi-7B-shaped RQ-Transformer frame step, {K} greedy frames from "
+                               f"offset 0, seed-{cfg.seed} N(0,0.02) weights, uniform user tokens",
+                   "batch": cfg.batch, "band": band, "accumulate": "f32", "exec": args.exec,
+                   "weight_bytes_per_frame": lin_bytes},
+        "tokens_per_s": round(9 * fps, 1),
+        "frame_roofline": {"bytes_per_frame": fb, "achieved_gbs": round(fb / (dt / K) / 1e9, 1),
+                           "frac": round(fb / (dt / K) / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": {k: {kk: (round(vv, 2) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k, v in stages.items()},
+        "profiled_frame_us": round(prof_frame_us, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,247 @@
+/*
+ * moshi_mi355x.h -- C ABI of the MI355X (gfx950) Moshi RQ-Transformer frame step.
+ *
+ * One call of moshi_frame_step runs one 80 ms frame of Moshi's RQ-Transformer LM on the GPU:
+ * the delay-aligned token ring, the summed 17-stream embedding, the temporal decoder at one
+ * position against its KV cache, the text head with greedy argmax, and the 8 sequential
+ * depformer codebook steps, each ending in a greedy argmax.  The operation is the one the
+ * docs.rs page "inferencelayer 0.2.4 src/moshi_lm.rs" defines (module doc, MoshiLm::step_ext and
+ * the items it calls); that page is cited below as [LM].
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named host_* or documented as host memory are plain CPU memory owned by the
+ *     caller; the library copies what it needs before returning and keeps no reference.
+ *   - All device memory (weights, KV caches, ring, activations) is owned by the moshi_state and
+ *     released by moshi_destroy.  Nothing here takes torch or HIP types other than an optional
+ *     hipStream_t passed as void*.
+ *   - Calls on one moshi_state are not reentrant: use one state per thread.
+ *   - Every call returns a moshi_status; on failure moshi_last_error(state) holds a message.
+ *     A device (HIP) error returns MOSHI_EDEVICE and leaves the session contents undefined
+ *     until moshi_reset.
+ */
+#ifndef MOSHI_MI355X_H
+#define MOSHI_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOSHI_OK = 0,
+  MOSHI_NONE = 1,      /* the step ran, but no conversation has output yet ([LM] step: none
+                          until offset > max_delay) */
+  MOSHI_EINVAL = -1,   /* bad argument (state unchanged) */
+  MOSHI_ESTATE = -2,   /* call out of order, e.g. a step before all weights are loaded */
+  MOSHI_ESHAPE = -3,   /* unknown tensor name, wrong shape or dtype at load */
+  MOSHI_ENOMEM = -4,   /* device or pinned host allocation failed */
+  MOSHI_EDEVICE = -5,  /* HIP error; session contents undefined until moshi_reset */
+  MOSHI_ERANGE = -6    /* the step would write past kv_capacity (state unchanged) */
+} moshi_status;
+
+/* Weight band: the storage type of every linear weight on the device. */
+typedef enum {
+  MOSHI_BAND_F32 = 0,  /* float32 linears, embeddings and KV cache ([LM] Band::F32, the parity band) */
+  MOSHI_BAND_BF16 = 1, /* bfloat16 linears, embeddings and KV cache, float32 arithmetic */
+  MOSHI_BAND_I8 = 2    /* int8 linears with one float32 scale per output row ([LM] Band::I8);
+                          embeddings and KV cache bfloat16.  Quantised at load, see
+                          moshi_load_weights. */
+} moshi_band;
+
+typedef enum { MOSHI_DTYPE_F32 = 0, MOSHI_DTYPE_BF16 = 1 } moshi_dtype;
+
+/* How a frame is issued to the GPU. */
+typedef enum {
+  MOSHI_EXEC_GRAPH = 0,  /* the whole frame is captured once into a hipGraph and replayed */
+  MOSHI_EXEC_STREAM = 1  /* kernels are launched one by one on the stream each frame */
+} moshi_exec;
+
+/*
+ * Model shape and session layout (plain C struct).  The Moshi-7B shape ([LM] constants) is
+ * n_layers 32, d_model 4096, n_heads 32, ffn_hidden 11264, context 3000, text_card 32000,
+ * audio_card 2048, dep_layers 6, dep_d_model 1024, dep_heads 16, dep_ffn_hidden 2816, dep_q 8,
+ * rope_theta 10000, rms_eps 1e-8.
+ *   text_card / audio_card : head widths; the INITIAL tokens are text_card and audio_card and
+ *                            the embedding tables have card + 1 rows ([LM] module doc).
+ *   batch                  : independent conversations stepped together (each with its own
+ *                            ring, offset and KV cache).
+ *   kv_capacity            : positions of temporal KV held per conversation; 0 means context.
+ *                            Must be <= context.  When equal to context the cache is a ring and
+ *                            the offset may grow without bound (sliding window of the last
+ *                            `context` positions, absolute rope positions); when smaller, a step
+ *                            at offset >= kv_capacity returns MOSHI_ERANGE.
+ *   exec                   : a moshi_exec value.
+ * Constraints (else MOSHI_EINVAL): d_model % n_heads == 0 with head_dim 64 or 128;
+ * dep_d_model % dep_heads == 0; 1 <= dep_q <= 16 (Moshi uses 8); d_model, ffn_hidden,
+ * dep_d_model and dep_ffn_hidden multiples of 16 and at most 16384; batch >= 1.
+ */
+typedef struct moshi_config {
+  int32_t n_layers, d_model, n_heads, ffn_hidden, context;
+  int32_t text_card, audio_card;
+  int32_t dep_layers, dep_d_model, dep_heads, dep_ffn_hidden, dep_q;
+  float rope_theta, rms_eps;
+  int32_t band, batch, kv_capacity, exec;
+} moshi_config;
+
+/*
+ * One tensor handed to moshi_load_weights.  `name` and `shape` follow the checkpoint layout
+ * that [LM] MoshiLm::load_band reads:
+ *   emb.{0..15}.weight [audio_card+1, d_model]           text_emb.weight [text_card+1, d_model]
+ *   transformer.layers.{l}.norm1.alpha / norm2.alpha [d_model]
+ *   transformer.layers.{l}.self_attn.in_projs.0.weight [3 d_model, d_model]   (rows q | k | v)
+ *   transformer.layers.{l}.self_attn.out_projs.0.weight [d_model, d_model]
+ *   transformer.layers.{l}.gating.linear_in.weight [2 ffn_hidden, d_model]    (rows gate | mult)
+ *   transformer.layers.{l}.gating.linear_out.weight [d_model, ffn_hidden]
+ *   out_norm.alpha [d_model]                              text_linear.weight [text_card, d_model]
+ *   depformer_in.{s}.weight [dep_d_model, d_model]        linears.{s}.weight [audio_card, dep_d_model]
+ *   depformer_text_emb.weight [text_card+1, dep_d_model]  depformer_emb.{0..6}.weight [audio_card+1, dep_d_model]
+ *   depformer.layers.{j}.norm1.alpha / norm2.alpha [dep_d_model]   (shared by the 8 steps)
+ *   depformer.layers.{j}.self_attn.in_projs.{s}.weight [3 dep_d_model, dep_d_model]
+ *   depformer.layers.{j}.self_attn.out_projs.{s}.weight [dep_d_model, dep_d_model]
+ *   depformer.layers.{j}.gating.{s}.linear_in.weight [2 dep_ffn_hidden, dep_d_model]
+ *   depformer.layers.{j}.gating.{s}.linear_out.weight [dep_d_model, dep_ffn_hidden]
+ * Matrices are row-major [rows, cols] (output row r is contiguous).  `data` is host memory
+ * holding float32 or bfloat16 (raw uint16 bits) as `dtype` says; ndim is 1 or 2.
+ */
+typedef struct moshi_tensor {
+  const char *name;
+  int32_t dtype; /* moshi_dtype */
+  int32_t ndim;
+  int64_t shape[2];
+  const void *data;
+} moshi_tensor;
+
+/*
+ * Where moshi_read_trace copies the last step's stages ([LM] StepTrace).  Every pointer is
+ * caller-owned host memory or NULL (skipped).
+ */
+typedef struct moshi_trace {
+  int32_t *input_tokens;    /* [2 dep_q + 1] gathered model input tokens */
+  float *emb_sum;           /* [d_model] summed embedding */
+  float *transformer_out;   /* [d_model] post-out_norm hidden */
+  float *text_logits;       /* [text_card] */
+  float *audio_logits;      /* [dep_q][audio_card] */
+  int32_t *tokens;          /* [1 + dep_q] text token, then the dep_q audio tokens */
+} moshi_trace;
+
+typedef struct moshi_state moshi_state;
+
+/*
+ * Create a session on the current HIP device.  `hip_stream` is a hipStream_t to run on, or NULL
+ * for a stream the library creates.  Allocates all device memory up front (weights, KV caches
+ * of batch x n_layers x kv_capacity positions, ring, activations).  The session starts reset
+ * ([LM] state(): ring all -2, offset 0, no KV).  Errors: MOSHI_EINVAL (bad config),
+ * MOSHI_ENOMEM, MOSHI_EDEVICE (no usable GPU).  On error *out is NULL.
+ */
+moshi_status moshi_create(const moshi_config *cfg, void *hip_stream, moshi_state **out);
+
+/*
+ * Copy `n` tensors to the device (may be called several times; a later tensor of the same name
+ * replaces the earlier one).  Storage follows the band: MOSHI_BAND_F32 widens bfloat16 input to
+ * float32; MOSHI_BAND_BF16 rounds float32 input to bfloat16 (nearest-even); MOSHI_BAND_I8
+ * quantises every linear per output row r: s_r = max_k |w_rk| / 127 (float32), q_rk =
+ * round-half-away-from-zero(w_rk / s_r) clamped to [-127, 127], q = 0 when s_r = 0, and the
+ * product is s_r * sum_k q_rk x_k.  Norm gains are always float32.  Errors: MOSHI_ESHAPE
+ * (unknown name, wrong shape, bad dtype), MOSHI_EDEVICE.
+ */
+moshi_status moshi_load_weights(moshi_state *s, const moshi_tensor *tensors, int32_t n);
+
+/*
+ * One frame for every conversation ([LM] step_ext, greedy).  user_tokens [batch][dep_q] host
+ * int32: each in [0, audio_card) or -1 (embeds to exact zero).  Any other value gives
+ * MOSHI_EINVAL before device work, leaving the state unchanged.  On success out [batch][1+dep_q]
+ * (host) receives the delay-realigned [text, audio x dep_q] of each conversation that has one
+ * (offset > 1 after the step), and has_out [batch] (host; may be NULL when batch == 1) says
+ * which.  Returns MOSHI_OK if any conversation produced output, MOSHI_NONE if none did.
+ * Errors: MOSHI_ESTATE (weights incomplete), MOSHI_ERANGE, MOSHI_EDEVICE.
+ */
+moshi_status moshi_frame_step(moshi_state *s, const int32_t *user_tokens, int32_t *out,
+                              uint8_t *has_out);
+
+/* Reset conversation `conv` (or all when conv == -1) to [LM] state(): ring -2, offset 0, empty
+ * KV.  Weights are kept.  Errors: MOSHI_EINVAL (conv out of range), MOSHI_EDEVICE. */
+moshi_status moshi_reset(moshi_state *s, int32_t conv);
+
+/* Free every device and host allocation of the session.  NULL is ignored. */
+void moshi_destroy(moshi_state *s);
+
+/* Message of the last failed call on `s` (empty string if none; static text when s is NULL). */
+const char *moshi_last_error(const moshi_state *s);
+
+/* Name of a moshi_status value. */
+const char *moshi_status_string(int32_t status);
+
+/* ---- session hooks (tests, teacher forcing, measurement) ------------------------------------ */
+
+/* Absolute offset of conversation `conv`, i.e. the temporal position of its next step ([LM]
+ * MoshiState::clock). */
+moshi_status moshi_get_offset(const moshi_state *s, int32_t conv, int64_t *offset);
+
+/* [LM] MoshiState::force_generated: overwrite the tokens written by the last step of `conv`
+ * (ring slot offset % 3) with text and audio[dep_q] (host).  Used to judge a non-parity band
+ * step by step on a reference trajectory.  text in [0, text_card), audio in [0, audio_card). */
+moshi_status moshi_force_generated(moshi_state *s, int32_t conv, int32_t text, const int32_t *audio);
+
+/* Copy the last step's stages of `conv` to host memory (see moshi_trace). */
+moshi_status moshi_read_trace(moshi_state *s, int32_t conv, const moshi_trace *trace);
+
+/* [LM] step_forced, T times: teacher-forced steps of conversation `conv` that advance the
+ * temporal KV cache on the gathered inputs, skip the heads and the depformer, and record the
+ * forced text [T] and agent [T][dep_q] tokens in the ring; user [T][dep_q] as in
+ * moshi_frame_step.  All arrays are host int32. */
+moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const int32_t *text,
+                                  const int32_t *agent, const int32_t *user);
+
+/* Bytes of linear weights (what one frame must stream) and of all device weights. */
+moshi_status moshi_weight_bytes(const moshi_state *s, int64_t *linear_bytes, int64_t *all_bytes);
+
+/* The HIP stream the session runs on (a hipStream_t). */
+void *moshi_stream(const moshi_state *s);
+
+/* Stages of one frame, in launch order (each is one kernel per launch). */
+typedef enum {
+  MOSHI_STAGE_EMBED = 0,     /* user write, gather, 17-row embedding sum */
+  MOSHI_STAGE_QKV,           /* temporal norm1 + q|k|v + rope + KV append   (x n_layers) */
+  MOSHI_STAGE_ATTN,          /* temporal decode attention                   (x n_layers) */
+  MOSHI_STAGE_OUT_PROJ,      /* temporal out_proj + residual                (x n_layers) */
+  MOSHI_STAGE_GATE_IN,       /* temporal norm2 + linear_in + silu * mult    (x n_layers) */
+  MOSHI_STAGE_GATE_OUT,      /* temporal linear_out + residual              (x n_layers) */
+  MOSHI_STAGE_TEXT_HEAD,     /* out_norm + text head + greedy argmax */
+  MOSHI_STAGE_DEP_IN,        /* depformer_in for all codebooks */
+  MOSHI_STAGE_DEP_QKV,       /* depformer (entry) norm1 + q|k|v   (x dep_q x dep_layers) */
+  MOSHI_STAGE_DEP_OUT,       /* depformer attention + out_proj    (x dep_q x dep_layers) */
+  MOSHI_STAGE_DEP_GATE_IN,   /* depformer norm2 + linear_in       (x dep_q x dep_layers) */
+  MOSHI_STAGE_DEP_GATE_OUT,  /* depformer linear_out + residual   (x dep_q x dep_layers) */
+  MOSHI_STAGE_DEP_HEAD,      /* codebook head + greedy argmax     (x dep_q) */
+  MOSHI_STAGE_FRAME_END,     /* offset, ring write, realigned output */
+  MOSHI_N_STAGES
+} moshi_stage;
+
+/*
+ * Measurement: run `n_frames` real frames (state advances as with moshi_frame_step) with the
+ * kernels launched one by one and every launch bracketed by a HIP event pair on the session
+ * stream.  user_tokens [n_frames][batch][dep_q] host.  stage_us[MOSHI_N_STAGES] receives the
+ * summed event time per stage (microseconds) and stage_launches[MOSHI_N_STAGES] the launch
+ * counts.  Errors as moshi_frame_step.
+ */
+moshi_status moshi_profile_frames(moshi_state *s, int32_t n_frames, const int32_t *user_tokens,
+                                  double *stage_us, int64_t *stage_launches);
+
+/* ---- kernel-level hooks (tests and micro-benchmarks) ---------------------------------------- */
+
+/*
+ * y[N] = W[N][K] . x[K] with the library's weight-streaming GEMV, on fresh device copies of the
+ * host arrays.  band picks the weight storage (W is given as float32 host data and converted as
+ * moshi_load_weights would).  If iters > 0 the kernel is also launched `iters` more times between
+ * HIP events and *avg_us receives the mean duration.  Errors: MOSHI_EINVAL, MOSHI_ENOMEM,
+ * MOSHI_EDEVICE.
+ */
+moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W, const float *x,
+                              float *y, int32_t iters, float *avg_us);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOSHI_MI355X_H */

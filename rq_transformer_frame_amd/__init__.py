@@ -1,0 +1,245 @@
+"""Python binding of the MI355X Moshi RQ-Transformer frame-step library (libmoshi_mi355x.so).
+
+Argument marshalling only: every step of the frame runs in the library's HIP kernels.  The names
+mirror the C ABI in include/moshi_mi355x.h.  There is no CPU fallback: if the library is not
+built, importing the session class raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoshi_mi355x.so")
+
+MOSHI_OK, MOSHI_NONE = 0, 1
+MOSHI_EINVAL, MOSHI_ESTATE, MOSHI_ESHAPE, MOSHI_ENOMEM, MOSHI_EDEVICE, MOSHI_ERANGE = -1, -2, -3, -4, -5, -6
+BANDS = {"f32": 0, "bf16": 1, "i8": 2}
+EXEC = {"graph": 0, "stream": 1}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+# every function the header declares, with (restype, argtypes)
+_vp, _i32, _i64, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+_SIGS = {
+    "moshi_create": (_i32, [_vp, _vp, _vp]),
+    "moshi_load_weights": (_i32, [_vp, _vp, _i32]),
+    "moshi_frame_step": (_i32, [_vp, _vp, _vp, _vp]),
+    "moshi_reset": (_i32, [_vp, _i32]),
+    "moshi_destroy": (None, [_vp]),
+    "moshi_last_error": (ctypes.c_char_p, [_vp]),
+    "moshi_status_string": (ctypes.c_char_p, [_i32]),
+    "moshi_get_offset": (_i32, [_vp, _i32, _vp]),
+    "moshi_force_generated": (_i32, [_vp, _i32, _i32, _vp]),
+    "moshi_read_trace": (_i32, [_vp, _i32, _vp]),
+    "moshi_prefill_forced": (_i32, [_vp, _i32, _i32, _vp, _vp, _vp]),
+    "moshi_weight_bytes": (_i32, [_vp, _vp, _vp]),
+    "moshi_stream": (_vp, [_vp]),
+    "moshi_debug_gemv": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "moshi_profile_frames": (_i32, [_vp, _i32, _vp, _vp, _vp]),
+}
+
+STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv", "dep_out",
+          "dep_gate_in", "dep_gate_out", "dep_head", "frame_end"]
+
+
+class MoshiError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with __graft_entry__.build() "
+                              "(rq_transformer_frame_amd/build.py); there is no CPU fallback")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "d_model", "n_heads", "ffn_hidden", "context",
+                                               "text_card", "audio_card", "dep_layers", "dep_d_model",
+                                               "dep_heads", "dep_ffn_hidden", "dep_q")] + [
+        ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
+        (n, ctypes.c_int32) for n in ("band", "batch", "kv_capacity", "exec")]
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 2), ("data", ctypes.c_void_p)]
+
+
+class _Trace(ctypes.Structure):
+    _fields_ = [("input_tokens", ctypes.c_void_p), ("emb_sum", ctypes.c_void_p),
+                ("transformer_out", ctypes.c_void_p), ("text_logits", ctypes.c_void_p),
+                ("audio_logits", ctypes.c_void_p), ("tokens", ctypes.c_void_p)]
+
+
+_SHAPE_FIELDS = ("n_layers", "d_model", "n_heads", "ffn_hidden", "context", "text_card", "audio_card",
+                 "dep_layers", "dep_d_model", "dep_heads", "dep_ffn_hidden", "dep_q", "rope_theta", "rms_eps")
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+class Session:
+    """A moshi_state.  `shape` is any object with the moshi_config field names as attributes
+    (n_layers, d_model, ...); band is 'f32', 'bf16' or 'i8'; exec is 'graph' or 'stream';
+    `stream` is an optional hipStream_t handle (int) to run on."""
+
+    def __init__(self, shape, band: str | None = None, batch: int | None = None, kv_capacity: int = 0,
+                 exec: str = "graph", stream: int | None = None):
+        self.lib = load_library()
+        c = _Config()
+        for f in _SHAPE_FIELDS:
+            setattr(c, f, getattr(shape, f))
+        c.band = BANDS[band or getattr(shape, "band")]
+        c.batch = batch if batch is not None else getattr(shape, "batch", 1)
+        c.kv_capacity = kv_capacity
+        c.exec = EXEC[exec]
+        self.cfg = c
+        self.B, self.Q = c.batch, c.dep_q
+        self.NS = 2 * c.dep_q + 1
+        h = ctypes.c_void_p()
+        st = self.lib.moshi_create(ctypes.byref(c), stream, ctypes.byref(h))
+        if st != MOSHI_OK:
+            raise MoshiError(st, f"moshi_create failed: {self.lib.moshi_status_string(st).decode()}")
+        self.h = h
+
+    # -- helpers -----------------------------------------------------------------------------
+    def _check(self, st: int, what: str) -> int:
+        if st < 0:
+            raise MoshiError(st, f"{what}: {self.lib.moshi_status_string(st).decode()}: "
+                                 f"{self.lib.moshi_last_error(self.h).decode()}")
+        return st
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.moshi_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.close()
+
+    # -- API ---------------------------------------------------------------------------------
+    def load_weights(self, weights: dict, chunk: int = 64):
+        """weights: name -> float32 array or uint16 array of bfloat16 bits."""
+        items = list(weights.items())
+        for i in range(0, len(items), chunk):
+            part = items[i:i + chunk]
+            arr = (_Tensor * len(part))()
+            keep = []
+            for j, (name, a) in enumerate(part):
+                a = np.ascontiguousarray(a)
+                if a.dtype == np.float32:
+                    dt = DTYPE_F32
+                elif a.dtype == np.uint16:
+                    dt = DTYPE_BF16
+                else:
+                    raise TypeError(f"{name}: dtype {a.dtype} (want float32 or uint16 bf16 bits)")
+                nb = name.encode()
+                keep += [a, nb]
+                arr[j].name = nb
+                arr[j].dtype = dt
+                arr[j].ndim = a.ndim
+                arr[j].shape[0] = a.shape[0]
+                arr[j].shape[1] = a.shape[1] if a.ndim > 1 else 0
+                arr[j].data = _ptr(a)
+            self._check(self.lib.moshi_load_weights(self.h, arr, len(part)), "moshi_load_weights")
+
+    def step(self, user):
+        """One frame.  user: [batch][dep_q] (or [dep_q] at batch 1).  Returns (status, out
+        [batch][1+dep_q] int32, has_out [batch] bool)."""
+        u = np.ascontiguousarray(np.asarray(user, np.int32).reshape(self.B, self.Q))
+        out = np.full((self.B, self.Q + 1), -3, np.int32)
+        has = np.zeros(self.B, np.uint8)
+        st = self._check(self.lib.moshi_frame_step(self.h, _ptr(u), _ptr(out), _ptr(has)), "moshi_frame_step")
+        return st, out, has.astype(bool)
+
+    def reset(self, conv: int = -1):
+        self._check(self.lib.moshi_reset(self.h, conv), "moshi_reset")
+
+    def offset(self, conv: int = 0) -> int:
+        v = ctypes.c_int64()
+        self._check(self.lib.moshi_get_offset(self.h, conv, ctypes.byref(v)), "moshi_get_offset")
+        return v.value
+
+    def force_generated(self, conv: int, text: int, audio):
+        a = np.ascontiguousarray(np.asarray(audio, np.int32))
+        self._check(self.lib.moshi_force_generated(self.h, conv, int(text), _ptr(a)), "moshi_force_generated")
+
+    def read_trace(self, conv: int = 0) -> dict:
+        c = self.cfg
+        t = dict(input_tokens=np.zeros(self.NS, np.int32), emb_sum=np.zeros(c.d_model, np.float32),
+                 transformer_out=np.zeros(c.d_model, np.float32), text_logits=np.zeros(c.text_card, np.float32),
+                 audio_logits=np.zeros((c.dep_q, c.audio_card), np.float32), tokens=np.zeros(1 + c.dep_q, np.int32))
+        tr = _Trace(*[_ptr(t[k]) for k in ("input_tokens", "emb_sum", "transformer_out", "text_logits",
+                                           "audio_logits", "tokens")])
+        self._check(self.lib.moshi_read_trace(self.h, conv, ctypes.byref(tr)), "moshi_read_trace")
+        t["text_token"] = int(t["tokens"][0])
+        t["audio_tokens"] = [int(v) for v in t["tokens"][1:]]
+        return t
+
+    def prefill_forced(self, conv: int, text, agent, user):
+        text = np.ascontiguousarray(np.asarray(text, np.int32))
+        agent = np.ascontiguousarray(np.asarray(agent, np.int32))
+        user = np.ascontiguousarray(np.asarray(user, np.int32))
+        T = len(text)
+        self._check(self.lib.moshi_prefill_forced(self.h, conv, T, _ptr(text), _ptr(agent), _ptr(user)),
+                    "moshi_prefill_forced")
+
+    def weight_bytes(self):
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        self._check(self.lib.moshi_weight_bytes(self.h, ctypes.byref(a), ctypes.byref(b)), "moshi_weight_bytes")
+        return a.value, b.value
+
+    def profile_frames(self, users):
+        """Run len(users) real frames with every kernel launch timed by HIP events.  users:
+        [frames][batch][dep_q].  Returns {stage: (launches, total_us)}."""
+        u = np.ascontiguousarray(np.asarray(users, np.int32).reshape(-1, self.B, self.Q))
+        us = np.zeros(len(STAGES), np.float64)
+        n = np.zeros(len(STAGES), np.int64)
+        self._check(self.lib.moshi_profile_frames(self.h, len(u), _ptr(u), _ptr(us), _ptr(n)), "moshi_profile_frames")
+        return {name: (int(n[i]), float(us[i])) for i, name in enumerate(STAGES)}
+
+    @property
+    def stream(self) -> int:
+        return self.lib.moshi_stream(self.h)
+
+
+def debug_gemv(band: str, W: np.ndarray, x: np.ndarray, iters: int = 0):
+    """y = W . x with the library's GEMV kernel (W float32 [N, K], converted per band).  Returns
+    (y, mean kernel microseconds or None)."""
+    lib = load_library()
+    W = np.ascontiguousarray(W, np.float32)
+    x = np.ascontiguousarray(x, np.float32)
+    N, K = W.shape
+    y = np.zeros(N, np.float32)
+    us = ctypes.c_float(0)
+    st = lib.moshi_debug_gemv(BANDS[band], N, K, _ptr(W), _ptr(x), _ptr(y), iters, ctypes.byref(us))
+    if st != MOSHI_OK:
+        raise MoshiError(st, f"moshi_debug_gemv: {lib.moshi_status_string(st).decode()}")
+    return y, (us.value if iters > 0 else None)

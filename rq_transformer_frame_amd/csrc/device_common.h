@@ -1,0 +1,243 @@
+// Device-side primitives shared by the frame-step kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mk {
+
+constexpr int WAVE = 64;
+constexpr int BLOCK = 256;
+constexpr int NWAVES = BLOCK / WAVE;
+constexpr int MAX_STREAMS = 64;  // 2 * dep_q + 1 upper bound
+
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// float32 -> bfloat16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7F800000u) == 0x7F800000u) return (bf16_t)((b >> 16) | ((b & 0xFFFFu) ? 0x40u : 0u));
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (bf16_t)(b >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// Sum over the 64 lanes; the result is taken from lane 0 by callers that need one value.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+  return v;
+}
+
+// Sum over 64 lanes, lane 0's value broadcast so every lane holds identical bits.
+__device__ __forceinline__ float wave_sum_bcast(float v) { return __shfl(wave_sum(v), 0, WAVE); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, WAVE));
+  return v;
+}
+
+// Block-wide sum: each wave's lane-0 sum goes to LDS, then every thread adds the wave sums in
+// the same order, so all threads hold the same value.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ float block_max(float v, float *red) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int i = 1; i < NWAVES; ++i) t = fmaxf(t, red[i]);
+  __syncthreads();
+  return t;
+}
+
+// ---- greedy argmax candidates ------------------------------------------------------------
+// First-wins argmax: among values strictly above -inf (NaN never qualifies) the largest wins,
+// ties go to the smaller index; no candidate at all means index 0.
+struct ArgBest {
+  float v;
+  int i;  // -1: no candidate
+};
+
+__device__ __forceinline__ ArgBest arg_none() { return ArgBest{-INFINITY, -1}; }
+
+__device__ __forceinline__ ArgBest arg_take(ArgBest a, float v, int i) {
+  if (v > -INFINITY) {  // false for NaN and -inf
+    if (a.i < 0 || v > a.v || (v == a.v && i < a.i)) return ArgBest{v, i};
+  }
+  return a;
+}
+
+__device__ __forceinline__ ArgBest arg_merge(ArgBest a, ArgBest b) {
+  if (b.i < 0) return a;
+  if (a.i < 0) return b;
+  if (b.v > a.v || (b.v == a.v && b.i < a.i)) return b;
+  return a;
+}
+
+__device__ __forceinline__ ArgBest wave_arg(ArgBest a) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    ArgBest o{__shfl_xor(a.v, m, WAVE), __shfl_xor(a.i, m, WAVE)};
+    a = arg_merge(a, o);
+  }
+  return a;
+}
+
+// ---- 16-byte weight vectors -------------------------------------------------------------
+template <typename WT> struct WVec;
+
+template <> struct WVec<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void cvt(const uint4 &u, float *f) {
+    f[0] = __uint_as_float(u.x);
+    f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z);
+    f[3] = __uint_as_float(u.w);
+  }
+};
+
+template <> struct WVec<bf16_t> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void cvt(const uint4 &u, float *f) {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    f[4] = __uint_as_float(u.z << 16);
+    f[5] = __uint_as_float(u.z & 0xFFFF0000u);
+    f[6] = __uint_as_float(u.w << 16);
+    f[7] = __uint_as_float(u.w & 0xFFFF0000u);
+  }
+};
+
+template <> struct WVec<int8_t> {
+  static constexpr int N = 16;
+  __device__ __forceinline__ static void cvt(const uint4 &u, float *f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) f[4 * j + b] = (float)(int32_t)(int8_t)((w[j] >> (8 * b)) & 0xFFu);
+    }
+  }
+};
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load with the non-temporal hint (weights are read once per frame).
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return uint4{v.x, v.y, v.z, v.w};
+}
+
+// One wave computes the dot products of R weight rows (row r starts at W + rowoff[r]) with the
+// vector xs[0..K) held in LDS.  Lane l handles the 16-byte vectors l, l + 64, l + 128, ... of
+// each row; U vectors per row are loaded before any arithmetic so that R * U loads are in flight
+// per lane.  K must be a multiple of the vector width.  acc[r] is the lane's partial sum.
+template <typename WT, int R, int U>
+__device__ __forceinline__ void wave_rows_dot(const WT *__restrict__ W, int K, const int64_t *rowoff,
+                                              const float *__restrict__ xs, float *acc) {
+  constexpr int N = WVec<WT>::N;
+  const int lane = threadIdx.x & 63;
+  const int nv = K / N;
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  int v0 = 0;
+  for (; v0 + U * WAVE <= nv; v0 += U * WAVE) {
+    uint4 w[R][U];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[r][u] = ld_stream(reinterpret_cast<const uint4 *>(W + rowoff[r]) + v0 + u * WAVE + lane);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float *xp = xs + (size_t)(v0 + u * WAVE + lane) * N;
+      float xv[N];
+#pragma unroll
+      for (int i = 0; i < N; ++i) xv[i] = xp[i];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float wf[N];
+        WVec<WT>::cvt(w[r][u], wf);
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[r] = fmaf(wf[i], xv[i], acc[r]);
+      }
+    }
+  }
+  for (int v = v0 + lane; v < nv; v += WAVE) {
+    const float *xp = xs + (size_t)v * N;
+    float xv[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) xv[i] = xp[i];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint4 wv = ld_stream(reinterpret_cast<const uint4 *>(W + rowoff[r]) + v);
+      float wf[N];
+      WVec<WT>::cvt(wv, wf);
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[r] = fmaf(wf[i], xv[i], acc[r]);
+    }
+  }
+}
+
+// xs[k] = src[k] for k < K, then a barrier.
+__device__ __forceinline__ void stage_vec(const float *__restrict__ src, int K, float *xs) {
+  for (int k = threadIdx.x; k < K; k += BLOCK) xs[k] = src[k];
+  __syncthreads();
+}
+
+// xs = rms_norm(src; alpha): y = x * alpha * 1/sqrt(eps + mean(x^2)) (eps inside the mean).
+__device__ __forceinline__ void stage_rms(const float *__restrict__ src, const float *__restrict__ alpha, int K,
+                                          float eps, float *xs, float *red) {
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < K; k += BLOCK) {
+    const float v = src[k];
+    xs[k] = v;
+    ss = fmaf(v, v, ss);
+  }
+  const float tot = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(eps + tot / (float)K);
+  for (int k = threadIdx.x; k < K; k += BLOCK) xs[k] = (xs[k] * alpha[k]) * inv;
+  __syncthreads();
+}
+
+// In-place rms_norm of xs[0..K) already staged in LDS.
+__device__ __forceinline__ void rms_in_place(float *xs, const float *__restrict__ alpha, int K, float eps, float *red) {
+  float ss = 0.f;
+  for (int k = threadIdx.x; k < K; k += BLOCK) ss = fmaf(xs[k], xs[k], ss);
+  const float tot = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(eps + tot / (float)K);
+  for (int k = threadIdx.x; k < K; k += BLOCK) xs[k] = (xs[k] * alpha[k]) * inv;
+  __syncthreads();
+}
+
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+// Delay of stream s for dep_q codebooks: text 0 | generated cb0 0, cb1.. 1 | user cb0 0, cb1.. 1.
+__device__ __forceinline__ int stream_delay(int s, int Q) {
+  if (s == 0) return 0;
+  const int k = (s - 1) % Q;
+  return k == 0 ? 0 : 1;
+}
+
+}  // namespace mk

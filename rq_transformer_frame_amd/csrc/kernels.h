@@ -1,0 +1,613 @@
+// Frame-step kernels for gfx950.  Kernels used by several stages take the stage id as a template
+// tag, so that each stage is its own symbol in profiler traces.  Each kernel is one stage of the Moshi RQ-Transformer frame as
+// the docs.rs page "inferencelayer 0.2.4 src/moshi_lm.rs" defines it (cited as [LM]); the weight
+// streaming GEMV core is shared by every projection.
+#pragma once
+#include "device_common.h"
+
+namespace mk {
+
+// Shapes of one session (all ints are element counts).
+struct Dims {
+  int B;                // conversations
+  int L, D, H, hd, F;   // temporal: layers, width, heads, head dim, FFN hidden
+  int C, cap;           // context window, KV slots held per conversation
+  int Vt, Va;           // text / audio head widths (tables have one more row)
+  int Ld, Dd, Hd, hdd, Fd, Q;  // depformer
+  int NS;               // 2 * Q + 1 token streams
+  int S;                // temporal attention splits over positions
+  float eps;
+};
+
+// Device-resident session state and activations.
+struct Bufs {
+  int32_t *ring;        // [B][NS][3]  token ring ([LM] MoshiState cache)
+  int64_t *offset;      // [B]         absolute position of the next step
+  int32_t *user;        // [B][Q]      this step's user tokens
+  int32_t *inputs;      // [B][NS]     gathered model inputs (trace)
+  float *x;             // [B][D]      temporal residual stream
+  float *emb_sum;       // [B][D]      summed embedding (trace)
+  float *hidden;        // [B][D]      post-out_norm hidden
+  float *q;             // [B][D]      roped query
+  float *o;             // [B][D]      attention output
+  float *a;             // [B][F]      silu(gate) * mult
+  float *text_logits;   // [B][Vt]
+  int32_t *tokens;      // [B][1+Q]    text, audio cb0..Q-1 of this step
+  float *din;           // [B][Q][Dd]  depformer_in[cb] . hidden
+  float *y;             // [B][Dd]     depformer residual stream
+  float *dq;            // [B][Dd]
+  float *dkv;           // [B][Ld][Q][2][Dd] per-frame depformer KV
+  float *da;            // [B][Fd]
+  float *audio_logits;  // [B][Q][Va]
+  int32_t *outpack;     // [B][1+Q] realigned output, then [B] has_out
+  float *attn_part;     // [B][H][S][hd+2] (max, sum, o[hd]) per split
+  uint32_t *attn_cnt;   // [B][H]
+  ArgBest *am_part;     // [B][1+Q][AM_MAX_BLOCKS]
+  uint32_t *am_cnt;     // [B][1+Q]
+  float *rope_freq;     // [hd/2]
+};
+
+constexpr int AM_MAX_BLOCKS = 1024;
+
+template <typename KT>
+struct KV {
+  KT *k, *v;  // [B][L][H][cap][hd]
+};
+
+// --------------------------------------------------------------------------------------------
+// a1-a3: user write, gather with INITIAL substitution, 17-row embedding sum ([LM] step_ext
+// steps 1-3, MoshiLm::embed).  Grid (ceil(D / BLOCK), nb); conversation b = b0 + blockIdx.y.
+// `user` holds nb rows of Q tokens.
+// --------------------------------------------------------------------------------------------
+template <typename ET>
+__global__ __launch_bounds__(BLOCK) void k_embed_begin(Dims d, Bufs s, const ET *__restrict__ emb_audio,
+                                                       const ET *__restrict__ emb_text,
+                                                       const int32_t *__restrict__ user, int b0) {
+  __shared__ int tok[MAX_STREAMS];
+  const int b = b0 + blockIdx.y;
+  const int64_t off = s.offset[b];
+  const int32_t *urow = user + (size_t)blockIdx.y * d.Q;
+  if (threadIdx.x < d.NS) {
+    const int st = threadIdx.x;
+    const int delay = stream_delay(st, d.Q);
+    int v;
+    if (off <= delay)
+      v = (st == 0) ? d.Vt : d.Va;  // INITIAL token
+    else if (st >= d.Q + 1 && delay == 0)
+      v = urow[st - d.Q - 1];  // written this step at slot off % 3 and read back at once
+    else
+      v = s.ring[((size_t)b * d.NS + st) * 3 + (int)(off % 3)];
+    tok[st] = v;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x < d.NS) {
+    const int st = threadIdx.x;
+    s.inputs[(size_t)b * d.NS + st] = tok[st];
+    if (st >= d.Q + 1)
+      s.ring[((size_t)b * d.NS + st) * 3 + (int)((off + stream_delay(st, d.Q)) % 3)] = urow[st - d.Q - 1];
+  }
+  for (int c = blockIdx.x * BLOCK + threadIdx.x; c < d.D; c += gridDim.x * BLOCK) {
+    float acc = 0.f;
+    for (int k = 0; k < 2 * d.Q; ++k) {
+      int t = tok[1 + k];
+      if (t != -1) {
+        t = t < 0 ? 0 : t;
+        acc += to_f(emb_audio[((size_t)k * (d.Va + 1) + t) * d.D + c]);
+      }
+    }
+    int t = tok[0];
+    if (t != -1) {
+      t = t < 0 ? 0 : t;
+      acc += to_f(emb_text[(size_t)t * d.D + c]);
+    }
+    s.x[(size_t)b * d.D + c] = acc;
+    s.emb_sum[(size_t)b * d.D + c] = acc;
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// a4.1: x -> rms_norm(norm1) -> fused q|k|v rows -> interleaved rope on q, k at pos = offset ->
+// q to s.q, k and v to KV slot offset % cap ([LM] temporal_step, rope_row).  Each wave owns a
+// row pair (2i, 2i+1), i.e. one rope pair.  Dynamic LDS: D floats.
+// --------------------------------------------------------------------------------------------
+template <typename WT, typename KT, int U>
+__global__ __launch_bounds__(BLOCK) void k_qkv_rope(Dims d, Bufs s, KV<KT> kv, const WT *__restrict__ w,
+                                                    const float *__restrict__ wscale,
+                                                    const float *__restrict__ norm, int layer, int b0) {
+  extern __shared__ float xs[];
+  __shared__ float red[NWAVES];
+  const int b = b0 + blockIdx.y;
+  stage_rms(s.x + (size_t)b * d.D, norm, d.D, d.eps, xs, red);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t pos = s.offset[b];
+  const int slot = (int)(pos % d.cap);
+  const int npairs = 3 * d.D / 2;
+  for (int pr = blockIdx.x * NWAVES + wave; pr < npairs; pr += gridDim.x * NWAVES) {
+    const int r0 = 2 * pr;
+    const int64_t ro[2] = {(int64_t)r0 * d.D, (int64_t)(r0 + 1) * d.D};
+    float acc[2];
+    wave_rows_dot<WT, 2, U>(w, d.D, ro, xs, acc);
+    acc[0] = wave_sum(acc[0]);
+    acc[1] = wave_sum(acc[1]);
+    if (lane == 0) {
+      float v0 = acc[0], v1 = acc[1];
+      if (wscale) {
+        v0 *= wscale[r0];
+        v1 *= wscale[r0 + 1];
+      }
+      const int part = r0 / d.D;  // 0 q, 1 k, 2 v
+      const int rr = r0 - part * d.D;
+      const int h = rr / d.hd, e = rr - h * d.hd;
+      if (part < 2) {
+        const float ang = s.rope_freq[e >> 1] * (float)pos;
+        double sd, cd;
+        sincos((double)ang, &sd, &cd);
+        const float sn = (float)sd, cs = (float)cd;
+        const float a0 = v0 * cs - v1 * sn;
+        const float a1 = v0 * sn + v1 * cs;
+        v0 = a0;
+        v1 = a1;
+      }
+      if (part == 0) {
+        s.q[(size_t)b * d.D + rr] = v0;
+        s.q[(size_t)b * d.D + rr + 1] = v1;
+      } else {
+        KT *cache = part == 1 ? kv.k : kv.v;
+        const size_t idx = ((((size_t)b * d.L + layer) * d.H + h) * d.cap + slot) * d.hd + e;
+        cache[idx] = from_f<KT>(v0);
+        cache[idx + 1] = from_f<KT>(v1);
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// a4.2: single-query attention of head h over the n = min(offset + 1, context) cached positions
+// ([LM] attend: scale 1/sqrt(hd) after the dot, max-subtracted softmax).  Grid (H, S, nb): split
+// sp takes a contiguous slice of the slots [0, n) (the softmax is order-free), writes its local
+// (max, sum, sum e*v), and the last split to finish combines the S partials in split order.
+// Dynamic LDS: ceil(cap / S) floats.
+// --------------------------------------------------------------------------------------------
+template <typename KT, int HD>
+__global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int layer, int b0) {
+  extern __shared__ float sc[];
+  __shared__ float red[NWAVES];
+  __shared__ float ored[NWAVES][HD];
+  __shared__ int s_last;
+  constexpr int EPL = HD / 16;  // elements per lane; 16 lanes cover one position's head slice
+  const int h = blockIdx.x, sp = blockIdx.y, S = gridDim.y;
+  const int b = b0 + blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
+  const int64_t pos = s.offset[b];
+  const int n = (int)(pos + 1 < (int64_t)d.C ? pos + 1 : (int64_t)d.C);
+  const int chunk = (n + S - 1) / S;
+  const int j0 = sp * chunk;
+  const int j1 = min(n, j0 + chunk);
+  const int len = j1 > j0 ? j1 - j0 : 0;
+
+  float qv[EPL];
+  const float *qp = s.q + (size_t)b * d.D + h * HD + sub * EPL;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) qv[i] = qp[i];
+  const float scale = 1.0f / sqrtf((float)HD);
+  const size_t base = (((size_t)b * d.L + layer) * d.H + h) * (size_t)d.cap * HD;
+  const KT *kb = kv.k + base, *vb = kv.v + base;
+
+  for (int jb = j0 + wave * 4; jb < j1; jb += NWAVES * 4) {
+    const int j = jb + g;
+    const bool ok = j < j1;
+    float dot = 0.f;
+    if (ok) {
+      const KT *kp = kb + (size_t)j * HD + sub * EPL;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], to_f(kp[i]), dot);
+    }
+    dot += __shfl_xor(dot, 8, WAVE);
+    dot += __shfl_xor(dot, 4, WAVE);
+    dot += __shfl_xor(dot, 2, WAVE);
+    dot += __shfl_xor(dot, 1, WAVE);
+    if (ok && sub == 0) sc[j - j0] = dot * scale;
+  }
+  __syncthreads();
+  float m = -INFINITY;
+  for (int t = threadIdx.x; t < len; t += BLOCK) m = fmaxf(m, sc[t]);
+  m = block_max(m, red);
+  float l = 0.f;
+  for (int t = threadIdx.x; t < len; t += BLOCK) {
+    const float e = expf(sc[t] - m);
+    sc[t] = e;
+    l += e;
+  }
+  l = block_sum(l, red);  // ends with a barrier, so sc[] is complete
+
+  float op[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) op[i] = 0.f;
+  for (int jb = j0 + wave * 4; jb < j1; jb += NWAVES * 4) {
+    const int j = jb + g;
+    if (j < j1) {
+      const float e = sc[j - j0];
+      const KT *vp = vb + (size_t)j * HD + sub * EPL;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) op[i] = fmaf(e, to_f(vp[i]), op[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    op[i] += __shfl_xor(op[i], 16, WAVE);
+    op[i] += __shfl_xor(op[i], 32, WAVE);
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) ored[wave][sub * EPL + i] = op[i];
+  }
+  __syncthreads();
+  float *part = s.attn_part + (((size_t)b * d.H + h) * S + sp) * (HD + 2);
+  for (int t = threadIdx.x; t < HD; t += BLOCK) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NWAVES; ++w2) acc += ored[w2][t];
+    part[2 + t] = acc;
+  }
+  if (threadIdx.x == 0) {
+    part[0] = m;
+    part[1] = l;
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = atomicAdd(&s.attn_cnt[(size_t)b * d.H + h], 1u);
+    s_last = (prev == (uint32_t)(S - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const float *p0 = s.attn_part + ((size_t)b * d.H + h) * S * (HD + 2);
+  float M = -INFINITY;
+  for (int k = 0; k < S; ++k) M = fmaxf(M, p0[(size_t)k * (HD + 2)]);
+  float Lsum = 0.f;
+  for (int k = 0; k < S; ++k) {
+    const float mk = p0[(size_t)k * (HD + 2)];
+    if (mk > -INFINITY) Lsum += expf(mk - M) * p0[(size_t)k * (HD + 2) + 1];
+  }
+  for (int t = threadIdx.x; t < HD; t += BLOCK) {
+    float acc = 0.f;
+    for (int k = 0; k < S; ++k) {
+      const float mk = p0[(size_t)k * (HD + 2)];
+      if (mk > -INFINITY) acc += expf(mk - M) * p0[(size_t)k * (HD + 2) + 2 + t];
+    }
+    s.o[(size_t)b * d.D + h * HD + t] = acc / Lsum;
+  }
+  if (threadIdx.x == 0) s.attn_cnt[(size_t)b * d.H + h] = 0u;
+}
+
+// --------------------------------------------------------------------------------------------
+// Residual projection: out[r] += (W . in)[r] ([LM] out_proj and gate_out followed by the
+// residual add).  `in` and `out` are per-conversation vectors with strides in_ld / out_ld.
+// Dynamic LDS: K floats.
+// --------------------------------------------------------------------------------------------
+template <typename WT, int R, int U, int TAG>
+__global__ __launch_bounds__(BLOCK) void k_gemv_residual(const WT *__restrict__ w, const float *__restrict__ wscale,
+                                                         int N, int K, const float *__restrict__ in, int in_ld,
+                                                         float *__restrict__ out, int out_ld, int b0) {
+  extern __shared__ float xs[];
+  const int b = b0 + blockIdx.y;
+  stage_vec(in + (size_t)b * in_ld, K, xs);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ngroups = (N + R - 1) / R;
+  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
+    int64_t ro[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, N - 1) * K;
+    float acc[R];
+    wave_rows_dot<WT, R, U>(w, K, ro, xs, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum(acc[r]);
+      const int row = gi * R + r;
+      if (lane == 0 && row < N) out[(size_t)b * out_ld + row] += wscale ? v * wscale[row] : v;
+    }
+  }
+}
+
+// Plain projection: out[r] = (W . in)[r] (depformer_in for all codebooks at once).
+template <typename WT, int R, int U, int TAG>
+__global__ __launch_bounds__(BLOCK) void k_gemv_store(const WT *__restrict__ w, const float *__restrict__ wscale,
+                                                      int N, int K, const float *__restrict__ in, int in_ld,
+                                                      float *__restrict__ out, int out_ld, int b0) {
+  extern __shared__ float xs[];
+  const int b = b0 + blockIdx.y;
+  stage_vec(in + (size_t)b * in_ld, K, xs);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ngroups = (N + R - 1) / R;
+  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
+    int64_t ro[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, N - 1) * K;
+    float acc[R];
+    wave_rows_dot<WT, R, U>(w, K, ro, xs, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum(acc[r]);
+      const int row = gi * R + r;
+      if (lane == 0 && row < N) out[(size_t)b * out_ld + row] = wscale ? v * wscale[row] : v;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// a5 (first half): h = rms_norm(x; norm2), g = linear_in . h, a[j] = silu(g[j]) * g[F + j]
+// ([LM] temporal_step / depformer_cycle gating, rows packed [gate | mult]).  A wave owns the
+// row pair (j, F + j).  Dynamic LDS: K floats.
+// --------------------------------------------------------------------------------------------
+template <typename WT, int U, int TAG>
+__global__ __launch_bounds__(BLOCK) void k_gate(const WT *__restrict__ w, const float *__restrict__ wscale, int F,
+                                                int K, const float *__restrict__ x, int x_ld,
+                                                const float *__restrict__ norm, float eps,
+                                                float *__restrict__ a, int a_ld, int b0) {
+  extern __shared__ float xs[];
+  __shared__ float red[NWAVES];
+  const int b = b0 + blockIdx.y;
+  stage_rms(x + (size_t)b * x_ld, norm, K, eps, xs, red);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int j = blockIdx.x * NWAVES + wave; j < F; j += gridDim.x * NWAVES) {
+    const int64_t ro[2] = {(int64_t)j * K, (int64_t)(F + j) * K};
+    float acc[2];
+    wave_rows_dot<WT, 2, U>(w, K, ro, xs, acc);
+    float gv = wave_sum(acc[0]), mv = wave_sum(acc[1]);
+    if (lane == 0) {
+      if (wscale) {
+        gv *= wscale[j];
+        mv *= wscale[F + j];
+      }
+      a[(size_t)b * a_ld + j] = silu(gv) * mv;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// a6-a8 heads: logits = W . v with v = rms_norm(src; norm) (text head after out_norm) or v = src
+// (depformer heads read y with no norm), then first-wins argmax of the logits into tok_out.
+// Blocks keep their best row in am_part; the last block to finish merges them in block order.
+// With hid_out set, block 0 also stores the normalised vector (the post-out_norm hidden).
+// Dynamic LDS: K floats.
+// --------------------------------------------------------------------------------------------
+template <typename WT, int R, int U, int TAG>
+__global__ __launch_bounds__(BLOCK) void k_head_argmax(const WT *__restrict__ w, const float *__restrict__ wscale,
+                                                       int N, int K, const float *__restrict__ src, int src_ld,
+                                                       const float *__restrict__ norm, float eps,
+                                                       float *__restrict__ hid_out, float *__restrict__ logits,
+                                                       int logits_ld, ArgBest *__restrict__ am_part, int am_ld,
+                                                       uint32_t *__restrict__ am_cnt, int cnt_ld,
+                                                       int32_t *__restrict__ tok_out, int tok_ld, int b0) {
+  extern __shared__ float xs[];
+  __shared__ float red[NWAVES];
+  __shared__ ArgBest wbest[NWAVES];
+  __shared__ int s_last;
+  const int b = b0 + blockIdx.y;
+  if (norm)
+    stage_rms(src + (size_t)b * src_ld, norm, K, eps, xs, red);
+  else
+    stage_vec(src + (size_t)b * src_ld, K, xs);
+  if (hid_out && blockIdx.x == 0)
+    for (int k = threadIdx.x; k < K; k += BLOCK) hid_out[(size_t)b * src_ld + k] = xs[k];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ngroups = (N + R - 1) / R;
+  ArgBest best = arg_none();
+  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
+    int64_t ro[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, N - 1) * K;
+    float acc[R];
+    wave_rows_dot<WT, R, U>(w, K, ro, xs, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float v = wave_sum(acc[r]);
+      const int row = gi * R + r;
+      if (lane == 0 && row < N) {
+        if (wscale) v *= wscale[row];
+        logits[(size_t)b * logits_ld + row] = v;
+        best = arg_take(best, v, row);
+      }
+    }
+  }
+  if (lane == 0) wbest[wave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ArgBest bb = wbest[0];
+    for (int i = 1; i < NWAVES; ++i) bb = arg_merge(bb, wbest[i]);
+    am_part[(size_t)b * am_ld + blockIdx.x] = bb;
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = atomicAdd(&am_cnt[(size_t)b * cnt_ld], 1u);
+    s_last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  if (threadIdx.x < WAVE) {
+    ArgBest bb = arg_none();
+    for (int i = threadIdx.x; i < (int)gridDim.x; i += WAVE) bb = arg_merge(bb, am_part[(size_t)b * am_ld + i]);
+    bb = wave_arg(bb);
+    if (threadIdx.x == 0) {
+      tok_out[(size_t)b * tok_ld] = bb.i < 0 ? 0 : bb.i;
+      am_cnt[(size_t)b * cnt_ld] = 0u;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// a8 depformer step cb, layer j, first half: y (layer 0: depformer_in[cb] . hidden + emb(prev))
+// -> rms_norm(norm1_j) -> q|k|v rows of in_projs[j][cb] (no rope) -> q to dq, k and v to the
+// per-frame cache entry (j, cb) ([LM] depformer_cycle).  Dynamic LDS: Dd floats.
+// --------------------------------------------------------------------------------------------
+template <typename WT, typename ET, int R, int U>
+__global__ __launch_bounds__(BLOCK) void k_dep_qkv(Dims d, Bufs s, const WT *__restrict__ w,
+                                                   const float *__restrict__ wscale, const float *__restrict__ norm,
+                                                   const ET *__restrict__ table, int layer, int cb, int b0) {
+  extern __shared__ float xs[];
+  __shared__ float red[NWAVES];
+  const int b = b0 + blockIdx.y;
+  const int Dd = d.Dd;
+  float *y = s.y + (size_t)b * Dd;
+  if (layer == 0) {
+    int prev = s.tokens[(size_t)b * (1 + d.Q) + cb];  // text for cb 0, else audio[cb - 1]
+    const float *dinp = s.din + ((size_t)b * d.Q + cb) * Dd;
+    for (int k = threadIdx.x; k < Dd; k += BLOCK) {
+      float v = dinp[k];
+      if (prev != -1) v += to_f(table[(size_t)(prev < 0 ? 0 : prev) * Dd + k]);
+      xs[k] = v;
+      if (blockIdx.x == 0) y[k] = v;
+    }
+    __syncthreads();
+    rms_in_place(xs, norm, Dd, d.eps, red);
+  } else {
+    stage_rms(y, norm, Dd, d.eps, xs, red);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = 3 * Dd;
+  const int ngroups = (N + R - 1) / R;
+  float *kvbase = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q + cb) * 2) * Dd;
+  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
+    int64_t ro[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, N - 1) * Dd;
+    float acc[R];
+    wave_rows_dot<WT, R, U>(w, Dd, ro, xs, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float v = wave_sum(acc[r]);
+      const int row = gi * R + r;
+      if (lane == 0 && row < N) {
+        if (wscale) v *= wscale[row];
+        if (row < Dd)
+          s.dq[(size_t)b * Dd + row] = v;
+        else
+          kvbase[row - Dd] = v;  // k at [0, Dd), v at [Dd, 2 Dd)
+      }
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// a8 depformer step cb, layer j, attention + out_proj: every block recomputes the attention of
+// dq over the cb + 1 cache entries of layer j (all heads; [LM] attend) into LDS, then
+// y[r] += out_projs[j][cb] . o.  Dynamic LDS: Dd floats.
+// --------------------------------------------------------------------------------------------
+template <typename WT, int R, int U>
+__global__ __launch_bounds__(BLOCK) void k_dep_out(Dims d, Bufs s, const WT *__restrict__ w,
+                                                   const float *__restrict__ wscale, int layer, int cb, int b0) {
+  extern __shared__ float xs[];
+  const int b = b0 + blockIdx.y;
+  const int Dd = d.Dd, hdd = d.hdd;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float *q = s.dq + (size_t)b * Dd;
+  const float *kv0 = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q) * 2) * Dd;
+  const float scale = 1.0f / sqrtf((float)hdd);
+  const int npos = cb + 1;
+  for (int hh = wave; hh < d.Hd; hh += NWAVES) {
+    float sc[16];
+    float m = -INFINITY;
+    for (int p = 0; p < npos; ++p) {
+      const float *kp = kv0 + (size_t)p * 2 * Dd + hh * hdd;
+      float dot = 0.f;
+      for (int e = lane; e < hdd; e += WAVE) dot = fmaf(q[hh * hdd + e], kp[e], dot);
+      sc[p] = wave_sum_bcast(dot) * scale;
+      m = fmaxf(m, sc[p]);
+    }
+    float den = 0.f;
+    for (int p = 0; p < npos; ++p) {
+      sc[p] = expf(sc[p] - m);
+      den += sc[p];
+    }
+    for (int e = lane; e < hdd; e += WAVE) {
+      float o = 0.f;
+      for (int p = 0; p < npos; ++p) o = fmaf(sc[p] / den, kv0[(size_t)p * 2 * Dd + Dd + hh * hdd + e], o);
+      xs[hh * hdd + e] = o;
+    }
+  }
+  __syncthreads();
+  const int ngroups = (Dd + R - 1) / R;
+  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
+    int64_t ro[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, Dd - 1) * Dd;
+    float acc[R];
+    wave_rows_dot<WT, R, U>(w, Dd, ro, xs, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float v = wave_sum(acc[r]);
+      const int row = gi * R + r;
+      if (lane == 0 && row < Dd) s.y[(size_t)b * Dd + row] += wscale ? v * wscale[row] : v;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------------------------
+// a9: offset += 1, ring slot offset % 3 <- this step's text and audio tokens, then the
+// delay-realigned output read at (offset - 1 + delay) % 3 once offset > 1 ([LM] step_ext steps
+// 7-8).  With `forced` set (teacher-forced prefill, [LM] step_forced) the ring gets forced[0..Q]
+// instead and no output is produced.  Grid (nb), one thread does the work.
+// --------------------------------------------------------------------------------------------
+struct Forced {
+  int32_t t[17];
+};
+
+__global__ void k_frame_end(Dims d, Bufs s, int b0, int use_forced, Forced forced) {
+  if (threadIdx.x != 0) return;
+  const int b = b0 + blockIdx.x;
+  const int64_t off = s.offset[b] + 1;
+  s.offset[b] = off;
+  const int p = (int)(off % 3);
+  int32_t *rg = s.ring + (size_t)b * d.NS * 3;
+  const int32_t *tk = s.tokens + (size_t)b * (1 + d.Q);
+  for (int st = 0; st <= d.Q; ++st) rg[st * 3 + p] = use_forced ? forced.t[st] : tk[st];
+  int32_t *out = s.outpack + (size_t)b * (1 + d.Q);
+  int32_t *has = s.outpack + (size_t)d.B * (1 + d.Q) + b;
+  if (!use_forced && off > 1) {
+    for (int st = 0; st <= d.Q; ++st) out[st] = rg[st * 3 + (int)((off - 1 + stream_delay(st, d.Q)) % 3)];
+    *has = 1;
+  } else {
+    *has = 0;
+  }
+}
+
+// [LM] state(): ring <- -2, offset <- 0 for conversations [b0, b0 + gridDim.x).
+__global__ void k_reset(Dims d, Bufs s, int b0) {
+  const int b = b0 + blockIdx.x;
+  for (int i = threadIdx.x; i < d.NS * 3; i += blockDim.x) s.ring[(size_t)b * d.NS * 3 + i] = -2;
+  if (threadIdx.x == 0) s.offset[b] = 0;
+}
+
+// [LM] force_generated: ring slot offset % 3 of the text and generated streams <- forced tokens.
+__global__ void k_force(Dims d, Bufs s, int b, Forced forced) {
+  if (threadIdx.x != 0) return;
+  const int p = (int)(s.offset[b] % 3);
+  for (int st = 0; st <= d.Q; ++st) s.ring[((size_t)b * d.NS + st) * 3 + p] = forced.t[st];
+}
+
+// Per-row symmetric int8 quantisation (load time): s_r = max|w_r| / 127, q = round half away
+// from zero of w / s_r, clamped to [-127, 127]; q = 0 when s_r = 0.  One block per row.
+__global__ __launch_bounds__(BLOCK) void k_quant_rows(const float *__restrict__ w, int64_t K, int8_t *__restrict__ q,
+                                                      float *__restrict__ scale, int64_t row0) {
+  __shared__ float red[NWAVES];
+  const int64_t r = row0 + blockIdx.x;
+  const float *wr = w + (size_t)blockIdx.x * K;
+  float am = 0.f;
+  for (int64_t k = threadIdx.x; k < K; k += BLOCK) am = fmaxf(am, fabsf(wr[k]));
+  am = block_max(am, red);
+  const float s_r = am / 127.0f;
+  for (int64_t k = threadIdx.x; k < K; k += BLOCK) {
+    float v = 0.f;
+    if (s_r > 0.f) {
+      v = roundf(wr[k] / s_r);
+      v = fminf(fmaxf(v, -127.f), 127.f);
+    }
+    q[(size_t)r * K + k] = (int8_t)(int)v;
+  }
+  if (threadIdx.x == 0) scale[r] = s_r;
+}
+
+}  // namespace mk

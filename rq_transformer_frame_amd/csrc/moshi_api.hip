@@ -1,0 +1,951 @@
+// Host side of the MI355X Moshi frame step: session state, device arenas, weight loading,
+// frame orchestration (stream launches or one hipGraph per frame) and the C ABI declared in
+// include/moshi_mi355x.h.  The step follows the docs.rs page "inferencelayer 0.2.4
+// src/moshi_lm.rs" ([LM]): MoshiLm::step_ext and the items it calls.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <unordered_map>
+#include <vector>
+
+#include "kernels.h"
+#include "moshi_mi355x.h"
+
+using mk::bf16_t;
+
+namespace {
+
+enum Kind { K_LINEAR = 0, K_EMBED = 1, K_NORM = 2 };
+
+struct Slot {
+  std::string name;
+  int64_t rows, cols;  // cols == 0 for 1-D
+  Kind kind;
+  size_t off = 0, soff = 0;  // byte offsets of data / int8 scales in the weight arena
+  bool loaded = false;
+};
+
+struct LayerW {
+  int in, out, gin, gout, norm1, norm2;  // slot indices
+};
+
+uint16_t host_f2bf(float f) {
+  uint32_t b;
+  std::memcpy(&b, &f, 4);
+  if ((b & 0x7F800000u) == 0x7F800000u) return (uint16_t)((b >> 16) | ((b & 0xFFFFu) ? 0x40u : 0u));
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+float host_bf2f(uint16_t v) {
+  uint32_t b = (uint32_t)v << 16;
+  float f;
+  std::memcpy(&f, &b, 4);
+  return f;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct moshi_state {
+  moshi_config cfg{};
+  mk::Dims d{};
+  int device = 0;
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+
+  // weights
+  char *warena = nullptr;
+  size_t wbytes = 0;
+  int64_t linear_bytes = 0;
+  std::vector<Slot> slots;
+  std::unordered_map<std::string, int> slot_of;
+  int n_loaded = 0;
+  int emb_group = -1, text_emb = -1, out_norm = -1, text_lin = -1, dep_text_emb = -1;
+  std::vector<int> emb, din, lin, dep_emb;
+  std::vector<LayerW> layers;
+  std::vector<int> dnorm1, dnorm2;
+  std::vector<std::vector<LayerW>> dlayers;  // [layer][cb]
+
+  // session
+  char *sarena = nullptr;
+  size_t sbytes = 0;
+  mk::Bufs b{};
+  void *kc = nullptr, *vc = nullptr;
+  int32_t *h_pin = nullptr;  // pinned: user [B][Q] then outpack [B][1+Q] + [B]
+  std::vector<int64_t> h_offset;
+
+  hipGraphExec_t gexec = nullptr;
+  std::string err;
+  bool broken = false;
+
+  template <typename T>
+  T *wptr(size_t off) const {
+    return reinterpret_cast<T *>(warena + off);
+  }
+  const void *data(int slot) const { return warena + slots[slot].off; }
+  const float *scale(int slot) const {
+    return cfg.band == MOSHI_BAND_I8 ? reinterpret_cast<const float *>(warena + slots[slot].soff) : nullptr;
+  }
+};
+
+namespace {
+
+moshi_status fail(moshi_state *s, moshi_status code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (s) s->err = buf;
+  if (s && code == MOSHI_EDEVICE) s->broken = true;
+  return code;
+}
+
+#define HIP_TRY(s, expr)                                                                    \
+  do {                                                                                      \
+    hipError_t e_ = (expr);                                                                 \
+    if (e_ != hipSuccess) return fail((s), MOSHI_EDEVICE, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+size_t linear_elt(int band) { return band == MOSHI_BAND_F32 ? 4 : band == MOSHI_BAND_BF16 ? 2 : 1; }
+size_t embed_elt(int band) { return band == MOSHI_BAND_F32 ? 4 : 2; }
+
+// Lay out every checkpoint tensor in one arena.  Groups that a kernel indexes as one array are
+// contiguous: the 2Q audio tables, the Q depformer_in matrices (and their scales), the Q-1
+// depformer audio tables.
+void plan_weights(moshi_state *s) {
+  const moshi_config &c = s->cfg;
+  const int band = c.band;
+  const int64_t D = c.d_model, F = c.ffn_hidden, Dd = c.dep_d_model, Fd = c.dep_ffn_hidden;
+  const int64_t Vt = c.text_card, Va = c.audio_card;
+  const int Q = c.dep_q;
+  size_t off = 0;
+  auto add = [&](const std::string &name, int64_t rows, int64_t cols, Kind kind) {
+    Slot sl;
+    sl.name = name;
+    sl.rows = rows;
+    sl.cols = cols;
+    sl.kind = kind;
+    s->slot_of[name] = (int)s->slots.size();
+    s->slots.push_back(sl);
+    return (int)s->slots.size() - 1;
+  };
+  auto place = [&](int i) {
+    Slot &sl = s->slots[i];
+    const int64_t n = sl.rows * std::max<int64_t>(sl.cols, 1);
+    const size_t elt = sl.kind == K_LINEAR ? linear_elt(band) : sl.kind == K_EMBED ? embed_elt(band) : 4;
+    sl.off = off;
+    off += (size_t)n * elt;
+    if (sl.kind == K_LINEAR) s->linear_bytes += (int64_t)n * (int64_t)elt;
+  };
+  auto place_scales = [&](int i) {
+    if (band != MOSHI_BAND_I8) return;
+    s->slots[i].soff = off;
+    off += (size_t)s->slots[i].rows * 4;
+    s->linear_bytes += s->slots[i].rows * 4;
+  };
+  // audio tables, contiguous [2Q][Va+1][D]
+  for (int k = 0; k < 2 * Q; ++k) s->emb.push_back(add("emb." + std::to_string(k) + ".weight", Va + 1, D, K_EMBED));
+  for (int i : s->emb) place(i);
+  off = align256(off);
+  s->text_emb = add("text_emb.weight", Vt + 1, D, K_EMBED);
+  place(s->text_emb);
+  off = align256(off);
+  for (int l = 0; l < c.n_layers; ++l) {
+    const std::string p = "transformer.layers." + std::to_string(l);
+    LayerW lw;
+    lw.norm1 = add(p + ".norm1.alpha", D, 0, K_NORM);
+    lw.norm2 = add(p + ".norm2.alpha", D, 0, K_NORM);
+    lw.in = add(p + ".self_attn.in_projs.0.weight", 3 * D, D, K_LINEAR);
+    lw.out = add(p + ".self_attn.out_projs.0.weight", D, D, K_LINEAR);
+    lw.gin = add(p + ".gating.linear_in.weight", 2 * F, D, K_LINEAR);
+    lw.gout = add(p + ".gating.linear_out.weight", D, F, K_LINEAR);
+    for (int i : {lw.norm1, lw.norm2, lw.in, lw.out, lw.gin, lw.gout}) {
+      place(i);
+      off = align256(off);
+      place_scales(i);
+      off = align256(off);
+    }
+    s->layers.push_back(lw);
+  }
+  s->out_norm = add("out_norm.alpha", D, 0, K_NORM);
+  place(s->out_norm);
+  off = align256(off);
+  s->text_lin = add("text_linear.weight", Vt, D, K_LINEAR);
+  place(s->text_lin);
+  off = align256(off);
+  place_scales(s->text_lin);
+  off = align256(off);
+  // depformer_in, contiguous [Q][Dd][D] and scales [Q][Dd]
+  for (int k = 0; k < Q; ++k) s->din.push_back(add("depformer_in." + std::to_string(k) + ".weight", Dd, D, K_LINEAR));
+  for (int i : s->din) place(i);
+  off = align256(off);
+  for (int i : s->din) place_scales(i);
+  off = align256(off);
+  s->dep_text_emb = add("depformer_text_emb.weight", Vt + 1, Dd, K_EMBED);
+  place(s->dep_text_emb);
+  off = align256(off);
+  for (int k = 0; k < Q - 1; ++k)
+    s->dep_emb.push_back(add("depformer_emb." + std::to_string(k) + ".weight", Va + 1, Dd, K_EMBED));
+  for (int i : s->dep_emb) place(i);
+  off = align256(off);
+  for (int l = 0; l < c.dep_layers; ++l) {
+    const std::string p = "depformer.layers." + std::to_string(l);
+    s->dnorm1.push_back(add(p + ".norm1.alpha", Dd, 0, K_NORM));
+    place(s->dnorm1.back());
+    off = align256(off);
+    s->dnorm2.push_back(add(p + ".norm2.alpha", Dd, 0, K_NORM));
+    place(s->dnorm2.back());
+    off = align256(off);
+    std::vector<LayerW> per;
+    for (int k = 0; k < Q; ++k) {
+      LayerW lw;
+      lw.norm1 = s->dnorm1.back();
+      lw.norm2 = s->dnorm2.back();
+      lw.in = add(p + ".self_attn.in_projs." + std::to_string(k) + ".weight", 3 * Dd, Dd, K_LINEAR);
+      lw.out = add(p + ".self_attn.out_projs." + std::to_string(k) + ".weight", Dd, Dd, K_LINEAR);
+      lw.gin = add(p + ".gating." + std::to_string(k) + ".linear_in.weight", 2 * Fd, Dd, K_LINEAR);
+      lw.gout = add(p + ".gating." + std::to_string(k) + ".linear_out.weight", Dd, Fd, K_LINEAR);
+      for (int i : {lw.in, lw.out, lw.gin, lw.gout}) {
+        place(i);
+        off = align256(off);
+        place_scales(i);
+        off = align256(off);
+      }
+      per.push_back(lw);
+    }
+    s->dlayers.push_back(per);
+  }
+  for (int k = 0; k < Q; ++k) {
+    s->lin.push_back(add("linears." + std::to_string(k) + ".weight", Va, Dd, K_LINEAR));
+    place(s->lin.back());
+    off = align256(off);
+    place_scales(s->lin.back());
+    off = align256(off);
+  }
+  s->wbytes = align256(off);
+}
+
+// Session buffers in one arena.
+moshi_status alloc_session(moshi_state *s) {
+  const mk::Dims &d = s->d;
+  const size_t B = d.B;
+  const size_t kvelt = s->cfg.band == MOSHI_BAND_F32 ? 4 : 2;
+  size_t off = 0;
+  struct Req {
+    void **dst;
+    size_t bytes;
+  };
+  std::vector<Req> reqs;
+  auto req = [&](void **dst, size_t bytes) { reqs.push_back({dst, bytes}); };
+  mk::Bufs &b = s->b;
+  req((void **)&b.ring, B * d.NS * 3 * 4);
+  req((void **)&b.offset, B * 8);
+  req((void **)&b.user, B * d.Q * 4);
+  req((void **)&b.inputs, B * d.NS * 4);
+  req((void **)&b.x, B * d.D * 4);
+  req((void **)&b.emb_sum, B * d.D * 4);
+  req((void **)&b.hidden, B * d.D * 4);
+  req((void **)&b.q, B * d.D * 4);
+  req((void **)&b.o, B * d.D * 4);
+  req((void **)&b.a, B * d.F * 4);
+  req((void **)&b.text_logits, B * d.Vt * 4);
+  req((void **)&b.tokens, B * (1 + d.Q) * 4);
+  req((void **)&b.din, B * d.Q * d.Dd * 4);
+  req((void **)&b.y, B * d.Dd * 4);
+  req((void **)&b.dq, B * d.Dd * 4);
+  req((void **)&b.dkv, B * d.Ld * d.Q * 2 * d.Dd * 4);
+  req((void **)&b.da, B * d.Fd * 4);
+  req((void **)&b.audio_logits, B * d.Q * d.Va * 4);
+  req((void **)&b.outpack, B * (1 + d.Q) * 4 + B * 4);
+  req((void **)&b.attn_part, B * d.H * d.S * (d.hd + 2) * 4);
+  req((void **)&b.attn_cnt, B * d.H * 4);
+  req((void **)&b.am_part, B * (1 + d.Q) * mk::AM_MAX_BLOCKS * sizeof(mk::ArgBest));
+  req((void **)&b.am_cnt, B * (1 + d.Q) * 4);
+  req((void **)&b.rope_freq, (size_t)(d.hd / 2) * 4);
+  req(&s->kc, B * d.L * d.H * (size_t)d.cap * d.hd * kvelt);
+  req(&s->vc, B * d.L * d.H * (size_t)d.cap * d.hd * kvelt);
+  std::vector<size_t> offs;
+  for (auto &r : reqs) {
+    offs.push_back(off);
+    off = align256(off + r.bytes);
+  }
+  s->sbytes = off;
+  hipError_t e = hipMalloc(&s->sarena, s->sbytes);
+  if (e != hipSuccess) return fail(s, MOSHI_ENOMEM, "session arena of %zu bytes: %s", s->sbytes, hipGetErrorString(e));
+  for (size_t i = 0; i < reqs.size(); ++i) *reqs[i].dst = s->sarena + offs[i];
+  // counters must start at zero; everything else is written before it is read
+  HIP_TRY(s, hipMemset(s->sarena, 0, s->sbytes));
+  // rope frequencies f_i = exp(-ln(theta) * 2 i / hd), formed in float32 ([LM] rope_row)
+  std::vector<float> fr(d.hd / 2);
+  const float ln_theta = (float)std::log((double)s->cfg.rope_theta);
+  for (int i = 0; i < d.hd / 2; ++i) {
+    const float arg = ((-ln_theta) * 2.0f) * (float)i / (float)d.hd;
+    fr[i] = (float)std::exp((double)arg);
+  }
+  HIP_TRY(s, hipMemcpy(b.rope_freq, fr.data(), fr.size() * 4, hipMemcpyHostToDevice));
+  hipError_t he = hipHostMalloc((void **)&s->h_pin, (B * d.Q + B * (1 + d.Q) + B) * 4, hipHostMallocDefault);
+  if (he != hipSuccess) return fail(s, MOSHI_ENOMEM, "pinned host buffer: %s", hipGetErrorString(he));
+  return MOSHI_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Kernel launch configuration
+// ---------------------------------------------------------------------------------------------
+constexpr int MAX_GEMV_BLOCKS = 2048;
+
+int blocks_for(int64_t units, int per_block, int cap = MAX_GEMV_BLOCKS) {
+  int64_t g = (units + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (int)std::min<int64_t>(g, cap);
+}
+
+// Optional per-launch HIP event timing (measurement hook): each launch is bracketed by an event
+// pair on the session stream and tagged with its stage.
+struct Prof {
+  std::vector<hipEvent_t> ev;
+  std::vector<int> stage;  // stage of event pair i
+  size_t used = 0;
+};
+
+template <typename WT, typename ET, typename KT>
+void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const int32_t *user_dev,
+                     const mk::Forced &forced, Prof *prof) {
+  using namespace mk;
+  const Dims &d = s->d;
+  Bufs &b = s->b;
+  hipStream_t st = s->stream;
+  const KV<KT> kv{reinterpret_cast<KT *>(s->kc), reinterpret_cast<KT *>(s->vc)};
+  auto W = [&](int slot) { return reinterpret_cast<const WT *>(s->data(slot)); };
+  auto E = [&](int slot) { return reinterpret_cast<const ET *>(s->data(slot)); };
+  auto N = [&](int slot) { return reinterpret_cast<const float *>(s->data(slot)); };
+  auto run = [&](int stage, auto &&launch) {
+    if (prof && prof->used + 2 <= prof->ev.size()) {
+      (void)hipEventRecord(prof->ev[prof->used], st);
+      launch();
+      (void)hipEventRecord(prof->ev[prof->used + 1], st);
+      prof->stage[prof->used / 2] = stage;
+      prof->used += 2;
+    } else {
+      launch();
+    }
+  };
+
+  run(MOSHI_STAGE_EMBED, [&] {
+    k_embed_begin<ET><<<dim3(blocks_for(d.D, BLOCK, 64), nb), BLOCK, 0, st>>>(d, b, E(s->emb[0]), E(s->text_emb),
+                                                                                user_dev, b0);
+  });
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW &lw = s->layers[l];
+    run(MOSHI_STAGE_QKV, [&] {
+      k_qkv_rope<WT, KT, 4><<<dim3(blocks_for(3 * d.D / 2, NWAVES), nb), BLOCK, d.D * 4, st>>>(
+          d, b, kv, W(lw.in), s->scale(lw.in), N(lw.norm1), l, b0);
+    });
+    const int chunk = (d.cap + d.S - 1) / d.S;
+    run(MOSHI_STAGE_ATTN, [&] {
+      if (d.hd == 128)
+        k_attn<KT, 128><<<dim3(d.H, d.S, nb), BLOCK, chunk * 4, st>>>(d, b, kv, l, b0);
+      else
+        k_attn<KT, 64><<<dim3(d.H, d.S, nb), BLOCK, chunk * 4, st>>>(d, b, kv, l, b0);
+    });
+    run(MOSHI_STAGE_OUT_PROJ, [&] {
+      k_gemv_residual<WT, 2, 4, MOSHI_STAGE_OUT_PROJ><<<dim3(blocks_for(d.D, 2 * NWAVES), nb), BLOCK, d.D * 4, st>>>(
+          W(lw.out), s->scale(lw.out), d.D, d.D, b.o, d.D, b.x, d.D, b0);
+    });
+    run(MOSHI_STAGE_GATE_IN, [&] {
+      k_gate<WT, 4, MOSHI_STAGE_GATE_IN><<<dim3(blocks_for(d.F, NWAVES), nb), BLOCK, d.D * 4, st>>>(
+          W(lw.gin), s->scale(lw.gin), d.F, d.D, b.x, d.D, N(lw.norm2), d.eps, b.a, d.F, b0);
+    });
+    run(MOSHI_STAGE_GATE_OUT, [&] {
+      k_gemv_residual<WT, 2, 4, MOSHI_STAGE_GATE_OUT><<<dim3(blocks_for(d.D, 2 * NWAVES), nb), BLOCK, d.F * 4, st>>>(
+          W(lw.gout), s->scale(lw.gout), d.D, d.F, b.a, d.F, b.x, d.D, b0);
+    });
+  }
+  if (!temporal_only) {
+    const int AM = (1 + d.Q) * AM_MAX_BLOCKS;
+    // out_norm -> hidden, text head, greedy text token into tokens[0]
+    run(MOSHI_STAGE_TEXT_HEAD, [&] {
+      k_head_argmax<WT, 2, 4, MOSHI_STAGE_TEXT_HEAD>
+          <<<dim3(blocks_for(d.Vt, 2 * NWAVES, AM_MAX_BLOCKS), nb), BLOCK, d.D * 4, st>>>(
+              W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, b.x, d.D, N(s->out_norm), d.eps, b.hidden,
+              b.text_logits, d.Vt, b.am_part, AM, b.am_cnt, 1 + d.Q, b.tokens, 1 + d.Q, b0);
+    });
+    // depformer_in[cb] . hidden for every codebook at once
+    run(MOSHI_STAGE_DEP_IN, [&] {
+      k_gemv_store<WT, 2, 4, MOSHI_STAGE_DEP_IN>
+          <<<dim3(blocks_for((int64_t)d.Q * d.Dd, 2 * NWAVES), nb), BLOCK, d.D * 4, st>>>(
+              W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, b.hidden, d.D, b.din, d.Q * d.Dd, b0);
+    });
+    for (int cb = 0; cb < d.Q; ++cb) {
+      const ET *table = cb == 0 ? E(s->dep_text_emb) : E(s->dep_emb[cb - 1]);
+      for (int j = 0; j < d.Ld; ++j) {
+        const LayerW &lw = s->dlayers[j][cb];
+        run(MOSHI_STAGE_DEP_QKV, [&] {
+          k_dep_qkv<WT, ET, 2, 4><<<dim3(blocks_for(3 * d.Dd, 2 * NWAVES), nb), BLOCK, d.Dd * 4, st>>>(
+              d, b, W(lw.in), s->scale(lw.in), N(lw.norm1), table, j, cb, b0);
+        });
+        run(MOSHI_STAGE_DEP_OUT, [&] {
+          k_dep_out<WT, 2, 4><<<dim3(blocks_for(d.Dd, 2 * NWAVES), nb), BLOCK, d.Dd * 4, st>>>(
+              d, b, W(lw.out), s->scale(lw.out), j, cb, b0);
+        });
+        run(MOSHI_STAGE_DEP_GATE_IN, [&] {
+          k_gate<WT, 4, MOSHI_STAGE_DEP_GATE_IN><<<dim3(blocks_for(d.Fd, NWAVES), nb), BLOCK, d.Dd * 4, st>>>(
+              W(lw.gin), s->scale(lw.gin), d.Fd, d.Dd, b.y, d.Dd, N(lw.norm2), d.eps, b.da, d.Fd, b0);
+        });
+        run(MOSHI_STAGE_DEP_GATE_OUT, [&] {
+          k_gemv_residual<WT, 2, 4, MOSHI_STAGE_DEP_GATE_OUT>
+              <<<dim3(blocks_for(d.Dd, 2 * NWAVES), nb), BLOCK, d.Fd * 4, st>>>(
+                  W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, b.da, d.Fd, b.y, d.Dd, b0);
+        });
+      }
+      run(MOSHI_STAGE_DEP_HEAD, [&] {
+        k_head_argmax<WT, 2, 4, MOSHI_STAGE_DEP_HEAD>
+            <<<dim3(blocks_for(d.Va, 2 * NWAVES, AM_MAX_BLOCKS), nb), BLOCK, d.Dd * 4, st>>>(
+                W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, b.y, d.Dd, nullptr, d.eps, nullptr,
+                b.audio_logits + (size_t)cb * d.Va, d.Q * d.Va, b.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS, AM,
+                b.am_cnt + 1 + cb, 1 + d.Q, b.tokens + 1 + cb, 1 + d.Q, b0);
+      });
+    }
+  }
+  run(MOSHI_STAGE_FRAME_END, [&] { k_frame_end<<<nb, 64, 0, st>>>(d, b, b0, temporal_only ? 1 : 0, forced); });
+}
+
+void enqueue_frame(moshi_state *s, int b0, int nb, bool temporal_only, const int32_t *user_dev,
+                   const mk::Forced &forced, Prof *prof = nullptr) {
+  switch (s->cfg.band) {
+    case MOSHI_BAND_F32:
+      enqueue_frame_t<float, float, float>(s, b0, nb, temporal_only, user_dev, forced, prof);
+      break;
+    case MOSHI_BAND_BF16:
+      enqueue_frame_t<bf16_t, bf16_t, bf16_t>(s, b0, nb, temporal_only, user_dev, forced, prof);
+      break;
+    default:
+      enqueue_frame_t<int8_t, bf16_t, bf16_t>(s, b0, nb, temporal_only, user_dev, forced, prof);
+      break;
+  }
+}
+
+moshi_status ensure_graph(moshi_state *s) {
+  if (s->gexec) return MOSHI_OK;
+  hipGraph_t g = nullptr;
+  HIP_TRY(s, hipStreamBeginCapture(s->stream, hipStreamCaptureModeThreadLocal));
+  mk::Forced none{};
+  enqueue_frame(s, 0, s->d.B, false, s->b.user, none, nullptr);
+  hipError_t e = hipStreamEndCapture(s->stream, &g);
+  if (e != hipSuccess) return fail(s, MOSHI_EDEVICE, "graph capture: %s", hipGetErrorString(e));
+  e = hipGraphInstantiate(&s->gexec, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  if (e != hipSuccess) {
+    s->gexec = nullptr;
+    return fail(s, MOSHI_EDEVICE, "graph instantiate: %s", hipGetErrorString(e));
+  }
+  return MOSHI_OK;
+}
+
+moshi_status check_config(const moshi_config *c, std::string &why) {
+  auto bad = [&](const char *m) {
+    why = m;
+    return MOSHI_EINVAL;
+  };
+  if (!c) return bad("config is NULL");
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->ffn_hidden < 1 || c->context < 1)
+    return bad("temporal dimensions must be positive");
+  if (c->dep_layers < 1 || c->dep_d_model < 1 || c->dep_heads < 1 || c->dep_ffn_hidden < 1)
+    return bad("depformer dimensions must be positive");
+  if (c->dep_q < 1 || c->dep_q > 16) return bad("dep_q must be in [1, 16]");
+  if (c->text_card < 1 || c->audio_card < 1) return bad("cards must be positive");
+  if (c->d_model % c->n_heads) return bad("d_model must be a multiple of n_heads");
+  const int hd = c->d_model / c->n_heads;
+  if (hd != 64 && hd != 128) return bad("temporal head_dim must be 64 or 128");
+  if (c->dep_d_model % c->dep_heads) return bad("dep_d_model must be a multiple of dep_heads");
+  for (int k : {c->d_model, c->ffn_hidden, c->dep_d_model, c->dep_ffn_hidden})
+    if (k % 16 || k > 16384) return bad("linear input widths must be multiples of 16 and at most 16384");
+  if (c->band < MOSHI_BAND_F32 || c->band > MOSHI_BAND_I8) return bad("unknown band");
+  if (c->batch < 1) return bad("batch must be >= 1");
+  if (c->kv_capacity < 0 || c->kv_capacity > c->context) return bad("kv_capacity must be in [0, context]");
+  if (c->exec != MOSHI_EXEC_GRAPH && c->exec != MOSHI_EXEC_STREAM) return bad("unknown exec mode");
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return bad("rms_eps must be >= 0 and rope_theta > 0");
+  return MOSHI_OK;
+}
+
+moshi_status bind_device(moshi_state *s) {
+  HIP_TRY(s, hipSetDevice(s->device));
+  return MOSHI_OK;
+}
+
+}  // namespace
+
+// =============================================================================================
+// C ABI
+// =============================================================================================
+extern "C" {
+
+const char *moshi_status_string(int32_t st) {
+  switch (st) {
+    case MOSHI_OK: return "MOSHI_OK";
+    case MOSHI_NONE: return "MOSHI_NONE";
+    case MOSHI_EINVAL: return "MOSHI_EINVAL";
+    case MOSHI_ESTATE: return "MOSHI_ESTATE";
+    case MOSHI_ESHAPE: return "MOSHI_ESHAPE";
+    case MOSHI_ENOMEM: return "MOSHI_ENOMEM";
+    case MOSHI_EDEVICE: return "MOSHI_EDEVICE";
+    case MOSHI_ERANGE: return "MOSHI_ERANGE";
+    default: return "unknown status";
+  }
+}
+
+const char *moshi_last_error(const moshi_state *s) { return s ? s->err.c_str() : "no state"; }
+
+moshi_status moshi_create(const moshi_config *cfg, void *hip_stream, moshi_state **out) {
+  if (!out) return MOSHI_EINVAL;
+  *out = nullptr;
+  std::string why;
+  if (check_config(cfg, why) != MOSHI_OK) {
+    fprintf(stderr, "moshi_create: %s\n", why.c_str());
+    return MOSHI_EINVAL;
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MOSHI_EDEVICE;
+  moshi_state *s = new moshi_state();
+  s->cfg = *cfg;
+  if (s->cfg.kv_capacity == 0) s->cfg.kv_capacity = s->cfg.context;
+  if (hipGetDevice(&s->device) != hipSuccess) {
+    delete s;
+    return MOSHI_EDEVICE;
+  }
+  mk::Dims &d = s->d;
+  d.B = cfg->batch;
+  d.L = cfg->n_layers;
+  d.D = cfg->d_model;
+  d.H = cfg->n_heads;
+  d.hd = d.D / d.H;
+  d.F = cfg->ffn_hidden;
+  d.C = cfg->context;
+  d.cap = s->cfg.kv_capacity;
+  d.Vt = cfg->text_card;
+  d.Va = cfg->audio_card;
+  d.Ld = cfg->dep_layers;
+  d.Dd = cfg->dep_d_model;
+  d.Hd = cfg->dep_heads;
+  d.hdd = d.Dd / d.Hd;
+  d.Fd = cfg->dep_ffn_hidden;
+  d.Q = cfg->dep_q;
+  d.NS = 2 * d.Q + 1;
+  d.S = std::max(1, std::min(32, (d.cap + 127) / 128));
+  d.eps = cfg->rms_eps;
+  s->h_offset.assign(d.B, 0);
+  moshi_status st = MOSHI_OK;
+  if (hip_stream) {
+    s->stream = (hipStream_t)hip_stream;
+  } else {
+    if (hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) != hipSuccess) {
+      delete s;
+      return MOSHI_EDEVICE;
+    }
+    s->own_stream = true;
+  }
+  plan_weights(s);
+  hipError_t e = hipMalloc(&s->warena, s->wbytes);
+  if (e != hipSuccess) {
+    fprintf(stderr, "moshi_create: weight arena of %zu bytes: %s\n", s->wbytes, hipGetErrorString(e));
+    moshi_destroy(s);
+    return MOSHI_ENOMEM;
+  }
+  st = alloc_session(s);
+  if (st != MOSHI_OK) {
+    fprintf(stderr, "moshi_create: %s\n", s->err.c_str());
+    moshi_destroy(s);
+    return st;
+  }
+  mk::Bufs bb = s->b;
+  mk::k_reset<<<d.B, 64, 0, s->stream>>>(d, bb, 0);
+  if (hipStreamSynchronize(s->stream) != hipSuccess) {
+    moshi_destroy(s);
+    return MOSHI_EDEVICE;
+  }
+  *out = s;
+  return MOSHI_OK;
+}
+
+void moshi_destroy(moshi_state *s) {
+  if (!s) return;
+  (void)hipSetDevice(s->device);
+  if (s->stream) (void)hipStreamSynchronize(s->stream);
+  if (s->gexec) (void)hipGraphExecDestroy(s->gexec);
+  if (s->warena) (void)hipFree(s->warena);
+  if (s->sarena) (void)hipFree(s->sarena);
+  if (s->h_pin) (void)hipHostFree(s->h_pin);
+  if (s->own_stream && s->stream) (void)hipStreamDestroy(s->stream);
+  delete s;
+}
+
+moshi_status moshi_load_weights(moshi_state *s, const moshi_tensor *t, int32_t n) {
+  if (!s) return MOSHI_EINVAL;
+  if (n < 0 || (n > 0 && !t)) return fail(s, MOSHI_EINVAL, "bad tensor array");
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  const int band = s->cfg.band;
+  // validate everything before touching the device
+  for (int i = 0; i < n; ++i) {
+    if (!t[i].name || !t[i].data) return fail(s, MOSHI_EINVAL, "tensor %d has no name or data", i);
+    auto it = s->slot_of.find(t[i].name);
+    if (it == s->slot_of.end()) return fail(s, MOSHI_ESHAPE, "unknown tensor %s", t[i].name);
+    const Slot &sl = s->slots[it->second];
+    const int want_nd = sl.cols ? 2 : 1;
+    if (t[i].ndim != want_nd || t[i].shape[0] != sl.rows || (want_nd == 2 && t[i].shape[1] != sl.cols))
+      return fail(s, MOSHI_ESHAPE, "%s: expected shape [%lld%s%lld]", t[i].name, (long long)sl.rows,
+                  want_nd == 2 ? ", " : "", want_nd == 2 ? (long long)sl.cols : 0LL);
+    if (t[i].dtype != MOSHI_DTYPE_F32 && t[i].dtype != MOSHI_DTYPE_BF16)
+      return fail(s, MOSHI_ESHAPE, "%s: dtype must be float32 or bfloat16", t[i].name);
+  }
+  float *staging = nullptr;
+  size_t staging_n = 0;
+  std::vector<float> hf;
+  std::vector<uint16_t> hb;
+  moshi_status rc = MOSHI_OK;
+  for (int i = 0; i < n && rc == MOSHI_OK; ++i) {
+    const int si = s->slot_of[t[i].name];
+    Slot &sl = s->slots[si];
+    const size_t cnt = (size_t)sl.rows * (size_t)std::max<int64_t>(sl.cols, 1);
+    const bool in_f32 = t[i].dtype == MOSHI_DTYPE_F32;
+    const float *srcf = reinterpret_cast<const float *>(t[i].data);
+    const uint16_t *srcb = reinterpret_cast<const uint16_t *>(t[i].data);
+    auto as_f32 = [&]() -> const float * {
+      if (in_f32) return srcf;
+      hf.resize(cnt);
+      for (size_t k = 0; k < cnt; ++k) hf[k] = host_bf2f(srcb[k]);
+      return hf.data();
+    };
+    auto as_bf16 = [&]() -> const uint16_t * {
+      if (!in_f32) return srcb;
+      hb.resize(cnt);
+      for (size_t k = 0; k < cnt; ++k) hb[k] = host_f2bf(srcf[k]);
+      return hb.data();
+    };
+    void *dst = s->warena + sl.off;
+    hipError_t e = hipSuccess;
+    if (sl.kind == K_NORM || (band == MOSHI_BAND_F32)) {
+      e = hipMemcpy(dst, as_f32(), cnt * 4, hipMemcpyHostToDevice);
+    } else if (sl.kind == K_EMBED || band == MOSHI_BAND_BF16) {
+      e = hipMemcpy(dst, as_bf16(), cnt * 2, hipMemcpyHostToDevice);
+    } else {  // int8 linear: quantise on the device
+      if (staging_n < cnt) {
+        if (staging) (void)hipFree(staging);
+        staging = nullptr;
+        staging_n = 0;
+        e = hipMalloc(&staging, cnt * 4);
+        if (e != hipSuccess) {
+          rc = fail(s, MOSHI_ENOMEM, "staging %zu bytes: %s", cnt * 4, hipGetErrorString(e));
+          break;
+        }
+        staging_n = cnt;
+      }
+      e = hipMemcpy(staging, as_f32(), cnt * 4, hipMemcpyHostToDevice);
+      if (e == hipSuccess) {
+        mk::k_quant_rows<<<(unsigned)sl.rows, mk::BLOCK, 0, s->stream>>>(
+            staging, sl.cols, reinterpret_cast<int8_t *>(dst), reinterpret_cast<float *>(s->warena + sl.soff), 0);
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
+      }
+    }
+    if (e != hipSuccess) {
+      rc = fail(s, MOSHI_EDEVICE, "loading %s: %s", t[i].name, hipGetErrorString(e));
+      break;
+    }
+    if (!sl.loaded) {
+      sl.loaded = true;
+      s->n_loaded++;
+    }
+  }
+  if (staging) (void)hipFree(staging);
+  return rc;
+}
+
+moshi_status moshi_weight_bytes(const moshi_state *s, int64_t *linear_bytes, int64_t *all_bytes) {
+  if (!s) return MOSHI_EINVAL;
+  if (linear_bytes) *linear_bytes = s->linear_bytes;
+  if (all_bytes) *all_bytes = (int64_t)s->wbytes;
+  return MOSHI_OK;
+}
+
+void *moshi_stream(const moshi_state *s) { return s ? (void *)s->stream : nullptr; }
+
+static moshi_status ready(moshi_state *s) {
+  if (s->n_loaded != (int)s->slots.size()) {
+    for (const Slot &sl : s->slots)
+      if (!sl.loaded) return fail(s, MOSHI_ESTATE, "weights incomplete: %s not loaded", sl.name.c_str());
+  }
+  if (s->broken) return fail(s, MOSHI_ESTATE, "a device error occurred; call moshi_reset first");
+  return MOSHI_OK;
+}
+
+static moshi_status check_step_inputs(moshi_state *s, const int32_t *user) {
+  const mk::Dims &d = s->d;
+  for (int i = 0; i < d.B * d.Q; ++i)
+    if (!(user[i] == -1 || (user[i] >= 0 && user[i] < d.Va)))
+      return fail(s, MOSHI_EINVAL, "user token %d at [%d][%d] is outside [0, %d) and not -1", user[i], i / d.Q,
+                  i % d.Q, d.Va);
+  if (d.cap < d.C)
+    for (int b = 0; b < d.B; ++b)
+      if (s->h_offset[b] >= d.cap)
+        return fail(s, MOSHI_ERANGE, "conversation %d is at offset %lld, kv_capacity is %d", b,
+                    (long long)s->h_offset[b], d.cap);
+  return MOSHI_OK;
+}
+
+// One frame: upload the user tokens, run the frame (graph replay, or launches with optional
+// event timing), fetch the realigned outputs, synchronise.
+static moshi_status run_frame(moshi_state *s, const int32_t *user, int32_t *out, uint8_t *has_out, Prof *prof) {
+  const mk::Dims &d = s->d;
+  int32_t *hu = s->h_pin;
+  int32_t *ho = s->h_pin + d.B * d.Q;
+  std::memcpy(hu, user, sizeof(int32_t) * d.B * d.Q);
+  HIP_TRY(s, hipMemcpyAsync(s->b.user, hu, sizeof(int32_t) * d.B * d.Q, hipMemcpyHostToDevice, s->stream));
+  if (s->cfg.exec == MOSHI_EXEC_GRAPH && !prof) {
+    moshi_status rc = ensure_graph(s);
+    if (rc != MOSHI_OK) return rc;
+    HIP_TRY(s, hipGraphLaunch(s->gexec, s->stream));
+  } else {
+    mk::Forced none{};
+    enqueue_frame(s, 0, d.B, false, s->b.user, none, prof);
+    HIP_TRY(s, hipGetLastError());
+  }
+  const size_t ob = sizeof(int32_t) * ((size_t)d.B * (1 + d.Q) + d.B);
+  HIP_TRY(s, hipMemcpyAsync(ho, s->b.outpack, ob, hipMemcpyDeviceToHost, s->stream));
+  HIP_TRY(s, hipStreamSynchronize(s->stream));
+  int any = 0;
+  for (int b = 0; b < d.B; ++b) {
+    s->h_offset[b]++;
+    const int has = ho[(size_t)d.B * (1 + d.Q) + b];
+    if (has_out) has_out[b] = (uint8_t)(has ? 1 : 0);
+    if (has) {
+      any = 1;
+      if (out) std::memcpy(out + (size_t)b * (1 + d.Q), ho + (size_t)b * (1 + d.Q), sizeof(int32_t) * (1 + d.Q));
+    }
+  }
+  return any ? MOSHI_OK : MOSHI_NONE;
+}
+
+moshi_status moshi_frame_step(moshi_state *s, const int32_t *user, int32_t *out, uint8_t *has_out) {
+  if (!s) return MOSHI_EINVAL;
+  if (!user || !out || (!has_out && s->d.B > 1)) return fail(s, MOSHI_EINVAL, "NULL token or output buffer");
+  moshi_status rc = ready(s);
+  if (rc == MOSHI_OK) rc = check_step_inputs(s, user);
+  if (rc != MOSHI_OK) return rc;
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  return run_frame(s, user, out, has_out, nullptr);
+}
+
+moshi_status moshi_profile_frames(moshi_state *s, int32_t n_frames, const int32_t *user_tokens, double *stage_us,
+                                  int64_t *stage_launches) {
+  if (!s) return MOSHI_EINVAL;
+  if (n_frames < 0 || (n_frames > 0 && !user_tokens) || !stage_us || !stage_launches)
+    return fail(s, MOSHI_EINVAL, "bad profile arguments");
+  moshi_status rc = ready(s);
+  if (rc != MOSHI_OK) return rc;
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  for (int i = 0; i < MOSHI_N_STAGES; ++i) {
+    stage_us[i] = 0.0;
+    stage_launches[i] = 0;
+  }
+  const mk::Dims &d = s->d;
+  Prof prof;
+  const size_t pairs = 64 + (size_t)d.L * 5 + (size_t)d.Q * (d.Ld * 4 + 1);
+  prof.ev.resize(2 * pairs, nullptr);
+  prof.stage.resize(pairs, 0);
+  for (auto &e : prof.ev) HIP_TRY(s, hipEventCreate(&e));
+  std::vector<uint8_t> has(d.B);
+  for (int f = 0; f < n_frames && rc >= 0; ++f) {
+    const int32_t *u = user_tokens + (size_t)f * d.B * d.Q;
+    rc = check_step_inputs(s, u);
+    if (rc != MOSHI_OK) break;
+    prof.used = 0;
+    rc = run_frame(s, u, nullptr, has.data(), &prof);
+    if (rc < 0) break;
+    for (size_t i = 0; i + 1 < prof.used; i += 2) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, prof.ev[i], prof.ev[i + 1]) == hipSuccess) {
+        stage_us[prof.stage[i / 2]] += 1000.0 * ms;
+        stage_launches[prof.stage[i / 2]] += 1;
+      }
+    }
+  }
+  for (auto &e : prof.ev)
+    if (e) (void)hipEventDestroy(e);
+  return rc < 0 ? rc : MOSHI_OK;
+}
+
+moshi_status moshi_reset(moshi_state *s, int32_t conv) {
+  if (!s) return MOSHI_EINVAL;
+  if (conv < -1 || conv >= s->d.B) return fail(s, MOSHI_EINVAL, "conversation %d out of range", conv);
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  const int b0 = conv < 0 ? 0 : conv, nb = conv < 0 ? s->d.B : 1;
+  mk::k_reset<<<nb, 64, 0, s->stream>>>(s->d, s->b, b0);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
+  if (e != hipSuccess) return fail(s, MOSHI_EDEVICE, "reset: %s", hipGetErrorString(e));
+  for (int b = b0; b < b0 + nb; ++b) s->h_offset[b] = 0;
+  s->broken = false;
+  return MOSHI_OK;
+}
+
+moshi_status moshi_get_offset(const moshi_state *s, int32_t conv, int64_t *offset) {
+  if (!s || !offset || conv < 0 || conv >= s->d.B) return MOSHI_EINVAL;
+  *offset = s->h_offset[conv];
+  return MOSHI_OK;
+}
+
+moshi_status moshi_force_generated(moshi_state *s, int32_t conv, int32_t text, const int32_t *audio) {
+  if (!s) return MOSHI_EINVAL;
+  if (conv < 0 || conv >= s->d.B || !audio) return fail(s, MOSHI_EINVAL, "bad conversation or NULL audio");
+  if (text < 0 || text >= s->d.Vt) return fail(s, MOSHI_EINVAL, "forced text token %d not in [0, %d)", text, s->d.Vt);
+  mk::Forced f{};
+  f.t[0] = text;
+  for (int k = 0; k < s->d.Q; ++k) {
+    if (audio[k] < 0 || audio[k] >= s->d.Va)
+      return fail(s, MOSHI_EINVAL, "forced audio token %d not in [0, %d)", audio[k], s->d.Va);
+    f.t[1 + k] = audio[k];
+  }
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  mk::k_force<<<1, 64, 0, s->stream>>>(s->d, s->b, conv, f);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
+  if (e != hipSuccess) return fail(s, MOSHI_EDEVICE, "force: %s", hipGetErrorString(e));
+  return MOSHI_OK;
+}
+
+moshi_status moshi_read_trace(moshi_state *s, int32_t conv, const moshi_trace *tr) {
+  if (!s) return MOSHI_EINVAL;
+  if (!tr || conv < 0 || conv >= s->d.B) return fail(s, MOSHI_EINVAL, "bad conversation or NULL trace");
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  const mk::Dims &d = s->d;
+  HIP_TRY(s, hipStreamSynchronize(s->stream));
+  auto cp = [&](void *dst, const void *src, size_t bytes) -> hipError_t {
+    return dst ? hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost) : hipSuccess;
+  };
+  const size_t b = (size_t)conv;
+  HIP_TRY(s, cp(tr->input_tokens, s->b.inputs + b * d.NS, 4 * d.NS));
+  HIP_TRY(s, cp(tr->emb_sum, s->b.emb_sum + b * d.D, 4 * (size_t)d.D));
+  HIP_TRY(s, cp(tr->transformer_out, s->b.hidden + b * d.D, 4 * (size_t)d.D));
+  HIP_TRY(s, cp(tr->text_logits, s->b.text_logits + b * d.Vt, 4 * (size_t)d.Vt));
+  HIP_TRY(s, cp(tr->audio_logits, s->b.audio_logits + b * d.Q * d.Va, 4 * (size_t)d.Q * d.Va));
+  HIP_TRY(s, cp(tr->tokens, s->b.tokens + b * (1 + d.Q), 4 * (size_t)(1 + d.Q)));
+  return MOSHI_OK;
+}
+
+moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const int32_t *text,
+                                  const int32_t *agent, const int32_t *user) {
+  if (!s) return MOSHI_EINVAL;
+  if (conv < 0 || conv >= s->d.B || T < 0) return fail(s, MOSHI_EINVAL, "bad conversation or length");
+  if (T == 0) return MOSHI_OK;
+  if (!text || !agent || !user) return fail(s, MOSHI_EINVAL, "NULL token array");
+  moshi_status rc = ready(s);
+  if (rc != MOSHI_OK) return rc;
+  const mk::Dims &d = s->d;
+  for (int t = 0; t < T; ++t) {
+    if (text[t] < 0 || text[t] >= d.Vt) return fail(s, MOSHI_EINVAL, "forced text token %d out of range", text[t]);
+    for (int k = 0; k < d.Q; ++k) {
+      const int a = agent[(size_t)t * d.Q + k], u = user[(size_t)t * d.Q + k];
+      if (a < 0 || a >= d.Va) return fail(s, MOSHI_EINVAL, "forced agent token %d out of range", a);
+      if (!(u == -1 || (u >= 0 && u < d.Va))) return fail(s, MOSHI_EINVAL, "user token %d out of range", u);
+    }
+  }
+  if (d.cap < d.C && s->h_offset[conv] + T > d.cap)
+    return fail(s, MOSHI_ERANGE, "prefill of %d positions from offset %lld exceeds kv_capacity %d", T,
+                (long long)s->h_offset[conv], d.cap);
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  int32_t *du = nullptr;
+  HIP_TRY(s, hipMalloc(&du, sizeof(int32_t) * (size_t)T * d.Q));
+  hipError_t e = hipMemcpy(du, user, sizeof(int32_t) * (size_t)T * d.Q, hipMemcpyHostToDevice);
+  for (int t = 0; t < T && e == hipSuccess; ++t) {
+    mk::Forced f{};
+    f.t[0] = text[t];
+    for (int k = 0; k < d.Q; ++k) f.t[1 + k] = agent[(size_t)t * d.Q + k];
+    enqueue_frame(s, conv, 1, true, du + (size_t)t * d.Q, f, nullptr);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
+  (void)hipFree(du);
+  if (e != hipSuccess) return fail(s, MOSHI_EDEVICE, "prefill: %s", hipGetErrorString(e));
+  s->h_offset[conv] += T;
+  return MOSHI_OK;
+}
+
+moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W, const float *x, float *y,
+                              int32_t iters, float *avg_us) {
+  if (N < 1 || K < 16 || K % 16 || K > 16384 || !W || !x || !y || band < 0 || band > 2) return MOSHI_EINVAL;
+  const size_t cnt = (size_t)N * K;
+  const size_t elt = linear_elt(band);
+  char *dw = nullptr;
+  float *ds = nullptr, *dx = nullptr, *dy = nullptr, *stg = nullptr;
+  hipStream_t st = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  moshi_status rc = MOSHI_OK;
+  auto chk = [&](hipError_t e) {
+    if (e != hipSuccess && rc == MOSHI_OK) {
+      fprintf(stderr, "moshi_debug_gemv: %s\n", hipGetErrorString(e));
+      rc = e == hipErrorOutOfMemory ? MOSHI_ENOMEM : MOSHI_EDEVICE;
+    }
+    return rc == MOSHI_OK;
+  };
+  if (chk(hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) && chk(hipMalloc(&dw, cnt * elt)) &&
+      chk(hipMalloc(&ds, (size_t)N * 4)) && chk(hipMalloc(&dx, (size_t)K * 4)) && chk(hipMalloc(&dy, (size_t)N * 4)) &&
+      chk(hipMemcpy(dx, x, (size_t)K * 4, hipMemcpyHostToDevice))) {
+    if (band == MOSHI_BAND_F32) {
+      chk(hipMemcpy(dw, W, cnt * 4, hipMemcpyHostToDevice));
+    } else if (band == MOSHI_BAND_BF16) {
+      std::vector<uint16_t> hb(cnt);
+      for (size_t k = 0; k < cnt; ++k) hb[k] = host_f2bf(W[k]);
+      chk(hipMemcpy(dw, hb.data(), cnt * 2, hipMemcpyHostToDevice));
+    } else if (chk(hipMalloc(&stg, cnt * 4)) && chk(hipMemcpy(stg, W, cnt * 4, hipMemcpyHostToDevice))) {
+      mk::k_quant_rows<<<(unsigned)N, mk::BLOCK, 0, st>>>(stg, K, reinterpret_cast<int8_t *>(dw), ds, 0);
+      chk(hipGetLastError());
+    }
+  }
+  auto launch = [&]() {
+    const dim3 grid(blocks_for(N, 2 * mk::NWAVES));
+    const float *sc = band == MOSHI_BAND_I8 ? ds : nullptr;
+    if (band == MOSHI_BAND_F32)
+      mk::k_gemv_store<float, 2, 4, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const float *>(dw), sc, N, K, dx,
+                                                                     K, dy, N, 0);
+    else if (band == MOSHI_BAND_BF16)
+      mk::k_gemv_store<bf16_t, 2, 4, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const bf16_t *>(dw), sc, N, K,
+                                                                      dx, K, dy, N, 0);
+    else
+      mk::k_gemv_store<int8_t, 2, 4, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const int8_t *>(dw), sc, N, K,
+                                                                      dx, K, dy, N, 0);
+  };
+  if (rc == MOSHI_OK) {
+    launch();
+    chk(hipGetLastError());
+    chk(hipStreamSynchronize(st));
+  }
+  if (rc == MOSHI_OK && iters > 0 && avg_us) {
+    if (chk(hipEventCreate(&e0)) && chk(hipEventCreate(&e1)) && chk(hipEventRecord(e0, st))) {
+      for (int i = 0; i < iters; ++i) launch();
+      chk(hipEventRecord(e1, st));
+      chk(hipEventSynchronize(e1));
+      float ms = 0.f;
+      chk(hipEventElapsedTime(&ms, e0, e1));
+      *avg_us = ms * 1000.f / (float)iters;
+    }
+  }
+  if (rc == MOSHI_OK) chk(hipMemcpy(y, dy, (size_t)N * 4, hipMemcpyDeviceToHost));
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (stg) (void)hipFree(stg);
+  if (dw) (void)hipFree(dw);
+  if (ds) (void)hipFree(ds);
+  if (dx) (void)hipFree(dx);
+  if (dy) (void)hipFree(dy);
+  if (st) (void)hipStreamDestroy(st);
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+"""Kernel-level parity of the weight-streaming GEMV (float32, bfloat16 and int8 bands) against
+float64 products of the same stored weights, at ragged small shapes and at the Moshi-7B
+projection shapes (sampled rows)."""
+import numpy as np
+import pytest
+
+import rq_transformer_frame_amd as rq
+import synth
+from oracle import quantize_rows_int8
+
+pytestmark = pytest.mark.gpu
+
+
+def stored(band, W):
+    """The weights as the band stores them, widened to float64 (and the int8 scales)."""
+    if band == "f32":
+        return W.astype(np.float64), None
+    if band == "bf16":
+        return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(W)).astype(np.float64), None
+    q, s = quantize_rows_int8(W)
+    return q.astype(np.float64), s.astype(np.float64)
+
+
+@pytest.mark.parametrize("band", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("N,K", [(1, 16), (37, 48), (130, 272), (1000, 256), (2048, 1024), (333, 2816)])
+def test_gemv_small_and_ragged(band, N, K):
+    W = synth.normal(1, f"k/W{N}x{K}", (N, K), 0.02)
+    x = synth.normal(1, f"k/x{K}", (K,), 1.0)
+    y, _ = rq.debug_gemv(band, W, x)
+    Ws, s = stored(band, W)
+    ref = Ws @ x.astype(np.float64)
+    if s is not None:
+        ref *= s
+    err = np.max(np.abs(y - ref)) / np.max(np.abs(ref))
+    assert err < 2e-6, err
+
+
+@pytest.mark.parametrize("band", ["bf16", "i8"])
+@pytest.mark.parametrize("N,K", [(12288, 4096), (22528, 4096), (4096, 11264), (32000, 4096), (8192, 4096)])
+def test_gemv_moshi7b_shapes_sampled_rows(band, N, K):
+    W = synth.normal(2, f"k7/W{N}x{K}", (N, K), 0.02)
+    x = synth.normal(2, f"k7/x{K}", (K,), 1.0)
+    y, us = rq.debug_gemv(band, W, x, iters=10)
+    rows = np.unique(synth.uniform_int(2, f"k7/rows{N}", (256,), N))
+    rows = np.concatenate([[0, N - 1], rows])
+    Ws, s = stored(band, W[rows])
+    ref = Ws @ x.astype(np.float64)
+    if s is not None:
+        ref *= s
+    err = np.max(np.abs(y[rows] - ref)) / np.max(np.abs(ref))
+    bytes_ = N * K * (2 if band == "bf16" else 1) + (N * 4 if band == "i8" else 0)
+    print(f"gemv {band} {N}x{K}: {us:.1f} us, {bytes_ / us / 1e3:.0f} GB/s")
+    assert err < 2e-6, err

@@ -1,0 +1,251 @@
+"""GPU parity on the tiny float32 RQ-Transformer (2+2 layers, d256/d128, 17 streams, 16 frames):
+tokens, ring and outputs bit-exact against the CPU oracle, logits within 1e-4 relative error,
+plus the edge cases of the boundary (reset, -1 tokens, invalid tokens, capacity, eviction,
+teacher forcing, prefill, batches)."""
+import numpy as np
+import pytest
+
+import rq_transformer_frame_amd as rq
+import synth
+from oracle import OracleLM
+from tests.gpu_util import cosine, rel_err
+
+pytestmark = pytest.mark.gpu
+
+CFG = synth.TINY
+TOL = 1e-4
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return synth.gen_weights(CFG)
+
+
+@pytest.fixture(scope="module")
+def oracle(weights):
+    return OracleLM(CFG, weights)
+
+
+def compare_step(tr, ref, st, out, has, frame):
+    assert tr["input_tokens"].tolist() == ref["input_tokens"].tolist(), frame
+    np.testing.assert_allclose(tr["emb_sum"], ref["emb_sum"], rtol=1e-6, atol=1e-7)
+    assert rel_err(tr["transformer_out"], ref["transformer_out"]) <= TOL, frame
+    assert rel_err(tr["text_logits"], ref["text_logits"]) <= TOL, frame
+    for cb in range(CFG.dep_q):
+        assert rel_err(tr["audio_logits"][cb], ref["audio_logits"][cb]) <= TOL, (frame, cb)
+    assert tr["text_token"] == ref["text_token"], frame
+    assert tr["audio_tokens"] == ref["audio_tokens"], frame
+    assert bool(has[0]) == (ref["out"] is not None), frame
+    assert st == (rq.MOSHI_NONE if ref["out"] is None else rq.MOSHI_OK)
+    if ref["out"] is not None:
+        assert out[0].tolist() == ref["out"], frame
+
+
+@pytest.mark.parametrize("exec_mode", ["graph", "stream"])
+def test_tiny_free_running_matches_oracle(weights, oracle, exec_mode):
+    users = synth.user_tokens(CFG, CFG.frames)
+    ost = oracle.new_state()
+    with rq.Session(CFG, exec=exec_mode) as s:
+        s.load_weights(weights)
+        for f in range(CFG.frames):
+            ref = oracle.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            compare_step(s.read_trace(0), ref, st, out, has, f)
+            assert s.offset(0) == f + 1
+
+
+def test_tiny_sliding_window_past_context(weights, oracle):
+    """74 frames with context 64: the KV ring wraps and attention keeps the last 64 positions."""
+    users = synth.user_tokens(CFG, 74)
+    ost = oracle.new_state()
+    with rq.Session(CFG) as s:
+        s.load_weights(weights)
+        for f in range(74):
+            ref = oracle.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            compare_step(s.read_trace(0), ref, st, out, has, f)
+
+
+def test_tiny_runs_are_bitwise_deterministic(weights):
+    users = synth.user_tokens(CFG, 6)
+    logs = []
+    for _ in range(2):
+        with rq.Session(CFG) as s:
+            s.load_weights(weights)
+            for f in range(6):
+                s.step(users[f])
+            logs.append(s.read_trace(0))
+    for k in ("text_logits", "audio_logits", "transformer_out"):
+        assert logs[0][k].tobytes() == logs[1][k].tobytes(), k
+
+
+def test_reset_mid_stream_repeats_frame_zero(weights, oracle):
+    users = synth.user_tokens(CFG, 5)
+    with rq.Session(CFG) as s:
+        s.load_weights(weights)
+        s.step(users[0])
+        first = s.read_trace(0)
+        for f in range(1, 5):
+            s.step(users[f])
+        s.reset(0)
+        assert s.offset(0) == 0
+        st, _, has = s.step(users[0])
+        again = s.read_trace(0)
+        assert st == rq.MOSHI_NONE and not has[0]
+        assert again["text_logits"].tobytes() == first["text_logits"].tobytes()
+        assert again["tokens"].tolist() == first["tokens"].tolist()
+
+
+def test_minus_one_user_tokens_embed_to_zero(weights, oracle):
+    users = synth.user_tokens(CFG, 4)
+    users[1, 3] = -1
+    users[2, :] = -1
+    ost = oracle.new_state()
+    with rq.Session(CFG) as s:
+        s.load_weights(weights)
+        for f in range(4):
+            ref = oracle.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            compare_step(s.read_trace(0), ref, st, out, has, f)
+
+
+def test_invalid_user_token_leaves_state_unchanged(weights, oracle):
+    users = synth.user_tokens(CFG, 3)
+    ost = oracle.new_state()
+    with rq.Session(CFG) as s:
+        s.load_weights(weights)
+        ref = oracle.step(ost, users[0])
+        st, out, has = s.step(users[0])
+        compare_step(s.read_trace(0), ref, st, out, has, 0)
+        for bad in (2048, -2, 99999):
+            u = users[1].copy()
+            u[5] = bad
+            with pytest.raises(rq.MoshiError) as ei:
+                s.step(u)
+            assert ei.value.status == rq.MOSHI_EINVAL
+            assert s.offset(0) == 1
+        ref = oracle.step(ost, users[1])
+        st, out, has = s.step(users[1])
+        compare_step(s.read_trace(0), ref, st, out, has, 1)
+
+
+def test_step_before_weights_is_a_state_error(weights):
+    with rq.Session(CFG) as s:
+        with pytest.raises(rq.MoshiError) as ei:
+            s.step(np.zeros(8, np.int32))
+        assert ei.value.status == rq.MOSHI_ESTATE
+        part = {k: v for k, v in list(weights.items())[:10]}
+        s.load_weights(part)
+        with pytest.raises(rq.MoshiError) as ei:
+            s.step(np.zeros(8, np.int32))
+        assert ei.value.status == rq.MOSHI_ESTATE
+
+
+def test_load_rejects_unknown_names_and_bad_shapes(weights):
+    with rq.Session(CFG) as s:
+        with pytest.raises(rq.MoshiError) as ei:
+            s.load_weights({"no.such.weight": np.zeros((2, 2), np.float32)})
+        assert ei.value.status == rq.MOSHI_ESHAPE
+        with pytest.raises(rq.MoshiError) as ei:
+            s.load_weights({"text_linear.weight": np.zeros((999, 256), np.float32)})
+        assert ei.value.status == rq.MOSHI_ESHAPE
+
+
+def test_kv_capacity_below_context_refuses_to_overflow(weights, oracle):
+    users = synth.user_tokens(CFG, 5)
+    ost = oracle.new_state()
+    with rq.Session(CFG, kv_capacity=4) as s:
+        s.load_weights(weights)
+        for f in range(4):
+            ref = oracle.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            compare_step(s.read_trace(0), ref, st, out, has, f)
+        with pytest.raises(rq.MoshiError) as ei:
+            s.step(users[4])
+        assert ei.value.status == rq.MOSHI_ERANGE
+        assert s.offset(0) == 4
+
+
+def test_teacher_forcing_follows_the_reference_trajectory(weights, oracle):
+    """[LM] force_generated: after each step the generated slot is overwritten with reference
+    tokens, so each step is judged on the reference trajectory."""
+    users = synth.user_tokens(CFG, 8)
+    forced = synth.uniform_int(9, "t/force", (8, 9), CFG.audio_card)
+    forced[:, 0] %= CFG.text_card
+    ost = oracle.new_state()
+    with rq.Session(CFG) as s:
+        s.load_weights(weights)
+        for f in range(8):
+            ref = oracle.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            compare_step(s.read_trace(0), ref, st, out, has, f)
+            oracle.force_generated(ost, int(forced[f, 0]), forced[f, 1:])
+            s.force_generated(0, int(forced[f, 0]), forced[f, 1:])
+
+
+@pytest.mark.parametrize("T", [1, 5, 70])
+def test_prefill_forced_then_greedy(weights, oracle, T):
+    text, agent, user = synth.prefill_tokens(CFG, T)
+    text %= CFG.text_card
+    ost = oracle.new_state()
+    oracle.prefill_forced(ost, text, agent, user)
+    users = synth.user_tokens(CFG, 3, start_frame=T)
+    with rq.Session(CFG) as s:
+        s.load_weights(weights)
+        s.prefill_forced(0, text, agent, user)
+        assert s.offset(0) == T
+        for f in range(3):
+            ref = oracle.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            compare_step(s.read_trace(0), ref, st, out, has, T + f)
+
+
+def test_batch_of_three_conversations_matches_single_runs(weights, oracle):
+    B = 3
+    users = np.stack([synth.user_tokens(CFG, 6, conv=b) for b in range(B)], axis=1)  # [f][b][8]
+    refs = []
+    for b in range(B):
+        ost = oracle.new_state()
+        refs.append([oracle.step(ost, users[f, b]) for f in range(6)])
+    with rq.Session(CFG, batch=B) as s:
+        s.load_weights(weights)
+        for f in range(6):
+            st, out, has = s.step(users[f])
+            for b in range(B):
+                tr = s.read_trace(b)
+                ref = refs[b][f]
+                assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], (f, b)
+                assert rel_err(tr["text_logits"], ref["text_logits"]) <= TOL
+                assert bool(has[b]) == (ref["out"] is not None)
+                if ref["out"] is not None:
+                    assert out[b].tolist() == ref["out"]
+        s.reset(1)
+        assert [s.offset(b) for b in range(B)] == [6, 0, 6]
+
+
+@pytest.mark.parametrize("band", ["bf16", "i8"])
+def test_low_precision_bands_on_the_tiny_model(weights, band):
+    """bf16 band vs the oracle on the same bf16-rounded weights; int8 band vs the int8-dequantised
+    oracle (storage loss only).  Teacher-forced onto the oracle's tokens."""
+    w16 = {k: (synth.f32_to_bf16_bits(v) if v.ndim == 2 else v) for k, v in weights.items()}
+    ref_lm = OracleLM(CFG, w16, band="i8sim" if band == "i8" else "f32")
+    users = synth.user_tokens(CFG, 8)
+    ost = ref_lm.new_state()
+    agree, total, cos_min = 0, 0, 1.0
+    with rq.Session(CFG, band=band) as s:
+        s.load_weights(w16)
+        for f in range(8):
+            ref = ref_lm.step(ost, users[f])
+            s.step(users[f])
+            tr = s.read_trace(0)
+            cos_min = min(cos_min, cosine(tr["text_logits"], ref["text_logits"]),
+                          *[cosine(tr["audio_logits"][c], ref["audio_logits"][c]) for c in range(8)])
+            got = [tr["text_token"]] + tr["audio_tokens"]
+            want = [ref["text_token"]] + ref["audio_tokens"]
+            agree += sum(int(a == b) for a, b in zip(got, want))
+            total += 9
+            ref_lm.force_generated(ost, ref["text_token"], ref["audio_tokens"])
+            s.force_generated(0, ref["text_token"], ref["audio_tokens"])
+    print(f"{band}: min cosine {cos_min:.6f}, agreement {agree}/{total}")
+    assert cos_min >= 0.999
+    assert agree / total >= 0.99
