@@ -8,7 +8,7 @@ namespace mk {
 constexpr int WAVE = 64;
 constexpr int BLOCK = 256;
 constexpr int NWAVES = BLOCK / WAVE;
-constexpr int MAX_STREAMS = 64;  // 2 * dep_q + 1 upper bound
+constexpr int MAX_STREAMS = 33;  // 2 * dep_q + 1 upper bound (dep_q <= 16)
 
 typedef uint16_t bf16_t;
 
@@ -151,9 +151,9 @@ __device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
 }
 
 // One wave computes the dot products of R weight rows (row r starts at W + rowoff[r]) with the
-// vector xs[0..K) held in LDS.  Lane l handles the 16-byte vectors l, l + 64, l + 128, ... of
-// each row; U vectors per row are loaded before any arithmetic so that R * U loads are in flight
-// per lane.  K must be a multiple of the vector width.  acc[r] is the lane's partial sum.
+// vector xs[0..K) held in LDS, for any K (multiple of the vector width): lane l handles the
+// 16-byte vectors l, l + 64, l + 128, ... of each row, U vectors per row in flight at a time.
+// acc[r] is the lane's partial sum.
 template <typename WT, int R, int U>
 __device__ __forceinline__ void wave_rows_dot(const WT *__restrict__ W, int K, const int64_t *rowoff,
                                               const float *__restrict__ xs, float *acc) {
@@ -200,22 +200,118 @@ __device__ __forceinline__ void wave_rows_dot(const WT *__restrict__ W, int K, c
   }
 }
 
+// Register tile of one wave: R whole weight rows, VPL 16-byte vectors per lane per row (vector v
+// = lane + 64 i; vectors past the row end read as zero).  load() issues every load of the tile at
+// once and returns; dot() consumes the tile against xs in LDS.  Splitting the two lets a kernel
+// issue its weight loads before its prologue and prefetch the next rows while it reduces.
+// VPL == 0 is the generic form for any K: load() only records the rows and dot() streams them.
+template <typename WT, int R, int VPL>
+struct RowTile {
+  static constexpr int N = WVec<WT>::N;
+  uint4 w[R][VPL];
+  __device__ __forceinline__ void load(const WT *__restrict__ W, int K, const int *rows) {
+    const int lane = threadIdx.x & 63;
+    const int nv = K / N;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint4 *p = reinterpret_cast<const uint4 *>(W + (size_t)rows[r] * K);
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int v = lane + WAVE * i;
+        w[r][i] = v < nv ? ld_stream(p + v) : uint4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  __device__ __forceinline__ void dot(const WT *__restrict__, int K, const float *__restrict__ xs, float *acc) const {
+    const int lane = threadIdx.x & 63;
+    const int nv = K / N;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int v = lane + WAVE * i;
+      if (v < nv) {
+        const float *xp = xs + (size_t)v * N;
+        float xv[N];
+#pragma unroll
+        for (int e = 0; e < N; ++e) xv[e] = xp[e];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float wf[N];
+          WVec<WT>::cvt(w[r][i], wf);
+#pragma unroll
+          for (int e = 0; e < N; ++e) acc[r] = fmaf(wf[e], xv[e], acc[r]);
+        }
+      }
+    }
+  }
+};
+
+template <typename WT, int R>
+struct RowTile<WT, R, 0> {
+  int64_t ro[R];
+  __device__ __forceinline__ void load(const WT *__restrict__, int K, const int *rows) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) ro[r] = (int64_t)rows[r] * K;
+  }
+  __device__ __forceinline__ void dot(const WT *__restrict__ W, int K, const float *__restrict__ xs, float *acc) const {
+    wave_rows_dot<WT, R, 8>(W, K, ro, xs, acc);
+  }
+};
+
+// ---- cross-block exchange inside one kernel -------------------------------------------------
+// Data another block of the same kernel reads is written with system-scope stores (write-through
+// past the per-XCD L2) and read with system-scope loads; the writer waits for its stores to
+// complete (s_waitcnt vmcnt(0)) before it signals with an atomic.
+__device__ __forceinline__ void st_sys(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); }
+__device__ __forceinline__ float ld_sys(const float *p) {
+  return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Staging of a block's input vector into LDS.  Every thread issues STAGE_UNR float4 loads before
+// it stores any of them (one memory round trip per STAGE_UNR * BLOCK * 4 floats instead of one
+// per BLOCK floats).  K is a multiple of 4 and src is 16-byte aligned.
+constexpr int STAGE_UNR = 8;
+
+// xs[k] = src[k] for k < K; returns this thread's partial sum of squares.  No barrier.
+__device__ __forceinline__ float stage_copy(const float *__restrict__ src, int K, float *xs) {
+  const int K4 = K >> 2;
+  const float4 *s4 = reinterpret_cast<const float4 *>(src);
+  float4 *x4 = reinterpret_cast<float4 *>(xs);
+  float ss = 0.f;
+  for (int base = 0; base < K4; base += STAGE_UNR * BLOCK) {
+    float4 v[STAGE_UNR];
+#pragma unroll
+    for (int u = 0; u < STAGE_UNR; ++u) {
+      const int i = base + u * BLOCK + threadIdx.x;
+      v[u] = i < K4 ? s4[i] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < STAGE_UNR; ++u) {
+      const int i = base + u * BLOCK + threadIdx.x;
+      if (i < K4) {
+        x4[i] = v[u];
+        ss = fmaf(v[u].x, v[u].x, ss);
+        ss = fmaf(v[u].y, v[u].y, ss);
+        ss = fmaf(v[u].z, v[u].z, ss);
+        ss = fmaf(v[u].w, v[u].w, ss);
+      }
+    }
+  }
+  return ss;
+}
+
 // xs[k] = src[k] for k < K, then a barrier.
 __device__ __forceinline__ void stage_vec(const float *__restrict__ src, int K, float *xs) {
-  for (int k = threadIdx.x; k < K; k += BLOCK) xs[k] = src[k];
+  (void)stage_copy(src, K, xs);
   __syncthreads();
 }
 
 // xs = rms_norm(src; alpha): y = x * alpha * 1/sqrt(eps + mean(x^2)) (eps inside the mean).
 __device__ __forceinline__ void stage_rms(const float *__restrict__ src, const float *__restrict__ alpha, int K,
                                           float eps, float *xs, float *red) {
-  float ss = 0.f;
-  for (int k = threadIdx.x; k < K; k += BLOCK) {
-    const float v = src[k];
-    xs[k] = v;
-    ss = fmaf(v, v, ss);
-  }
-  const float tot = block_sum(ss, red);
+  const float tot = block_sum(stage_copy(src, K, xs), red);  // block_sum's barriers publish xs
   const float inv = 1.0f / sqrtf(eps + tot / (float)K);
   for (int k = threadIdx.x; k < K; k += BLOCK) xs[k] = (xs[k] * alpha[k]) * inv;
   __syncthreads();

@@ -1,7 +1,11 @@
-// Frame-step kernels for gfx950.  Kernels used by several stages take the stage id as a template
-// tag, so that each stage is its own symbol in profiler traces.  Each kernel is one stage of the Moshi RQ-Transformer frame as
-// the docs.rs page "inferencelayer 0.2.4 src/moshi_lm.rs" defines it (cited as [LM]); the weight
-// streaming GEMV core is shared by every projection.
+// Frame-step kernels for gfx950.  Each kernel is one stage of the Moshi RQ-Transformer frame as
+// the docs.rs page "inferencelayer 0.2.4 src/moshi_lm.rs" defines it (cited as [LM]).
+//
+// Weight-streaming projections share one pattern: every wave owns whole output rows (a row
+// group), issues all loads of its first group BEFORE the block's prologue (norm, attention, ...)
+// and prefetches its next group while it reduces the current one; the grid is sized to the CUs
+// and strides over row groups.  Kernels used by several stages take the stage id as a template
+// tag so that each stage is its own symbol in profiler traces.
 #pragma once
 #include "device_common.h"
 
@@ -9,15 +13,20 @@ namespace mk {
 
 // Shapes of one session (all ints are element counts).
 struct Dims {
-  int B;                // conversations
-  int L, D, H, hd, F;   // temporal: layers, width, heads, head dim, FFN hidden
-  int C, cap;           // context window, KV slots held per conversation
-  int Vt, Va;           // text / audio head widths (tables have one more row)
+  int B;                       // conversations
+  int L, D, H, hd, F;          // temporal: layers, width, heads, head dim, FFN hidden
+  int C, cap;                  // context window, KV slots held per conversation
+  int Vt, Va;                  // text / audio head widths (tables have one more row)
   int Ld, Dd, Hd, hdd, Fd, Q;  // depformer
-  int NS;               // 2 * Q + 1 token streams
-  int S;                // temporal attention splits over positions
+  int NS;                      // 2 * Q + 1 token streams
+  int S;                       // temporal attention: most splits over positions
   float eps;
 };
+
+constexpr int AM_MAX_BLOCKS = 1024;  // argmax partials per head
+constexpr int ATTN_MAX_S = 32;       // temporal attention splits
+constexpr int ATTN_MIN_CHUNK = 64;   // positions per split before another split is used
+constexpr int DEP_MAX_POS = 16;      // depformer steps (dep_q) per frame
 
 // Device-resident session state and activations.
 struct Bufs {
@@ -40,19 +49,33 @@ struct Bufs {
   float *da;            // [B][Fd]
   float *audio_logits;  // [B][Q][Va]
   int32_t *outpack;     // [B][1+Q] realigned output, then [B] has_out
-  float *attn_part;     // [B][H][S][hd+2] (max, sum, o[hd]) per split
+  float *attn_part;     // [B][H][ATTN_MAX_S][hd+2] (max, sum, o[hd]) per split
   uint32_t *attn_cnt;   // [B][H]
-  ArgBest *am_part;     // [B][1+Q][AM_MAX_BLOCKS]
-  uint32_t *am_cnt;     // [B][1+Q]
+  ArgBest *am_part;     // [B][1+Q][AM_MAX_BLOCKS] best row of each head block
   float *rope_freq;     // [hd/2]
 };
-
-constexpr int AM_MAX_BLOCKS = 1024;
 
 template <typename KT>
 struct KV {
   KT *k, *v;  // [B][L][H][cap][hd]
 };
+
+// ---- argmax partials --------------------------------------------------------------------------
+// Each head block stores the best (value, row) of its rows; the next kernel that needs the
+// token merges them (first-wins; no candidate gives 0).
+__device__ __forceinline__ int reduce_head_partials(const ArgBest *__restrict__ part, int n) {
+  __shared__ ArgBest wb[NWAVES];
+  ArgBest bb = arg_none();
+  for (int i = threadIdx.x; i < n; i += BLOCK) bb = arg_merge(bb, part[i]);
+  bb = wave_arg(bb);
+  if ((threadIdx.x & 63) == 0) wb[threadIdx.x >> 6] = bb;
+  __syncthreads();
+  ArgBest t = wb[0];
+#pragma unroll
+  for (int i = 1; i < NWAVES; ++i) t = arg_merge(t, wb[i]);
+  __syncthreads();
+  return t.i < 0 ? 0 : t.i;
+}
 
 // --------------------------------------------------------------------------------------------
 // a1-a3: user write, gather with INITIAL substitution, 17-row embedding sum ([LM] step_ext
@@ -86,20 +109,24 @@ __global__ __launch_bounds__(BLOCK) void k_embed_begin(Dims d, Bufs s, const ET 
     if (st >= d.Q + 1)
       s.ring[((size_t)b * d.NS + st) * 3 + (int)((off + stream_delay(st, d.Q)) % 3)] = urow[st - d.Q - 1];
   }
+  // every row value of a column is loaded before the sum, which then runs in the stream order
   for (int c = blockIdx.x * BLOCK + threadIdx.x; c < d.D; c += gridDim.x * BLOCK) {
-    float acc = 0.f;
-    for (int k = 0; k < 2 * d.Q; ++k) {
-      int t = tok[1 + k];
-      if (t != -1) {
-        t = t < 0 ? 0 : t;
-        acc += to_f(emb_audio[((size_t)k * (d.Va + 1) + t) * d.D + c]);
+    float v[MAX_STREAMS];
+#pragma unroll
+    for (int k = 0; k < MAX_STREAMS; ++k) {
+      if (k < d.NS) {
+        const int t = tok[k];
+        const int row = t < 0 ? 0 : t;
+        v[k] = t == -1 ? 0.f
+                       : to_f(k == 0 ? emb_text[(size_t)row * d.D + c]
+                                     : emb_audio[((size_t)(k - 1) * (d.Va + 1) + row) * d.D + c]);
       }
     }
-    int t = tok[0];
-    if (t != -1) {
-      t = t < 0 ? 0 : t;
-      acc += to_f(emb_text[(size_t)t * d.D + c]);
-    }
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 1; k < MAX_STREAMS; ++k)
+      if (k < d.NS && tok[k] != -1) acc += v[k];
+    if (tok[0] != -1) acc += v[0];
     s.x[(size_t)b * d.D + c] = acc;
     s.emb_sum[(size_t)b * d.D + c] = acc;
   }
@@ -107,26 +134,34 @@ __global__ __launch_bounds__(BLOCK) void k_embed_begin(Dims d, Bufs s, const ET 
 
 // --------------------------------------------------------------------------------------------
 // a4.1: x -> rms_norm(norm1) -> fused q|k|v rows -> interleaved rope on q, k at pos = offset ->
-// q to s.q, k and v to KV slot offset % cap ([LM] temporal_step, rope_row).  Each wave owns a
-// row pair (2i, 2i+1), i.e. one rope pair.  Dynamic LDS: D floats.
+// q to s.q, k and v to KV slot offset % cap ([LM] temporal_step, rope_row).  A wave's row group
+// is the pair (2i, 2i+1), i.e. one rope pair.  Dynamic LDS: D floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, typename KT, int U>
+template <typename WT, typename KT, int VPL>
 __global__ __launch_bounds__(BLOCK) void k_qkv_rope(Dims d, Bufs s, KV<KT> kv, const WT *__restrict__ w,
                                                     const float *__restrict__ wscale,
                                                     const float *__restrict__ norm, int layer, int b0) {
   extern __shared__ float xs[];
   __shared__ float red[NWAVES];
   const int b = b0 + blockIdx.y;
-  stage_rms(s.x + (size_t)b * d.D, norm, d.D, d.eps, xs, red);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int npairs = 3 * d.D / 2;
+  const int stride = gridDim.x * NWAVES;
+  int pr = blockIdx.x * NWAVES + wave;
+  RowTile<WT, 2, VPL> t;
+  int rows[2] = {min(2 * pr, 3 * d.D - 2), min(2 * pr, 3 * d.D - 2) + 1};
+  if (pr < npairs) t.load(w, d.D, rows);
+  stage_rms(s.x + (size_t)b * d.D, norm, d.D, d.eps, xs, red);
   const int64_t pos = s.offset[b];
   const int slot = (int)(pos % d.cap);
-  const int npairs = 3 * d.D / 2;
-  for (int pr = blockIdx.x * NWAVES + wave; pr < npairs; pr += gridDim.x * NWAVES) {
-    const int r0 = 2 * pr;
-    const int64_t ro[2] = {(int64_t)r0 * d.D, (int64_t)(r0 + 1) * d.D};
+  for (; pr < npairs; pr += stride) {
     float acc[2];
-    wave_rows_dot<WT, 2, U>(w, d.D, ro, xs, acc);
+    t.dot(w, d.D, xs, acc);
+    const int r0 = 2 * pr;
+    if (pr + stride < npairs) {
+      const int nr[2] = {2 * (pr + stride), 2 * (pr + stride) + 1};
+      t.load(w, d.D, nr);
+    }
     acc[0] = wave_sum(acc[0]);
     acc[1] = wave_sum(acc[1]);
     if (lane == 0) {
@@ -163,9 +198,10 @@ __global__ __launch_bounds__(BLOCK) void k_qkv_rope(Dims d, Bufs s, KV<KT> kv, c
 
 // --------------------------------------------------------------------------------------------
 // a4.2: single-query attention of head h over the n = min(offset + 1, context) cached positions
-// ([LM] attend: scale 1/sqrt(hd) after the dot, max-subtracted softmax).  Grid (H, S, nb): split
-// sp takes a contiguous slice of the slots [0, n) (the softmax is order-free), writes its local
-// (max, sum, sum e*v), and the last split to finish combines the S partials in split order.
+// ([LM] attend: scale 1/sqrt(hd) after the dot, max-subtracted softmax).  Grid (H, S, nb); only
+// S_eff = min(S, ceil(n / 64)) splits take part.  Split sp takes a contiguous slice of the slots
+// [0, n) (the softmax is order-free) and computes its local (max, sum, sum e*v); with one split it
+// writes o directly, otherwise the last split to finish merges the partials in split order.
 // Dynamic LDS: ceil(cap / S) floats.
 // --------------------------------------------------------------------------------------------
 template <typename KT, int HD>
@@ -173,13 +209,17 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   extern __shared__ float sc[];
   __shared__ float red[NWAVES];
   __shared__ float ored[NWAVES][HD];
+  __shared__ float pbuf[ATTN_MAX_S * (HD + 2)];
+  __shared__ float pws[ATTN_MAX_S];
   __shared__ int s_last;
   constexpr int EPL = HD / 16;  // elements per lane; 16 lanes cover one position's head slice
-  const int h = blockIdx.x, sp = blockIdx.y, S = gridDim.y;
+  const int h = blockIdx.x, sp = blockIdx.y;
   const int b = b0 + blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
   const int64_t pos = s.offset[b];
   const int n = (int)(pos + 1 < (int64_t)d.C ? pos + 1 : (int64_t)d.C);
+  const int S = min((int)gridDim.y, max(1, (n + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK));
+  if (sp >= S) return;
   const int chunk = (n + S - 1) / S;
   const int j0 = sp * chunk;
   const int j1 = min(n, j0 + chunk);
@@ -242,105 +282,107 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
     for (int i = 0; i < EPL; ++i) ored[wave][sub * EPL + i] = op[i];
   }
   __syncthreads();
-  float *part = s.attn_part + (((size_t)b * d.H + h) * S + sp) * (HD + 2);
+  float *out = s.o + (size_t)b * d.D + h * HD;
+  if (S == 1) {
+    for (int t = threadIdx.x; t < HD; t += BLOCK) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NWAVES; ++w2) acc += ored[w2][t];
+      out[t] = acc / l;
+    }
+    return;
+  }
+  float *part = s.attn_part + (((size_t)b * d.H + h) * ATTN_MAX_S + sp) * (HD + 2);
   for (int t = threadIdx.x; t < HD; t += BLOCK) {
     float acc = 0.f;
 #pragma unroll
     for (int w2 = 0; w2 < NWAVES; ++w2) acc += ored[w2][t];
-    part[2 + t] = acc;
+    st_sys(part + 2 + t, acc);
   }
   if (threadIdx.x == 0) {
-    part[0] = m;
-    part[1] = l;
+    st_sys(part, m);
+    st_sys(part + 1, l);
   }
-  __threadfence();
+  wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&s.attn_cnt[(size_t)b * d.H + h], 1u);
+    const uint32_t prev = __hip_atomic_fetch_add(&s.attn_cnt[(size_t)b * d.H + h], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (uint32_t)(S - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
-  const float *p0 = s.attn_part + ((size_t)b * d.H + h) * S * (HD + 2);
+  // last split: stage every partial in LDS with one parallel pass, then merge in split order
+  const float *p0 = s.attn_part + ((size_t)b * d.H + h) * ATTN_MAX_S * (HD + 2);
+  for (int i = threadIdx.x; i < S * (HD + 2); i += BLOCK) pbuf[i] = ld_sys(p0 + i);
+  __syncthreads();
   float M = -INFINITY;
-  for (int k = 0; k < S; ++k) M = fmaxf(M, p0[(size_t)k * (HD + 2)]);
-  float Lsum = 0.f;
-  for (int k = 0; k < S; ++k) {
-    const float mk = p0[(size_t)k * (HD + 2)];
-    if (mk > -INFINITY) Lsum += expf(mk - M) * p0[(size_t)k * (HD + 2) + 1];
+  for (int k = 0; k < S; ++k) M = fmaxf(M, pbuf[k * (HD + 2)]);
+  if (threadIdx.x < S) {
+    const float mk = pbuf[threadIdx.x * (HD + 2)];
+    pws[threadIdx.x] = mk > -INFINITY ? expf(mk - M) : 0.f;
   }
+  __syncthreads();
+  float Lsum = 0.f;
+  for (int k = 0; k < S; ++k) Lsum += pws[k] * pbuf[k * (HD + 2) + 1];
   for (int t = threadIdx.x; t < HD; t += BLOCK) {
     float acc = 0.f;
-    for (int k = 0; k < S; ++k) {
-      const float mk = p0[(size_t)k * (HD + 2)];
-      if (mk > -INFINITY) acc += expf(mk - M) * p0[(size_t)k * (HD + 2) + 2 + t];
-    }
-    s.o[(size_t)b * d.D + h * HD + t] = acc / Lsum;
+    for (int k = 0; k < S; ++k) acc += pws[k] * pbuf[k * (HD + 2) + 2 + t];
+    out[t] = acc / Lsum;
   }
-  if (threadIdx.x == 0) s.attn_cnt[(size_t)b * d.H + h] = 0u;
+  if (threadIdx.x == 0) __hip_atomic_store(&s.attn_cnt[(size_t)b * d.H + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // --------------------------------------------------------------------------------------------
-// Residual projection: out[r] += (W . in)[r] ([LM] out_proj and gate_out followed by the
-// residual add).  `in` and `out` are per-conversation vectors with strides in_ld / out_ld.
-// Dynamic LDS: K floats.
+// Projection of `in` into `out`: out[r] = (W . in)[r] (STORE) or out[r] += (W . in)[r] (residual
+// add: [LM] out_proj / gate_out followed by the residual).  R rows per group.  Dynamic LDS: K.
 // --------------------------------------------------------------------------------------------
-template <typename WT, int R, int U, int TAG>
-__global__ __launch_bounds__(BLOCK) void k_gemv_residual(const WT *__restrict__ w, const float *__restrict__ wscale,
-                                                         int N, int K, const float *__restrict__ in, int in_ld,
-                                                         float *__restrict__ out, int out_ld, int b0) {
+template <typename WT, int R, int VPL, bool ADD, int TAG>
+__global__ __launch_bounds__(BLOCK) void k_gemv(const WT *__restrict__ w, const float *__restrict__ wscale, int N,
+                                                int K, const float *__restrict__ in, int in_ld,
+                                                float *__restrict__ out, int out_ld, int b0) {
   extern __shared__ float xs[];
   const int b = b0 + blockIdx.y;
-  stage_vec(in + (size_t)b * in_ld, K, xs);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ngroups = (N + R - 1) / R;
-  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
-    int64_t ro[R];
+  const int stride = gridDim.x * NWAVES;
+  int gi = blockIdx.x * NWAVES + wave;
+  RowTile<WT, R, VPL> t;
+  int rows[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, N - 1) * K;
+  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, N - 1);
+  if (gi < ngroups) t.load(w, K, rows);
+  stage_vec(in + (size_t)b * in_ld, K, xs);
+  for (; gi < ngroups; gi += stride) {
     float acc[R];
-    wave_rows_dot<WT, R, U>(w, K, ro, xs, acc);
+    t.dot(w, K, xs, acc);
+    if (gi + stride < ngroups) {
+      int nr[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) nr[r] = min((gi + stride) * R + r, N - 1);
+      t.load(w, K, nr);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float v = wave_sum(acc[r]);
       const int row = gi * R + r;
-      if (lane == 0 && row < N) out[(size_t)b * out_ld + row] += wscale ? v * wscale[row] : v;
-    }
-  }
-}
-
-// Plain projection: out[r] = (W . in)[r] (depformer_in for all codebooks at once).
-template <typename WT, int R, int U, int TAG>
-__global__ __launch_bounds__(BLOCK) void k_gemv_store(const WT *__restrict__ w, const float *__restrict__ wscale,
-                                                      int N, int K, const float *__restrict__ in, int in_ld,
-                                                      float *__restrict__ out, int out_ld, int b0) {
-  extern __shared__ float xs[];
-  const int b = b0 + blockIdx.y;
-  stage_vec(in + (size_t)b * in_ld, K, xs);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ngroups = (N + R - 1) / R;
-  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
-    int64_t ro[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, N - 1) * K;
-    float acc[R];
-    wave_rows_dot<WT, R, U>(w, K, ro, xs, acc);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = wave_sum(acc[r]);
-      const int row = gi * R + r;
-      if (lane == 0 && row < N) out[(size_t)b * out_ld + row] = wscale ? v * wscale[row] : v;
+      if (lane == 0 && row < N) {
+        const float y = wscale ? v * wscale[row] : v;
+        if (ADD)
+          out[(size_t)b * out_ld + row] += y;
+        else
+          out[(size_t)b * out_ld + row] = y;
+      }
     }
   }
 }
 
 // --------------------------------------------------------------------------------------------
 // a5 (first half): h = rms_norm(x; norm2), g = linear_in . h, a[j] = silu(g[j]) * g[F + j]
-// ([LM] temporal_step / depformer_cycle gating, rows packed [gate | mult]).  A wave owns the
-// row pair (j, F + j).  Dynamic LDS: K floats.
+// ([LM] temporal_step / depformer_cycle gating, rows packed [gate | mult]).  A wave's row group
+// is the pair (j, F + j).  Dynamic LDS: K floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, int U, int TAG>
+template <typename WT, int VPL, int TAG>
 __global__ __launch_bounds__(BLOCK) void k_gate(const WT *__restrict__ w, const float *__restrict__ wscale, int F,
                                                 int K, const float *__restrict__ x, int x_ld,
                                                 const float *__restrict__ norm, float eps,
@@ -348,12 +390,20 @@ __global__ __launch_bounds__(BLOCK) void k_gate(const WT *__restrict__ w, const 
   extern __shared__ float xs[];
   __shared__ float red[NWAVES];
   const int b = b0 + blockIdx.y;
-  stage_rms(x + (size_t)b * x_ld, norm, K, eps, xs, red);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int j = blockIdx.x * NWAVES + wave; j < F; j += gridDim.x * NWAVES) {
-    const int64_t ro[2] = {(int64_t)j * K, (int64_t)(F + j) * K};
+  const int stride = gridDim.x * NWAVES;
+  int j = blockIdx.x * NWAVES + wave;
+  RowTile<WT, 2, VPL> t;
+  int rows[2] = {min(j, F - 1), F + min(j, F - 1)};
+  if (j < F) t.load(w, K, rows);
+  stage_rms(x + (size_t)b * x_ld, norm, K, eps, xs, red);
+  for (; j < F; j += stride) {
     float acc[2];
-    wave_rows_dot<WT, 2, U>(w, K, ro, xs, acc);
+    t.dot(w, K, xs, acc);
+    if (j + stride < F) {
+      const int nr[2] = {j + stride, F + j + stride};
+      t.load(w, K, nr);
+    }
     float gv = wave_sum(acc[0]), mv = wave_sum(acc[1]);
     if (lane == 0) {
       if (wscale) {
@@ -367,39 +417,45 @@ __global__ __launch_bounds__(BLOCK) void k_gate(const WT *__restrict__ w, const 
 
 // --------------------------------------------------------------------------------------------
 // a6-a8 heads: logits = W . v with v = rms_norm(src; norm) (text head after out_norm) or v = src
-// (depformer heads read y with no norm), then first-wins argmax of the logits into tok_out.
-// Blocks keep their best row in am_part; the last block to finish merges them in block order.
-// With hid_out set, block 0 also stores the normalised vector (the post-out_norm hidden).
-// Dynamic LDS: K floats.
+// (depformer heads read y with no norm).  Each block stores the best (value, row) of its rows in
+// am_part[blockIdx.x]; the kernel that needs the token merges them.  With hid_out set, block 0
+// also stores the normalised vector (the post-out_norm hidden).  Dynamic LDS: K floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, int R, int U, int TAG>
-__global__ __launch_bounds__(BLOCK) void k_head_argmax(const WT *__restrict__ w, const float *__restrict__ wscale,
-                                                       int N, int K, const float *__restrict__ src, int src_ld,
-                                                       const float *__restrict__ norm, float eps,
-                                                       float *__restrict__ hid_out, float *__restrict__ logits,
-                                                       int logits_ld, ArgBest *__restrict__ am_part, int am_ld,
-                                                       uint32_t *__restrict__ am_cnt, int cnt_ld,
-                                                       int32_t *__restrict__ tok_out, int tok_ld, int b0) {
+template <typename WT, int R, int VPL, int TAG>
+__global__ __launch_bounds__(BLOCK) void k_head(const WT *__restrict__ w, const float *__restrict__ wscale, int N,
+                                                int K, const float *__restrict__ src, int src_ld,
+                                                const float *__restrict__ norm, float eps,
+                                                float *__restrict__ hid_out, float *__restrict__ logits,
+                                                int logits_ld, ArgBest *__restrict__ am_part, int am_ld, int b0) {
   extern __shared__ float xs[];
   __shared__ float red[NWAVES];
   __shared__ ArgBest wbest[NWAVES];
-  __shared__ int s_last;
   const int b = b0 + blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ngroups = (N + R - 1) / R;
+  const int stride = gridDim.x * NWAVES;
+  int gi = blockIdx.x * NWAVES + wave;
+  RowTile<WT, R, VPL> t;
+  int rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, N - 1);
+  if (gi < ngroups) t.load(w, K, rows);
   if (norm)
     stage_rms(src + (size_t)b * src_ld, norm, K, eps, xs, red);
   else
     stage_vec(src + (size_t)b * src_ld, K, xs);
   if (hid_out && blockIdx.x == 0)
     for (int k = threadIdx.x; k < K; k += BLOCK) hid_out[(size_t)b * src_ld + k] = xs[k];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ngroups = (N + R - 1) / R;
   ArgBest best = arg_none();
-  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
-    int64_t ro[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, N - 1) * K;
+  for (; gi < ngroups; gi += stride) {
     float acc[R];
-    wave_rows_dot<WT, R, U>(w, K, ro, xs, acc);
+    t.dot(w, K, xs, acc);
+    if (gi + stride < ngroups) {
+      int nr[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) nr[r] = min((gi + stride) * R + r, N - 1);
+      t.load(w, K, nr);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float v = wave_sum(acc[r]);
@@ -418,46 +474,41 @@ __global__ __launch_bounds__(BLOCK) void k_head_argmax(const WT *__restrict__ w,
     for (int i = 1; i < NWAVES; ++i) bb = arg_merge(bb, wbest[i]);
     am_part[(size_t)b * am_ld + blockIdx.x] = bb;
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&am_cnt[(size_t)b * cnt_ld], 1u);
-    s_last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (threadIdx.x < WAVE) {
-    ArgBest bb = arg_none();
-    for (int i = threadIdx.x; i < (int)gridDim.x; i += WAVE) bb = arg_merge(bb, am_part[(size_t)b * am_ld + i]);
-    bb = wave_arg(bb);
-    if (threadIdx.x == 0) {
-      tok_out[(size_t)b * tok_ld] = bb.i < 0 ? 0 : bb.i;
-      am_cnt[(size_t)b * cnt_ld] = 0u;
-    }
-  }
 }
 
 // --------------------------------------------------------------------------------------------
-// a8 depformer step cb, layer j, first half: y (layer 0: depformer_in[cb] . hidden + emb(prev))
-// -> rms_norm(norm1_j) -> q|k|v rows of in_projs[j][cb] (no rope) -> q to dq, k and v to the
-// per-frame cache entry (j, cb) ([LM] depformer_cycle).  Dynamic LDS: Dd floats.
+// a8 depformer step cb, layer j, first half: y (layer 0: depformer_in[cb] . hidden + emb(prev),
+// prev = the previous head's token, merged here from its block partials) -> rms_norm(norm1_j) ->
+// q|k|v rows of in_projs[j][cb] (no rope) -> q to dq, k and v to the per-frame cache entry
+// (j, cb) ([LM] depformer_cycle).  Dynamic LDS: Dd floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, typename ET, int R, int U>
+template <typename WT, typename ET, int R, int VPL>
 __global__ __launch_bounds__(BLOCK) void k_dep_qkv(Dims d, Bufs s, const WT *__restrict__ w,
                                                    const float *__restrict__ wscale, const float *__restrict__ norm,
-                                                   const ET *__restrict__ table, int layer, int cb, int b0) {
+                                                   const ET *__restrict__ table, int layer, int cb, int prev_parts,
+                                                   int b0) {
   extern __shared__ float xs[];
   __shared__ float red[NWAVES];
   const int b = b0 + blockIdx.y;
   const int Dd = d.Dd;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int N = 3 * Dd;
+  const int ngroups = (N + R - 1) / R;
+  const int stride = gridDim.x * NWAVES;
+  int gi = blockIdx.x * NWAVES + wave;
+  RowTile<WT, R, VPL> t;
+  int rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, N - 1);
+  if (gi < ngroups) t.load(w, Dd, rows);
   float *y = s.y + (size_t)b * Dd;
   if (layer == 0) {
-    int prev = s.tokens[(size_t)b * (1 + d.Q) + cb];  // text for cb 0, else audio[cb - 1]
+    const int prev =
+        reduce_head_partials(s.am_part + ((size_t)b * (1 + d.Q) + cb) * AM_MAX_BLOCKS, prev_parts);
+    if (blockIdx.x == 0 && threadIdx.x == 0) s.tokens[(size_t)b * (1 + d.Q) + cb] = prev;
     const float *dinp = s.din + ((size_t)b * d.Q + cb) * Dd;
     for (int k = threadIdx.x; k < Dd; k += BLOCK) {
-      float v = dinp[k];
-      if (prev != -1) v += to_f(table[(size_t)(prev < 0 ? 0 : prev) * Dd + k]);
+      const float v = dinp[k] + to_f(table[(size_t)prev * Dd + k]);  // argmax tokens are >= 0
       xs[k] = v;
       if (blockIdx.x == 0) y[k] = v;
     }
@@ -466,16 +517,16 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv(Dims d, Bufs s, const WT *__r
   } else {
     stage_rms(y, norm, Dd, d.eps, xs, red);
   }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int N = 3 * Dd;
-  const int ngroups = (N + R - 1) / R;
   float *kvbase = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q + cb) * 2) * Dd;
-  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
-    int64_t ro[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, N - 1) * Dd;
+  for (; gi < ngroups; gi += stride) {
     float acc[R];
-    wave_rows_dot<WT, R, U>(w, Dd, ro, xs, acc);
+    t.dot(w, Dd, xs, acc);
+    if (gi + stride < ngroups) {
+      int nr[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) nr[r] = min((gi + stride) * R + r, N - 1);
+      t.load(w, Dd, nr);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float v = wave_sum(acc[r]);
@@ -493,49 +544,91 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv(Dims d, Bufs s, const WT *__r
 
 // --------------------------------------------------------------------------------------------
 // a8 depformer step cb, layer j, attention + out_proj: every block recomputes the attention of
-// dq over the cb + 1 cache entries of layer j (all heads; [LM] attend) into LDS, then
-// y[r] += out_projs[j][cb] . o.  Dynamic LDS: Dd floats.
+// dq over the cb + 1 cache entries of layer j ([LM] attend; weights e_p / den) into LDS -- 16
+// lanes per head, EPL dims per lane, all loads issued at once -- then y[r] += out_projs[j][cb] . o.
+// Dynamic LDS: Dd floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, int R, int U>
+template <typename WT, int R, int VPL, int EPL>
 __global__ __launch_bounds__(BLOCK) void k_dep_out(Dims d, Bufs s, const WT *__restrict__ w,
                                                    const float *__restrict__ wscale, int layer, int cb, int b0) {
   extern __shared__ float xs[];
   const int b = b0 + blockIdx.y;
   const int Dd = d.Dd, hdd = d.hdd;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
+  const int ngroups = (Dd + R - 1) / R;
+  const int stride = gridDim.x * NWAVES;
+  int gi = blockIdx.x * NWAVES + wave;
+  RowTile<WT, R, VPL> t;
+  int rows[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, Dd - 1);
+  if (gi < ngroups) t.load(w, Dd, rows);
+
   const float *q = s.dq + (size_t)b * Dd;
   const float *kv0 = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q) * 2) * Dd;
   const float scale = 1.0f / sqrtf((float)hdd);
   const int npos = cb + 1;
-  for (int hh = wave; hh < d.Hd; hh += NWAVES) {
-    float sc[16];
+  for (int hh = wave * 4 + g; hh < d.Hd; hh += NWAVES * 4) {  // 16 lanes per head
+    const int e0 = hh * hdd + sub * EPL;
+    float qv[EPL], kk[DEP_MAX_POS][EPL], vv[DEP_MAX_POS][EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) qv[i] = q[e0 + i];
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p)
+      if (p < npos) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          kk[p][i] = kv0[(size_t)p * 2 * Dd + e0 + i];
+          vv[p][i] = kv0[(size_t)p * 2 * Dd + Dd + e0 + i];
+        }
+      }
+    float sc[DEP_MAX_POS];
     float m = -INFINITY;
-    for (int p = 0; p < npos; ++p) {
-      const float *kp = kv0 + (size_t)p * 2 * Dd + hh * hdd;
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p) {
       float dot = 0.f;
-      for (int e = lane; e < hdd; e += WAVE) dot = fmaf(q[hh * hdd + e], kp[e], dot);
-      sc[p] = wave_sum_bcast(dot) * scale;
-      m = fmaxf(m, sc[p]);
+      if (p < npos) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
+      }
+      dot += __shfl_xor(dot, 8, WAVE);
+      dot += __shfl_xor(dot, 4, WAVE);
+      dot += __shfl_xor(dot, 2, WAVE);
+      dot += __shfl_xor(dot, 1, WAVE);
+      dot = __shfl(dot, lane & 48, WAVE);  // the group's first lane: identical bits in the group
+      sc[p] = dot * scale;
+      if (p < npos) m = fmaxf(m, sc[p]);
     }
     float den = 0.f;
-    for (int p = 0; p < npos; ++p) {
-      sc[p] = expf(sc[p] - m);
-      den += sc[p];
-    }
-    for (int e = lane; e < hdd; e += WAVE) {
-      float o = 0.f;
-      for (int p = 0; p < npos; ++p) o = fmaf(sc[p] / den, kv0[(size_t)p * 2 * Dd + Dd + hh * hdd + e], o);
-      xs[hh * hdd + e] = o;
-    }
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p)
+      if (p < npos) {
+        sc[p] = expf(sc[p] - m);
+        den += sc[p];
+      }
+    float o[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p)
+      if (p < npos) {
+        const float wgt = sc[p] / den;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) o[i] = fmaf(wgt, vv[p][i], o[i]);
+      }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) xs[e0 + i] = o[i];
   }
   __syncthreads();
-  const int ngroups = (Dd + R - 1) / R;
-  for (int gi = blockIdx.x * NWAVES + wave; gi < ngroups; gi += gridDim.x * NWAVES) {
-    int64_t ro[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) ro[r] = (int64_t)min(gi * R + r, Dd - 1) * Dd;
+  for (; gi < ngroups; gi += stride) {
     float acc[R];
-    wave_rows_dot<WT, R, U>(w, Dd, ro, xs, acc);
+    t.dot(w, Dd, xs, acc);
+    if (gi + stride < ngroups) {
+      int nr[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) nr[r] = min((gi + stride) * R + r, Dd - 1);
+      t.load(w, Dd, nr);
+    }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const float v = wave_sum(acc[r]);
@@ -546,23 +639,29 @@ __global__ __launch_bounds__(BLOCK) void k_dep_out(Dims d, Bufs s, const WT *__r
 }
 
 // --------------------------------------------------------------------------------------------
-// a9: offset += 1, ring slot offset % 3 <- this step's text and audio tokens, then the
-// delay-realigned output read at (offset - 1 + delay) % 3 once offset > 1 ([LM] step_ext steps
-// 7-8).  With `forced` set (teacher-forced prefill, [LM] step_forced) the ring gets forced[0..Q]
-// instead and no output is produced.  Grid (nb), one thread does the work.
+// a9: merge the last head's argmax partials into its token, then offset += 1, ring slot
+// offset % 3 <- this step's text and audio tokens, and the delay-realigned output read at
+// (offset - 1 + delay) % 3 once offset > 1 ([LM] step_ext steps 7-8).  With `forced` set
+// (teacher-forced prefill, [LM] step_forced) the ring gets forced[0..Q] instead and no output is
+// produced.  Grid (nb), BLOCK threads.
 // --------------------------------------------------------------------------------------------
 struct Forced {
   int32_t t[17];
 };
 
-__global__ void k_frame_end(Dims d, Bufs s, int b0, int use_forced, Forced forced) {
-  if (threadIdx.x != 0) return;
+__global__ __launch_bounds__(BLOCK) void k_frame_end(Dims d, Bufs s, int b0, int use_forced, Forced forced,
+                                                     int last_parts) {
   const int b = b0 + blockIdx.x;
+  int32_t *tk = s.tokens + (size_t)b * (1 + d.Q);
+  if (!use_forced) {
+    const int last = reduce_head_partials(s.am_part + ((size_t)b * (1 + d.Q) + d.Q) * AM_MAX_BLOCKS, last_parts);
+    if (threadIdx.x == 0) tk[d.Q] = last;
+  }
+  if (threadIdx.x != 0) return;
   const int64_t off = s.offset[b] + 1;
   s.offset[b] = off;
   const int p = (int)(off % 3);
   int32_t *rg = s.ring + (size_t)b * d.NS * 3;
-  const int32_t *tk = s.tokens + (size_t)b * (1 + d.Q);
   for (int st = 0; st <= d.Q; ++st) rg[st * 3 + p] = use_forced ? forced.t[st] : tk[st];
   int32_t *out = s.outpack + (size_t)b * (1 + d.Q);
   int32_t *has = s.outpack + (size_t)d.B * (1 + d.Q) + b;

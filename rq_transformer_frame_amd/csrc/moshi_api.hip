@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -57,6 +58,7 @@ struct moshi_state {
   moshi_config cfg{};
   mk::Dims d{};
   int device = 0;
+  int cus = 256;  // compute units of the device (grid sizing)
   hipStream_t stream = nullptr;
   bool own_stream = false;
 
@@ -265,10 +267,9 @@ moshi_status alloc_session(moshi_state *s) {
   req((void **)&b.da, B * d.Fd * 4);
   req((void **)&b.audio_logits, B * d.Q * d.Va * 4);
   req((void **)&b.outpack, B * (1 + d.Q) * 4 + B * 4);
-  req((void **)&b.attn_part, B * d.H * d.S * (d.hd + 2) * 4);
+  req((void **)&b.attn_part, B * d.H * mk::ATTN_MAX_S * (d.hd + 2) * 4);
   req((void **)&b.attn_cnt, B * d.H * 4);
   req((void **)&b.am_part, B * (1 + d.Q) * mk::AM_MAX_BLOCKS * sizeof(mk::ArgBest));
-  req((void **)&b.am_cnt, B * (1 + d.Q) * 4);
   req((void **)&b.rope_freq, (size_t)(d.hd / 2) * 4);
   req(&s->kc, B * d.L * d.H * (size_t)d.cap * d.hd * kvelt);
   req(&s->vc, B * d.L * d.H * (size_t)d.cap * d.hd * kvelt);
@@ -299,12 +300,46 @@ moshi_status alloc_session(moshi_state *s) {
 // ---------------------------------------------------------------------------------------------
 // Kernel launch configuration
 // ---------------------------------------------------------------------------------------------
-constexpr int MAX_GEMV_BLOCKS = 2048;
+constexpr int BLOCKS_PER_CU = 4;  // resident blocks per CU targeted by the grid-stride kernels
 
-int blocks_for(int64_t units, int per_block, int cap = MAX_GEMV_BLOCKS) {
+int blocks_for(int64_t units, int per_block, int cap) {
   int64_t g = (units + per_block - 1) / per_block;
   if (g < 1) g = 1;
   return (int)std::min<int64_t>(g, cap);
+}
+
+// Calls f(std::integral_constant<int, VPL>) with the register-tile width for input width K: the
+// smallest specialised count of 16-byte vectors per lane that covers a row, or 0 (generic loop).
+template <typename WT, typename F>
+void with_vpl(int K, F &&f) {
+  const int need = (K / mk::WVec<WT>::N + mk::WAVE - 1) / mk::WAVE;
+  using std::integral_constant;
+  if constexpr (std::is_same<WT, bf16_t>::value) {
+    if (need <= 2) return f(integral_constant<int, 2>{});
+    if (need <= 6) return f(integral_constant<int, 6>{});
+    if (need <= 8) return f(integral_constant<int, 8>{});
+    if (need <= 22) return f(integral_constant<int, 22>{});
+  } else if constexpr (std::is_same<WT, int8_t>::value) {
+    if (need <= 1) return f(integral_constant<int, 1>{});
+    if (need <= 3) return f(integral_constant<int, 3>{});
+    if (need <= 4) return f(integral_constant<int, 4>{});
+    if (need <= 11) return f(integral_constant<int, 11>{});
+  } else {
+    if (need <= 1) return f(integral_constant<int, 1>{});
+    if (need <= 3) return f(integral_constant<int, 3>{});
+  }
+  f(integral_constant<int, 0>{});
+}
+
+template <typename F>
+void with_epl(int hdd, F &&f) {
+  using std::integral_constant;
+  switch (hdd) {
+    case 16: return f(integral_constant<int, 1>{});
+    case 32: return f(integral_constant<int, 2>{});
+    case 64: return f(integral_constant<int, 4>{});
+    default: return f(integral_constant<int, 8>{});
+  }
 }
 
 // Optional per-launch HIP event timing (measurement hook): each launch is bracketed by an event
@@ -337,6 +372,9 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
       launch();
     }
   };
+  const int cap = s->cus * BLOCKS_PER_CU;
+  // grid of a kernel whose waves each own `groups_per_wave`-sized row groups
+  auto grid = [&](int64_t groups) { return dim3(blocks_for(groups, NWAVES, cap), nb); };
 
   run(MOSHI_STAGE_EMBED, [&] {
     k_embed_begin<ET><<<dim3(blocks_for(d.D, BLOCK, 64), nb), BLOCK, 0, st>>>(d, b, E(s->emb[0]), E(s->text_emb),
@@ -345,8 +383,10 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
   for (int l = 0; l < d.L; ++l) {
     const LayerW &lw = s->layers[l];
     run(MOSHI_STAGE_QKV, [&] {
-      k_qkv_rope<WT, KT, 4><<<dim3(blocks_for(3 * d.D / 2, NWAVES), nb), BLOCK, d.D * 4, st>>>(
-          d, b, kv, W(lw.in), s->scale(lw.in), N(lw.norm1), l, b0);
+      with_vpl<WT>(d.D, [&](auto v) {
+        k_qkv_rope<WT, KT, decltype(v)::value><<<grid(3 * d.D / 2), BLOCK, d.D * 4, st>>>(
+            d, b, kv, W(lw.in), s->scale(lw.in), N(lw.norm1), l, b0);
+      });
     });
     const int chunk = (d.cap + d.S - 1) / d.S;
     run(MOSHI_STAGE_ATTN, [&] {
@@ -356,65 +396,88 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
         k_attn<KT, 64><<<dim3(d.H, d.S, nb), BLOCK, chunk * 4, st>>>(d, b, kv, l, b0);
     });
     run(MOSHI_STAGE_OUT_PROJ, [&] {
-      k_gemv_residual<WT, 2, 4, MOSHI_STAGE_OUT_PROJ><<<dim3(blocks_for(d.D, 2 * NWAVES), nb), BLOCK, d.D * 4, st>>>(
-          W(lw.out), s->scale(lw.out), d.D, d.D, b.o, d.D, b.x, d.D, b0);
+      with_vpl<WT>(d.D, [&](auto v) {
+        k_gemv<WT, 2, decltype(v)::value, true, MOSHI_STAGE_OUT_PROJ><<<grid(d.D / 2), BLOCK, d.D * 4, st>>>(
+            W(lw.out), s->scale(lw.out), d.D, d.D, b.o, d.D, b.x, d.D, b0);
+      });
     });
     run(MOSHI_STAGE_GATE_IN, [&] {
-      k_gate<WT, 4, MOSHI_STAGE_GATE_IN><<<dim3(blocks_for(d.F, NWAVES), nb), BLOCK, d.D * 4, st>>>(
-          W(lw.gin), s->scale(lw.gin), d.F, d.D, b.x, d.D, N(lw.norm2), d.eps, b.a, d.F, b0);
+      with_vpl<WT>(d.D, [&](auto v) {
+        k_gate<WT, decltype(v)::value, MOSHI_STAGE_GATE_IN><<<grid(d.F), BLOCK, d.D * 4, st>>>(
+            W(lw.gin), s->scale(lw.gin), d.F, d.D, b.x, d.D, N(lw.norm2), d.eps, b.a, d.F, b0);
+      });
     });
     run(MOSHI_STAGE_GATE_OUT, [&] {
-      k_gemv_residual<WT, 2, 4, MOSHI_STAGE_GATE_OUT><<<dim3(blocks_for(d.D, 2 * NWAVES), nb), BLOCK, d.F * 4, st>>>(
-          W(lw.gout), s->scale(lw.gout), d.D, d.F, b.a, d.F, b.x, d.D, b0);
+      with_vpl<WT>(d.F, [&](auto v) {
+        k_gemv<WT, 1, decltype(v)::value, true, MOSHI_STAGE_GATE_OUT><<<grid(d.D), BLOCK, d.F * 4, st>>>(
+            W(lw.gout), s->scale(lw.gout), d.D, d.F, b.a, d.F, b.x, d.D, b0);
+      });
     });
   }
+  int prev_parts = 1;
   if (!temporal_only) {
     const int AM = (1 + d.Q) * AM_MAX_BLOCKS;
-    // out_norm -> hidden, text head, greedy text token into tokens[0]
+    // out_norm -> hidden, text head; argmax partials in slot 0
+    const dim3 gt(blocks_for((d.Vt + 1) / 2, NWAVES, std::min(cap, AM_MAX_BLOCKS)), nb);
+    prev_parts = (int)gt.x;
     run(MOSHI_STAGE_TEXT_HEAD, [&] {
-      k_head_argmax<WT, 2, 4, MOSHI_STAGE_TEXT_HEAD>
-          <<<dim3(blocks_for(d.Vt, 2 * NWAVES, AM_MAX_BLOCKS), nb), BLOCK, d.D * 4, st>>>(
-              W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, b.x, d.D, N(s->out_norm), d.eps, b.hidden,
-              b.text_logits, d.Vt, b.am_part, AM, b.am_cnt, 1 + d.Q, b.tokens, 1 + d.Q, b0);
+      with_vpl<WT>(d.D, [&](auto v) {
+        k_head<WT, 2, decltype(v)::value, MOSHI_STAGE_TEXT_HEAD><<<gt, BLOCK, d.D * 4, st>>>(
+            W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, b.x, d.D, N(s->out_norm), d.eps, b.hidden,
+            b.text_logits, d.Vt, b.am_part, AM, b0);
+      });
     });
     // depformer_in[cb] . hidden for every codebook at once
     run(MOSHI_STAGE_DEP_IN, [&] {
-      k_gemv_store<WT, 2, 4, MOSHI_STAGE_DEP_IN>
-          <<<dim3(blocks_for((int64_t)d.Q * d.Dd, 2 * NWAVES), nb), BLOCK, d.D * 4, st>>>(
-              W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, b.hidden, d.D, b.din, d.Q * d.Dd, b0);
+      with_vpl<WT>(d.D, [&](auto v) {
+        k_gemv<WT, 2, decltype(v)::value, false, MOSHI_STAGE_DEP_IN><<<grid(d.Q * d.Dd / 2), BLOCK, d.D * 4, st>>>(
+            W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, b.hidden, d.D, b.din, d.Q * d.Dd, b0);
+      });
     });
     for (int cb = 0; cb < d.Q; ++cb) {
       const ET *table = cb == 0 ? E(s->dep_text_emb) : E(s->dep_emb[cb - 1]);
       for (int j = 0; j < d.Ld; ++j) {
         const LayerW &lw = s->dlayers[j][cb];
         run(MOSHI_STAGE_DEP_QKV, [&] {
-          k_dep_qkv<WT, ET, 2, 4><<<dim3(blocks_for(3 * d.Dd, 2 * NWAVES), nb), BLOCK, d.Dd * 4, st>>>(
-              d, b, W(lw.in), s->scale(lw.in), N(lw.norm1), table, j, cb, b0);
+          with_vpl<WT>(d.Dd, [&](auto v) {
+            k_dep_qkv<WT, ET, 2, decltype(v)::value><<<grid(3 * d.Dd / 2), BLOCK, d.Dd * 4, st>>>(
+                d, b, W(lw.in), s->scale(lw.in), N(lw.norm1), table, j, cb, prev_parts, b0);
+          });
         });
         run(MOSHI_STAGE_DEP_OUT, [&] {
-          k_dep_out<WT, 2, 4><<<dim3(blocks_for(d.Dd, 2 * NWAVES), nb), BLOCK, d.Dd * 4, st>>>(
-              d, b, W(lw.out), s->scale(lw.out), j, cb, b0);
+          with_vpl<WT>(d.Dd, [&](auto v) {
+            with_epl(d.hdd, [&](auto e) {
+              k_dep_out<WT, 2, decltype(v)::value, decltype(e)::value><<<grid(d.Dd / 2), BLOCK, d.Dd * 4, st>>>(
+                  d, b, W(lw.out), s->scale(lw.out), j, cb, b0);
+            });
+          });
         });
         run(MOSHI_STAGE_DEP_GATE_IN, [&] {
-          k_gate<WT, 4, MOSHI_STAGE_DEP_GATE_IN><<<dim3(blocks_for(d.Fd, NWAVES), nb), BLOCK, d.Dd * 4, st>>>(
-              W(lw.gin), s->scale(lw.gin), d.Fd, d.Dd, b.y, d.Dd, N(lw.norm2), d.eps, b.da, d.Fd, b0);
+          with_vpl<WT>(d.Dd, [&](auto v) {
+            k_gate<WT, decltype(v)::value, MOSHI_STAGE_DEP_GATE_IN><<<grid(d.Fd), BLOCK, d.Dd * 4, st>>>(
+                W(lw.gin), s->scale(lw.gin), d.Fd, d.Dd, b.y, d.Dd, N(lw.norm2), d.eps, b.da, d.Fd, b0);
+          });
         });
         run(MOSHI_STAGE_DEP_GATE_OUT, [&] {
-          k_gemv_residual<WT, 2, 4, MOSHI_STAGE_DEP_GATE_OUT>
-              <<<dim3(blocks_for(d.Dd, 2 * NWAVES), nb), BLOCK, d.Fd * 4, st>>>(
-                  W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, b.da, d.Fd, b.y, d.Dd, b0);
+          with_vpl<WT>(d.Fd, [&](auto v) {
+            k_gemv<WT, 2, decltype(v)::value, true, MOSHI_STAGE_DEP_GATE_OUT><<<grid(d.Dd / 2), BLOCK, d.Fd * 4, st>>>(
+                W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, b.da, d.Fd, b.y, d.Dd, b0);
+          });
         });
       }
+      const dim3 gh(blocks_for((d.Va + 1) / 2, NWAVES, std::min(cap, AM_MAX_BLOCKS)), nb);
+      prev_parts = (int)gh.x;
       run(MOSHI_STAGE_DEP_HEAD, [&] {
-        k_head_argmax<WT, 2, 4, MOSHI_STAGE_DEP_HEAD>
-            <<<dim3(blocks_for(d.Va, 2 * NWAVES, AM_MAX_BLOCKS), nb), BLOCK, d.Dd * 4, st>>>(
-                W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, b.y, d.Dd, nullptr, d.eps, nullptr,
-                b.audio_logits + (size_t)cb * d.Va, d.Q * d.Va, b.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS, AM,
-                b.am_cnt + 1 + cb, 1 + d.Q, b.tokens + 1 + cb, 1 + d.Q, b0);
+        with_vpl<WT>(d.Dd, [&](auto v) {
+          k_head<WT, 2, decltype(v)::value, MOSHI_STAGE_DEP_HEAD><<<gh, BLOCK, d.Dd * 4, st>>>(
+              W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, b.y, d.Dd, nullptr, d.eps, nullptr,
+              b.audio_logits + (size_t)cb * d.Va, d.Q * d.Va, b.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS, AM, b0);
+        });
       });
     }
   }
-  run(MOSHI_STAGE_FRAME_END, [&] { k_frame_end<<<nb, 64, 0, st>>>(d, b, b0, temporal_only ? 1 : 0, forced); });
+  run(MOSHI_STAGE_FRAME_END,
+      [&] { k_frame_end<<<nb, BLOCK, 0, st>>>(d, b, b0, temporal_only ? 1 : 0, forced, prev_parts); });
 }
 
 void enqueue_frame(moshi_state *s, int b0, int nb, bool temporal_only, const int32_t *user_dev,
@@ -465,6 +528,8 @@ moshi_status check_config(const moshi_config *c, std::string &why) {
   const int hd = c->d_model / c->n_heads;
   if (hd != 64 && hd != 128) return bad("temporal head_dim must be 64 or 128");
   if (c->dep_d_model % c->dep_heads) return bad("dep_d_model must be a multiple of dep_heads");
+  const int hdd = c->dep_d_model / c->dep_heads;
+  if (hdd != 16 && hdd != 32 && hdd != 64 && hdd != 128) return bad("depformer head_dim must be 16, 32, 64 or 128");
   for (int k : {c->d_model, c->ffn_hidden, c->dep_d_model, c->dep_ffn_hidden})
     if (k % 16 || k > 16384) return bad("linear input widths must be multiples of 16 and at most 16384");
   if (c->band < MOSHI_BAND_F32 || c->band > MOSHI_BAND_I8) return bad("unknown band");
@@ -516,7 +581,8 @@ moshi_status moshi_create(const moshi_config *cfg, void *hip_stream, moshi_state
   moshi_state *s = new moshi_state();
   s->cfg = *cfg;
   if (s->cfg.kv_capacity == 0) s->cfg.kv_capacity = s->cfg.context;
-  if (hipGetDevice(&s->device) != hipSuccess) {
+  if (hipGetDevice(&s->device) != hipSuccess ||
+      hipDeviceGetAttribute(&s->cus, hipDeviceAttributeMultiprocessorCount, s->device) != hipSuccess) {
     delete s;
     return MOSHI_EDEVICE;
   }
@@ -538,7 +604,7 @@ moshi_status moshi_create(const moshi_config *cfg, void *hip_stream, moshi_state
   d.Fd = cfg->dep_ffn_hidden;
   d.Q = cfg->dep_q;
   d.NS = 2 * d.Q + 1;
-  d.S = std::max(1, std::min(32, (d.cap + 127) / 128));
+  d.S = std::max(1, std::min(mk::ATTN_MAX_S, (d.cap + mk::ATTN_MIN_CHUNK - 1) / mk::ATTN_MIN_CHUNK));
   d.eps = cfg->rms_eps;
   s->h_offset.assign(d.B, 0);
   moshi_status st = MOSHI_OK;
@@ -909,17 +975,23 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
     }
   }
   auto launch = [&]() {
-    const dim3 grid(blocks_for(N, 2 * mk::NWAVES));
+    const dim3 grid(blocks_for((N + 1) / 2, mk::NWAVES, 1024));
     const float *sc = band == MOSHI_BAND_I8 ? ds : nullptr;
     if (band == MOSHI_BAND_F32)
-      mk::k_gemv_store<float, 2, 4, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const float *>(dw), sc, N, K, dx,
-                                                                     K, dy, N, 0);
+      with_vpl<float>(K, [&](auto v) {
+        mk::k_gemv<float, 2, decltype(v)::value, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(
+            reinterpret_cast<const float *>(dw), sc, N, K, dx, K, dy, N, 0);
+      });
     else if (band == MOSHI_BAND_BF16)
-      mk::k_gemv_store<bf16_t, 2, 4, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const bf16_t *>(dw), sc, N, K,
-                                                                      dx, K, dy, N, 0);
+      with_vpl<bf16_t>(K, [&](auto v) {
+        mk::k_gemv<bf16_t, 2, decltype(v)::value, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(
+            reinterpret_cast<const bf16_t *>(dw), sc, N, K, dx, K, dy, N, 0);
+      });
     else
-      mk::k_gemv_store<int8_t, 2, 4, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const int8_t *>(dw), sc, N, K,
-                                                                      dx, K, dy, N, 0);
+      with_vpl<int8_t>(K, [&](auto v) {
+        mk::k_gemv<int8_t, 2, decltype(v)::value, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(
+            reinterpret_cast<const int8_t *>(dw), sc, N, K, dx, K, dy, N, 0);
+      });
   };
   if (rc == MOSHI_OK) {
     launch();
