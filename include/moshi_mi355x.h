@@ -53,8 +53,12 @@ typedef enum { MOSHI_DTYPE_F32 = 0, MOSHI_DTYPE_BF16 = 1 } moshi_dtype;
 
 /* How a frame is issued to the GPU. */
 typedef enum {
-  MOSHI_EXEC_GRAPH = 0,  /* the whole frame is captured once into a hipGraph and replayed */
-  MOSHI_EXEC_STREAM = 1  /* kernels are launched one by one on the stream each frame */
+  MOSHI_EXEC_GRAPH = 0,      /* the whole frame is captured once into a hipGraph and replayed */
+  MOSHI_EXEC_STREAM = 1,     /* kernels are launched one by one on the stream each frame */
+  MOSHI_EXEC_PERSISTENT = 2  /* one cooperative kernel per frame, one block per CU, phases chained
+                                by device-side completion counters (batch 1; shapes with a compiled
+                                variant, else moshi_create returns MOSHI_EINVAL).  Teacher-forced
+                                prefill still runs as stream launches. */
 } moshi_exec;
 
 /*
@@ -192,6 +196,18 @@ moshi_status moshi_read_trace(moshi_state *s, int32_t conv, const moshi_trace *t
  * moshi_frame_step.  All arrays are host int32. */
 moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const int32_t *text,
                                   const int32_t *agent, const int32_t *user);
+
+/* GPU time of frames: with enable >= 0 the per-frame HIP event pair around the frame's device
+ * work (graph replay or persistent kernel, recorded on the session stream) is switched on (1)
+ * or off (0) and the totals are cleared; with enable < 0 nothing changes.  *total_us and *frames
+ * (optional) receive the totals since the last clear. */
+moshi_status moshi_gpu_time(moshi_state *s, int32_t enable, double *total_us, int64_t *frames);
+
+/* Measurement (persistent executor): with enable = 1 the following frames record, per phase, the
+ * device wall-clock time at which block 0 finished its share and at which the phase completed;
+ * ts [max_phases][2] (host, optional) receives the last frame's record in microseconds from the
+ * frame's first arrival, *n_phases the phase count.  enable = 0 switches it off. */
+moshi_status moshi_phase_times(moshi_state *s, int32_t enable, double *ts, int32_t max_phases, int32_t *n_phases);
 
 /* Bytes of linear weights (what one frame must stream) and of all device weights. */
 moshi_status moshi_weight_bytes(const moshi_state *s, int64_t *linear_bytes, int64_t *all_bytes);

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libmoshi_mi355x.so")
 MOSHI_OK, MOSHI_NONE = 0, 1
 MOSHI_EINVAL, MOSHI_ESTATE, MOSHI_ESHAPE, MOSHI_ENOMEM, MOSHI_EDEVICE, MOSHI_ERANGE = -1, -2, -3, -4, -5, -6
 BANDS = {"f32": 0, "bf16": 1, "i8": 2}
-EXEC = {"graph": 0, "stream": 1}
+EXEC = {"graph": 0, "stream": 1, "persistent": 2}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # every function the header declares, with (restype, argtypes)
@@ -38,6 +38,8 @@ _SIGS = {
     "moshi_stream": (_vp, [_vp]),
     "moshi_debug_gemv": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
     "moshi_profile_frames": (_i32, [_vp, _i32, _vp, _vp, _vp]),
+    "moshi_gpu_time": (_i32, [_vp, _i32, _vp, _vp]),
+    "moshi_phase_times": (_i32, [_vp, _i32, _vp, _i32, _vp]),
 }
 
 STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv", "dep_out",
@@ -224,6 +226,23 @@ class Session:
         n = np.zeros(len(STAGES), np.int64)
         self._check(self.lib.moshi_profile_frames(self.h, len(u), _ptr(u), _ptr(us), _ptr(n)), "moshi_profile_frames")
         return {name: (int(n[i]), float(us[i])) for i, name in enumerate(STAGES)}
+
+    def gpu_time(self, enable: int = -1):
+        """Totals of the per-frame HIP-event GPU time (us, frames) since the last clear; enable 1/0
+        switches the timing on/off and clears, -1 only reads."""
+        us, n = ctypes.c_double(), ctypes.c_int64()
+        self._check(self.lib.moshi_gpu_time(self.h, enable, ctypes.byref(us), ctypes.byref(n)), "moshi_gpu_time")
+        return us.value, n.value
+
+    def phase_times(self, enable: int = -1):
+        """Persistent executor: per-phase [block-0 arrival, completion] times (us) of the last
+        frame; enable 1/0 switches the recording on/off."""
+        n = ctypes.c_int32()
+        self._check(self.lib.moshi_phase_times(self.h, -1, None, 0, ctypes.byref(n)), "moshi_phase_times")
+        ts = np.zeros((n.value, 2), np.float64)
+        self._check(self.lib.moshi_phase_times(self.h, enable, _ptr(ts), n.value, ctypes.byref(n)),
+                    "moshi_phase_times")
+        return ts
 
     @property
     def stream(self) -> int:

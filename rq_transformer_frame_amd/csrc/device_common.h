@@ -48,24 +48,26 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Block-wide sum: each wave's lane-0 sum goes to LDS, then every thread adds the wave sums in
 // the same order, so all threads hold the same value.
+template <int NT = BLOCK>
 __device__ __forceinline__ float block_sum(float v, float *red) {
   v = wave_sum(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float t = 0.f;
 #pragma unroll
-  for (int i = 0; i < NWAVES; ++i) t += red[i];
+  for (int i = 0; i < NT / WAVE; ++i) t += red[i];
   __syncthreads();
   return t;
 }
 
+template <int NT = BLOCK>
 __device__ __forceinline__ float block_max(float v, float *red) {
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
   float t = red[0];
 #pragma unroll
-  for (int i = 1; i < NWAVES; ++i) t = fmaxf(t, red[i]);
+  for (int i = 1; i < NT / WAVE; ++i) t = fmaxf(t, red[i]);
   __syncthreads();
   return t;
 }
@@ -274,28 +276,56 @@ __device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" :
 // per BLOCK floats).  K is a multiple of 4 and src is 16-byte aligned.
 constexpr int STAGE_UNR = 8;
 
-// xs[k] = src[k] for k < K; returns this thread's partial sum of squares.  No barrier.
+// xs[k] = src[k] for k < K; returns this thread's partial sum of squares.  No barrier.  With SYS
+// the source is read with system-scope 8-byte loads (data another block of the same kernel wrote),
+// U loads per thread in flight per pass.
+template <int NT = BLOCK, bool SYS = false, int U = 2 * STAGE_UNR>
 __device__ __forceinline__ float stage_copy(const float *__restrict__ src, int K, float *xs) {
-  const int K4 = K >> 2;
-  const float4 *s4 = reinterpret_cast<const float4 *>(src);
-  float4 *x4 = reinterpret_cast<float4 *>(xs);
   float ss = 0.f;
-  for (int base = 0; base < K4; base += STAGE_UNR * BLOCK) {
-    float4 v[STAGE_UNR];
+  if (!SYS) {
+    const int K4 = K >> 2;
+    const float4 *s4 = reinterpret_cast<const float4 *>(src);
+    float4 *x4 = reinterpret_cast<float4 *>(xs);
+    for (int base = 0; base < K4; base += STAGE_UNR * NT) {
+      float4 v[STAGE_UNR];
 #pragma unroll
-    for (int u = 0; u < STAGE_UNR; ++u) {
-      const int i = base + u * BLOCK + threadIdx.x;
-      v[u] = i < K4 ? s4[i] : float4{0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < STAGE_UNR; ++u) {
+        const int i = base + u * NT + threadIdx.x;
+        v[u] = i < K4 ? s4[i] : float4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < STAGE_UNR; ++u) {
+        const int i = base + u * NT + threadIdx.x;
+        if (i < K4) {
+          x4[i] = v[u];
+          ss = fmaf(v[u].x, v[u].x, ss);
+          ss = fmaf(v[u].y, v[u].y, ss);
+          ss = fmaf(v[u].z, v[u].z, ss);
+          ss = fmaf(v[u].w, v[u].w, ss);
+        }
+      }
     }
+  } else {
+    const int K2 = K >> 1;
+    const uint64_t *s2 = reinterpret_cast<const uint64_t *>(src);
+    for (int base = 0; base < K2; base += U * NT) {
+      uint64_t v[U];
 #pragma unroll
-    for (int u = 0; u < STAGE_UNR; ++u) {
-      const int i = base + u * BLOCK + threadIdx.x;
-      if (i < K4) {
-        x4[i] = v[u];
-        ss = fmaf(v[u].x, v[u].x, ss);
-        ss = fmaf(v[u].y, v[u].y, ss);
-        ss = fmaf(v[u].z, v[u].z, ss);
-        ss = fmaf(v[u].w, v[u].w, ss);
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * NT + threadIdx.x;
+        v[u] = i < K2 ? __hip_atomic_load(const_cast<uint64_t *>(s2 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                      : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = base + u * NT + threadIdx.x;
+        if (i < K2) {
+          const float a = __uint_as_float((uint32_t)v[u]), b = __uint_as_float((uint32_t)(v[u] >> 32));
+          xs[2 * i] = a;
+          xs[2 * i + 1] = b;
+          ss = fmaf(a, a, ss);
+          ss = fmaf(b, b, ss);
+        }
       }
     }
   }
@@ -303,27 +333,30 @@ __device__ __forceinline__ float stage_copy(const float *__restrict__ src, int K
 }
 
 // xs[k] = src[k] for k < K, then a barrier.
+template <int NT = BLOCK, bool SYS = false, int U = 2 * STAGE_UNR>
 __device__ __forceinline__ void stage_vec(const float *__restrict__ src, int K, float *xs) {
-  (void)stage_copy(src, K, xs);
+  (void)stage_copy<NT, SYS, U>(src, K, xs);
   __syncthreads();
 }
 
 // xs = rms_norm(src; alpha): y = x * alpha * 1/sqrt(eps + mean(x^2)) (eps inside the mean).
+template <int NT = BLOCK, bool SYS = false, int U = 2 * STAGE_UNR>
 __device__ __forceinline__ void stage_rms(const float *__restrict__ src, const float *__restrict__ alpha, int K,
                                           float eps, float *xs, float *red) {
-  const float tot = block_sum(stage_copy(src, K, xs), red);  // block_sum's barriers publish xs
+  const float tot = block_sum<NT>(stage_copy<NT, SYS, U>(src, K, xs), red);  // block_sum's barriers publish xs
   const float inv = 1.0f / sqrtf(eps + tot / (float)K);
-  for (int k = threadIdx.x; k < K; k += BLOCK) xs[k] = (xs[k] * alpha[k]) * inv;
+  for (int k = threadIdx.x; k < K; k += NT) xs[k] = (xs[k] * alpha[k]) * inv;
   __syncthreads();
 }
 
 // In-place rms_norm of xs[0..K) already staged in LDS.
+template <int NT = BLOCK>
 __device__ __forceinline__ void rms_in_place(float *xs, const float *__restrict__ alpha, int K, float eps, float *red) {
   float ss = 0.f;
-  for (int k = threadIdx.x; k < K; k += BLOCK) ss = fmaf(xs[k], xs[k], ss);
-  const float tot = block_sum(ss, red);
+  for (int k = threadIdx.x; k < K; k += NT) ss = fmaf(xs[k], xs[k], ss);
+  const float tot = block_sum<NT>(ss, red);
   const float inv = 1.0f / sqrtf(eps + tot / (float)K);
-  for (int k = threadIdx.x; k < K; k += BLOCK) xs[k] = (xs[k] * alpha[k]) * inv;
+  for (int k = threadIdx.x; k < K; k += NT) xs[k] = (xs[k] * alpha[k]) * inv;
   __syncthreads();
 }
 

@@ -1,0 +1,870 @@
+// Persistent frame kernel: one cooperative launch runs a whole B=1 frame of the Moshi
+// RQ-Transformer ([LM]: the docs.rs page "inferencelayer 0.2.4 src/moshi_lm.rs", MoshiLm::step_ext)
+// as a chain of phases, one block per CU.
+//
+// Every phase is a weight-streaming projection (or the temporal attention) spread over all waves
+// of the grid.  Phase p+1's first weight tile is loaded into registers BEFORE the block waits for
+// phase p to complete, so HBM keeps streaming across phase boundaries and the wait is hidden
+// behind the fetch.  Completion of a phase is counted in 8 arrival counters (one per XCD slot, 64 B
+// apart); a waiter sums them.  Activations that other blocks read (x, q, o, a, y, dq, dkv, ...) are
+// written with system-scope stores (write-through past the per-XCD L2) after which the writer
+// waits for its stores (s_waitcnt) before it arrives, and are read with system-scope loads.  Every
+// wait is a bounded spin: on timeout the block raises the error flag and the whole grid exits.
+#pragma once
+#include "kernels.h"
+
+namespace mk {
+
+constexpr int PBLOCK = 512;
+constexpr int PWAVES = PBLOCK / WAVE;
+constexpr int SYNC_SLOTS = 8;
+constexpr int SYNC_STRIDE = 16;  // uint32 per counter slot (64 bytes)
+constexpr int PQ = 8;                // most depformer steps (dep_q) the persistent kernel takes
+constexpr int PSTREAMS = 2 * PQ + 1; // most token streams
+
+struct LayerPtrs {
+  const void *w_in, *w_out, *w_gin, *w_gout;
+  const float *s_in, *s_out, *s_gin, *s_gout;
+  const float *norm1, *norm2;
+};
+
+struct PArgs {
+  Dims d;
+  Bufs s;
+  void *kc, *vc;
+  const void *emb_audio, *emb_text;
+  const LayerPtrs *tl;  // [L]
+  const LayerPtrs *dl;  // [Ld][Q]
+  const float *out_norm;
+  const void *w_text;
+  const float *s_text;
+  const void *w_din;  // [Q * Dd][D]
+  const float *s_din;
+  const void *dep_table[PQ];  // cb 0: depformer text table, cb > 0: depformer_emb[cb - 1]
+  const void *w_lin[PQ];
+  const float *s_lin[PQ];
+  uint32_t *sync;  // [phases][SYNC_SLOTS * SYNC_STRIDE]
+  int *err;        // error flag (also copied back to the host with the outputs)
+  int spin_limit;
+  uint64_t *phase_ts;  // optional [phases][2]: block 0's arrival and the phase's completion time
+};
+
+// Four consecutive table values as one load (8 bytes of bf16 or 16 bytes of float), widened to
+// float32 only when summed.
+template <typename ET> struct Packed4;
+template <> struct Packed4<bf16_t> {
+  typedef uint2 type;
+  __device__ __forceinline__ static void unpack(const uint2 &u, float *f) {
+    f[0] = __uint_as_float(u.x << 16);
+    f[1] = __uint_as_float(u.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(u.y << 16);
+    f[3] = __uint_as_float(u.y & 0xFFFF0000u);
+  }
+};
+template <> struct Packed4<float> {
+  typedef float4 type;
+  __device__ __forceinline__ static void unpack(const float4 &u, float *f) {
+    f[0] = u.x;
+    f[1] = u.y;
+    f[2] = u.z;
+    f[3] = u.w;
+  }
+};
+
+__device__ __forceinline__ void st_sys_u32(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void st_sys_u64(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ uint64_t ld_sys_u64(const uint64_t *p) {
+  return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+template <typename KT> __device__ __forceinline__ void st_sys_pair(KT *p, float a, float b);
+template <> __device__ __forceinline__ void st_sys_pair<float>(float *p, float a, float b) {
+  st_sys_u64(reinterpret_cast<uint64_t *>(p), (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32));
+}
+template <> __device__ __forceinline__ void st_sys_pair<bf16_t>(bf16_t *p, float a, float b) {
+  st_sys_u32(reinterpret_cast<uint32_t *>(p), (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16));
+}
+
+__device__ __forceinline__ void st_sys_arg(ArgBest *p, ArgBest v) {
+  st_sys_u64(reinterpret_cast<uint64_t *>(p), (uint64_t)__float_as_uint(v.v) | ((uint64_t)(uint32_t)v.i << 32));
+}
+__device__ __forceinline__ ArgBest ld_sys_arg(const ArgBest *p) {
+  const uint64_t u = ld_sys_u64(reinterpret_cast<const uint64_t *>(p));
+  return ArgBest{__uint_as_float((uint32_t)u), (int)(uint32_t)(u >> 32)};
+}
+
+// Stage two vectors written by other blocks (system-scope 8-byte loads; per pass U1 and U2 loads
+// per thread are issued before any LDS store): dst1[0..K1) = src1, dst2[0..K2) = src2 (K even).
+template <int U1, int U2>
+__device__ __forceinline__ void stage2_sys(const float *src1, int K1, float *dst1, const float *src2, int K2,
+                                           float *dst2) {
+  const uint64_t *a1 = reinterpret_cast<const uint64_t *>(src1);
+  const uint64_t *a2 = reinterpret_cast<const uint64_t *>(src2);
+  const int n1 = K1 >> 1, n2 = K2 >> 1;
+  for (int b1 = 0, b2 = 0; b1 < n1 || b2 < n2; b1 += U1 * PBLOCK, b2 += U2 * PBLOCK) {
+    uint64_t v1[U1], v2[U2];
+#pragma unroll
+    for (int u = 0; u < U1; ++u) {
+      const int i = b1 + u * PBLOCK + threadIdx.x;
+      v1[u] = i < n1 ? ld_sys_u64(a1 + i) : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int i = b2 + u * PBLOCK + threadIdx.x;
+      v2[u] = i < n2 ? ld_sys_u64(a2 + i) : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < U1; ++u) {
+      const int i = b1 + u * PBLOCK + threadIdx.x;
+      if (i < n1) {
+        dst1[2 * i] = __uint_as_float((uint32_t)v1[u]);
+        dst1[2 * i + 1] = __uint_as_float((uint32_t)(v1[u] >> 32));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U2; ++u) {
+      const int i = b2 + u * PBLOCK + threadIdx.x;
+      if (i < n2) {
+        dst2[2 * i] = __uint_as_float((uint32_t)v2[u]);
+        dst2[2 * i + 1] = __uint_as_float((uint32_t)(v2[u] >> 32));
+      }
+    }
+  }
+  __syncthreads();
+}
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+// Per-thread 8-byte loads that stage an input of the longest width a register tile of VPL
+// 16-byte vectors per lane covers (tile width bounds the input length): one pass in the usual
+// case, more passes for the generic tile (VPL 0).
+template <typename WT, int VPL>
+constexpr int stage_u() {
+  return VPL == 0 ? 4 : (VPL * WAVE * (16 / (int)sizeof(WT)) / 2 + PBLOCK - 1) / PBLOCK;
+}
+
+// ---- phase completion ------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t *phase_ctr(const PArgs &a, int p) {
+  return a.sync + (size_t)p * SYNC_SLOTS * SYNC_STRIDE;
+}
+
+// All of this block's stores of the phase are complete (s_waitcnt in every thread, then the
+// barrier); then one arrival is counted.
+__device__ __forceinline__ void p_arrive(const PArgs &a, int p) {
+  wait_mem();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(phase_ctr(a, p) + (blockIdx.x % SYNC_SLOTS) * SYNC_STRIDE, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (a.phase_ts && blockIdx.x == 0) a.phase_ts[2 * p] = wall_clock64();
+  }
+}
+
+// Wait until every block has arrived at phase p.  Returns false (and raises the error flag) if
+// the error flag is up or the spin limit is reached: the caller then leaves the kernel.
+__device__ __forceinline__ bool p_wait(const PArgs &a, int p, int *s_ok) {
+  if (threadIdx.x < WAVE) {
+    const int lane = threadIdx.x;
+    const uint32_t *c = phase_ctr(a, p);
+    const uint32_t target = gridDim.x;
+    int ok = 1;
+    for (int spins = 0;; ++spins) {
+      uint32_t v = lane < SYNC_SLOTS
+                       ? __hip_atomic_load(const_cast<uint32_t *>(c + lane * SYNC_STRIDE), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT)
+                       : 0u;
+      v += __shfl_xor(v, 1, WAVE);
+      v += __shfl_xor(v, 2, WAVE);
+      v += __shfl_xor(v, 4, WAVE);
+      v = __shfl(v, 0, WAVE);
+      if (v >= target) break;
+      int e = lane == 0 ? __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      e = __shfl(e, 0, WAVE);
+      if (e != 0 || spins >= a.spin_limit) {
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (lane == 0) {
+      if (!ok) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_ok = ok;
+      if (a.phase_ts && blockIdx.x == 0) a.phase_ts[2 * p + 1] = wall_clock64();
+    }
+  }
+  __syncthreads();
+  return *s_ok != 0;
+}
+
+// ---- one register tile shared by every phase ---------------------------------------------------
+// T 16-byte vectors per lane; a phase views it as R rows of VPL vectors (R * VPL <= T).  Sharing one
+// buffer keeps a single tile's worth of registers live across the whole kernel.
+template <int T>
+struct TileBuf {
+  uint4 w[T];
+};
+
+template <typename WT, int R, int VPL, int T>
+__device__ __forceinline__ void tile_load(TileBuf<T> &t, const WT *__restrict__ W, int K, const int *rows) {
+  static_assert(R * VPL <= T, "tile view larger than the buffer");
+  constexpr int N = WVec<WT>::N;
+  const int lane = threadIdx.x & 63;
+  const int nv = K / N;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(W + (size_t)rows[r] * K);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int v = lane + WAVE * i;
+      t.w[r * VPL + i] = v < nv ? ld_stream(p + v) : uint4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <typename WT, int R, int VPL, int T>
+__device__ __forceinline__ void tile_dot(const TileBuf<T> &t, int K, const float *__restrict__ xs, float *acc) {
+  constexpr int N = WVec<WT>::N;
+  const int lane = threadIdx.x & 63;
+  const int nv = K / N;
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int v = lane + WAVE * i;
+    if (v < nv) {
+      const float *xp = xs + (size_t)v * N;
+      float xv[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) xv[e] = xp[e];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float wf[N];
+        WVec<WT>::cvt(t.w[r * VPL + i], wf);
+#pragma unroll
+        for (int e = 0; e < N; ++e) acc[r] = fmaf(wf[e], xv[e], acc[r]);
+      }
+    }
+  }
+}
+
+// ---- row phases --------------------------------------------------------------------------------
+// Global wave index and count of the persistent grid.
+__device__ __forceinline__ int gwave() { return blockIdx.x * PWAVES + (threadIdx.x >> 6); }
+__device__ __forceinline__ int nwaves() { return gridDim.x * PWAVES; }
+
+// Row group gi of a plain projection: rows gi*R .. gi*R+R-1 (clamped).
+template <int R>
+__device__ __forceinline__ void plain_rows(int gi, int N, int *rows) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, N - 1);
+}
+// Row group j of a gated projection: rows j (gate) and F + j (mult).
+__device__ __forceinline__ void gate_rows(int j, int F, int *rows) {
+  const int jj = min(j, F - 1);
+  rows[0] = jj;
+  rows[1] = F + jj;
+}
+
+template <typename WT, int R, int VPL, int T>
+__device__ __forceinline__ void prefetch_plain(const WT *W, int N, int K, TileBuf<T> &t) {
+  const int gi = gwave();
+  if (gi < (N + R - 1) / R) {
+    int rows[R];
+    plain_rows<R>(gi, N, rows);
+    tile_load<WT, R, VPL>(t, W, K, rows);
+  }
+}
+template <typename WT, int VPL, int T>
+__device__ __forceinline__ void prefetch_gate(const WT *W, int F, int K, TileBuf<T> &t) {
+  const int j = gwave();
+  if (j < F) {
+    int rows[2];
+    gate_rows(j, F, rows);
+    tile_load<WT, 2, VPL>(t, W, K, rows);
+  }
+}
+
+// Run the plain projection rows of this wave against xs; the first tile is already in t.
+// epi(row, value) runs in lane 0 of the owning wave.
+template <typename WT, int R, int VPL, int T, typename Epi>
+__device__ __forceinline__ void run_plain(const WT *W, const float *wscale, int N, int K, const float *xs,
+                                          TileBuf<T> &t, Epi &&epi) {
+  const int lane = threadIdx.x & 63, TW = nwaves();
+  const int ng = (N + R - 1) / R;
+  for (int gi = gwave(); gi < ng; gi += TW) {
+    float acc[R];
+    tile_dot<WT, R, VPL>(t, K, xs, acc);
+    if (gi + TW < ng) {
+      int nr[R];
+      plain_rows<R>(gi + TW, N, nr);
+      tile_load<WT, R, VPL>(t, W, K, nr);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float v = wave_sum(acc[r]);
+      const int row = gi * R + r;
+      if (lane == 0 && row < N) {
+        if (wscale) v *= wscale[row];
+        epi(row, v);
+      }
+    }
+  }
+}
+
+// Gated projection: a[j] = silu(g_j) * m_j for this wave's pairs (j, F + j).
+template <typename WT, int VPL, int T>
+__device__ __forceinline__ void run_gate(const WT *W, const float *wscale, int F, int K, const float *xs,
+                                         TileBuf<T> &t, float *a_out) {
+  const int lane = threadIdx.x & 63, TW = nwaves();
+  for (int j = gwave(); j < F; j += TW) {
+    float acc[2];
+    tile_dot<WT, 2, VPL>(t, K, xs, acc);
+    if (j + TW < F) {
+      int nr[2];
+      gate_rows(j + TW, F, nr);
+      tile_load<WT, 2, VPL>(t, W, K, nr);
+    }
+    float gv = wave_sum(acc[0]), mv = wave_sum(acc[1]);
+    if (lane == 0) {
+      if (wscale) {
+        gv *= wscale[j];
+        mv *= wscale[F + j];
+      }
+      st_sys(a_out + j, silu(gv) * mv);
+    }
+  }
+}
+
+// Block-wide first-wins merge of the waves' best rows (lane 0 of each wave holds its best).
+__device__ __forceinline__ ArgBest block_arg(ArgBest best, ArgBest *wb) {
+  if ((threadIdx.x & 63) == 0) wb[threadIdx.x >> 6] = best;
+  __syncthreads();
+  ArgBest t = wb[0];
+#pragma unroll
+  for (int i = 1; i < PWAVES; ++i) t = arg_merge(t, wb[i]);
+  __syncthreads();
+  return t;
+}
+
+// Merge the per-block partials of one head (system-scope loads) into its token.
+__device__ __forceinline__ int merge_head(const ArgBest *part, int n, ArgBest *wb) {
+  ArgBest bb = arg_none();
+  for (int i = threadIdx.x; i < n; i += PBLOCK) bb = arg_merge(bb, ld_sys_arg(part + i));
+  bb = wave_arg(bb);
+  const ArgBest t = block_arg(bb, wb);
+  return t.i < 0 ? 0 : t.i;
+}
+
+// ---- the frame ---------------------------------------------------------------------------------
+// Template: weight / embedding / KV storage types, temporal head dim, depformer dims per lane
+// (head_dim / 16) and the register-tile widths for inputs of width D, F, Dd and Fd.
+// The arguments live in device memory (written once per session): reading them where they are
+// used keeps the ~150 dwords of pointers and sizes out of the registers of every phase.
+template <typename WT, typename ET, typename KT, int HD, int DEPL, int VD, int VF, int VDd, int VFd>
+__global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__restrict__ pa) {
+  const PArgs &a = *pa;
+  extern __shared__ float xs[];  // max(D, F, Dd, Fd) floats; the attention phase reuses it
+  __shared__ float red[PWAVES];
+  __shared__ ArgBest wb[PWAVES];
+  __shared__ int tok[PSTREAMS];
+  __shared__ float rcs[HD];  // rope cos, sin of this frame's position, pair i at [2i], [2i+1]
+  __shared__ float ored[PWAVES][HD];
+  __shared__ int s_ok, s_last;
+  const Dims &d = a.d;
+  const Bufs &s = a.s;
+  KT *kc = reinterpret_cast<KT *>(a.kc);
+  KT *vc = reinterpret_cast<KT *>(a.vc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t pos = s.offset[0];
+  const int slot = (int)(pos % d.cap);
+  const int NPT = 5 * d.L;  // temporal phases
+  const int P_HEAD = NPT;
+
+  // ---- a1-a3: gather (every block), user ring write (block 0), embedding sum (every block) ----
+  if (threadIdx.x < d.NS) {
+    const int st = threadIdx.x;
+    const int delay = stream_delay(st, d.Q);
+    int v;
+    if (pos <= delay)
+      v = (st == 0) ? d.Vt : d.Va;
+    else if (st >= d.Q + 1 && delay == 0)
+      v = s.user[st - d.Q - 1];
+    else
+      v = s.ring[st * 3 + (int)(pos % 3)];
+    tok[st] = v;
+  }
+  if (threadIdx.x < HD / 2) {  // rope angle f_i * pos formed in float32, sin/cos in double
+    const float ang = s.rope_freq[threadIdx.x] * (float)pos;
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    rcs[2 * threadIdx.x] = (float)cd;
+    rcs[2 * threadIdx.x + 1] = (float)sd;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x < d.NS) {
+    const int st = threadIdx.x;
+    s.inputs[st] = tok[st];
+    if (st >= d.Q + 1) s.ring[st * 3 + (int)((pos + stream_delay(st, d.Q)) % 3)] = s.user[st - d.Q - 1];
+  }
+  {
+    // four consecutive columns per thread and load; all rows of a column group are loaded before
+    // the sum, which runs in the stream order (audio tables, then text)
+    const ET *ea = reinterpret_cast<const ET *>(a.emb_audio);
+    const ET *et = reinterpret_cast<const ET *>(a.emb_text);
+    for (int c = 4 * threadIdx.x; c < d.D; c += 4 * PBLOCK) {
+      typename Packed4<ET>::type raw[PSTREAMS];
+#pragma unroll
+      for (int k = 0; k < PSTREAMS; ++k)
+        if (k < d.NS) {
+          const int t = tok[k];
+          const int row = t < 0 ? 0 : t;
+          const ET *src = k == 0 ? et + (size_t)row * d.D + c : ea + ((size_t)(k - 1) * (d.Va + 1) + row) * d.D + c;
+          raw[k] = *reinterpret_cast<const typename Packed4<ET>::type *>(src);
+        }
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 1; k < PSTREAMS; ++k)
+        if (k < d.NS && tok[k] != -1) {
+          float f[4];
+          Packed4<ET>::unpack(raw[k], f);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += f[e];
+        }
+      if (tok[0] != -1) {
+        float f[4];
+        Packed4<ET>::unpack(raw[0], f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += f[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xs[c + e] = acc[e];
+        if (blockIdx.x == 0) {
+          st_sys(s.x + c + e, acc[e]);
+          s.emb_sum[c + e] = acc[e];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  const WT *Wt;
+  constexpr int UD = stage_u<WT, VD>(), UF = stage_u<WT, VF>(), UDd = stage_u<WT, VDd>(), UFd = stage_u<WT, VFd>();
+  // one register tile for every phase: views R=2 x VD (qkv, out_proj, gate_in, text head,
+  // dep_in), R=1 x VF (gate_out), R=2 x VDd (depformer qkv, out, gate_in, heads), R=2 x VFd
+  // (depformer gate_out)
+  constexpr int TT = cmax(cmax(2 * VD, VF), cmax(2 * VDd, 2 * VFd));
+  TileBuf<TT> tD;
+  TileBuf<TT> &tF = tD, &tS = tD, &tT = tD;
+  prefetch_plain<WT, 2, VD>(reinterpret_cast<const WT *>(a.tl[0].w_in), 3 * d.D, d.D, tD);
+
+  // ---- a4-a5: temporal layers ----
+  for (int l = 0; l < d.L; ++l) {
+    const LayerPtrs lp = a.tl[l];
+    const int P = 5 * l;
+    // qkv + rope + KV append
+    if (l == 0)
+      rms_in_place<PBLOCK>(xs, lp.norm1, d.D, d.eps, red);
+    else
+      stage_rms<PBLOCK, true, UD>(s.x, lp.norm1, d.D, d.eps, xs, red);
+    Wt = reinterpret_cast<const WT *>(lp.w_in);
+    {
+      const int TW = nwaves();
+      const int npairs = 3 * d.D / 2;
+      for (int pr = gwave(); pr < npairs; pr += TW) {
+        float acc[2];
+        tile_dot<WT, 2, VD>(tD, d.D, xs, acc);
+        if (pr + TW < npairs) {
+          const int nr[2] = {2 * (pr + TW), 2 * (pr + TW) + 1};
+          tile_load<WT, 2, VD>(tD, Wt, d.D, nr);
+        }
+        acc[0] = wave_sum(acc[0]);
+        acc[1] = wave_sum(acc[1]);
+        if (lane == 0) {
+          const int r0 = 2 * pr;
+          float v0 = acc[0], v1 = acc[1];
+          if (lp.s_in) {
+            v0 *= lp.s_in[r0];
+            v1 *= lp.s_in[r0 + 1];
+          }
+          const int part = r0 / d.D;
+          const int rr = r0 - part * d.D;
+          const int h = rr / HD, e = rr - h * HD;
+          if (part < 2) {
+            const float cs = rcs[e], sn = rcs[e + 1];
+            const float a0 = v0 * cs - v1 * sn;
+            const float a1 = v0 * sn + v1 * cs;
+            v0 = a0;
+            v1 = a1;
+          }
+          if (part == 0) {
+            st_sys_u64(reinterpret_cast<uint64_t *>(s.q + rr),
+                       (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32));
+          } else {
+            KT *cache = part == 1 ? kc : vc;
+            st_sys_pair<KT>(cache + ((((size_t)l * d.H + h) * d.cap + slot) * HD + e), v0, v1);
+          }
+        }
+      }
+    }
+    p_arrive(a, P);
+    prefetch_plain<WT, 2, VD>(reinterpret_cast<const WT *>(lp.w_out), d.D, d.D, tD);  // out_proj, after attention
+    if (!p_wait(a, P, &s_ok)) return;
+
+    // attention: block bi < H * S takes head bi % H, split bi / H
+    {
+      const int n = (int)(pos + 1 < (int64_t)d.C ? pos + 1 : (int64_t)d.C);
+      const int S = min(ATTN_MAX_S, max(1, (n + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK));
+      const int bi = blockIdx.x;
+      if (bi < d.H * S) {
+        constexpr int EPL = HD / 16;
+        const int h = bi % d.H, sp = bi / d.H;
+        const int g = lane >> 4, sub = lane & 15;
+        const int chunk = (n + S - 1) / S;
+        const int j0 = sp * chunk, j1 = min(n, j0 + chunk);
+        const int len = j1 > j0 ? j1 - j0 : 0;
+        float *sc = xs;  // scores
+        float qv[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) qv[i] = ld_sys(s.q + h * HD + sub * EPL + i);
+        const float scale = 1.0f / sqrtf((float)HD);
+        const size_t base = ((size_t)l * d.H + h) * (size_t)d.cap * HD;
+        const KT *kb = kc + base, *vb = vc + base;
+        for (int jb = j0 + wave * 4; jb < j1; jb += PWAVES * 4) {
+          const int j = jb + g;
+          const bool ok = j < j1;
+          float dot = 0.f;
+          if (ok) {
+            const KT *kp = kb + (size_t)j * HD + sub * EPL;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], to_f(kp[i]), dot);
+          }
+          dot += __shfl_xor(dot, 8, WAVE);
+          dot += __shfl_xor(dot, 4, WAVE);
+          dot += __shfl_xor(dot, 2, WAVE);
+          dot += __shfl_xor(dot, 1, WAVE);
+          if (ok && sub == 0) sc[j - j0] = dot * scale;
+        }
+        __syncthreads();
+        float m = -INFINITY;
+        for (int t = threadIdx.x; t < len; t += PBLOCK) m = fmaxf(m, sc[t]);
+        m = block_max<PBLOCK>(m, red);
+        float lsum = 0.f;
+        for (int t = threadIdx.x; t < len; t += PBLOCK) {
+          const float e = expf(sc[t] - m);
+          sc[t] = e;
+          lsum += e;
+        }
+        lsum = block_sum<PBLOCK>(lsum, red);
+        float op[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) op[i] = 0.f;
+        for (int jb = j0 + wave * 4; jb < j1; jb += PWAVES * 4) {
+          const int j = jb + g;
+          if (j < j1) {
+            const float e = sc[j - j0];
+            const KT *vp = vb + (size_t)j * HD + sub * EPL;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) op[i] = fmaf(e, to_f(vp[i]), op[i]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          op[i] += __shfl_xor(op[i], 16, WAVE);
+          op[i] += __shfl_xor(op[i], 32, WAVE);
+        }
+        if (g == 0) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) ored[wave][sub * EPL + i] = op[i];
+        }
+        __syncthreads();
+        if (S == 1) {
+          for (int t = threadIdx.x; t < HD; t += PBLOCK) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < PWAVES; ++w2) acc += ored[w2][t];
+            st_sys(s.o + h * HD + t, acc / lsum);
+          }
+        } else {
+          float *part = s.attn_part + ((size_t)h * ATTN_MAX_S + sp) * (HD + 2);
+          for (int t = threadIdx.x; t < HD; t += PBLOCK) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < PWAVES; ++w2) acc += ored[w2][t];
+            st_sys(part + 2 + t, acc);
+          }
+          if (threadIdx.x == 0) {
+            st_sys(part, m);
+            st_sys(part + 1, lsum);
+          }
+          wait_mem();
+          __syncthreads();
+          if (threadIdx.x == 0) {
+            const uint32_t prev =
+                __hip_atomic_fetch_add(&s.attn_cnt[h], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (uint32_t)(S - 1));
+          }
+          __syncthreads();
+          if (s_last) {
+            float *pbuf = xs;  // S * (HD + 2) floats
+            const float *p0 = s.attn_part + (size_t)h * ATTN_MAX_S * (HD + 2);
+            for (int i = threadIdx.x; i < S * (HD + 2); i += PBLOCK) pbuf[i] = ld_sys(p0 + i);
+            __syncthreads();
+            float M = -INFINITY;
+            for (int k = 0; k < S; ++k) M = fmaxf(M, pbuf[k * (HD + 2)]);
+            float *pws = xs + ATTN_MAX_S * (HD + 2);
+            if (threadIdx.x < S) {
+              const float mk = pbuf[threadIdx.x * (HD + 2)];
+              pws[threadIdx.x] = mk > -INFINITY ? expf(mk - M) : 0.f;
+            }
+            __syncthreads();
+            float Lsum = 0.f;
+            for (int k = 0; k < S; ++k) Lsum += pws[k] * pbuf[k * (HD + 2) + 1];
+            for (int t = threadIdx.x; t < HD; t += PBLOCK) {
+              float acc = 0.f;
+              for (int k = 0; k < S; ++k) acc += pws[k] * pbuf[k * (HD + 2) + 2 + t];
+              st_sys(s.o + h * HD + t, acc / Lsum);
+            }
+            if (threadIdx.x == 0) __hip_atomic_store(&s.attn_cnt[h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+      }
+    }
+    p_arrive(a, P + 1);
+    if (!p_wait(a, P + 1, &s_ok)) return;
+
+    // out_proj + residual (x staged next to o)
+    stage2_sys<UD, UD>(s.o, d.D, xs, s.x, d.D, xs + d.D);
+    Wt = reinterpret_cast<const WT *>(lp.w_out);
+    run_plain<WT, 2, VD>(Wt, lp.s_out, d.D, d.D, xs, tD, [&](int row, float v) { st_sys(s.x + row, xs[d.D + row] + v); });
+    p_arrive(a, P + 2);
+    prefetch_gate<WT, VD>(reinterpret_cast<const WT *>(lp.w_gin), d.F, d.D, tD);
+    if (!p_wait(a, P + 2, &s_ok)) return;
+
+    // norm2 + gate_in + silu * mult
+    stage_rms<PBLOCK, true, UD>(s.x, lp.norm2, d.D, d.eps, xs, red);
+    run_gate<WT, VD>(reinterpret_cast<const WT *>(lp.w_gin), lp.s_gin, d.F, d.D, xs, tD, s.a);
+    p_arrive(a, P + 3);
+    prefetch_plain<WT, 1, VF>(reinterpret_cast<const WT *>(lp.w_gout), d.D, d.F, tF);
+    if (!p_wait(a, P + 3, &s_ok)) return;
+
+    // gate_out + residual (x staged next to a)
+    stage2_sys<UF, UD>(s.a, d.F, xs, s.x, d.D, xs + d.F);
+    Wt = reinterpret_cast<const WT *>(lp.w_gout);
+    run_plain<WT, 1, VF>(Wt, lp.s_gout, d.D, d.F, xs, tF, [&](int row, float v) { st_sys(s.x + row, xs[d.F + row] + v); });
+    p_arrive(a, P + 4);
+    if (l + 1 < d.L)
+      prefetch_plain<WT, 2, VD>(reinterpret_cast<const WT *>(a.tl[l + 1].w_in), 3 * d.D, d.D, tD);
+    else
+      prefetch_plain<WT, 2, VD>(reinterpret_cast<const WT *>(a.w_text), d.Vt, d.D, tD);
+    if (!p_wait(a, P + 4, &s_ok)) return;
+  }
+
+  // ---- a6-a7: out_norm, text head (argmax partials) and depformer_in for every codebook ----
+  {
+    stage_rms<PBLOCK, true, UD>(s.x, a.out_norm, d.D, d.eps, xs, red);
+    if (blockIdx.x == 0)
+      for (int k = threadIdx.x; k < d.D; k += PBLOCK) s.hidden[k] = xs[k];
+    ArgBest best = arg_none();
+    Wt = reinterpret_cast<const WT *>(a.w_text);
+    run_plain<WT, 2, VD>(Wt, a.s_text, d.Vt, d.D, xs, tD, [&](int row, float v) {
+      s.text_logits[row] = v;
+      best = arg_take(best, v, row);
+    });
+    best = wave_arg(best);
+    best = block_arg(best, wb);
+    if (threadIdx.x == 0) st_sys_arg(s.am_part + blockIdx.x, best);
+    Wt = reinterpret_cast<const WT *>(a.w_din);
+    prefetch_plain<WT, 2, VD>(Wt, d.Q * d.Dd, d.D, tD);
+    run_plain<WT, 2, VD>(Wt, a.s_din, d.Q * d.Dd, d.D, xs, tD, [&](int row, float v) { st_sys(s.din + row, v); });
+  }
+  p_arrive(a, P_HEAD);
+  prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(a.dl[0].w_in), 3 * d.Dd, d.Dd, tS);
+  if (!p_wait(a, P_HEAD, &s_ok)) return;
+
+  // ---- a8: depformer, 8 sequential codebook steps ----
+  const ET *tbl;
+  for (int cb = 0; cb < d.Q; ++cb) {
+    const int PC = P_HEAD + 1 + cb * (4 * d.Ld + 1);
+    for (int j = 0; j < d.Ld; ++j) {
+      const LayerPtrs lp = a.dl[j * d.Q + cb];
+      const int P = PC + 4 * j;
+      // entry (layer 0): previous token, y = depformer_in[cb] . hidden + emb(prev)
+      if (j == 0) {
+        const int prev = merge_head(s.am_part + (size_t)cb * AM_MAX_BLOCKS, gridDim.x, wb);
+        if (blockIdx.x == 0 && threadIdx.x == 0) s.tokens[cb] = prev;
+        tbl = reinterpret_cast<const ET *>(a.dep_table[cb]);
+        for (int k = threadIdx.x; k < d.Dd; k += PBLOCK) {
+          const float v = ld_sys(s.din + (size_t)cb * d.Dd + k) + to_f(tbl[(size_t)prev * d.Dd + k]);
+          xs[k] = v;
+          if (blockIdx.x == 0) st_sys(s.y + k, v);
+        }
+        __syncthreads();
+        rms_in_place<PBLOCK>(xs, lp.norm1, d.Dd, d.eps, red);
+      } else {
+        stage_rms<PBLOCK, true, UDd>(s.y, lp.norm1, d.Dd, d.eps, xs, red);
+      }
+      float *kvbase = s.dkv + ((size_t)j * d.Q + cb) * 2 * d.Dd;
+      Wt = reinterpret_cast<const WT *>(lp.w_in);
+      run_plain<WT, 2, VDd>(Wt, lp.s_in, 3 * d.Dd, d.Dd, xs, tS, [&](int row, float v) {
+        if (row < d.Dd)
+          st_sys(s.dq + row, v);
+        else
+          st_sys(kvbase + row - d.Dd, v);
+      });
+      p_arrive(a, P);
+      prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(lp.w_out), d.Dd, d.Dd, tS);
+      if (!p_wait(a, P, &s_ok)) return;
+
+      // attention of dq over the cb + 1 entries of layer j (every block), then out_proj + residual
+      float *ys = xs + d.Dd;  // y, for the residual
+      {
+        constexpr int UY = UDd;  // y fits one pass when the tile width covers Dd
+        uint64_t yv[UY];
+#pragma unroll
+        for (int u = 0; u < UY; ++u) {
+          const int i = u * PBLOCK + threadIdx.x;
+          yv[u] = i < (d.Dd >> 1) ? ld_sys_u64(reinterpret_cast<const uint64_t *>(s.y) + i) : 0ull;
+        }
+        const int g = lane >> 4, sub = lane & 15;
+        const float *kv0 = s.dkv + (size_t)j * d.Q * 2 * d.Dd;
+        const float scale = 1.0f / sqrtf((float)d.hdd);
+        const int npos = cb + 1;
+        for (int hh = wave * 4 + g; hh < d.Hd; hh += PWAVES * 4) {
+          const int e0 = hh * d.hdd + sub * DEPL;
+          float qv[DEPL], kk[PQ][DEPL], vv[PQ][DEPL];
+#pragma unroll
+          for (int i = 0; i < DEPL; ++i) qv[i] = ld_sys(s.dq + e0 + i);
+#pragma unroll
+          for (int p = 0; p < PQ; ++p)
+            if (p < npos) {
+#pragma unroll
+              for (int i = 0; i < DEPL; ++i) {
+                kk[p][i] = ld_sys(kv0 + (size_t)p * 2 * d.Dd + e0 + i);
+                vv[p][i] = ld_sys(kv0 + (size_t)p * 2 * d.Dd + d.Dd + e0 + i);
+              }
+            }
+          float sc[PQ];
+          float m = -INFINITY;
+#pragma unroll
+          for (int p = 0; p < PQ; ++p) {
+            float dot = 0.f;
+            if (p < npos) {
+#pragma unroll
+              for (int i = 0; i < DEPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
+            }
+            dot += __shfl_xor(dot, 8, WAVE);
+            dot += __shfl_xor(dot, 4, WAVE);
+            dot += __shfl_xor(dot, 2, WAVE);
+            dot += __shfl_xor(dot, 1, WAVE);
+            dot = __shfl(dot, lane & 48, WAVE);
+            sc[p] = dot * scale;
+            if (p < npos) m = fmaxf(m, sc[p]);
+          }
+          float den = 0.f;
+#pragma unroll
+          for (int p = 0; p < PQ; ++p)
+            if (p < npos) {
+              sc[p] = expf(sc[p] - m);
+              den += sc[p];
+            }
+          float o[DEPL];
+#pragma unroll
+          for (int i = 0; i < DEPL; ++i) o[i] = 0.f;
+#pragma unroll
+          for (int p = 0; p < PQ; ++p)
+            if (p < npos) {
+              const float wgt = sc[p] / den;
+#pragma unroll
+              for (int i = 0; i < DEPL; ++i) o[i] = fmaf(wgt, vv[p][i], o[i]);
+            }
+#pragma unroll
+          for (int i = 0; i < DEPL; ++i) xs[e0 + i] = o[i];
+        }
+#pragma unroll
+        for (int u = 0; u < UY; ++u) {
+          const int i = u * PBLOCK + threadIdx.x;
+          if (i < (d.Dd >> 1)) {
+            ys[2 * i] = __uint_as_float((uint32_t)yv[u]);
+            ys[2 * i + 1] = __uint_as_float((uint32_t)(yv[u] >> 32));
+          }
+        }
+        __syncthreads();
+      }
+      Wt = reinterpret_cast<const WT *>(lp.w_out);
+      run_plain<WT, 2, VDd>(Wt, lp.s_out, d.Dd, d.Dd, xs, tS, [&](int row, float v) { st_sys(s.y + row, ys[row] + v); });
+      p_arrive(a, P + 1);
+      prefetch_gate<WT, VDd>(reinterpret_cast<const WT *>(lp.w_gin), d.Fd, d.Dd, tS);
+      if (!p_wait(a, P + 1, &s_ok)) return;
+
+      // norm2 + gate_in + silu * mult
+      stage_rms<PBLOCK, true, UDd>(s.y, lp.norm2, d.Dd, d.eps, xs, red);
+      run_gate<WT, VDd>(reinterpret_cast<const WT *>(lp.w_gin), lp.s_gin, d.Fd, d.Dd, xs, tS, s.da);
+      p_arrive(a, P + 2);
+      prefetch_plain<WT, 2, VFd>(reinterpret_cast<const WT *>(lp.w_gout), d.Dd, d.Fd, tT);
+      if (!p_wait(a, P + 2, &s_ok)) return;
+
+      // gate_out + residual (y staged next to da)
+      stage2_sys<UFd, UDd>(s.da, d.Fd, xs, s.y, d.Dd, xs + d.Fd);
+      Wt = reinterpret_cast<const WT *>(lp.w_gout);
+      run_plain<WT, 2, VFd>(Wt, lp.s_gout, d.Dd, d.Fd, xs, tT, [&](int row, float v) { st_sys(s.y + row, xs[d.Fd + row] + v); });
+      p_arrive(a, P + 3);
+      if (j + 1 < d.Ld)
+        prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(a.dl[(j + 1) * d.Q + cb].w_in), 3 * d.Dd, d.Dd, tS);
+      else
+        prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(a.w_lin[cb]), d.Va, d.Dd, tS);
+      if (!p_wait(a, P + 3, &s_ok)) return;
+    }
+    // codebook head (no norm) with argmax partials
+    {
+      const int P = PC + 4 * d.Ld;
+      stage_vec<PBLOCK, true, UDd>(s.y, d.Dd, xs);
+      ArgBest best = arg_none();
+      Wt = reinterpret_cast<const WT *>(a.w_lin[cb]);
+      float *lg = s.audio_logits + (size_t)cb * d.Va;
+      run_plain<WT, 2, VDd>(Wt, a.s_lin[cb], d.Va, d.Dd, xs, tS, [&](int row, float v) {
+        lg[row] = v;
+        best = arg_take(best, v, row);
+      });
+      best = wave_arg(best);
+      best = block_arg(best, wb);
+      if (threadIdx.x == 0) st_sys_arg(s.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS + blockIdx.x, best);
+      p_arrive(a, P);
+      if (cb + 1 < d.Q) {
+        prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(a.dl[cb + 1].w_in), 3 * d.Dd, d.Dd, tS);
+        if (!p_wait(a, P, &s_ok)) return;
+      }
+    }
+  }
+
+  // ---- a9: frame end (block 0) ----
+  if (blockIdx.x != 0) return;
+  const int P_LAST = P_HEAD + d.Q * (4 * d.Ld + 1);
+  if (!p_wait(a, P_LAST, &s_ok)) return;
+  const int last = merge_head(s.am_part + (size_t)d.Q * AM_MAX_BLOCKS, gridDim.x, wb);
+  if (threadIdx.x == 0) {
+    s.tokens[d.Q] = last;
+    const int64_t off = pos + 1;
+    s.offset[0] = off;
+    const int p = (int)(off % 3);
+    int32_t *tk = s.tokens;
+    for (int st = 0; st <= d.Q; ++st) s.ring[st * 3 + p] = tk[st];
+    int32_t *has = s.outpack + (1 + d.Q);
+    if (off > 1) {
+      for (int st = 0; st <= d.Q; ++st) s.outpack[st] = s.ring[st * 3 + (int)((off - 1 + stream_delay(st, d.Q)) % 3)];
+      *has = 1;
+    } else {
+      *has = 0;
+    }
+  }
+  // every block has arrived at every phase: clear the counters for the next frame
+  const int nph = P_LAST + 1;
+  for (int i = threadIdx.x; i < nph * SYNC_SLOTS; i += PBLOCK)
+    a.sync[(size_t)(i / SYNC_SLOTS) * SYNC_SLOTS * SYNC_STRIDE + (i % SYNC_SLOTS) * SYNC_STRIDE] = 0u;
+}
+
+}  // namespace mk

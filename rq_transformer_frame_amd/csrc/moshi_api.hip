@@ -14,7 +14,7 @@
 #include <unordered_map>
 #include <vector>
 
-#include "kernels.h"
+#include "frame_persistent.h"
 #include "moshi_mi355x.h"
 
 using mk::bf16_t;
@@ -86,6 +86,24 @@ struct moshi_state {
   hipGraphExec_t gexec = nullptr;
   std::string err;
   bool broken = false;
+
+  // persistent executor
+  const void *pkern = nullptr;  // selected k_frame_persistent instance
+  size_t plds = 0;              // its dynamic LDS bytes
+  int pgrid = 0;
+  uint32_t *sync = nullptr;     // phase counters
+  mk::LayerPtrs *d_tl = nullptr, *d_dl = nullptr;
+  mk::PArgs *d_pargs = nullptr;  // persistent kernel arguments (device copy)
+  uint64_t *d_phase_ts = nullptr;
+  int nph = 0;
+  bool phase_timing = false;
+  int *d_err = nullptr;
+
+  // frame GPU time
+  bool timing = false;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  double gpu_us = 0.0;
+  int64_t gpu_frames = 0;
 
   template <typename T>
   T *wptr(size_t off) const {
@@ -266,11 +284,18 @@ moshi_status alloc_session(moshi_state *s) {
   req((void **)&b.dkv, B * d.Ld * d.Q * 2 * d.Dd * 4);
   req((void **)&b.da, B * d.Fd * 4);
   req((void **)&b.audio_logits, B * d.Q * d.Va * 4);
-  req((void **)&b.outpack, B * (1 + d.Q) * 4 + B * 4);
+  req((void **)&b.outpack, B * (1 + d.Q) * 4 + B * 4 + 4);  // + error flag
   req((void **)&b.attn_part, B * d.H * mk::ATTN_MAX_S * (d.hd + 2) * 4);
   req((void **)&b.attn_cnt, B * d.H * 4);
   req((void **)&b.am_part, B * (1 + d.Q) * mk::AM_MAX_BLOCKS * sizeof(mk::ArgBest));
   req((void **)&b.rope_freq, (size_t)(d.hd / 2) * 4);
+  const size_t nph = (size_t)5 * d.L + 1 + (size_t)d.Q * (4 * d.Ld + 1) + 1;
+  req((void **)&s->sync, nph * mk::SYNC_SLOTS * mk::SYNC_STRIDE * 4);
+  req((void **)&s->d_tl, (size_t)d.L * sizeof(mk::LayerPtrs));
+  req((void **)&s->d_pargs, sizeof(mk::PArgs));
+  req((void **)&s->d_phase_ts, nph * 2 * 8);
+  s->nph = (int)nph;
+  req((void **)&s->d_dl, (size_t)d.Ld * d.Q * sizeof(mk::LayerPtrs));
   req(&s->kc, B * d.L * d.H * (size_t)d.cap * d.hd * kvelt);
   req(&s->vc, B * d.L * d.H * (size_t)d.cap * d.hd * kvelt);
   std::vector<size_t> offs;
@@ -292,7 +317,29 @@ moshi_status alloc_session(moshi_state *s) {
     fr[i] = (float)std::exp((double)arg);
   }
   HIP_TRY(s, hipMemcpy(b.rope_freq, fr.data(), fr.size() * 4, hipMemcpyHostToDevice));
-  hipError_t he = hipHostMalloc((void **)&s->h_pin, (B * d.Q + B * (1 + d.Q) + B) * 4, hipHostMallocDefault);
+  s->d_err = b.outpack + B * (1 + d.Q) + B;
+  // per-layer weight pointers for the persistent kernel
+  {
+    std::vector<mk::LayerPtrs> tl(d.L), dl((size_t)d.Ld * d.Q);
+    auto fill = [&](mk::LayerPtrs &p, const LayerW &lw) {
+      p.w_in = s->data(lw.in);
+      p.w_out = s->data(lw.out);
+      p.w_gin = s->data(lw.gin);
+      p.w_gout = s->data(lw.gout);
+      p.s_in = s->scale(lw.in);
+      p.s_out = s->scale(lw.out);
+      p.s_gin = s->scale(lw.gin);
+      p.s_gout = s->scale(lw.gout);
+      p.norm1 = reinterpret_cast<const float *>(s->data(lw.norm1));
+      p.norm2 = reinterpret_cast<const float *>(s->data(lw.norm2));
+    };
+    for (int l = 0; l < d.L; ++l) fill(tl[l], s->layers[l]);
+    for (int j = 0; j < d.Ld; ++j)
+      for (int cb = 0; cb < d.Q; ++cb) fill(dl[(size_t)j * d.Q + cb], s->dlayers[j][cb]);
+    HIP_TRY(s, hipMemcpy(s->d_tl, tl.data(), tl.size() * sizeof(mk::LayerPtrs), hipMemcpyHostToDevice));
+    HIP_TRY(s, hipMemcpy(s->d_dl, dl.data(), dl.size() * sizeof(mk::LayerPtrs), hipMemcpyHostToDevice));
+  }
+  hipError_t he = hipHostMalloc((void **)&s->h_pin, (B * d.Q + B * (1 + d.Q) + B + 1) * 4, hipHostMallocDefault);
   if (he != hipSuccess) return fail(s, MOSHI_ENOMEM, "pinned host buffer: %s", hipGetErrorString(he));
   return MOSHI_OK;
 }
@@ -329,6 +376,66 @@ void with_vpl(int K, F &&f) {
     if (need <= 3) return f(integral_constant<int, 3>{});
   }
   f(integral_constant<int, 0>{});
+}
+
+// The register-tile width with_vpl picks for input width K.
+template <typename WT>
+int vpl_of(int K) {
+  int v = -1;
+  with_vpl<WT>(K, [&](auto t) { v = decltype(t)::value; });
+  return v;
+}
+
+// Compiled persistent-kernel variants: (band, temporal head dim, depformer head dim / 16, tile
+// widths for inputs of width D, F, Dd, Fd).
+struct PVariant {
+  int band, hd, depl, vd, vf, vdd, vfd;
+  const void *fn;
+};
+
+template <typename WT, typename ET, typename KT, int HD, int DEPL, int VD, int VF, int VDd, int VFd>
+PVariant pvariant(int band) {
+  return PVariant{band, HD, DEPL, VD, VF, VDd, VFd,
+                  reinterpret_cast<const void *>(&mk::k_frame_persistent<WT, ET, KT, HD, DEPL, VD, VF, VDd, VFd>)};
+}
+
+const PVariant *persistent_variants(int *n) {
+  static const PVariant v[] = {
+      // Moshi-7B shape
+      pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 8, 22, 2, 6>(MOSHI_BAND_BF16),
+      pvariant<int8_t, bf16_t, bf16_t, 128, 4, 4, 11, 1, 3>(MOSHI_BAND_I8),
+      // tiny RQ-Transformer (d256 / d128, head dim 64)
+      pvariant<float, float, float, 64, 4, 1, 3, 1, 3>(MOSHI_BAND_F32),
+      pvariant<bf16_t, bf16_t, bf16_t, 64, 4, 2, 2, 2, 2>(MOSHI_BAND_BF16),
+      pvariant<int8_t, bf16_t, bf16_t, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
+  };
+  *n = (int)(sizeof(v) / sizeof(v[0]));
+  return v;
+}
+
+const void *select_persistent(const moshi_config &c, size_t *lds) {
+  const int D = c.d_model, F = c.ffn_hidden, Dd = c.dep_d_model, Fd = c.dep_ffn_hidden;
+  const int hd = D / c.n_heads, hdd = Dd / c.dep_heads;
+  int vd, vf, vdd, vfd;
+  if (c.band == MOSHI_BAND_F32) {
+    vd = vpl_of<float>(D), vf = vpl_of<float>(F), vdd = vpl_of<float>(Dd), vfd = vpl_of<float>(Fd);
+  } else if (c.band == MOSHI_BAND_BF16) {
+    vd = vpl_of<bf16_t>(D), vf = vpl_of<bf16_t>(F), vdd = vpl_of<bf16_t>(Dd), vfd = vpl_of<bf16_t>(Fd);
+  } else {
+    vd = vpl_of<int8_t>(D), vf = vpl_of<int8_t>(F), vdd = vpl_of<int8_t>(Dd), vfd = vpl_of<int8_t>(Fd);
+  }
+  if (c.dep_q > mk::PQ) return nullptr;
+  int n = 0;
+  const PVariant *v = persistent_variants(&n);
+  for (int i = 0; i < n; ++i)
+    if (v[i].band == c.band && v[i].hd == hd && v[i].depl * 16 == hdd && v[i].vd == vd && v[i].vf == vf &&
+        v[i].vdd == vdd && v[i].vfd == vfd) {
+      const size_t fl = std::max({(size_t)2 * D, (size_t)F + D, (size_t)2 * Dd, (size_t)Fd + Dd,
+                                  (size_t)mk::ATTN_MAX_S * (hd + 2) + mk::ATTN_MAX_S});
+      *lds = fl * 4;
+      return v[i].fn;
+    }
+  return nullptr;
 }
 
 template <typename F>
@@ -495,6 +602,44 @@ void enqueue_frame(moshi_state *s, int b0, int nb, bool temporal_only, const int
   }
 }
 
+// Fill the persistent kernel's argument block in device memory (once per session).
+moshi_status write_pargs(moshi_state *s) {
+  const mk::Dims &d = s->d;
+  mk::PArgs a{};
+  a.d = d;
+  a.s = s->b;
+  a.kc = s->kc;
+  a.vc = s->vc;
+  a.emb_audio = s->data(s->emb[0]);
+  a.emb_text = s->data(s->text_emb);
+  a.tl = s->d_tl;
+  a.dl = s->d_dl;
+  a.out_norm = reinterpret_cast<const float *>(s->data(s->out_norm));
+  a.w_text = s->data(s->text_lin);
+  a.s_text = s->scale(s->text_lin);
+  a.w_din = s->data(s->din[0]);
+  a.s_din = s->scale(s->din[0]);
+  for (int cb = 0; cb < d.Q; ++cb) {
+    a.dep_table[cb] = cb == 0 ? s->data(s->dep_text_emb) : s->data(s->dep_emb[cb - 1]);
+    a.w_lin[cb] = s->data(s->lin[cb]);
+    a.s_lin[cb] = s->scale(s->lin[cb]);
+  }
+  a.sync = s->sync;
+  a.err = s->d_err;
+  a.spin_limit = 1 << 20;
+  a.phase_ts = s->phase_timing ? s->d_phase_ts : nullptr;
+  HIP_TRY(s, hipMemcpy(s->d_pargs, &a, sizeof(a), hipMemcpyHostToDevice));
+  return MOSHI_OK;
+}
+
+moshi_status launch_persistent(moshi_state *s) {
+  mk::PArgs *pa = s->d_pargs;
+  void *args[] = {&pa};
+  HIP_TRY(s, hipLaunchCooperativeKernel(s->pkern, dim3(s->pgrid), dim3(mk::PBLOCK), args, (unsigned)s->plds,
+                                        s->stream));
+  return MOSHI_OK;
+}
+
 moshi_status ensure_graph(moshi_state *s) {
   if (s->gexec) return MOSHI_OK;
   hipGraph_t g = nullptr;
@@ -535,7 +680,7 @@ moshi_status check_config(const moshi_config *c, std::string &why) {
   if (c->band < MOSHI_BAND_F32 || c->band > MOSHI_BAND_I8) return bad("unknown band");
   if (c->batch < 1) return bad("batch must be >= 1");
   if (c->kv_capacity < 0 || c->kv_capacity > c->context) return bad("kv_capacity must be in [0, context]");
-  if (c->exec != MOSHI_EXEC_GRAPH && c->exec != MOSHI_EXEC_STREAM) return bad("unknown exec mode");
+  if (c->exec < MOSHI_EXEC_GRAPH || c->exec > MOSHI_EXEC_PERSISTENT) return bad("unknown exec mode");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return bad("rms_eps must be >= 0 and rope_theta > 0");
   return MOSHI_OK;
 }
@@ -630,6 +775,26 @@ moshi_status moshi_create(const moshi_config *cfg, void *hip_stream, moshi_state
     moshi_destroy(s);
     return st;
   }
+  if (cfg->exec == MOSHI_EXEC_PERSISTENT) {
+    s->pkern = d.B == 1 ? select_persistent(s->cfg, &s->plds) : nullptr;
+    int per_cu = 0;
+    if (!s->pkern || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, s->pkern, mk::PBLOCK, s->plds) != hipSuccess ||
+        per_cu < 1) {
+      fprintf(stderr, "moshi_create: no persistent frame kernel for this shape/batch (batch must be 1)\n");
+      moshi_destroy(s);
+      return MOSHI_EINVAL;
+    }
+    s->pgrid = s->cus;  // one block per CU
+    if (write_pargs(s) != MOSHI_OK) {
+      fprintf(stderr, "moshi_create: %s\n", s->err.c_str());
+      moshi_destroy(s);
+      return MOSHI_EDEVICE;
+    }
+  }
+  if (hipEventCreate(&s->ev0) != hipSuccess || hipEventCreate(&s->ev1) != hipSuccess) {
+    moshi_destroy(s);
+    return MOSHI_EDEVICE;
+  }
   mk::Bufs bb = s->b;
   mk::k_reset<<<d.B, 64, 0, s->stream>>>(d, bb, 0);
   if (hipStreamSynchronize(s->stream) != hipSuccess) {
@@ -645,6 +810,8 @@ void moshi_destroy(moshi_state *s) {
   (void)hipSetDevice(s->device);
   if (s->stream) (void)hipStreamSynchronize(s->stream);
   if (s->gexec) (void)hipGraphExecDestroy(s->gexec);
+  if (s->ev0) (void)hipEventDestroy(s->ev0);
+  if (s->ev1) (void)hipEventDestroy(s->ev1);
   if (s->warena) (void)hipFree(s->warena);
   if (s->sarena) (void)hipFree(s->sarena);
   if (s->h_pin) (void)hipHostFree(s->h_pin);
@@ -733,6 +900,40 @@ moshi_status moshi_load_weights(moshi_state *s, const moshi_tensor *t, int32_t n
   return rc;
 }
 
+moshi_status moshi_phase_times(moshi_state *s, int32_t enable, double *ts, int32_t max_phases, int32_t *n_phases) {
+  if (!s) return MOSHI_EINVAL;
+  if (!s->pkern) return fail(s, MOSHI_ESTATE, "phase times need the persistent executor");
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  if (n_phases) *n_phases = s->nph;
+  if (ts && max_phases > 0) {
+    std::vector<uint64_t> raw((size_t)s->nph * 2);
+    HIP_TRY(s, hipStreamSynchronize(s->stream));
+    HIP_TRY(s, hipMemcpy(raw.data(), s->d_phase_ts, raw.size() * 8, hipMemcpyDeviceToHost));
+    int khz = 0;
+    HIP_TRY(s, hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, s->device));
+    const uint64_t t0 = raw[0];
+    for (int p = 0; p < std::min(max_phases, s->nph); ++p)
+      for (int k = 0; k < 2; ++k) ts[2 * p + k] = (double)(int64_t)(raw[2 * p + k] - t0) * 1000.0 / (double)khz;
+  }
+  if (enable >= 0 && (enable != 0) != s->phase_timing) {
+    s->phase_timing = enable != 0;
+    return write_pargs(s);
+  }
+  return MOSHI_OK;
+}
+
+moshi_status moshi_gpu_time(moshi_state *s, int32_t enable, double *total_us, int64_t *frames) {
+  if (!s) return MOSHI_EINVAL;
+  if (total_us) *total_us = s->gpu_us;
+  if (frames) *frames = s->gpu_frames;
+  if (enable >= 0) {
+    s->timing = enable != 0;
+    s->gpu_us = 0.0;
+    s->gpu_frames = 0;
+  }
+  return MOSHI_OK;
+}
+
 moshi_status moshi_weight_bytes(const moshi_state *s, int64_t *linear_bytes, int64_t *all_bytes) {
   if (!s) return MOSHI_EINVAL;
   if (linear_bytes) *linear_bytes = s->linear_bytes;
@@ -773,7 +974,12 @@ static moshi_status run_frame(moshi_state *s, const int32_t *user, int32_t *out,
   int32_t *ho = s->h_pin + d.B * d.Q;
   std::memcpy(hu, user, sizeof(int32_t) * d.B * d.Q);
   HIP_TRY(s, hipMemcpyAsync(s->b.user, hu, sizeof(int32_t) * d.B * d.Q, hipMemcpyHostToDevice, s->stream));
-  if (s->cfg.exec == MOSHI_EXEC_GRAPH && !prof) {
+  const bool timed = s->timing && !prof;
+  if (timed) HIP_TRY(s, hipEventRecord(s->ev0, s->stream));
+  if (s->cfg.exec == MOSHI_EXEC_PERSISTENT && !prof) {
+    moshi_status rc = launch_persistent(s);
+    if (rc != MOSHI_OK) return rc;
+  } else if (s->cfg.exec == MOSHI_EXEC_GRAPH && !prof) {
     moshi_status rc = ensure_graph(s);
     if (rc != MOSHI_OK) return rc;
     HIP_TRY(s, hipGraphLaunch(s->gexec, s->stream));
@@ -782,9 +988,22 @@ static moshi_status run_frame(moshi_state *s, const int32_t *user, int32_t *out,
     enqueue_frame(s, 0, d.B, false, s->b.user, none, prof);
     HIP_TRY(s, hipGetLastError());
   }
-  const size_t ob = sizeof(int32_t) * ((size_t)d.B * (1 + d.Q) + d.B);
+  if (timed) HIP_TRY(s, hipEventRecord(s->ev1, s->stream));
+  const size_t ob = sizeof(int32_t) * ((size_t)d.B * (1 + d.Q) + d.B + 1);
   HIP_TRY(s, hipMemcpyAsync(ho, s->b.outpack, ob, hipMemcpyDeviceToHost, s->stream));
   HIP_TRY(s, hipStreamSynchronize(s->stream));
+  if (timed) {
+    float ms = 0.f;
+    HIP_TRY(s, hipEventElapsedTime(&ms, s->ev0, s->ev1));
+    s->gpu_us += 1000.0 * ms;
+    s->gpu_frames += 1;
+  }
+  if (ho[(size_t)d.B * (1 + d.Q) + d.B] != 0) {  // a phase wait of the persistent kernel timed out
+    (void)hipMemsetAsync(s->sync, 0, (size_t)((char *)s->d_tl - (char *)s->sync), s->stream);
+    (void)hipMemsetAsync(s->d_err, 0, 4, s->stream);
+    (void)hipStreamSynchronize(s->stream);
+    return fail(s, MOSHI_EDEVICE, "persistent frame kernel: a phase wait timed out");
+  }
   int any = 0;
   for (int b = 0; b < d.B; ++b) {
     s->h_offset[b]++;

@@ -1,7 +1,7 @@
 """Moshi-7B-shaped bfloat16 parity (B=1, seed-1 weights): the GPU frame step, teacher-forced onto
 the CPU oracle's greedy trajectory ([LM] force_generated), must keep every logits row at cosine
 >= 0.999 and agree on >= 99% of the greedy tokens.  The oracle runs the same bf16 weights widened
-to float32.  Runs in the graph launch configuration the bench times."""
+to float32.  Runs in the persistent configuration the bench times, and in the graph one."""
 import time
 
 import numpy as np
@@ -26,15 +26,20 @@ def weights():
     return w
 
 
+@pytest.fixture(scope="module")
+def oracle(weights):
+    return OracleLM(CFG, weights)
+
+
 @pytest.mark.timeout(900)
-def test_moshi7b_bf16_teacher_forced_matches_oracle(weights):
+@pytest.mark.parametrize("exec_mode", ["persistent", "graph"])
+def test_moshi7b_bf16_teacher_forced_matches_oracle(weights, oracle, exec_mode):
     users = synth.user_tokens(CFG, FRAMES)
-    with rq.Session(CFG, exec="graph") as s:
+    with rq.Session(CFG, exec=exec_mode) as s:
         t = time.time()
         s.load_weights(weights)
         print(f"loaded in {time.time() - t:.1f}s", flush=True)
-        lm = OracleLM(CFG, weights)
-        print("oracle ready", flush=True)
+        lm = oracle
         ost = lm.new_state()
         agree = total = 0
         cos_min = 1.0

@@ -41,7 +41,7 @@ def compare_step(tr, ref, st, out, has, frame):
         assert out[0].tolist() == ref["out"], frame
 
 
-@pytest.mark.parametrize("exec_mode", ["graph", "stream"])
+@pytest.mark.parametrize("exec_mode", ["graph", "stream", "persistent"])
 def test_tiny_free_running_matches_oracle(weights, oracle, exec_mode):
     users = synth.user_tokens(CFG, CFG.frames)
     ost = oracle.new_state()
@@ -54,11 +54,12 @@ def test_tiny_free_running_matches_oracle(weights, oracle, exec_mode):
             assert s.offset(0) == f + 1
 
 
-def test_tiny_sliding_window_past_context(weights, oracle):
+@pytest.mark.parametrize("exec_mode", ["graph", "persistent"])
+def test_tiny_sliding_window_past_context(weights, oracle, exec_mode):
     """74 frames with context 64: the KV ring wraps and attention keeps the last 64 positions."""
     users = synth.user_tokens(CFG, 74)
     ost = oracle.new_state()
-    with rq.Session(CFG) as s:
+    with rq.Session(CFG, exec=exec_mode) as s:
         s.load_weights(weights)
         for f in range(74):
             ref = oracle.step(ost, users[f])
@@ -66,11 +67,12 @@ def test_tiny_sliding_window_past_context(weights, oracle):
             compare_step(s.read_trace(0), ref, st, out, has, f)
 
 
-def test_tiny_runs_are_bitwise_deterministic(weights):
+@pytest.mark.parametrize("exec_mode", ["graph", "persistent"])
+def test_tiny_runs_are_bitwise_deterministic(weights, exec_mode):
     users = synth.user_tokens(CFG, 6)
     logs = []
     for _ in range(2):
-        with rq.Session(CFG) as s:
+        with rq.Session(CFG, exec=exec_mode) as s:
             s.load_weights(weights)
             for f in range(6):
                 s.step(users[f])
@@ -183,14 +185,39 @@ def test_teacher_forcing_follows_the_reference_trajectory(weights, oracle):
             s.force_generated(0, int(forced[f, 0]), forced[f, 1:])
 
 
+def test_persistent_executor_needs_batch_one(weights):
+    with pytest.raises(rq.MoshiError) as ei:
+        rq.Session(CFG, batch=2, exec="persistent")
+    assert ei.value.status == rq.MOSHI_EINVAL
+
+
+def test_persistent_and_graph_executors_agree(weights):
+    """Both executors run the same per-row arithmetic: the logits agree to float32 rounding and
+    the tokens exactly over a free-running trace."""
+    users = synth.user_tokens(CFG, 10)
+    traces = {}
+    for mode in ("graph", "persistent"):
+        with rq.Session(CFG, exec=mode) as s:
+            s.load_weights(weights)
+            traces[mode] = []
+            for f in range(10):
+                s.step(users[f])
+                traces[mode].append(s.read_trace(0))
+    for f in range(10):
+        g, p = traces["graph"][f], traces["persistent"][f]
+        assert g["tokens"].tolist() == p["tokens"].tolist(), f
+        assert rel_err(p["text_logits"], g["text_logits"]) <= 1e-5, f
+
+
 @pytest.mark.parametrize("T", [1, 5, 70])
-def test_prefill_forced_then_greedy(weights, oracle, T):
+@pytest.mark.parametrize("exec_mode", ["graph", "persistent"])
+def test_prefill_forced_then_greedy(weights, oracle, T, exec_mode):
     text, agent, user = synth.prefill_tokens(CFG, T)
     text %= CFG.text_card
     ost = oracle.new_state()
     oracle.prefill_forced(ost, text, agent, user)
     users = synth.user_tokens(CFG, 3, start_frame=T)
-    with rq.Session(CFG) as s:
+    with rq.Session(CFG, exec=exec_mode) as s:
         s.load_weights(weights)
         s.prefill_forced(0, text, agent, user)
         assert s.offset(0) == T
@@ -223,8 +250,9 @@ def test_batch_of_three_conversations_matches_single_runs(weights, oracle):
         assert [s.offset(b) for b in range(B)] == [6, 0, 6]
 
 
+@pytest.mark.parametrize("exec_mode", ["graph", "persistent"])
 @pytest.mark.parametrize("band", ["bf16", "i8"])
-def test_low_precision_bands_on_the_tiny_model(weights, band):
+def test_low_precision_bands_on_the_tiny_model(weights, band, exec_mode):
     """bf16 band vs the oracle on the same bf16-rounded weights; int8 band vs the int8-dequantised
     oracle (storage loss only).  Teacher-forced onto the oracle's tokens."""
     w16 = {k: (synth.f32_to_bf16_bits(v) if v.ndim == 2 else v) for k, v in weights.items()}
@@ -232,7 +260,7 @@ def test_low_precision_bands_on_the_tiny_model(weights, band):
     users = synth.user_tokens(CFG, 8)
     ost = ref_lm.new_state()
     agree, total, cos_min = 0, 0, 1.0
-    with rq.Session(CFG, band=band) as s:
+    with rq.Session(CFG, band=band, exec=exec_mode) as s:
         s.load_weights(w16)
         for f in range(8):
             ref = ref_lm.step(ost, users[f])
