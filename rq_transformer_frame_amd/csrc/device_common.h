@@ -152,114 +152,145 @@ __device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
   return uint4{v.x, v.y, v.z, v.w};
 }
 
-// One wave computes the dot products of R weight rows (row r starts at W + rowoff[r]) with the
-// vector xs[0..K) held in LDS, for any K (multiple of the vector width): lane l handles the
-// 16-byte vectors l, l + 64, l + 128, ... of each row, U vectors per row in flight at a time.
-// acc[r] is the lane's partial sum.
-template <typename WT, int R, int U>
-__device__ __forceinline__ void wave_rows_dot(const WT *__restrict__ W, int K, const int64_t *rowoff,
-                                              const float *__restrict__ xs, float *acc) {
-  constexpr int N = WVec<WT>::N;
-  const int lane = threadIdx.x & 63;
-  const int nv = K / N;
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  int v0 = 0;
-  for (; v0 + U * WAVE <= nv; v0 += U * WAVE) {
-    uint4 w[R][U];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int u = 0; u < U; ++u) w[r][u] = ld_stream(reinterpret_cast<const uint4 *>(W + rowoff[r]) + v0 + u * WAVE + lane);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float *xp = xs + (size_t)(v0 + u * WAVE + lane) * N;
-      float xv[N];
-#pragma unroll
-      for (int i = 0; i < N; ++i) xv[i] = xp[i];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float wf[N];
-        WVec<WT>::cvt(w[r][u], wf);
-#pragma unroll
-        for (int i = 0; i < N; ++i) acc[r] = fmaf(wf[i], xv[i], acc[r]);
-      }
-    }
-  }
-  for (int v = v0 + lane; v < nv; v += WAVE) {
-    const float *xp = xs + (size_t)v * N;
-    float xv[N];
-#pragma unroll
-    for (int i = 0; i < N; ++i) xv[i] = xp[i];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint4 wv = ld_stream(reinterpret_cast<const uint4 *>(W + rowoff[r]) + v);
-      float wf[N];
-      WVec<WT>::cvt(wv, wf);
-#pragma unroll
-      for (int i = 0; i < N; ++i) acc[r] = fmaf(wf[i], xv[i], acc[r]);
-    }
-  }
-}
+// ---- weight streaming ------------------------------------------------------------------------
+// A wave's share of a projection y = W . x: the rows [r0, r1) of W (row-major, K columns), walked
+// in chunks of SCH 16-byte vectors per lane (8 KB per wave), always two chunks in flight.  Chunk c
+// of a row covers the vectors c*SCH*64 + i*64 + lane (i < SCH) of the row.  Loads go through a
+// buffer resource spanning exactly the row, so vectors past the row end read as zero without a
+// memory access and every chunk is the same SCH unconditional loads: with no loads under a
+// branch, the compiler can count the loads in flight and wait for one chunk at a time (loads
+// complete in order; a branch around a load makes it wait for all of them).  The input vector is
+// read from LDS.  begin() issues the first two chunks and returns, so a kernel can start its
+// weight stream before its prologue; run() walks the rest and calls epi(row, value) once per row,
+// in every lane, with the wave-reduced dot product times the row's scale (int8 rows).  Epilogues
+// must not load from global memory, for the same reason.
+constexpr int SCH = 8;
+constexpr int BUF_DWORD3 = 0x00020000;  // raw 32-bit buffer resource word 3 for gfx9-family parts
+constexpr int BUF_NT = 2;               // cache policy: nontemporal (streamed once)
 
-// Register tile of one wave: R whole weight rows, VPL 16-byte vectors per lane per row (vector v
-// = lane + 64 i; vectors past the row end read as zero).  load() issues every load of the tile at
-// once and returns; dot() consumes the tile against xs in LDS.  Splitting the two lets a kernel
-// issue its weight loads before its prologue and prefetch the next rows while it reduces.
-// VPL == 0 is the generic form for any K: load() only records the rows and dot() streams them.
-template <typename WT, int R, int VPL>
-struct RowTile {
+typedef unsigned int u32x4b __attribute__((ext_vector_type(4)));
+
+template <typename WT>
+struct RowStream {
   static constexpr int N = WVec<WT>::N;
-  uint4 w[R][VPL];
-  __device__ __forceinline__ void load(const WT *__restrict__ W, int K, const int *rows) {
+  uint4 a[SCH], b[SCH];
+  float sa, sb;  // scales of the rows whose last chunk is in a / b
+  const WT *W;
+  const float *S;
+  int K, nv, nch, r0, T;
+  int lq, lc;  // row (relative to r0) and chunk of the next load
+  int cq, cc;  // row and chunk of the next chunk consumed
+
+  // Load chunk (lq, lc) into buf and advance.
+  __device__ __forceinline__ void load(uint4 (&buf)[SCH], float &sc) {
     const int lane = threadIdx.x & 63;
-    const int nv = K / N;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(W + (size_t)(r0 + lq) * K), (short)0, nv * 16, BUF_DWORD3);
+    const int soff = lc * (SCH * WAVE * 16);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const uint4 *p = reinterpret_cast<const uint4 *>(W + (size_t)rows[r] * K);
-#pragma unroll
-      for (int i = 0; i < VPL; ++i) {
-        const int v = lane + WAVE * i;
-        w[r][i] = v < nv ? ld_stream(p + v) : uint4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < SCH; ++i) {
+      const u32x4b v = __builtin_amdgcn_raw_buffer_load_b128(rs, (i * WAVE + lane) * 16, soff, BUF_NT);
+      buf[i] = uint4{v[0], v[1], v[2], v[3]};
+    }
+    if (S && lc == nch - 1) sc = S[r0 + lq];
+    if (++lc == nch) {
+      lc = 0;
+      ++lq;
     }
   }
-  __device__ __forceinline__ void dot(const WT *__restrict__, int K, const float *__restrict__ xs, float *acc) const {
-    const int lane = threadIdx.x & 63;
-    const int nv = K / N;
+
+  __device__ __forceinline__ void begin(const WT *__restrict__ W_, const float *__restrict__ S_, int K_, int r0_,
+                                        int r1_) {
+    W = W_;
+    S = S_;
+    K = K_;
+    nv = K_ / N;
+    nch = (nv + SCH * WAVE - 1) / (SCH * WAVE);
+    r0 = r0_;
+    T = (r1_ > r0_ ? r1_ - r0_ : 0) * nch;
+    lq = lc = 0;
+    sa = sb = 1.f;
+    if (T > 0) load(a, sa);
+    if (T > 1) load(b, sb);
+  }
+
+  __device__ __forceinline__ float dot1(const uint4 &w, const float *__restrict__ xp, float acc) const {
+    float xv[N], wf[N];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int v = lane + WAVE * i;
-      if (v < nv) {
-        const float *xp = xs + (size_t)v * N;
-        float xv[N];
-#pragma unroll
-        for (int e = 0; e < N; ++e) xv[e] = xp[e];
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          float wf[N];
-          WVec<WT>::cvt(w[r][i], wf);
-#pragma unroll
-          for (int e = 0; e < N; ++e) acc[r] = fmaf(wf[e], xv[e], acc[r]);
-        }
-      }
+    for (int e = 0; e < N; e += 4) {
+      const float4 q = *reinterpret_cast<const float4 *>(xp + e);
+      xv[e] = q.x;
+      xv[e + 1] = q.y;
+      xv[e + 2] = q.z;
+      xv[e + 3] = q.w;
     }
+    WVec<WT>::cvt(w, wf);
+#pragma unroll
+    for (int e = 0; e < N; ++e) acc = fmaf(wf[e], xv[e], acc);
+    return acc;
+  }
+
+  __device__ __forceinline__ float dot(const uint4 (&buf)[SCH], int c, const float *__restrict__ xs, float acc) const {
+    const int lane = threadIdx.x & 63;
+    const int left = nv - c * (SCH * WAVE);
+    const float *xp = xs + (size_t)(c * (SCH * WAVE) + lane) * N;
+    if (left >= SCH * WAVE) {
+#pragma unroll
+      for (int i = 0; i < SCH; ++i) acc = dot1(buf[i], xp + i * WAVE * N, acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < SCH; ++i)
+        if (i * WAVE + lane < left) acc = dot1(buf[i], xp + i * WAVE * N, acc);
+    }
+    return acc;
+  }
+
+  // Consume the chunk in buf (row cq, chunk cc); a finished row goes to the epilogue.
+  template <typename Epi>
+  __device__ __forceinline__ void consume(const uint4 (&buf)[SCH], float sc, const float *__restrict__ xs,
+                                          float &acc, Epi &epi) {
+    acc = dot(buf, cc, xs, acc);
+    if (cc == nch - 1) {
+      float v = wave_sum(acc);
+      if (S) v *= sc;
+      epi(r0 + cq, v);
+      acc = 0.f;
+      cc = 0;
+      ++cq;
+    } else {
+      ++cc;
+    }
+  }
+
+  // Steady state: every iteration consumes two chunks and loads the two after them, with no
+  // condition on the loads; the last (up to three) chunks are peeled.
+  template <typename Epi>
+  __device__ __forceinline__ void run(const float *__restrict__ xs, Epi &&epi) {
+    float acc = 0.f;
+    cq = cc = 0;
+    int t = 0;
+    for (; t + 3 < T; t += 2) {
+      consume(a, sa, xs, acc, epi);
+      load(a, sa);
+      consume(b, sb, xs, acc, epi);
+      load(b, sb);
+    }
+    const int rem = T - t;
+    if (rem >= 1) consume(a, sa, xs, acc, epi);
+    if (rem == 3) load(a, sa);
+    if (rem >= 2) consume(b, sb, xs, acc, epi);
+    if (rem == 3) consume(a, sa, xs, acc, epi);
   }
 };
 
-template <typename WT, int R>
-struct RowTile<WT, R, 0> {
-  int64_t ro[R];
-  __device__ __forceinline__ void load(const WT *__restrict__, int K, const int *rows) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) ro[r] = (int64_t)rows[r] * K;
-  }
-  __device__ __forceinline__ void dot(const WT *__restrict__ W, int K, const float *__restrict__ xs, float *acc) const {
-    wave_rows_dot<WT, R, 8>(W, K, ro, xs, acc);
-  }
-};
+// Index of the calling wave in its block, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Balanced contiguous share of `units` units of P rows for wave w of TW: rows [lo, hi).
+__device__ __forceinline__ void wave_rows(int w, int TW, int units, int P, int &lo, int &hi) {
+  lo = (int)(((int64_t)w * units) / TW) * P;
+  hi = (int)(((int64_t)(w + 1) * units) / TW) * P;
+}
 
 // ---- cross-block exchange inside one kernel -------------------------------------------------
 // Data another block of the same kernel reads is written with system-scope stores (write-through

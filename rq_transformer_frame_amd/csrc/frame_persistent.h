@@ -139,14 +139,6 @@ __device__ __forceinline__ void stage2_sys(const float *src1, int K1, float *dst
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-// Per-thread 8-byte loads that stage an input of the longest width a register tile of VPL
-// 16-byte vectors per lane covers (tile width bounds the input length): one pass in the usual
-// case, more passes for the generic tile (VPL 0).
-template <typename WT, int VPL>
-constexpr int stage_u() {
-  return VPL == 0 ? 4 : (VPL * WAVE * (16 / (int)sizeof(WT)) / 2 + PBLOCK - 1) / PBLOCK;
-}
-
 // ---- phase completion ------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t *phase_ctr(const PArgs &a, int p) {
   return a.sync + (size_t)p * SYNC_SLOTS * SYNC_STRIDE;
@@ -200,143 +192,18 @@ __device__ __forceinline__ bool p_wait(const PArgs &a, int p, int *s_ok) {
   return *s_ok != 0;
 }
 
-// ---- one register tile shared by every phase ---------------------------------------------------
-// T 16-byte vectors per lane; a phase views it as R rows of VPL vectors (R * VPL <= T).  Sharing one
-// buffer keeps a single tile's worth of registers live across the whole kernel.
-template <int T>
-struct TileBuf {
-  uint4 w[T];
-};
-
-template <typename WT, int R, int VPL, int T>
-__device__ __forceinline__ void tile_load(TileBuf<T> &t, const WT *__restrict__ W, int K, const int *rows) {
-  static_assert(R * VPL <= T, "tile view larger than the buffer");
-  constexpr int N = WVec<WT>::N;
-  const int lane = threadIdx.x & 63;
-  const int nv = K / N;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const uint4 *p = reinterpret_cast<const uint4 *>(W + (size_t)rows[r] * K);
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int v = lane + WAVE * i;
-      t.w[r * VPL + i] = v < nv ? ld_stream(p + v) : uint4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-template <typename WT, int R, int VPL, int T>
-__device__ __forceinline__ void tile_dot(const TileBuf<T> &t, int K, const float *__restrict__ xs, float *acc) {
-  constexpr int N = WVec<WT>::N;
-  const int lane = threadIdx.x & 63;
-  const int nv = K / N;
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.f;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int v = lane + WAVE * i;
-    if (v < nv) {
-      const float *xp = xs + (size_t)v * N;
-      float xv[N];
-#pragma unroll
-      for (int e = 0; e < N; ++e) xv[e] = xp[e];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float wf[N];
-        WVec<WT>::cvt(t.w[r * VPL + i], wf);
-#pragma unroll
-        for (int e = 0; e < N; ++e) acc[r] = fmaf(wf[e], xv[e], acc[r]);
-      }
-    }
-  }
-}
-
 // ---- row phases --------------------------------------------------------------------------------
 // Global wave index and count of the persistent grid.
-__device__ __forceinline__ int gwave() { return blockIdx.x * PWAVES + (threadIdx.x >> 6); }
+__device__ __forceinline__ int gwave() { return blockIdx.x * PWAVES + wave_id(); }
 __device__ __forceinline__ int nwaves() { return gridDim.x * PWAVES; }
 
-// Row group gi of a plain projection: rows gi*R .. gi*R+R-1 (clamped).
-template <int R>
-__device__ __forceinline__ void plain_rows(int gi, int N, int *rows) {
-#pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, N - 1);
-}
-// Row group j of a gated projection: rows j (gate) and F + j (mult).
-__device__ __forceinline__ void gate_rows(int j, int F, int *rows) {
-  const int jj = min(j, F - 1);
-  rows[0] = jj;
-  rows[1] = F + jj;
-}
-
-template <typename WT, int R, int VPL, int T>
-__device__ __forceinline__ void prefetch_plain(const WT *W, int N, int K, TileBuf<T> &t) {
-  const int gi = gwave();
-  if (gi < (N + R - 1) / R) {
-    int rows[R];
-    plain_rows<R>(gi, N, rows);
-    tile_load<WT, R, VPL>(t, W, K, rows);
-  }
-}
-template <typename WT, int VPL, int T>
-__device__ __forceinline__ void prefetch_gate(const WT *W, int F, int K, TileBuf<T> &t) {
-  const int j = gwave();
-  if (j < F) {
-    int rows[2];
-    gate_rows(j, F, rows);
-    tile_load<WT, 2, VPL>(t, W, K, rows);
-  }
-}
-
-// Run the plain projection rows of this wave against xs; the first tile is already in t.
-// epi(row, value) runs in lane 0 of the owning wave.
-template <typename WT, int R, int VPL, int T, typename Epi>
-__device__ __forceinline__ void run_plain(const WT *W, const float *wscale, int N, int K, const float *xs,
-                                          TileBuf<T> &t, Epi &&epi) {
-  const int lane = threadIdx.x & 63, TW = nwaves();
-  const int ng = (N + R - 1) / R;
-  for (int gi = gwave(); gi < ng; gi += TW) {
-    float acc[R];
-    tile_dot<WT, R, VPL>(t, K, xs, acc);
-    if (gi + TW < ng) {
-      int nr[R];
-      plain_rows<R>(gi + TW, N, nr);
-      tile_load<WT, R, VPL>(t, W, K, nr);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float v = wave_sum(acc[r]);
-      const int row = gi * R + r;
-      if (lane == 0 && row < N) {
-        if (wscale) v *= wscale[row];
-        epi(row, v);
-      }
-    }
-  }
-}
-
-// Gated projection: a[j] = silu(g_j) * m_j for this wave's pairs (j, F + j).
-template <typename WT, int VPL, int T>
-__device__ __forceinline__ void run_gate(const WT *W, const float *wscale, int F, int K, const float *xs,
-                                         TileBuf<T> &t, float *a_out) {
-  const int lane = threadIdx.x & 63, TW = nwaves();
-  for (int j = gwave(); j < F; j += TW) {
-    float acc[2];
-    tile_dot<WT, 2, VPL>(t, K, xs, acc);
-    if (j + TW < F) {
-      int nr[2];
-      gate_rows(j + TW, F, nr);
-      tile_load<WT, 2, VPL>(t, W, K, nr);
-    }
-    float gv = wave_sum(acc[0]), mv = wave_sum(acc[1]);
-    if (lane == 0) {
-      if (wscale) {
-        gv *= wscale[j];
-        mv *= wscale[F + j];
-      }
-      st_sys(a_out + j, silu(gv) * mv);
-    }
-  }
+// Start this wave's balanced share of a projection phase (units of P rows over the whole grid).
+// Called before the wait for the previous phase: the weight stream does not depend on it.
+template <typename WT>
+__device__ __forceinline__ void p_begin(RowStream<WT> &rs, const void *W, const float *S, int K, int units, int P) {
+  int lo, hi;
+  wave_rows(gwave(), nwaves(), units, P, lo, hi);
+  rs.begin(reinterpret_cast<const WT *>(W), S, K, lo, hi);
 }
 
 // Block-wide first-wins merge of the waves' best rows (lane 0 of each wave holds its best).
@@ -361,10 +228,10 @@ __device__ __forceinline__ int merge_head(const ArgBest *part, int n, ArgBest *w
 
 // ---- the frame ---------------------------------------------------------------------------------
 // Template: weight / embedding / KV storage types, temporal head dim, depformer dims per lane
-// (head_dim / 16) and the register-tile widths for inputs of width D, F, Dd and Fd.
+// (head_dim / 16) and the staging loads per thread for inputs of width D, F, Dd and Fd.
 // The arguments live in device memory (written once per session): reading them where they are
 // used keeps the ~150 dwords of pointers and sizes out of the registers of every phase.
-template <typename WT, typename ET, typename KT, int HD, int DEPL, int VD, int VF, int VDd, int VFd>
+template <typename WT, typename ET, typename KT, int HD, int DEPL, int UD, int UF, int UDd, int UFd>
 __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__restrict__ pa) {
   const PArgs &a = *pa;
   extern __shared__ float xs[];  // max(D, F, Dd, Fd) floats; the attention phase reuses it
@@ -452,67 +319,51 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
   }
   __syncthreads();
 
-  const WT *Wt;
-  constexpr int UD = stage_u<WT, VD>(), UF = stage_u<WT, VF>(), UDd = stage_u<WT, VDd>(), UFd = stage_u<WT, VFd>();
-  // one register tile for every phase: views R=2 x VD (qkv, out_proj, gate_in, text head,
-  // dep_in), R=1 x VF (gate_out), R=2 x VDd (depformer qkv, out, gate_in, heads), R=2 x VFd
-  // (depformer gate_out)
-  constexpr int TT = cmax(cmax(2 * VD, VF), cmax(2 * VDd, 2 * VFd));
-  TileBuf<TT> tD;
-  TileBuf<TT> &tF = tD, &tS = tD, &tT = tD;
-  prefetch_plain<WT, 2, VD>(reinterpret_cast<const WT *>(a.tl[0].w_in), 3 * d.D, d.D, tD);
+  // one weight stream for every phase; each phase's first chunks are requested before the wait
+  // for the phase it depends on
+  RowStream<WT> rs;
+  p_begin(rs, a.tl[0].w_in, a.tl[0].s_in, d.D, 3 * d.D / 2, 2);
 
   // ---- a4-a5: temporal layers ----
   for (int l = 0; l < d.L; ++l) {
     const LayerPtrs lp = a.tl[l];
     const int P = 5 * l;
-    // qkv + rope + KV append
+    // qkv + rope + KV append: row pairs (2i, 2i+1) are whole rope pairs
     if (l == 0)
       rms_in_place<PBLOCK>(xs, lp.norm1, d.D, d.eps, red);
     else
       stage_rms<PBLOCK, true, UD>(s.x, lp.norm1, d.D, d.eps, xs, red);
-    Wt = reinterpret_cast<const WT *>(lp.w_in);
     {
-      const int TW = nwaves();
-      const int npairs = 3 * d.D / 2;
-      for (int pr = gwave(); pr < npairs; pr += TW) {
-        float acc[2];
-        tile_dot<WT, 2, VD>(tD, d.D, xs, acc);
-        if (pr + TW < npairs) {
-          const int nr[2] = {2 * (pr + TW), 2 * (pr + TW) + 1};
-          tile_load<WT, 2, VD>(tD, Wt, d.D, nr);
+      float pend = 0.f;
+      rs.run(xs, [&](int row, float v) {
+        if (lane != 0) return;
+        if ((row & 1) == 0) {
+          pend = v;
+          return;
         }
-        acc[0] = wave_sum(acc[0]);
-        acc[1] = wave_sum(acc[1]);
-        if (lane == 0) {
-          const int r0 = 2 * pr;
-          float v0 = acc[0], v1 = acc[1];
-          if (lp.s_in) {
-            v0 *= lp.s_in[r0];
-            v1 *= lp.s_in[r0 + 1];
-          }
-          const int part = r0 / d.D;
-          const int rr = r0 - part * d.D;
-          const int h = rr / HD, e = rr - h * HD;
-          if (part < 2) {
-            const float cs = rcs[e], sn = rcs[e + 1];
-            const float a0 = v0 * cs - v1 * sn;
-            const float a1 = v0 * sn + v1 * cs;
-            v0 = a0;
-            v1 = a1;
-          }
-          if (part == 0) {
-            st_sys_u64(reinterpret_cast<uint64_t *>(s.q + rr),
-                       (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32));
-          } else {
-            KT *cache = part == 1 ? kc : vc;
-            st_sys_pair<KT>(cache + ((((size_t)l * d.H + h) * d.cap + slot) * HD + e), v0, v1);
-          }
+        const int r0 = row - 1;
+        float v0 = pend, v1 = v;
+        const int part = r0 / d.D;
+        const int rr = r0 - part * d.D;
+        const int h = rr / HD, e = rr - h * HD;
+        if (part < 2) {
+          const float cs = rcs[e], sn = rcs[e + 1];
+          const float a0 = v0 * cs - v1 * sn;
+          const float a1 = v0 * sn + v1 * cs;
+          v0 = a0;
+          v1 = a1;
         }
-      }
+        if (part == 0) {
+          st_sys_u64(reinterpret_cast<uint64_t *>(s.q + rr),
+                     (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32));
+        } else {
+          KT *cache = part == 1 ? kc : vc;
+          st_sys_pair<KT>(cache + ((((size_t)l * d.H + h) * d.cap + slot) * HD + e), v0, v1);
+        }
+      });
     }
     p_arrive(a, P);
-    prefetch_plain<WT, 2, VD>(reinterpret_cast<const WT *>(lp.w_out), d.D, d.D, tD);  // out_proj, after attention
+    p_begin(rs, lp.w_out, lp.s_out, d.D, d.D, 1);  // out_proj, after attention
     if (!p_wait(a, P, &s_ok)) return;
 
     // attention: block bi < H * S takes head bi % H, split bi / H
@@ -639,28 +490,39 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
 
     // out_proj + residual (x staged next to o)
     stage2_sys<UD, UD>(s.o, d.D, xs, s.x, d.D, xs + d.D);
-    Wt = reinterpret_cast<const WT *>(lp.w_out);
-    run_plain<WT, 2, VD>(Wt, lp.s_out, d.D, d.D, xs, tD, [&](int row, float v) { st_sys(s.x + row, xs[d.D + row] + v); });
+    rs.run(xs, [&](int row, float v) {
+      if (lane == 0) st_sys(s.x + row, xs[d.D + row] + v);
+    });
     p_arrive(a, P + 2);
-    prefetch_gate<WT, VD>(reinterpret_cast<const WT *>(lp.w_gin), d.F, d.D, tD);
+    p_begin(rs, lp.w_gin, lp.s_gin, d.D, d.F, 2);
     if (!p_wait(a, P + 2, &s_ok)) return;
 
-    // norm2 + gate_in + silu * mult
+    // norm2 + gate_in + silu * mult (rows interleaved: 2j gate, 2j + 1 mult)
     stage_rms<PBLOCK, true, UD>(s.x, lp.norm2, d.D, d.eps, xs, red);
-    run_gate<WT, VD>(reinterpret_cast<const WT *>(lp.w_gin), lp.s_gin, d.F, d.D, xs, tD, s.a);
+    {
+      float gv = 0.f;
+      rs.run(xs, [&](int row, float v) {
+        if (lane != 0) return;
+        if ((row & 1) == 0)
+          gv = v;
+        else
+          st_sys(s.a + (row >> 1), silu(gv) * v);
+      });
+    }
     p_arrive(a, P + 3);
-    prefetch_plain<WT, 1, VF>(reinterpret_cast<const WT *>(lp.w_gout), d.D, d.F, tF);
+    p_begin(rs, lp.w_gout, lp.s_gout, d.F, d.D, 1);
     if (!p_wait(a, P + 3, &s_ok)) return;
 
     // gate_out + residual (x staged next to a)
     stage2_sys<UF, UD>(s.a, d.F, xs, s.x, d.D, xs + d.F);
-    Wt = reinterpret_cast<const WT *>(lp.w_gout);
-    run_plain<WT, 1, VF>(Wt, lp.s_gout, d.D, d.F, xs, tF, [&](int row, float v) { st_sys(s.x + row, xs[d.F + row] + v); });
+    rs.run(xs, [&](int row, float v) {
+      if (lane == 0) st_sys(s.x + row, xs[d.F + row] + v);
+    });
     p_arrive(a, P + 4);
     if (l + 1 < d.L)
-      prefetch_plain<WT, 2, VD>(reinterpret_cast<const WT *>(a.tl[l + 1].w_in), 3 * d.D, d.D, tD);
+      p_begin(rs, a.tl[l + 1].w_in, a.tl[l + 1].s_in, d.D, 3 * d.D / 2, 2);
     else
-      prefetch_plain<WT, 2, VD>(reinterpret_cast<const WT *>(a.w_text), d.Vt, d.D, tD);
+      p_begin(rs, a.w_text, a.s_text, d.D, d.Vt, 1);
     if (!p_wait(a, P + 4, &s_ok)) return;
   }
 
@@ -670,20 +532,21 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
     if (blockIdx.x == 0)
       for (int k = threadIdx.x; k < d.D; k += PBLOCK) s.hidden[k] = xs[k];
     ArgBest best = arg_none();
-    Wt = reinterpret_cast<const WT *>(a.w_text);
-    run_plain<WT, 2, VD>(Wt, a.s_text, d.Vt, d.D, xs, tD, [&](int row, float v) {
+    rs.run(xs, [&](int row, float v) {
+      if (lane != 0) return;
       s.text_logits[row] = v;
       best = arg_take(best, v, row);
     });
     best = wave_arg(best);
     best = block_arg(best, wb);
     if (threadIdx.x == 0) st_sys_arg(s.am_part + blockIdx.x, best);
-    Wt = reinterpret_cast<const WT *>(a.w_din);
-    prefetch_plain<WT, 2, VD>(Wt, d.Q * d.Dd, d.D, tD);
-    run_plain<WT, 2, VD>(Wt, a.s_din, d.Q * d.Dd, d.D, xs, tD, [&](int row, float v) { st_sys(s.din + row, v); });
+    p_begin(rs, a.w_din, a.s_din, d.D, d.Q * d.Dd, 1);
+    rs.run(xs, [&](int row, float v) {
+      if (lane == 0) st_sys(s.din + row, v);
+    });
   }
   p_arrive(a, P_HEAD);
-  prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(a.dl[0].w_in), 3 * d.Dd, d.Dd, tS);
+  p_begin(rs, a.dl[0].w_in, a.dl[0].s_in, d.Dd, 3 * d.Dd, 1);
   if (!p_wait(a, P_HEAD, &s_ok)) return;
 
   // ---- a8: depformer, 8 sequential codebook steps ----
@@ -709,21 +572,21 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         stage_rms<PBLOCK, true, UDd>(s.y, lp.norm1, d.Dd, d.eps, xs, red);
       }
       float *kvbase = s.dkv + ((size_t)j * d.Q + cb) * 2 * d.Dd;
-      Wt = reinterpret_cast<const WT *>(lp.w_in);
-      run_plain<WT, 2, VDd>(Wt, lp.s_in, 3 * d.Dd, d.Dd, xs, tS, [&](int row, float v) {
+      rs.run(xs, [&](int row, float v) {
+        if (lane != 0) return;
         if (row < d.Dd)
           st_sys(s.dq + row, v);
         else
           st_sys(kvbase + row - d.Dd, v);
       });
       p_arrive(a, P);
-      prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(lp.w_out), d.Dd, d.Dd, tS);
+      p_begin(rs, lp.w_out, lp.s_out, d.Dd, d.Dd, 1);
       if (!p_wait(a, P, &s_ok)) return;
 
       // attention of dq over the cb + 1 entries of layer j (every block), then out_proj + residual
       float *ys = xs + d.Dd;  // y, for the residual
       {
-        constexpr int UY = UDd;  // y fits one pass when the tile width covers Dd
+        constexpr int UY = UDd;  // y in UDd loads per thread (one pass when Dd <= 2 * UDd * PBLOCK)
         uint64_t yv[UY];
 #pragma unroll
         for (int u = 0; u < UY; ++u) {
@@ -795,28 +658,39 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         }
         __syncthreads();
       }
-      Wt = reinterpret_cast<const WT *>(lp.w_out);
-      run_plain<WT, 2, VDd>(Wt, lp.s_out, d.Dd, d.Dd, xs, tS, [&](int row, float v) { st_sys(s.y + row, ys[row] + v); });
+      rs.run(xs, [&](int row, float v) {
+        if (lane == 0) st_sys(s.y + row, ys[row] + v);
+      });
       p_arrive(a, P + 1);
-      prefetch_gate<WT, VDd>(reinterpret_cast<const WT *>(lp.w_gin), d.Fd, d.Dd, tS);
+      p_begin(rs, lp.w_gin, lp.s_gin, d.Dd, d.Fd, 2);
       if (!p_wait(a, P + 1, &s_ok)) return;
 
-      // norm2 + gate_in + silu * mult
+      // norm2 + gate_in + silu * mult (rows interleaved)
       stage_rms<PBLOCK, true, UDd>(s.y, lp.norm2, d.Dd, d.eps, xs, red);
-      run_gate<WT, VDd>(reinterpret_cast<const WT *>(lp.w_gin), lp.s_gin, d.Fd, d.Dd, xs, tS, s.da);
+      {
+        float gv = 0.f;
+        rs.run(xs, [&](int row, float v) {
+          if (lane != 0) return;
+          if ((row & 1) == 0)
+            gv = v;
+          else
+            st_sys(s.da + (row >> 1), silu(gv) * v);
+        });
+      }
       p_arrive(a, P + 2);
-      prefetch_plain<WT, 2, VFd>(reinterpret_cast<const WT *>(lp.w_gout), d.Dd, d.Fd, tT);
+      p_begin(rs, lp.w_gout, lp.s_gout, d.Fd, d.Dd, 1);
       if (!p_wait(a, P + 2, &s_ok)) return;
 
       // gate_out + residual (y staged next to da)
       stage2_sys<UFd, UDd>(s.da, d.Fd, xs, s.y, d.Dd, xs + d.Fd);
-      Wt = reinterpret_cast<const WT *>(lp.w_gout);
-      run_plain<WT, 2, VFd>(Wt, lp.s_gout, d.Dd, d.Fd, xs, tT, [&](int row, float v) { st_sys(s.y + row, xs[d.Fd + row] + v); });
+      rs.run(xs, [&](int row, float v) {
+        if (lane == 0) st_sys(s.y + row, xs[d.Fd + row] + v);
+      });
       p_arrive(a, P + 3);
       if (j + 1 < d.Ld)
-        prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(a.dl[(j + 1) * d.Q + cb].w_in), 3 * d.Dd, d.Dd, tS);
+        p_begin(rs, a.dl[(j + 1) * d.Q + cb].w_in, a.dl[(j + 1) * d.Q + cb].s_in, d.Dd, 3 * d.Dd, 1);
       else
-        prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(a.w_lin[cb]), d.Va, d.Dd, tS);
+        p_begin(rs, a.w_lin[cb], a.s_lin[cb], d.Dd, d.Va, 1);
       if (!p_wait(a, P + 3, &s_ok)) return;
     }
     // codebook head (no norm) with argmax partials
@@ -824,9 +698,9 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
       const int P = PC + 4 * d.Ld;
       stage_vec<PBLOCK, true, UDd>(s.y, d.Dd, xs);
       ArgBest best = arg_none();
-      Wt = reinterpret_cast<const WT *>(a.w_lin[cb]);
       float *lg = s.audio_logits + (size_t)cb * d.Va;
-      run_plain<WT, 2, VDd>(Wt, a.s_lin[cb], d.Va, d.Dd, xs, tS, [&](int row, float v) {
+      rs.run(xs, [&](int row, float v) {
+        if (lane != 0) return;
         lg[row] = v;
         best = arg_take(best, v, row);
       });
@@ -835,7 +709,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
       if (threadIdx.x == 0) st_sys_arg(s.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS + blockIdx.x, best);
       p_arrive(a, P);
       if (cb + 1 < d.Q) {
-        prefetch_plain<WT, 2, VDd>(reinterpret_cast<const WT *>(a.dl[cb + 1].w_in), 3 * d.Dd, d.Dd, tS);
+        p_begin(rs, a.dl[cb + 1].w_in, a.dl[cb + 1].s_in, d.Dd, 3 * d.Dd, 1);
         if (!p_wait(a, P, &s_ok)) return;
       }
     }

@@ -1,10 +1,9 @@
 // Frame-step kernels for gfx950.  Each kernel is one stage of the Moshi RQ-Transformer frame as
 // the docs.rs page "inferencelayer 0.2.4 src/moshi_lm.rs" defines it (cited as [LM]).
 //
-// Weight-streaming projections share one pattern: every wave owns whole output rows (a row
-// group), issues all loads of its first group BEFORE the block's prologue (norm, attention, ...)
-// and prefetches its next group while it reduces the current one; the grid is sized to the CUs
-// and strides over row groups.  Kernels used by several stages take the stage id as a template
+// Weight-streaming projections share one pattern (RowStream): every wave owns a balanced,
+// contiguous range of output rows, starts streaming them (two 8 KB chunks in flight) BEFORE the
+// block's prologue (norm, attention, ...), and keeps two chunks in flight until its range ends.  Kernels used by several stages take the stage id as a template
 // tag so that each stage is its own symbol in profiler traces.
 #pragma once
 #include "device_common.h"
@@ -134,66 +133,61 @@ __global__ __launch_bounds__(BLOCK) void k_embed_begin(Dims d, Bufs s, const ET 
 
 // --------------------------------------------------------------------------------------------
 // a4.1: x -> rms_norm(norm1) -> fused q|k|v rows -> interleaved rope on q, k at pos = offset ->
-// q to s.q, k and v to KV slot offset % cap ([LM] temporal_step, rope_row).  A wave's row group
-// is the pair (2i, 2i+1), i.e. one rope pair.  Dynamic LDS: D floats.
+// q to s.q, k and v to KV slot offset % cap ([LM] temporal_step, rope_row).  Waves own balanced
+// ranges of row pairs (2i, 2i+1), i.e. whole rope pairs.  Dynamic LDS: D + hd floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, typename KT, int VPL>
+template <typename WT, typename KT>
 __global__ __launch_bounds__(BLOCK) void k_qkv_rope(Dims d, Bufs s, KV<KT> kv, const WT *__restrict__ w,
                                                     const float *__restrict__ wscale,
                                                     const float *__restrict__ norm, int layer, int b0) {
-  extern __shared__ float xs[];
+  extern __shared__ float xs[];  // D floats, then the rope table: cos, sin of pair i at [2i], [2i+1]
   __shared__ float red[NWAVES];
   const int b = b0 + blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int npairs = 3 * d.D / 2;
-  const int stride = gridDim.x * NWAVES;
-  int pr = blockIdx.x * NWAVES + wave;
-  RowTile<WT, 2, VPL> t;
-  int rows[2] = {min(2 * pr, 3 * d.D - 2), min(2 * pr, 3 * d.D - 2) + 1};
-  if (pr < npairs) t.load(w, d.D, rows);
-  stage_rms(s.x + (size_t)b * d.D, norm, d.D, d.eps, xs, red);
+  const int lane = threadIdx.x & 63;
+  int lo, hi;
+  wave_rows(blockIdx.x * NWAVES + wave_id(), gridDim.x * NWAVES, 3 * d.D / 2, 2, lo, hi);
+  RowStream<WT> st;
+  st.begin(w, wscale, d.D, lo, hi);
   const int64_t pos = s.offset[b];
   const int slot = (int)(pos % d.cap);
-  for (; pr < npairs; pr += stride) {
-    float acc[2];
-    t.dot(w, d.D, xs, acc);
-    const int r0 = 2 * pr;
-    if (pr + stride < npairs) {
-      const int nr[2] = {2 * (pr + stride), 2 * (pr + stride) + 1};
-      t.load(w, d.D, nr);
-    }
-    acc[0] = wave_sum(acc[0]);
-    acc[1] = wave_sum(acc[1]);
-    if (lane == 0) {
-      float v0 = acc[0], v1 = acc[1];
-      if (wscale) {
-        v0 *= wscale[r0];
-        v1 *= wscale[r0 + 1];
-      }
-      const int part = r0 / d.D;  // 0 q, 1 k, 2 v
-      const int rr = r0 - part * d.D;
-      const int h = rr / d.hd, e = rr - h * d.hd;
-      if (part < 2) {
-        const float ang = s.rope_freq[e >> 1] * (float)pos;
-        double sd, cd;
-        sincos((double)ang, &sd, &cd);
-        const float sn = (float)sd, cs = (float)cd;
-        const float a0 = v0 * cs - v1 * sn;
-        const float a1 = v0 * sn + v1 * cs;
-        v0 = a0;
-        v1 = a1;
-      }
-      if (part == 0) {
-        s.q[(size_t)b * d.D + rr] = v0;
-        s.q[(size_t)b * d.D + rr + 1] = v1;
-      } else {
-        KT *cache = part == 1 ? kv.k : kv.v;
-        const size_t idx = ((((size_t)b * d.L + layer) * d.H + h) * d.cap + slot) * d.hd + e;
-        cache[idx] = from_f<KT>(v0);
-        cache[idx + 1] = from_f<KT>(v1);
-      }
-    }
+  float *rcs = xs + d.D;
+  for (int i = threadIdx.x; i < d.hd / 2; i += BLOCK) {  // angle f_i * pos in float32, sin/cos in double
+    const float ang = s.rope_freq[i] * (float)pos;
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    rcs[2 * i] = (float)cd;
+    rcs[2 * i + 1] = (float)sd;
   }
+  stage_rms(s.x + (size_t)b * d.D, norm, d.D, d.eps, xs, red);  // its barriers publish rcs
+  float pend = 0.f;
+  st.run(xs, [&](int row, float v) {
+    if (lane != 0) return;
+    if ((row & 1) == 0) {
+      pend = v;
+      return;
+    }
+    const int r0 = row - 1;
+    float v0 = pend, v1 = v;
+    const int part = r0 / d.D;  // 0 q, 1 k, 2 v
+    const int rr = r0 - part * d.D;
+    const int h = rr / d.hd, e = rr - h * d.hd;
+    if (part < 2) {
+      const float cs = rcs[e], sn = rcs[e + 1];
+      const float a0 = v0 * cs - v1 * sn;
+      const float a1 = v0 * sn + v1 * cs;
+      v0 = a0;
+      v1 = a1;
+    }
+    if (part == 0) {
+      s.q[(size_t)b * d.D + rr] = v0;
+      s.q[(size_t)b * d.D + rr + 1] = v1;
+    } else {
+      KT *cache = part == 1 ? kv.k : kv.v;
+      const size_t idx = ((((size_t)b * d.L + layer) * d.H + h) * d.cap + slot) * d.hd + e;
+      cache[idx] = from_f<KT>(v0);
+      cache[idx + 1] = from_f<KT>(v1);
+    }
+  });
 }
 
 // --------------------------------------------------------------------------------------------
@@ -335,54 +329,48 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
 
 // --------------------------------------------------------------------------------------------
 // Projection of `in` into `out`: out[r] = (W . in)[r] (STORE) or out[r] += (W . in)[r] (residual
-// add: [LM] out_proj / gate_out followed by the residual).  R rows per group.  Dynamic LDS: K.
+// add: [LM] out_proj / gate_out followed by the residual).  Dynamic LDS: K floats, plus (ADD) one
+// float per row of the block's share.
 // --------------------------------------------------------------------------------------------
-template <typename WT, int R, int VPL, bool ADD, int TAG>
+template <typename WT, bool ADD, int TAG>
 __global__ __launch_bounds__(BLOCK) void k_gemv(const WT *__restrict__ w, const float *__restrict__ wscale, int N,
                                                 int K, const float *__restrict__ in, int in_ld,
                                                 float *__restrict__ out, int out_ld, int b0) {
-  extern __shared__ float xs[];
+  extern __shared__ float xs[];  // K floats, then (ADD) this block's row results
   const int b = b0 + blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ngroups = (N + R - 1) / R;
-  const int stride = gridDim.x * NWAVES;
-  int gi = blockIdx.x * NWAVES + wave;
-  RowTile<WT, R, VPL> t;
-  int rows[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, N - 1);
-  if (gi < ngroups) t.load(w, K, rows);
+  const int lane = threadIdx.x & 63;
+  const int w0 = blockIdx.x * NWAVES, TW = gridDim.x * NWAVES;
+  int lo, hi, blo, bhi;
+  wave_rows(w0 + wave_id(), TW, N, 1, lo, hi);
+  RowStream<WT> st;
+  st.begin(w, wscale, K, lo, hi);
   stage_vec(in + (size_t)b * in_ld, K, xs);
-  for (; gi < ngroups; gi += stride) {
-    float acc[R];
-    t.dot(w, K, xs, acc);
-    if (gi + stride < ngroups) {
-      int nr[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) nr[r] = min((gi + stride) * R + r, N - 1);
-      t.load(w, K, nr);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = wave_sum(acc[r]);
-      const int row = gi * R + r;
-      if (lane == 0 && row < N) {
-        const float y = wscale ? v * wscale[row] : v;
-        if (ADD)
-          out[(size_t)b * out_ld + row] += y;
-        else
-          out[(size_t)b * out_ld + row] = y;
-      }
-    }
+  float *o = out + (size_t)b * out_ld;
+  if (!ADD) {
+    st.run(xs, [&](int row, float v) {
+      if (lane == 0) o[row] = v;
+    });
+    return;
   }
+  // residual add after the stream: a load of o inside the loop would drain the chunks in flight
+  int t0, t1;
+  wave_rows(w0, TW, N, 1, blo, t1);
+  wave_rows(w0 + NWAVES - 1, TW, N, 1, t0, bhi);
+  float *ys = xs + K;
+  st.run(xs, [&](int row, float v) {
+    if (lane == 0) ys[row - blo] = v;
+  });
+  __syncthreads();
+  for (int r = blo + threadIdx.x; r < bhi; r += BLOCK) o[r] += ys[r - blo];
 }
 
 // --------------------------------------------------------------------------------------------
-// a5 (first half): h = rms_norm(x; norm2), g = linear_in . h, a[j] = silu(g[j]) * g[F + j]
-// ([LM] temporal_step / depformer_cycle gating, rows packed [gate | mult]).  A wave's row group
-// is the pair (j, F + j).  Dynamic LDS: K floats.
+// a5 (first half): h = rms_norm(x; norm2), g = linear_in . h, a[j] = silu(g_gate[j]) * g_mult[j]
+// ([LM] temporal_step / depformer_cycle gating).  The device copy of linear_in has its rows
+// interleaved at load time (row 2j = gate row j, row 2j+1 = mult row j), so a wave's balanced range
+// of row pairs yields whole outputs.  Dynamic LDS: K floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, int VPL, int TAG>
+template <typename WT, int TAG>
 __global__ __launch_bounds__(BLOCK) void k_gate(const WT *__restrict__ w, const float *__restrict__ wscale, int F,
                                                 int K, const float *__restrict__ x, int x_ld,
                                                 const float *__restrict__ norm, float eps,
@@ -390,29 +378,20 @@ __global__ __launch_bounds__(BLOCK) void k_gate(const WT *__restrict__ w, const 
   extern __shared__ float xs[];
   __shared__ float red[NWAVES];
   const int b = b0 + blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int stride = gridDim.x * NWAVES;
-  int j = blockIdx.x * NWAVES + wave;
-  RowTile<WT, 2, VPL> t;
-  int rows[2] = {min(j, F - 1), F + min(j, F - 1)};
-  if (j < F) t.load(w, K, rows);
+  const int lane = threadIdx.x & 63;
+  int lo, hi;
+  wave_rows(blockIdx.x * NWAVES + wave_id(), gridDim.x * NWAVES, F, 2, lo, hi);
+  RowStream<WT> st;
+  st.begin(w, wscale, K, lo, hi);
   stage_rms(x + (size_t)b * x_ld, norm, K, eps, xs, red);
-  for (; j < F; j += stride) {
-    float acc[2];
-    t.dot(w, K, xs, acc);
-    if (j + stride < F) {
-      const int nr[2] = {j + stride, F + j + stride};
-      t.load(w, K, nr);
+  float gv = 0.f;
+  st.run(xs, [&](int row, float v) {
+    if ((row & 1) == 0) {
+      gv = v;
+      return;
     }
-    float gv = wave_sum(acc[0]), mv = wave_sum(acc[1]);
-    if (lane == 0) {
-      if (wscale) {
-        gv *= wscale[j];
-        mv *= wscale[F + j];
-      }
-      a[(size_t)b * a_ld + j] = silu(gv) * mv;
-    }
-  }
+    if (lane == 0) a[(size_t)b * a_ld + (row >> 1)] = silu(gv) * v;
+  });
 }
 
 // --------------------------------------------------------------------------------------------
@@ -421,7 +400,7 @@ __global__ __launch_bounds__(BLOCK) void k_gate(const WT *__restrict__ w, const 
 // am_part[blockIdx.x]; the kernel that needs the token merges them.  With hid_out set, block 0
 // also stores the normalised vector (the post-out_norm hidden).  Dynamic LDS: K floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, int R, int VPL, int TAG>
+template <typename WT, int TAG>
 __global__ __launch_bounds__(BLOCK) void k_head(const WT *__restrict__ w, const float *__restrict__ wscale, int N,
                                                 int K, const float *__restrict__ src, int src_ld,
                                                 const float *__restrict__ norm, float eps,
@@ -432,14 +411,10 @@ __global__ __launch_bounds__(BLOCK) void k_head(const WT *__restrict__ w, const 
   __shared__ ArgBest wbest[NWAVES];
   const int b = b0 + blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ngroups = (N + R - 1) / R;
-  const int stride = gridDim.x * NWAVES;
-  int gi = blockIdx.x * NWAVES + wave;
-  RowTile<WT, R, VPL> t;
-  int rows[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, N - 1);
-  if (gi < ngroups) t.load(w, K, rows);
+  int lo, hi;
+  wave_rows(blockIdx.x * NWAVES + wave_id(), gridDim.x * NWAVES, N, 1, lo, hi);
+  RowStream<WT> st;
+  st.begin(w, wscale, K, lo, hi);
   if (norm)
     stage_rms(src + (size_t)b * src_ld, norm, K, eps, xs, red);
   else
@@ -447,26 +422,12 @@ __global__ __launch_bounds__(BLOCK) void k_head(const WT *__restrict__ w, const 
   if (hid_out && blockIdx.x == 0)
     for (int k = threadIdx.x; k < K; k += BLOCK) hid_out[(size_t)b * src_ld + k] = xs[k];
   ArgBest best = arg_none();
-  for (; gi < ngroups; gi += stride) {
-    float acc[R];
-    t.dot(w, K, xs, acc);
-    if (gi + stride < ngroups) {
-      int nr[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) nr[r] = min((gi + stride) * R + r, N - 1);
-      t.load(w, K, nr);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float v = wave_sum(acc[r]);
-      const int row = gi * R + r;
-      if (lane == 0 && row < N) {
-        if (wscale) v *= wscale[row];
-        logits[(size_t)b * logits_ld + row] = v;
-        best = arg_take(best, v, row);
-      }
-    }
-  }
+  float *lg = logits + (size_t)b * logits_ld;
+  st.run(xs, [&](int row, float v) {
+    if (lane != 0) return;
+    lg[row] = v;
+    best = arg_take(best, v, row);
+  });
   if (lane == 0) wbest[wave] = best;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -482,7 +443,7 @@ __global__ __launch_bounds__(BLOCK) void k_head(const WT *__restrict__ w, const 
 // q|k|v rows of in_projs[j][cb] (no rope) -> q to dq, k and v to the per-frame cache entry
 // (j, cb) ([LM] depformer_cycle).  Dynamic LDS: Dd floats.
 // --------------------------------------------------------------------------------------------
-template <typename WT, typename ET, int R, int VPL>
+template <typename WT, typename ET>
 __global__ __launch_bounds__(BLOCK) void k_dep_qkv(Dims d, Bufs s, const WT *__restrict__ w,
                                                    const float *__restrict__ wscale, const float *__restrict__ norm,
                                                    const ET *__restrict__ table, int layer, int cb, int prev_parts,
@@ -491,16 +452,11 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv(Dims d, Bufs s, const WT *__r
   __shared__ float red[NWAVES];
   const int b = b0 + blockIdx.y;
   const int Dd = d.Dd;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int N = 3 * Dd;
-  const int ngroups = (N + R - 1) / R;
-  const int stride = gridDim.x * NWAVES;
-  int gi = blockIdx.x * NWAVES + wave;
-  RowTile<WT, R, VPL> t;
-  int rows[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, N - 1);
-  if (gi < ngroups) t.load(w, Dd, rows);
+  const int lane = threadIdx.x & 63;
+  int lo, hi;
+  wave_rows(blockIdx.x * NWAVES + wave_id(), gridDim.x * NWAVES, 3 * Dd, 1, lo, hi);
+  RowStream<WT> st;
+  st.begin(w, wscale, Dd, lo, hi);
   float *y = s.y + (size_t)b * Dd;
   if (layer == 0) {
     const int prev =
@@ -518,51 +474,32 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv(Dims d, Bufs s, const WT *__r
     stage_rms(y, norm, Dd, d.eps, xs, red);
   }
   float *kvbase = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q + cb) * 2) * Dd;
-  for (; gi < ngroups; gi += stride) {
-    float acc[R];
-    t.dot(w, Dd, xs, acc);
-    if (gi + stride < ngroups) {
-      int nr[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) nr[r] = min((gi + stride) * R + r, N - 1);
-      t.load(w, Dd, nr);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float v = wave_sum(acc[r]);
-      const int row = gi * R + r;
-      if (lane == 0 && row < N) {
-        if (wscale) v *= wscale[row];
-        if (row < Dd)
-          s.dq[(size_t)b * Dd + row] = v;
-        else
-          kvbase[row - Dd] = v;  // k at [0, Dd), v at [Dd, 2 Dd)
-      }
-    }
-  }
+  st.run(xs, [&](int row, float v) {
+    if (lane != 0) return;
+    if (row < Dd)
+      s.dq[(size_t)b * Dd + row] = v;
+    else
+      kvbase[row - Dd] = v;  // k at [0, Dd), v at [Dd, 2 Dd)
+  });
 }
 
 // --------------------------------------------------------------------------------------------
 // a8 depformer step cb, layer j, attention + out_proj: every block recomputes the attention of
 // dq over the cb + 1 cache entries of layer j ([LM] attend; weights e_p / den) into LDS -- 16
 // lanes per head, EPL dims per lane, all loads issued at once -- then y[r] += out_projs[j][cb] . o.
-// Dynamic LDS: Dd floats.
+// Dynamic LDS: Dd floats plus one float per row of the block's share.
 // --------------------------------------------------------------------------------------------
-template <typename WT, int R, int VPL, int EPL>
+template <typename WT, int EPL>
 __global__ __launch_bounds__(BLOCK) void k_dep_out(Dims d, Bufs s, const WT *__restrict__ w,
                                                    const float *__restrict__ wscale, int layer, int cb, int b0) {
   extern __shared__ float xs[];
   const int b = b0 + blockIdx.y;
   const int Dd = d.Dd, hdd = d.hdd;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
-  const int ngroups = (Dd + R - 1) / R;
-  const int stride = gridDim.x * NWAVES;
-  int gi = blockIdx.x * NWAVES + wave;
-  RowTile<WT, R, VPL> t;
-  int rows[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rows[r] = min(gi * R + r, Dd - 1);
-  if (gi < ngroups) t.load(w, Dd, rows);
+  int lo, hi;
+  wave_rows(blockIdx.x * NWAVES + wave_id(), gridDim.x * NWAVES, Dd, 1, lo, hi);
+  RowStream<WT> st;
+  st.begin(w, wscale, Dd, lo, hi);
 
   const float *q = s.dq + (size_t)b * Dd;
   const float *kv0 = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q) * 2) * Dd;
@@ -620,22 +557,16 @@ __global__ __launch_bounds__(BLOCK) void k_dep_out(Dims d, Bufs s, const WT *__r
     for (int i = 0; i < EPL; ++i) xs[e0 + i] = o[i];
   }
   __syncthreads();
-  for (; gi < ngroups; gi += stride) {
-    float acc[R];
-    t.dot(w, Dd, xs, acc);
-    if (gi + stride < ngroups) {
-      int nr[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) nr[r] = min((gi + stride) * R + r, Dd - 1);
-      t.load(w, Dd, nr);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float v = wave_sum(acc[r]);
-      const int row = gi * R + r;
-      if (lane == 0 && row < Dd) s.y[(size_t)b * Dd + row] += wscale ? v * wscale[row] : v;
-    }
-  }
+  int blo, bhi, t0, t1;
+  wave_rows(blockIdx.x * NWAVES, gridDim.x * NWAVES, Dd, 1, blo, t1);
+  wave_rows(blockIdx.x * NWAVES + NWAVES - 1, gridDim.x * NWAVES, Dd, 1, t0, bhi);
+  float *ys = xs + Dd;  // this block's row results; the residual add follows the stream
+  st.run(xs, [&](int row, float v) {
+    if (lane == 0) ys[row - blo] = v;
+  });
+  __syncthreads();
+  float *yb = s.y + (size_t)b * Dd;
+  for (int r = blo + threadIdx.x; r < bhi; r += BLOCK) yb[r] += ys[r - blo];
 }
 
 // --------------------------------------------------------------------------------------------

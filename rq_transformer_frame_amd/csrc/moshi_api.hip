@@ -27,6 +27,7 @@ struct Slot {
   std::string name;
   int64_t rows, cols;  // cols == 0 for 1-D
   Kind kind;
+  bool pair_rows = false;    // gated linear_in: rows stored interleaved (gate j, mult j)
   size_t off = 0, soff = 0;  // byte offsets of data / int8 scales in the weight arena
   bool loaded = false;
 };
@@ -186,6 +187,7 @@ void plan_weights(moshi_state *s) {
     lw.in = add(p + ".self_attn.in_projs.0.weight", 3 * D, D, K_LINEAR);
     lw.out = add(p + ".self_attn.out_projs.0.weight", D, D, K_LINEAR);
     lw.gin = add(p + ".gating.linear_in.weight", 2 * F, D, K_LINEAR);
+    s->slots[lw.gin].pair_rows = true;
     lw.gout = add(p + ".gating.linear_out.weight", D, F, K_LINEAR);
     for (int i : {lw.norm1, lw.norm2, lw.in, lw.out, lw.gin, lw.gout}) {
       place(i);
@@ -232,6 +234,7 @@ void plan_weights(moshi_state *s) {
       lw.in = add(p + ".self_attn.in_projs." + std::to_string(k) + ".weight", 3 * Dd, Dd, K_LINEAR);
       lw.out = add(p + ".self_attn.out_projs." + std::to_string(k) + ".weight", Dd, Dd, K_LINEAR);
       lw.gin = add(p + ".gating." + std::to_string(k) + ".linear_in.weight", 2 * Fd, Dd, K_LINEAR);
+      s->slots[lw.gin].pair_rows = true;
       lw.gout = add(p + ".gating." + std::to_string(k) + ".linear_out.weight", Dd, Fd, K_LINEAR);
       for (int i : {lw.in, lw.out, lw.gin, lw.gout}) {
         place(i);
@@ -347,7 +350,7 @@ moshi_status alloc_session(moshi_state *s) {
 // ---------------------------------------------------------------------------------------------
 // Kernel launch configuration
 // ---------------------------------------------------------------------------------------------
-constexpr int BLOCKS_PER_CU = 4;  // resident blocks per CU targeted by the grid-stride kernels
+constexpr int BLOCKS_PER_CU = 4;  // resident blocks per CU targeted by the streaming kernels
 
 int blocks_for(int64_t units, int per_block, int cap) {
   int64_t g = (units + per_block - 1) / per_block;
@@ -355,87 +358,77 @@ int blocks_for(int64_t units, int per_block, int cap) {
   return (int)std::min<int64_t>(g, cap);
 }
 
-// Calls f(std::integral_constant<int, VPL>) with the register-tile width for input width K: the
-// smallest specialised count of 16-byte vectors per lane that covers a row, or 0 (generic loop).
-template <typename WT, typename F>
-void with_vpl(int K, F &&f) {
-  const int need = (K / mk::WVec<WT>::N + mk::WAVE - 1) / mk::WAVE;
-  using std::integral_constant;
-  if constexpr (std::is_same<WT, bf16_t>::value) {
-    if (need <= 2) return f(integral_constant<int, 2>{});
-    if (need <= 6) return f(integral_constant<int, 6>{});
-    if (need <= 8) return f(integral_constant<int, 8>{});
-    if (need <= 22) return f(integral_constant<int, 22>{});
-  } else if constexpr (std::is_same<WT, int8_t>::value) {
-    if (need <= 1) return f(integral_constant<int, 1>{});
-    if (need <= 3) return f(integral_constant<int, 3>{});
-    if (need <= 4) return f(integral_constant<int, 4>{});
-    if (need <= 11) return f(integral_constant<int, 11>{});
-  } else {
-    if (need <= 1) return f(integral_constant<int, 1>{});
-    if (need <= 3) return f(integral_constant<int, 3>{});
-  }
-  f(integral_constant<int, 0>{});
+// Blocks of a projection over `units` equal work units (a row, or a row pair): the fewest waves
+// that reach the smallest possible largest share with at most max_blocks blocks, so that shares
+// differ by at most one unit and no wave idles for a whole unit.
+int proj_blocks(int64_t units, int max_blocks) {
+  const int64_t twmax = (int64_t)max_blocks * mk::NWAVES;
+  const int64_t m = std::max<int64_t>(1, (units + twmax - 1) / twmax);
+  const int64_t tw = (units + m - 1) / m;
+  return (int)std::max<int64_t>(1, (tw + mk::NWAVES - 1) / mk::NWAVES);
 }
 
-// The register-tile width with_vpl picks for input width K.
-template <typename WT>
-int vpl_of(int K) {
-  int v = -1;
-  with_vpl<WT>(K, [&](auto t) { v = decltype(t)::value; });
-  return v;
+// Most rows one block of `blocks` owns (the LDS it needs for its row results).
+int64_t block_rows(int64_t units, int P, int blocks) {
+  const int64_t tw = (int64_t)blocks * mk::NWAVES;
+  return (units + tw - 1) / tw * mk::NWAVES * P;
 }
 
-// Compiled persistent-kernel variants: (band, temporal head dim, depformer head dim / 16, tile
-// widths for inputs of width D, F, Dd, Fd).
+// Compiled persistent-kernel variants: (band, temporal head dim, depformer head dim / 16, staging
+// loads per thread for inputs of width D, F, Dd, Fd).  The staging counts only set how many loads
+// each thread issues per pass, so a shape without its own variant runs the generic one.
 struct PVariant {
-  int band, hd, depl, vd, vf, vdd, vfd;
+  int band, hd, depl, ud, uf, udd, ufd;
   const void *fn;
 };
 
-template <typename WT, typename ET, typename KT, int HD, int DEPL, int VD, int VF, int VDd, int VFd>
+template <typename WT, typename ET, typename KT, int HD, int DEPL, int UD, int UF, int UDd, int UFd>
 PVariant pvariant(int band) {
-  return PVariant{band, HD, DEPL, VD, VF, VDd, VFd,
-                  reinterpret_cast<const void *>(&mk::k_frame_persistent<WT, ET, KT, HD, DEPL, VD, VF, VDd, VFd>)};
+  return PVariant{band, HD, DEPL, UD, UF, UDd, UFd,
+                  reinterpret_cast<const void *>(&mk::k_frame_persistent<WT, ET, KT, HD, DEPL, UD, UF, UDd, UFd>)};
 }
 
 const PVariant *persistent_variants(int *n) {
   static const PVariant v[] = {
-      // Moshi-7B shape
-      pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 8, 22, 2, 6>(MOSHI_BAND_BF16),
+      // Moshi-7B shape (d4096 / ffn 11264, depformer d1024 / ffn 2816)
+      pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 4, 11, 1, 3>(MOSHI_BAND_BF16),
       pvariant<int8_t, bf16_t, bf16_t, 128, 4, 4, 11, 1, 3>(MOSHI_BAND_I8),
-      // tiny RQ-Transformer (d256 / d128, head dim 64)
-      pvariant<float, float, float, 64, 4, 1, 3, 1, 3>(MOSHI_BAND_F32),
-      pvariant<bf16_t, bf16_t, bf16_t, 64, 4, 2, 2, 2, 2>(MOSHI_BAND_BF16),
+      // small shapes, one pass per 1024-wide input
+      pvariant<float, float, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_F32),
+      pvariant<bf16_t, bf16_t, bf16_t, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_BF16),
       pvariant<int8_t, bf16_t, bf16_t, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
+      pvariant<float, float, float, 128, 4, 1, 1, 1, 1>(MOSHI_BAND_F32),
+      pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 1, 1, 1, 1>(MOSHI_BAND_BF16),
+      pvariant<int8_t, bf16_t, bf16_t, 128, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
   };
   *n = (int)(sizeof(v) / sizeof(v[0]));
   return v;
 }
 
+int stage_passes(int K) { return (K / 2 + mk::PBLOCK - 1) / mk::PBLOCK; }
+
 const void *select_persistent(const moshi_config &c, size_t *lds) {
   const int D = c.d_model, F = c.ffn_hidden, Dd = c.dep_d_model, Fd = c.dep_ffn_hidden;
   const int hd = D / c.n_heads, hdd = Dd / c.dep_heads;
-  int vd, vf, vdd, vfd;
-  if (c.band == MOSHI_BAND_F32) {
-    vd = vpl_of<float>(D), vf = vpl_of<float>(F), vdd = vpl_of<float>(Dd), vfd = vpl_of<float>(Fd);
-  } else if (c.band == MOSHI_BAND_BF16) {
-    vd = vpl_of<bf16_t>(D), vf = vpl_of<bf16_t>(F), vdd = vpl_of<bf16_t>(Dd), vfd = vpl_of<bf16_t>(Fd);
-  } else {
-    vd = vpl_of<int8_t>(D), vf = vpl_of<int8_t>(F), vdd = vpl_of<int8_t>(Dd), vfd = vpl_of<int8_t>(Fd);
-  }
   if (c.dep_q > mk::PQ) return nullptr;
+  const int ud = stage_passes(D), uf = stage_passes(F), udd = stage_passes(Dd), ufd = stage_passes(Fd);
   int n = 0;
   const PVariant *v = persistent_variants(&n);
-  for (int i = 0; i < n; ++i)
-    if (v[i].band == c.band && v[i].hd == hd && v[i].depl * 16 == hdd && v[i].vd == vd && v[i].vf == vf &&
-        v[i].vdd == vdd && v[i].vfd == vfd) {
-      const size_t fl = std::max({(size_t)2 * D, (size_t)F + D, (size_t)2 * Dd, (size_t)Fd + Dd,
-                                  (size_t)mk::ATTN_MAX_S * (hd + 2) + mk::ATTN_MAX_S});
-      *lds = fl * 4;
-      return v[i].fn;
+  const PVariant *pick = nullptr;
+  for (int i = 0; i < n; ++i) {
+    if (v[i].band != c.band || v[i].hd != hd || v[i].depl * 16 != hdd) continue;
+    if (v[i].ud == ud && v[i].uf == uf && v[i].udd == udd && v[i].ufd == ufd) {
+      pick = &v[i];
+      break;
     }
-  return nullptr;
+    // the depformer attention phase stages y in a single pass of udd loads per thread
+    if (!pick && v[i].ud == 1 && v[i].uf == 1 && v[i].udd >= udd && v[i].ufd == 1) pick = &v[i];
+  }
+  if (!pick) return nullptr;
+  const size_t fl = std::max({(size_t)2 * D, (size_t)F + D, (size_t)2 * Dd, (size_t)Fd + Dd,
+                              (size_t)mk::ATTN_MAX_S * (hd + 2) + mk::ATTN_MAX_S});
+  *lds = fl * 4;
+  return pick->fn;
 }
 
 template <typename F>
@@ -480,20 +473,20 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
     }
   };
   const int cap = s->cus * BLOCKS_PER_CU;
-  // grid of a kernel whose waves each own `groups_per_wave`-sized row groups
-  auto grid = [&](int64_t groups) { return dim3(blocks_for(groups, NWAVES, cap), nb); };
+  const int hcap = std::min(cap, AM_MAX_BLOCKS);
+  const size_t f4 = sizeof(float);
 
   run(MOSHI_STAGE_EMBED, [&] {
     k_embed_begin<ET><<<dim3(blocks_for(d.D, BLOCK, 64), nb), BLOCK, 0, st>>>(d, b, E(s->emb[0]), E(s->text_emb),
                                                                                 user_dev, b0);
   });
+  const int g_qkv = proj_blocks(3 * d.D / 2, cap), g_out = proj_blocks(d.D, cap), g_gin = proj_blocks(d.F, cap);
+  const size_t l_out = (d.D + block_rows(d.D, 1, g_out)) * f4, l_gout = (d.F + block_rows(d.D, 1, g_out)) * f4;
   for (int l = 0; l < d.L; ++l) {
     const LayerW &lw = s->layers[l];
     run(MOSHI_STAGE_QKV, [&] {
-      with_vpl<WT>(d.D, [&](auto v) {
-        k_qkv_rope<WT, KT, decltype(v)::value><<<grid(3 * d.D / 2), BLOCK, d.D * 4, st>>>(
-            d, b, kv, W(lw.in), s->scale(lw.in), N(lw.norm1), l, b0);
-      });
+      k_qkv_rope<WT, KT><<<dim3(g_qkv, nb), BLOCK, (d.D + d.hd) * f4, st>>>(d, b, kv, W(lw.in), s->scale(lw.in),
+                                                                           N(lw.norm1), l, b0);
     });
     const int chunk = (d.cap + d.S - 1) / d.S;
     run(MOSHI_STAGE_ATTN, [&] {
@@ -503,83 +496,65 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
         k_attn<KT, 64><<<dim3(d.H, d.S, nb), BLOCK, chunk * 4, st>>>(d, b, kv, l, b0);
     });
     run(MOSHI_STAGE_OUT_PROJ, [&] {
-      with_vpl<WT>(d.D, [&](auto v) {
-        k_gemv<WT, 2, decltype(v)::value, true, MOSHI_STAGE_OUT_PROJ><<<grid(d.D / 2), BLOCK, d.D * 4, st>>>(
-            W(lw.out), s->scale(lw.out), d.D, d.D, b.o, d.D, b.x, d.D, b0);
-      });
+      k_gemv<WT, true, MOSHI_STAGE_OUT_PROJ><<<dim3(g_out, nb), BLOCK, l_out, st>>>(
+          W(lw.out), s->scale(lw.out), d.D, d.D, b.o, d.D, b.x, d.D, b0);
     });
     run(MOSHI_STAGE_GATE_IN, [&] {
-      with_vpl<WT>(d.D, [&](auto v) {
-        k_gate<WT, decltype(v)::value, MOSHI_STAGE_GATE_IN><<<grid(d.F), BLOCK, d.D * 4, st>>>(
-            W(lw.gin), s->scale(lw.gin), d.F, d.D, b.x, d.D, N(lw.norm2), d.eps, b.a, d.F, b0);
-      });
+      k_gate<WT, MOSHI_STAGE_GATE_IN><<<dim3(g_gin, nb), BLOCK, d.D * f4, st>>>(
+          W(lw.gin), s->scale(lw.gin), d.F, d.D, b.x, d.D, N(lw.norm2), d.eps, b.a, d.F, b0);
     });
     run(MOSHI_STAGE_GATE_OUT, [&] {
-      with_vpl<WT>(d.F, [&](auto v) {
-        k_gemv<WT, 1, decltype(v)::value, true, MOSHI_STAGE_GATE_OUT><<<grid(d.D), BLOCK, d.F * 4, st>>>(
-            W(lw.gout), s->scale(lw.gout), d.D, d.F, b.a, d.F, b.x, d.D, b0);
-      });
+      k_gemv<WT, true, MOSHI_STAGE_GATE_OUT><<<dim3(g_out, nb), BLOCK, l_gout, st>>>(
+          W(lw.gout), s->scale(lw.gout), d.D, d.F, b.a, d.F, b.x, d.D, b0);
     });
   }
   int prev_parts = 1;
   if (!temporal_only) {
     const int AM = (1 + d.Q) * AM_MAX_BLOCKS;
     // out_norm -> hidden, text head; argmax partials in slot 0
-    const dim3 gt(blocks_for((d.Vt + 1) / 2, NWAVES, std::min(cap, AM_MAX_BLOCKS)), nb);
-    prev_parts = (int)gt.x;
+    const int g_text = proj_blocks(d.Vt, hcap);
+    prev_parts = g_text;
     run(MOSHI_STAGE_TEXT_HEAD, [&] {
-      with_vpl<WT>(d.D, [&](auto v) {
-        k_head<WT, 2, decltype(v)::value, MOSHI_STAGE_TEXT_HEAD><<<gt, BLOCK, d.D * 4, st>>>(
-            W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, b.x, d.D, N(s->out_norm), d.eps, b.hidden,
-            b.text_logits, d.Vt, b.am_part, AM, b0);
-      });
+      k_head<WT, MOSHI_STAGE_TEXT_HEAD><<<dim3(g_text, nb), BLOCK, d.D * f4, st>>>(
+          W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, b.x, d.D, N(s->out_norm), d.eps, b.hidden,
+          b.text_logits, d.Vt, b.am_part, AM, b0);
     });
     // depformer_in[cb] . hidden for every codebook at once
     run(MOSHI_STAGE_DEP_IN, [&] {
-      with_vpl<WT>(d.D, [&](auto v) {
-        k_gemv<WT, 2, decltype(v)::value, false, MOSHI_STAGE_DEP_IN><<<grid(d.Q * d.Dd / 2), BLOCK, d.D * 4, st>>>(
-            W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, b.hidden, d.D, b.din, d.Q * d.Dd, b0);
-      });
+      k_gemv<WT, false, MOSHI_STAGE_DEP_IN><<<dim3(proj_blocks(d.Q * d.Dd, cap), nb), BLOCK, d.D * f4, st>>>(
+          W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, b.hidden, d.D, b.din, d.Q * d.Dd, b0);
     });
+    const int g_dqkv = proj_blocks(3 * d.Dd, cap), g_dout = proj_blocks(d.Dd, cap), g_dgin = proj_blocks(d.Fd, cap);
+    const size_t l_dout = (d.Dd + block_rows(d.Dd, 1, g_dout)) * f4, l_dgout = (d.Fd + block_rows(d.Dd, 1, g_dout)) * f4;
+    const int g_dhead = proj_blocks(d.Va, hcap);
     for (int cb = 0; cb < d.Q; ++cb) {
       const ET *table = cb == 0 ? E(s->dep_text_emb) : E(s->dep_emb[cb - 1]);
       for (int j = 0; j < d.Ld; ++j) {
         const LayerW &lw = s->dlayers[j][cb];
         run(MOSHI_STAGE_DEP_QKV, [&] {
-          with_vpl<WT>(d.Dd, [&](auto v) {
-            k_dep_qkv<WT, ET, 2, decltype(v)::value><<<grid(3 * d.Dd / 2), BLOCK, d.Dd * 4, st>>>(
-                d, b, W(lw.in), s->scale(lw.in), N(lw.norm1), table, j, cb, prev_parts, b0);
-          });
+          k_dep_qkv<WT, ET><<<dim3(g_dqkv, nb), BLOCK, d.Dd * f4, st>>>(d, b, W(lw.in), s->scale(lw.in), N(lw.norm1),
+                                                                         table, j, cb, prev_parts, b0);
         });
         run(MOSHI_STAGE_DEP_OUT, [&] {
-          with_vpl<WT>(d.Dd, [&](auto v) {
-            with_epl(d.hdd, [&](auto e) {
-              k_dep_out<WT, 2, decltype(v)::value, decltype(e)::value><<<grid(d.Dd / 2), BLOCK, d.Dd * 4, st>>>(
-                  d, b, W(lw.out), s->scale(lw.out), j, cb, b0);
-            });
+          with_epl(d.hdd, [&](auto e) {
+            k_dep_out<WT, decltype(e)::value><<<dim3(g_dout, nb), BLOCK, l_dout, st>>>(d, b, W(lw.out),
+                                                                                     s->scale(lw.out), j, cb, b0);
           });
         });
         run(MOSHI_STAGE_DEP_GATE_IN, [&] {
-          with_vpl<WT>(d.Dd, [&](auto v) {
-            k_gate<WT, decltype(v)::value, MOSHI_STAGE_DEP_GATE_IN><<<grid(d.Fd), BLOCK, d.Dd * 4, st>>>(
-                W(lw.gin), s->scale(lw.gin), d.Fd, d.Dd, b.y, d.Dd, N(lw.norm2), d.eps, b.da, d.Fd, b0);
-          });
+          k_gate<WT, MOSHI_STAGE_DEP_GATE_IN><<<dim3(g_dgin, nb), BLOCK, d.Dd * f4, st>>>(
+              W(lw.gin), s->scale(lw.gin), d.Fd, d.Dd, b.y, d.Dd, N(lw.norm2), d.eps, b.da, d.Fd, b0);
         });
         run(MOSHI_STAGE_DEP_GATE_OUT, [&] {
-          with_vpl<WT>(d.Fd, [&](auto v) {
-            k_gemv<WT, 2, decltype(v)::value, true, MOSHI_STAGE_DEP_GATE_OUT><<<grid(d.Dd / 2), BLOCK, d.Fd * 4, st>>>(
-                W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, b.da, d.Fd, b.y, d.Dd, b0);
-          });
+          k_gemv<WT, true, MOSHI_STAGE_DEP_GATE_OUT><<<dim3(g_dout, nb), BLOCK, l_dgout, st>>>(
+              W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, b.da, d.Fd, b.y, d.Dd, b0);
         });
       }
-      const dim3 gh(blocks_for((d.Va + 1) / 2, NWAVES, std::min(cap, AM_MAX_BLOCKS)), nb);
-      prev_parts = (int)gh.x;
+      prev_parts = g_dhead;
       run(MOSHI_STAGE_DEP_HEAD, [&] {
-        with_vpl<WT>(d.Dd, [&](auto v) {
-          k_head<WT, 2, decltype(v)::value, MOSHI_STAGE_DEP_HEAD><<<gh, BLOCK, d.Dd * 4, st>>>(
-              W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, b.y, d.Dd, nullptr, d.eps, nullptr,
-              b.audio_logits + (size_t)cb * d.Va, d.Q * d.Va, b.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS, AM, b0);
-        });
+        k_head<WT, MOSHI_STAGE_DEP_HEAD><<<dim3(g_dhead, nb), BLOCK, d.Dd * f4, st>>>(
+            W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, b.y, d.Dd, nullptr, d.eps, nullptr,
+            b.audio_logits + (size_t)cb * d.Va, d.Q * d.Va, b.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS, AM, b0);
       });
     }
   }
@@ -862,11 +837,30 @@ moshi_status moshi_load_weights(moshi_state *s, const moshi_tensor *t, int32_t n
       return hb.data();
     };
     void *dst = s->warena + sl.off;
+    // gated linear_in: the device copy holds row j of each half next to each other (rows 2j, 2j+1)
+    std::vector<float> pf;
+    std::vector<uint16_t> pb;
+    if (sl.pair_rows) {
+      const float *f = (band == MOSHI_BAND_BF16 || (sl.kind == K_EMBED)) ? nullptr : as_f32();
+      const uint16_t *h = f ? nullptr : as_bf16();
+      const int64_t half = sl.rows / 2, cols = sl.cols;
+      if (f) pf.resize(cnt);
+      else pb.resize(cnt);
+      for (int64_t j = 0; j < 2 * half; ++j) {
+        const int64_t src = (j & 1) ? half + j / 2 : j / 2;
+        if (f)
+          std::memcpy(&pf[(size_t)j * cols], f + (size_t)src * cols, (size_t)cols * 4);
+        else
+          std::memcpy(&pb[(size_t)j * cols], h + (size_t)src * cols, (size_t)cols * 2);
+      }
+    }
+    auto lin_f32 = [&]() -> const float * { return sl.pair_rows ? pf.data() : as_f32(); };
+    auto lin_bf16 = [&]() -> const uint16_t * { return sl.pair_rows ? pb.data() : as_bf16(); };
     hipError_t e = hipSuccess;
     if (sl.kind == K_NORM || (band == MOSHI_BAND_F32)) {
-      e = hipMemcpy(dst, as_f32(), cnt * 4, hipMemcpyHostToDevice);
+      e = hipMemcpy(dst, lin_f32(), cnt * 4, hipMemcpyHostToDevice);
     } else if (sl.kind == K_EMBED || band == MOSHI_BAND_BF16) {
-      e = hipMemcpy(dst, as_bf16(), cnt * 2, hipMemcpyHostToDevice);
+      e = hipMemcpy(dst, lin_bf16(), cnt * 2, hipMemcpyHostToDevice);
     } else {  // int8 linear: quantise on the device
       if (staging_n < cnt) {
         if (staging) (void)hipFree(staging);
@@ -879,7 +873,7 @@ moshi_status moshi_load_weights(moshi_state *s, const moshi_tensor *t, int32_t n
         }
         staging_n = cnt;
       }
-      e = hipMemcpy(staging, as_f32(), cnt * 4, hipMemcpyHostToDevice);
+      e = hipMemcpy(staging, lin_f32(), cnt * 4, hipMemcpyHostToDevice);
       if (e == hipSuccess) {
         mk::k_quant_rows<<<(unsigned)sl.rows, mk::BLOCK, 0, s->stream>>>(
             staging, sl.cols, reinterpret_cast<int8_t *>(dst), reinterpret_cast<float *>(s->warena + sl.soff), 0);
@@ -1194,23 +1188,17 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
     }
   }
   auto launch = [&]() {
-    const dim3 grid(blocks_for((N + 1) / 2, mk::NWAVES, 1024));
+    const dim3 grid(proj_blocks(N, 1024));
     const float *sc = band == MOSHI_BAND_I8 ? ds : nullptr;
     if (band == MOSHI_BAND_F32)
-      with_vpl<float>(K, [&](auto v) {
-        mk::k_gemv<float, 2, decltype(v)::value, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(
-            reinterpret_cast<const float *>(dw), sc, N, K, dx, K, dy, N, 0);
-      });
+      mk::k_gemv<float, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const float *>(dw), sc,
+                                                                            N, K, dx, K, dy, N, 0);
     else if (band == MOSHI_BAND_BF16)
-      with_vpl<bf16_t>(K, [&](auto v) {
-        mk::k_gemv<bf16_t, 2, decltype(v)::value, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(
-            reinterpret_cast<const bf16_t *>(dw), sc, N, K, dx, K, dy, N, 0);
-      });
+      mk::k_gemv<bf16_t, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const bf16_t *>(dw),
+                                                                             sc, N, K, dx, K, dy, N, 0);
     else
-      with_vpl<int8_t>(K, [&](auto v) {
-        mk::k_gemv<int8_t, 2, decltype(v)::value, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(
-            reinterpret_cast<const int8_t *>(dw), sc, N, K, dx, K, dy, N, 0);
-      });
+      mk::k_gemv<int8_t, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const int8_t *>(dw),
+                                                                             sc, N, K, dx, K, dy, N, 0);
   };
   if (rc == MOSHI_OK) {
     launch();
