@@ -1,5 +1,6 @@
 // Device-side primitives shared by the frame-step kernels (gfx950, wave64).
 #pragma once
+#include <type_traits>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -300,6 +301,18 @@ __device__ __forceinline__ void st_sys(float *p, float v) { __hip_atomic_store(p
 __device__ __forceinline__ float ld_sys(const float *p) {
   return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
+
+// 16 bytes at byte offset `off` of an activation buffer written by another block of the same
+// kernel, with the cache policy of a system-scope load (sc0 sc1: past both cache levels), through
+// a buffer resource so that four floats move in one instruction.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(const void *base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ float4 ld_sys4(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 17);
+  return float4{__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3])};
+}
 __device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Staging of a block's input vector into LDS.  Every thread issues STAGE_UNR float4 loads before
@@ -308,8 +321,8 @@ __device__ __forceinline__ void wait_mem() { asm volatile("s_waitcnt vmcnt(0)" :
 constexpr int STAGE_UNR = 8;
 
 // xs[k] = src[k] for k < K; returns this thread's partial sum of squares.  No barrier.  With SYS
-// the source is read with system-scope 8-byte loads (data another block of the same kernel wrote),
-// U loads per thread in flight per pass.
+// the source is read with system-coherent 16-byte loads (data another block of the same kernel
+// wrote), U loads per thread in flight per pass.
 template <int NT = BLOCK, bool SYS = false, int U = 2 * STAGE_UNR>
 __device__ __forceinline__ float stage_copy(const float *__restrict__ src, int K, float *xs) {
   float ss = 0.f;
@@ -337,25 +350,25 @@ __device__ __forceinline__ float stage_copy(const float *__restrict__ src, int K
       }
     }
   } else {
-    const int K2 = K >> 1;
-    const uint64_t *s2 = reinterpret_cast<const uint64_t *>(src);
-    for (int base = 0; base < K2; base += U * NT) {
-      uint64_t v[U];
+    const int K4 = K >> 2;
+    const __amdgpu_buffer_rsrc_t r = act_rsrc(src);
+    float4 *x4 = reinterpret_cast<float4 *>(xs);
+    for (int base = 0; base < K4; base += U * NT) {
+      float4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = base + u * NT + threadIdx.x;
-        v[u] = i < K2 ? __hip_atomic_load(const_cast<uint64_t *>(s2 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
-                      : 0ull;
+        v[u] = i < K4 ? ld_sys4(r, i * 16) : float4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = base + u * NT + threadIdx.x;
-        if (i < K2) {
-          const float a = __uint_as_float((uint32_t)v[u]), b = __uint_as_float((uint32_t)(v[u] >> 32));
-          xs[2 * i] = a;
-          xs[2 * i + 1] = b;
-          ss = fmaf(a, a, ss);
-          ss = fmaf(b, b, ss);
+        if (i < K4) {
+          x4[i] = v[u];
+          ss = fmaf(v[u].x, v[u].x, ss);
+          ss = fmaf(v[u].y, v[u].y, ss);
+          ss = fmaf(v[u].z, v[u].z, ss);
+          ss = fmaf(v[u].w, v[u].w, ss);
         }
       }
     }

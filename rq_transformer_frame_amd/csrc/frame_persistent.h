@@ -5,8 +5,8 @@
 // Every phase is a weight-streaming projection (or the temporal attention) spread over all waves
 // of the grid.  Phase p+1's first weight tile is loaded into registers BEFORE the block waits for
 // phase p to complete, so HBM keeps streaming across phase boundaries and the wait is hidden
-// behind the fetch.  Completion of a phase is counted in 8 arrival counters (one per XCD slot, 64 B
-// apart); a waiter sums them.  Activations that other blocks read (x, q, o, a, y, dq, dkv, ...) are
+// behind the fetch.  Completion of a phase is signalled by per-block flags that carry a tag
+// growing with the frame serial number and the phase; a waiter reads all flags.  Activations that other blocks read (x, q, o, a, y, dq, dkv, ...) are
 // written with system-scope stores (write-through past the per-XCD L2) after which the writer
 // waits for its stores (s_waitcnt) before it arrives, and are read with system-scope loads.  Every
 // wait is a bounded spin: on timeout the block raises the error flag and the whole grid exits.
@@ -17,8 +17,6 @@ namespace mk {
 
 constexpr int PBLOCK = 512;
 constexpr int PWAVES = PBLOCK / WAVE;
-constexpr int SYNC_SLOTS = 8;
-constexpr int SYNC_STRIDE = 16;  // uint32 per counter slot (64 bytes)
 constexpr int PQ = 8;                // most depformer steps (dep_q) the persistent kernel takes
 constexpr int PSTREAMS = 2 * PQ + 1; // most token streams
 
@@ -43,7 +41,7 @@ struct PArgs {
   const void *dep_table[PQ];  // cb 0: depformer text table, cb > 0: depformer_emb[cb - 1]
   const void *w_lin[PQ];
   const float *s_lin[PQ];
-  uint32_t *sync;  // [phases][SYNC_SLOTS * SYNC_STRIDE]
+  uint32_t *sync;  // [gridDim.x] per-block phase flags
   int *err;        // error flag (also copied back to the host with the outputs)
   int spin_limit;
   uint64_t *phase_ts;  // optional [phases][2]: block 0's arrival and the phase's completion time
@@ -97,41 +95,37 @@ __device__ __forceinline__ ArgBest ld_sys_arg(const ArgBest *p) {
   return ArgBest{__uint_as_float((uint32_t)u), (int)(uint32_t)(u >> 32)};
 }
 
-// Stage two vectors written by other blocks (system-scope 8-byte loads; per pass U1 and U2 loads
-// per thread are issued before any LDS store): dst1[0..K1) = src1, dst2[0..K2) = src2 (K even).
+// Stage two vectors written by other blocks (system-coherent 16-byte loads; per pass U1 and U2
+// loads per thread are issued before any LDS store): dst1[0..K1) = src1, dst2[0..K2) = src2
+// (K1, K2 multiples of 4).
 template <int U1, int U2>
 __device__ __forceinline__ void stage2_sys(const float *src1, int K1, float *dst1, const float *src2, int K2,
                                            float *dst2) {
-  const uint64_t *a1 = reinterpret_cast<const uint64_t *>(src1);
-  const uint64_t *a2 = reinterpret_cast<const uint64_t *>(src2);
-  const int n1 = K1 >> 1, n2 = K2 >> 1;
+  const __amdgpu_buffer_rsrc_t r1 = act_rsrc(src1), r2 = act_rsrc(src2);
+  float4 *d1 = reinterpret_cast<float4 *>(dst1);
+  float4 *d2 = reinterpret_cast<float4 *>(dst2);
+  const int n1 = K1 >> 2, n2 = K2 >> 2;
   for (int b1 = 0, b2 = 0; b1 < n1 || b2 < n2; b1 += U1 * PBLOCK, b2 += U2 * PBLOCK) {
-    uint64_t v1[U1], v2[U2];
+    float4 v1[U1], v2[U2];
 #pragma unroll
     for (int u = 0; u < U1; ++u) {
       const int i = b1 + u * PBLOCK + threadIdx.x;
-      v1[u] = i < n1 ? ld_sys_u64(a1 + i) : 0ull;
+      v1[u] = i < n1 ? ld_sys4(r1, i * 16) : float4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < U2; ++u) {
       const int i = b2 + u * PBLOCK + threadIdx.x;
-      v2[u] = i < n2 ? ld_sys_u64(a2 + i) : 0ull;
+      v2[u] = i < n2 ? ld_sys4(r2, i * 16) : float4{0.f, 0.f, 0.f, 0.f};
     }
 #pragma unroll
     for (int u = 0; u < U1; ++u) {
       const int i = b1 + u * PBLOCK + threadIdx.x;
-      if (i < n1) {
-        dst1[2 * i] = __uint_as_float((uint32_t)v1[u]);
-        dst1[2 * i + 1] = __uint_as_float((uint32_t)(v1[u] >> 32));
-      }
+      if (i < n1) d1[i] = v1[u];
     }
 #pragma unroll
     for (int u = 0; u < U2; ++u) {
       const int i = b2 + u * PBLOCK + threadIdx.x;
-      if (i < n2) {
-        dst2[2 * i] = __uint_as_float((uint32_t)v2[u]);
-        dst2[2 * i + 1] = __uint_as_float((uint32_t)(v2[u] >> 32));
-      }
+      if (i < n2) d2[i] = v2[u];
     }
   }
   __syncthreads();
@@ -140,47 +134,51 @@ __device__ __forceinline__ void stage2_sys(const float *src1, int K1, float *dst
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
 // ---- phase completion ------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t *phase_ctr(const PArgs &a, int p) {
-  return a.sync + (size_t)p * SYNC_SLOTS * SYNC_STRIDE;
-}
+// Every block owns one 32-bit flag (packed, so a waiting wave reads them all with a few loads in
+// one round trip).  Arriving at phase p of the frame with serial number `serial` stores the tag
+// serial * nph + p + 1 into the block's flag (a system-scope store: no read-modify-write, no
+// contention); waiting for phase p means every flag has reached that tag.  Tags only grow (modulo
+// 2^32, compared by signed difference), so flags are never cleared between frames.
+__device__ __forceinline__ uint32_t p_tag(uint32_t serial, int nph, int p) { return serial * (uint32_t)nph + (uint32_t)p + 1u; }
 
 // All of this block's stores of the phase are complete (s_waitcnt in every thread, then the
-// barrier); then one arrival is counted.
-__device__ __forceinline__ void p_arrive(const PArgs &a, int p) {
+// barrier); then the block's flag is raised.
+__device__ __forceinline__ void p_arrive(const PArgs &a, uint32_t tag, int p) {
   wait_mem();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(phase_ctr(a, p) + (blockIdx.x % SYNC_SLOTS) * SYNC_STRIDE, 1u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+    st_sys_u32(a.sync + blockIdx.x, tag);
     if (a.phase_ts && blockIdx.x == 0) a.phase_ts[2 * p] = wall_clock64();
   }
 }
 
-// Wait until every block has arrived at phase p.  Returns false (and raises the error flag) if
+__device__ __forceinline__ uint32_t ld_sys_u32(const uint32_t *p) {
+  return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Wait until every block's flag has reached `tag`.  Returns false (and raises the error flag) if
 // the error flag is up or the spin limit is reached: the caller then leaves the kernel.
-__device__ __forceinline__ bool p_wait(const PArgs &a, int p, int *s_ok) {
+__device__ __forceinline__ bool p_wait(const PArgs &a, uint32_t tag, int p, int *s_ok) {
   if (threadIdx.x < WAVE) {
     const int lane = threadIdx.x;
-    const uint32_t *c = phase_ctr(a, p);
-    const uint32_t target = gridDim.x;
+    const int nb = gridDim.x;
     int ok = 1;
     for (int spins = 0;; ++spins) {
-      uint32_t v = lane < SYNC_SLOTS
-                       ? __hip_atomic_load(const_cast<uint32_t *>(c + lane * SYNC_STRIDE), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT)
-                       : 0u;
-      v += __shfl_xor(v, 1, WAVE);
-      v += __shfl_xor(v, 2, WAVE);
-      v += __shfl_xor(v, 4, WAVE);
-      v = __shfl(v, 0, WAVE);
-      if (v >= target) break;
+      uint32_t f[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) f[u] = lane + u * WAVE < nb ? ld_sys_u32(a.sync + lane + u * WAVE) : tag;
+      bool done = true;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) done = done && (int32_t)(f[u] - tag) >= 0;
+      for (int i = lane + 4 * WAVE; i < nb; i += WAVE) done = done && (int32_t)(ld_sys_u32(a.sync + i) - tag) >= 0;
+      if (__all(done)) break;
       int e = lane == 0 ? __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
       e = __shfl(e, 0, WAVE);
       if (e != 0 || spins >= a.spin_limit) {
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
     if (lane == 0) {
       if (!ok) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -232,7 +230,7 @@ __device__ __forceinline__ int merge_head(const ArgBest *part, int n, ArgBest *w
 // The arguments live in device memory (written once per session): reading them where they are
 // used keeps the ~150 dwords of pointers and sizes out of the registers of every phase.
 template <typename WT, typename ET, typename KT, int HD, int DEPL, int UD, int UF, int UDd, int UFd>
-__global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__restrict__ pa) {
+__global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__restrict__ pa, uint32_t serial) {
   const PArgs &a = *pa;
   extern __shared__ float xs[];  // max(D, F, Dd, Fd) floats; the attention phase reuses it
   __shared__ float red[PWAVES];
@@ -250,6 +248,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
   const int slot = (int)(pos % d.cap);
   const int NPT = 5 * d.L;  // temporal phases
   const int P_HEAD = NPT;
+  const int NPH = P_HEAD + d.Q * (4 * d.Ld + 1) + 1;  // phases of the frame
 
   // ---- a1-a3: gather (every block), user ring write (block 0), embedding sum (every block) ----
   if (threadIdx.x < d.NS) {
@@ -362,9 +361,9 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         }
       });
     }
-    p_arrive(a, P);
+    p_arrive(a, p_tag(serial, NPH, P), P);
     p_begin(rs, lp.w_out, lp.s_out, d.D, d.D, 1);  // out_proj, after attention
-    if (!p_wait(a, P, &s_ok)) return;
+    if (!p_wait(a, p_tag(serial, NPH, P), P, &s_ok)) return;
 
     // attention: block bi < H * S takes head bi % H, split bi / H
     {
@@ -380,8 +379,17 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         const int len = j1 > j0 ? j1 - j0 : 0;
         float *sc = xs;  // scores
         float qv[EPL];
+        {
+          const __amdgpu_buffer_rsrc_t rq = act_rsrc(s.q);
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) qv[i] = ld_sys(s.q + h * HD + sub * EPL + i);
+          for (int i = 0; i < EPL; i += 4) {
+            const float4 t4 = ld_sys4(rq, (h * HD + sub * EPL + i) * 4);
+            qv[i] = t4.x;
+            qv[i + 1] = t4.y;
+            qv[i + 2] = t4.z;
+            qv[i + 3] = t4.w;
+          }
+        }
         const float scale = 1.0f / sqrtf((float)HD);
         const size_t base = ((size_t)l * d.H + h) * (size_t)d.cap * HD;
         const KT *kb = kc + base, *vb = vc + base;
@@ -485,17 +493,17 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         }
       }
     }
-    p_arrive(a, P + 1);
-    if (!p_wait(a, P + 1, &s_ok)) return;
+    p_arrive(a, p_tag(serial, NPH, P + 1), P + 1);
+    if (!p_wait(a, p_tag(serial, NPH, P + 1), P + 1, &s_ok)) return;
 
     // out_proj + residual (x staged next to o)
     stage2_sys<UD, UD>(s.o, d.D, xs, s.x, d.D, xs + d.D);
     rs.run(xs, [&](int row, float v) {
       if (lane == 0) st_sys(s.x + row, xs[d.D + row] + v);
     });
-    p_arrive(a, P + 2);
+    p_arrive(a, p_tag(serial, NPH, P + 2), P + 2);
     p_begin(rs, lp.w_gin, lp.s_gin, d.D, d.F, 2);
-    if (!p_wait(a, P + 2, &s_ok)) return;
+    if (!p_wait(a, p_tag(serial, NPH, P + 2), P + 2, &s_ok)) return;
 
     // norm2 + gate_in + silu * mult (rows interleaved: 2j gate, 2j + 1 mult)
     stage_rms<PBLOCK, true, UD>(s.x, lp.norm2, d.D, d.eps, xs, red);
@@ -509,21 +517,21 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
           st_sys(s.a + (row >> 1), silu(gv) * v);
       });
     }
-    p_arrive(a, P + 3);
+    p_arrive(a, p_tag(serial, NPH, P + 3), P + 3);
     p_begin(rs, lp.w_gout, lp.s_gout, d.F, d.D, 1);
-    if (!p_wait(a, P + 3, &s_ok)) return;
+    if (!p_wait(a, p_tag(serial, NPH, P + 3), P + 3, &s_ok)) return;
 
     // gate_out + residual (x staged next to a)
     stage2_sys<UF, UD>(s.a, d.F, xs, s.x, d.D, xs + d.F);
     rs.run(xs, [&](int row, float v) {
       if (lane == 0) st_sys(s.x + row, xs[d.F + row] + v);
     });
-    p_arrive(a, P + 4);
+    p_arrive(a, p_tag(serial, NPH, P + 4), P + 4);
     if (l + 1 < d.L)
       p_begin(rs, a.tl[l + 1].w_in, a.tl[l + 1].s_in, d.D, 3 * d.D / 2, 2);
     else
       p_begin(rs, a.w_text, a.s_text, d.D, d.Vt, 1);
-    if (!p_wait(a, P + 4, &s_ok)) return;
+    if (!p_wait(a, p_tag(serial, NPH, P + 4), P + 4, &s_ok)) return;
   }
 
   // ---- a6-a7: out_norm, text head (argmax partials) and depformer_in for every codebook ----
@@ -545,9 +553,9 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
       if (lane == 0) st_sys(s.din + row, v);
     });
   }
-  p_arrive(a, P_HEAD);
+  p_arrive(a, p_tag(serial, NPH, P_HEAD), P_HEAD);
   p_begin(rs, a.dl[0].w_in, a.dl[0].s_in, d.Dd, 3 * d.Dd, 1);
-  if (!p_wait(a, P_HEAD, &s_ok)) return;
+  if (!p_wait(a, p_tag(serial, NPH, P_HEAD), P_HEAD, &s_ok)) return;
 
   // ---- a8: depformer, 8 sequential codebook steps ----
   const ET *tbl;
@@ -579,36 +587,53 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         else
           st_sys(kvbase + row - d.Dd, v);
       });
-      p_arrive(a, P);
+      p_arrive(a, p_tag(serial, NPH, P), P);
       p_begin(rs, lp.w_out, lp.s_out, d.Dd, d.Dd, 1);
-      if (!p_wait(a, P, &s_ok)) return;
+      if (!p_wait(a, p_tag(serial, NPH, P), P, &s_ok)) return;
 
       // attention of dq over the cb + 1 entries of layer j (every block), then out_proj + residual
       float *ys = xs + d.Dd;  // y, for the residual
       {
-        constexpr int UY = UDd;  // y in UDd loads per thread (one pass when Dd <= 2 * UDd * PBLOCK)
-        uint64_t yv[UY];
+        constexpr int UY = UDd;  // y in UDd 16-byte loads per thread (one pass when Dd <= 4 * UDd * PBLOCK)
+        const __amdgpu_buffer_rsrc_t ry = act_rsrc(s.y), rq = act_rsrc(s.dq);
+        float4 yv[UY];
 #pragma unroll
         for (int u = 0; u < UY; ++u) {
           const int i = u * PBLOCK + threadIdx.x;
-          yv[u] = i < (d.Dd >> 1) ? ld_sys_u64(reinterpret_cast<const uint64_t *>(s.y) + i) : 0ull;
+          yv[u] = i < (d.Dd >> 2) ? ld_sys4(ry, i * 16) : float4{0.f, 0.f, 0.f, 0.f};
         }
         const int g = lane >> 4, sub = lane & 15;
         const float *kv0 = s.dkv + (size_t)j * d.Q * 2 * d.Dd;
+        const __amdgpu_buffer_rsrc_t rkv = act_rsrc(kv0);
         const float scale = 1.0f / sqrtf((float)d.hdd);
         const int npos = cb + 1;
         for (int hh = wave * 4 + g; hh < d.Hd; hh += PWAVES * 4) {
           const int e0 = hh * d.hdd + sub * DEPL;
           float qv[DEPL], kk[PQ][DEPL], vv[PQ][DEPL];
+          static_assert(DEPL % 4 == 0, "depformer dims per lane load as float4");
 #pragma unroll
-          for (int i = 0; i < DEPL; ++i) qv[i] = ld_sys(s.dq + e0 + i);
+          for (int i = 0; i < DEPL; i += 4) {
+            const float4 t4 = ld_sys4(rq, (e0 + i) * 4);
+            qv[i] = t4.x;
+            qv[i + 1] = t4.y;
+            qv[i + 2] = t4.z;
+            qv[i + 3] = t4.w;
+          }
 #pragma unroll
           for (int p = 0; p < PQ; ++p)
             if (p < npos) {
 #pragma unroll
-              for (int i = 0; i < DEPL; ++i) {
-                kk[p][i] = ld_sys(kv0 + (size_t)p * 2 * d.Dd + e0 + i);
-                vv[p][i] = ld_sys(kv0 + (size_t)p * 2 * d.Dd + d.Dd + e0 + i);
+              for (int i = 0; i < DEPL; i += 4) {
+                const float4 k4 = ld_sys4(rkv, (p * 2 * d.Dd + e0 + i) * 4);
+                const float4 v4 = ld_sys4(rkv, (p * 2 * d.Dd + d.Dd + e0 + i) * 4);
+                kk[p][i] = k4.x;
+                kk[p][i + 1] = k4.y;
+                kk[p][i + 2] = k4.z;
+                kk[p][i + 3] = k4.w;
+                vv[p][i] = v4.x;
+                vv[p][i + 1] = v4.y;
+                vv[p][i + 2] = v4.z;
+                vv[p][i + 3] = v4.w;
               }
             }
           float sc[PQ];
@@ -651,19 +676,16 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
 #pragma unroll
         for (int u = 0; u < UY; ++u) {
           const int i = u * PBLOCK + threadIdx.x;
-          if (i < (d.Dd >> 1)) {
-            ys[2 * i] = __uint_as_float((uint32_t)yv[u]);
-            ys[2 * i + 1] = __uint_as_float((uint32_t)(yv[u] >> 32));
-          }
+          if (i < (d.Dd >> 2)) reinterpret_cast<float4 *>(ys)[i] = yv[u];
         }
         __syncthreads();
       }
       rs.run(xs, [&](int row, float v) {
         if (lane == 0) st_sys(s.y + row, ys[row] + v);
       });
-      p_arrive(a, P + 1);
+      p_arrive(a, p_tag(serial, NPH, P + 1), P + 1);
       p_begin(rs, lp.w_gin, lp.s_gin, d.Dd, d.Fd, 2);
-      if (!p_wait(a, P + 1, &s_ok)) return;
+      if (!p_wait(a, p_tag(serial, NPH, P + 1), P + 1, &s_ok)) return;
 
       // norm2 + gate_in + silu * mult (rows interleaved)
       stage_rms<PBLOCK, true, UDd>(s.y, lp.norm2, d.Dd, d.eps, xs, red);
@@ -677,21 +699,21 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
             st_sys(s.da + (row >> 1), silu(gv) * v);
         });
       }
-      p_arrive(a, P + 2);
+      p_arrive(a, p_tag(serial, NPH, P + 2), P + 2);
       p_begin(rs, lp.w_gout, lp.s_gout, d.Fd, d.Dd, 1);
-      if (!p_wait(a, P + 2, &s_ok)) return;
+      if (!p_wait(a, p_tag(serial, NPH, P + 2), P + 2, &s_ok)) return;
 
       // gate_out + residual (y staged next to da)
       stage2_sys<UFd, UDd>(s.da, d.Fd, xs, s.y, d.Dd, xs + d.Fd);
       rs.run(xs, [&](int row, float v) {
         if (lane == 0) st_sys(s.y + row, xs[d.Fd + row] + v);
       });
-      p_arrive(a, P + 3);
+      p_arrive(a, p_tag(serial, NPH, P + 3), P + 3);
       if (j + 1 < d.Ld)
         p_begin(rs, a.dl[(j + 1) * d.Q + cb].w_in, a.dl[(j + 1) * d.Q + cb].s_in, d.Dd, 3 * d.Dd, 1);
       else
         p_begin(rs, a.w_lin[cb], a.s_lin[cb], d.Dd, d.Va, 1);
-      if (!p_wait(a, P + 3, &s_ok)) return;
+      if (!p_wait(a, p_tag(serial, NPH, P + 3), P + 3, &s_ok)) return;
     }
     // codebook head (no norm) with argmax partials
     {
@@ -707,18 +729,18 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
       best = wave_arg(best);
       best = block_arg(best, wb);
       if (threadIdx.x == 0) st_sys_arg(s.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS + blockIdx.x, best);
-      p_arrive(a, P);
+      p_arrive(a, p_tag(serial, NPH, P), P);
       if (cb + 1 < d.Q) {
         p_begin(rs, a.dl[cb + 1].w_in, a.dl[cb + 1].s_in, d.Dd, 3 * d.Dd, 1);
-        if (!p_wait(a, P, &s_ok)) return;
+        if (!p_wait(a, p_tag(serial, NPH, P), P, &s_ok)) return;
       }
     }
   }
 
   // ---- a9: frame end (block 0) ----
   if (blockIdx.x != 0) return;
-  const int P_LAST = P_HEAD + d.Q * (4 * d.Ld + 1);
-  if (!p_wait(a, P_LAST, &s_ok)) return;
+  const int P_LAST = NPH - 1;
+  if (!p_wait(a, p_tag(serial, NPH, P_LAST), P_LAST, &s_ok)) return;
   const int last = merge_head(s.am_part + (size_t)d.Q * AM_MAX_BLOCKS, gridDim.x, wb);
   if (threadIdx.x == 0) {
     s.tokens[d.Q] = last;
@@ -735,10 +757,6 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
       *has = 0;
     }
   }
-  // every block has arrived at every phase: clear the counters for the next frame
-  const int nph = P_LAST + 1;
-  for (int i = threadIdx.x; i < nph * SYNC_SLOTS; i += PBLOCK)
-    a.sync[(size_t)(i / SYNC_SLOTS) * SYNC_SLOTS * SYNC_STRIDE + (i % SYNC_SLOTS) * SYNC_STRIDE] = 0u;
 }
 
 }  // namespace mk

@@ -508,17 +508,45 @@ __global__ __launch_bounds__(BLOCK) void k_dep_out(Dims d, Bufs s, const WT *__r
   for (int hh = wave * 4 + g; hh < d.Hd; hh += NWAVES * 4) {  // 16 lanes per head
     const int e0 = hh * hdd + sub * EPL;
     float qv[EPL], kk[DEP_MAX_POS][EPL], vv[DEP_MAX_POS][EPL];
+    if constexpr (EPL % 4 == 0) {  // 16-byte loads
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) qv[i] = q[e0 + i];
-#pragma unroll
-    for (int p = 0; p < DEP_MAX_POS; ++p)
-      if (p < npos) {
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          kk[p][i] = kv0[(size_t)p * 2 * Dd + e0 + i];
-          vv[p][i] = kv0[(size_t)p * 2 * Dd + Dd + e0 + i];
-        }
+      for (int i = 0; i < EPL; i += 4) {
+        const float4 t4 = *reinterpret_cast<const float4 *>(q + e0 + i);
+        qv[i] = t4.x;
+        qv[i + 1] = t4.y;
+        qv[i + 2] = t4.z;
+        qv[i + 3] = t4.w;
       }
+#pragma unroll
+      for (int p = 0; p < DEP_MAX_POS; ++p)
+        if (p < npos) {
+#pragma unroll
+          for (int i = 0; i < EPL; i += 4) {
+            const float4 k4 = *reinterpret_cast<const float4 *>(kv0 + (size_t)p * 2 * Dd + e0 + i);
+            const float4 v4 = *reinterpret_cast<const float4 *>(kv0 + (size_t)p * 2 * Dd + Dd + e0 + i);
+            kk[p][i] = k4.x;
+            kk[p][i + 1] = k4.y;
+            kk[p][i + 2] = k4.z;
+            kk[p][i + 3] = k4.w;
+            vv[p][i] = v4.x;
+            vv[p][i + 1] = v4.y;
+            vv[p][i + 2] = v4.z;
+            vv[p][i + 3] = v4.w;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) qv[i] = q[e0 + i];
+#pragma unroll
+      for (int p = 0; p < DEP_MAX_POS; ++p)
+        if (p < npos) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) {
+            kk[p][i] = kv0[(size_t)p * 2 * Dd + e0 + i];
+            vv[p][i] = kv0[(size_t)p * 2 * Dd + Dd + e0 + i];
+          }
+        }
+    }
     float sc[DEP_MAX_POS];
     float m = -INFINITY;
 #pragma unroll

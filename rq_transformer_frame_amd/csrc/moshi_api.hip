@@ -92,7 +92,8 @@ struct moshi_state {
   const void *pkern = nullptr;  // selected k_frame_persistent instance
   size_t plds = 0;              // its dynamic LDS bytes
   int pgrid = 0;
-  uint32_t *sync = nullptr;     // phase counters
+  uint32_t *sync = nullptr;     // per-block phase flags of the persistent kernel
+  uint32_t pserial = 0;         // persistent launches so far
   mk::LayerPtrs *d_tl = nullptr, *d_dl = nullptr;
   mk::PArgs *d_pargs = nullptr;  // persistent kernel arguments (device copy)
   uint64_t *d_phase_ts = nullptr;
@@ -293,7 +294,7 @@ moshi_status alloc_session(moshi_state *s) {
   req((void **)&b.am_part, B * (1 + d.Q) * mk::AM_MAX_BLOCKS * sizeof(mk::ArgBest));
   req((void **)&b.rope_freq, (size_t)(d.hd / 2) * 4);
   const size_t nph = (size_t)5 * d.L + 1 + (size_t)d.Q * (4 * d.Ld + 1) + 1;
-  req((void **)&s->sync, nph * mk::SYNC_SLOTS * mk::SYNC_STRIDE * 4);
+  req((void **)&s->sync, (size_t)std::max(s->cus, 64) * 4);  // one phase flag per persistent block
   req((void **)&s->d_tl, (size_t)d.L * sizeof(mk::LayerPtrs));
   req((void **)&s->d_pargs, sizeof(mk::PArgs));
   req((void **)&s->d_phase_ts, nph * 2 * 8);
@@ -391,21 +392,18 @@ PVariant pvariant(int band) {
 const PVariant *persistent_variants(int *n) {
   static const PVariant v[] = {
       // Moshi-7B shape (d4096 / ffn 11264, depformer d1024 / ffn 2816)
-      pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 4, 11, 1, 3>(MOSHI_BAND_BF16),
-      pvariant<int8_t, bf16_t, bf16_t, 128, 4, 4, 11, 1, 3>(MOSHI_BAND_I8),
-      // small shapes, one pass per 1024-wide input
+      pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_BF16),
+      pvariant<int8_t, bf16_t, bf16_t, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_I8),
+      // small shapes, one pass per 2048-wide input
       pvariant<float, float, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_F32),
       pvariant<bf16_t, bf16_t, bf16_t, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_BF16),
       pvariant<int8_t, bf16_t, bf16_t, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
-      pvariant<float, float, float, 128, 4, 1, 1, 1, 1>(MOSHI_BAND_F32),
-      pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 1, 1, 1, 1>(MOSHI_BAND_BF16),
-      pvariant<int8_t, bf16_t, bf16_t, 128, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
   };
   *n = (int)(sizeof(v) / sizeof(v[0]));
   return v;
 }
 
-int stage_passes(int K) { return (K / 2 + mk::PBLOCK - 1) / mk::PBLOCK; }
+int stage_passes(int K) { return (K / 4 + mk::PBLOCK - 1) / mk::PBLOCK; }  // 16-byte loads per thread
 
 const void *select_persistent(const moshi_config &c, size_t *lds) {
   const int D = c.d_model, F = c.ffn_hidden, Dd = c.dep_d_model, Fd = c.dep_ffn_hidden;
@@ -609,7 +607,8 @@ moshi_status write_pargs(moshi_state *s) {
 
 moshi_status launch_persistent(moshi_state *s) {
   mk::PArgs *pa = s->d_pargs;
-  void *args[] = {&pa};
+  uint32_t serial = s->pserial++;  // phase flags of frame n carry tags above every tag of frame n - 1
+  void *args[] = {&pa, &serial};
   HIP_TRY(s, hipLaunchCooperativeKernel(s->pkern, dim3(s->pgrid), dim3(mk::PBLOCK), args, (unsigned)s->plds,
                                         s->stream));
   return MOSHI_OK;
@@ -993,7 +992,7 @@ static moshi_status run_frame(moshi_state *s, const int32_t *user, int32_t *out,
     s->gpu_frames += 1;
   }
   if (ho[(size_t)d.B * (1 + d.Q) + d.B] != 0) {  // a phase wait of the persistent kernel timed out
-    (void)hipMemsetAsync(s->sync, 0, (size_t)((char *)s->d_tl - (char *)s->sync), s->stream);
+    // the phase flags stay: later frames wait for larger tags
     (void)hipMemsetAsync(s->d_err, 0, 4, s->stream);
     (void)hipStreamSynchronize(s->stream);
     return fail(s, MOSHI_EDEVICE, "persistent frame kernel: a phase wait timed out");
