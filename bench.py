@@ -29,9 +29,10 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def stage_bytes(cfg, band: str, n_kv: float) -> dict:
+def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1) -> dict:
     """Algorithmic HBM bytes of one launch of each stage: the weights it must stream once, the
-    KV it must read, and its activation vectors (read once, written once)."""
+    KV it must read (n_kv positions per conversation), and its activation vectors (read once,
+    written once), for `rows` conversations."""
     D, F, Dd, Fd, Q = cfg.d_model, cfg.ffn_hidden, cfg.dep_d_model, cfg.dep_ffn_hidden, cfg.dep_q
     Vt, Va, L = cfg.text_card, cfg.audio_card, cfg.n_layers
     we = {"f32": 4, "bf16": 2, "i8": 1}[band]
@@ -41,11 +42,11 @@ def stage_bytes(cfg, band: str, n_kv: float) -> dict:
     def lin(n, k):
         return n * k * we + n * sc
 
-    f = 4  # float32 activations
+    f = 4 * rows  # float32 activations, one row per conversation
     return {
-        "embed": (2 * Q + 1) * D * (2 if band != "f32" else 4) + 2 * D * f,
+        "embed": (2 * Q + 1) * D * (2 if band != "f32" else 4) * rows + 2 * D * f,
         "qkv": lin(3 * D, D) + 2 * D * f + D * f + 2 * D * kve,
-        "attn": 2 * n_kv * D * kve + 2 * D * f,
+        "attn": 2 * n_kv * D * kve * rows + 2 * D * f,
         "out_proj": lin(D, D) + D * f + 2 * D * f,
         "gate_in": lin(2 * F, D) + 2 * D * f + F * f,
         "gate_out": lin(D, F) + F * f + 2 * D * f,
@@ -61,11 +62,12 @@ def stage_bytes(cfg, band: str, n_kv: float) -> dict:
 
 
 def frame_bytes(weight_bytes: int, cfg, band: str, positions) -> float:
-    """Weights + KV read per frame (the frame-level roofline of the method), averaged over the
-    given positions."""
+    """Weights (streamed once per frame for all conversations) + the KV every conversation reads,
+    per frame, averaged over the frames: positions is [B][frames] (or [frames] at B = 1)."""
     kve = 4 if band == "f32" else 2
-    n = np.minimum(np.asarray(positions) + 1, cfg.context)
-    return weight_bytes + float(np.mean(n)) * cfg.n_layers * 2 * cfg.d_model * kve
+    pos = np.atleast_2d(np.asarray(positions))
+    n = np.minimum(pos + 1, cfg.context)
+    return weight_bytes + float(np.mean(n.sum(axis=0))) * cfg.n_layers * 2 * cfg.d_model * kve
 
 
 def cpu_baseline(cfg, weights, users, budget_s: float, max_frames: int):
@@ -113,11 +115,13 @@ def main():
 
     cfg = synth.CONFIGS[args.config]
     band = cfg.band
+    B = cfg.batch
     t = time.time()
     weights = synth.gen_weights(cfg)
     log(f"generated {cfg.name} weights (seed {cfg.seed}) in {time.time() - t:.1f}s")
     K, W = args.steps, args.warmup
-    users = synth.user_tokens(cfg, max(K, W, args.profile_frames))
+    nprof = args.profile_frames
+    nframes = nprof + W + K
 
     sess = rq.Session(cfg, exec=args.exec)
     t = time.time()
@@ -125,34 +129,64 @@ def main():
     log(f"loaded weights in {time.time() - t:.1f}s")
     lin_bytes, all_bytes = sess.weight_bytes()
 
+    # untimed setup: teacher-forced prefixes (long-context prefill, or per-conversation start
+    # offsets of the batched workload)
+    starts = np.zeros(B, np.int64)
+    if cfg.prefill:
+        starts[:] = cfg.prefill
+    elif cfg.max_start_offset:
+        starts[:] = synth.start_offsets(cfg)
+    prefill_s = None
+    if starts.any():
+        t = time.time()
+        for b in range(B):
+            if starts[b]:
+                text, agent, user = synth.prefill_tokens(cfg, int(starts[b]), conv=b)
+                sess.prefill_forced(b, text, agent, user)
+        prefill_s = time.time() - t
+        log(f"prefilled {int(starts.sum())} positions over {B} conversation(s) in {prefill_s:.2f}s")
+    # users[f] is [B][Q] (B = 1: [1][Q])
+    users = np.stack([synth.user_tokens(cfg, nframes, conv=b, start_frame=int(starts[b])) for b in range(B)], axis=1)
+
     # per-stage HIP-event profile on the session stream (kernels launched one by one)
-    prof = sess.profile_frames(users[:args.profile_frames])
-    sess.reset()
-    sb = stage_bytes(cfg, band, n_kv=float(np.mean(np.arange(1, args.profile_frames + 1))))
+    prof = sess.profile_frames(users[:nprof])
+    from_zero = not starts.any()
+    if from_zero:
+        sess.reset()
+        pos0 = starts
+    else:
+        pos0 = starts + nprof
+    sb = stage_bytes(cfg, band, n_kv=float(np.mean(np.minimum(pos0 + 1, cfg.context))), rows=B)
     stages = {}
     for name, (n, us) in prof.items():
         if n:
-            stages[name] = {"launches": n, "avg_us": us / n, "total_us_per_frame": us / args.profile_frames,
+            stages[name] = {"launches": n, "avg_us": us / n, "total_us_per_frame": us / nprof,
                             "bytes_per_launch": sb[name],
                             "gbs": sb[name] / (us / n) / 1e3 if us > 0 else None}
     dom = max((k for k in stages if k != "frame_end"), key=lambda k: stages[k]["total_us_per_frame"])
     prof_frame_us = sum(v["total_us_per_frame"] for v in stages.values())
-    log(f"profiled {args.profile_frames} frames; dominant stage {dom}: "
+    log(f"profiled {nprof} frames; dominant stage {dom}: "
         f"{stages[dom]['avg_us']:.1f} us/launch, {stages[dom]['gbs']:.0f} GB/s")
 
+    f0 = 0 if from_zero else nprof
     for f in range(W):
-        sess.step(users[f])
-    sess.reset()
+        sess.step(users[f0 + f])
+    if from_zero:
+        sess.reset()
+        ft = 0
+    else:
+        ft = f0 + W
+    tpos = (pos0 + (0 if from_zero else W))[:, None] + np.arange(K)[None, :]  # positions of the timed frames
     sess.gpu_time(1)  # HIP events around each frame's device work, on the session stream
     t0 = time.perf_counter()
     for f in range(K):
-        sess.step(users[f])
+        sess.step(users[ft + f])
     dt = time.perf_counter() - t0
     gpu_us, gpu_n = sess.gpu_time(0)
     fps = K / dt
-    fb = frame_bytes(lin_bytes, cfg, band, np.arange(K))
-    log(f"{K} frames in {dt:.3f}s: {fps:.1f} frames/s, {fb / (dt / K) / 1e9:.0f} GB/s frame-level; "
-        f"GPU {gpu_us / gpu_n:.1f} us/frame")
+    fb = frame_bytes(lin_bytes, cfg, band, tpos)
+    log(f"{K} frames in {dt:.3f}s: {fps:.1f} frames/s ({B * fps:.1f} conversation-frames/s), "
+        f"{fb / (dt / K) / 1e9:.0f} GB/s frame-level; GPU {gpu_us / gpu_n:.1f} us/frame")
     sess.close()
 
     if args.exec == "persistent":
@@ -169,19 +203,31 @@ def main():
                     "bytes_per_launch": d["bytes_per_launch"], "avg_us": round(d["avg_us"], 2)}
 
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, weights, users, args.cpu_seconds, max_frames=30)
+    if not args.no_cpu_baseline and from_zero and B == 1:
+        cpu = cpu_baseline(cfg, weights, users[:, 0], args.cpu_seconds, max_frames=30)
         log(f"cpu baseline: {cpu['value']:.3f} frames/s on {cpu['cores']} threads")
 
+    metric, unit, value, what = METRIC, "frames/s", fps, "greedy frames from offset 0"
+    if band == "i8":
+        metric = "frames/s (80 ms) at B=1, Moshi-7B shape int8 per-row weights; % of HBM roofline"
+    if cfg.prefill:
+        metric = f"frames/s (80 ms) at B=1 after a {cfg.prefill}-frame prefill, Moshi-7B shape bf16; % of HBM roofline"
+        what = f"greedy frames at positions {int(tpos.min())}..{int(tpos.max())} after a teacher-forced prefill"
+    if B > 1:
+        metric = f"conversation-frames/s at B={B}, Moshi-7B shape bf16; % of HBM roofline"
+        unit, value = "conversation-frames/s", B * fps
+        what = (f"greedy frames of {B} conversations stepped together, each after a teacher-forced prefix "
+                f"of U{{0..{cfg.max_start_offset - 1}}} frames")
     out = {
-        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "metric": metric, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(1000 * dt / K, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if band == "bf16" else band, "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: Moshi-7B-shaped RQ-Transformer frame step, {K} greedy frames from "
-                               f"offset 0, seed-{cfg.seed} N(0,0.02) weights, uniform user tokens",
-                   "batch": cfg.batch, "band": band, "accumulate": "f32", "exec": args.exec,
-                   "weight_bytes_per_frame": lin_bytes},
-        "tokens_per_s": round(9 * fps, 1),
+        "config": {"workload": f"{cfg.name}: Moshi-7B-shaped RQ-Transformer frame step, {K} {what}, "
+                               f"seed-{cfg.seed} N(0,0.02) weights, uniform user tokens",
+                   "batch": B, "band": band, "accumulate": "f32", "exec": args.exec,
+                   "weight_bytes_per_frame": lin_bytes,
+                   "prefill_positions": int(starts.sum()), "prefill_s": None if prefill_s is None else round(prefill_s, 3)},
+        "tokens_per_s": round(9 * B * fps, 1),
         "frame_roofline": {"bytes_per_frame": fb, "achieved_gbs": round(fb / (dt / K) / 1e9, 1),
                            "frac": round(fb / (dt / K) / 1e9 / HBM_PEAK_GBS, 4),
                            "gpu_us_per_frame": round(gpu_us / gpu_n, 2)},

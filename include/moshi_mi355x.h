@@ -256,6 +256,17 @@ moshi_status moshi_profile_frames(moshi_state *s, int32_t n_frames, const int32_
 moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W, const float *x,
                               float *y, int32_t iters, float *avg_us);
 
+/*
+ * Y[M][N] = X[M][K] . W[N][K]^T with the library's matrix-core projection (the batched-frame and
+ * prefill path), on fresh device copies of the host arrays.  W is given as float32 and stored per
+ * band as moshi_load_weights would (f32, bf16, or int8 with per-row scales); X is float32 and is
+ * rounded to bf16 for the bf16 and int8 bands, as the batched path rounds its activations.  Y is
+ * float32 [M][N], written on success.  iters / avg_us as for moshi_debug_gemv.  Requires M >= 1,
+ * N >= 1, K >= 16 and K % 16 == 0.  Errors: MOSHI_EINVAL, MOSHI_ENOMEM, MOSHI_EDEVICE.
+ */
+moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, const float *W, const float *X,
+                              float *Y, int32_t iters, float *avg_us);
+
 #ifdef __cplusplus
 }
 #endif

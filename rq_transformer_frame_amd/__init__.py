@@ -37,6 +37,7 @@ _SIGS = {
     "moshi_weight_bytes": (_i32, [_vp, _vp, _vp]),
     "moshi_stream": (_vp, [_vp]),
     "moshi_debug_gemv": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "moshi_debug_gemm": (_i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
     "moshi_profile_frames": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "moshi_gpu_time": (_i32, [_vp, _i32, _vp, _vp]),
     "moshi_phase_times": (_i32, [_vp, _i32, _vp, _i32, _vp]),
@@ -262,3 +263,22 @@ def debug_gemv(band: str, W: np.ndarray, x: np.ndarray, iters: int = 0):
     if st != MOSHI_OK:
         raise MoshiError(st, f"moshi_debug_gemv: {lib.moshi_status_string(st).decode()}")
     return y, (us.value if iters > 0 else None)
+
+
+def debug_gemm(band: str, W: np.ndarray, X: np.ndarray, iters: int = 0):
+    """Y = X . W^T with the library's matrix-core projection (W float32 [N, K] stored per band, X
+    float32 [M, K], rounded to bf16 for the bf16 and int8 bands).  Returns (Y, mean kernel
+    microseconds or None)."""
+    lib = load_library()
+    W = np.ascontiguousarray(W, np.float32)
+    X = np.ascontiguousarray(X, np.float32)
+    N, K = W.shape
+    M, K2 = X.shape
+    if K2 != K:
+        raise ValueError("X and W disagree on K")
+    Y = np.zeros((M, N), np.float32)
+    us = ctypes.c_float(0)
+    st = lib.moshi_debug_gemm(BANDS[band], M, N, K, _ptr(W), _ptr(X), _ptr(Y), iters, ctypes.byref(us))
+    if st != MOSHI_OK:
+        raise MoshiError(st, f"moshi_debug_gemm: {lib.moshi_status_string(st).decode()}")
+    return Y, (us.value if iters > 0 else None)

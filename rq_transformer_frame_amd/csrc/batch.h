@@ -1,0 +1,291 @@
+// Row-batched frame path: the frame of several conversations (one activation row per
+// conversation) and the teacher-forced prefill of one conversation (one row per position) run
+// their projections on the matrix cores (gemm.h).  The kernels here are the steps around those
+// products, one block per activation row unless stated: the norm and bf16 rounding of a
+// projection's input, rope and the KV append, the gated-unit product, the argmax of a head, the
+// depformer entry and attention ([LM]: the docs.rs page "inferencelayer 0.2.4 src/moshi_lm.rs").
+#pragma once
+#include "gemm.h"
+#include "kernels.h"
+
+namespace mk {
+
+// Which conversation and absolute position an activation row stands for.  In a frame, row m is
+// conversation b0 + m at its own offset; in a prefill every row belongs to conversation `conv`,
+// at consecutive positions pos0 + m.
+struct RowMap {
+  int conv;  // < 0: frame
+  int b0;
+  int64_t pos0;
+  __device__ __forceinline__ int conv_of(int m) const { return conv < 0 ? b0 + m : conv; }
+  __device__ __forceinline__ int64_t pos_of(const Bufs &s, int m) const {
+    return conv < 0 ? s.offset[b0 + m] : pos0 + m;
+  }
+};
+
+// X[m] = rms_norm(src[m]; alpha) (or src[m] when alpha is null), rounded to XT; with `copy` set
+// the float32 result also goes to copy[m] (the post-out_norm hidden).  Dynamic LDS: K floats.
+template <typename XT>
+__global__ __launch_bounds__(BLOCK) void k_rows_cvt(const float *__restrict__ src, int lds,
+                                                    const float *__restrict__ alpha, float eps, int K,
+                                                    XT *__restrict__ X, int ldx, float *__restrict__ copy, int ldc) {
+  extern __shared__ float xs[];
+  __shared__ float red[NWAVES];
+  const int m = blockIdx.x;
+  if (alpha)
+    stage_rms(src + (size_t)m * lds, alpha, K, eps, xs, red);
+  else
+    stage_vec(src + (size_t)m * lds, K, xs);
+  for (int k = threadIdx.x; k < K; k += BLOCK) {
+    X[(size_t)m * ldx + k] = from_f<XT>(xs[k]);
+    if (copy) copy[(size_t)m * ldc + k] = xs[k];
+  }
+}
+
+// a4.1 after the fused q|k|v product Y[m] (3 D columns): interleaved rope on q and k at the
+// row's position (angle f_i * pos in float32, sin / cos in double), q to q_out[m], k and v to
+// the row's conversation's KV slot pos % cap of `layer` ([LM] temporal_step, rope_row).
+template <typename KT>
+__global__ __launch_bounds__(BLOCK) void k_qkv_post(Dims d, Bufs s, KV<KT> kv, const float *__restrict__ Y, int ldy,
+                                                    float *__restrict__ q_out, int layer, RowMap rm) {
+  __shared__ float rcs[256];  // cos, sin of pair i at [2i], [2i + 1] (head dim <= 256)
+  const int m = blockIdx.x;
+  const int conv = rm.conv_of(m);
+  const int64_t pos = rm.pos_of(s, m);
+  const int slot = (int)(pos % d.cap);
+  for (int i = threadIdx.x; i < d.hd / 2; i += BLOCK) {
+    const float ang = s.rope_freq[i] * (float)pos;
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    rcs[2 * i] = (float)cd;
+    rcs[2 * i + 1] = (float)sd;
+  }
+  __syncthreads();
+  const float *y = Y + (size_t)m * ldy;
+  for (int p = threadIdx.x; p < 3 * d.D / 2; p += BLOCK) {
+    const int r0 = 2 * p;
+    float v0 = y[r0], v1 = y[r0 + 1];
+    const int part = r0 / d.D;  // 0 q, 1 k, 2 v
+    const int rr = r0 - part * d.D;
+    const int h = rr / d.hd, e = rr - h * d.hd;
+    if (part < 2) {
+      const float cs = rcs[e], sn = rcs[e + 1];
+      const float a0 = v0 * cs - v1 * sn;
+      const float a1 = v0 * sn + v1 * cs;
+      v0 = a0;
+      v1 = a1;
+    }
+    if (part == 0) {
+      q_out[(size_t)m * d.D + rr] = v0;
+      q_out[(size_t)m * d.D + rr + 1] = v1;
+    } else {
+      KT *cache = part == 1 ? kv.k : kv.v;
+      const size_t idx = ((((size_t)conv * d.L + layer) * d.H + h) * d.cap + slot) * d.hd + e;
+      cache[idx] = from_f<KT>(v0);
+      cache[idx + 1] = from_f<KT>(v1);
+    }
+  }
+}
+
+// a5 between the two gated-unit products: X[m][j] = silu(Y[m][2j]) * Y[m][2j + 1] (the device
+// copy of linear_in has gate row j and mult row j interleaved), rounded to XT.  Grid
+// (rows, ceil(F / BLOCK)).
+template <typename XT>
+__global__ __launch_bounds__(BLOCK) void k_gate_post(const float *__restrict__ Y, int ldy, int F, XT *__restrict__ X,
+                                                     int ldx) {
+  const int m = blockIdx.x;
+  const int j = blockIdx.y * BLOCK + threadIdx.x;
+  if (j >= F) return;
+  const float2 gm = *reinterpret_cast<const float2 *>(Y + (size_t)m * ldy + 2 * j);
+  X[(size_t)m * ldx + j] = from_f<XT>(silu(gm.x) * gm.y);
+}
+
+// a7 / a8 greedy head: the first-wins argmax of logits row m (N values), stored as the single
+// partial part[m * stride] that the consumers of a head's token merge.
+__global__ __launch_bounds__(BLOCK) void k_argmax_rows(const float *__restrict__ L, int ld, int N,
+                                                       ArgBest *__restrict__ part, int stride) {
+  __shared__ ArgBest wb[NWAVES];
+  const int m = blockIdx.x;
+  const float *l = L + (size_t)m * ld;
+  ArgBest best = arg_none();
+  for (int i = threadIdx.x; i < N; i += BLOCK) best = arg_take(best, l[i], i);
+  best = wave_arg(best);
+  if ((threadIdx.x & 63) == 0) wb[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ArgBest t = wb[0];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) t = arg_merge(t, wb[w]);
+    part[(size_t)m * stride] = t;
+  }
+}
+
+// a8 entry of depformer step cb for conversation b0 + m: prev = the previous head's token,
+// y = depformer_in[cb] . hidden + table[prev], X[m] = rms_norm(y; norm1 of layer 0) as XT.
+// Dynamic LDS: Dd floats.
+template <typename ET, typename XT>
+__global__ __launch_bounds__(BLOCK) void k_dep_entry(Dims d, Bufs s, const ET *__restrict__ table, int cb,
+                                                     const float *__restrict__ norm, XT *__restrict__ X, int ldx,
+                                                     int b0) {
+  extern __shared__ float xs[];
+  __shared__ float red[NWAVES];
+  const int m = blockIdx.x, b = b0 + m;
+  const int Dd = d.Dd;
+  const int prev = reduce_head_partials(s.am_part + ((size_t)b * (1 + d.Q) + cb) * AM_MAX_BLOCKS, 1);
+  if (threadIdx.x == 0) s.tokens[(size_t)b * (1 + d.Q) + cb] = prev;
+  const float *dinp = s.din + ((size_t)b * d.Q + cb) * Dd;
+  float *y = s.y + (size_t)b * Dd;
+  for (int k = threadIdx.x; k < Dd; k += BLOCK) {
+    const float v = dinp[k] + to_f(table[(size_t)prev * Dd + k]);  // argmax tokens are >= 0
+    xs[k] = v;
+    y[k] = v;
+  }
+  __syncthreads();
+  rms_in_place(xs, norm, Dd, d.eps, red);
+  for (int k = threadIdx.x; k < Dd; k += BLOCK) X[(size_t)m * ldx + k] = from_f<XT>(xs[k]);
+}
+
+// a8 after the depformer q|k|v product Y[m] (3 Dd columns, no rope): q to dq, k and v to the
+// per-frame cache entry (layer, cb) of conversation b0 + m.
+__global__ __launch_bounds__(BLOCK) void k_dep_qkv_post(Dims d, Bufs s, const float *__restrict__ Y, int ldy,
+                                                        int layer, int cb, int b0) {
+  const int m = blockIdx.x, b = b0 + m;
+  const int Dd = d.Dd;
+  const float *y = Y + (size_t)m * ldy;
+  float *kvbase = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q + cb) * 2) * Dd;
+  for (int r = threadIdx.x; r < 3 * Dd; r += BLOCK) {
+    if (r < Dd)
+      s.dq[(size_t)b * Dd + r] = y[r];
+    else
+      kvbase[r - Dd] = y[r];
+  }
+}
+
+// a8 depformer attention of conversation b0 + m: dq over the cb + 1 cache entries of `layer`
+// ([LM] attend; weights e_p / den), 16 lanes per head, EPL dims per lane; o goes to X[m] as XT.
+template <typename XT, int EPL>
+__global__ __launch_bounds__(BLOCK) void k_dep_attn(Dims d, Bufs s, int layer, int cb, XT *__restrict__ X, int ldx,
+                                                    int b0) {
+  const int m = blockIdx.x, b = b0 + m;
+  const int Dd = d.Dd, hdd = d.hdd;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
+  const float *q = s.dq + (size_t)b * Dd;
+  const float *kv0 = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q) * 2) * Dd;
+  const float scale = 1.0f / sqrtf((float)hdd);
+  const int npos = cb + 1;
+  for (int hh = wave * 4 + g; hh < d.Hd; hh += NWAVES * 4) {
+    const int e0 = hh * hdd + sub * EPL;
+    float qv[EPL], kk[DEP_MAX_POS][EPL], vv[DEP_MAX_POS][EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) qv[i] = q[e0 + i];
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p)
+      if (p < npos) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          kk[p][i] = kv0[(size_t)p * 2 * Dd + e0 + i];
+          vv[p][i] = kv0[(size_t)p * 2 * Dd + Dd + e0 + i];
+        }
+      }
+    float sc[DEP_MAX_POS];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p) {
+      float dot = 0.f;
+      if (p < npos) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
+      }
+      dot += __shfl_xor(dot, 8, WAVE);
+      dot += __shfl_xor(dot, 4, WAVE);
+      dot += __shfl_xor(dot, 2, WAVE);
+      dot += __shfl_xor(dot, 1, WAVE);
+      dot = __shfl(dot, lane & 48, WAVE);
+      sc[p] = dot * scale;
+      if (p < npos) mx = fmaxf(mx, sc[p]);
+    }
+    float den = 0.f;
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p)
+      if (p < npos) {
+        sc[p] = expf(sc[p] - mx);
+        den += sc[p];
+      }
+    float o[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p)
+      if (p < npos) {
+        const float wgt = sc[p] / den;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) o[i] = fmaf(wgt, vv[p][i], o[i]);
+      }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) X[(size_t)m * ldx + e0 + i] = from_f<XT>(o[i]);
+  }
+}
+
+// a11 bookkeeping of a teacher-forced prefill of T frames of conversation `conv`, one thread:
+// for each frame, the user write and the gather of the 17 model inputs (into rows[t]), then the
+// forced ring write and the offset step, exactly as the frame kernels do them one frame at a time.
+__global__ void k_prefill_ring(Dims d, Bufs s, int conv, int T, const int32_t *__restrict__ text,
+                               const int32_t *__restrict__ agent, const int32_t *__restrict__ user,
+                               int32_t *__restrict__ rows) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  int32_t *rg = s.ring + (size_t)conv * d.NS * 3;
+  int64_t off = s.offset[conv];
+  for (int t = 0; t < T; ++t) {
+    const int32_t *u = user + (size_t)t * d.Q;
+    for (int st = 0; st < d.NS; ++st) {
+      const int delay = stream_delay(st, d.Q);
+      int v;
+      if (off <= delay)
+        v = (st == 0) ? d.Vt : d.Va;
+      else if (st >= d.Q + 1 && delay == 0)
+        v = u[st - d.Q - 1];
+      else
+        v = rg[st * 3 + (int)(off % 3)];
+      rows[(size_t)t * d.NS + st] = v;
+    }
+    for (int st = d.Q + 1; st < d.NS; ++st) rg[st * 3 + (int)((off + stream_delay(st, d.Q)) % 3)] = u[st - d.Q - 1];
+    off += 1;
+    const int p = (int)(off % 3);
+    rg[p] = text[t];
+    for (int k = 0; k < d.Q; ++k) rg[(1 + k) * 3 + p] = agent[(size_t)t * d.Q + k];
+  }
+  s.offset[conv] = off;
+}
+
+// a3 for prefill rows: x[t] = the 17-row embedding sum of rows[t] (audio tables in stream order,
+// then text; -1 adds nothing, < -1 reads row 0).  Grid (ceil(D / BLOCK), T).
+template <typename ET>
+__global__ __launch_bounds__(BLOCK) void k_embed_rows(Dims d, const int32_t *__restrict__ rows,
+                                                      const ET *__restrict__ emb_audio,
+                                                      const ET *__restrict__ emb_text, float *__restrict__ x) {
+  __shared__ int tok[MAX_STREAMS];
+  const int t = blockIdx.y;
+  if (threadIdx.x < d.NS) tok[threadIdx.x] = rows[(size_t)t * d.NS + threadIdx.x];
+  __syncthreads();
+  for (int c = blockIdx.x * BLOCK + threadIdx.x; c < d.D; c += gridDim.x * BLOCK) {
+    float v[MAX_STREAMS];
+#pragma unroll
+    for (int k = 0; k < MAX_STREAMS; ++k) {
+      if (k < d.NS) {
+        const int tk = tok[k];
+        const int row = tk < 0 ? 0 : tk;
+        v[k] = tk == -1 ? 0.f
+                        : to_f(k == 0 ? emb_text[(size_t)row * d.D + c]
+                                      : emb_audio[((size_t)(k - 1) * (d.Va + 1) + row) * d.D + c]);
+      }
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 1; k < MAX_STREAMS; ++k)
+      if (k < d.NS && tok[k] != -1) acc += v[k];
+    if (tok[0] != -1) acc += v[0];
+    x[(size_t)t * d.D + c] = acc;
+  }
+}
+
+}  // namespace mk

@@ -168,6 +168,7 @@ __device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
 constexpr int SCH = 8;
 constexpr int BUF_DWORD3 = 0x00020000;  // raw 32-bit buffer resource word 3 for gfx9-family parts
 constexpr int BUF_NT = 2;               // cache policy: nontemporal (streamed once)
+constexpr int BUF_OOB = 0x7FFFFFF0;     // an offset past the end of every buffer resource used here
 
 typedef unsigned int u32x4b __attribute__((ext_vector_type(4)));
 

@@ -198,8 +198,19 @@ __global__ __launch_bounds__(BLOCK) void k_qkv_rope(Dims d, Bufs s, KV<KT> kv, c
 // writes o directly, otherwise the last split to finish merges the partials in split order.
 // Dynamic LDS: ceil(cap / S) floats.
 // --------------------------------------------------------------------------------------------
+// Query rows of the attention: in a frame (conv < 0) block z serves conversation b0 + z with its q
+// row, its offset and its cache; in a prefill block z serves query row z of q / o, at position
+// pos0 + z of conversation `conv` (launched with one split: every query attends to its own
+// window [max(0, pos + 1 - C), pos], all of which is in the cache before the launch).
+struct AttnQ {
+  const float *q;
+  float *o;
+  int conv;
+  int64_t pos0;
+};
+
 template <typename KT, int HD>
-__global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int layer, int b0) {
+__global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int layer, int b0, AttnQ aq) {
   extern __shared__ float sc[];
   __shared__ float red[NWAVES];
   __shared__ float ored[NWAVES][HD];
@@ -208,9 +219,10 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   __shared__ int s_last;
   constexpr int EPL = HD / 16;  // elements per lane; 16 lanes cover one position's head slice
   const int h = blockIdx.x, sp = blockIdx.y;
-  const int b = b0 + blockIdx.z;
+  const bool pf = aq.conv >= 0;
+  const int b = pf ? aq.conv : b0 + blockIdx.z;  // conversation whose cache is read
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
-  const int64_t pos = s.offset[b];
+  const int64_t pos = pf ? aq.pos0 + blockIdx.z : s.offset[b];
   const int n = (int)(pos + 1 < (int64_t)d.C ? pos + 1 : (int64_t)d.C);
   const int S = min((int)gridDim.y, max(1, (n + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK));
   if (sp >= S) return;
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   const int len = j1 > j0 ? j1 - j0 : 0;
 
   float qv[EPL];
-  const float *qp = s.q + (size_t)b * d.D + h * HD + sub * EPL;
+  const float *qp = (pf ? aq.q + (size_t)blockIdx.z * d.D : s.q + (size_t)b * d.D) + h * HD + sub * EPL;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) qv[i] = qp[i];
   const float scale = 1.0f / sqrtf((float)HD);
@@ -276,7 +288,7 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
     for (int i = 0; i < EPL; ++i) ored[wave][sub * EPL + i] = op[i];
   }
   __syncthreads();
-  float *out = s.o + (size_t)b * d.D + h * HD;
+  float *out = (pf ? aq.o + (size_t)blockIdx.z * d.D : s.o + (size_t)b * d.D) + h * HD;
   if (S == 1) {
     for (int t = threadIdx.x; t < HD; t += BLOCK) {
       float acc = 0.f;

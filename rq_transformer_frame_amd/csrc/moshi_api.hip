@@ -9,11 +9,13 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <type_traits>
 #include <string>
 #include <unordered_map>
 #include <vector>
 
+#include "batch.h"
 #include "frame_persistent.h"
 #include "moshi_mi355x.h"
 
@@ -22,6 +24,8 @@ using mk::bf16_t;
 namespace {
 
 enum Kind { K_LINEAR = 0, K_EMBED = 1, K_NORM = 2 };
+
+constexpr int PF_ROWS = 256;  // prefill positions per row-batched chunk
 
 struct Slot {
   std::string name;
@@ -92,6 +96,14 @@ struct moshi_state {
   const void *pkern = nullptr;  // selected k_frame_persistent instance
   size_t plds = 0;              // its dynamic LDS bytes
   int pgrid = 0;
+  // row-batched path (frames of several conversations, prefill): projection inputs (bf16, or
+  // f32 for the f32 band), projection outputs, and the prefill's per-position rows
+  void *gx = nullptr;
+  float *gy = nullptr;
+  int grows = 0;                // rows gx / gy hold
+  float *pf_x = nullptr, *pf_q = nullptr, *pf_o = nullptr;
+  int32_t *pf_rows = nullptr;   // [PF_ROWS][NS] gathered inputs
+  int32_t *pf_tok = nullptr;    // [PF_ROWS][1 + 2 Q] forced text, agent, user tokens of a chunk
   uint32_t *sync = nullptr;     // per-block phase flags of the persistent kernel
   uint32_t pserial = 0;         // persistent launches so far
   mk::LayerPtrs *d_tl = nullptr, *d_dl = nullptr;
@@ -300,6 +312,20 @@ moshi_status alloc_session(moshi_state *s) {
   req((void **)&s->d_phase_ts, nph * 2 * 8);
   s->nph = (int)nph;
   req((void **)&s->d_dl, (size_t)d.Ld * d.Q * sizeof(mk::LayerPtrs));
+  {
+    const size_t rows = std::max<size_t>(B > 1 ? B : 0, PF_ROWS);
+    const size_t xelt = s->cfg.band == MOSHI_BAND_F32 ? 4 : 2;
+    const size_t kmax = std::max({(size_t)d.D, (size_t)d.F, (size_t)d.Dd, (size_t)d.Fd});
+    const size_t nmax = std::max({(size_t)3 * d.D, (size_t)2 * d.F, (size_t)3 * d.Dd, (size_t)2 * d.Fd});
+    s->grows = (int)rows;
+    req(&s->gx, rows * kmax * xelt);
+    req((void **)&s->gy, rows * nmax * 4);
+    req((void **)&s->pf_x, (size_t)PF_ROWS * d.D * 4);
+    req((void **)&s->pf_q, (size_t)PF_ROWS * d.D * 4);
+    req((void **)&s->pf_o, (size_t)PF_ROWS * d.D * 4);
+    req((void **)&s->pf_rows, (size_t)PF_ROWS * d.NS * 4);
+    req((void **)&s->pf_tok, (size_t)PF_ROWS * (1 + 2 * d.Q) * 4);
+  }
   req(&s->kc, B * d.L * d.H * (size_t)d.cap * d.hd * kvelt);
   req(&s->vc, B * d.L * d.H * (size_t)d.cap * d.hd * kvelt);
   std::vector<size_t> offs;
@@ -489,9 +515,9 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
     const int chunk = (d.cap + d.S - 1) / d.S;
     run(MOSHI_STAGE_ATTN, [&] {
       if (d.hd == 128)
-        k_attn<KT, 128><<<dim3(d.H, d.S, nb), BLOCK, chunk * 4, st>>>(d, b, kv, l, b0);
+        k_attn<KT, 128><<<dim3(d.H, d.S, nb), BLOCK, chunk * 4, st>>>(d, b, kv, l, b0, AttnQ{nullptr, nullptr, -1, 0});
       else
-        k_attn<KT, 64><<<dim3(d.H, d.S, nb), BLOCK, chunk * 4, st>>>(d, b, kv, l, b0);
+        k_attn<KT, 64><<<dim3(d.H, d.S, nb), BLOCK, chunk * 4, st>>>(d, b, kv, l, b0, AttnQ{nullptr, nullptr, -1, 0});
     });
     run(MOSHI_STAGE_OUT_PROJ, [&] {
       k_gemv<WT, true, MOSHI_STAGE_OUT_PROJ><<<dim3(g_out, nb), BLOCK, l_out, st>>>(
@@ -560,8 +586,184 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
       [&] { k_frame_end<<<nb, BLOCK, 0, st>>>(d, b, b0, temporal_only ? 1 : 0, forced, prev_parts); });
 }
 
+// Temporal layers over `rows` activation rows x (ldx = D) on the matrix cores: one projection per
+// weight matrix for all rows.  Rows map to (conversation, position) through rm; q_rows / o_rows
+// are the rows' query and attention output buffers.
+template <typename WT, typename KT>
+void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, float *o_rows, mk::RowMap rm,
+                           int attn_splits, const std::function<void(int, const std::function<void()> &)> &run) {
+  using namespace mk;
+  typedef typename GemmX<WT>::type XT;
+  const Dims &d = s->d;
+  Bufs &b = s->b;
+  hipStream_t st = s->stream;
+  const KV<KT> kv{reinterpret_cast<KT *>(s->kc), reinterpret_cast<KT *>(s->vc)};
+  auto W = [&](int slot) { return reinterpret_cast<const WT *>(s->data(slot)); };
+  auto N = [&](int slot) { return reinterpret_cast<const float *>(s->data(slot)); };
+  XT *X = reinterpret_cast<XT *>(s->gx);
+  float *Y = s->gy;
+  const dim3 gm_rows(1, (rows + GM - 1) / GM);
+  auto gemm_grid = [&](int n) { return dim3((n + GN - 1) / GN, gm_rows.y); };
+  const size_t f4 = sizeof(float);
+  for (int l = 0; l < d.L; ++l) {
+    const LayerW &lw = s->layers[l];
+    run(MOSHI_STAGE_QKV, [&] {
+      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm1), d.eps, d.D, X, d.D, nullptr, 0);
+      k_gemm<WT, false, MOSHI_STAGE_QKV><<<gemm_grid(3 * d.D), GBLOCK, 0, st>>>(W(lw.in), s->scale(lw.in), 3 * d.D,
+                                                                               d.D, X, d.D, rows, Y, 3 * d.D);
+      k_qkv_post<KT><<<rows, BLOCK, 0, st>>>(d, b, kv, Y, 3 * d.D, q_rows, l, rm);
+    });
+    run(MOSHI_STAGE_ATTN, [&] {
+      const int chunk = (d.cap + attn_splits - 1) / attn_splits;
+      const AttnQ aq{q_rows, o_rows, rm.conv, rm.pos0};
+      if (d.hd == 128)
+        k_attn<KT, 128><<<dim3(d.H, attn_splits, rows), BLOCK, chunk * 4, st>>>(d, b, kv, l, rm.b0, aq);
+      else
+        k_attn<KT, 64><<<dim3(d.H, attn_splits, rows), BLOCK, chunk * 4, st>>>(d, b, kv, l, rm.b0, aq);
+    });
+    run(MOSHI_STAGE_OUT_PROJ, [&] {
+      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(o_rows, d.D, nullptr, d.eps, d.D, X, d.D, nullptr, 0);
+      k_gemm<WT, true, MOSHI_STAGE_OUT_PROJ><<<gemm_grid(d.D), GBLOCK, 0, st>>>(W(lw.out), s->scale(lw.out), d.D, d.D,
+                                                                              X, d.D, rows, x, d.D);
+    });
+    run(MOSHI_STAGE_GATE_IN, [&] {
+      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm2), d.eps, d.D, X, d.D, nullptr, 0);
+      k_gemm<WT, false, MOSHI_STAGE_GATE_IN><<<gemm_grid(2 * d.F), GBLOCK, 0, st>>>(
+          W(lw.gin), s->scale(lw.gin), 2 * d.F, d.D, X, d.D, rows, Y, 2 * d.F);
+      k_gate_post<XT><<<dim3(rows, (d.F + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.F, d.F, X, d.F);
+    });
+    run(MOSHI_STAGE_GATE_OUT, [&] {
+      k_gemm<WT, true, MOSHI_STAGE_GATE_OUT><<<gemm_grid(d.D), GBLOCK, 0, st>>>(W(lw.gout), s->scale(lw.gout), d.D,
+                                                                              d.F, X, d.F, rows, x, d.D);
+    });
+  }
+}
+
+// One frame of conversations [b0, b0 + nb) (nb >= 2) on the row-batched path ([LM] step_ext
+// steps 1-9 per conversation; every projection streams its weights once for all of them).
+template <typename WT, typename ET, typename KT>
+void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev, Prof *prof) {
+  using namespace mk;
+  typedef typename GemmX<WT>::type XT;
+  const Dims &d = s->d;
+  Bufs &b = s->b;
+  hipStream_t st = s->stream;
+  auto W = [&](int slot) { return reinterpret_cast<const WT *>(s->data(slot)); };
+  auto E = [&](int slot) { return reinterpret_cast<const ET *>(s->data(slot)); };
+  auto N = [&](int slot) { return reinterpret_cast<const float *>(s->data(slot)); };
+  std::function<void(int, const std::function<void()> &)> run = [&](int stage, const std::function<void()> &launch) {
+    if (prof && prof->used + 2 <= prof->ev.size()) {
+      (void)hipEventRecord(prof->ev[prof->used], st);
+      launch();
+      (void)hipEventRecord(prof->ev[prof->used + 1], st);
+      prof->stage[prof->used / 2] = stage;
+      prof->used += 2;
+    } else {
+      launch();
+    }
+  };
+  XT *X = reinterpret_cast<XT *>(s->gx);
+  float *Y = s->gy;
+  const int rows = nb;
+  auto gemm_grid = [&](int n) { return dim3((n + GN - 1) / GN, (rows + GM - 1) / GM); };
+  const size_t f4 = sizeof(float);
+  float *x = b.x + (size_t)b0 * d.D;
+
+  run(MOSHI_STAGE_EMBED, [&] {
+    k_embed_begin<ET><<<dim3(blocks_for(d.D, BLOCK, 64), nb), BLOCK, 0, st>>>(d, b, E(s->emb[0]), E(s->text_emb),
+                                                                                user_dev, b0);
+  });
+  enqueue_temporal_rows<WT, KT>(s, rows, x, b.q + (size_t)b0 * d.D, b.o + (size_t)b0 * d.D, RowMap{-1, b0, 0}, d.S,
+                                run);
+  const int AM = AM_MAX_BLOCKS;
+  run(MOSHI_STAGE_TEXT_HEAD, [&] {
+    k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(s->out_norm), d.eps, d.D, X, d.D,
+                                                  b.hidden + (size_t)b0 * d.D, d.D);
+    k_gemm<WT, false, MOSHI_STAGE_TEXT_HEAD><<<gemm_grid(d.Vt), GBLOCK, 0, st>>>(
+        W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, X, d.D, rows, b.text_logits + (size_t)b0 * d.Vt, d.Vt);
+    k_argmax_rows<<<rows, BLOCK, 0, st>>>(b.text_logits + (size_t)b0 * d.Vt, d.Vt, d.Vt,
+                                          b.am_part + (size_t)b0 * (1 + d.Q) * AM, (1 + d.Q) * AM);
+  });
+  run(MOSHI_STAGE_DEP_IN, [&] {
+    k_gemm<WT, false, MOSHI_STAGE_DEP_IN><<<gemm_grid(d.Q * d.Dd), GBLOCK, 0, st>>>(
+        W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, X, d.D, rows, b.din + (size_t)b0 * d.Q * d.Dd, d.Q * d.Dd);
+  });
+  float *y = b.y + (size_t)b0 * d.Dd;
+  for (int cb = 0; cb < d.Q; ++cb) {
+    const ET *table = cb == 0 ? E(s->dep_text_emb) : E(s->dep_emb[cb - 1]);
+    for (int j = 0; j < d.Ld; ++j) {
+      const LayerW &lw = s->dlayers[j][cb];
+      run(MOSHI_STAGE_DEP_QKV, [&] {
+        if (j == 0)
+          k_dep_entry<ET, XT><<<rows, BLOCK, d.Dd * f4, st>>>(d, b, table, cb, N(lw.norm1), X, d.Dd, b0);
+        else
+          k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm1), d.eps, d.Dd, X, d.Dd, nullptr, 0);
+        k_gemm<WT, false, MOSHI_STAGE_DEP_QKV><<<gemm_grid(3 * d.Dd), GBLOCK, 0, st>>>(
+            W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X, d.Dd, rows, Y, 3 * d.Dd);
+        k_dep_qkv_post<<<rows, BLOCK, 0, st>>>(d, b, Y, 3 * d.Dd, j, cb, b0);
+      });
+      run(MOSHI_STAGE_DEP_OUT, [&] {
+        with_epl(d.hdd, [&](auto e) {
+          k_dep_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, j, cb, X, d.Dd, b0);
+        });
+        k_gemm<WT, true, MOSHI_STAGE_DEP_OUT><<<gemm_grid(d.Dd), GBLOCK, 0, st>>>(W(lw.out), s->scale(lw.out), d.Dd,
+                                                                                d.Dd, X, d.Dd, rows, y, d.Dd);
+      });
+      run(MOSHI_STAGE_DEP_GATE_IN, [&] {
+        k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm2), d.eps, d.Dd, X, d.Dd, nullptr, 0);
+        k_gemm<WT, false, MOSHI_STAGE_DEP_GATE_IN><<<gemm_grid(2 * d.Fd), GBLOCK, 0, st>>>(
+            W(lw.gin), s->scale(lw.gin), 2 * d.Fd, d.Dd, X, d.Dd, rows, Y, 2 * d.Fd);
+        k_gate_post<XT><<<dim3(rows, (d.Fd + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.Fd, d.Fd, X, d.Fd);
+      });
+      run(MOSHI_STAGE_DEP_GATE_OUT, [&] {
+        k_gemm<WT, true, MOSHI_STAGE_DEP_GATE_OUT><<<gemm_grid(d.Dd), GBLOCK, 0, st>>>(
+            W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, X, d.Fd, rows, y, d.Dd);
+      });
+    }
+    run(MOSHI_STAGE_DEP_HEAD, [&] {
+      k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, nullptr, d.eps, d.Dd, X, d.Dd, nullptr, 0);
+      float *lg = b.audio_logits + (size_t)b0 * d.Q * d.Va + (size_t)cb * d.Va;
+      k_gemm<WT, false, MOSHI_STAGE_DEP_HEAD><<<gemm_grid(d.Va), GBLOCK, 0, st>>>(
+          W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, X, d.Dd, rows, lg, d.Q * d.Va);
+      k_argmax_rows<<<rows, BLOCK, 0, st>>>(lg, d.Q * d.Va, d.Va, b.am_part + ((size_t)b0 * (1 + d.Q) + 1 + cb) * AM,
+                                            (1 + d.Q) * AM);
+    });
+  }
+  run(MOSHI_STAGE_FRAME_END, [&] { k_frame_end<<<nb, BLOCK, 0, st>>>(d, b, b0, 0, mk::Forced{}, 1); });
+}
+
+// Teacher-forced prefill of T (<= PF_ROWS) positions of conversation conv from device token
+// arrays (text [T], agent [T][Q], user [T][Q]): the ring replay, then the temporal layers for
+// all positions at once.  Every position's window lies below the cache capacity.
+template <typename WT, typename ET, typename KT>
+void enqueue_prefill_rows(moshi_state *s, int conv, int T, int64_t pos0, const int32_t *text, const int32_t *agent,
+                          const int32_t *user) {
+  using namespace mk;
+  const Dims &d = s->d;
+  hipStream_t st = s->stream;
+  auto E = [&](int slot) { return reinterpret_cast<const ET *>(s->data(slot)); };
+  k_prefill_ring<<<1, 64, 0, st>>>(d, s->b, conv, T, text, agent, user, s->pf_rows);
+  k_embed_rows<ET><<<dim3(blocks_for(d.D, BLOCK, 64), T), BLOCK, 0, st>>>(d, s->pf_rows, E(s->emb[0]),
+                                                                           E(s->text_emb), s->pf_x);
+  std::function<void(int, const std::function<void()> &)> run = [](int, const std::function<void()> &f) { f(); };
+  enqueue_temporal_rows<WT, KT>(s, T, s->pf_x, s->pf_q, s->pf_o, RowMap{conv, 0, pos0}, 1, run);
+}
+
 void enqueue_frame(moshi_state *s, int b0, int nb, bool temporal_only, const int32_t *user_dev,
                    const mk::Forced &forced, Prof *prof = nullptr) {
+  if (nb >= 2 && !temporal_only) {  // several conversations: projections on the matrix cores
+    switch (s->cfg.band) {
+      case MOSHI_BAND_F32:
+        enqueue_frame_rows<float, float, float>(s, b0, nb, user_dev, prof);
+        break;
+      case MOSHI_BAND_BF16:
+        enqueue_frame_rows<bf16_t, bf16_t, bf16_t>(s, b0, nb, user_dev, prof);
+        break;
+      default:
+        enqueue_frame_rows<int8_t, bf16_t, bf16_t>(s, b0, nb, user_dev, prof);
+    }
+    return;
+  }
   switch (s->cfg.band) {
     case MOSHI_BAND_F32:
       enqueue_frame_t<float, float, float>(s, b0, nb, temporal_only, user_dev, forced, prof);
@@ -1138,18 +1340,49 @@ moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const
     return fail(s, MOSHI_ERANGE, "prefill of %d positions from offset %lld exceeds kv_capacity %d", T,
                 (long long)s->h_offset[conv], d.cap);
   if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
-  int32_t *du = nullptr;
-  HIP_TRY(s, hipMalloc(&du, sizeof(int32_t) * (size_t)T * d.Q));
-  hipError_t e = hipMemcpy(du, user, sizeof(int32_t) * (size_t)T * d.Q, hipMemcpyHostToDevice);
-  for (int t = 0; t < T && e == hipSuccess; ++t) {
-    mk::Forced f{};
-    f.t[0] = text[t];
-    for (int k = 0; k < d.Q; ++k) f.t[1 + k] = agent[(size_t)t * d.Q + k];
-    enqueue_frame(s, conv, 1, true, du + (size_t)t * d.Q, f, nullptr);
+  // device copy of the forced tokens: text [T], agent [T][Q], user [T][Q]
+  const size_t nt = (size_t)T * (1 + 2 * d.Q);
+  std::vector<int32_t> h(nt);
+  std::memcpy(h.data(), text, sizeof(int32_t) * T);
+  std::memcpy(h.data() + T, agent, sizeof(int32_t) * (size_t)T * d.Q);
+  std::memcpy(h.data() + T + (size_t)T * d.Q, user, sizeof(int32_t) * (size_t)T * d.Q);
+  int32_t *dt = nullptr;
+  HIP_TRY(s, hipMalloc(&dt, sizeof(int32_t) * nt));
+  const int32_t *dtext = dt, *dagent = dt + T, *duser = dt + T + (size_t)T * d.Q;
+  hipError_t e = hipMemcpy(dt, h.data(), sizeof(int32_t) * nt, hipMemcpyHostToDevice);
+  // Positions whose window has not begun to slide (and whose slots are not reused) run as row
+  // batches on the matrix cores; the rest one frame at a time.
+  const int64_t limit = std::min<int64_t>(d.C, d.cap);
+  for (int t = 0; t < T && e == hipSuccess;) {
+    const int64_t pos = s->h_offset[conv] + t;
+    const int64_t room = limit - pos;
+    if (room >= 2 && T - t >= 2) {
+      const int n = (int)std::min<int64_t>({room, (int64_t)PF_ROWS, (int64_t)(T - t)});
+      switch (s->cfg.band) {
+        case MOSHI_BAND_F32:
+          enqueue_prefill_rows<float, float, float>(s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q,
+                                                    duser + (size_t)t * d.Q);
+          break;
+        case MOSHI_BAND_BF16:
+          enqueue_prefill_rows<bf16_t, bf16_t, bf16_t>(s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q,
+                                                       duser + (size_t)t * d.Q);
+          break;
+        default:
+          enqueue_prefill_rows<int8_t, bf16_t, bf16_t>(s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q,
+                                                       duser + (size_t)t * d.Q);
+      }
+      t += n;
+    } else {
+      mk::Forced f{};
+      f.t[0] = text[t];
+      for (int k = 0; k < d.Q; ++k) f.t[1 + k] = agent[(size_t)t * d.Q + k];
+      enqueue_frame(s, conv, 1, true, duser + (size_t)t * d.Q, f, nullptr);
+      t += 1;
+    }
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
-  (void)hipFree(du);
+  (void)hipFree(dt);
   if (e != hipSuccess) return fail(s, MOSHI_EDEVICE, "prefill: %s", hipGetErrorString(e));
   s->h_offset[conv] += T;
   return MOSHI_OK;
@@ -1215,6 +1448,83 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
     }
   }
   if (rc == MOSHI_OK) chk(hipMemcpy(y, dy, (size_t)N * 4, hipMemcpyDeviceToHost));
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (stg) (void)hipFree(stg);
+  if (dw) (void)hipFree(dw);
+  if (ds) (void)hipFree(ds);
+  if (dx) (void)hipFree(dx);
+  if (dy) (void)hipFree(dy);
+  if (st) (void)hipStreamDestroy(st);
+  return rc;
+}
+
+moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, const float *W, const float *X,
+                              float *Y, int32_t iters, float *avg_us) {
+  if (M < 1 || N < 1 || K < 16 || K % 16 || !W || !X || !Y || band < 0 || band > 2) return MOSHI_EINVAL;
+  const size_t wcnt = (size_t)N * K, xcnt = (size_t)M * K;
+  const size_t welt = linear_elt(band), xelt = band == MOSHI_BAND_F32 ? 4 : 2;
+  if (wcnt * welt >= ((size_t)1 << 31) || xcnt * xelt >= ((size_t)1 << 31)) return MOSHI_EINVAL;
+  char *dw = nullptr, *dx = nullptr;
+  float *ds = nullptr, *dy = nullptr, *stg = nullptr;
+  hipStream_t st = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  moshi_status rc = MOSHI_OK;
+  auto chk = [&](hipError_t e) {
+    if (e != hipSuccess && rc == MOSHI_OK) {
+      fprintf(stderr, "moshi_debug_gemm: %s\n", hipGetErrorString(e));
+      rc = e == hipErrorOutOfMemory ? MOSHI_ENOMEM : MOSHI_EDEVICE;
+    }
+    return rc == MOSHI_OK;
+  };
+  if (chk(hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) && chk(hipMalloc(&dw, wcnt * welt)) &&
+      chk(hipMalloc(&ds, (size_t)N * 4)) && chk(hipMalloc(&dx, xcnt * xelt)) &&
+      chk(hipMalloc(&dy, (size_t)M * N * 4))) {
+    if (band == MOSHI_BAND_F32) {
+      chk(hipMemcpy(dw, W, wcnt * 4, hipMemcpyHostToDevice));
+      chk(hipMemcpy(dx, X, xcnt * 4, hipMemcpyHostToDevice));
+    } else {
+      std::vector<uint16_t> hx(xcnt);
+      for (size_t k = 0; k < xcnt; ++k) hx[k] = host_f2bf(X[k]);
+      chk(hipMemcpy(dx, hx.data(), xcnt * 2, hipMemcpyHostToDevice));
+      if (band == MOSHI_BAND_BF16) {
+        std::vector<uint16_t> hb(wcnt);
+        for (size_t k = 0; k < wcnt; ++k) hb[k] = host_f2bf(W[k]);
+        chk(hipMemcpy(dw, hb.data(), wcnt * 2, hipMemcpyHostToDevice));
+      } else if (chk(hipMalloc(&stg, wcnt * 4)) && chk(hipMemcpy(stg, W, wcnt * 4, hipMemcpyHostToDevice))) {
+        mk::k_quant_rows<<<(unsigned)N, mk::BLOCK, 0, st>>>(stg, K, reinterpret_cast<int8_t *>(dw), ds, 0);
+        chk(hipGetLastError());
+      }
+    }
+  }
+  auto launch = [&]() {
+    const dim3 grid((N + mk::GN - 1) / mk::GN, (M + mk::GM - 1) / mk::GM);
+    if (band == MOSHI_BAND_F32)
+      mk::k_gemm<float, false, MOSHI_N_STAGES><<<grid, mk::GBLOCK, 0, st>>>(
+          reinterpret_cast<const float *>(dw), nullptr, N, K, reinterpret_cast<const float *>(dx), K, M, dy, N);
+    else if (band == MOSHI_BAND_BF16)
+      mk::k_gemm<bf16_t, false, MOSHI_N_STAGES><<<grid, mk::GBLOCK, 0, st>>>(
+          reinterpret_cast<const bf16_t *>(dw), nullptr, N, K, reinterpret_cast<const bf16_t *>(dx), K, M, dy, N);
+    else
+      mk::k_gemm<int8_t, false, MOSHI_N_STAGES><<<grid, mk::GBLOCK, 0, st>>>(
+          reinterpret_cast<const int8_t *>(dw), ds, N, K, reinterpret_cast<const bf16_t *>(dx), K, M, dy, N);
+  };
+  if (rc == MOSHI_OK) {
+    launch();
+    chk(hipGetLastError());
+    chk(hipStreamSynchronize(st));
+  }
+  if (rc == MOSHI_OK && iters > 0 && avg_us) {
+    if (chk(hipEventCreate(&e0)) && chk(hipEventCreate(&e1)) && chk(hipEventRecord(e0, st))) {
+      for (int i = 0; i < iters; ++i) launch();
+      chk(hipEventRecord(e1, st));
+      chk(hipEventSynchronize(e1));
+      float ms = 0.f;
+      chk(hipEventElapsedTime(&ms, e0, e1));
+      *avg_us = ms * 1000.f / (float)iters;
+    }
+  }
+  if (rc == MOSHI_OK) chk(hipMemcpy(Y, dy, (size_t)M * N * 4, hipMemcpyDeviceToHost));
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
   if (stg) (void)hipFree(stg);

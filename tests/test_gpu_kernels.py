@@ -51,3 +51,45 @@ def test_gemv_moshi7b_shapes_sampled_rows(band, N, K):
     bytes_ = N * K * (2 if band == "bf16" else 1) + (N * 4 if band == "i8" else 0)
     print(f"gemv {band} {N}x{K}: {us:.1f} us, {bytes_ / us / 1e3:.0f} GB/s")
     assert err < 2e-6, err
+
+
+def rounded_x(band, X):
+    """The activations as the matrix-core path feeds them (bf16 for the bf16 and int8 bands)."""
+    if band == "f32":
+        return X.astype(np.float64)
+    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(X)).astype(np.float64)
+
+
+@pytest.mark.parametrize("band", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 37, 48), (5, 64, 352), (64, 96, 256), (70, 1000, 704),
+                                   (3, 130, 1040), (64, 2048, 1024)])
+def test_gemm_small_and_ragged(band, M, N, K):
+    W = synth.normal(3, f"g/W{N}x{K}", (N, K), 0.02)
+    X = synth.normal(3, f"g/X{M}x{K}", (M, K), 1.0)
+    Y, _ = rq.debug_gemm(band, W, X)
+    Ws, s = stored(band, W)
+    ref = rounded_x(band, X) @ Ws.T
+    if s is not None:
+        ref *= s[None, :]
+    err = np.max(np.abs(Y - ref)) / np.max(np.abs(ref))
+    assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("band", ["bf16", "i8"])
+@pytest.mark.parametrize("N,K", [(12288, 4096), (4096, 4096), (22528, 4096), (4096, 11264), (32000, 4096)])
+def test_gemm_moshi7b_shapes_batch64(band, N, K):
+    M = 64
+    W = synth.normal(4, f"g7/W{N}x{K}", (N, K), 0.02)
+    X = synth.normal(4, f"g7/X{K}", (M, K), 1.0)
+    Y, us = rq.debug_gemm(band, W, X, iters=10)
+    rows = np.unique(synth.uniform_int(4, f"g7/rows{N}", (128,), N))
+    rows = np.concatenate([[0, N - 1], rows])
+    Ws, s = stored(band, W[rows])
+    ref = rounded_x(band, X) @ Ws.T
+    if s is not None:
+        ref *= s[None, :]
+    err = np.max(np.abs(Y[:, rows] - ref)) / np.max(np.abs(ref))
+    bytes_ = N * K * (2 if band == "bf16" else 1) + (N * 4 if band == "i8" else 0)
+    print(f"gemm M=64 {band} {N}x{K}: {us:.1f} us, {bytes_ / us / 1e3:.0f} GB/s weights, "
+          f"{2 * M * N * K / us / 1e6:.1f} TFLOP/s")
+    assert err < 1e-5, err

@@ -41,6 +41,21 @@ def compare_step(tr, ref, st, out, has, frame):
         assert out[0].tolist() == ref["out"], frame
 
 
+def frame_agreement(tr, ref):
+    """Per-frame comparison for the low-precision bands: the cosine of every logits vector whose
+    conditioning agrees (the text head always; the head of codebook c only while the text token and
+    codebooks < c picked the oracle's tokens, since within a frame each depformer step feeds on the
+    previous step's own token), and the token matches."""
+    got = [tr["text_token"]] + tr["audio_tokens"]
+    want = [ref["text_token"]] + ref["audio_tokens"]
+    cos = [cosine(tr["text_logits"], ref["text_logits"])]
+    for c in range(len(want) - 1):
+        if got[: c + 1] != want[: c + 1]:
+            break
+        cos.append(cosine(tr["audio_logits"][c], ref["audio_logits"][c]))
+    return min(cos), sum(int(a == b) for a, b in zip(got, want))
+
+
 @pytest.mark.parametrize("exec_mode", ["graph", "stream", "persistent"])
 def test_tiny_free_running_matches_oracle(weights, oracle, exec_mode):
     users = synth.user_tokens(CFG, CFG.frames)
@@ -265,15 +280,56 @@ def test_low_precision_bands_on_the_tiny_model(weights, band, exec_mode):
         for f in range(8):
             ref = ref_lm.step(ost, users[f])
             s.step(users[f])
-            tr = s.read_trace(0)
-            cos_min = min(cos_min, cosine(tr["text_logits"], ref["text_logits"]),
-                          *[cosine(tr["audio_logits"][c], ref["audio_logits"][c]) for c in range(8)])
-            got = [tr["text_token"]] + tr["audio_tokens"]
-            want = [ref["text_token"]] + ref["audio_tokens"]
-            agree += sum(int(a == b) for a, b in zip(got, want))
-            total += 9
+            c, a = frame_agreement(s.read_trace(0), ref)
+            cos_min, agree, total = min(cos_min, c), agree + a, total + 9
             ref_lm.force_generated(ost, ref["text_token"], ref["audio_tokens"])
             s.force_generated(0, ref["text_token"], ref["audio_tokens"])
     print(f"{band}: min cosine {cos_min:.6f}, agreement {agree}/{total}")
     assert cos_min >= 0.999
     assert agree / total >= 0.99
+
+
+@pytest.mark.parametrize("band", ["bf16", "i8"])
+def test_batched_low_precision_bands_match_oracle(weights, band):
+    """Three conversations on the matrix-core path in the bf16 and int8 bands, each teacher-forced
+    onto its own oracle run (bf16-rounded weights; the int8 band against the int8-dequantised
+    oracle).  The batched path also rounds its projection inputs to bf16."""
+    B = 3
+    w16 = {k: (synth.f32_to_bf16_bits(v) if v.ndim == 2 else v) for k, v in weights.items()}
+    ref_lm = OracleLM(CFG, w16, band="i8sim" if band == "i8" else "f32")
+    users = np.stack([synth.user_tokens(CFG, 8, conv=b) for b in range(B)], axis=1)
+    osts = [ref_lm.new_state() for _ in range(B)]
+    agree, total, cos_min = 0, 0, 1.0
+    with rq.Session(CFG, band=band, batch=B) as s:
+        s.load_weights(w16)
+        for f in range(8):
+            s.step(users[f])
+            for b in range(B):
+                ref = ref_lm.step(osts[b], users[f, b])
+                c, a = frame_agreement(s.read_trace(b), ref)
+                cos_min, agree, total = min(cos_min, c), agree + a, total + 9
+                ref_lm.force_generated(osts[b], ref["text_token"], ref["audio_tokens"])
+                s.force_generated(b, ref["text_token"], ref["audio_tokens"])
+    print(f"batched {band}: min cosine {cos_min:.6f}, agreement {agree}/{total}")
+    assert cos_min >= 0.999
+    assert agree / total >= 0.99
+
+
+def test_prefill_row_batches_then_single_frames(weights, oracle):
+    """A prefill long enough to run row batches up to the context limit and then single frames
+    past it (window slide), against the oracle."""
+    T = 67
+    text, agent, user = synth.prefill_tokens(CFG, T, conv=1)
+    text %= CFG.text_card
+    ost = oracle.new_state()
+    oracle.prefill_forced(ost, text, agent, user)
+    users = synth.user_tokens(CFG, 4, conv=1, start_frame=T)
+    with rq.Session(CFG) as s:
+        s.load_weights(weights)
+        s.prefill_forced(0, text[:30], agent[:30], user[:30])
+        s.prefill_forced(0, text[30:], agent[30:], user[30:])
+        assert s.offset(0) == T
+        for f in range(4):
+            ref = oracle.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            compare_step(s.read_trace(0), ref, st, out, has, T + f)
