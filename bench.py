@@ -29,14 +29,13 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1) -> dict:
+def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1, kve: int = 4) -> dict:
     """Algorithmic HBM bytes of one launch of each stage: the weights it must stream once, the
     KV it must read (n_kv positions per conversation), and its activation vectors (read once,
     written once), for `rows` conversations."""
     D, F, Dd, Fd, Q = cfg.d_model, cfg.ffn_hidden, cfg.dep_d_model, cfg.dep_ffn_hidden, cfg.dep_q
     Vt, Va, L = cfg.text_card, cfg.audio_card, cfg.n_layers
     we = {"f32": 4, "bf16": 2, "i8": 1}[band]
-    kve = 4 if band == "f32" else 2
     sc = 4 if band == "i8" else 0  # per-row scales
 
     def lin(n, k):
@@ -45,7 +44,7 @@ def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1) -> dict:
     f = 4 * rows  # float32 activations, one row per conversation
     return {
         "embed": (2 * Q + 1) * D * (2 if band != "f32" else 4) * rows + 2 * D * f,
-        "qkv": lin(3 * D, D) + 2 * D * f + D * f + 2 * D * kve,
+        "qkv": lin(3 * D, D) + 2 * D * f + D * f + 2 * D * kve * rows,
         "attn": 2 * n_kv * D * kve * rows + 2 * D * f,
         "out_proj": lin(D, D) + D * f + 2 * D * f,
         "gate_in": lin(2 * F, D) + 2 * D * f + F * f,
@@ -61,10 +60,10 @@ def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1) -> dict:
     }
 
 
-def frame_bytes(weight_bytes: int, cfg, band: str, positions) -> float:
-    """Weights (streamed once per frame for all conversations) + the KV every conversation reads,
-    per frame, averaged over the frames: positions is [B][frames] (or [frames] at B = 1)."""
-    kve = 4 if band == "f32" else 2
+def frame_bytes(weight_bytes: int, cfg, kve: int, positions) -> float:
+    """Weights (streamed once per frame for all conversations) + the KV every conversation reads
+    (kve bytes per element), per frame, averaged over the frames: positions is [B][frames] (or
+    [frames] at B = 1)."""
     pos = np.atleast_2d(np.asarray(positions))
     n = np.minimum(pos + 1, cfg.context)
     return weight_bytes + float(np.mean(n.sum(axis=0))) * cfg.n_layers * 2 * cfg.d_model * kve
@@ -103,6 +102,7 @@ def main():
     ap.add_argument("--profile-frames", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--kv", default="f32", choices=["f32", "bf16"], help="KV cache storage")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -123,7 +123,9 @@ def main():
     nprof = args.profile_frames
     nframes = nprof + W + K
 
-    sess = rq.Session(cfg, exec=args.exec)
+    kv = args.kv
+    kve = 4 if kv == "f32" else 2
+    sess = rq.Session(cfg, exec=args.exec, kv=kv)
     t = time.time()
     sess.load_weights(weights)
     log(f"loaded weights in {time.time() - t:.1f}s")
@@ -156,7 +158,7 @@ def main():
         pos0 = starts
     else:
         pos0 = starts + nprof
-    sb = stage_bytes(cfg, band, n_kv=float(np.mean(np.minimum(pos0 + 1, cfg.context))), rows=B)
+    sb = stage_bytes(cfg, band, n_kv=float(np.mean(np.minimum(pos0 + 1, cfg.context))), rows=B, kve=kve)
     stages = {}
     for name, (n, us) in prof.items():
         if n:
@@ -184,7 +186,7 @@ def main():
     dt = time.perf_counter() - t0
     gpu_us, gpu_n = sess.gpu_time(0)
     fps = K / dt
-    fb = frame_bytes(lin_bytes, cfg, band, tpos)
+    fb = frame_bytes(lin_bytes, cfg, kve, tpos)
     log(f"{K} frames in {dt:.3f}s: {fps:.1f} frames/s ({B * fps:.1f} conversation-frames/s), "
         f"{fb / (dt / K) / 1e9:.0f} GB/s frame-level; GPU {gpu_us / gpu_n:.1f} us/frame")
     sess.close()
@@ -224,7 +226,7 @@ def main():
         "dtype": "bf16" if band == "bf16" else band, "data": "synthetic",
         "config": {"workload": f"{cfg.name}: Moshi-7B-shaped RQ-Transformer frame step, {K} {what}, "
                                f"seed-{cfg.seed} N(0,0.02) weights, uniform user tokens",
-                   "batch": B, "band": band, "accumulate": "f32", "exec": args.exec,
+                   "batch": B, "band": band, "kv": kv, "accumulate": "f32", "exec": args.exec,
                    "weight_bytes_per_frame": lin_bytes,
                    "prefill_positions": int(starts.sum()), "prefill_s": None if prefill_s is None else round(prefill_s, 3)},
         "tokens_per_s": round(9 * B * fps, 1),

@@ -42,12 +42,19 @@ typedef enum {
 
 /* Weight band: the storage type of every linear weight on the device. */
 typedef enum {
-  MOSHI_BAND_F32 = 0,  /* float32 linears, embeddings and KV cache ([LM] Band::F32, the parity band) */
-  MOSHI_BAND_BF16 = 1, /* bfloat16 linears, embeddings and KV cache, float32 arithmetic */
+  MOSHI_BAND_F32 = 0,  /* float32 linears and embeddings ([LM] Band::F32, the parity band) */
+  MOSHI_BAND_BF16 = 1, /* bfloat16 linears and embeddings, float32 arithmetic */
   MOSHI_BAND_I8 = 2    /* int8 linears with one float32 scale per output row ([LM] Band::I8);
-                          embeddings and KV cache bfloat16.  Quantised at load, see
-                          moshi_load_weights. */
+                          embeddings bfloat16.  Quantised at load, see moshi_load_weights. */
 } moshi_band;
+
+/* Storage type of the temporal KV cache. */
+typedef enum {
+  MOSHI_KV_F32 = 0,  /* float32 (the default, every band): no storage loss, so long contexts keep
+                        the greedy tokens of the float32 definition */
+  MOSHI_KV_BF16 = 1  /* bfloat16 (bf16 and int8 bands only): half the KV bytes, at a storage loss
+                        that grows with the context length */
+} moshi_kv;
 
 typedef enum { MOSHI_DTYPE_F32 = 0, MOSHI_DTYPE_BF16 = 1 } moshi_dtype;
 
@@ -76,9 +83,11 @@ typedef enum {
  *                            `context` positions, absolute rope positions); when smaller, a step
  *                            at offset >= kv_capacity returns MOSHI_ERANGE.
  *   exec                   : a moshi_exec value.
+ *   kv_dtype               : a moshi_kv value (0 = float32).
  * Constraints (else MOSHI_EINVAL): d_model % n_heads == 0 with head_dim 64 or 128;
  * dep_d_model % dep_heads == 0; 1 <= dep_q <= 16 (Moshi uses 8); d_model, ffn_hidden,
- * dep_d_model and dep_ffn_hidden multiples of 16 and at most 16384; batch >= 1.
+ * dep_d_model and dep_ffn_hidden multiples of 16 and at most 16384; batch >= 1; kv_dtype
+ * MOSHI_KV_BF16 only with the bf16 and int8 bands.
  */
 typedef struct moshi_config {
   int32_t n_layers, d_model, n_heads, ffn_hidden, context;
@@ -86,6 +95,7 @@ typedef struct moshi_config {
   int32_t dep_layers, dep_d_model, dep_heads, dep_ffn_hidden, dep_q;
   float rope_theta, rms_eps;
   int32_t band, batch, kv_capacity, exec;
+  int32_t kv_dtype;
 } moshi_config;
 
 /*

@@ -18,6 +18,7 @@ MOSHI_OK, MOSHI_NONE = 0, 1
 MOSHI_EINVAL, MOSHI_ESTATE, MOSHI_ESHAPE, MOSHI_ENOMEM, MOSHI_EDEVICE, MOSHI_ERANGE = -1, -2, -3, -4, -5, -6
 BANDS = {"f32": 0, "bf16": 1, "i8": 2}
 EXEC = {"graph": 0, "stream": 1, "persistent": 2}
+KV = {"f32": 0, "bf16": 1}
 DTYPE_F32, DTYPE_BF16 = 0, 1
 
 # every function the header declares, with (restype, argtypes)
@@ -77,7 +78,7 @@ class _Config(ctypes.Structure):
                                                "text_card", "audio_card", "dep_layers", "dep_d_model",
                                                "dep_heads", "dep_ffn_hidden", "dep_q")] + [
         ("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
-        (n, ctypes.c_int32) for n in ("band", "batch", "kv_capacity", "exec")]
+        (n, ctypes.c_int32) for n in ("band", "batch", "kv_capacity", "exec", "kv_dtype")]
 
 
 class _Tensor(ctypes.Structure):
@@ -101,11 +102,12 @@ def _ptr(a: np.ndarray) -> int:
 
 class Session:
     """A moshi_state.  `shape` is any object with the moshi_config field names as attributes
-    (n_layers, d_model, ...); band is 'f32', 'bf16' or 'i8'; exec is 'graph' or 'stream';
-    `stream` is an optional hipStream_t handle (int) to run on."""
+    (n_layers, d_model, ...); band is 'f32', 'bf16' or 'i8'; kv is the KV cache storage, 'f32'
+    (default) or 'bf16' (bf16 and i8 bands); exec is 'graph', 'stream' or 'persistent'; `stream`
+    is an optional hipStream_t handle (int) to run on."""
 
     def __init__(self, shape, band: str | None = None, batch: int | None = None, kv_capacity: int = 0,
-                 exec: str = "graph", stream: int | None = None):
+                 exec: str = "graph", stream: int | None = None, kv: str | None = None):
         self.lib = load_library()
         c = _Config()
         for f in _SHAPE_FIELDS:
@@ -114,6 +116,7 @@ class Session:
         c.batch = batch if batch is not None else getattr(shape, "batch", 1)
         c.kv_capacity = kv_capacity
         c.exec = EXEC[exec]
+        c.kv_dtype = KV[kv or getattr(shape, "kv", "f32")]
         self.cfg = c
         self.B, self.Q = c.batch, c.dep_q
         self.NS = 2 * c.dep_q + 1

@@ -23,7 +23,7 @@ struct RowMap {
   }
 };
 
-// X[m] = rms_norm(src[m]; alpha) (or src[m] when alpha is null), rounded to XT; with `copy` set
+// X[m] = rms_norm(src[m]; alpha) (or src[m] when alpha is null) in the XPut layout; with `copy` set
 // the float32 result also goes to copy[m] (the post-out_norm hidden).  Dynamic LDS: K floats.
 template <typename XT>
 __global__ __launch_bounds__(BLOCK) void k_rows_cvt(const float *__restrict__ src, int lds,
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(BLOCK) void k_rows_cvt(const float *__restrict__ sr
   else
     stage_vec(src + (size_t)m * lds, K, xs);
   for (int k = threadIdx.x; k < K; k += BLOCK) {
-    X[(size_t)m * ldx + k] = from_f<XT>(xs[k]);
+    XPut<XT>::put(X + (size_t)m * ldx, K, k, xs[k]);
     if (copy) copy[(size_t)m * ldc + k] = xs[k];
   }
 }
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(BLOCK) void k_qkv_post(Dims d, Bufs s, KV<KT> kv, c
 }
 
 // a5 between the two gated-unit products: X[m][j] = silu(Y[m][2j]) * Y[m][2j + 1] (the device
-// copy of linear_in has gate row j and mult row j interleaved), rounded to XT.  Grid
+// copy of linear_in has gate row j and mult row j interleaved), in the XPut layout.  Grid
 // (rows, ceil(F / BLOCK)).
 template <typename XT>
 __global__ __launch_bounds__(BLOCK) void k_gate_post(const float *__restrict__ Y, int ldy, int F, XT *__restrict__ X,
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(BLOCK) void k_gate_post(const float *__restrict__ Y
   const int j = blockIdx.y * BLOCK + threadIdx.x;
   if (j >= F) return;
   const float2 gm = *reinterpret_cast<const float2 *>(Y + (size_t)m * ldy + 2 * j);
-  X[(size_t)m * ldx + j] = from_f<XT>(silu(gm.x) * gm.y);
+  XPut<XT>::put(X + (size_t)m * ldx, F, j, silu(gm.x) * gm.y);
 }
 
 // a7 / a8 greedy head: the first-wins argmax of logits row m (N values), stored as the single
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(BLOCK) void k_argmax_rows(const float *__restrict__
 }
 
 // a8 entry of depformer step cb for conversation b0 + m: prev = the previous head's token,
-// y = depformer_in[cb] . hidden + table[prev], X[m] = rms_norm(y; norm1 of layer 0) as XT.
+// y = depformer_in[cb] . hidden + table[prev], X[m] = rms_norm(y; norm1 of layer 0) (XPut layout).
 // Dynamic LDS: Dd floats.
 template <typename ET, typename XT>
 __global__ __launch_bounds__(BLOCK) void k_dep_entry(Dims d, Bufs s, const ET *__restrict__ table, int cb,
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_entry(Dims d, Bufs s, const ET *_
   }
   __syncthreads();
   rms_in_place(xs, norm, Dd, d.eps, red);
-  for (int k = threadIdx.x; k < Dd; k += BLOCK) X[(size_t)m * ldx + k] = from_f<XT>(xs[k]);
+  for (int k = threadIdx.x; k < Dd; k += BLOCK) XPut<XT>::put(X + (size_t)m * ldx, Dd, k, xs[k]);
 }
 
 // a8 after the depformer q|k|v product Y[m] (3 Dd columns, no rope): q to dq, k and v to the
@@ -162,7 +162,8 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv_post(Dims d, Bufs s, const fl
 }
 
 // a8 depformer attention of conversation b0 + m: dq over the cb + 1 cache entries of `layer`
-// ([LM] attend; weights e_p / den), 16 lanes per head, EPL dims per lane; o goes to X[m] as XT.
+// ([LM] attend; weights e_p / den), 16 lanes per head, EPL dims per lane; o goes to X[m] (XPut
+// layout).
 template <typename XT, int EPL>
 __global__ __launch_bounds__(BLOCK) void k_dep_attn(Dims d, Bufs s, int layer, int cb, XT *__restrict__ X, int ldx,
                                                     int b0) {
@@ -222,7 +223,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_attn(Dims d, Bufs s, int layer, i
         for (int i = 0; i < EPL; ++i) o[i] = fmaf(wgt, vv[p][i], o[i]);
       }
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) X[(size_t)m * ldx + e0 + i] = from_f<XT>(o[i]);
+    for (int i = 0; i < EPL; ++i) XPut<XT>::put(X + (size_t)m * ldx, Dd, e0 + i, o[i]);
   }
 }
 

@@ -4,9 +4,9 @@
 // one row at a time ([LM] temporal_step / depformer_cycle linears); with M conversations (or M
 // prefill positions) the weights are streamed once for all of them.
 //
-// Operands: bf16 and int8 weights multiply a bf16 copy of the activations (v_mfma_f32_32x32x16_bf16,
-// fp32 accumulation; int8 values convert to bf16 exactly); f32 weights multiply f32 activations
-// (v_mfma_f32_32x32x2_f32).
+// Operands: bf16 and int8 weights multiply the activations split into bf16 hi and lo parts
+// (v_mfma_f32_32x32x16_bf16 twice, fp32 accumulation; int8 values convert to bf16 exactly); f32
+// weights multiply f32 activations (v_mfma_f32_32x32x2_f32).
 //
 // Tiling: a block owns 32 weight rows and 64 activation rows; its 4 waves split K and their
 // accumulators are summed in LDS in wave order.  Per 64-wide K block, lane l (n = l % 32,
@@ -32,6 +32,25 @@ constexpr int GBLOCK = GWAVES * WAVE;
 // Activation element type paired with a weight type.
 template <typename WT> struct GemmX { typedef bf16_t type; };
 template <> struct GemmX<float> { typedef float type; };
+
+// A projection input row holds K values.  With bf16 operands each value v is stored as the pair
+// hi = bf16(v), lo = bf16(v - hi) (row = [hi of K columns | lo of K columns], so the row stride is
+// at least 2 K): the products hi . w + lo . w carry v to about 16 significant bits, and the
+// matrix-core result matches float32 activations far below the bf16 weights' own rounding.
+// float32 operands store v once.
+template <typename XT> struct XPut;
+template <> struct XPut<float> {
+  static constexpr int PLANES = 1;
+  __device__ __forceinline__ static void put(float *row, int K, int k, float v) { row[k] = v; }
+};
+template <> struct XPut<bf16_t> {
+  static constexpr int PLANES = 2;
+  __device__ __forceinline__ static void put(bf16_t *row, int K, int k, float v) {
+    const bf16_t hi = f2bf(v);
+    row[k] = hi;
+    row[K + k] = f2bf(v - bf2f(hi));
+  }
+};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
@@ -62,22 +81,29 @@ struct GemmCore;
 
 template <>
 struct GemmCore<bf16_t> {
-  // w: 32 bf16 of weight row n (4 x 16 B); x0, x1: 32 bf16 of activation rows m, m + 32
-  uint4 w[4], x0[4], x1[4];
+  // w: 32 bf16 of weight row n (4 x 16 B); x0, x1: 32 bf16 (hi) of activation rows m, m + 32;
+  // l0, l1: their lo parts (xlo bytes further on)
+  uint4 w[4], x0[4], x1[4], l0[4], l1[4];
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx, int woff, int xoff0,
-                                       int xoff1, int kleft) {
+                                       int xoff1, int kleft, int xlo) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) w[s] = buf_ld16(rw, (woff < 0 || 8 * s >= kleft) ? BUF_OOB : woff + 16 * s);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x0[s] = buf_ld16(rx, (xoff0 < 0 || 8 * s >= kleft) ? BUF_OOB : xoff0 + 16 * s);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x1[s] = buf_ld16(rx, (xoff1 < 0 || 8 * s >= kleft) ? BUF_OOB : xoff1 + 16 * s);
+    for (int s = 0; s < 4; ++s) {
+      const bool ok0 = xoff0 >= 0 && 8 * s < kleft, ok1 = xoff1 >= 0 && 8 * s < kleft;
+      x0[s] = buf_ld16(rx, ok0 ? xoff0 + 16 * s : BUF_OOB);
+      l0[s] = buf_ld16(rx, ok0 ? xoff0 + xlo + 16 * s : BUF_OOB);
+      x1[s] = buf_ld16(rx, ok1 ? xoff1 + 16 * s : BUF_OOB);
+      l1[s] = buf_ld16(rx, ok1 ? xoff1 + xlo + 16 * s : BUF_OOB);
+    }
   }
   __device__ __forceinline__ void mma(f32x16 &c0, f32x16 &c1) const {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x0[s]), as_bf16x8(w[s]), c0, 0, 0, 0);
       c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x1[s]), as_bf16x8(w[s]), c1, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(l0[s]), as_bf16x8(w[s]), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(l1[s]), as_bf16x8(w[s]), c1, 0, 0, 0);
     }
   }
   static constexpr int WELT = 2;
@@ -85,15 +111,19 @@ struct GemmCore<bf16_t> {
 
 template <>
 struct GemmCore<int8_t> {
-  uint4 wq[2], x0[4], x1[4];  // 32 int8 weights
+  uint4 wq[2], x0[4], x1[4], l0[4], l1[4];  // 32 int8 weights; activations as for bf16
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx, int woff, int xoff0,
-                                       int xoff1, int kleft) {
+                                       int xoff1, int kleft, int xlo) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) wq[s] = buf_ld16(rw, (woff < 0 || 16 * s >= kleft) ? BUF_OOB : woff + 16 * s);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x0[s] = buf_ld16(rx, (xoff0 < 0 || 8 * s >= kleft) ? BUF_OOB : xoff0 + 16 * s);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x1[s] = buf_ld16(rx, (xoff1 < 0 || 8 * s >= kleft) ? BUF_OOB : xoff1 + 16 * s);
+    for (int s = 0; s < 4; ++s) {
+      const bool ok0 = xoff0 >= 0 && 8 * s < kleft, ok1 = xoff1 >= 0 && 8 * s < kleft;
+      x0[s] = buf_ld16(rx, ok0 ? xoff0 + 16 * s : BUF_OOB);
+      l0[s] = buf_ld16(rx, ok0 ? xoff0 + xlo + 16 * s : BUF_OOB);
+      x1[s] = buf_ld16(rx, ok1 ? xoff1 + 16 * s : BUF_OOB);
+      l1[s] = buf_ld16(rx, ok1 ? xoff1 + xlo + 16 * s : BUF_OOB);
+    }
   }
   __device__ __forceinline__ void mma(f32x16 &c0, f32x16 &c1) const {
 #pragma unroll
@@ -102,6 +132,8 @@ struct GemmCore<int8_t> {
       const uint4 wb = (s & 1) ? i8_to_bf16x8(q.z, q.w) : i8_to_bf16x8(q.x, q.y);
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x0[s]), as_bf16x8(wb), c0, 0, 0, 0);
       c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(x1[s]), as_bf16x8(wb), c1, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(l0[s]), as_bf16x8(wb), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(l1[s]), as_bf16x8(wb), c1, 0, 0, 0);
     }
   }
   static constexpr int WELT = 1;
@@ -111,7 +143,7 @@ template <>
 struct GemmCore<float> {
   uint4 w[8], x0[8], x1[8];  // 32 floats each
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx, int woff, int xoff0,
-                                       int xoff1, int kleft) {
+                                       int xoff1, int kleft, int) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) w[s] = buf_ld16(rw, (woff < 0 || 4 * s >= kleft) ? BUF_OOB : woff + 16 * s);
 #pragma unroll
@@ -136,8 +168,9 @@ struct GemmCore<float> {
 };
 
 // Y[m][n] (ADD: +=) sum_k X[m][k] W[n][k] (* wscale[n]) for m < M, n < N.  Grid (ceil(N / 32),
-// ceil(M / 64)), GBLOCK threads.  X: [M][ldx] elements of GemmX<WT>::type; Y: [M][ldy] floats.
-// The byte sizes of W and of X must stay below 2^31.
+// ceil(M / 64)), GBLOCK threads.  X: [M][ldx] elements of GemmX<WT>::type in the XPut layout
+// (bf16: hi and lo planes of K columns each); Y: [M][ldy] floats.  The byte sizes of W and of X
+// must stay below 2^31.
 template <typename WT, bool ADD, int TAG>
 __global__ __launch_bounds__(GBLOCK) void k_gemm(const WT *__restrict__ W, const float *__restrict__ wscale, int N,
                                                  int K, const typename GemmX<WT>::type *__restrict__ X, int ldx,
@@ -165,7 +198,7 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm(const WT *__restrict__ W, const
     const int wo = (kin && n < N) ? (int)(((size_t)n * K + k) * WE) : -1;
     const int xa = (kin && ma < M) ? (int)(((size_t)ma * ldx + k) * XE) : -1;
     const int xb = (kin && mb < M) ? (int)(((size_t)mb * ldx + k) * XE) : -1;
-    c.load(rw, rx, wo, xa, xb, K - k);
+    c.load(rw, rx, wo, xa, xb, K - k, K * XE);
   };
   // Both buffers are refilled unconditionally (past kb1 with out-of-range loads that read zero
   // and move no data), so no load sits under a branch and the waits stay per buffer.

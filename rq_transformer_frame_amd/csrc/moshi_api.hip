@@ -151,6 +151,27 @@ moshi_status fail(moshi_state *s, moshi_status code, const char *fmt, ...) {
 size_t linear_elt(int band) { return band == MOSHI_BAND_F32 ? 4 : band == MOSHI_BAND_BF16 ? 2 : 1; }
 size_t embed_elt(int band) { return band == MOSHI_BAND_F32 ? 4 : 2; }
 
+// The storage types of a session: weights, embedding tables, KV cache.
+template <typename W, typename E, typename K>
+struct Types {
+  typedef W WT;
+  typedef E ET;
+  typedef K KT;
+};
+
+template <typename F>
+void with_types(const moshi_config &c, F &&f) {
+  const bool kvb = c.kv_dtype == MOSHI_KV_BF16;
+  switch (c.band) {
+    case MOSHI_BAND_F32:
+      return f(Types<float, float, float>{});
+    case MOSHI_BAND_BF16:
+      return kvb ? f(Types<bf16_t, bf16_t, bf16_t>{}) : f(Types<bf16_t, bf16_t, float>{});
+    default:
+      return kvb ? f(Types<int8_t, bf16_t, bf16_t>{}) : f(Types<int8_t, bf16_t, float>{});
+  }
+}
+
 // Lay out every checkpoint tensor in one arena.  Groups that a kernel indexes as one array are
 // contiguous: the 2Q audio tables, the Q depformer_in matrices (and their scales), the Q-1
 // depformer audio tables.
@@ -273,7 +294,7 @@ void plan_weights(moshi_state *s) {
 moshi_status alloc_session(moshi_state *s) {
   const mk::Dims &d = s->d;
   const size_t B = d.B;
-  const size_t kvelt = s->cfg.band == MOSHI_BAND_F32 ? 4 : 2;
+  const size_t kvelt = s->cfg.kv_dtype == MOSHI_KV_BF16 ? 2 : 4;
   size_t off = 0;
   struct Req {
     void **dst;
@@ -314,7 +335,7 @@ moshi_status alloc_session(moshi_state *s) {
   req((void **)&s->d_dl, (size_t)d.Ld * d.Q * sizeof(mk::LayerPtrs));
   {
     const size_t rows = std::max<size_t>(B > 1 ? B : 0, PF_ROWS);
-    const size_t xelt = s->cfg.band == MOSHI_BAND_F32 ? 4 : 2;
+    const size_t xelt = s->cfg.band == MOSHI_BAND_F32 ? 4 : 2 * 2;  // bf16 hi and lo planes
     const size_t kmax = std::max({(size_t)d.D, (size_t)d.F, (size_t)d.Dd, (size_t)d.Fd});
     const size_t nmax = std::max({(size_t)3 * d.D, (size_t)2 * d.F, (size_t)3 * d.Dd, (size_t)2 * d.Fd});
     s->grows = (int)rows;
@@ -405,25 +426,26 @@ int64_t block_rows(int64_t units, int P, int blocks) {
 // loads per thread for inputs of width D, F, Dd, Fd).  The staging counts only set how many loads
 // each thread issues per pass, so a shape without its own variant runs the generic one.
 struct PVariant {
-  int band, hd, depl, ud, uf, udd, ufd;
+  int band, kv, hd, depl, ud, uf, udd, ufd;
   const void *fn;
 };
 
 template <typename WT, typename ET, typename KT, int HD, int DEPL, int UD, int UF, int UDd, int UFd>
 PVariant pvariant(int band) {
-  return PVariant{band, HD, DEPL, UD, UF, UDd, UFd,
+  return PVariant{band, std::is_same<KT, float>::value ? MOSHI_KV_F32 : MOSHI_KV_BF16, HD, DEPL, UD, UF, UDd, UFd,
                   reinterpret_cast<const void *>(&mk::k_frame_persistent<WT, ET, KT, HD, DEPL, UD, UF, UDd, UFd>)};
 }
 
 const PVariant *persistent_variants(int *n) {
   static const PVariant v[] = {
       // Moshi-7B shape (d4096 / ffn 11264, depformer d1024 / ffn 2816)
+      pvariant<bf16_t, bf16_t, float, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_BF16),
       pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_BF16),
-      pvariant<int8_t, bf16_t, bf16_t, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_I8),
+      pvariant<int8_t, bf16_t, float, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_I8),
       // small shapes, one pass per 2048-wide input
       pvariant<float, float, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_F32),
-      pvariant<bf16_t, bf16_t, bf16_t, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_BF16),
-      pvariant<int8_t, bf16_t, bf16_t, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
+      pvariant<bf16_t, bf16_t, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_BF16),
+      pvariant<int8_t, bf16_t, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
   };
   *n = (int)(sizeof(v) / sizeof(v[0]));
   return v;
@@ -440,7 +462,7 @@ const void *select_persistent(const moshi_config &c, size_t *lds) {
   const PVariant *v = persistent_variants(&n);
   const PVariant *pick = nullptr;
   for (int i = 0; i < n; ++i) {
-    if (v[i].band != c.band || v[i].hd != hd || v[i].depl * 16 != hdd) continue;
+    if (v[i].band != c.band || v[i].kv != c.kv_dtype || v[i].hd != hd || v[i].depl * 16 != hdd) continue;
     if (v[i].ud == ud && v[i].uf == uf && v[i].udd == udd && v[i].ufd == ufd) {
       pick = &v[i];
       break;
@@ -601,6 +623,7 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
   auto W = [&](int slot) { return reinterpret_cast<const WT *>(s->data(slot)); };
   auto N = [&](int slot) { return reinterpret_cast<const float *>(s->data(slot)); };
   XT *X = reinterpret_cast<XT *>(s->gx);
+  const int P = XPut<XT>::PLANES;  // activation planes per row (bf16: hi, lo)
   float *Y = s->gy;
   const dim3 gm_rows(1, (rows + GM - 1) / GM);
   auto gemm_grid = [&](int n) { return dim3((n + GN - 1) / GN, gm_rows.y); };
@@ -608,9 +631,9 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
   for (int l = 0; l < d.L; ++l) {
     const LayerW &lw = s->layers[l];
     run(MOSHI_STAGE_QKV, [&] {
-      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm1), d.eps, d.D, X, d.D, nullptr, 0);
+      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm1), d.eps, d.D, X, P * d.D, nullptr, 0);
       k_gemm<WT, false, MOSHI_STAGE_QKV><<<gemm_grid(3 * d.D), GBLOCK, 0, st>>>(W(lw.in), s->scale(lw.in), 3 * d.D,
-                                                                               d.D, X, d.D, rows, Y, 3 * d.D);
+                                                                               d.D, X, P * d.D, rows, Y, 3 * d.D);
       k_qkv_post<KT><<<rows, BLOCK, 0, st>>>(d, b, kv, Y, 3 * d.D, q_rows, l, rm);
     });
     run(MOSHI_STAGE_ATTN, [&] {
@@ -622,19 +645,19 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
         k_attn<KT, 64><<<dim3(d.H, attn_splits, rows), BLOCK, chunk * 4, st>>>(d, b, kv, l, rm.b0, aq);
     });
     run(MOSHI_STAGE_OUT_PROJ, [&] {
-      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(o_rows, d.D, nullptr, d.eps, d.D, X, d.D, nullptr, 0);
+      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(o_rows, d.D, nullptr, d.eps, d.D, X, P * d.D, nullptr, 0);
       k_gemm<WT, true, MOSHI_STAGE_OUT_PROJ><<<gemm_grid(d.D), GBLOCK, 0, st>>>(W(lw.out), s->scale(lw.out), d.D, d.D,
-                                                                              X, d.D, rows, x, d.D);
+                                                                              X, P * d.D, rows, x, d.D);
     });
     run(MOSHI_STAGE_GATE_IN, [&] {
-      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm2), d.eps, d.D, X, d.D, nullptr, 0);
+      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm2), d.eps, d.D, X, P * d.D, nullptr, 0);
       k_gemm<WT, false, MOSHI_STAGE_GATE_IN><<<gemm_grid(2 * d.F), GBLOCK, 0, st>>>(
-          W(lw.gin), s->scale(lw.gin), 2 * d.F, d.D, X, d.D, rows, Y, 2 * d.F);
-      k_gate_post<XT><<<dim3(rows, (d.F + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.F, d.F, X, d.F);
+          W(lw.gin), s->scale(lw.gin), 2 * d.F, d.D, X, P * d.D, rows, Y, 2 * d.F);
+      k_gate_post<XT><<<dim3(rows, (d.F + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.F, d.F, X, P * d.F);
     });
     run(MOSHI_STAGE_GATE_OUT, [&] {
       k_gemm<WT, true, MOSHI_STAGE_GATE_OUT><<<gemm_grid(d.D), GBLOCK, 0, st>>>(W(lw.gout), s->scale(lw.gout), d.D,
-                                                                              d.F, X, d.F, rows, x, d.D);
+                                                                              d.F, X, P * d.F, rows, x, d.D);
     });
   }
 }
@@ -663,6 +686,7 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
     }
   };
   XT *X = reinterpret_cast<XT *>(s->gx);
+  const int P = XPut<XT>::PLANES;  // activation planes per row (bf16: hi, lo)
   float *Y = s->gy;
   const int rows = nb;
   auto gemm_grid = [&](int n) { return dim3((n + GN - 1) / GN, (rows + GM - 1) / GM); };
@@ -677,16 +701,16 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
                                 run);
   const int AM = AM_MAX_BLOCKS;
   run(MOSHI_STAGE_TEXT_HEAD, [&] {
-    k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(s->out_norm), d.eps, d.D, X, d.D,
+    k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(s->out_norm), d.eps, d.D, X, P * d.D,
                                                   b.hidden + (size_t)b0 * d.D, d.D);
     k_gemm<WT, false, MOSHI_STAGE_TEXT_HEAD><<<gemm_grid(d.Vt), GBLOCK, 0, st>>>(
-        W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, X, d.D, rows, b.text_logits + (size_t)b0 * d.Vt, d.Vt);
+        W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, X, P * d.D, rows, b.text_logits + (size_t)b0 * d.Vt, d.Vt);
     k_argmax_rows<<<rows, BLOCK, 0, st>>>(b.text_logits + (size_t)b0 * d.Vt, d.Vt, d.Vt,
                                           b.am_part + (size_t)b0 * (1 + d.Q) * AM, (1 + d.Q) * AM);
   });
   run(MOSHI_STAGE_DEP_IN, [&] {
     k_gemm<WT, false, MOSHI_STAGE_DEP_IN><<<gemm_grid(d.Q * d.Dd), GBLOCK, 0, st>>>(
-        W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, X, d.D, rows, b.din + (size_t)b0 * d.Q * d.Dd, d.Q * d.Dd);
+        W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, X, P * d.D, rows, b.din + (size_t)b0 * d.Q * d.Dd, d.Q * d.Dd);
   });
   float *y = b.y + (size_t)b0 * d.Dd;
   for (int cb = 0; cb < d.Q; ++cb) {
@@ -695,36 +719,36 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
       const LayerW &lw = s->dlayers[j][cb];
       run(MOSHI_STAGE_DEP_QKV, [&] {
         if (j == 0)
-          k_dep_entry<ET, XT><<<rows, BLOCK, d.Dd * f4, st>>>(d, b, table, cb, N(lw.norm1), X, d.Dd, b0);
+          k_dep_entry<ET, XT><<<rows, BLOCK, d.Dd * f4, st>>>(d, b, table, cb, N(lw.norm1), X, P * d.Dd, b0);
         else
-          k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm1), d.eps, d.Dd, X, d.Dd, nullptr, 0);
+          k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm1), d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
         k_gemm<WT, false, MOSHI_STAGE_DEP_QKV><<<gemm_grid(3 * d.Dd), GBLOCK, 0, st>>>(
-            W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X, d.Dd, rows, Y, 3 * d.Dd);
+            W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X, P * d.Dd, rows, Y, 3 * d.Dd);
         k_dep_qkv_post<<<rows, BLOCK, 0, st>>>(d, b, Y, 3 * d.Dd, j, cb, b0);
       });
       run(MOSHI_STAGE_DEP_OUT, [&] {
         with_epl(d.hdd, [&](auto e) {
-          k_dep_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, j, cb, X, d.Dd, b0);
+          k_dep_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, j, cb, X, P * d.Dd, b0);
         });
         k_gemm<WT, true, MOSHI_STAGE_DEP_OUT><<<gemm_grid(d.Dd), GBLOCK, 0, st>>>(W(lw.out), s->scale(lw.out), d.Dd,
-                                                                                d.Dd, X, d.Dd, rows, y, d.Dd);
+                                                                                d.Dd, X, P * d.Dd, rows, y, d.Dd);
       });
       run(MOSHI_STAGE_DEP_GATE_IN, [&] {
-        k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm2), d.eps, d.Dd, X, d.Dd, nullptr, 0);
+        k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm2), d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
         k_gemm<WT, false, MOSHI_STAGE_DEP_GATE_IN><<<gemm_grid(2 * d.Fd), GBLOCK, 0, st>>>(
-            W(lw.gin), s->scale(lw.gin), 2 * d.Fd, d.Dd, X, d.Dd, rows, Y, 2 * d.Fd);
-        k_gate_post<XT><<<dim3(rows, (d.Fd + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.Fd, d.Fd, X, d.Fd);
+            W(lw.gin), s->scale(lw.gin), 2 * d.Fd, d.Dd, X, P * d.Dd, rows, Y, 2 * d.Fd);
+        k_gate_post<XT><<<dim3(rows, (d.Fd + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.Fd, d.Fd, X, P * d.Fd);
       });
       run(MOSHI_STAGE_DEP_GATE_OUT, [&] {
         k_gemm<WT, true, MOSHI_STAGE_DEP_GATE_OUT><<<gemm_grid(d.Dd), GBLOCK, 0, st>>>(
-            W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, X, d.Fd, rows, y, d.Dd);
+            W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, X, P * d.Fd, rows, y, d.Dd);
       });
     }
     run(MOSHI_STAGE_DEP_HEAD, [&] {
-      k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, nullptr, d.eps, d.Dd, X, d.Dd, nullptr, 0);
+      k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, nullptr, d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
       float *lg = b.audio_logits + (size_t)b0 * d.Q * d.Va + (size_t)cb * d.Va;
       k_gemm<WT, false, MOSHI_STAGE_DEP_HEAD><<<gemm_grid(d.Va), GBLOCK, 0, st>>>(
-          W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, X, d.Dd, rows, lg, d.Q * d.Va);
+          W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, X, P * d.Dd, rows, lg, d.Q * d.Va);
       k_argmax_rows<<<rows, BLOCK, 0, st>>>(lg, d.Q * d.Va, d.Va, b.am_part + ((size_t)b0 * (1 + d.Q) + 1 + cb) * AM,
                                             (1 + d.Q) * AM);
     });
@@ -751,30 +775,14 @@ void enqueue_prefill_rows(moshi_state *s, int conv, int T, int64_t pos0, const i
 
 void enqueue_frame(moshi_state *s, int b0, int nb, bool temporal_only, const int32_t *user_dev,
                    const mk::Forced &forced, Prof *prof = nullptr) {
-  if (nb >= 2 && !temporal_only) {  // several conversations: projections on the matrix cores
-    switch (s->cfg.band) {
-      case MOSHI_BAND_F32:
-        enqueue_frame_rows<float, float, float>(s, b0, nb, user_dev, prof);
-        break;
-      case MOSHI_BAND_BF16:
-        enqueue_frame_rows<bf16_t, bf16_t, bf16_t>(s, b0, nb, user_dev, prof);
-        break;
-      default:
-        enqueue_frame_rows<int8_t, bf16_t, bf16_t>(s, b0, nb, user_dev, prof);
-    }
-    return;
-  }
-  switch (s->cfg.band) {
-    case MOSHI_BAND_F32:
-      enqueue_frame_t<float, float, float>(s, b0, nb, temporal_only, user_dev, forced, prof);
-      break;
-    case MOSHI_BAND_BF16:
-      enqueue_frame_t<bf16_t, bf16_t, bf16_t>(s, b0, nb, temporal_only, user_dev, forced, prof);
-      break;
-    default:
-      enqueue_frame_t<int8_t, bf16_t, bf16_t>(s, b0, nb, temporal_only, user_dev, forced, prof);
-      break;
-  }
+  with_types(s->cfg, [&](auto t) {
+    typedef decltype(t) T;
+    if (nb >= 2 && !temporal_only)  // several conversations: projections on the matrix cores
+      enqueue_frame_rows<typename T::WT, typename T::ET, typename T::KT>(s, b0, nb, user_dev, prof);
+    else
+      enqueue_frame_t<typename T::WT, typename T::ET, typename T::KT>(s, b0, nb, temporal_only, user_dev, forced,
+                                                                       prof);
+  });
 }
 
 // Fill the persistent kernel's argument block in device memory (once per session).
@@ -857,6 +865,8 @@ moshi_status check_config(const moshi_config *c, std::string &why) {
   if (c->batch < 1) return bad("batch must be >= 1");
   if (c->kv_capacity < 0 || c->kv_capacity > c->context) return bad("kv_capacity must be in [0, context]");
   if (c->exec < MOSHI_EXEC_GRAPH || c->exec > MOSHI_EXEC_PERSISTENT) return bad("unknown exec mode");
+  if (c->kv_dtype != MOSHI_KV_F32 && c->kv_dtype != MOSHI_KV_BF16) return bad("unknown kv_dtype");
+  if (c->kv_dtype == MOSHI_KV_BF16 && c->band == MOSHI_BAND_F32) return bad("the f32 band keeps a float32 KV cache");
   if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f)) return bad("rms_eps must be >= 0 and rope_theta > 0");
   return MOSHI_OK;
 }
@@ -1358,19 +1368,11 @@ moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const
     const int64_t room = limit - pos;
     if (room >= 2 && T - t >= 2) {
       const int n = (int)std::min<int64_t>({room, (int64_t)PF_ROWS, (int64_t)(T - t)});
-      switch (s->cfg.band) {
-        case MOSHI_BAND_F32:
-          enqueue_prefill_rows<float, float, float>(s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q,
-                                                    duser + (size_t)t * d.Q);
-          break;
-        case MOSHI_BAND_BF16:
-          enqueue_prefill_rows<bf16_t, bf16_t, bf16_t>(s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q,
-                                                       duser + (size_t)t * d.Q);
-          break;
-        default:
-          enqueue_prefill_rows<int8_t, bf16_t, bf16_t>(s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q,
-                                                       duser + (size_t)t * d.Q);
-      }
+      with_types(s->cfg, [&](auto tt) {
+        typedef decltype(tt) T;
+        enqueue_prefill_rows<typename T::WT, typename T::ET, typename T::KT>(
+            s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q, duser + (size_t)t * d.Q);
+      });
       t += n;
     } else {
       mk::Forced f{};
@@ -1463,7 +1465,7 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
                               float *Y, int32_t iters, float *avg_us) {
   if (M < 1 || N < 1 || K < 16 || K % 16 || !W || !X || !Y || band < 0 || band > 2) return MOSHI_EINVAL;
   const size_t wcnt = (size_t)N * K, xcnt = (size_t)M * K;
-  const size_t welt = linear_elt(band), xelt = band == MOSHI_BAND_F32 ? 4 : 2;
+  const size_t welt = linear_elt(band), xelt = band == MOSHI_BAND_F32 ? 4 : 4;  // bf16: hi and lo planes
   if (wcnt * welt >= ((size_t)1 << 31) || xcnt * xelt >= ((size_t)1 << 31)) return MOSHI_EINVAL;
   char *dw = nullptr, *dx = nullptr;
   float *ds = nullptr, *dy = nullptr, *stg = nullptr;
@@ -1484,9 +1486,15 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
       chk(hipMemcpy(dw, W, wcnt * 4, hipMemcpyHostToDevice));
       chk(hipMemcpy(dx, X, xcnt * 4, hipMemcpyHostToDevice));
     } else {
-      std::vector<uint16_t> hx(xcnt);
-      for (size_t k = 0; k < xcnt; ++k) hx[k] = host_f2bf(X[k]);
-      chk(hipMemcpy(dx, hx.data(), xcnt * 2, hipMemcpyHostToDevice));
+      std::vector<uint16_t> hx(2 * xcnt);  // per row: hi plane, then lo plane
+      for (size_t m = 0; m < (size_t)M; ++m)
+        for (size_t k = 0; k < (size_t)K; ++k) {
+          const float v = X[m * K + k];
+          const uint16_t hi = host_f2bf(v);
+          hx[m * 2 * K + k] = hi;
+          hx[m * 2 * K + K + k] = host_f2bf(v - host_bf2f(hi));
+        }
+      chk(hipMemcpy(dx, hx.data(), xcnt * 4, hipMemcpyHostToDevice));
       if (band == MOSHI_BAND_BF16) {
         std::vector<uint16_t> hb(wcnt);
         for (size_t k = 0; k < wcnt; ++k) hb[k] = host_f2bf(W[k]);
@@ -1504,10 +1512,10 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
           reinterpret_cast<const float *>(dw), nullptr, N, K, reinterpret_cast<const float *>(dx), K, M, dy, N);
     else if (band == MOSHI_BAND_BF16)
       mk::k_gemm<bf16_t, false, MOSHI_N_STAGES><<<grid, mk::GBLOCK, 0, st>>>(
-          reinterpret_cast<const bf16_t *>(dw), nullptr, N, K, reinterpret_cast<const bf16_t *>(dx), K, M, dy, N);
+          reinterpret_cast<const bf16_t *>(dw), nullptr, N, K, reinterpret_cast<const bf16_t *>(dx), 2 * K, M, dy, N);
     else
       mk::k_gemm<int8_t, false, MOSHI_N_STAGES><<<grid, mk::GBLOCK, 0, st>>>(
-          reinterpret_cast<const int8_t *>(dw), ds, N, K, reinterpret_cast<const bf16_t *>(dx), K, M, dy, N);
+          reinterpret_cast<const int8_t *>(dw), ds, N, K, reinterpret_cast<const bf16_t *>(dx), 2 * K, M, dy, N);
   };
   if (rc == MOSHI_OK) {
     launch();

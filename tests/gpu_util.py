@@ -18,3 +18,18 @@ def cosine(g, o):
 def top2_margin(v):
     s = np.sort(np.asarray(v, np.float64))
     return float(s[-1] - s[-2])
+
+
+def frame_agreement(tr, ref):
+    """Per-frame comparison for the low-precision bands: the cosine of every logits vector whose
+    conditioning agrees (the text head always; the head of codebook c only while the text token and
+    codebooks < c picked the oracle's tokens, since within a frame each depformer step feeds on the
+    previous step's own token), and the token matches."""
+    got = [tr["text_token"]] + tr["audio_tokens"]
+    want = [ref["text_token"]] + ref["audio_tokens"]
+    cos = [cosine(tr["text_logits"], ref["text_logits"])]
+    for c in range(len(want) - 1):
+        if got[: c + 1] != want[: c + 1]:
+            break
+        cos.append(cosine(tr["audio_logits"][c], ref["audio_logits"][c]))
+    return min(cos), sum(int(a == b) for a, b in zip(got, want))

@@ -54,10 +54,14 @@ def test_gemv_moshi7b_shapes_sampled_rows(band, N, K):
 
 
 def rounded_x(band, X):
-    """The activations as the matrix-core path feeds them (bf16 for the bf16 and int8 bands)."""
+    """The activations as the matrix-core path feeds them: float32 values, split for the bf16 and
+    int8 bands into bf16 hi and lo parts whose sum keeps about 16 significant bits."""
+    X = X.astype(np.float64)
     if band == "f32":
-        return X.astype(np.float64)
-    return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(X)).astype(np.float64)
+        return X
+    hi = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(X.astype(np.float32))).astype(np.float64)
+    lo = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits((X - hi).astype(np.float32))).astype(np.float64)
+    return hi + lo
 
 
 @pytest.mark.parametrize("band", ["f32", "bf16", "i8"])

@@ -8,7 +8,7 @@ import pytest
 import rq_transformer_frame_amd as rq
 import synth
 from oracle import OracleLM
-from tests.gpu_util import cosine, rel_err
+from tests.gpu_util import cosine, frame_agreement, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -39,21 +39,6 @@ def compare_step(tr, ref, st, out, has, frame):
     assert st == (rq.MOSHI_NONE if ref["out"] is None else rq.MOSHI_OK)
     if ref["out"] is not None:
         assert out[0].tolist() == ref["out"], frame
-
-
-def frame_agreement(tr, ref):
-    """Per-frame comparison for the low-precision bands: the cosine of every logits vector whose
-    conditioning agrees (the text head always; the head of codebook c only while the text token and
-    codebooks < c picked the oracle's tokens, since within a frame each depformer step feeds on the
-    previous step's own token), and the token matches."""
-    got = [tr["text_token"]] + tr["audio_tokens"]
-    want = [ref["text_token"]] + ref["audio_tokens"]
-    cos = [cosine(tr["text_logits"], ref["text_logits"])]
-    for c in range(len(want) - 1):
-        if got[: c + 1] != want[: c + 1]:
-            break
-        cos.append(cosine(tr["audio_logits"][c], ref["audio_logits"][c]))
-    return min(cos), sum(int(a == b) for a, b in zip(got, want))
 
 
 @pytest.mark.parametrize("exec_mode", ["graph", "stream", "persistent"])
@@ -333,3 +318,29 @@ def test_prefill_row_batches_then_single_frames(weights, oracle):
             ref = oracle.step(ost, users[f])
             st, out, has = s.step(users[f])
             compare_step(s.read_trace(0), ref, st, out, has, T + f)
+
+
+@pytest.mark.parametrize("batch", [1, 3])
+def test_bf16_kv_cache_on_the_tiny_model(weights, batch):
+    """The opt-in bfloat16 KV cache (bf16 band), single-conversation and batched paths, against the
+    oracle on the same bf16-rounded weights (the KV storage loss stays within the bar at this
+    context length)."""
+    w16 = {k: (synth.f32_to_bf16_bits(v) if v.ndim == 2 else v) for k, v in weights.items()}
+    ref_lm = OracleLM(CFG, w16)
+    users = np.stack([synth.user_tokens(CFG, 8, conv=b) for b in range(batch)], axis=1)
+    osts = [ref_lm.new_state() for _ in range(batch)]
+    agree, total, cos_min = 0, 0, 1.0
+    with rq.Session(CFG, band="bf16", batch=batch, kv="bf16") as s:
+        s.load_weights(w16)
+        for f in range(8):
+            s.step(users[f])
+            for b in range(batch):
+                ref = ref_lm.step(osts[b], users[f, b])
+                c, a = frame_agreement(s.read_trace(b), ref)
+                cos_min, agree, total = min(cos_min, c), agree + a, total + 9
+                ref_lm.force_generated(osts[b], ref["text_token"], ref["audio_tokens"])
+                s.force_generated(b, ref["text_token"], ref["audio_tokens"])
+    print(f"bf16 KV batch {batch}: min cosine {cos_min:.6f}, agreement {agree}/{total}")
+    assert cos_min >= 0.999
+    assert agree / total >= 0.99
+
