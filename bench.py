@@ -1,8 +1,9 @@
 """Frame-step benchmark: Moshi-7B-shaped RQ-Transformer, bfloat16 weights, B=1, on one MI355X.
 
 One step = one 80 ms frame through the whole hot path (ring, embedding sum, 32 temporal layers,
-text head + argmax, 8 depformer codebook steps, ring update), issued as one hipGraph replay per
-frame.  After W warm-up frames the session is reset and K frames are timed from offset 0 (the
+text head + argmax, 8 depformer codebook steps, ring update), issued as one persistent kernel
+launch per frame (--exec graph: one hipGraph replay; --exec stream: kernel by kernel).  Other
+workloads (--config): int8 weights, a long-context prefill, 64 conversations stepped together.  After W warm-up frames the session is reset and K frames are timed from offset 0 (the
 workload: 250 greedy frames, seed-1 random-init weights, uniform user tokens).
 
 Prints one JSON line with frames/s, the roofline of the dominant kernel (measured with HIP
@@ -23,6 +24,37 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "frames/s (80 ms) at B=1, Moshi-7B shape bf16; % of HBM roofline"
+
+
+# HBM bytes per dispatch of the dominant kernels, from two rocprofv3 --pmc runs (FETCH_SIZE,
+# WRITE_SIZE) scaled by a 256 MiB device-to-device copy in the same runs (profiles/ holds the
+# summaries and commands).  Valid only for the kernel sources they were taken on: the bench
+# reports traffic null when the sources' hash differs.
+TRAFFIC = {
+    "sources_sha256": "a64a0c3b18ac2fba30a31a0918f8598248504b343dc5ed366370bd62f83809f6",
+    "per_dispatch": {
+        "moshi7b_bf16_b1/frame_persistent": 14858311299,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
+        "moshi7b_bf16_b1/gate_in": 185103370,
+    },
+}
+
+
+def sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "rq_transformer_frame_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config: str, kernel: str):
+    if TRAFFIC["sources_sha256"] != sources_sha256():
+        return None
+    return TRAFFIC["per_dispatch"].get(f"{config}/{kernel}")
 
 
 def log(msg):
@@ -98,11 +130,14 @@ def main():
     ap.add_argument("--steps", type=int, default=250)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="moshi7b_bf16_b1")
-    ap.add_argument("--exec", default="graph", choices=["graph", "persistent", "stream"])
+    ap.add_argument("--exec", default="persistent", choices=["graph", "persistent", "stream"])
     ap.add_argument("--profile-frames", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kv", default="f32", choices=["f32", "bf16"], help="KV cache storage")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first copy this many MiB device to device (a kernel of known traffic, for "
+                         "scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -112,6 +147,15 @@ def main():
 
     import rq_transformer_frame_amd as rq
     import synth
+
+    if args.copy_mb:
+        import torch
+        a = torch.empty(args.copy_mb << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_mb} MiB device to device")
+        del a, b
 
     cfg = synth.CONFIGS[args.config]
     band = cfg.band
@@ -125,6 +169,8 @@ def main():
 
     kv = args.kv
     kve = 4 if kv == "f32" else 2
+    if B > 1 and args.exec == "persistent":  # the persistent frame kernel serves one conversation
+        args.exec = "graph"
     sess = rq.Session(cfg, exec=args.exec, kv=kv)
     t = time.time()
     sess.load_weights(weights)
@@ -196,12 +242,13 @@ def main():
         avg = gpu_us / gpu_n
         roofline = {"bound": "hbm", "kernel": "k_frame_persistent (one launch per frame)",
                     "achieved": round(fb / avg / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(fb / avg / 1e3 / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(fb / avg / 1e3 / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(cfg.name, "frame_persistent"),
                     "bytes_per_launch": fb, "avg_us": round(avg, 2)}
     else:
         d = stages[dom]
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, dom),
                     "bytes_per_launch": d["bytes_per_launch"], "avg_us": round(d["avg_us"], 2)}
 
     cpu = None

@@ -1,0 +1,90 @@
+"""Summaries of rocprofv3 output for the frame-step kernels.
+
+    python -m rq_transformer_frame_amd.profsum stats <kernel_stats.csv> [bench.json]
+    python -m rq_transformer_frame_amd.profsum traffic <fetch counter_collection.csv> <write ...csv> <copy MiB>
+
+`stats` prints a markdown table of the per-kernel averages (stage names recovered from the kernels'
+stage tags; algorithmic GB/s when the bench JSON line of the same run is given).  `traffic` prints
+per-kernel HBM bytes per dispatch from a FETCH_SIZE run and a WRITE_SIZE run, each scaled by what
+the same counter reads for the first device-to-device copy of `copy MiB` in that run.
+"""
+from __future__ import annotations
+
+import collections
+import csv
+import json
+import re
+import sys
+
+STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv",
+          "dep_out", "dep_gate_in", "dep_gate_out", "dep_head", "frame_end"]
+
+
+def stage_of(name: str) -> str:
+    """The frame stage a kernel symbol belongs to (stage tags are the last template argument)."""
+    for key, stage in (("k_qkv_rope", "qkv"), ("k_attn", "attn"), ("k_dep_qkv", "dep_qkv"),
+                       ("k_dep_out", "dep_out"), ("k_embed_begin", "embed"), ("k_frame_end", "frame_end"),
+                       ("k_frame_persistent", "whole frame (persistent kernel)")):
+        if key in name:
+            return stage
+    m = re.search(r"mk::k_(?:gemv|gate|head|gemm)<[^>]*?,\s*(\d+)>", name)
+    if m and int(m.group(1)) < len(STAGES):
+        return STAGES[int(m.group(1))]
+    return name.split("(")[0]
+
+
+def stats(path: str, bench: str | None = None) -> str:
+    rows = list(csv.DictReader(open(path)))
+    per_stage = {}
+    if bench:
+        line = json.loads(open(bench).read().strip().splitlines()[-1])
+        per_stage = {k: v.get("bytes_per_launch") for k, v in line.get("stages", {}).items()}
+    tot = sum(float(r["TotalDurationNs"]) for r in rows)
+    out = ["| stage (kernel) | calls | avg us | min us | share | algorithmic GB/s (avg) |",
+           "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        st = stage_of(r["Name"])
+        avg = float(r["AverageNs"]) / 1e3
+        b = per_stage.get(st)
+        gbs = f"{b / avg / 1e3:.0f}" if b else ""
+        out.append(f"| {st} | {r['Calls']} | {avg:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                   f"{100 * float(r['TotalDurationNs']) / tot:.1f}% | {gbs} |")
+    return "\n".join(out)
+
+
+def traffic(fetch: str, write: str, copy_mib: float) -> str:
+    def load(p):
+        d = collections.defaultdict(list)
+        first_copy = None
+        for r in csv.DictReader(open(p)):
+            v = float(r["Counter_Value"])
+            if first_copy is None and "copyBuffer" in r["Kernel_Name"]:
+                first_copy = v
+            d[r["Kernel_Name"]].append(v)
+        return d, first_copy
+
+    f, fc = load(fetch)
+    w, wc = load(write)
+    kib = copy_mib * 1024.0
+    ff, fw = kib / fc, kib / wc  # the copy reads and writes copy_mib MiB
+    out = [f"Scale factors from the {copy_mib:g} MiB copy: FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {fw:.3f}.", "",
+           "| stage (kernel) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per dispatch (scaled) |",
+           "|---|---|---|---|---|"]
+    for name in sorted(f, key=lambda n: -sum(f[n]) / len(f[n])):
+        if "rocclr" in name:
+            continue
+        fv = sum(f[name]) / len(f[name])
+        wv = sum(w.get(name, [0.0])) / max(len(w.get(name, [])), 1)
+        out.append(f"| {stage_of(name)} | {len(f[name])} | {fv:.1f} | {wv:.1f} | "
+                   f"{(fv * ff + wv * fw) * 1024:.0f} |")
+    return "\n".join(out)
+
+
+if __name__ == "__main__":
+    if len(sys.argv) >= 3 and sys.argv[1] == "stats":
+        print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else None))
+    elif len(sys.argv) == 5 and sys.argv[1] == "traffic":
+        print(traffic(sys.argv[2], sys.argv[3], float(sys.argv[4])))
+    else:
+        print(__doc__)
+        sys.exit(2)
