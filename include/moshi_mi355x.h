@@ -219,6 +219,12 @@ moshi_status moshi_gpu_time(moshi_state *s, int32_t enable, double *total_us, in
  * frame's first arrival, *n_phases the phase count.  enable = 0 switches it off. */
 moshi_status moshi_phase_times(moshi_state *s, int32_t enable, double *ts, int32_t max_phases, int32_t *n_phases);
 
+/* Measurement (persistent executor): after moshi_phase_times(s, 2, ...) the frames also record
+ * every block's arrival at every phase; ts [n_phases][n_blocks] (host, up to max_values values)
+ * receives the last frame's record in microseconds from its first arrival, *n_blocks the grid
+ * size.  MOSHI_ESTATE if the record was never switched on. */
+moshi_status moshi_block_times(moshi_state *s, double *ts, int32_t max_values, int32_t *n_blocks);
+
 /* Bytes of linear weights (what one frame must stream) and of all device weights. */
 moshi_status moshi_weight_bytes(const moshi_state *s, int64_t *linear_bytes, int64_t *all_bytes);
 

@@ -39,6 +39,7 @@ _SIGS = {
     "moshi_stream": (_vp, [_vp]),
     "moshi_debug_gemv": (_i32, [_i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
     "moshi_debug_gemm": (_i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "moshi_block_times": (_i32, [_vp, _vp, _i32, _vp]),
     "moshi_profile_frames": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "moshi_gpu_time": (_i32, [_vp, _i32, _vp, _vp]),
     "moshi_phase_times": (_i32, [_vp, _i32, _vp, _i32, _vp]),
@@ -240,12 +241,24 @@ class Session:
 
     def phase_times(self, enable: int = -1):
         """Persistent executor: per-phase [block-0 arrival, completion] times (us) of the last
-        frame; enable 1/0 switches the recording on/off."""
+        frame; enable 1/0 switches the recording on/off, 2 also records every block's arrival
+        (block_times)."""
         n = ctypes.c_int32()
         self._check(self.lib.moshi_phase_times(self.h, -1, None, 0, ctypes.byref(n)), "moshi_phase_times")
         ts = np.zeros((n.value, 2), np.float64)
         self._check(self.lib.moshi_phase_times(self.h, enable, _ptr(ts), n.value, ctypes.byref(n)),
                     "moshi_phase_times")
+        return ts
+
+    def block_times(self):
+        """Persistent executor, after phase_times(2): every block's arrival time (us) at every
+        phase of the last frame, [phases][blocks]."""
+        n = ctypes.c_int32()
+        self._check(self.lib.moshi_phase_times(self.h, -1, None, 0, ctypes.byref(n)), "moshi_phase_times")
+        nb = ctypes.c_int32()
+        self._check(self.lib.moshi_block_times(self.h, None, 0, ctypes.byref(nb)), "moshi_block_times")
+        ts = np.zeros((n.value, nb.value), np.float64)
+        self._check(self.lib.moshi_block_times(self.h, _ptr(ts), ts.size, ctypes.byref(nb)), "moshi_block_times")
         return ts
 
     @property

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(BLOCK) void k_gate_post(const float *__restrict__ Y
 
 // a7 / a8 greedy head: the first-wins argmax of logits row m (N values), stored as the single
 // partial part[m * stride] that the consumers of a head's token merge.
-__global__ __launch_bounds__(BLOCK) void k_argmax_rows(const float *__restrict__ L, int ld, int N,
+static __global__ __launch_bounds__(BLOCK) void k_argmax_rows(const float *__restrict__ L, int ld, int N,
                                                        ArgBest *__restrict__ part, int stride) {
   __shared__ ArgBest wb[NWAVES];
   const int m = blockIdx.x;
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_entry(Dims d, Bufs s, const ET *_
 
 // a8 after the depformer q|k|v product Y[m] (3 Dd columns, no rope): q to dq, k and v to the
 // per-frame cache entry (layer, cb) of conversation b0 + m.
-__global__ __launch_bounds__(BLOCK) void k_dep_qkv_post(Dims d, Bufs s, const float *__restrict__ Y, int ldy,
+static __global__ __launch_bounds__(BLOCK) void k_dep_qkv_post(Dims d, Bufs s, const float *__restrict__ Y, int ldy,
                                                         int layer, int cb, int b0) {
   const int m = blockIdx.x, b = b0 + m;
   const int Dd = d.Dd;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_attn(Dims d, Bufs s, int layer, i
 // a11 bookkeeping of a teacher-forced prefill of T frames of conversation `conv`, one thread:
 // for each frame, the user write and the gather of the 17 model inputs (into rows[t]), then the
 // forced ring write and the offset step, exactly as the frame kernels do them one frame at a time.
-__global__ void k_prefill_ring(Dims d, Bufs s, int conv, int T, const int32_t *__restrict__ text,
+static __global__ void k_prefill_ring(Dims d, Bufs s, int conv, int T, const int32_t *__restrict__ text,
                                const int32_t *__restrict__ agent, const int32_t *__restrict__ user,
                                int32_t *__restrict__ rows) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;

@@ -45,6 +45,7 @@ struct PArgs {
   int *err;        // error flag (also copied back to the host with the outputs)
   int spin_limit;
   uint64_t *phase_ts;  // optional [phases][2]: block 0's arrival and the phase's completion time
+  uint64_t *block_ts;  // optional [phases][gridDim.x]: every block's arrival time
 };
 
 // Four consecutive table values as one load (8 bytes of bf16 or 16 bytes of float), widened to
@@ -149,6 +150,7 @@ __device__ __forceinline__ void p_arrive(const PArgs &a, uint32_t tag, int p) {
   if (threadIdx.x == 0) {
     st_sys_u32(a.sync + blockIdx.x, tag);
     if (a.phase_ts && blockIdx.x == 0) a.phase_ts[2 * p] = wall_clock64();
+    if (a.block_ts) a.block_ts[(size_t)p * gridDim.x + blockIdx.x] = wall_clock64();
   }
 }
 
@@ -368,7 +370,9 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
     // attention: block bi < H * S takes head bi % H, split bi / H
     {
       const int n = (int)(pos + 1 < (int64_t)d.C ? pos + 1 : (int64_t)d.C);
-      const int S = min(ATTN_MAX_S, max(1, (n + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK));
+      // splits: enough for ATTN_MIN_CHUNK positions each, at most ATTN_MAX_S, and every (head,
+      // split) pair needs a block of its own (the grid holds at least H blocks)
+      const int S = min(min(ATTN_MAX_S, (int)gridDim.x / d.H), max(1, (n + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK));
       const int bi = blockIdx.x;
       if (bi < d.H * S) {
         constexpr int EPL = HD / 16;

@@ -620,7 +620,7 @@ struct Forced {
   int32_t t[17];
 };
 
-__global__ __launch_bounds__(BLOCK) void k_frame_end(Dims d, Bufs s, int b0, int use_forced, Forced forced,
+static __global__ __launch_bounds__(BLOCK) void k_frame_end(Dims d, Bufs s, int b0, int use_forced, Forced forced,
                                                      int last_parts) {
   const int b = b0 + blockIdx.x;
   int32_t *tk = s.tokens + (size_t)b * (1 + d.Q);
@@ -645,14 +645,14 @@ __global__ __launch_bounds__(BLOCK) void k_frame_end(Dims d, Bufs s, int b0, int
 }
 
 // [LM] state(): ring <- -2, offset <- 0 for conversations [b0, b0 + gridDim.x).
-__global__ void k_reset(Dims d, Bufs s, int b0) {
+static __global__ void k_reset(Dims d, Bufs s, int b0) {
   const int b = b0 + blockIdx.x;
   for (int i = threadIdx.x; i < d.NS * 3; i += blockDim.x) s.ring[(size_t)b * d.NS * 3 + i] = -2;
   if (threadIdx.x == 0) s.offset[b] = 0;
 }
 
 // [LM] force_generated: ring slot offset % 3 of the text and generated streams <- forced tokens.
-__global__ void k_force(Dims d, Bufs s, int b, Forced forced) {
+static __global__ void k_force(Dims d, Bufs s, int b, Forced forced) {
   if (threadIdx.x != 0) return;
   const int p = (int)(s.offset[b] % 3);
   for (int st = 0; st <= d.Q; ++st) s.ring[((size_t)b * d.NS + st) * 3 + p] = forced.t[st];
@@ -660,7 +660,7 @@ __global__ void k_force(Dims d, Bufs s, int b, Forced forced) {
 
 // Per-row symmetric int8 quantisation (load time): s_r = max|w_r| / 127, q = round half away
 // from zero of w / s_r, clamped to [-127, 127]; q = 0 when s_r = 0.  One block per row.
-__global__ __launch_bounds__(BLOCK) void k_quant_rows(const float *__restrict__ w, int64_t K, int8_t *__restrict__ q,
+static __global__ __launch_bounds__(BLOCK) void k_quant_rows(const float *__restrict__ w, int64_t K, int8_t *__restrict__ q,
                                                       float *__restrict__ scale, int64_t row0) {
   __shared__ float red[NWAVES];
   const int64_t r = row0 + blockIdx.x;

@@ -16,7 +16,7 @@
 #include <vector>
 
 #include "batch.h"
-#include "frame_persistent.h"
+#include "persistent_variants.h"
 #include "moshi_mi355x.h"
 
 using mk::bf16_t;
@@ -109,6 +109,8 @@ struct moshi_state {
   mk::LayerPtrs *d_tl = nullptr, *d_dl = nullptr;
   mk::PArgs *d_pargs = nullptr;  // persistent kernel arguments (device copy)
   uint64_t *d_phase_ts = nullptr;
+  uint64_t *d_block_ts = nullptr;  // per-block arrival times (allocated on first request)
+  bool block_timing = false;
   int nph = 0;
   bool phase_timing = false;
   int *d_err = nullptr;
@@ -422,44 +424,22 @@ int64_t block_rows(int64_t units, int P, int blocks) {
   return (units + tw - 1) / tw * mk::NWAVES * P;
 }
 
-// Compiled persistent-kernel variants: (band, temporal head dim, depformer head dim / 16, staging
-// loads per thread for inputs of width D, F, Dd, Fd).  The staging counts only set how many loads
-// each thread issues per pass, so a shape without its own variant runs the generic one.
-struct PVariant {
-  int band, kv, hd, depl, ud, uf, udd, ufd;
-  const void *fn;
-};
-
-template <typename WT, typename ET, typename KT, int HD, int DEPL, int UD, int UF, int UDd, int UFd>
-PVariant pvariant(int band) {
-  return PVariant{band, std::is_same<KT, float>::value ? MOSHI_KV_F32 : MOSHI_KV_BF16, HD, DEPL, UD, UF, UDd, UFd,
-                  reinterpret_cast<const void *>(&mk::k_frame_persistent<WT, ET, KT, HD, DEPL, UD, UF, UDd, UFd>)};
-}
-
-const PVariant *persistent_variants(int *n) {
-  static const PVariant v[] = {
-      // Moshi-7B shape (d4096 / ffn 11264, depformer d1024 / ffn 2816)
-      pvariant<bf16_t, bf16_t, float, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_BF16),
-      pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_BF16),
-      pvariant<int8_t, bf16_t, float, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_I8),
-      // small shapes, one pass per 2048-wide input
-      pvariant<float, float, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_F32),
-      pvariant<bf16_t, bf16_t, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_BF16),
-      pvariant<int8_t, bf16_t, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
-  };
-  *n = (int)(sizeof(v) / sizeof(v[0]));
-  return v;
-}
-
 int stage_passes(int K) { return (K / 4 + mk::PBLOCK - 1) / mk::PBLOCK; }  // 16-byte loads per thread
 
-const void *select_persistent(const moshi_config &c, size_t *lds) {
+// The persistent kernel runs one block per CU; the temporal attention needs a block per head.
+// Returns the kernel, its dynamic LDS and grid, or null when the shape has no persistent variant.
+const void *select_persistent(const moshi_config &c, int cus, size_t *lds, int *grid) {
   const int D = c.d_model, F = c.ffn_hidden, Dd = c.dep_d_model, Fd = c.dep_ffn_hidden;
   const int hd = D / c.n_heads, hdd = Dd / c.dep_heads;
   if (c.dep_q > mk::PQ) return nullptr;
+  const int g = cus;
+  if (g < c.n_heads) return nullptr;
   const int ud = stage_passes(D), uf = stage_passes(F), udd = stage_passes(Dd), ufd = stage_passes(Fd);
   int n = 0;
-  const PVariant *v = persistent_variants(&n);
+  const PVariant hd128[] = {pvariant_hd128_bf16_kvf32(), pvariant_hd128_bf16_kvbf16(), pvariant_hd128_i8_kvf32()};
+  const PVariant *v = hd128;
+  n = 3;
+  if (hd != 128) v = pvariants_hd64(&n);
   const PVariant *pick = nullptr;
   for (int i = 0; i < n; ++i) {
     if (v[i].band != c.band || v[i].kv != c.kv_dtype || v[i].hd != hd || v[i].depl * 16 != hdd) continue;
@@ -471,9 +451,13 @@ const void *select_persistent(const moshi_config &c, size_t *lds) {
     if (!pick && v[i].ud == 1 && v[i].uf == 1 && v[i].udd >= udd && v[i].ufd == 1) pick = &v[i];
   }
   if (!pick) return nullptr;
-  const size_t fl = std::max({(size_t)2 * D, (size_t)F + D, (size_t)2 * Dd, (size_t)Fd + Dd,
+  // attention scores of one split: at most max(ATTN_MIN_CHUNK, ceil(C / most splits)) positions
+  const int smax = std::min(mk::ATTN_MAX_S, g / c.n_heads);
+  const size_t chunk = std::max(mk::ATTN_MIN_CHUNK, (c.context + smax - 1) / smax);
+  const size_t fl = std::max({(size_t)2 * D, (size_t)F + D, (size_t)2 * Dd, (size_t)Fd + Dd, chunk,
                               (size_t)mk::ATTN_MAX_S * (hd + 2) + mk::ATTN_MAX_S});
   *lds = fl * 4;
+  *grid = g;
   return pick->fn;
 }
 
@@ -811,6 +795,7 @@ moshi_status write_pargs(moshi_state *s) {
   a.err = s->d_err;
   a.spin_limit = 1 << 20;
   a.phase_ts = s->phase_timing ? s->d_phase_ts : nullptr;
+  a.block_ts = s->block_timing ? s->d_block_ts : nullptr;
   HIP_TRY(s, hipMemcpy(s->d_pargs, &a, sizeof(a), hipMemcpyHostToDevice));
   return MOSHI_OK;
 }
@@ -962,7 +947,7 @@ moshi_status moshi_create(const moshi_config *cfg, void *hip_stream, moshi_state
     return st;
   }
   if (cfg->exec == MOSHI_EXEC_PERSISTENT) {
-    s->pkern = d.B == 1 ? select_persistent(s->cfg, &s->plds) : nullptr;
+    s->pkern = d.B == 1 ? select_persistent(s->cfg, s->cus, &s->plds, &s->pgrid) : nullptr;
     int per_cu = 0;
     if (!s->pkern || hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, s->pkern, mk::PBLOCK, s->plds) != hipSuccess ||
         per_cu < 1) {
@@ -970,7 +955,7 @@ moshi_status moshi_create(const moshi_config *cfg, void *hip_stream, moshi_state
       moshi_destroy(s);
       return MOSHI_EINVAL;
     }
-    s->pgrid = s->cus;  // one block per CU
+    // at most one block per CU (co-resident by the cooperative launch)
     if (write_pargs(s) != MOSHI_OK) {
       fprintf(stderr, "moshi_create: %s\n", s->err.c_str());
       moshi_destroy(s);
@@ -998,6 +983,7 @@ void moshi_destroy(moshi_state *s) {
   if (s->gexec) (void)hipGraphExecDestroy(s->gexec);
   if (s->ev0) (void)hipEventDestroy(s->ev0);
   if (s->ev1) (void)hipEventDestroy(s->ev1);
+  if (s->d_block_ts) (void)hipFree(s->d_block_ts);
   if (s->warena) (void)hipFree(s->warena);
   if (s->sarena) (void)hipFree(s->sarena);
   if (s->h_pin) (void)hipHostFree(s->h_pin);
@@ -1120,9 +1106,32 @@ moshi_status moshi_phase_times(moshi_state *s, int32_t enable, double *ts, int32
     for (int p = 0; p < std::min(max_phases, s->nph); ++p)
       for (int k = 0; k < 2; ++k) ts[2 * p + k] = (double)(int64_t)(raw[2 * p + k] - t0) * 1000.0 / (double)khz;
   }
-  if (enable >= 0 && (enable != 0) != s->phase_timing) {
+  if (enable >= 0 && ((enable != 0) != s->phase_timing || (enable == 2) != s->block_timing)) {
+    if (enable == 2 && !s->d_block_ts)
+      HIP_TRY(s, hipMalloc(&s->d_block_ts, (size_t)s->nph * s->pgrid * 8));
     s->phase_timing = enable != 0;
+    s->block_timing = enable == 2;
     return write_pargs(s);
+  }
+  return MOSHI_OK;
+}
+
+moshi_status moshi_block_times(moshi_state *s, double *ts, int32_t max_values, int32_t *n_blocks) {
+  if (!s) return MOSHI_EINVAL;
+  if (!s->pkern) return fail(s, MOSHI_ESTATE, "block times need the persistent executor");
+  if (!s->d_block_ts) return fail(s, MOSHI_ESTATE, "block times were not switched on");
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  if (n_blocks) *n_blocks = s->pgrid;
+  if (ts && max_values > 0) {
+    std::vector<uint64_t> raw((size_t)s->nph * s->pgrid);
+    HIP_TRY(s, hipStreamSynchronize(s->stream));
+    HIP_TRY(s, hipMemcpy(raw.data(), s->d_block_ts, raw.size() * 8, hipMemcpyDeviceToHost));
+    int khz = 0;
+    HIP_TRY(s, hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, s->device));
+    uint64_t t0 = raw[0];
+    for (size_t i = 0; i < (size_t)s->pgrid; ++i) t0 = std::min(t0, raw[i]);
+    for (size_t i = 0; i < std::min(raw.size(), (size_t)max_values); ++i)
+      ts[i] = (double)(int64_t)(raw[i] - t0) * 1000.0 / (double)khz;
   }
   return MOSHI_OK;
 }

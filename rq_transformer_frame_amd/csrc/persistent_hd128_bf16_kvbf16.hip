@@ -1,0 +1,6 @@
+// Persistent frame kernel instance: temporal head dim 128, bf16 weights, bf16 KV.
+#include "persistent_variants.h"
+
+using mk::bf16_t;
+
+PVariant pvariant_hd128_bf16_kvbf16() { return pvariant<bf16_t, bf16_t, bf16_t, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_BF16); }

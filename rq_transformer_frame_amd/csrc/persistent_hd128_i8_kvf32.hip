@@ -1,0 +1,6 @@
+// Persistent frame kernel instance: temporal head dim 128, int8 weights, float32 KV.
+#include "persistent_variants.h"
+
+using mk::bf16_t;
+
+PVariant pvariant_hd128_i8_kvf32() { return pvariant<int8_t, bf16_t, float, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_I8); }

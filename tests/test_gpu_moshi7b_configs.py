@@ -3,7 +3,8 @@
 cosine >= 0.999, and >= 99% of the greedy tokens equal.
 
 - long context: a 2900-frame teacher-forced prefill (row batches on the matrix cores) then greedy
-  frames at positions 2900.., against the oracle's batched causal prefill;
+  frames at positions 2900.. on the graph and the persistent executor, against the oracle's
+  batched causal prefill;
 - int8 weights (per-row scales): against the int8-dequantised oracle (storage loss only); the
   float32 oracle's agreement is printed to separate quantisation loss from kernel error;
 - 64 conversations stepped together after per-conversation prefixes: every conversation against
@@ -37,29 +38,36 @@ def test_long_context_prefill_then_greedy_matches_oracle():
     text, agent, user = synth.prefill_tokens(cfg, T)
     users = synth.user_tokens(cfg, frames, start_frame=T)
     t0 = tick("weights", t0)
-    with rq.Session(cfg) as s:
-        s.load_weights(w)
-        s.prefill_forced(0, text, agent, user)
-        assert s.offset(0) == T
-        t0 = tick("GPU prefill", t0)
-        lm = OracleLM(cfg, w)
-        st = lm.new_state()
-        lm.prefill_forced(st, text, agent, user)
-        t0 = tick("oracle prefill", t0)
-        cos_min, agree, total = 1.0, 0, 0
-        for f in range(frames):
-            ref = lm.step(st, users[f])
-            s.step(users[f])
-            tr = s.read_trace(0)
-            assert tr["input_tokens"].tolist() == ref["input_tokens"].tolist(), f
-            c, a = frame_agreement(tr, ref)
-            cos_min, agree, total = min(cos_min, c), agree + a, total + 9
-            lm.force_generated(st, ref["text_token"], ref["audio_tokens"])
-            s.force_generated(0, ref["text_token"], ref["audio_tokens"])
-            t0 = tick(f"frame at position {T + f}: min cos {c:.6f}, tokens {a}/9", t0)
-    print(f"long context: min cosine {cos_min:.6f}, agreement {agree}/{total}")
-    assert cos_min >= 0.999
-    assert agree / total >= 0.99
+    lm = OracleLM(cfg, w)
+    st = lm.new_state()
+    lm.prefill_forced(st, text, agent, user)
+    t0 = tick("oracle prefill", t0)
+    refs = []
+    for f in range(frames):
+        ref = lm.step(st, users[f])
+        refs.append(ref)
+        lm.force_generated(st, ref["text_token"], ref["audio_tokens"])
+    t0 = tick("oracle frames", t0)
+    del lm
+    # the graph executor, and the persistent one the bench times
+    for mode in ("graph", "persistent"):
+        with rq.Session(cfg, exec=mode) as s:
+            s.load_weights(w)
+            s.prefill_forced(0, text, agent, user)
+            assert s.offset(0) == T
+            t0 = tick(f"{mode}: GPU prefill", t0)
+            cos_min, agree, total = 1.0, 0, 0
+            for f, ref in enumerate(refs):
+                s.step(users[f])
+                tr = s.read_trace(0)
+                assert tr["input_tokens"].tolist() == ref["input_tokens"].tolist(), (mode, f)
+                c, a = frame_agreement(tr, ref)
+                cos_min, agree, total = min(cos_min, c), agree + a, total + 9
+                s.force_generated(0, ref["text_token"], ref["audio_tokens"])
+                t0 = tick(f"{mode}: frame at position {T + f}: min cos {c:.6f}, tokens {a}/9", t0)
+        print(f"long context ({mode}): min cosine {cos_min:.6f}, agreement {agree}/{total}")
+        assert cos_min >= 0.999
+        assert agree / total >= 0.99
 
 
 @pytest.mark.timeout(1200)

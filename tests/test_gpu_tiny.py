@@ -344,3 +344,33 @@ def test_bf16_kv_cache_on_the_tiny_model(weights, batch):
     assert cos_min >= 0.999
     assert agree / total >= 0.99
 
+
+
+@pytest.mark.parametrize("exec_mode", ["graph", "persistent"])
+def test_long_prefill_many_attention_splits_matches_oracle(exec_mode):
+    """16 heads and 1400 cached positions: the temporal attention runs in many position splits
+    per head, more than the persistent grid has blocks per head (256 blocks / 16 heads, so the
+    split count is capped at 16), and the splits are merged by their running max and sum.
+    Float32, against the oracle."""
+    cfg = CFG.with_(name="tiny_f32_h16_long", d_model=1024, n_heads=16, context=1536)
+    T = 1400
+    w = synth.gen_weights(cfg)
+    lm = OracleLM(cfg, w)
+    text, agent, user = synth.prefill_tokens(cfg, T, conv=2)
+    text %= cfg.text_card
+    ost = lm.new_state()
+    lm.prefill_forced(ost, text, agent, user)
+    users = synth.user_tokens(cfg, 3, conv=2, start_frame=T)
+    with rq.Session(cfg, exec=exec_mode) as s:
+        s.load_weights(w)
+        s.prefill_forced(0, text, agent, user)
+        for f in range(3):
+            ref = lm.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            tr = s.read_trace(0)
+            assert tr["input_tokens"].tolist() == ref["input_tokens"].tolist(), f
+            assert rel_err(tr["transformer_out"], ref["transformer_out"]) <= TOL, f
+            assert rel_err(tr["text_logits"], ref["text_logits"]) <= TOL, f
+            for cb in range(cfg.dep_q):
+                assert rel_err(tr["audio_logits"][cb], ref["audio_logits"][cb]) <= TOL, (f, cb)
+            assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], f
