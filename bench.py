@@ -140,10 +140,12 @@ def main():
                          "scaling hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the B=1 frame step does not shard; see DESIGN.md for how batched conversations would)",
-              file=sys.stderr)
+        print(f"bench.py: this benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the B=1 frame step does not shard; batched conversations would be data-parallel, one "
+              "process per GPU)", file=sys.stderr)
         sys.exit(2)
+    if args.profile_frames < 1:
+        ap.error("--profile-frames must be at least 1 (the per-stage profile gives the roofline)")
 
     import rq_transformer_frame_amd as rq
     import synth

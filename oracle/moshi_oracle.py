@@ -17,7 +17,7 @@ whose argument the page builds in float32 (ln/exp of the rope frequency, sin/cos
 angle) are evaluated in float64 and rounded once to float32, i.e. the correctly rounded float32
 value of the page's float32 argument.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
   * rope pairs are interleaved (2i, 2i+1) -- [LM] module doc and rope_row (rlx_lm.rs says
     rotate-half; [LM] wins);
   * the depformer is conditioned on the post-out_norm hidden ([LM]; rlx_lm.rs feeds pre-norm);

@@ -239,4 +239,209 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm(const WT *__restrict__ W, const
   }
 }
 
+
+// ---- wide tiles, both operands streamed through an LDS ring -------------------------------------
+// For bf16 and int8 weights.  A block owns XN = 128 weight rows (32 per wave) and XM = 64
+// activation rows; its waves do not split K.  Every K block (64 columns) of both operands goes
+// straight from memory into one stage of a ring of XST LDS stages with LDS-direct loads (no
+// registers), XST - 1 K blocks ahead of the multiply.  The activation tile (hi and lo planes) is
+// loaded once per block and read by all four waves (tiles that split K over waves reload it per
+// wave).  Each 1 KB load fills whole 128-byte row segments (8 rows of a 64-column bf16 block, or
+// 16 rows of int8), so every cache line is fetched by one instruction; within a row the 16-byte
+// pieces are stored XOR-swizzled by the row (piece p of row r at slot p ^ (r % slots)), so the
+// matrix-core fragment reads (lane l: row l % 32, pieces of columns 32 (l / 32) ..) hit distinct
+// banks.
+// A grid z dimension splits K: every split writes its partial tile to `part` ([split][M][N]
+// floats) and k_gemm_reduce adds the splits in order, so the result does not depend on timing.
+constexpr int XN = 128;  // weight rows per block
+constexpr int XM = 64;   // activation rows per block
+constexpr int XKB = 64;  // K block
+constexpr int XST = 5;   // LDS stages (bf16: 5 x 32 KB, the whole LDS of a CU)
+
+// Weight chunks per wave and K block: bf16 one per 16-column step (8 bf16 per lane), int8 one per
+// two steps (16 int8 per lane).
+// (PER elements per 16-byte piece, PPR pieces per 64-column row, RPC rows per 1 KB chunk)
+template <typename WT> struct XWC;
+template <> struct XWC<bf16_t> { static constexpr int N = 4, ELT = 2, PER = 8, PPR = 8, RPC = 8; };
+template <> struct XWC<int8_t> { static constexpr int N = 2, ELT = 1, PER = 16, PPR = 4, RPC = 16; };
+
+// s_waitcnt immediate that waits until at most n vector memory operations are outstanding
+// (expcnt and lgkmcnt left at their maxima: no wait on them).
+constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw 32-bit buffer descriptor of `bytes` bytes at base (loads past the end read zero).
+__device__ __forceinline__ i32x4 raw_desc(const void *base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a), __builtin_amdgcn_readfirstlane((int)(a >> 32) & 0xFFFF),
+               __builtin_amdgcn_readfirstlane(bytes), BUF_DWORD3};
+}
+
+// LDS-direct load: lane l's 16 bytes at byte offset voff of the buffer go to LDS at lds + 16 l
+// (lds wave-uniform).  Issued from inline assembly so that the compiler does not track it: it
+// would otherwise wait for every such load before the next LDS read.  The caller waits for it with
+// an explicit s_waitcnt (a wave's vector memory operations complete in issue order).
+__device__ __forceinline__ void lds_load16(i32x4 desc, const void *lds, int voff) {
+  const int a = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(desc)
+               : "memory", "m0");
+}
+
+// Y[m][n] (ADD: +=) sum_k X[m][k] W[n][k] (* wscale[n]), or with gridDim.z > 1 the partial sums of
+// K blocks [z * kbs, (z + 1) * kbs) into part[z][m][n].  Grid (ceil(N / XN), ceil(M / XM), splits),
+// GBLOCK threads.  X: [M][ldx] bf16 in the hi | lo layout (planes K apart); K a multiple of 16.
+template <typename WT, bool ADD, int TAG>
+__global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, const float *__restrict__ wscale, int N,
+                                                   int K, const bf16_t *__restrict__ X, int ldx, int M,
+                                                   float *__restrict__ Y, int ldy, float *__restrict__ part, int kbs) {
+  constexpr int WC = XWC<WT>::N, WE = XWC<WT>::ELT;
+  constexpr int XCH = 16;                      // activation chunks per stage: [step][plane][m tile]
+  constexpr int NCH = XCH + GWAVES * WC;       // chunks per stage
+  constexpr int NL = XCH / GWAVES + WC;        // loads each wave issues per K block
+  __shared__ __align__(16) uint4 ring[XST][NCH * WAVE];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int n0 = blockIdx.x * XN, m0 = blockIdx.y * XM;
+  const int ln = lane & 31, g = lane >> 5;
+  const int n = n0 + wave * 32 + ln;
+  const i32x4 rw = raw_desc(W, (int)((size_t)N * K * WE));
+  const i32x4 rx = raw_desc(X, (int)((size_t)M * ldx * 2));
+  const int nkb = (K + XKB - 1) / XKB;
+  const int kb0 = blockIdx.z * kbs, kb1 = min(nkb, kb0 + kbs);
+  constexpr int PER = XWC<WT>::PER, PPR = XWC<WT>::PPR, RPC = XWC<WT>::RPC;
+  // this wave's activation chunks c = 4 wave + i: plane c / 8, rows 8 (c % 8) .. + 8 of the tile;
+  // lane l fills slot l % 8 of row 8 (c % 8) + l / 8 with piece (l % 8) ^ (row % 8)
+  int xo[XCH / GWAVES], xcol[XCH / GWAVES];
+#pragma unroll
+  for (int i = 0; i < XCH / GWAVES; ++i) {
+    const int c = GWAVES * wave + i;
+    const int pl = c >> 3, r = 8 * (c & 7) + (lane >> 3);
+    const int m = m0 + r;
+    xcol[i] = 8 * ((lane & 7) ^ (r & 7));
+    xo[i] = m < M ? (int)(((size_t)m * ldx + (size_t)pl * K + xcol[i]) * 2) : -1;
+  }
+  // this wave's weight chunks c: rows RPC c .. + RPC of its 32; lane l fills slot l % PPR of row
+  // RPC c + l / PPR with piece (l % PPR) ^ (row % PPR)
+  int wo[WC], wcol[WC];
+#pragma unroll
+  for (int c = 0; c < WC; ++c) {
+    const int rr = RPC * c + lane / PPR;
+    const int nr = n0 + wave * 32 + rr;
+    wcol[c] = PER * ((lane % PPR) ^ (rr % PPR));
+    wo[c] = nr < N ? (int)(((size_t)nr * K + wcol[c]) * WE) : -1;
+  }
+  // K block kb into a stage (past kb1 or K: out-of-range loads, which read zero and move no data,
+  // so every wave issues the same count and the waits below stay exact)
+  auto issue = [&](uint4 *stg, int kb) {
+    const int k = kb * XKB;
+    const bool in = kb < kb1;
+#pragma unroll
+    for (int i = 0; i < XCH / GWAVES; ++i) {
+      const int off = (in && xo[i] >= 0 && k + xcol[i] < K) ? xo[i] + k * 2 : BUF_OOB;
+      lds_load16(rx, stg + (GWAVES * wave + i) * WAVE, off);
+    }
+#pragma unroll
+    for (int c = 0; c < WC; ++c) {
+      const int off = (in && wo[c] >= 0 && k + wcol[c] < K) ? wo[c] + k * WE : BUF_OOB;
+      lds_load16(rw, stg + (XCH + wave * WC + c) * WAVE, off);
+    }
+  };
+  f32x16 c0 = {}, c1 = {};
+  auto compute = [&](const uint4 *stg) {
+    // all of this K block's fragments first (one wave per SIMD: nothing else hides LDS latency)
+    // weight pieces 4 g + s (bf16) or 2 g + t (int8) of row l % 32; activation piece 4 g + s of
+    // row 32 tile + l % 32 in plane 0 (hi) and 1 (lo)
+    uint4 wq[WC], xf[16];
+    const uint4 *wst = stg + (XCH + wave * WC) * WAVE;
+#pragma unroll
+    for (int c = 0; c < WC; ++c) {
+      const int pi = WC * g + c;
+      wq[c] = wst[(ln / RPC) * WAVE + (ln % RPC) * PPR + (pi ^ (ln % PPR))];
+    }
+#pragma unroll
+    for (int stp = 0; stp < 4; ++stp)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // j: (plane, m tile) = (j / 2, j % 2)
+        const int pl = j >> 1, r = 32 * (j & 1) + ln;
+        xf[4 * stp + j] = stg[(pl * 8 + (r >> 3)) * WAVE + (r & 7) * 8 + ((4 * g + stp) ^ (r & 7))];
+      }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the multiplies
+#pragma unroll
+    for (int stp = 0; stp < 4; ++stp) {
+      uint4 wv;
+      if constexpr (WC == 4) {
+        wv = wq[stp];
+      } else {
+        const uint4 &q = wq[stp >> 1];
+        wv = (stp & 1) ? i8_to_bf16x8(q.z, q.w) : i8_to_bf16x8(q.x, q.y);
+      }
+      const bf16x8 wb = as_bf16x8(wv);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 0]), wb, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 1]), wb, c1, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 2]), wb, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 3]), wb, c1, 0, 0, 0);
+    }
+  };
+  // Barrier without a memory fence: a fenced barrier would wait for every LDS-direct load in
+  // flight.  Each wave first waits for its own loads of the stage about to be read (the oldest
+  // NL of the (XST - 1) NL it has in flight); after the barrier every wave's copies of it are in
+  // LDS, and every wave is done reading the stage the next issue overwrites.
+  auto sync = [&] {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm((XST - 2) * NL));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+#pragma unroll
+  for (int i = 0; i < XST - 1; ++i) issue(ring[i], kb0 + i);
+  int cur = 0;  // stage of K block kb
+  for (int kb = kb0; kb < kb1; ++kb) {
+    sync();
+    issue(ring[cur == 0 ? XST - 1 : cur - 1], kb + XST - 1);
+    compute(ring[cur]);
+    cur = cur == XST - 1 ? 0 : cur + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // no copy may still be writing LDS at exit
+  // element i of lane l: activation row (i / 4) * 8 + g * 4 + (i % 4) (+ 32 for c1), weight row n
+  if (n >= N) return;
+  const float sc = (wscale && gridDim.z == 1) ? wscale[n] : 1.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = (i >> 2) * 8 + g * 4 + (i & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = m0 + r + 32 * h;
+      if (m >= M) continue;
+      const float v = h ? c1[i] : c0[i];
+      if (gridDim.z > 1) {
+        part[((size_t)blockIdx.z * M + m) * N + n] = v;
+      } else {
+        float *yp = Y + (size_t)m * ldy + n;
+        if (ADD)
+          *yp += v * sc;
+        else
+          *yp = v * sc;
+      }
+    }
+  }
+}
+
+// Y[m][n] (ADD: +=) (sum over the splits in order of part[s][m][n]) * wscale[n].  Grid
+// (ceil(N / BLOCK), M).
+template <bool ADD>
+__global__ __launch_bounds__(BLOCK) void k_gemm_reduce(const float *__restrict__ part, int S, int M, int N,
+                                                       const float *__restrict__ wscale, float *__restrict__ Y,
+                                                       int ldy) {
+  const int n = blockIdx.x * BLOCK + threadIdx.x, m = blockIdx.y;
+  if (n >= N) return;
+  float v = 0.f;
+  for (int s = 0; s < S; ++s) v += part[((size_t)s * M + m) * N + n];
+  if (wscale) v *= wscale[n];
+  float *yp = Y + (size_t)m * ldy + n;
+  if (ADD)
+    *yp += v;
+  else
+    *yp = v;
+}
+
 }  // namespace mk

@@ -100,6 +100,7 @@ struct moshi_state {
   // f32 for the f32 band), projection outputs, and the prefill's per-position rows
   void *gx = nullptr;
   float *gy = nullptr;
+  float *gpart = nullptr;       // split-K partial tiles of the matrix-core projections
   int grows = 0;                // rows gx / gy hold
   float *pf_x = nullptr, *pf_q = nullptr, *pf_o = nullptr;
   int32_t *pf_rows = nullptr;   // [PF_ROWS][NS] gathered inputs
@@ -293,6 +294,10 @@ void plan_weights(moshi_state *s) {
 }
 
 // Session buffers in one arena.
+// Split-K partial tiles the scratch holds (splits x tiles never exceed it).
+int gemm_part_tiles(int cus) { return 8 * cus; }
+size_t gemm_part_bytes(int cus) { return (size_t)gemm_part_tiles(cus) * mk::XN * mk::XM * sizeof(float); }
+
 moshi_status alloc_session(moshi_state *s) {
   const mk::Dims &d = s->d;
   const size_t B = d.B;
@@ -343,6 +348,7 @@ moshi_status alloc_session(moshi_state *s) {
     s->grows = (int)rows;
     req(&s->gx, rows * kmax * xelt);
     req((void **)&s->gy, rows * nmax * 4);
+    req((void **)&s->gpart, gemm_part_bytes(s->cus));
     req((void **)&s->pf_x, (size_t)PF_ROWS * d.D * 4);
     req((void **)&s->pf_q, (size_t)PF_ROWS * d.D * 4);
     req((void **)&s->pf_o, (size_t)PF_ROWS * d.D * 4);
@@ -434,6 +440,7 @@ const void *select_persistent(const moshi_config &c, int cus, size_t *lds, int *
   if (c.dep_q > mk::PQ) return nullptr;
   const int g = cus;
   if (g < c.n_heads) return nullptr;
+  if ((D | F | Dd | Fd) & 3) return nullptr;  // inputs are staged 16 bytes per lane
   const int ud = stage_passes(D), uf = stage_passes(F), udd = stage_passes(Dd), ufd = stage_passes(Fd);
   int n = 0;
   const PVariant hd128[] = {pvariant_hd128_bf16_kvf32(), pvariant_hd128_bf16_kvbf16(), pvariant_hd128_i8_kvf32()};
@@ -592,6 +599,52 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
       [&] { k_frame_end<<<nb, BLOCK, 0, st>>>(d, b, b0, temporal_only ? 1 : 0, forced, prev_parts); });
 }
 
+// Split of a wide-tile projection over K.  One block runs per CU (its LDS ring takes most of the
+// CU's LDS), so the (N / XN) x (M / XM) tiles times the splits run in rounds of `cus` blocks.  The
+// split minimises rounds x K blocks per split, plus the partial tiles' write and read (counted in
+// the same unit: one K block of every CU's weight rows) and a reduction launch; the partials must
+// fit `cap_tiles` tiles of the scratch.
+void gemm_split(int N, int K, int M, int cus, int cap_tiles, int &S, int &kbs) {
+  const int nb = ((N + mk::XN - 1) / mk::XN) * ((M + mk::XM - 1) / mk::XM);
+  const int nkb = (K + mk::XKB - 1) / mk::XKB;
+  const double step_bytes = (double)cus * mk::XN * mk::XKB * 2;
+  double best = 1e30;
+  S = 1;
+  kbs = nkb;
+  for (int want = 1; want <= std::min(nkb, 32); ++want) {
+    const int kb = (nkb + want - 1) / want, sp = (nkb + kb - 1) / kb;
+    if (sp > 1 && sp * nb > cap_tiles) break;
+    const double rounds = (double)((sp * nb + cus - 1) / cus);
+    const double cost = rounds * kb + (sp > 1 ? 2.0 * sp * M * N * 4 / step_bytes + 4.0 : 0.0);
+    if (cost < best) {
+      best = cost;
+      S = sp;
+      kbs = kb;
+    }
+  }
+}
+
+// Projection Y (ADD: +=) X W^T (times the int8 row scales) for M activation rows on the matrix
+// cores: bf16 and int8 weights on the wide LDS-shared tiles (split over K into `part` plus an
+// ordered reduction when the tiles alone do not fill the chip), float32 weights on the 32-row
+// tiles.  X is in the XPut layout with row stride ldx.
+template <typename WT, bool ADD, int TAG>
+void gemm(hipStream_t st, int cus, float *part, const WT *W, const float *scale, int N, int K,
+          const typename mk::GemmX<WT>::type *X, int ldx, int M, float *Y, int ldy) {
+  using namespace mk;
+  if constexpr (std::is_same<WT, float>::value) {
+    k_gemm<float, ADD, TAG><<<dim3((N + GN - 1) / GN, (M + GM - 1) / GM), GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M,
+                                                                                          Y, ldy);
+  } else {
+    int S = 1, kbs = 1;
+    gemm_split(N, K, M, cus, gemm_part_tiles(cus), S, kbs);
+    k_gemm_x<WT, ADD, TAG><<<dim3((N + XN - 1) / XN, (M + XM - 1) / XM, S), GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M,
+                                                                                            Y, ldy, part, kbs);
+    if (S > 1)
+      k_gemm_reduce<ADD><<<dim3((N + BLOCK - 1) / BLOCK, M), BLOCK, 0, st>>>(part, S, M, N, scale, Y, ldy);
+  }
+}
+
 // Temporal layers over `rows` activation rows x (ldx = D) on the matrix cores: one projection per
 // weight matrix for all rows.  Rows map to (conversation, position) through rm; q_rows / o_rows
 // are the rows' query and attention output buffers.
@@ -609,14 +662,12 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
   XT *X = reinterpret_cast<XT *>(s->gx);
   const int P = XPut<XT>::PLANES;  // activation planes per row (bf16: hi, lo)
   float *Y = s->gy;
-  const dim3 gm_rows(1, (rows + GM - 1) / GM);
-  auto gemm_grid = [&](int n) { return dim3((n + GN - 1) / GN, gm_rows.y); };
   const size_t f4 = sizeof(float);
   for (int l = 0; l < d.L; ++l) {
     const LayerW &lw = s->layers[l];
     run(MOSHI_STAGE_QKV, [&] {
       k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm1), d.eps, d.D, X, P * d.D, nullptr, 0);
-      k_gemm<WT, false, MOSHI_STAGE_QKV><<<gemm_grid(3 * d.D), GBLOCK, 0, st>>>(W(lw.in), s->scale(lw.in), 3 * d.D,
+      gemm<WT, false, MOSHI_STAGE_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.D,
                                                                                d.D, X, P * d.D, rows, Y, 3 * d.D);
       k_qkv_post<KT><<<rows, BLOCK, 0, st>>>(d, b, kv, Y, 3 * d.D, q_rows, l, rm);
     });
@@ -630,17 +681,16 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
     });
     run(MOSHI_STAGE_OUT_PROJ, [&] {
       k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(o_rows, d.D, nullptr, d.eps, d.D, X, P * d.D, nullptr, 0);
-      k_gemm<WT, true, MOSHI_STAGE_OUT_PROJ><<<gemm_grid(d.D), GBLOCK, 0, st>>>(W(lw.out), s->scale(lw.out), d.D, d.D,
+      gemm<WT, true, MOSHI_STAGE_OUT_PROJ>(st, s->cus, s->gpart, W(lw.out), s->scale(lw.out), d.D, d.D,
                                                                               X, P * d.D, rows, x, d.D);
     });
     run(MOSHI_STAGE_GATE_IN, [&] {
       k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm2), d.eps, d.D, X, P * d.D, nullptr, 0);
-      k_gemm<WT, false, MOSHI_STAGE_GATE_IN><<<gemm_grid(2 * d.F), GBLOCK, 0, st>>>(
-          W(lw.gin), s->scale(lw.gin), 2 * d.F, d.D, X, P * d.D, rows, Y, 2 * d.F);
+      gemm<WT, false, MOSHI_STAGE_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), 2 * d.F, d.D, X, P * d.D, rows, Y, 2 * d.F);
       k_gate_post<XT><<<dim3(rows, (d.F + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.F, d.F, X, P * d.F);
     });
     run(MOSHI_STAGE_GATE_OUT, [&] {
-      k_gemm<WT, true, MOSHI_STAGE_GATE_OUT><<<gemm_grid(d.D), GBLOCK, 0, st>>>(W(lw.gout), s->scale(lw.gout), d.D,
+      gemm<WT, true, MOSHI_STAGE_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.D,
                                                                               d.F, X, P * d.F, rows, x, d.D);
     });
   }
@@ -673,7 +723,6 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
   const int P = XPut<XT>::PLANES;  // activation planes per row (bf16: hi, lo)
   float *Y = s->gy;
   const int rows = nb;
-  auto gemm_grid = [&](int n) { return dim3((n + GN - 1) / GN, (rows + GM - 1) / GM); };
   const size_t f4 = sizeof(float);
   float *x = b.x + (size_t)b0 * d.D;
 
@@ -687,14 +736,12 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
   run(MOSHI_STAGE_TEXT_HEAD, [&] {
     k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(s->out_norm), d.eps, d.D, X, P * d.D,
                                                   b.hidden + (size_t)b0 * d.D, d.D);
-    k_gemm<WT, false, MOSHI_STAGE_TEXT_HEAD><<<gemm_grid(d.Vt), GBLOCK, 0, st>>>(
-        W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, X, P * d.D, rows, b.text_logits + (size_t)b0 * d.Vt, d.Vt);
+    gemm<WT, false, MOSHI_STAGE_TEXT_HEAD>(st, s->cus, s->gpart, W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, X, P * d.D, rows, b.text_logits + (size_t)b0 * d.Vt, d.Vt);
     k_argmax_rows<<<rows, BLOCK, 0, st>>>(b.text_logits + (size_t)b0 * d.Vt, d.Vt, d.Vt,
                                           b.am_part + (size_t)b0 * (1 + d.Q) * AM, (1 + d.Q) * AM);
   });
   run(MOSHI_STAGE_DEP_IN, [&] {
-    k_gemm<WT, false, MOSHI_STAGE_DEP_IN><<<gemm_grid(d.Q * d.Dd), GBLOCK, 0, st>>>(
-        W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, X, P * d.D, rows, b.din + (size_t)b0 * d.Q * d.Dd, d.Q * d.Dd);
+    gemm<WT, false, MOSHI_STAGE_DEP_IN>(st, s->cus, s->gpart, W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, X, P * d.D, rows, b.din + (size_t)b0 * d.Q * d.Dd, d.Q * d.Dd);
   });
   float *y = b.y + (size_t)b0 * d.Dd;
   for (int cb = 0; cb < d.Q; ++cb) {
@@ -706,33 +753,29 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
           k_dep_entry<ET, XT><<<rows, BLOCK, d.Dd * f4, st>>>(d, b, table, cb, N(lw.norm1), X, P * d.Dd, b0);
         else
           k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm1), d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
-        k_gemm<WT, false, MOSHI_STAGE_DEP_QKV><<<gemm_grid(3 * d.Dd), GBLOCK, 0, st>>>(
-            W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X, P * d.Dd, rows, Y, 3 * d.Dd);
+        gemm<WT, false, MOSHI_STAGE_DEP_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X, P * d.Dd, rows, Y, 3 * d.Dd);
         k_dep_qkv_post<<<rows, BLOCK, 0, st>>>(d, b, Y, 3 * d.Dd, j, cb, b0);
       });
       run(MOSHI_STAGE_DEP_OUT, [&] {
         with_epl(d.hdd, [&](auto e) {
           k_dep_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, j, cb, X, P * d.Dd, b0);
         });
-        k_gemm<WT, true, MOSHI_STAGE_DEP_OUT><<<gemm_grid(d.Dd), GBLOCK, 0, st>>>(W(lw.out), s->scale(lw.out), d.Dd,
+        gemm<WT, true, MOSHI_STAGE_DEP_OUT>(st, s->cus, s->gpart, W(lw.out), s->scale(lw.out), d.Dd,
                                                                                 d.Dd, X, P * d.Dd, rows, y, d.Dd);
       });
       run(MOSHI_STAGE_DEP_GATE_IN, [&] {
         k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm2), d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
-        k_gemm<WT, false, MOSHI_STAGE_DEP_GATE_IN><<<gemm_grid(2 * d.Fd), GBLOCK, 0, st>>>(
-            W(lw.gin), s->scale(lw.gin), 2 * d.Fd, d.Dd, X, P * d.Dd, rows, Y, 2 * d.Fd);
+        gemm<WT, false, MOSHI_STAGE_DEP_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), 2 * d.Fd, d.Dd, X, P * d.Dd, rows, Y, 2 * d.Fd);
         k_gate_post<XT><<<dim3(rows, (d.Fd + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.Fd, d.Fd, X, P * d.Fd);
       });
       run(MOSHI_STAGE_DEP_GATE_OUT, [&] {
-        k_gemm<WT, true, MOSHI_STAGE_DEP_GATE_OUT><<<gemm_grid(d.Dd), GBLOCK, 0, st>>>(
-            W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, X, P * d.Fd, rows, y, d.Dd);
+        gemm<WT, true, MOSHI_STAGE_DEP_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, X, P * d.Fd, rows, y, d.Dd);
       });
     }
     run(MOSHI_STAGE_DEP_HEAD, [&] {
       k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, nullptr, d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
       float *lg = b.audio_logits + (size_t)b0 * d.Q * d.Va + (size_t)cb * d.Va;
-      k_gemm<WT, false, MOSHI_STAGE_DEP_HEAD><<<gemm_grid(d.Va), GBLOCK, 0, st>>>(
-          W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, X, P * d.Dd, rows, lg, d.Q * d.Va);
+      gemm<WT, false, MOSHI_STAGE_DEP_HEAD>(st, s->cus, s->gpart, W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, X, P * d.Dd, rows, lg, d.Q * d.Va);
       k_argmax_rows<<<rows, BLOCK, 0, st>>>(lg, d.Q * d.Va, d.Va, b.am_part + ((size_t)b0 * (1 + d.Q) + 1 + cb) * AM,
                                             (1 + d.Q) * AM);
     });
@@ -1477,10 +1520,11 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
   const size_t welt = linear_elt(band), xelt = band == MOSHI_BAND_F32 ? 4 : 4;  // bf16: hi and lo planes
   if (wcnt * welt >= ((size_t)1 << 31) || xcnt * xelt >= ((size_t)1 << 31)) return MOSHI_EINVAL;
   char *dw = nullptr, *dx = nullptr;
-  float *ds = nullptr, *dy = nullptr, *stg = nullptr;
+  float *ds = nullptr, *dy = nullptr, *stg = nullptr, *dp = nullptr;
   hipStream_t st = nullptr;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   moshi_status rc = MOSHI_OK;
+  int dev = 0, cus = 0;
   auto chk = [&](hipError_t e) {
     if (e != hipSuccess && rc == MOSHI_OK) {
       fprintf(stderr, "moshi_debug_gemm: %s\n", hipGetErrorString(e));
@@ -1488,9 +1532,10 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
     }
     return rc == MOSHI_OK;
   };
-  if (chk(hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) && chk(hipMalloc(&dw, wcnt * welt)) &&
+  if (chk(hipGetDevice(&dev)) && chk(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) &&
+      chk(hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) && chk(hipMalloc(&dw, wcnt * welt)) &&
       chk(hipMalloc(&ds, (size_t)N * 4)) && chk(hipMalloc(&dx, xcnt * xelt)) &&
-      chk(hipMalloc(&dy, (size_t)M * N * 4))) {
+      chk(hipMalloc(&dy, (size_t)M * N * 4)) && chk(hipMalloc(&dp, gemm_part_bytes(cus)))) {
     if (band == MOSHI_BAND_F32) {
       chk(hipMemcpy(dw, W, wcnt * 4, hipMemcpyHostToDevice));
       chk(hipMemcpy(dx, X, xcnt * 4, hipMemcpyHostToDevice));
@@ -1514,17 +1559,17 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
       }
     }
   }
+  // the launches the frame path makes (wide tiles and K splits for bf16 and int8)
   auto launch = [&]() {
-    const dim3 grid((N + mk::GN - 1) / mk::GN, (M + mk::GM - 1) / mk::GM);
     if (band == MOSHI_BAND_F32)
-      mk::k_gemm<float, false, MOSHI_N_STAGES><<<grid, mk::GBLOCK, 0, st>>>(
-          reinterpret_cast<const float *>(dw), nullptr, N, K, reinterpret_cast<const float *>(dx), K, M, dy, N);
+      gemm<float, false, MOSHI_N_STAGES>(st, cus, dp, reinterpret_cast<const float *>(dw), nullptr, N, K,
+                                         reinterpret_cast<const float *>(dx), K, M, dy, N);
     else if (band == MOSHI_BAND_BF16)
-      mk::k_gemm<bf16_t, false, MOSHI_N_STAGES><<<grid, mk::GBLOCK, 0, st>>>(
-          reinterpret_cast<const bf16_t *>(dw), nullptr, N, K, reinterpret_cast<const bf16_t *>(dx), 2 * K, M, dy, N);
+      gemm<bf16_t, false, MOSHI_N_STAGES>(st, cus, dp, reinterpret_cast<const bf16_t *>(dw), nullptr, N, K,
+                                          reinterpret_cast<const bf16_t *>(dx), 2 * K, M, dy, N);
     else
-      mk::k_gemm<int8_t, false, MOSHI_N_STAGES><<<grid, mk::GBLOCK, 0, st>>>(
-          reinterpret_cast<const int8_t *>(dw), ds, N, K, reinterpret_cast<const bf16_t *>(dx), 2 * K, M, dy, N);
+      gemm<int8_t, false, MOSHI_N_STAGES>(st, cus, dp, reinterpret_cast<const int8_t *>(dw), ds, N, K,
+                                          reinterpret_cast<const bf16_t *>(dx), 2 * K, M, dy, N);
   };
   if (rc == MOSHI_OK) {
     launch();
@@ -1545,6 +1590,7 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
   if (e0) (void)hipEventDestroy(e0);
   if (e1) (void)hipEventDestroy(e1);
   if (stg) (void)hipFree(stg);
+  if (dp) (void)hipFree(dp);
   if (dw) (void)hipFree(dw);
   if (ds) (void)hipFree(ds);
   if (dx) (void)hipFree(dx);
