@@ -2,11 +2,14 @@
 
     python -m rq_transformer_frame_amd.profsum stats <kernel_stats.csv> [bench.json]
     python -m rq_transformer_frame_amd.profsum traffic <fetch counter_collection.csv> <write ...csv> <copy MiB>
+    python -m rq_transformer_frame_amd.profsum steps <kernel_trace.csv> <marker kernel> <steps>
 
 `stats` prints a markdown table of the per-kernel averages (stage names recovered from the kernels'
 stage tags; algorithmic GB/s when the bench JSON line of the same run is given).  `traffic` prints
 per-kernel HBM bytes per dispatch from a FETCH_SIZE run and a WRITE_SIZE run, each scaled by what
-the same counter reads for the first device-to-device copy of `copy MiB` in that run.
+the same counter reads for the first device-to-device copy of `copy MiB` in that run.  `steps`
+keeps the dispatches after the last one whose name contains `marker` (e.g. the end of a prefill)
+and prints per-stage averages and microseconds per step over `steps` steps.
 """
 from __future__ import annotations
 
@@ -24,10 +27,11 @@ def stage_of(name: str) -> str:
     """The frame stage a kernel symbol belongs to (stage tags are the last template argument)."""
     for key, stage in (("k_qkv_rope", "qkv"), ("k_attn", "attn"), ("k_dep_qkv", "dep_qkv"),
                        ("k_dep_out", "dep_out"), ("k_embed_begin", "embed"), ("k_frame_end", "frame_end"),
-                       ("k_frame_persistent", "whole frame (persistent kernel)")):
+                       ("k_frame_persistent", "whole frame (persistent kernel)"),
+                       ("k_gemm_reduce", "split-K reduction")):
         if key in name:
             return stage
-    m = re.search(r"mk::k_(?:gemv|gate|head|gemm)<[^>]*?,\s*(\d+)>", name)
+    m = re.search(r"mk::k_(?:gemv|gate|head|gemm|gemm_x)<[^>]*?,\s*(\d+)>", name)
     if m and int(m.group(1)) < len(STAGES):
         return STAGES[int(m.group(1))]
     return name.split("(")[0]
@@ -80,11 +84,30 @@ def traffic(fetch: str, write: str, copy_mib: float) -> str:
     return "\n".join(out)
 
 
+def steps(path: str, marker: str, nsteps: int) -> str:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    last = max((i for i, r in enumerate(rows) if marker in r["Kernel_Name"]), default=-1)
+    agg = collections.defaultdict(lambda: [0, 0.0])
+    for r in rows[last + 1:]:
+        st = stage_of(r["Kernel_Name"])
+        agg[st][0] += 1
+        agg[st][1] += (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    tot = sum(v[1] for v in agg.values())
+    out = [f"{len(rows) - last - 1} dispatches after the last `{marker}`, {tot / nsteps:.1f} us of kernel time per step.",
+           "", "| stage (kernel) | dispatches | avg us | us per step | share |", "|---|---|---|---|---|"]
+    for st, (n, t) in sorted(agg.items(), key=lambda x: -x[1][1]):
+        out.append(f"| {st} | {n} | {t / n:.2f} | {t / nsteps:.1f} | {100 * t / tot:.1f}% |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "stats":
         print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else None))
     elif len(sys.argv) == 5 and sys.argv[1] == "traffic":
         print(traffic(sys.argv[2], sys.argv[3], float(sys.argv[4])))
+    elif len(sys.argv) == 5 and sys.argv[1] == "steps":
+        print(steps(sys.argv[2], sys.argv[3], int(sys.argv[4])))
     else:
         print(__doc__)
         sys.exit(2)
