@@ -285,6 +285,135 @@ struct RowStream {
   }
 };
 
+// int8 weights: rows are walked in pairs, so that each input fragment read from LDS (16 floats per
+// lane and 16-byte vector) feeds both rows' products; int8 carries 16 weights per vector, and with
+// one row at a time the LDS reads (4 bytes per weight byte) and the widening share the CU with the
+// stream.  A chunk is SCH_I8 vectors per lane of both rows of the pair; two pair-chunks are in
+// flight (the same 16 KB per wave as the single-row stream).  A pair past the end of the wave's
+// rows (odd count) reads zeros for its second row and emits only the first.  Rows are emitted in
+// increasing order.
+constexpr int SCH_I8 = 4;
+
+template <>
+struct RowStream<int8_t> {
+  static constexpr int N = 16;
+  uint4 a0[SCH_I8], b0[SCH_I8], a1[SCH_I8], b1[SCH_I8];  // pair-chunk t (a: first row, b: second)
+  float sa0, sb0, sa1, sb1;
+  const int8_t *W;
+  const float *S;
+  int K, nv, nch, r0, r1, T;
+  int lp, lc;  // pair and chunk of the next load
+  int cp, cc;  // pair and chunk of the next chunk consumed
+
+  __device__ __forceinline__ void load(uint4 (&A)[SCH_I8], uint4 (&B)[SCH_I8], float &sa, float &sb) {
+    const int lane = threadIdx.x & 63;
+    const int ra = r0 + 2 * lp, rb = ra + 1;
+    const __amdgpu_buffer_rsrc_t rsa =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(W + (size_t)ra * K), (short)0, nv * 16, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rsb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(W + (size_t)rb * K), (short)0, rb < r1 ? nv * 16 : 0, BUF_DWORD3);
+    const int soff = lc * (SCH_I8 * WAVE * 16);
+#pragma unroll
+    for (int i = 0; i < SCH_I8; ++i) {
+      const u32x4b va = __builtin_amdgcn_raw_buffer_load_b128(rsa, (i * WAVE + lane) * 16, soff, BUF_NT);
+      const u32x4b vb = __builtin_amdgcn_raw_buffer_load_b128(rsb, (i * WAVE + lane) * 16, soff, BUF_NT);
+      A[i] = uint4{va[0], va[1], va[2], va[3]};
+      B[i] = uint4{vb[0], vb[1], vb[2], vb[3]};
+    }
+    if (S && lc == nch - 1) {
+      sa = S[ra];
+      sb = rb < r1 ? S[rb] : 0.f;
+    }
+    if (++lc == nch) {
+      lc = 0;
+      ++lp;
+    }
+  }
+
+  __device__ __forceinline__ void begin(const int8_t *__restrict__ W_, const float *__restrict__ S_, int K_, int r0_,
+                                        int r1_) {
+    W = W_;
+    S = S_;
+    K = K_;
+    nv = K_ / N;
+    nch = (nv + SCH_I8 * WAVE - 1) / (SCH_I8 * WAVE);
+    r0 = r0_;
+    r1 = r1_ > r0_ ? r1_ : r0_;
+    T = ((r1 - r0 + 1) / 2) * nch;
+    lp = lc = 0;
+    sa0 = sb0 = sa1 = sb1 = 1.f;
+    if (T > 0) load(a0, b0, sa0, sb0);
+    if (T > 1) load(a1, b1, sa1, sb1);
+  }
+
+  __device__ __forceinline__ static float cvt_dot(const uint4 &w, const float *xv, float acc) {
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc = fmaf((float)(int32_t)(int8_t)((d[j] >> (8 * b)) & 0xFFu), xv[4 * j + b], acc);
+    return acc;
+  }
+
+  // Consume pair-chunk (A, B) (pair cp, chunk cc); finished rows go to the epilogue.
+  template <typename Epi>
+  __device__ __forceinline__ void consume(const uint4 (&A)[SCH_I8], const uint4 (&B)[SCH_I8], float sa, float sb,
+                                          const float *__restrict__ xs, float &acca, float &accb, Epi &epi) {
+    const int lane = threadIdx.x & 63;
+    const int left = nv - cc * (SCH_I8 * WAVE);
+    const float *xp = xs + (size_t)(cc * (SCH_I8 * WAVE) + lane) * N;
+#pragma unroll
+    for (int i = 0; i < SCH_I8; ++i) {
+      if (left >= SCH_I8 * WAVE || i * WAVE + lane < left) {
+        float xv[N];
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+          const float4 q = *reinterpret_cast<const float4 *>(xp + i * WAVE * N + e);
+          xv[e] = q.x;
+          xv[e + 1] = q.y;
+          xv[e + 2] = q.z;
+          xv[e + 3] = q.w;
+        }
+        acca = cvt_dot(A[i], xv, acca);
+        accb = cvt_dot(B[i], xv, accb);
+      }
+    }
+    if (cc == nch - 1) {
+      const int ra = r0 + 2 * cp, rb = ra + 1;
+      float va = wave_sum(acca), vb = wave_sum(accb);
+      if (S) {
+        va *= sa;
+        vb *= sb;
+      }
+      epi(ra, va);
+      if (rb < r1) epi(rb, vb);
+      acca = accb = 0.f;
+      cc = 0;
+      ++cp;
+    } else {
+      ++cc;
+    }
+  }
+
+  template <typename Epi>
+  __device__ __forceinline__ void run(const float *__restrict__ xs, Epi &&epi) {
+    float acca = 0.f, accb = 0.f;
+    cp = cc = 0;
+    int t = 0;
+    for (; t + 3 < T; t += 2) {
+      consume(a0, b0, sa0, sb0, xs, acca, accb, epi);
+      load(a0, b0, sa0, sb0);
+      consume(a1, b1, sa1, sb1, xs, acca, accb, epi);
+      load(a1, b1, sa1, sb1);
+    }
+    const int rem = T - t;
+    if (rem >= 1) consume(a0, b0, sa0, sb0, xs, acca, accb, epi);
+    if (rem == 3) load(a0, b0, sa0, sb0);
+    if (rem >= 2) consume(a1, b1, sa1, sb1, xs, acca, accb, epi);
+    if (rem == 3) consume(a0, b0, sa0, sb0, xs, acca, accb, epi);
+  }
+};
+
 // Index of the calling wave in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
