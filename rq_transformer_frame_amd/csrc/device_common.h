@@ -285,21 +285,21 @@ struct RowStream {
   }
 };
 
-// int8 weights: rows are walked in pairs, so that each input fragment read from LDS (16 floats per
-// lane and 16-byte vector) feeds both rows' products; int8 carries 16 weights per vector, and with
-// one row at a time the LDS reads (4 bytes per weight byte) and the widening share the CU with the
+// bf16 and int8 weights: rows are walked in pairs, so that each input fragment read from LDS
+// (N floats per lane and 16-byte vector) feeds both rows' products; with one row at a time the
+// LDS reads (4 bytes per weight byte for int8, 2 for bf16) and the widening share the CU with the
 // stream.  A chunk is SCH_I8 vectors per lane of both rows of the pair; two pair-chunks are in
 // flight (the same 16 KB per wave as the single-row stream).  A pair past the end of the wave's
 // rows (odd count) reads zeros for its second row and emits only the first.  Rows are emitted in
 // increasing order.
 constexpr int SCH_I8 = 4;
 
-template <>
-struct RowStream<int8_t> {
-  static constexpr int N = 16;
+template <typename WT>
+struct PairStream {
+  static constexpr int N = WVec<WT>::N;
   uint4 a0[SCH_I8], b0[SCH_I8], a1[SCH_I8], b1[SCH_I8];  // pair-chunk t (a: first row, b: second)
   float sa0, sb0, sa1, sb1;
-  const int8_t *W;
+  const WT *W;
   const float *S;
   int K, nv, nch, r0, r1, T;
   int lp, lc;  // pair and chunk of the next load
@@ -330,7 +330,7 @@ struct RowStream<int8_t> {
     }
   }
 
-  __device__ __forceinline__ void begin(const int8_t *__restrict__ W_, const float *__restrict__ S_, int K_, int r0_,
+  __device__ __forceinline__ void begin(const WT *__restrict__ W_, const float *__restrict__ S_, int K_, int r0_,
                                         int r1_) {
     W = W_;
     S = S_;
@@ -347,11 +347,10 @@ struct RowStream<int8_t> {
   }
 
   __device__ __forceinline__ static float cvt_dot(const uint4 &w, const float *xv, float acc) {
-    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+    float wf[N];
+    WVec<WT>::cvt(w, wf);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int b = 0; b < 4; ++b) acc = fmaf((float)(int32_t)(int8_t)((d[j] >> (8 * b)) & 0xFFu), xv[4 * j + b], acc);
+    for (int e = 0; e < N; ++e) acc = fmaf(wf[e], xv[e], acc);
     return acc;
   }
 
@@ -413,6 +412,9 @@ struct RowStream<int8_t> {
     if (rem == 3) consume(a0, b0, sa0, sb0, xs, acca, accb, epi);
   }
 };
+
+template <> struct RowStream<int8_t> : PairStream<int8_t> {};
+template <> struct RowStream<bf16_t> : PairStream<bf16_t> {};
 
 // Index of the calling wave in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
