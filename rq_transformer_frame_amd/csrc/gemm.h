@@ -241,26 +241,27 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm(const WT *__restrict__ W, const
 
 
 // ---- wide tiles, both operands streamed through an LDS ring -------------------------------------
-// For bf16 and int8 weights.  A block owns XN = 128 weight rows (32 per wave) and XM = 64
-// activation rows; its waves do not split K.  Every K block (64 columns) of both operands goes
-// straight from memory into one stage of a ring of XST LDS stages with LDS-direct loads (no
-// registers), XST - 1 K blocks ahead of the multiply.  The activation tile (hi and lo planes) is
-// loaded once per block and read by all four waves (tiles that split K over waves reload it per
-// wave).  Each 1 KB load fills whole 128-byte row segments (8 rows of a 64-column bf16 block, or
+// For bf16 and int8 weights.  A block owns 128 NT weight rows (32 NT per wave, NT = 1 or 2) and
+// XM = 64 activation rows; its waves do not split K.  Every K block (64 columns) of both operands goes
+// straight from memory into one stage of a ring of LDS stages with LDS-direct loads (no
+// registers), as many K blocks ahead of the multiply as the LDS holds stages, minus one.  The
+// activation tile (hi and lo planes) is loaded once per block and read by all four waves (tiles
+// that split K over waves reload it per wave), and every activation fragment a wave reads from LDS
+// feeds the products of its NT 32-row weight tiles (two tiles halve the LDS reads per product but
+// halve the number of blocks: the host takes them for wide projections).  Each 1 KB load fills whole 128-byte row segments (8 rows of a 64-column bf16 block, or
 // 16 rows of int8), so every cache line is fetched by one instruction; within a row the 16-byte
 // pieces are stored XOR-swizzled by the row (piece p of row r at slot p ^ (r % slots)), so the
 // matrix-core fragment reads (lane l: row l % 32, pieces of columns 32 (l / 32) ..) hit distinct
 // banks.
 // A grid z dimension splits K: every split writes its partial tile to `part` ([split][M][N]
 // floats) and k_gemm_reduce adds the splits in order, so the result does not depend on timing.
-constexpr int XN = 128;  // weight rows per block
-constexpr int XM = 64;   // activation rows per block
-constexpr int XKB = 64;  // K block
-constexpr int XST = 5;   // LDS stages (bf16: 5 x 32 KB, the whole LDS of a CU)
+constexpr int XNMAX = 2;                // most 32-row weight tiles per wave
+constexpr int XM = 64;                  // activation rows per block
+constexpr int XKB = 64;                 // K block
+constexpr int XLDS = 160 * 1024;        // the LDS of a CU: the ring takes as many stages as fit
 
-// Weight chunks per wave and K block: bf16 one per 16-column step (8 bf16 per lane), int8 one per
-// two steps (16 int8 per lane).
-// (PER elements per 16-byte piece, PPR pieces per 64-column row, RPC rows per 1 KB chunk)
+// Weight chunks per 32 weight rows and K block: bf16 4 (8 bf16 per lane), int8 2 (16 int8 per
+// lane); PER elements per 16-byte piece, PPR pieces per 64-column row, RPC rows per 1 KB chunk.
 template <typename WT> struct XWC;
 template <> struct XWC<bf16_t> { static constexpr int N = 4, ELT = 2, PER = 8, PPR = 8, RPC = 8; };
 template <> struct XWC<int8_t> { static constexpr int N = 2, ELT = 1, PER = 16, PPR = 4, RPC = 16; };
@@ -289,21 +290,23 @@ __device__ __forceinline__ void lds_load16(i32x4 desc, const void *lds, int voff
 }
 
 // Y[m][n] (ADD: +=) sum_k X[m][k] W[n][k] (* wscale[n]), or with gridDim.z > 1 the partial sums of
-// K blocks [z * kbs, (z + 1) * kbs) into part[z][m][n].  Grid (ceil(N / XN), ceil(M / XM), splits),
+// K blocks [z * kbs, (z + 1) * kbs) into part[z][m][n].  Grid (ceil(N / (128 NT)), ceil(M / XM), splits),
 // GBLOCK threads.  X: [M][ldx] bf16 in the hi | lo layout (planes K apart); K a multiple of 16.
-template <typename WT, bool ADD, int TAG>
+template <typename WT, bool ADD, int TAG, int XNT>
 __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, const float *__restrict__ wscale, int N,
                                                    int K, const bf16_t *__restrict__ X, int ldx, int M,
                                                    float *__restrict__ Y, int ldy, float *__restrict__ part, int kbs) {
-  constexpr int WC = XWC<WT>::N, WE = XWC<WT>::ELT;
-  constexpr int XCH = 16;                      // activation chunks per stage: [step][plane][m tile]
+  constexpr int WC = XWC<WT>::N * XNT, WE = XWC<WT>::ELT;  // weight chunks per wave
+  constexpr int XCH = 16;                      // activation chunks per stage: [plane][8-row group]
   constexpr int NCH = XCH + GWAVES * WC;       // chunks per stage
   constexpr int NL = XCH / GWAVES + WC;        // loads each wave issues per K block
+  constexpr int XST = XLDS / (NCH * WAVE * 16);  // stages (bf16: 3 x 48 KB, int8: 5 x 32 KB)
+  static_assert(XST >= 3, "the ring needs at least three stages");
   __shared__ __align__(16) uint4 ring[XST][NCH * WAVE];
   const int lane = threadIdx.x & 63, wave = wave_id();
-  const int n0 = blockIdx.x * XN, m0 = blockIdx.y * XM;
+  const int n0 = blockIdx.x * (GWAVES * 32 * XNT), m0 = blockIdx.y * XM;
   const int ln = lane & 31, g = lane >> 5;
-  const int n = n0 + wave * 32 + ln;
+  const int nw = n0 + wave * 32 * XNT;  // the wave's first weight row
   const i32x4 rw = raw_desc(W, (int)((size_t)N * K * WE));
   const i32x4 rx = raw_desc(X, (int)((size_t)M * ldx * 2));
   const int nkb = (K + XKB - 1) / XKB;
@@ -320,13 +323,13 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
     xcol[i] = 8 * ((lane & 7) ^ (r & 7));
     xo[i] = m < M ? (int)(((size_t)m * ldx + (size_t)pl * K + xcol[i]) * 2) : -1;
   }
-  // this wave's weight chunks c: rows RPC c .. + RPC of its 32; lane l fills slot l % PPR of row
-  // RPC c + l / PPR with piece (l % PPR) ^ (row % PPR)
+  // this wave's weight chunks c: rows RPC c .. + RPC of its 32 XNT; lane l fills slot l % PPR of
+  // row RPC c + l / PPR with piece (l % PPR) ^ (row % PPR)
   int wo[WC], wcol[WC];
 #pragma unroll
   for (int c = 0; c < WC; ++c) {
     const int rr = RPC * c + lane / PPR;
-    const int nr = n0 + wave * 32 + rr;
+    const int nr = nw + rr;
     wcol[c] = PER * ((lane % PPR) ^ (rr % PPR));
     wo[c] = nr < N ? (int)(((size_t)nr * K + wcol[c]) * WE) : -1;
   }
@@ -346,18 +349,21 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
       lds_load16(rw, stg + (XCH + wave * WC + c) * WAVE, off);
     }
   };
-  f32x16 c0 = {}, c1 = {};
+  f32x16 acc[XNT][2] = {};  // [weight tile][activation tile]
   auto compute = [&](const uint4 *stg) {
     // all of this K block's fragments first (one wave per SIMD: nothing else hides LDS latency)
-    // weight pieces 4 g + s (bf16) or 2 g + t (int8) of row l % 32; activation piece 4 g + s of
-    // row 32 tile + l % 32 in plane 0 (hi) and 1 (lo)
-    uint4 wq[WC], xf[16];
+    // weight pieces 4 g + s (bf16) or 2 g + t (int8) of row 32 t + l % 32; activation piece
+    // 4 g + s of row 32 tile + l % 32 in plane 0 (hi) and 1 (lo)
+    constexpr int WCT = XWC<WT>::N;  // weight chunks per 32 rows
+    uint4 wq[XNT][WCT], xf[16];
     const uint4 *wst = stg + (XCH + wave * WC) * WAVE;
 #pragma unroll
-    for (int c = 0; c < WC; ++c) {
-      const int pi = WC * g + c;
-      wq[c] = wst[(ln / RPC) * WAVE + (ln % RPC) * PPR + (pi ^ (ln % PPR))];
-    }
+    for (int t = 0; t < XNT; ++t)
+#pragma unroll
+      for (int c = 0; c < WCT; ++c) {
+        const int pi = WCT * g + c, r = 32 * t + ln;
+        wq[t][c] = wst[(r / RPC) * WAVE + (r % RPC) * PPR + (pi ^ (r % PPR))];
+      }
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
@@ -367,20 +373,23 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
       }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the multiplies
 #pragma unroll
-    for (int stp = 0; stp < 4; ++stp) {
-      uint4 wv;
-      if constexpr (WC == 4) {
-        wv = wq[stp];
-      } else {
-        const uint4 &q = wq[stp >> 1];
-        wv = (stp & 1) ? i8_to_bf16x8(q.z, q.w) : i8_to_bf16x8(q.x, q.y);
+    for (int stp = 0; stp < 4; ++stp)
+#pragma unroll
+      for (int t = 0; t < XNT; ++t) {
+        uint4 wv;
+        if constexpr (WCT == 4) {
+          wv = wq[t][stp];
+        } else {
+          const uint4 &q = wq[t][stp >> 1];
+          wv = (stp & 1) ? i8_to_bf16x8(q.z, q.w) : i8_to_bf16x8(q.x, q.y);
+        }
+        const bf16x8 wb = as_bf16x8(wv);
+        f32x16 &a0 = acc[t][0], &a1 = acc[t][1];
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 0]), wb, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 1]), wb, a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 2]), wb, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 3]), wb, a1, 0, 0, 0);
       }
-      const bf16x8 wb = as_bf16x8(wv);
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 0]), wb, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 1]), wb, c1, 0, 0, 0);
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 2]), wb, c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[4 * stp + 3]), wb, c1, 0, 0, 0);
-    }
   };
   // Barrier without a memory fence: a fenced barrier would wait for every LDS-direct load in
   // flight.  Each wave first waits for its own loads of the stage about to be read (the oldest
@@ -402,25 +411,30 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
     cur = cur == XST - 1 ? 0 : cur + 1;
   }
   __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // no copy may still be writing LDS at exit
-  // element i of lane l: activation row (i / 4) * 8 + g * 4 + (i % 4) (+ 32 for c1), weight row n
-  if (n >= N) return;
-  const float sc = (wscale && gridDim.z == 1) ? wscale[n] : 1.f;
+  // element i of lane l in acc[t][h]: activation row (i / 4) * 8 + g * 4 + (i % 4) + 32 h,
+  // weight row nw + 32 t + l % 32
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = (i >> 2) * 8 + g * 4 + (i & 3);
+  for (int t = 0; t < XNT; ++t) {
+    const int n = nw + 32 * t + ln;
+    if (n >= N) continue;
+    const float sc = (wscale && gridDim.z == 1) ? wscale[n] : 1.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int m = m0 + r + 32 * h;
-      if (m >= M) continue;
-      const float v = h ? c1[i] : c0[i];
-      if (gridDim.z > 1) {
-        part[((size_t)blockIdx.z * M + m) * N + n] = v;
-      } else {
-        float *yp = Y + (size_t)m * ldy + n;
-        if (ADD)
-          *yp += v * sc;
-        else
-          *yp = v * sc;
+    for (int i = 0; i < 16; ++i) {
+      const int r = (i >> 2) * 8 + g * 4 + (i & 3);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int m = m0 + r + 32 * h;
+        if (m >= M) continue;
+        const float v = acc[t][h][i];
+        if (gridDim.z > 1) {
+          part[((size_t)blockIdx.z * M + m) * N + n] = v;
+        } else {
+          float *yp = Y + (size_t)m * ldy + n;
+          if (ADD)
+            *yp += v * sc;
+          else
+            *yp = v * sc;
+        }
       }
     }
   }

@@ -296,7 +296,9 @@ void plan_weights(moshi_state *s) {
 // Session buffers in one arena.
 // Split-K partial tiles the scratch holds (splits x tiles never exceed it).
 int gemm_part_tiles(int cus) { return 8 * cus; }
-size_t gemm_part_bytes(int cus) { return (size_t)gemm_part_tiles(cus) * mk::XN * mk::XM * sizeof(float); }
+size_t gemm_part_bytes(int cus) {
+  return (size_t)gemm_part_tiles(cus) * (mk::GWAVES * 32 * mk::XNMAX) * mk::XM * sizeof(float);
+}
 
 moshi_status alloc_session(moshi_state *s) {
   const mk::Dims &d = s->d;
@@ -599,15 +601,16 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
       [&] { k_frame_end<<<nb, BLOCK, 0, st>>>(d, b, b0, temporal_only ? 1 : 0, forced, prev_parts); });
 }
 
-// Split of a wide-tile projection over K.  One block runs per CU (its LDS ring takes most of the
-// CU's LDS), so the (N / XN) x (M / XM) tiles times the splits run in rounds of `cus` blocks.  The
+// Split of a wide-tile projection over K (tiles of xn weight rows).  One block runs per CU (its
+// LDS ring takes most of the CU's LDS), so the (N / xn) x (M / XM) tiles times the splits run in
+// rounds of `cus` blocks.  The
 // split minimises rounds x K blocks per split, plus the partial tiles' write and read (counted in
 // the same unit: one K block of every CU's weight rows) and a reduction launch; the partials must
 // fit `cap_tiles` tiles of the scratch.
-void gemm_split(int N, int K, int M, int cus, int cap_tiles, int &S, int &kbs) {
-  const int nb = ((N + mk::XN - 1) / mk::XN) * ((M + mk::XM - 1) / mk::XM);
+void gemm_split(int N, int K, int M, int xn, int cus, int cap_tiles, int &S, int &kbs) {
+  const int nb = ((N + xn - 1) / xn) * ((M + mk::XM - 1) / mk::XM);
   const int nkb = (K + mk::XKB - 1) / mk::XKB;
-  const double step_bytes = (double)cus * mk::XN * mk::XKB * 2;
+  const double step_bytes = (double)cus * xn * mk::XKB * 2;
   double best = 1e30;
   S = 1;
   kbs = nkb;
@@ -636,10 +639,18 @@ void gemm(hipStream_t st, int cus, float *part, const WT *W, const float *scale,
     k_gemm<float, ADD, TAG><<<dim3((N + GN - 1) / GN, (M + GM - 1) / GM), GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M,
                                                                                           Y, ldy);
   } else {
+    // two weight tiles per wave for the long-K projections with many output rows or many
+    // activation rows (measured faster there; slower for narrow or short-K ones, whose tiles would
+    // not fill the chip without deeper K splits)
+    const bool wide = K >= 4096 && (N >= 8192 || M >= 256);
+    const int xn = GWAVES * 32 * (wide ? 2 : 1);
     int S = 1, kbs = 1;
-    gemm_split(N, K, M, cus, gemm_part_tiles(cus), S, kbs);
-    k_gemm_x<WT, ADD, TAG><<<dim3((N + XN - 1) / XN, (M + XM - 1) / XM, S), GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M,
-                                                                                            Y, ldy, part, kbs);
+    gemm_split(N, K, M, xn, cus, gemm_part_tiles(cus), S, kbs);
+    const dim3 grid((N + xn - 1) / xn, (M + XM - 1) / XM, S);
+    if (wide)
+      k_gemm_x<WT, ADD, TAG, 2><<<grid, GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M, Y, ldy, part, kbs);
+    else
+      k_gemm_x<WT, ADD, TAG, 1><<<grid, GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M, Y, ldy, part, kbs);
     if (S > 1)
       k_gemm_reduce<ADD><<<dim3((N + BLOCK - 1) / BLOCK, M), BLOCK, 0, st>>>(part, S, M, N, scale, Y, ldy);
   }
