@@ -28,26 +28,29 @@ METRIC = "frames/s (80 ms) at B=1, Moshi-7B shape bf16; % of HBM roofline"
 
 # HBM bytes per dispatch of the dominant kernels, from two rocprofv3 --pmc runs (FETCH_SIZE,
 # WRITE_SIZE) scaled by a 256 MiB device-to-device copy in the same runs (profiles/ holds the
-# summaries and commands).  Valid only for the kernel sources they were taken on: the bench
-# reports traffic null when the sources' hash differs.
+# summaries and commands).  Valid only for the kernel sources they were taken on (the files the
+# B=1 frame kernels are compiled from): the bench reports traffic null when their hash differs.
 TRAFFIC = {
-    "sources_sha256": "476a0ea9db879c1a4a02d7786976871e9523dd82b006d1d342b4ff4691effd01",
+    "sources_sha256": "416bd6218b3d72b054719a1bb402d1aabe5154aeed78e9323ff4c8a0cb9ba3eb",
     "per_dispatch": {
-        "moshi7b_bf16_b1/frame_persistent": 14857426795,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
-        "moshi7b_bf16_b1/gate_in": 185100969,
+        "moshi7b_bf16_b1/frame_persistent": 14854117905,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
+        "moshi7b_bf16_b1/gate_in": 185052295,
     },
 }
+
+
+TRAFFIC_SOURCES = ("device_common.h", "kernels.h", "frame_persistent.h", "persistent_variants.h",
+                   "persistent_hd128_bf16_kvf32.hip")
 
 
 def sources_sha256() -> str:
     import hashlib
     h = hashlib.sha256()
     src = os.path.join(ROOT, "rq_transformer_frame_amd", "csrc")
-    for name in sorted(os.listdir(src)):
-        if name.endswith((".h", ".hip")):
-            h.update(name.encode())
-            with open(os.path.join(src, name), "rb") as f:
-                h.update(f.read())
+    for name in TRAFFIC_SOURCES:
+        h.update(name.encode())
+        with open(os.path.join(src, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
