@@ -42,6 +42,61 @@ __global__ __launch_bounds__(BLOCK) void k_rows_cvt(const float *__restrict__ sr
   }
 }
 
+// Residual projection epilogue fused with the next input conversion: Y[m] += (sum over the splits,
+// in order, of part[s][m]) * wscale, then X[m] = rms_norm(Y[m]; alpha) (or Y[m] when alpha is null)
+// in the XPut layout -- the split reduction of k_gemm_x and k_rows_cvt in one launch.  One block
+// of ADD_BLOCK threads per row, four columns per thread and pass (N a multiple of 4), the loads of
+// up to 8 splits in flight at once.  Grid (M), dynamic LDS: N floats.
+constexpr int ADD_BLOCK = 1024;
+template <typename XT>
+__global__ __launch_bounds__(ADD_BLOCK) void k_add_rows_cvt(const float *__restrict__ part, int S, int M, int N,
+                                                            const float *__restrict__ wscale, float *__restrict__ Y,
+                                                            int ldy, const float *__restrict__ alpha, float eps,
+                                                            XT *__restrict__ X, int ldx) {
+  extern __shared__ float xs[];
+  __shared__ float red[ADD_BLOCK / WAVE];
+  const int m = blockIdx.x;
+  float ss = 0.f;
+  for (int c = 4 * threadIdx.x; c < N; c += 4 * ADD_BLOCK) {
+    float4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float4 p[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        p[u] = s0 + u < S ? *reinterpret_cast<const float4 *>(part + ((size_t)(s0 + u) * M + m) * N + c)
+                          : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {  // in split order
+        v.x += p[u].x;
+        v.y += p[u].y;
+        v.z += p[u].z;
+        v.w += p[u].w;
+      }
+    }
+    float *yp = Y + (size_t)m * ldy + c;
+    const float4 y = *reinterpret_cast<const float4 *>(yp);
+    float xn[4] = {v.x, v.y, v.z, v.w};
+    const float yv[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (wscale) xn[e] *= wscale[c + e];
+      xn[e] = yv[e] + xn[e];
+      xs[c + e] = xn[e];
+      ss = fmaf(xn[e], xn[e], ss);
+    }
+    *reinterpret_cast<float4 *>(yp) = float4{xn[0], xn[1], xn[2], xn[3]};
+  }
+  float inv = 1.f;
+  if (alpha) {
+    const float tot = block_sum<ADD_BLOCK>(ss, red);
+    inv = 1.0f / sqrtf(eps + tot / (float)N);
+  }
+  for (int c = 4 * threadIdx.x; c < N; c += 4 * ADD_BLOCK)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      XPut<XT>::put(X + (size_t)m * ldx, N, c + e, alpha ? (xs[c + e] * alpha[c + e]) * inv : xs[c + e]);
+}
+
 // a4.1 after the fused q|k|v product Y[m] (3 D columns): interleaved rope on q and k at the
 // row's position (angle f_i * pos in float32, sin / cos in double), q to q_out[m], k and v to
 // the row's conversation's KV slot pos % cap of `layer` ([LM] temporal_step, rope_row).

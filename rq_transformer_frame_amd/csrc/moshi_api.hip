@@ -627,8 +627,33 @@ void gemm_split(int N, int K, int M, int xn, int cus, int cap_tiles, int &S, int
   }
 }
 
+// Launch plan of a wide-tile projection: weight tiles per wave (two for the long-K projections
+// with many output rows or many activation rows, where they measured faster; narrow or short-K
+// ones keep one, since two would halve their block count) and the K split.
+struct GemmPlan {
+  int nt, S, kbs;
+};
+GemmPlan gemm_plan(int N, int K, int M, int cus) {
+  GemmPlan g{(K >= 4096 && (N >= 8192 || M >= 256)) ? 2 : 1, 1, 1};
+  gemm_split(N, K, M, mk::GWAVES * 32 * g.nt, cus, gemm_part_tiles(cus), g.S, g.kbs);
+  return g;
+}
+
+// k_gemm_x per plan: with a split only the partial tiles (into part).
+template <typename WT, bool ADD, int TAG>
+void gemm_x_launch(hipStream_t st, const GemmPlan &g, float *part, const WT *W, const float *scale, int N, int K,
+                   const bf16_t *X, int ldx, int M, float *Y, int ldy) {
+  using namespace mk;
+  const int xn = GWAVES * 32 * g.nt;
+  const dim3 grid((N + xn - 1) / xn, (M + XM - 1) / XM, g.S);
+  if (g.nt == 2)
+    k_gemm_x<WT, ADD, TAG, 2><<<grid, GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M, Y, ldy, part, g.kbs);
+  else
+    k_gemm_x<WT, ADD, TAG, 1><<<grid, GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M, Y, ldy, part, g.kbs);
+}
+
 // Projection Y (ADD: +=) X W^T (times the int8 row scales) for M activation rows on the matrix
-// cores: bf16 and int8 weights on the wide LDS-shared tiles (split over K into `part` plus an
+// cores: bf16 and int8 weights on the wide LDS-ring tiles (split over K into `part` plus an
 // ordered reduction when the tiles alone do not fill the chip), float32 weights on the 32-row
 // tiles.  X is in the XPut layout with row stride ldx.
 template <typename WT, bool ADD, int TAG>
@@ -639,21 +664,35 @@ void gemm(hipStream_t st, int cus, float *part, const WT *W, const float *scale,
     k_gemm<float, ADD, TAG><<<dim3((N + GN - 1) / GN, (M + GM - 1) / GM), GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M,
                                                                                           Y, ldy);
   } else {
-    // two weight tiles per wave for the long-K projections with many output rows or many
-    // activation rows (measured faster there; slower for narrow or short-K ones, whose tiles would
-    // not fill the chip without deeper K splits)
-    const bool wide = K >= 4096 && (N >= 8192 || M >= 256);
-    const int xn = GWAVES * 32 * (wide ? 2 : 1);
-    int S = 1, kbs = 1;
-    gemm_split(N, K, M, xn, cus, gemm_part_tiles(cus), S, kbs);
-    const dim3 grid((N + xn - 1) / xn, (M + XM - 1) / XM, S);
-    if (wide)
-      k_gemm_x<WT, ADD, TAG, 2><<<grid, GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M, Y, ldy, part, kbs);
-    else
-      k_gemm_x<WT, ADD, TAG, 1><<<grid, GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M, Y, ldy, part, kbs);
-    if (S > 1)
-      k_gemm_reduce<ADD><<<dim3((N + BLOCK - 1) / BLOCK, M), BLOCK, 0, st>>>(part, S, M, N, scale, Y, ldy);
+    const GemmPlan g = gemm_plan(N, K, M, cus);
+    gemm_x_launch<WT, ADD, TAG>(st, g, part, W, scale, N, K, X, ldx, M, Y, ldy);
+    if (g.S > 1)
+      k_gemm_reduce<ADD><<<dim3((N + BLOCK - 1) / BLOCK, M), BLOCK, 0, st>>>(part, g.S, M, N, scale, Y, ldy);
   }
+}
+
+// Residual projection Y += X W^T followed by the next projection's input conversion
+// Xo = rms_norm(Y; alpha) (alpha null: Y as is) in the XPut layout.  With a K split the split
+// reduction, the residual add and the conversion run as one kernel (k_add_rows_cvt); without one
+// the projection adds into Y itself and k_rows_cvt converts.  Xo may be X (the projection has
+// finished reading it when the conversion runs).
+template <typename WT, int TAG>
+void gemm_add_cvt(hipStream_t st, int cus, float *part, const WT *W, const float *scale, int N, int K,
+                  const typename mk::GemmX<WT>::type *X, int ldx, int M, float *Y, int ldy, const float *alpha,
+                  float eps, typename mk::GemmX<WT>::type *Xo, int ldxo) {
+  using namespace mk;
+  typedef typename GemmX<WT>::type XT;
+  if constexpr (!std::is_same<WT, float>::value) {
+    const GemmPlan g = gemm_plan(N, K, M, cus);
+    if (g.S > 1 && N % 4 == 0 && ldy % 4 == 0) {
+      gemm_x_launch<WT, true, TAG>(st, g, part, W, scale, N, K, X, ldx, M, Y, ldy);
+      k_add_rows_cvt<XT><<<M, ADD_BLOCK, (size_t)N * sizeof(float), st>>>(part, g.S, M, N, scale, Y, ldy, alpha, eps,
+                                                                           Xo, ldxo);
+      return;
+    }
+  }
+  gemm<WT, true, TAG>(st, cus, part, W, scale, N, K, X, ldx, M, Y, ldy);
+  k_rows_cvt<XT><<<M, BLOCK, (size_t)N * sizeof(float), st>>>(Y, ldy, alpha, eps, N, Xo, ldxo, nullptr, 0);
 }
 
 // Temporal layers over `rows` activation rows x (ldx = D) on the matrix cores: one projection per
@@ -677,7 +716,9 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
   for (int l = 0; l < d.L; ++l) {
     const LayerW &lw = s->layers[l];
     run(MOSHI_STAGE_QKV, [&] {
-      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm1), d.eps, d.D, X, P * d.D, nullptr, 0);
+      // layers after the first: the previous gate_out projection left rms_norm(x; norm1) in X
+      if (l == 0)
+        k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm1), d.eps, d.D, X, P * d.D, nullptr, 0);
       gemm<WT, false, MOSHI_STAGE_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.D,
                                                                                d.D, X, P * d.D, rows, Y, 3 * d.D);
       k_qkv_post<KT><<<rows, BLOCK, 0, st>>>(d, b, kv, Y, 3 * d.D, q_rows, l, rm);
@@ -692,17 +733,22 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
     });
     run(MOSHI_STAGE_OUT_PROJ, [&] {
       k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(o_rows, d.D, nullptr, d.eps, d.D, X, P * d.D, nullptr, 0);
-      gemm<WT, true, MOSHI_STAGE_OUT_PROJ>(st, s->cus, s->gpart, W(lw.out), s->scale(lw.out), d.D, d.D,
-                                                                              X, P * d.D, rows, x, d.D);
+      // x += o . W_out^T, then X = rms_norm(x; norm2) for gate_in
+      gemm_add_cvt<WT, MOSHI_STAGE_OUT_PROJ>(st, s->cus, s->gpart, W(lw.out), s->scale(lw.out), d.D, d.D, X, P * d.D,
+                                             rows, x, d.D, N(lw.norm2), d.eps, X, P * d.D);
     });
     run(MOSHI_STAGE_GATE_IN, [&] {
-      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm2), d.eps, d.D, X, P * d.D, nullptr, 0);
-      gemm<WT, false, MOSHI_STAGE_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), 2 * d.F, d.D, X, P * d.D, rows, Y, 2 * d.F);
+      gemm<WT, false, MOSHI_STAGE_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), 2 * d.F, d.D, X, P * d.D,
+                                           rows, Y, 2 * d.F);
       k_gate_post<XT><<<dim3(rows, (d.F + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.F, d.F, X, P * d.F);
     });
     run(MOSHI_STAGE_GATE_OUT, [&] {
-      gemm<WT, true, MOSHI_STAGE_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.D,
-                                                                              d.F, X, P * d.F, rows, x, d.D);
+      if (l + 1 < d.L)  // x += a . W_gout^T, then X = rms_norm(x; next layer's norm1)
+        gemm_add_cvt<WT, MOSHI_STAGE_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.D, d.F, X,
+                                               P * d.F, rows, x, d.D, N(s->layers[l + 1].norm1), d.eps, X, P * d.D);
+      else
+        gemm<WT, true, MOSHI_STAGE_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.D, d.F, X,
+                                             P * d.F, rows, x, d.D);
     });
   }
 }
@@ -760,10 +806,9 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
     for (int j = 0; j < d.Ld; ++j) {
       const LayerW &lw = s->dlayers[j][cb];
       run(MOSHI_STAGE_DEP_QKV, [&] {
+        // layers after the first: the previous gate_out projection left rms_norm(y; norm1) in X
         if (j == 0)
           k_dep_entry<ET, XT><<<rows, BLOCK, d.Dd * f4, st>>>(d, b, table, cb, N(lw.norm1), X, P * d.Dd, b0);
-        else
-          k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm1), d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
         gemm<WT, false, MOSHI_STAGE_DEP_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X, P * d.Dd, rows, Y, 3 * d.Dd);
         k_dep_qkv_post<<<rows, BLOCK, 0, st>>>(d, b, Y, 3 * d.Dd, j, cb, b0);
       });
@@ -771,20 +816,23 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
         with_epl(d.hdd, [&](auto e) {
           k_dep_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, j, cb, X, P * d.Dd, b0);
         });
-        gemm<WT, true, MOSHI_STAGE_DEP_OUT>(st, s->cus, s->gpart, W(lw.out), s->scale(lw.out), d.Dd,
-                                                                                d.Dd, X, P * d.Dd, rows, y, d.Dd);
+        // y += o . W_out^T, then X = rms_norm(y; norm2) for gate_in
+        gemm_add_cvt<WT, MOSHI_STAGE_DEP_OUT>(st, s->cus, s->gpart, W(lw.out), s->scale(lw.out), d.Dd, d.Dd, X,
+                                              P * d.Dd, rows, y, d.Dd, N(lw.norm2), d.eps, X, P * d.Dd);
       });
       run(MOSHI_STAGE_DEP_GATE_IN, [&] {
-        k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, N(lw.norm2), d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
         gemm<WT, false, MOSHI_STAGE_DEP_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), 2 * d.Fd, d.Dd, X, P * d.Dd, rows, Y, 2 * d.Fd);
         k_gate_post<XT><<<dim3(rows, (d.Fd + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.Fd, d.Fd, X, P * d.Fd);
       });
       run(MOSHI_STAGE_DEP_GATE_OUT, [&] {
-        gemm<WT, true, MOSHI_STAGE_DEP_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd, X, P * d.Fd, rows, y, d.Dd);
+        // y += a . W_gout^T, then X = rms_norm(y; next layer's norm1), or y as is for the head
+        const float *next = j + 1 < d.Ld ? N(s->dlayers[j + 1][cb].norm1) : nullptr;
+        gemm_add_cvt<WT, MOSHI_STAGE_DEP_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd,
+                                                   X, P * d.Fd, rows, y, d.Dd, next, d.eps, X, P * d.Dd);
       });
     }
     run(MOSHI_STAGE_DEP_HEAD, [&] {
-      k_rows_cvt<XT><<<rows, BLOCK, d.Dd * f4, st>>>(y, d.Dd, nullptr, d.eps, d.Dd, X, P * d.Dd, nullptr, 0);
+      // X holds y (converted by the last gate_out projection)
       float *lg = b.audio_logits + (size_t)b0 * d.Q * d.Va + (size_t)cb * d.Va;
       gemm<WT, false, MOSHI_STAGE_DEP_HEAD>(st, s->cus, s->gpart, W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, X, P * d.Dd, rows, lg, d.Q * d.Va);
       k_argmax_rows<<<rows, BLOCK, 0, st>>>(lg, d.Q * d.Va, d.Va, b.am_part + ((size_t)b0 * (1 + d.Q) + 1 + cb) * AM,
