@@ -155,6 +155,25 @@ __global__ __launch_bounds__(BLOCK) void k_gate_post(const float *__restrict__ Y
   XPut<XT>::put(X + (size_t)m * ldx, F, j, silu(gm.x) * gm.y);
 }
 
+// The gated unit's split reduction fused with its epilogue: the sum over the splits of the
+// interleaved gate / mult columns 2j, 2j + 1 (times their int8 row scales), then
+// X[m][j] = silu(gate) * mult in the XPut layout.  Two outputs per thread.  Grid
+// (ceil(F / (2 BLOCK)), M); F even.
+template <typename XT>
+__global__ __launch_bounds__(BLOCK) void k_reduce_gate(const float *__restrict__ part, int S, int M, int F,
+                                                       const float *__restrict__ wscale, XT *__restrict__ X, int ldx) {
+  const int j = 2 * (blockIdx.x * BLOCK + threadIdx.x), m = blockIdx.y;
+  if (j >= F) return;
+  const float4 v = split_sum4(part, S, M, 2 * F, m, 2 * j);  // gate j, mult j, gate j + 1, mult j + 1
+  float g[4] = {v.x, v.y, v.z, v.w};
+  if (wscale) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] *= wscale[2 * j + e];
+  }
+  XPut<XT>::put(X + (size_t)m * ldx, F, j, silu(g[0]) * g[1]);
+  XPut<XT>::put(X + (size_t)m * ldx, F, j + 1, silu(g[2]) * g[3]);
+}
+
 // a7 / a8 greedy head: the first-wins argmax of logits row m (N values), stored as the single
 // partial part[m * stride] that the consumers of a head's token merge.
 static __global__ __launch_bounds__(BLOCK) void k_argmax_rows(const float *__restrict__ L, int ld, int N,

@@ -440,22 +440,55 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
   }
 }
 
-// Y[m][n] (ADD: +=) (sum over the splits in order of part[s][m][n]) * wscale[n].  Grid
-// (ceil(N / BLOCK), M).
+// Sum over the splits, in order, of part[s][m][c .. c + 4) (the loads of up to 8 splits in flight).
+__device__ __forceinline__ float4 split_sum4(const float *__restrict__ part, int S, int M, int N, int m, int c) {
+  float4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float4 p[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      p[u] = s0 + u < S ? *reinterpret_cast<const float4 *>(part + ((size_t)(s0 + u) * M + m) * N + c)
+                        : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      v.x += p[u].x;
+      v.y += p[u].y;
+      v.z += p[u].z;
+      v.w += p[u].w;
+    }
+  }
+  return v;
+}
+
+// Y[m][n] (ADD: +=) (sum over the splits in order of part[s][m][n]) * wscale[n], four columns per
+// thread (when N is a multiple of 4 the partial rows are 16-byte aligned and read as float4;
+// otherwise one column at a time).  Grid (ceil(N / (4 BLOCK)), M).
 template <bool ADD>
 __global__ __launch_bounds__(BLOCK) void k_gemm_reduce(const float *__restrict__ part, int S, int M, int N,
                                                        const float *__restrict__ wscale, float *__restrict__ Y,
                                                        int ldy) {
-  const int n = blockIdx.x * BLOCK + threadIdx.x, m = blockIdx.y;
-  if (n >= N) return;
-  float v = 0.f;
-  for (int s = 0; s < S; ++s) v += part[((size_t)s * M + m) * N + n];
-  if (wscale) v *= wscale[n];
-  float *yp = Y + (size_t)m * ldy + n;
-  if (ADD)
-    *yp += v;
-  else
-    *yp = v;
+  const int c = 4 * (blockIdx.x * BLOCK + threadIdx.x), m = blockIdx.y;
+  if (c >= N) return;
+  float r[4] = {0.f, 0.f, 0.f, 0.f};
+  const int ne = min(4, N - c);
+  if ((N & 3) == 0) {
+    const float4 v = split_sum4(part, S, M, N, m, c);
+    r[0] = v.x;
+    r[1] = v.y;
+    r[2] = v.z;
+    r[3] = v.w;
+  } else {
+    for (int s = 0; s < S; ++s)
+      for (int e = 0; e < ne; ++e) r[e] += part[((size_t)s * M + m) * N + c + e];
+  }
+  float *yp = Y + (size_t)m * ldy + c;
+  for (int e = 0; e < ne; ++e) {
+    if (wscale) r[e] *= wscale[c + e];
+    if (ADD)
+      yp[e] += r[e];
+    else
+      yp[e] = r[e];
+  }
 }
 
 }  // namespace mk

@@ -667,8 +667,29 @@ void gemm(hipStream_t st, int cus, float *part, const WT *W, const float *scale,
     const GemmPlan g = gemm_plan(N, K, M, cus);
     gemm_x_launch<WT, ADD, TAG>(st, g, part, W, scale, N, K, X, ldx, M, Y, ldy);
     if (g.S > 1)
-      k_gemm_reduce<ADD><<<dim3((N + BLOCK - 1) / BLOCK, M), BLOCK, 0, st>>>(part, g.S, M, N, scale, Y, ldy);
+      k_gemm_reduce<ADD><<<dim3((N + 4 * BLOCK - 1) / (4 * BLOCK), M), BLOCK, 0, st>>>(part, g.S, M, N, scale, Y, ldy);
   }
+}
+
+// Gated unit's first projection: Y = X W^T over the 2 F interleaved gate / mult rows, then
+// Xo[m][j] = silu(Y[m][2j]) * Y[m][2j + 1] in the XPut layout.  With a K split the split reduction
+// and the epilogue are one kernel (k_reduce_gate); without one, k_gate_post reads Y.
+template <typename WT, int TAG>
+void gemm_gate(hipStream_t st, int cus, float *part, const WT *W, const float *scale, int F, int K,
+               const typename mk::GemmX<WT>::type *X, int ldx, int M, float *Y, typename mk::GemmX<WT>::type *Xo,
+               int ldxo) {
+  using namespace mk;
+  typedef typename GemmX<WT>::type XT;
+  if constexpr (!std::is_same<WT, float>::value) {
+    const GemmPlan g = gemm_plan(2 * F, K, M, cus);
+    if (g.S > 1 && F % 2 == 0 && ldxo % 2 == 0) {
+      gemm_x_launch<WT, false, TAG>(st, g, part, W, scale, 2 * F, K, X, ldx, M, Y, 2 * F);
+      k_reduce_gate<XT><<<dim3((F + 2 * BLOCK - 1) / (2 * BLOCK), M), BLOCK, 0, st>>>(part, g.S, M, F, scale, Xo, ldxo);
+      return;
+    }
+  }
+  gemm<WT, false, TAG>(st, cus, part, W, scale, 2 * F, K, X, ldx, M, Y, 2 * F);
+  k_gate_post<XT><<<dim3(M, (F + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * F, F, Xo, ldxo);
 }
 
 // Residual projection Y += X W^T followed by the next projection's input conversion
@@ -738,9 +759,8 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
                                              rows, x, d.D, N(lw.norm2), d.eps, X, P * d.D);
     });
     run(MOSHI_STAGE_GATE_IN, [&] {
-      gemm<WT, false, MOSHI_STAGE_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), 2 * d.F, d.D, X, P * d.D,
-                                           rows, Y, 2 * d.F);
-      k_gate_post<XT><<<dim3(rows, (d.F + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.F, d.F, X, P * d.F);
+      gemm_gate<WT, MOSHI_STAGE_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), d.F, d.D, X, P * d.D, rows,
+                                         Y, X, P * d.F);
     });
     run(MOSHI_STAGE_GATE_OUT, [&] {
       if (l + 1 < d.L)  // x += a . W_gout^T, then X = rms_norm(x; next layer's norm1)
@@ -821,8 +841,8 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
                                               P * d.Dd, rows, y, d.Dd, N(lw.norm2), d.eps, X, P * d.Dd);
       });
       run(MOSHI_STAGE_DEP_GATE_IN, [&] {
-        gemm<WT, false, MOSHI_STAGE_DEP_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), 2 * d.Fd, d.Dd, X, P * d.Dd, rows, Y, 2 * d.Fd);
-        k_gate_post<XT><<<dim3(rows, (d.Fd + BLOCK - 1) / BLOCK), BLOCK, 0, st>>>(Y, 2 * d.Fd, d.Fd, X, P * d.Fd);
+        gemm_gate<WT, MOSHI_STAGE_DEP_GATE_IN>(st, s->cus, s->gpart, W(lw.gin), s->scale(lw.gin), d.Fd, d.Dd, X,
+                                               P * d.Dd, rows, Y, X, P * d.Fd);
       });
       run(MOSHI_STAGE_DEP_GATE_OUT, [&] {
         // y += a . W_gout^T, then X = rms_norm(y; next layer's norm1), or y as is for the head
