@@ -134,6 +134,35 @@ __device__ __forceinline__ void stage2_sys(const float *src1, int K1, float *dst
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
+// Temporal attention: a block (one head, one position split) walks its positions in steps of
+// PWAVES * 4 and issues the cache loads of ATTN_U steps at once; a split takes P_ATTN_CHUNK
+// positions (one batch of loads per wave) before another block is used.
+constexpr int ATTN_U = 2;
+constexpr int P_ATTN_CHUNK = ATTN_U * PWAVES * 4;
+
+// N consecutive cache elements as floats (N a multiple of 4; float rows 16-byte aligned, bf16
+// rows 8-byte aligned).
+template <int N> __device__ __forceinline__ void ld_row(const float *p, float *o) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    const float4 t = *reinterpret_cast<const float4 *>(p + i);
+    o[i] = t.x;
+    o[i + 1] = t.y;
+    o[i + 2] = t.z;
+    o[i + 3] = t.w;
+  }
+}
+template <int N> __device__ __forceinline__ void ld_row(const bf16_t *p, float *o) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    const uint2 t = *reinterpret_cast<const uint2 *>(p + i);
+    o[i] = __uint_as_float(t.x << 16);
+    o[i + 1] = __uint_as_float(t.x & 0xffff0000u);
+    o[i + 2] = __uint_as_float(t.y << 16);
+    o[i + 3] = __uint_as_float(t.y & 0xffff0000u);
+  }
+}
+
 // ---- phase completion ------------------------------------------------------------------------
 // Every block owns one 32-bit flag (packed, so a waiting wave reads them all with a few loads in
 // one round trip).  Arriving at phase p of the frame with serial number `serial` stores the tag
@@ -370,9 +399,9 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
     // attention: block bi < H * S takes head bi % H, split bi / H
     {
       const int n = (int)(pos + 1 < (int64_t)d.C ? pos + 1 : (int64_t)d.C);
-      // splits: enough for ATTN_MIN_CHUNK positions each, at most ATTN_MAX_S, and every (head,
+      // splits: enough for P_ATTN_CHUNK positions each, at most ATTN_MAX_S, and every (head,
       // split) pair needs a block of its own (the grid holds at least H blocks)
-      const int S = min(min(ATTN_MAX_S, (int)gridDim.x / d.H), max(1, (n + ATTN_MIN_CHUNK - 1) / ATTN_MIN_CHUNK));
+      const int S = min(min(ATTN_MAX_S, (int)gridDim.x / d.H), max(1, (n + P_ATTN_CHUNK - 1) / P_ATTN_CHUNK));
       const int bi = blockIdx.x;
       if (bi < d.H * S) {
         constexpr int EPL = HD / 16;
@@ -397,20 +426,27 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         const float scale = 1.0f / sqrtf((float)HD);
         const size_t base = ((size_t)l * d.H + h) * (size_t)d.cap * HD;
         const KT *kb = kc + base, *vb = vc + base;
-        for (int jb = j0 + wave * 4; jb < j1; jb += PWAVES * 4) {
-          const int j = jb + g;
-          const bool ok = j < j1;
-          float dot = 0.f;
-          if (ok) {
-            const KT *kp = kb + (size_t)j * HD + sub * EPL;
+        // a wave takes positions jb + g, jb stepping by PWAVES * 4; the loads of ATTN_U steps are
+        // issued together (indexes past the split clamp to its last position, results discarded)
+        constexpr int STEP = ATTN_U * PWAVES * 4;
+        const int jl = j1 > j0 ? j1 - 1 : 0;
+        for (int jb0 = j0 + wave * 4; jb0 < j1; jb0 += STEP) {
+          float kr[ATTN_U][EPL];
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], to_f(kp[i]), dot);
+          for (int u = 0; u < ATTN_U; ++u)
+            ld_row<EPL>(kb + (size_t)min(jb0 + u * PWAVES * 4 + g, jl) * HD + sub * EPL, kr[u]);
+#pragma unroll
+          for (int u = 0; u < ATTN_U; ++u) {
+            const int j = jb0 + u * PWAVES * 4 + g;
+            float dot = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kr[u][i], dot);
+            dot += __shfl_xor(dot, 8, WAVE);
+            dot += __shfl_xor(dot, 4, WAVE);
+            dot += __shfl_xor(dot, 2, WAVE);
+            dot += __shfl_xor(dot, 1, WAVE);
+            if (j < j1 && sub == 0) sc[j - j0] = dot * scale;
           }
-          dot += __shfl_xor(dot, 8, WAVE);
-          dot += __shfl_xor(dot, 4, WAVE);
-          dot += __shfl_xor(dot, 2, WAVE);
-          dot += __shfl_xor(dot, 1, WAVE);
-          if (ok && sub == 0) sc[j - j0] = dot * scale;
         }
         __syncthreads();
         float m = -INFINITY;
@@ -426,13 +462,17 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         float op[EPL];
 #pragma unroll
         for (int i = 0; i < EPL; ++i) op[i] = 0.f;
-        for (int jb = j0 + wave * 4; jb < j1; jb += PWAVES * 4) {
-          const int j = jb + g;
-          if (j < j1) {
-            const float e = sc[j - j0];
-            const KT *vp = vb + (size_t)j * HD + sub * EPL;
+        for (int jb0 = j0 + wave * 4; jb0 < j1; jb0 += STEP) {
+          float vr[ATTN_U][EPL];
 #pragma unroll
-            for (int i = 0; i < EPL; ++i) op[i] = fmaf(e, to_f(vp[i]), op[i]);
+          for (int u = 0; u < ATTN_U; ++u)
+            ld_row<EPL>(vb + (size_t)min(jb0 + u * PWAVES * 4 + g, jl) * HD + sub * EPL, vr[u]);
+#pragma unroll
+          for (int u = 0; u < ATTN_U; ++u) {
+            const int j = jb0 + u * PWAVES * 4 + g;
+            const float e = j < j1 ? sc[j - j0] : 0.f;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) op[i] = fmaf(e, vr[u][i], op[i]);
           }
         }
 #pragma unroll

@@ -460,9 +460,9 @@ const void *select_persistent(const moshi_config &c, int cus, size_t *lds, int *
     if (!pick && v[i].ud == 1 && v[i].uf == 1 && v[i].udd >= udd && v[i].ufd == 1) pick = &v[i];
   }
   if (!pick) return nullptr;
-  // attention scores of one split: at most max(ATTN_MIN_CHUNK, ceil(C / most splits)) positions
+  // attention scores of one split: at most max(P_ATTN_CHUNK, ceil(C / most splits)) positions
   const int smax = std::min(mk::ATTN_MAX_S, g / c.n_heads);
-  const size_t chunk = std::max(mk::ATTN_MIN_CHUNK, (c.context + smax - 1) / smax);
+  const size_t chunk = std::max(mk::P_ATTN_CHUNK, (c.context + smax - 1) / smax);
   const size_t fl = std::max({(size_t)2 * D, (size_t)F + D, (size_t)2 * Dd, (size_t)Fd + Dd, chunk,
                               (size_t)mk::ATTN_MAX_S * (hd + 2) + mk::ATTN_MAX_S});
   *lds = fl * 4;
