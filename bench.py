@@ -31,7 +31,7 @@ METRIC = "frames/s (80 ms) at B=1, Moshi-7B shape bf16; % of HBM roofline"
 # summaries and commands).  Valid only for the kernel sources they were taken on (the files the
 # B=1 frame kernels are compiled from): the bench reports traffic null when their hash differs.
 TRAFFIC = {
-    "sources_sha256": "2b5f042e322cf71d6c2acc4a0402d8a7dcedc5bb729f580b794d79277355ef19",
+    "sources_sha256": "62cf8973abd62ca88913719c75f749b5b13374627be295a96eb9db6d3b01d2bd",
     "per_dispatch": {
         "moshi7b_bf16_b1/frame_persistent": 14854028565,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
         "moshi7b_bf16_b1/gate_in": 185063646,

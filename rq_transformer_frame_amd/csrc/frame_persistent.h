@@ -140,29 +140,6 @@ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 constexpr int ATTN_U = 2;
 constexpr int P_ATTN_CHUNK = ATTN_U * PWAVES * 4;
 
-// N consecutive cache elements as floats (N a multiple of 4; float rows 16-byte aligned, bf16
-// rows 8-byte aligned).
-template <int N> __device__ __forceinline__ void ld_row(const float *p, float *o) {
-#pragma unroll
-  for (int i = 0; i < N; i += 4) {
-    const float4 t = *reinterpret_cast<const float4 *>(p + i);
-    o[i] = t.x;
-    o[i + 1] = t.y;
-    o[i + 2] = t.z;
-    o[i + 3] = t.w;
-  }
-}
-template <int N> __device__ __forceinline__ void ld_row(const bf16_t *p, float *o) {
-#pragma unroll
-  for (int i = 0; i < N; i += 4) {
-    const uint2 t = *reinterpret_cast<const uint2 *>(p + i);
-    o[i] = __uint_as_float(t.x << 16);
-    o[i + 1] = __uint_as_float(t.x & 0xffff0000u);
-    o[i + 2] = __uint_as_float(t.y << 16);
-    o[i + 3] = __uint_as_float(t.y & 0xffff0000u);
-  }
-}
-
 // ---- phase completion ------------------------------------------------------------------------
 // Every block owns one 32-bit flag (packed, so a waiting wave reads them all with a few loads in
 // one round trip).  Arriving at phase p of the frame with serial number `serial` stores the tag

@@ -209,6 +209,33 @@ struct AttnQ {
   int64_t pos0;
 };
 
+// N consecutive cache elements as floats (N a multiple of 4; float rows 16-byte aligned, bf16
+// rows 8-byte aligned).
+template <int N> __device__ __forceinline__ void ld_row(const float *p, float *o) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    const float4 t = *reinterpret_cast<const float4 *>(p + i);
+    o[i] = t.x;
+    o[i + 1] = t.y;
+    o[i + 2] = t.z;
+    o[i + 3] = t.w;
+  }
+}
+template <int N> __device__ __forceinline__ void ld_row(const bf16_t *p, float *o) {
+#pragma unroll
+  for (int i = 0; i < N; i += 4) {
+    const uint2 t = *reinterpret_cast<const uint2 *>(p + i);
+    o[i] = __uint_as_float(t.x << 16);
+    o[i + 1] = __uint_as_float(t.x & 0xffff0000u);
+    o[i + 2] = __uint_as_float(t.y << 16);
+    o[i + 3] = __uint_as_float(t.y & 0xffff0000u);
+  }
+}
+
+// k_attn: a wave takes positions jb + g with jb stepping by NWAVES * 4 and issues the cache loads
+// of ATTN_KU steps at once (one split of ATTN_MIN_CHUNK positions is one batch of loads).
+constexpr int ATTN_KU = ATTN_MIN_CHUNK / (NWAVES * 4);
+
 template <typename KT, int HD>
 __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int layer, int b0, AttnQ aq) {
   extern __shared__ float sc[];
@@ -239,20 +266,27 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   const size_t base = (((size_t)b * d.L + layer) * d.H + h) * (size_t)d.cap * HD;
   const KT *kb = kv.k + base, *vb = kv.v + base;
 
-  for (int jb = j0 + wave * 4; jb < j1; jb += NWAVES * 4) {
-    const int j = jb + g;
-    const bool ok = j < j1;
-    float dot = 0.f;
-    if (ok) {
-      const KT *kp = kb + (size_t)j * HD + sub * EPL;
+  // indexes past the split clamp to its last position (results discarded), so the loads of a
+  // batch carry no branch
+  constexpr int STEP = ATTN_KU * NWAVES * 4;
+  const int jl = j1 > j0 ? j1 - 1 : 0;
+  for (int jb0 = j0 + wave * 4; jb0 < j1; jb0 += STEP) {
+    float kr[ATTN_KU][EPL];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], to_f(kp[i]), dot);
+    for (int u = 0; u < ATTN_KU; ++u)
+      ld_row<EPL>(kb + (size_t)min(jb0 + u * NWAVES * 4 + g, jl) * HD + sub * EPL, kr[u]);
+#pragma unroll
+    for (int u = 0; u < ATTN_KU; ++u) {
+      const int j = jb0 + u * NWAVES * 4 + g;
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kr[u][i], dot);
+      dot += __shfl_xor(dot, 8, WAVE);
+      dot += __shfl_xor(dot, 4, WAVE);
+      dot += __shfl_xor(dot, 2, WAVE);
+      dot += __shfl_xor(dot, 1, WAVE);
+      if (j < j1 && sub == 0) sc[j - j0] = dot * scale;
     }
-    dot += __shfl_xor(dot, 8, WAVE);
-    dot += __shfl_xor(dot, 4, WAVE);
-    dot += __shfl_xor(dot, 2, WAVE);
-    dot += __shfl_xor(dot, 1, WAVE);
-    if (ok && sub == 0) sc[j - j0] = dot * scale;
   }
   __syncthreads();
   float m = -INFINITY;
@@ -269,13 +303,17 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   float op[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) op[i] = 0.f;
-  for (int jb = j0 + wave * 4; jb < j1; jb += NWAVES * 4) {
-    const int j = jb + g;
-    if (j < j1) {
-      const float e = sc[j - j0];
-      const KT *vp = vb + (size_t)j * HD + sub * EPL;
+  for (int jb0 = j0 + wave * 4; jb0 < j1; jb0 += STEP) {
+    float vr[ATTN_KU][EPL];
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) op[i] = fmaf(e, to_f(vp[i]), op[i]);
+    for (int u = 0; u < ATTN_KU; ++u)
+      ld_row<EPL>(vb + (size_t)min(jb0 + u * NWAVES * 4 + g, jl) * HD + sub * EPL, vr[u]);
+#pragma unroll
+    for (int u = 0; u < ATTN_KU; ++u) {
+      const int j = jb0 + u * NWAVES * 4 + g;
+      const float e = j < j1 ? sc[j - j0] : 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) op[i] = fmaf(e, vr[u][i], op[i]);
     }
   }
 #pragma unroll
