@@ -97,18 +97,24 @@ __global__ __launch_bounds__(ADD_BLOCK) void k_add_rows_cvt(const float *__restr
       XPut<XT>::put(X + (size_t)m * ldx, N, c + e, alpha ? (xs[c + e] * alpha[c + e]) * inv : xs[c + e]);
 }
 
-// a4.1 after the fused q|k|v product Y[m] (3 D columns): interleaved rope on q and k at the
-// row's position (angle f_i * pos in float32, sin / cos in double), q to q_out[m], k and v to
-// the row's conversation's KV slot pos % cap of `layer` ([LM] temporal_step, rope_row).
+// a4.1 after the fused q|k|v product, one block per (head h, row m).  The head's q, k and v
+// columns (c = part * D + h * hd + e) are the sum over the S splits, in order, of
+// part[s][m][c] (row length 3 D), times the int8 row scales when wscale is set; with S = 1 and no
+// scales `part` is the product itself.  Then interleaved rope on q and k at the row's position
+// (angle f_i * pos in float32, sin / cos in double), q to q_out[m], k and v to the row's
+// conversation's KV slot pos % cap of `layer` ([LM] temporal_step, rope_row).  Four columns (two
+// rope pairs) per thread.  Grid (H, rows).
+constexpr int QKV_BLOCK = 128;
 template <typename KT>
-__global__ __launch_bounds__(BLOCK) void k_qkv_post(Dims d, Bufs s, KV<KT> kv, const float *__restrict__ Y, int ldy,
-                                                    float *__restrict__ q_out, int layer, RowMap rm) {
+__global__ __launch_bounds__(QKV_BLOCK) void k_qkv_post(Dims d, Bufs s, KV<KT> kv, const float *__restrict__ part,
+                                                        int S, int M, const float *__restrict__ wscale,
+                                                        float *__restrict__ q_out, int layer, RowMap rm) {
   __shared__ float rcs[256];  // cos, sin of pair i at [2i], [2i + 1] (head dim <= 256)
-  const int m = blockIdx.x;
+  const int h = blockIdx.x, m = blockIdx.y;
   const int conv = rm.conv_of(m);
   const int64_t pos = rm.pos_of(s, m);
   const int slot = (int)(pos % d.cap);
-  for (int i = threadIdx.x; i < d.hd / 2; i += BLOCK) {
+  for (int i = threadIdx.x; i < d.hd / 2; i += QKV_BLOCK) {
     const float ang = s.rope_freq[i] * (float)pos;
     double sd, cd;
     sincos((double)ang, &sd, &cd);
@@ -116,28 +122,33 @@ __global__ __launch_bounds__(BLOCK) void k_qkv_post(Dims d, Bufs s, KV<KT> kv, c
     rcs[2 * i + 1] = (float)sd;
   }
   __syncthreads();
-  const float *y = Y + (size_t)m * ldy;
-  for (int p = threadIdx.x; p < 3 * d.D / 2; p += BLOCK) {
-    const int r0 = 2 * p;
-    float v0 = y[r0], v1 = y[r0 + 1];
-    const int part = r0 / d.D;  // 0 q, 1 k, 2 v
-    const int rr = r0 - part * d.D;
-    const int h = rr / d.hd, e = rr - h * d.hd;
-    if (part < 2) {
-      const float cs = rcs[e], sn = rcs[e + 1];
-      const float a0 = v0 * cs - v1 * sn;
-      const float a1 = v0 * sn + v1 * cs;
-      v0 = a0;
-      v1 = a1;
+  const int N = 3 * d.D, per = d.hd / 4;
+  for (int t = threadIdx.x; t < 3 * per; t += QKV_BLOCK) {
+    const int pt = t / per, e = 4 * (t - pt * per);  // 0 q, 1 k, 2 v; element of the head
+    const int c = pt * d.D + h * d.hd + e;
+    const float4 v4 = split_sum4(part, S, M, N, m, c);
+    float r[4] = {v4.x, v4.y, v4.z, v4.w};
+    if (wscale) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) r[k] *= wscale[c + k];
     }
-    if (part == 0) {
-      q_out[(size_t)m * d.D + rr] = v0;
-      q_out[(size_t)m * d.D + rr + 1] = v1;
+    if (pt < 2) {
+#pragma unroll
+      for (int k = 0; k < 4; k += 2) {
+        const float cs = rcs[e + k], sn = rcs[e + k + 1];
+        const float a0 = r[k] * cs - r[k + 1] * sn;
+        const float a1 = r[k] * sn + r[k + 1] * cs;
+        r[k] = a0;
+        r[k + 1] = a1;
+      }
+    }
+    if (pt == 0) {
+      *reinterpret_cast<float4 *>(q_out + (size_t)m * d.D + h * d.hd + e) = float4{r[0], r[1], r[2], r[3]};
     } else {
-      KT *cache = part == 1 ? kv.k : kv.v;
+      KT *cache = pt == 1 ? kv.k : kv.v;
       const size_t idx = ((((size_t)conv * d.L + layer) * d.H + h) * d.cap + slot) * d.hd + e;
-      cache[idx] = from_f<KT>(v0);
-      cache[idx + 1] = from_f<KT>(v1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cache[idx + k] = from_f<KT>(r[k]);
     }
   }
 }

@@ -740,9 +740,25 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
       // layers after the first: the previous gate_out projection left rms_norm(x; norm1) in X
       if (l == 0)
         k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(lw.norm1), d.eps, d.D, X, P * d.D, nullptr, 0);
-      gemm<WT, false, MOSHI_STAGE_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.D,
-                                                                               d.D, X, P * d.D, rows, Y, 3 * d.D);
-      k_qkv_post<KT><<<rows, BLOCK, 0, st>>>(d, b, kv, Y, 3 * d.D, q_rows, l, rm);
+      // with a K split the split reduction runs inside the rope / KV-append kernel
+      const float *qsrc = Y, *qscale = nullptr;
+      int qS = 1;
+      bool split = false;
+      if constexpr (!std::is_same<WT, float>::value) {
+        const GemmPlan g = gemm_plan(3 * d.D, d.D, rows, s->cus);
+        if (g.S > 1) {
+          gemm_x_launch<WT, false, MOSHI_STAGE_QKV>(st, g, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.D, d.D, X,
+                                                     P * d.D, rows, Y, 3 * d.D);
+          qsrc = s->gpart;
+          qS = g.S;
+          qscale = s->scale(lw.in);
+          split = true;
+        }
+      }
+      if (!split)
+        gemm<WT, false, MOSHI_STAGE_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.D, d.D, X, P * d.D,
+                                         rows, Y, 3 * d.D);
+      k_qkv_post<KT><<<dim3(d.H, rows), QKV_BLOCK, 0, st>>>(d, b, kv, qsrc, qS, rows, qscale, q_rows, l, rm);
     });
     run(MOSHI_STAGE_ATTN, [&] {
       const int chunk = (d.cap + attn_splits - 1) / attn_splits;

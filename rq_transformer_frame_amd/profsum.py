@@ -24,14 +24,16 @@ STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head"
 
 
 def stage_of(name: str) -> str:
-    """The frame stage a kernel symbol belongs to (stage tags are the last template argument)."""
+    """The frame stage a kernel symbol belongs to (from its stage tag template argument)."""
     for key, stage in (("k_qkv_rope", "qkv"), ("k_attn", "attn"), ("k_dep_qkv", "dep_qkv"),
                        ("k_dep_out", "dep_out"), ("k_embed_begin", "embed"), ("k_frame_end", "frame_end"),
                        ("k_frame_persistent", "whole frame (persistent kernel)"),
                        ("k_gemm_reduce", "split-K reduction")):
         if key in name:
             return stage
-    m = re.search(r"mk::k_(?:gemv|gate|head|gemm|gemm_x)<[^>]*?,\s*(\d+)>", name)
+    # k_gemm_x<weight type, add, stage, activation tiles>: the stage is the third argument
+    m = re.search(r"mk::k_gemm_x<[^,>]+,\s*(?:true|false),\s*(\d+),\s*\d+>", name) or \
+        re.search(r"mk::k_(?:gemv|gate|head|gemm)<[^>]*?,\s*(\d+)>", name)
     if m and int(m.group(1)) < len(STAGES):
         return STAGES[int(m.group(1))]
     return name.split("(")[0]
