@@ -146,7 +146,7 @@ __global__ __launch_bounds__(QKV_BLOCK) void k_qkv_post(Dims d, Bufs s, KV<KT> k
       *reinterpret_cast<float4 *>(q_out + (size_t)m * d.D + h * d.hd + e) = float4{r[0], r[1], r[2], r[3]};
     } else {
       KT *cache = pt == 1 ? kv.k : kv.v;
-      const size_t idx = ((((size_t)conv * d.L + layer) * d.H + h) * d.cap + slot) * d.hd + e;
+      const size_t idx = kv_index(d, conv, layer, slot, h, e);
 #pragma unroll
       for (int k = 0; k < 4; ++k) cache[idx + k] = from_f<KT>(r[k]);
     }

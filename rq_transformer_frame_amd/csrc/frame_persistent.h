@@ -365,7 +365,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
                      (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32));
         } else {
           KT *cache = part == 1 ? kc : vc;
-          st_sys_pair<KT>(cache + ((((size_t)l * d.H + h) * d.cap + slot) * HD + e), v0, v1);
+          st_sys_pair<KT>(cache + kv_index(d, 0, l, slot, h, e), v0, v1);
         }
       });
     }
@@ -401,7 +401,8 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
           }
         }
         const float scale = 1.0f / sqrtf((float)HD);
-        const size_t base = ((size_t)l * d.H + h) * (size_t)d.cap * HD;
+        const size_t base = kv_index(d, 0, l, 0, h, 0);
+        const int PS = d.H * HD;  // elements from one cached position to the next
         const KT *kb = kc + base, *vb = vc + base;
         // a wave takes positions jb + g, jb stepping by PWAVES * 4; the loads of ATTN_U steps are
         // issued together (indexes past the split clamp to its last position, results discarded)
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
           float kr[ATTN_U][EPL];
 #pragma unroll
           for (int u = 0; u < ATTN_U; ++u)
-            ld_row<EPL>(kb + (size_t)min(jb0 + u * PWAVES * 4 + g, jl) * HD + sub * EPL, kr[u]);
+            ld_row<EPL>(kb + (size_t)min(jb0 + u * PWAVES * 4 + g, jl) * PS + sub * EPL, kr[u]);
 #pragma unroll
           for (int u = 0; u < ATTN_U; ++u) {
             const int j = jb0 + u * PWAVES * 4 + g;
@@ -443,7 +444,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
           float vr[ATTN_U][EPL];
 #pragma unroll
           for (int u = 0; u < ATTN_U; ++u)
-            ld_row<EPL>(vb + (size_t)min(jb0 + u * PWAVES * 4 + g, jl) * HD + sub * EPL, vr[u]);
+            ld_row<EPL>(vb + (size_t)min(jb0 + u * PWAVES * 4 + g, jl) * PS + sub * EPL, vr[u]);
 #pragma unroll
           for (int u = 0; u < ATTN_U; ++u) {
             const int j = jb0 + u * PWAVES * 4 + g;

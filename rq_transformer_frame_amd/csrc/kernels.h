@@ -54,9 +54,16 @@ struct Bufs {
   float *rope_freq;     // [hd/2]
 };
 
+// Element e of head h at cache slot `slot` of conversation b's layer: [B][L][cap][H][hd], so the
+// cached positions of one conversation's layer are one contiguous run (every head of a position
+// together), and a head's positions are H * hd elements apart.
+__device__ __forceinline__ size_t kv_index(const Dims &d, int b, int layer, int slot, int h, int e) {
+  return ((((size_t)b * d.L + layer) * d.cap + slot) * d.H + h) * d.hd + e;
+}
+
 template <typename KT>
 struct KV {
-  KT *k, *v;  // [B][L][H][cap][hd]
+  KT *k, *v;  // [B][L][cap][H][hd]
 };
 
 // ---- argmax partials --------------------------------------------------------------------------
@@ -183,7 +190,7 @@ __global__ __launch_bounds__(BLOCK) void k_qkv_rope(Dims d, Bufs s, KV<KT> kv, c
       s.q[(size_t)b * d.D + rr + 1] = v1;
     } else {
       KT *cache = part == 1 ? kv.k : kv.v;
-      const size_t idx = ((((size_t)b * d.L + layer) * d.H + h) * d.cap + slot) * d.hd + e;
+      const size_t idx = kv_index(d, b, layer, slot, h, e);
       cache[idx] = from_f<KT>(v0);
       cache[idx + 1] = from_f<KT>(v1);
     }
@@ -263,18 +270,22 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
 #pragma unroll
   for (int i = 0; i < EPL; ++i) qv[i] = qp[i];
   const float scale = 1.0f / sqrtf((float)HD);
-  const size_t base = (((size_t)b * d.L + layer) * d.H + h) * (size_t)d.cap * HD;
+  const size_t base = kv_index(d, b, layer, 0, h, 0);
+  const int PS = d.H * HD;  // elements from one cached position to the next
   const KT *kb = kv.k + base, *vb = kv.v + base;
 
   // indexes past the split clamp to its last position (results discarded), so the loads of a
-  // batch carry no branch
+  // batch carry no branch; the next batch's loads are issued before the current batch is used
+  // (two batches in flight per wave; the one past the end reads the last position again)
   constexpr int STEP = ATTN_KU * NWAVES * 4;
   const int jl = j1 > j0 ? j1 - 1 : 0;
-  for (int jb0 = j0 + wave * 4; jb0 < j1; jb0 += STEP) {
-    float kr[ATTN_KU][EPL];
+  const int jf = j0 + wave * 4;
+  auto load_batch = [&](const KT *src, int jb0, float(&r)[ATTN_KU][EPL]) {
 #pragma unroll
     for (int u = 0; u < ATTN_KU; ++u)
-      ld_row<EPL>(kb + (size_t)min(jb0 + u * NWAVES * 4 + g, jl) * HD + sub * EPL, kr[u]);
+      ld_row<EPL>(src + (size_t)min(jb0 + u * NWAVES * 4 + g, jl) * PS + sub * EPL, r[u]);
+  };
+  auto scores = [&](int jb0, const float(&kr)[ATTN_KU][EPL]) {
 #pragma unroll
     for (int u = 0; u < ATTN_KU; ++u) {
       const int j = jb0 + u * NWAVES * 4 + g;
@@ -286,6 +297,16 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
       dot += __shfl_xor(dot, 2, WAVE);
       dot += __shfl_xor(dot, 1, WAVE);
       if (j < j1 && sub == 0) sc[j - j0] = dot * scale;
+    }
+  };
+  {
+    float ka[ATTN_KU][EPL], kb2[ATTN_KU][EPL];
+    load_batch(kb, jf, ka);
+    for (int jb0 = jf; jb0 < j1; jb0 += 2 * STEP) {
+      load_batch(kb, jb0 + STEP, kb2);
+      scores(jb0, ka);
+      load_batch(kb, jb0 + 2 * STEP, ka);
+      scores(jb0 + STEP, kb2);
     }
   }
   __syncthreads();
@@ -303,17 +324,23 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   float op[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) op[i] = 0.f;
-  for (int jb0 = j0 + wave * 4; jb0 < j1; jb0 += STEP) {
-    float vr[ATTN_KU][EPL];
-#pragma unroll
-    for (int u = 0; u < ATTN_KU; ++u)
-      ld_row<EPL>(vb + (size_t)min(jb0 + u * NWAVES * 4 + g, jl) * HD + sub * EPL, vr[u]);
+  auto accum = [&](int jb0, const float(&vr)[ATTN_KU][EPL]) {
 #pragma unroll
     for (int u = 0; u < ATTN_KU; ++u) {
       const int j = jb0 + u * NWAVES * 4 + g;
       const float e = j < j1 ? sc[j - j0] : 0.f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) op[i] = fmaf(e, vr[u][i], op[i]);
+    }
+  };
+  {
+    float va[ATTN_KU][EPL], vb2[ATTN_KU][EPL];
+    load_batch(vb, jf, va);
+    for (int jb0 = jf; jb0 < j1; jb0 += 2 * STEP) {
+      load_batch(vb, jb0 + STEP, vb2);
+      accum(jb0, va);
+      load_batch(vb, jb0 + 2 * STEP, va);
+      accum(jb0 + STEP, vb2);
     }
   }
 #pragma unroll

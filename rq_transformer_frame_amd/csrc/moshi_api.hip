@@ -823,8 +823,12 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
     k_embed_begin<ET><<<dim3(blocks_for(d.D, BLOCK, 64), nb), BLOCK, 0, st>>>(d, b, E(s->emb[0]), E(s->text_emb),
                                                                                 user_dev, b0);
   });
-  enqueue_temporal_rows<WT, KT>(s, rows, x, b.q + (size_t)b0 * d.D, b.o + (size_t)b0 * d.D, RowMap{-1, b0, 0}, d.S,
-                                run);
+  // attention splits: enough (head, row, split) blocks to fill the chip a few times over and no
+  // more (the splits a conversation's positions do not reach exit at once, but are still
+  // dispatched; with many rows one split per (head, row) already fills it)
+  const int attn_splits = std::max(1, std::min(d.S, (4 * s->cus + d.H * rows - 1) / (d.H * rows)));
+  enqueue_temporal_rows<WT, KT>(s, rows, x, b.q + (size_t)b0 * d.D, b.o + (size_t)b0 * d.D, RowMap{-1, b0, 0},
+                                attn_splits, run);
   const int AM = AM_MAX_BLOCKS;
   run(MOSHI_STAGE_TEXT_HEAD, [&] {
     k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(s->out_norm), d.eps, d.D, X, P * d.D,
