@@ -1400,7 +1400,9 @@ moshi_status moshi_profile_frames(moshi_state *s, int32_t n_frames, const int32_
   const size_t pairs = 64 + (size_t)d.L * 5 + (size_t)d.Q * (d.Ld * 4 + 1);
   prof.ev.resize(2 * pairs, nullptr);
   prof.stage.resize(pairs, 0);
-  for (auto &e : prof.ev) HIP_TRY(s, hipEventCreate(&e));
+  // timing-only events: no system-scope fence (cache writeback and invalidation) when they are
+  // recorded, which would otherwise be charged to the stage they bracket
+  for (auto &e : prof.ev) HIP_TRY(s, hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
   std::vector<uint8_t> has(d.B);
   for (int f = 0; f < n_frames && rc >= 0; ++f) {
     const int32_t *u = user_tokens + (size_t)f * d.B * d.Q;
