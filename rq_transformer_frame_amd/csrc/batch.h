@@ -312,6 +312,100 @@ __global__ __launch_bounds__(BLOCK) void k_dep_attn(Dims d, Bufs s, int layer, i
   }
 }
 
+// a8 depformer step of conversation b0 + m after its q|k|v product, in one launch: the q, k and v
+// columns of each head are the sum over the S splits, in order, of part[s][m][c] (row length
+// 3 Dd), times the int8 row scales when wscale is set (S = 1 and no scales: `part` is the product
+// itself); k and v become the per-frame cache entry (layer, cb); then the attention of q over the
+// cb + 1 entries exactly as k_dep_attn, this step's entry taken from registers; o goes to X[m]
+// (XPut layout).  EPL (head dims per lane) a multiple of 4.
+template <typename XT, int EPL>
+__global__ __launch_bounds__(BLOCK) void k_dep_qkv_attn(Dims d, Bufs s, const float *__restrict__ part, int S, int M,
+                                                        const float *__restrict__ wscale, int layer, int cb,
+                                                        XT *__restrict__ X, int ldx, int b0) {
+  static_assert(EPL % 4 == 0, "columns are summed four at a time");
+  const int m = blockIdx.x, b = b0 + m;
+  const int Dd = d.Dd, hdd = d.hdd, N = 3 * Dd;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
+  float *kv0 = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q) * 2) * Dd;
+  float *kvc = kv0 + (size_t)cb * 2 * Dd;
+  const float scale = 1.0f / sqrtf((float)hdd);
+  const int npos = cb + 1;
+  for (int hh = wave * 4 + g; hh < d.Hd; hh += NWAVES * 4) {
+    const int e0 = hh * hdd + sub * EPL;
+    float qv[EPL], kk[DEP_MAX_POS][EPL], vv[DEP_MAX_POS][EPL], kc[EPL], vc[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; i += 4) {
+      const float4 a4 = split_sum4(part, S, M, N, m, e0 + i);
+      const float4 k4 = split_sum4(part, S, M, N, m, Dd + e0 + i);
+      const float4 v4 = split_sum4(part, S, M, N, m, 2 * Dd + e0 + i);
+      const float qa[4] = {a4.x, a4.y, a4.z, a4.w}, ka[4] = {k4.x, k4.y, k4.z, k4.w}, va[4] = {v4.x, v4.y, v4.z, v4.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        qv[i + t] = wscale ? qa[t] * wscale[e0 + i + t] : qa[t];
+        kc[i + t] = wscale ? ka[t] * wscale[Dd + e0 + i + t] : ka[t];
+        vc[i + t] = wscale ? va[t] * wscale[2 * Dd + e0 + i + t] : va[t];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      kvc[e0 + i] = kc[i];
+      kvc[Dd + e0 + i] = vc[i];
+    }
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p) {
+      if (p < cb) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          kk[p][i] = kv0[(size_t)p * 2 * Dd + e0 + i];
+          vv[p][i] = kv0[(size_t)p * 2 * Dd + Dd + e0 + i];
+        }
+      } else if (p == cb) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          kk[p][i] = kc[i];
+          vv[p][i] = vc[i];
+        }
+      }
+    }
+    float sc[DEP_MAX_POS];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p) {
+      float dot = 0.f;
+      if (p < npos) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
+      }
+      dot += __shfl_xor(dot, 8, WAVE);
+      dot += __shfl_xor(dot, 4, WAVE);
+      dot += __shfl_xor(dot, 2, WAVE);
+      dot += __shfl_xor(dot, 1, WAVE);
+      dot = __shfl(dot, lane & 48, WAVE);
+      sc[p] = dot * scale;
+      if (p < npos) mx = fmaxf(mx, sc[p]);
+    }
+    float den = 0.f;
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p)
+      if (p < npos) {
+        sc[p] = expf(sc[p] - mx);
+        den += sc[p];
+      }
+    float o[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p)
+      if (p < npos) {
+        const float wgt = sc[p] / den;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) o[i] = fmaf(wgt, vv[p][i], o[i]);
+      }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) XPut<XT>::put(X + (size_t)m * ldx, Dd, e0 + i, o[i]);
+  }
+}
+
 // a11 bookkeeping of a teacher-forced prefill of T frames of conversation `conv`, one thread:
 // for each frame, the user write and the gather of the 17 model inputs (into rows[t]), then the
 // forced ring write and the offset step, exactly as the frame kernels do them one frame at a time.

@@ -841,6 +841,8 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
     gemm<WT, false, MOSHI_STAGE_DEP_IN>(st, s->cus, s->gpart, W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, X, P * d.D, rows, b.din + (size_t)b0 * d.Q * d.Dd, d.Q * d.Dd);
   });
   float *y = b.y + (size_t)b0 * d.Dd;
+  // depformer heads of 64 or 128 dims (4 or 8 per lane): q|k|v epilogue and attention fused
+  const bool dep_fused = d.hdd % 64 == 0;
   for (int cb = 0; cb < d.Q; ++cb) {
     const ET *table = cb == 0 ? E(s->dep_text_emb) : E(s->dep_emb[cb - 1]);
     for (int j = 0; j < d.Ld; ++j) {
@@ -849,13 +851,41 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
         // layers after the first: the previous gate_out projection left rms_norm(y; norm1) in X
         if (j == 0)
           k_dep_entry<ET, XT><<<rows, BLOCK, d.Dd * f4, st>>>(d, b, table, cb, N(lw.norm1), X, P * d.Dd, b0);
-        gemm<WT, false, MOSHI_STAGE_DEP_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X, P * d.Dd, rows, Y, 3 * d.Dd);
-        k_dep_qkv_post<<<rows, BLOCK, 0, st>>>(d, b, Y, 3 * d.Dd, j, cb, b0);
+        if (dep_fused) {
+          // the split reduction, the cache entry and the attention run as one kernel
+          const float *src = Y, *sc = nullptr;
+          int S = 1;
+          bool split = false;
+          if constexpr (!std::is_same<WT, float>::value) {
+            const GemmPlan g = gemm_plan(3 * d.Dd, d.Dd, rows, s->cus);
+            if (g.S > 1) {
+              gemm_x_launch<WT, false, MOSHI_STAGE_DEP_QKV>(st, g, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd,
+                                                             X, P * d.Dd, rows, Y, 3 * d.Dd);
+              src = s->gpart;
+              S = g.S;
+              sc = s->scale(lw.in);
+              split = true;
+            }
+          }
+          if (!split)
+            gemm<WT, false, MOSHI_STAGE_DEP_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X,
+                                                 P * d.Dd, rows, Y, 3 * d.Dd);
+          with_epl(d.hdd, [&](auto e) {
+            if constexpr (decltype(e)::value % 4 == 0)
+              k_dep_qkv_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, src, S, rows, sc, j, cb, X,
+                                                                             P * d.Dd, b0);
+          });
+        } else {
+          gemm<WT, false, MOSHI_STAGE_DEP_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X,
+                                               P * d.Dd, rows, Y, 3 * d.Dd);
+          k_dep_qkv_post<<<rows, BLOCK, 0, st>>>(d, b, Y, 3 * d.Dd, j, cb, b0);
+        }
       });
       run(MOSHI_STAGE_DEP_OUT, [&] {
-        with_epl(d.hdd, [&](auto e) {
-          k_dep_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, j, cb, X, P * d.Dd, b0);
-        });
+        if (!dep_fused)
+          with_epl(d.hdd, [&](auto e) {
+            k_dep_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, j, cb, X, P * d.Dd, b0);
+          });
         // y += o . W_out^T, then X = rms_norm(y; norm2) for gate_in
         gemm_add_cvt<WT, MOSHI_STAGE_DEP_OUT>(st, s->cus, s->gpart, W(lw.out), s->scale(lw.out), d.Dd, d.Dd, X,
                                               P * d.Dd, rows, y, d.Dd, N(lw.norm2), d.eps, X, P * d.Dd);
