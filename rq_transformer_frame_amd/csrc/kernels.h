@@ -214,6 +214,9 @@ struct AttnQ {
   float *o;
   int conv;
   int64_t pos0;
+  bf16_t *xo;  // set: o goes straight to the next projection's input row z of xo (bf16 hi plane,
+               // then lo plane, row stride ldxo) instead of float32
+  int ldxo;
 };
 
 // N consecutive cache elements as floats (N a multiple of 4; float rows 16-byte aligned, bf16
@@ -354,12 +357,22 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   }
   __syncthreads();
   float *out = (pf ? aq.o + (size_t)blockIdx.z * d.D : s.o + (size_t)b * d.D) + h * HD;
+  auto put_o = [&](int t, float v) {
+    if (aq.xo) {
+      bf16_t *row = aq.xo + (size_t)blockIdx.z * aq.ldxo + h * HD;
+      const bf16_t hi = f2bf(v);
+      row[t] = hi;
+      row[d.D + t] = f2bf(v - bf2f(hi));
+    } else {
+      out[t] = v;
+    }
+  };
   if (S == 1) {
     for (int t = threadIdx.x; t < HD; t += BLOCK) {
       float acc = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < NWAVES; ++w2) acc += ored[w2][t];
-      out[t] = acc / l;
+      put_o(t, acc / l);
     }
     return;
   }
@@ -399,7 +412,7 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   for (int t = threadIdx.x; t < HD; t += BLOCK) {
     float acc = 0.f;
     for (int k = 0; k < S; ++k) acc += pws[k] * pbuf[k * (HD + 2) + 2 + t];
-    out[t] = acc / Lsum;
+    put_o(t, acc / Lsum);
   }
   if (threadIdx.x == 0) __hip_atomic_store(&s.attn_cnt[(size_t)b * d.H + h], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

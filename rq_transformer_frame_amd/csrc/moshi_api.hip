@@ -762,14 +762,18 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
     });
     run(MOSHI_STAGE_ATTN, [&] {
       const int chunk = (d.cap + attn_splits - 1) / attn_splits;
-      const AttnQ aq{q_rows, o_rows, rm.conv, rm.pos0};
+      // bf16 hi/lo projection inputs: the attention writes out_proj's input itself
+      bf16_t *xo = nullptr;
+      if constexpr (std::is_same<XT, bf16_t>::value) xo = X;
+      const AttnQ aq{q_rows, o_rows, rm.conv, rm.pos0, xo, P * d.D};
       if (d.hd == 128)
         k_attn<KT, 128><<<dim3(d.H, attn_splits, rows), BLOCK, chunk * 4, st>>>(d, b, kv, l, rm.b0, aq);
       else
         k_attn<KT, 64><<<dim3(d.H, attn_splits, rows), BLOCK, chunk * 4, st>>>(d, b, kv, l, rm.b0, aq);
     });
     run(MOSHI_STAGE_OUT_PROJ, [&] {
-      k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(o_rows, d.D, nullptr, d.eps, d.D, X, P * d.D, nullptr, 0);
+      if constexpr (!std::is_same<XT, bf16_t>::value)
+        k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(o_rows, d.D, nullptr, d.eps, d.D, X, P * d.D, nullptr, 0);
       // x += o . W_out^T, then X = rms_norm(x; norm2) for gate_in
       gemm_add_cvt<WT, MOSHI_STAGE_OUT_PROJ>(st, s->cus, s->gpart, W(lw.out), s->scale(lw.out), d.D, d.D, X, P * d.D,
                                              rows, x, d.D, N(lw.norm2), d.eps, X, P * d.D);
