@@ -258,7 +258,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline and from_zero and B == 1:
-        cpu = cpu_baseline(cfg, weights, users[:, 0], args.cpu_seconds, max_frames=30)
+        cpu = cpu_baseline(cfg, weights, users[:, 0], args.cpu_seconds, max_frames=len(users))
         log(f"cpu baseline: {cpu['value']:.3f} frames/s on {cpu['cores']} threads")
 
     metric, unit, value, what = METRIC, "frames/s", fps, "greedy frames from offset 0"
