@@ -42,6 +42,7 @@ struct PArgs {
   const void *w_lin[PQ];
   const float *s_lin[PQ];
   uint32_t *sync;  // [gridDim.x] per-block phase flags
+  uint64_t *ll;    // depformer exchange pairs {value, tag} (layout at st_ll)
   int *err;        // error flag (also copied back to the host with the outputs)
   int spin_limit;
   uint64_t *phase_ts;  // optional [phases][2]: block 0's arrival and the phase's completion time
@@ -196,6 +197,103 @@ __device__ __forceinline__ bool p_wait(const PArgs &a, uint32_t tag, int p, int 
   }
   __syncthreads();
   return *s_ok != 0;
+}
+
+// ---- flag-in-data exchange (depformer) ---------------------------------------------------------
+// Inside the depformer every value another block reads travels with a tag of the frame in the
+// same 8-byte system-scope store {value, tag}, and a reader polls the values themselves until each
+// carries the frame's tag.  Every location is written at most once per frame, so no grid-wide wait
+// separates these phases: a reader goes on one memory round trip after the producer's store lands,
+// where a phase flag costs the stores' completion, the flag store, the flag poll and a separate
+// load of the data.  Layout (pairs): y0 [Q][Dd], then per (layer j, step cb) a unit
+// [k: Dd][v: Dd][q: Dd][y1: Dd][a: Fd][y2: Dd].  Tags of an earlier frame never match.
+__device__ __forceinline__ void st_ll(uint64_t *p, float v, uint32_t tag) {
+  st_sys_u64(p, (uint64_t)__float_as_uint(v) | ((uint64_t)tag << 32));
+}
+
+__device__ __forceinline__ size_t ll_unit(const Dims &d, int j, int cb) {
+  return (size_t)d.Q * d.Dd + (size_t)(j * d.Q + cb) * (5 * d.Dd + d.Fd);
+}
+
+// Poll the 16 bytes (two pairs) at byte offset `off` until both carry `tag`.  Sets `bad` on the
+// spin limit or a raised error flag; the values are then meaningless and the caller exits.
+__device__ __forceinline__ void ll_settle(float4 &v, __amdgpu_buffer_rsrc_t r, int off, uint32_t tag, const PArgs &a,
+                                          int &bad) {
+  for (int spins = 0; !bad && (__float_as_uint(v.y) != tag || __float_as_uint(v.w) != tag); ++spins) {
+    if (spins >= a.spin_limit ||
+        ((spins & 255) == 255 && __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)) {
+      bad = 1;
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    v = ld_sys4(r, off);
+  }
+}
+
+// dst[k] = value of pair k of src for k < K (K even), U 16-byte loads per thread in flight per
+// pass; returns this thread's sum of squares.  No barrier.
+template <int U>
+__device__ __forceinline__ float ll_copy(const uint64_t *src, int K, uint32_t tag, float *dst, const PArgs &a,
+                                         int &bad) {
+  const __amdgpu_buffer_rsrc_t r = act_rsrc(src);
+  const int K2 = K >> 1;
+  float ss = 0.f;
+  for (int base = 0; base < K2; base += U * PBLOCK) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * PBLOCK + threadIdx.x;
+      if (i < K2) v[u] = ld_sys4(r, i * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * PBLOCK + threadIdx.x;
+      if (i < K2) {
+        ll_settle(v[u], r, i * 16, tag, a, bad);
+        dst[2 * i] = v[u].x;
+        dst[2 * i + 1] = v[u].z;
+        ss = fmaf(v[u].x, v[u].x, ss);
+        ss = fmaf(v[u].z, v[u].z, ss);
+      }
+    }
+  }
+  return ss;
+}
+
+// Block-wide verdict after a polled copy (a barrier): true if any thread gave up, with the error
+// flag raised so that the rest of the grid leaves too.
+__device__ __forceinline__ bool ll_fail(const PArgs &a, int bad) {
+  if (!__syncthreads_or(bad)) return false;
+  if (threadIdx.x == 0) __hip_atomic_store(a.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// xs = rms_norm(src; alpha) from a polled copy; false if the block must leave.
+template <int U>
+__device__ __forceinline__ bool ll_stage_rms(const uint64_t *src, const float *__restrict__ alpha, int K, float eps,
+                                             float *xs, float *red, uint32_t tag, const PArgs &a) {
+  int bad = 0;
+  const float ss = ll_copy<U>(src, K, tag, xs, a, bad);
+  if (ll_fail(a, bad)) return false;
+  const float tot = block_sum<PBLOCK>(ss, red);
+  const float inv = 1.0f / sqrtf(eps + tot / (float)K);
+  for (int k = threadIdx.x; k < K; k += PBLOCK) xs[k] = (xs[k] * alpha[k]) * inv;
+  __syncthreads();
+  return true;
+}
+
+// End of this block's part of an exchange phase: every wave is done with the staged input (LDS is
+// reused next); block 0's and every block's times are recorded as at a flag arrival.
+__device__ __forceinline__ void ll_arrive(const PArgs &a, int p) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (a.phase_ts && blockIdx.x == 0) a.phase_ts[2 * p] = wall_clock64();
+    if (a.block_ts) a.block_ts[(size_t)p * gridDim.x + blockIdx.x] = wall_clock64();
+  }
+}
+// Block 0 holds every input of the phase after p.
+__device__ __forceinline__ void ll_done(const PArgs &a, int p) {
+  if (a.phase_ts && blockIdx.x == 0 && threadIdx.x == 0) a.phase_ts[2 * p + 1] = wall_clock64();
 }
 
 // ---- row phases --------------------------------------------------------------------------------
@@ -580,12 +678,18 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
   if (!p_wait(a, p_tag(serial, NPH, P_HEAD), P_HEAD, &s_ok)) return;
 
   // ---- a8: depformer, 8 sequential codebook steps ----
+  // Inside a step the phases exchange their outputs as tagged pairs (no grid-wide wait); the
+  // codebook head still ends with one, since the next step merges every block's argmax partial.
+  const uint32_t ft = p_tag(serial, NPH, NPH - 1);  // this frame's exchange tag
+  const __amdgpu_buffer_rsrc_t rll = act_rsrc(a.ll);
   const ET *tbl;
   for (int cb = 0; cb < d.Q; ++cb) {
     const int PC = P_HEAD + 1 + cb * (4 * d.Ld + 1);
     for (int j = 0; j < d.Ld; ++j) {
       const LayerPtrs lp = a.dl[j * d.Q + cb];
       const int P = PC + 4 * j;
+      uint64_t *u = a.ll + ll_unit(d, j, cb);  // this (layer, step)'s k | v | q | y1 | a | y2
+      const size_t yin = j == 0 ? (size_t)cb * d.Dd : ll_unit(d, j - 1, cb) + 4 * d.Dd + d.Fd;
       // entry (layer 0): previous token, y = depformer_in[cb] . hidden + emb(prev)
       if (j == 0) {
         const int prev = merge_head(s.am_part + (size_t)cb * AM_MAX_BLOCKS, gridDim.x, wb);
@@ -594,56 +698,65 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         for (int k = threadIdx.x; k < d.Dd; k += PBLOCK) {
           const float v = ld_sys(s.din + (size_t)cb * d.Dd + k) + to_f(tbl[(size_t)prev * d.Dd + k]);
           xs[k] = v;
-          if (blockIdx.x == 0) st_sys(s.y + k, v);
+          if (blockIdx.x == 0) st_ll(a.ll + yin + k, v, ft);
         }
         __syncthreads();
         rms_in_place<PBLOCK>(xs, lp.norm1, d.Dd, d.eps, red);
       } else {
-        stage_rms<PBLOCK, true, UDd>(s.y, lp.norm1, d.Dd, d.eps, xs, red);
+        if (!ll_stage_rms<2 * UDd>(a.ll + yin, lp.norm1, d.Dd, d.eps, xs, red, ft, a)) return;
+        ll_done(a, P - 1);
       }
+      // k, v also go to the plain per-frame KV: later steps read them after the codebook head's
+      // grid-wide wait, which follows the completion of these stores
       float *kvbase = s.dkv + ((size_t)j * d.Q + cb) * 2 * d.Dd;
       rs.run(xs, [&](int row, float v) {
         if (lane != 0) return;
-        if (row < d.Dd)
-          st_sys(s.dq + row, v);
-        else
+        if (row < d.Dd) {
+          st_ll(u + 2 * d.Dd + row, v, ft);
+        } else {
+          st_ll(u + row - d.Dd, v, ft);
           st_sys(kvbase + row - d.Dd, v);
+        }
       });
-      p_arrive(a, p_tag(serial, NPH, P), P);
+      ll_arrive(a, P);
       p_begin(rs, lp.w_out, lp.s_out, d.Dd, d.Dd, 1);
-      if (!p_wait(a, p_tag(serial, NPH, P), P, &s_ok)) return;
 
-      // attention of dq over the cb + 1 entries of layer j (every block), then out_proj + residual
+      // attention of q over the cb + 1 entries of layer j (every block), then out_proj + residual
       float *ys = xs + d.Dd;  // y, for the residual
       {
-        constexpr int UY = UDd;  // y in UDd 16-byte loads per thread (one pass when Dd <= 4 * UDd * PBLOCK)
-        const __amdgpu_buffer_rsrc_t ry = act_rsrc(s.y), rq = act_rsrc(s.dq);
+        int bad = 0;
+        constexpr int UY = 2 * UDd;  // y pairs in UY 16-byte loads per thread (one pass when Dd <= 4 * UDd * PBLOCK)
+        const int Y2 = d.Dd >> 1;
         float4 yv[UY];
 #pragma unroll
-        for (int u = 0; u < UY; ++u) {
-          const int i = u * PBLOCK + threadIdx.x;
-          yv[u] = i < (d.Dd >> 2) ? ld_sys4(ry, i * 16) : float4{0.f, 0.f, 0.f, 0.f};
+        for (int uu = 0; uu < UY; ++uu) {
+          const int i = uu * PBLOCK + threadIdx.x;
+          if (i < Y2) yv[uu] = ld_sys4(rll, (int)((yin + 2 * i) * 8));
         }
         const int g = lane >> 4, sub = lane & 15;
-        const float *kv0 = s.dkv + (size_t)j * d.Q * 2 * d.Dd;
-        const __amdgpu_buffer_rsrc_t rkv = act_rsrc(kv0);
         const float scale = 1.0f / sqrtf((float)d.hdd);
         const int npos = cb + 1;
+        static_assert(DEPL % 2 == 0, "depformer dims per lane load as pairs of pairs");
+        constexpr int DL2 = DEPL / 2;
+        const float *kv0 = s.dkv + (size_t)j * d.Q * 2 * d.Dd;
+        const __amdgpu_buffer_rsrc_t rkv = act_rsrc(kv0);
         for (int hh = wave * 4 + g; hh < d.Hd; hh += PWAVES * 4) {
           const int e0 = hh * d.hdd + sub * DEPL;
+          // this step's q, k, v as tagged pairs; the earlier steps' k, v from the plain KV
+          float4 qr[DL2], kr[DL2], vr[DL2];
+          const int qoff = (int)((ll_unit(d, j, cb) + 2 * d.Dd + e0) * 8);
+          const int koff = (int)((ll_unit(d, j, cb) + e0) * 8);
+#pragma unroll
+          for (int i = 0; i < DL2; ++i) {
+            qr[i] = ld_sys4(rll, qoff + 16 * i);
+            kr[i] = ld_sys4(rll, koff + 16 * i);
+            vr[i] = ld_sys4(rll, koff + d.Dd * 8 + 16 * i);
+          }
           float qv[DEPL], kk[PQ][DEPL], vv[PQ][DEPL];
           static_assert(DEPL % 4 == 0, "depformer dims per lane load as float4");
 #pragma unroll
-          for (int i = 0; i < DEPL; i += 4) {
-            const float4 t4 = ld_sys4(rq, (e0 + i) * 4);
-            qv[i] = t4.x;
-            qv[i + 1] = t4.y;
-            qv[i + 2] = t4.z;
-            qv[i + 3] = t4.w;
-          }
-#pragma unroll
           for (int p = 0; p < PQ; ++p)
-            if (p < npos) {
+            if (p < cb) {
 #pragma unroll
               for (int i = 0; i < DEPL; i += 4) {
                 const float4 k4 = ld_sys4(rkv, (p * 2 * d.Dd + e0 + i) * 4);
@@ -656,6 +769,25 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
                 vv[p][i + 1] = v4.y;
                 vv[p][i + 2] = v4.z;
                 vv[p][i + 3] = v4.w;
+              }
+            }
+#pragma unroll
+          for (int i = 0; i < DL2; ++i) {
+            ll_settle(qr[i], rll, qoff + 16 * i, ft, a, bad);
+            ll_settle(kr[i], rll, koff + 16 * i, ft, a, bad);
+            ll_settle(vr[i], rll, koff + d.Dd * 8 + 16 * i, ft, a, bad);
+            qv[2 * i] = qr[i].x;
+            qv[2 * i + 1] = qr[i].z;
+          }
+#pragma unroll
+          for (int p = 0; p < PQ; ++p)
+            if (p == cb) {
+#pragma unroll
+              for (int i = 0; i < DL2; ++i) {
+                kk[p][2 * i] = kr[i].x;
+                kk[p][2 * i + 1] = kr[i].z;
+                vv[p][2 * i] = vr[i].x;
+                vv[p][2 * i + 1] = vr[i].z;
               }
             }
           float sc[PQ];
@@ -696,21 +828,26 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
           for (int i = 0; i < DEPL; ++i) xs[e0 + i] = o[i];
         }
 #pragma unroll
-        for (int u = 0; u < UY; ++u) {
-          const int i = u * PBLOCK + threadIdx.x;
-          if (i < (d.Dd >> 2)) reinterpret_cast<float4 *>(ys)[i] = yv[u];
+        for (int uu = 0; uu < UY; ++uu) {
+          const int i = uu * PBLOCK + threadIdx.x;
+          if (i < Y2) {
+            ll_settle(yv[uu], rll, (int)((yin + 2 * i) * 8), ft, a, bad);
+            ys[2 * i] = yv[uu].x;
+            ys[2 * i + 1] = yv[uu].z;
+          }
         }
-        __syncthreads();
+        if (ll_fail(a, bad)) return;
+        ll_done(a, P);
       }
       rs.run(xs, [&](int row, float v) {
-        if (lane == 0) st_sys(s.y + row, ys[row] + v);
+        if (lane == 0) st_ll(u + 3 * d.Dd + row, ys[row] + v, ft);
       });
-      p_arrive(a, p_tag(serial, NPH, P + 1), P + 1);
+      ll_arrive(a, P + 1);
       p_begin(rs, lp.w_gin, lp.s_gin, d.Dd, d.Fd, 2);
-      if (!p_wait(a, p_tag(serial, NPH, P + 1), P + 1, &s_ok)) return;
 
       // norm2 + gate_in + silu * mult (rows interleaved)
-      stage_rms<PBLOCK, true, UDd>(s.y, lp.norm2, d.Dd, d.eps, xs, red);
+      if (!ll_stage_rms<2 * UDd>(u + 3 * d.Dd, lp.norm2, d.Dd, d.eps, xs, red, ft, a)) return;
+      ll_done(a, P + 1);
       {
         float gv = 0.f;
         rs.run(xs, [&](int row, float v) {
@@ -718,29 +855,38 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
           if ((row & 1) == 0)
             gv = v;
           else
-            st_sys(s.da + (row >> 1), silu(gv) * v);
+            st_ll(u + 4 * d.Dd + (row >> 1), silu(gv) * v, ft);
         });
       }
-      p_arrive(a, p_tag(serial, NPH, P + 2), P + 2);
+      ll_arrive(a, P + 2);
       p_begin(rs, lp.w_gout, lp.s_gout, d.Fd, d.Dd, 1);
-      if (!p_wait(a, p_tag(serial, NPH, P + 2), P + 2, &s_ok)) return;
 
-      // gate_out + residual (y staged next to da)
-      stage2_sys<UFd, UDd>(s.da, d.Fd, xs, s.y, d.Dd, xs + d.Fd);
+      // gate_out + residual (y1 staged next to a)
+      {
+        int bad = 0;
+        (void)ll_copy<2 * UFd>(u + 4 * d.Dd, d.Fd, ft, xs, a, bad);
+        (void)ll_copy<2 * UDd>(u + 3 * d.Dd, d.Dd, ft, xs + d.Fd, a, bad);
+        if (ll_fail(a, bad)) return;
+        ll_done(a, P + 2);
+      }
       rs.run(xs, [&](int row, float v) {
-        if (lane == 0) st_sys(s.y + row, xs[d.Fd + row] + v);
+        if (lane == 0) st_ll(u + 4 * d.Dd + d.Fd + row, xs[d.Fd + row] + v, ft);
       });
-      p_arrive(a, p_tag(serial, NPH, P + 3), P + 3);
+      ll_arrive(a, P + 3);
       if (j + 1 < d.Ld)
         p_begin(rs, a.dl[(j + 1) * d.Q + cb].w_in, a.dl[(j + 1) * d.Q + cb].s_in, d.Dd, 3 * d.Dd, 1);
       else
         p_begin(rs, a.w_lin[cb], a.s_lin[cb], d.Dd, d.Va, 1);
-      if (!p_wait(a, p_tag(serial, NPH, P + 3), P + 3, &s_ok)) return;
     }
     // codebook head (no norm) with argmax partials
     {
       const int P = PC + 4 * d.Ld;
-      stage_vec<PBLOCK, true, UDd>(s.y, d.Dd, xs);
+      {
+        int bad = 0;
+        (void)ll_copy<2 * UDd>(a.ll + ll_unit(d, d.Ld - 1, cb) + 4 * d.Dd + d.Fd, d.Dd, ft, xs, a, bad);
+        if (ll_fail(a, bad)) return;
+        ll_done(a, P - 1);
+      }
       ArgBest best = arg_none();
       float *lg = s.audio_logits + (size_t)cb * d.Va;
       rs.run(xs, [&](int row, float v) {

@@ -106,6 +106,7 @@ struct moshi_state {
   int32_t *pf_rows = nullptr;   // [PF_ROWS][NS] gathered inputs
   int32_t *pf_tok = nullptr;    // [PF_ROWS][1 + 2 Q] forced text, agent, user tokens of a chunk
   uint32_t *sync = nullptr;     // per-block phase flags of the persistent kernel
+  uint64_t *ll = nullptr;       // the persistent kernel's depformer exchange pairs {value, tag}
   uint32_t pserial = 0;         // persistent launches so far
   mk::LayerPtrs *d_tl = nullptr, *d_dl = nullptr;
   mk::PArgs *d_pargs = nullptr;  // persistent kernel arguments (device copy)
@@ -337,6 +338,9 @@ moshi_status alloc_session(moshi_state *s) {
   req((void **)&b.rope_freq, (size_t)(d.hd / 2) * 4);
   const size_t nph = (size_t)5 * d.L + 1 + (size_t)d.Q * (4 * d.Ld + 1) + 1;
   req((void **)&s->sync, (size_t)std::max(s->cus, 64) * 4);  // one phase flag per persistent block
+  // y0 [Q][Dd], then per (depformer layer, step) k | v | q | y1 | a | y2; zeroed below, so the tag
+  // of every pair starts at 0, which no frame uses
+  req((void **)&s->ll, ((size_t)d.Q * d.Dd + (size_t)d.Ld * d.Q * (5 * d.Dd + d.Fd)) * 8);
   req((void **)&s->d_tl, (size_t)d.L * sizeof(mk::LayerPtrs));
   req((void **)&s->d_pargs, sizeof(mk::PArgs));
   req((void **)&s->d_phase_ts, nph * 2 * 8);
@@ -968,6 +972,7 @@ moshi_status write_pargs(moshi_state *s) {
     a.s_lin[cb] = s->scale(s->lin[cb]);
   }
   a.sync = s->sync;
+  a.ll = s->ll;
   a.err = s->d_err;
   a.spin_limit = 1 << 20;
   a.phase_ts = s->phase_timing ? s->d_phase_ts : nullptr;
