@@ -8,8 +8,10 @@
 // behind the fetch.  Completion of a phase is signalled by per-block flags that carry a tag
 // growing with the frame serial number and the phase; a waiter reads all flags.  Activations that other blocks read (x, q, o, a, y, dq, dkv, ...) are
 // written with system-scope stores (write-through past the per-XCD L2) after which the writer
-// waits for its stores (s_waitcnt) before it arrives, and are read with system-scope loads.  Every
-// wait is a bounded spin: on timeout the block raises the error flag and the whole grid exits.
+// waits for its stores (s_waitcnt) before it arrives, and are read with system-scope loads.  Inside
+// a depformer step the phases skip the flags: their outputs travel as {value, tag} pairs that the
+// readers poll (st_ll below).  Every wait is a bounded spin: on timeout the block raises the error
+// flag and the whole grid exits.
 #pragma once
 #include "kernels.h"
 
