@@ -225,6 +225,13 @@ moshi_status moshi_phase_times(moshi_state *s, int32_t enable, double *ts, int32
  * size.  MOSHI_ESTATE if the record was never switched on. */
 moshi_status moshi_block_times(moshi_state *s, double *ts, int32_t max_values, int32_t *n_blocks);
 
+/* Test hook (persistent executor): every wait of the frame kernel (a phase flag or a polled
+ * exchange value) gives up after `spins` polls (default 2^20, about a second); the kernel then
+ * raises its error flag, every block leaves, and moshi_frame_step returns MOSHI_EDEVICE (the
+ * session needs moshi_reset before the next frame).  It lets a test force that exit path from the
+ * host.  MOSHI_EINVAL for spins < 0, MOSHI_ESTATE for a session of another executor. */
+moshi_status moshi_set_spin_limit(moshi_state *s, int32_t spins);
+
 /* Bytes of linear weights (what one frame must stream) and of all device weights. */
 moshi_status moshi_weight_bytes(const moshi_state *s, int64_t *linear_bytes, int64_t *all_bytes);
 

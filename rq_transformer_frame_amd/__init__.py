@@ -43,6 +43,7 @@ _SIGS = {
     "moshi_profile_frames": (_i32, [_vp, _i32, _vp, _vp, _vp]),
     "moshi_gpu_time": (_i32, [_vp, _i32, _vp, _vp]),
     "moshi_phase_times": (_i32, [_vp, _i32, _vp, _i32, _vp]),
+    "moshi_set_spin_limit": (_i32, [_vp, _i32]),
 }
 
 STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv", "dep_out",
@@ -249,6 +250,10 @@ class Session:
         self._check(self.lib.moshi_phase_times(self.h, enable, _ptr(ts), n.value, ctypes.byref(n)),
                     "moshi_phase_times")
         return ts
+
+    def set_spin_limit(self, spins: int):
+        """Persistent executor: polls before a wait of the frame kernel gives up (test hook)."""
+        self._check(self.lib.moshi_set_spin_limit(self.h, int(spins)), "moshi_set_spin_limit")
 
     def block_times(self):
         """Persistent executor, after phase_times(2): every block's arrival time (us) at every

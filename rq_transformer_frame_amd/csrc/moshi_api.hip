@@ -108,6 +108,7 @@ struct moshi_state {
   uint32_t *sync = nullptr;     // per-block phase flags of the persistent kernel
   uint64_t *ll = nullptr;       // the persistent kernel's depformer exchange pairs {value, tag}
   uint32_t pserial = 0;         // persistent launches so far
+  int32_t spin_limit = 1 << 20; // polls before a wait of the persistent kernel gives up
   mk::LayerPtrs *d_tl = nullptr, *d_dl = nullptr;
   mk::PArgs *d_pargs = nullptr;  // persistent kernel arguments (device copy)
   uint64_t *d_phase_ts = nullptr;
@@ -974,7 +975,7 @@ moshi_status write_pargs(moshi_state *s) {
   a.sync = s->sync;
   a.ll = s->ll;
   a.err = s->d_err;
-  a.spin_limit = 1 << 20;
+  a.spin_limit = s->spin_limit;
   a.phase_ts = s->phase_timing ? s->d_phase_ts : nullptr;
   a.block_ts = s->block_timing ? s->d_block_ts : nullptr;
   HIP_TRY(s, hipMemcpy(s->d_pargs, &a, sizeof(a), hipMemcpyHostToDevice));
@@ -1475,6 +1476,16 @@ moshi_status moshi_reset(moshi_state *s, int32_t conv) {
   for (int b = b0; b < b0 + nb; ++b) s->h_offset[b] = 0;
   s->broken = false;
   return MOSHI_OK;
+}
+
+moshi_status moshi_set_spin_limit(moshi_state *s, int32_t spins) {
+  if (!s) return MOSHI_EINVAL;
+  if (spins < 0) return fail(s, MOSHI_EINVAL, "spin limit %d is negative", spins);
+  if (!s->pkern) return fail(s, MOSHI_ESTATE, "the session does not use the persistent executor");
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  HIP_TRY(s, hipStreamSynchronize(s->stream));  // no frame in flight reads the old argument block
+  s->spin_limit = spins;
+  return write_pargs(s);
 }
 
 moshi_status moshi_get_offset(const moshi_state *s, int32_t conv, int64_t *offset) {

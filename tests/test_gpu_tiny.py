@@ -374,3 +374,30 @@ def test_long_prefill_many_attention_splits_matches_oracle(exec_mode):
             for cb in range(cfg.dep_q):
                 assert rel_err(tr["audio_logits"][cb], ref["audio_logits"][cb]) <= TOL, (f, cb)
             assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], f
+
+
+def test_persistent_wait_timeout_exits_and_reset_recovers(weights, oracle):
+    """A wait of the persistent frame kernel that gives up (forced from the host: zero polls
+    allowed) raises the error flag, every block leaves the kernel, and the step returns
+    MOSHI_EDEVICE.  After a reset the frames match the oracle from offset 0 again: nothing the
+    aborted frame left in the phase flags or the depformer's tagged exchange values is taken for
+    a later frame's."""
+    users = synth.user_tokens(CFG, 6)
+    with rq.Session(CFG, exec="persistent") as s:
+        s.load_weights(weights)
+        s.step(users[0])  # a completed frame first: the exchange buffers hold its tagged values
+        s.set_spin_limit(0)
+        with pytest.raises(rq.MoshiError) as ei:
+            s.step(users[1])
+        assert ei.value.status == rq.MOSHI_EDEVICE
+        s.set_spin_limit(1 << 20)
+        s.reset()
+        ost = oracle.new_state()
+        for f in range(6):
+            ref = oracle.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            compare_step(s.read_trace(0), ref, st, out, has, f)
+    with rq.Session(CFG, exec="graph") as g:
+        with pytest.raises(rq.MoshiError) as ei:
+            g.set_spin_limit(10)
+        assert ei.value.status == rq.MOSHI_ESTATE
