@@ -130,7 +130,7 @@ def cpu_baseline(cfg, weights, users, budget_s: float, max_frames: int):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=250)
+    ap.add_argument("--steps", type=int, default=None, help="timed frames (default: the workload's frame count)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="moshi7b_bf16_b1")
     ap.add_argument("--exec", default="persistent", choices=["graph", "persistent", "stream"])
@@ -168,7 +168,7 @@ def main():
     t = time.time()
     weights = synth.gen_weights(cfg)
     log(f"generated {cfg.name} weights (seed {cfg.seed}) in {time.time() - t:.1f}s")
-    K, W = args.steps, args.warmup
+    K, W = (args.steps if args.steps is not None else cfg.frames), args.warmup
     nprof = args.profile_frames
     nframes = nprof + W + K
 
@@ -190,12 +190,16 @@ def main():
     elif cfg.max_start_offset:
         starts[:] = synth.start_offsets(cfg)
     prefill_s = None
-    if starts.any():
-        t = time.time()
+
+    def prefill():
         for b in range(B):
             if starts[b]:
                 text, agent, user = synth.prefill_tokens(cfg, int(starts[b]), conv=b)
                 sess.prefill_forced(b, text, agent, user)
+
+    if starts.any():
+        t = time.time()
+        prefill()
         prefill_s = time.time() - t
         log(f"prefilled {int(starts.sum())} positions over {B} conversation(s) in {prefill_s:.2f}s")
     # users[f] is [B][Q] (B = 1: [1][Q])
@@ -224,12 +228,13 @@ def main():
     f0 = 0 if from_zero else nprof
     for f in range(W):
         sess.step(users[f0 + f])
-    if from_zero:
-        sess.reset()
-        ft = 0
-    else:
-        ft = f0 + W
-    tpos = (pos0 + (0 if from_zero else W))[:, None] + np.arange(K)[None, :]  # positions of the timed frames
+    # back to the start of the workload (offset 0, or the end of the prefilled prefixes, prefilled
+    # again untimed), so the timed frames sit at the workload's own positions
+    sess.reset()
+    if not from_zero:
+        prefill()
+    ft = 0
+    tpos = starts[:, None] + np.arange(K)[None, :]  # positions of the timed frames
     sess.gpu_time(1)  # HIP events around each frame's device work, on the session stream
     t0 = time.perf_counter()
     for f in range(K):
