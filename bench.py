@@ -29,18 +29,20 @@ METRIC = "frames/s (80 ms) at B=1, Moshi-7B shape bf16; % of HBM roofline"
 # HBM bytes per dispatch of the dominant kernels, from two rocprofv3 --pmc runs (FETCH_SIZE,
 # WRITE_SIZE) scaled by a 256 MiB device-to-device copy in the same runs (profiles/ holds the
 # summaries and commands).  Valid only for the kernel sources they were taken on (the files the
-# B=1 frame kernels are compiled from): the bench reports traffic null when their hash differs.
+# B=1 frame kernels and the attention are compiled from, and the launch code): the bench reports
+# traffic null when their hash differs.
 TRAFFIC = {
-    "sources_sha256": "d58e1f9415ec5a4ac757664ae4432336200f9e253e5bdb34df5fe985971da1a9",
+    "sources_sha256": "a776bc3644a2afd3205f3cea2d8ec0c4cbbd323c9089653a3140518e0a562afc",
     "per_dispatch": {
         "moshi7b_bf16_b1/frame_persistent": 14875870583,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
         "moshi7b_bf16_b1/gate_in": 185062986,
+        "moshi7b_bf16_b64/attn": 1035621601,  # profiles/frame_moshi7b_bf16_b64_hbm_traffic.md
     },
 }
 
 
 TRAFFIC_SOURCES = ("device_common.h", "kernels.h", "frame_persistent.h", "persistent_variants.h",
-                   "persistent_hd128_bf16_kvf32.hip")
+                   "persistent_hd128_bf16_kvf32.hip", "moshi_api.hip")
 
 
 def sources_sha256() -> str:

@@ -58,15 +58,21 @@ def stats(path: str, bench: str | None = None) -> str:
     return "\n".join(out)
 
 
-def traffic(fetch: str, write: str, copy_mib: float) -> str:
+def traffic(fetch: str, write: str, copy_mib: float, after: str | None = None) -> str:
+    """Per-kernel HBM bytes per dispatch from a FETCH_SIZE and a WRITE_SIZE run, scaled by the
+    readings of the first device-to-device copy (copy_mib MiB).  With `after`, only the dispatches
+    that follow the last dispatch whose kernel name contains it count (the copy still scales)."""
     def load(p):
+        rows = sorted(csv.DictReader(open(p)), key=lambda r: int(r["Dispatch_Id"]))
+        last = max((i for i, r in enumerate(rows) if after and after in r["Kernel_Name"]), default=-1)
         d = collections.defaultdict(list)
         first_copy = None
-        for r in csv.DictReader(open(p)):
+        for i, r in enumerate(rows):
             v = float(r["Counter_Value"])
             if first_copy is None and "copyBuffer" in r["Kernel_Name"]:
                 first_copy = v
-            d[r["Kernel_Name"]].append(v)
+            if i > last:
+                d[r["Kernel_Name"]].append(v)
         return d, first_copy
 
     f, fc = load(fetch)
@@ -106,8 +112,8 @@ def steps(path: str, marker: str, nsteps: int) -> str:
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "stats":
         print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else None))
-    elif len(sys.argv) == 5 and sys.argv[1] == "traffic":
-        print(traffic(sys.argv[2], sys.argv[3], float(sys.argv[4])))
+    elif len(sys.argv) in (5, 6) and sys.argv[1] == "traffic":
+        print(traffic(sys.argv[2], sys.argv[3], float(sys.argv[4]), sys.argv[5] if len(sys.argv) == 6 else None))
     elif len(sys.argv) == 5 and sys.argv[1] == "steps":
         print(steps(sys.argv[2], sys.argv[3], int(sys.argv[4])))
     else:
