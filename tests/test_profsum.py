@@ -41,3 +41,18 @@ def test_traffic_scales_by_the_copy_and_filters_after_marker(tmp_path):
     assert cells[2].strip() == "2"
     assert int(cells[5]) == round((20 * 2 + 4) * 1024)
     assert "k_prefill_ring" not in after.split("| stage")[1].split("\n", 2)[2]
+
+
+def test_phase_kinds_of_the_persistent_frame():
+    # 32 temporal layers x 5 phases, the text head, then 8 codebook steps of 6 layers x 4 phases
+    # and a head: 32 * 5 + 1 + 8 * 25 = 361 phases
+    from collections import Counter
+
+    from rq_transformer_frame_amd.phase_timeline import phase_kind
+    kinds = [phase_kind(p, 32, 6) for p in range(361)]
+    c = Counter(kinds)
+    assert [c[k] for k in ("qkv", "attention", "out_proj", "gate_in", "gate_out")] == [32] * 5
+    assert c["text_head+dep_in"] == 1 and kinds[160] == "text_head+dep_in"
+    assert [c[k] for k in ("dep_qkv", "dep_attention+out_proj", "dep_gate_in", "dep_gate_out")] == [48] * 4
+    assert c["dep_head"] == 8 and kinds[360] == "dep_head" and kinds[185] == "dep_head"
+    assert kinds[161] == "dep_qkv" and kinds[186] == "dep_qkv"
