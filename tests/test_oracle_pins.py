@@ -422,3 +422,134 @@ def test_reset_state_repeats_the_first_frame():
     again = lm.step(lm.new_state(), [3] * 8)
     assert first["text_token"] == again["text_token"] and first["audio_tokens"] == again["audio_tokens"]
     np.testing.assert_array_equal(first["text_logits"], again["text_logits"])
+
+
+# ------------------------------------------------------------------ bf16 widening
+
+def test_bf16_widening_hand_values():
+    """bfloat16 bits are the top half of the float32: 0x3F80 is 1.0, 0xC020 is -2.5 and the
+    smallest subnormal 0x0001 is 2^-133."""
+    got = O.bf16_to_f32(np.array([0x3F80, 0xC020, 0x0001, 0x0000, 0x8000, 0x7F80], np.uint16))
+    assert got[0] == 1.0 and got[1] == -2.5 and got[2] == 2.0 ** -133
+    assert got[3] == 0.0 and np.signbit(got[4]) and got[5] == np.inf
+
+
+# ------------------------------------------------------------------ per-step depformer weights
+
+def test_depformer_steps_use_their_own_weights_and_cache_entries():
+    """Every step cb has its own projections ([LM] depformer_cycle reads in_projs[cb] etc.), and a
+    cached entry keeps the value its own step computed.  With q and k rows zero (uniform
+    attention), v rows = d[j][s] * I, out_proj = c[j][s] * I and the FFN zero, layer j gives
+    y_cb += c[j][cb] * mean_{p <= cb} d[j][p] * rms_norm(y_p; norm1_j), and linears[cb] = [I; 0]
+    exposes y in the logits.  Using step 0's (or layer j's) weights for every step, or recomputing
+    the cached values with the current step's weights, changes the logits."""
+    cfg = MINI.with_(dep_layers=2)
+    Dd, Q = cfg.dep_d_model, cfg.dep_q
+    w = mini_weights(cfg)
+    c = lambda j, s: 0.3 + 0.1 * s + 0.05 * j  # noqa: E731
+    dv = lambda j, s: 1.0 + 0.2 * s - 0.1 * j  # noqa: E731
+    alpha = [np.abs(synth.normal(8, f"pin/dn{j}", (Dd,), 1.0)) + F32(0.5) for j in range(2)]
+    for j in range(2):
+        p = f"depformer.layers.{j}"
+        w[f"{p}.norm1.alpha"][:] = alpha[j]
+        for s in range(Q):
+            Win = np.zeros((3 * Dd, Dd), F32)
+            Win[2 * Dd:] = F32(dv(j, s)) * np.eye(Dd, dtype=F32)
+            w[f"{p}.self_attn.in_projs.{s}.weight"][:] = Win
+            w[f"{p}.self_attn.out_projs.{s}.weight"][:] = F32(c(j, s)) * np.eye(Dd, dtype=F32)
+            w[f"{p}.gating.{s}.linear_out.weight"][:] = 0
+    for s in range(Q):
+        lin = np.zeros((cfg.audio_card, Dd), F32)
+        lin[:Dd] = np.eye(Dd, dtype=F32)
+        w[f"linears.{s}.weight"][:] = lin
+    lm = O.OracleLM(cfg, w)
+    st = lm.new_state()
+    rms = lambda y, a: y * a / np.sqrt(1e-8 + np.mean(y * y))  # noqa: E731
+    for t in range(2):
+        tr = lm.step(st, [t + 3] * 8)
+        hid = tr["transformer_out"].astype(np.float64)
+        prev = tr["text_token"]
+        cache = [[], []]
+        for cb in range(Q):
+            table = w["depformer_text_emb.weight"] if cb == 0 else w[f"depformer_emb.{cb - 1}.weight"]
+            y = w[f"depformer_in.{cb}.weight"].astype(np.float64) @ hid + table[prev]
+            for j in range(2):
+                cache[j].append(dv(j, cb) * rms(y, alpha[j].astype(np.float64)))
+                y = y + c(j, cb) * np.mean(cache[j], axis=0)
+            np.testing.assert_allclose(tr["audio_logits"][cb][:Dd], y, rtol=1e-4, atol=1e-5)
+            prev = tr["audio_tokens"][cb]
+
+
+# ------------------------------------------------------------------ rope inside the temporal step
+
+def test_temporal_step_ropes_q_and_k_at_the_absolute_position():
+    """One temporal layer whose q and k read only dims 0..3 of a residual that keeps those dims
+    (and its norm) fixed: the user's codebook-0 table writes a one-hot of the token into dims
+    4..11, every other table adds the same vector a on dims 0..3, the text table a too.  Then the
+    pre-rope q and k are the same at every position, and with interleaved rope the score of query
+    t against key j is (sum_i cos(f_i (t - j)) (q_2i k_2i + q_2i+1 k_2i+1) + sin(f_i (t - j))
+    (q_2i k_2i+1 - q_2i+1 k_2i)) / sqrt(hd), f_i = theta^(-2i/hd); v reads the one-hot dims, so
+    the attention output is a closed-form mix of the earlier tokens' one-hots.  out_proj = I, the
+    FFN is zero and text_linear = [I; 0] exposes out_norm(x + o).  Also the cached key of position
+    j is the pre-rope k turned by f_i * j.  Skipping rope, roping v, or turning q and k by
+    different positions changes these values.  (Turning both by pos + 1 leaves every score, and so
+    every output, unchanged; the cached-key check catches it.)"""
+    cfg = MINI.with_(n_layers=1, context=8, text_card=40, audio_card=32)
+    D, H = cfg.d_model, cfg.n_heads
+    hd = D // H
+    w = mini_weights(cfg)
+    for k in range(16):
+        w[f"emb.{k}.weight"][:] = 0
+    a = np.zeros(D, F32)
+    a[:4] = [0.8, -0.5, 0.3, 0.6]
+    w["text_emb.weight"][:] = a
+    cu = F32(0.9)
+    t8 = np.zeros((cfg.audio_card + 1, D), F32)
+    for r in range(cfg.audio_card + 1):
+        t8[r, 4 + r % 8] = cu
+    w["emb.8.weight"][:] = t8  # stream 9: the user's codebook 0 (delay 0)
+    p = "transformer.layers.0"
+    Win = np.zeros((3 * D, D), F32)
+    Win[:D, :4] = synth.normal(9, "pin/ropeq", (D, 4), 1.0)
+    Win[D:2 * D, :4] = synth.normal(9, "pin/ropek", (D, 4), 1.0)
+    for h in range(H):
+        Win[2 * D + h * hd: 2 * D + (h + 1) * hd, 4:12] = np.eye(hd, dtype=F32)
+    w[f"{p}.self_attn.in_projs.0.weight"][:] = Win
+    w[f"{p}.self_attn.out_projs.0.weight"][:] = np.eye(D, dtype=F32)
+    w[f"{p}.gating.linear_out.weight"][:] = 0
+    tl = np.zeros((cfg.text_card, D), F32)
+    tl[:D] = np.eye(D, dtype=F32)
+    w["text_linear.weight"][:] = tl
+    lm = O.OracleLM(cfg, w)
+    st = lm.new_state()
+    users = [[(5 * t + 3) % cfg.audio_card] + [1] * 7 for t in range(7)]
+    f = 10000.0 ** (-2.0 * np.arange(hd // 2) / hd)
+
+    def rot(v, ang):  # turn each interleaved pair of one head by ang[i]
+        z = v[0::2] + 1j * v[1::2]
+        z = z * np.exp(1j * ang)
+        out = np.empty(hd)
+        out[0::2], out[1::2] = z.real, z.imag
+        return out
+
+    onehots = []
+    for t in range(7):
+        tr = lm.step(st, users[t])
+        x = tr["emb_sum"].astype(np.float64)
+        inv = 1 / np.sqrt(1e-8 + np.mean(x * x))
+        q0 = Win[:D].astype(np.float64) @ (x * inv)
+        k0 = Win[D:2 * D].astype(np.float64) @ (x * inv)
+        onehots.append(x[4:12] * inv)
+        o = np.zeros(D)
+        for h in range(H):
+            sl = slice(h * hd, (h + 1) * hd)
+            qh, kh = q0[sl], k0[sl]
+            s = np.array([(rot(qh, f * (t - j)) @ kh) / np.sqrt(hd) for j in range(t + 1)])
+            e = np.exp(s - s.max())
+            o[sl] = (e / e.sum()) @ np.array(onehots)
+            # cached key of every position j <= t: k0 turned by f_i * j
+            for j in range(t + 1):
+                np.testing.assert_allclose(st.K[0][j][sl], rot(kh, f * j), rtol=1e-4, atol=1e-5)
+        x1 = x + o
+        hid = x1 / np.sqrt(1e-8 + np.mean(x1 * x1))
+        np.testing.assert_allclose(tr["text_logits"][:D], hid, rtol=1e-4, atol=1e-5)
