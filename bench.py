@@ -66,10 +66,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1, kve: int = 4) -> dict:
+KV_ALG = 2  # bytes per cached element that the method moves: a bfloat16 KV cache, whatever the
+            # storage the session keeps (float32 by default, for parity)
+
+
+def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1, kve: int = KV_ALG) -> dict:
     """Algorithmic HBM bytes of one launch of each stage: the weights it must stream once, the
-    KV it must read (n_kv positions per conversation), and its activation vectors (read once,
-    written once), for `rows` conversations."""
+    KV it must read (n_kv positions per conversation, kve bytes per element: bfloat16 for the
+    algorithmic count), and its activation vectors (read once, written once), for `rows`
+    conversations."""
     D, F, Dd, Fd, Q = cfg.d_model, cfg.ffn_hidden, cfg.dep_d_model, cfg.dep_ffn_hidden, cfg.dep_q
     Vt, Va, L = cfg.text_card, cfg.audio_card, cfg.n_layers
     we = {"f32": 4, "bf16": 2, "i8": 1}[band]
@@ -99,11 +104,52 @@ def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1, kve: int = 4) -> dic
 
 def frame_bytes(weight_bytes: int, cfg, kve: int, positions) -> float:
     """Weights (streamed once per frame for all conversations) + the KV every conversation reads
-    (kve bytes per element), per frame, averaged over the frames: positions is [B][frames] (or
-    [frames] at B = 1)."""
+    (kve bytes per element: KV_ALG for the algorithmic count), per frame, averaged over the frames:
+    positions is [B][frames] (or [frames] at B = 1)."""
     pos = np.atleast_2d(np.asarray(positions))
     n = np.minimum(pos + 1, cfg.context)
     return weight_bytes + float(np.mean(n.sum(axis=0))) * cfg.n_layers * 2 * cfg.d_model * kve
+
+
+def host_record() -> dict:
+    """The GPU host's CPU: logical CPUs, model name and RAM (from /proc)."""
+    rec = {"nproc": os.cpu_count(), "cpu_model": None, "ram_gb": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    rec["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    rec["ram_gb"] = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return rec
+
+
+def tiny_oracle_fps() -> dict:
+    """The oracle on the tiny float32 configuration (all 16 frames), with the BLAS thread pool at
+    its default size and limited to one thread."""
+    import threadpoolctl
+
+    import synth
+    from oracle import OracleLM
+    cfg = synth.TINY
+    lm = OracleLM(cfg, synth.gen_weights(cfg))
+    users = synth.user_tokens(cfg, cfg.frames)
+    out = {}
+    for label, limit in (("all_cores", None), ("one_core", 1)):
+        with threadpoolctl.threadpool_limits(limits=limit):
+            threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+            st = lm.new_state()
+            t0 = time.perf_counter()
+            for f in range(cfg.frames):
+                lm.step(st, users[f])
+            out[label] = {"frames_per_s": round(cfg.frames / (time.perf_counter() - t0), 2), "threads": int(threads)}
+    return out
 
 
 def cpu_baseline(cfg, weights, users, budget_s: float, max_frames: int):
@@ -126,7 +172,8 @@ def cpu_baseline(cfg, weights, users, budget_s: float, max_frames: int):
     del lm
     return {"value": done / dt, "unit": "frames/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {done} frames (offset 0..{done - 1}) of the same 7B bf16 B=1 workload, "
-                      f"float32 numpy oracle with the bf16 weights widened, {dt:.1f}s"}
+                      f"float32 numpy oracle with the bf16 weights widened, {dt:.1f}s",
+            "host": host_record(), "tiny_f32_16_frames": tiny_oracle_fps()}
 
 
 def main():
@@ -175,7 +222,7 @@ def main():
     nframes = nprof + W + K
 
     kv = args.kv
-    kve = 4 if kv == "f32" else 2
+    kve = 4 if kv == "f32" else 2  # bytes per cached element as stored
     if B > 1 and args.exec == "persistent":  # the persistent frame kernel serves one conversation
         args.exec = "graph"
     sess = rq.Session(cfg, exec=args.exec, kv=kv)
@@ -215,7 +262,7 @@ def main():
         pos0 = starts
     else:
         pos0 = starts + nprof
-    sb = stage_bytes(cfg, band, n_kv=float(np.mean(np.minimum(pos0 + 1, cfg.context))), rows=B, kve=kve)
+    sb = stage_bytes(cfg, band, n_kv=float(np.mean(np.minimum(pos0 + 1, cfg.context))), rows=B)
     stages = {}
     for name, (n, us) in prof.items():
         if n:
@@ -244,10 +291,13 @@ def main():
     dt = time.perf_counter() - t0
     gpu_us, gpu_n = sess.gpu_time(0)
     fps = K / dt
-    fb = frame_bytes(lin_bytes, cfg, kve, tpos)
+    fb = frame_bytes(lin_bytes, cfg, KV_ALG, tpos)
+    kv_surplus = frame_bytes(lin_bytes, cfg, kve, tpos) - fb  # extra KV bytes of a float32 cache
     log(f"{K} frames in {dt:.3f}s: {fps:.1f} frames/s ({B * fps:.1f} conversation-frames/s), "
         f"{fb / (dt / K) / 1e9:.0f} GB/s frame-level; GPU {gpu_us / gpu_n:.1f} us/frame")
     sess.close()
+    ceiling = rq.debug_read_bw(1 << 30, 20)
+    log(f"streaming-read ceiling: {ceiling:.0f} GB/s")
 
     if args.exec == "persistent":
         # the whole frame is one kernel: its algorithmic bytes are the frame's
@@ -256,12 +306,14 @@ def main():
                     "achieved": round(fb / avg / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(fb / avg / 1e3 / HBM_PEAK_GBS, 4),
                     "traffic": measured_traffic(cfg.name, "frame_persistent"),
-                    "bytes_per_launch": fb, "avg_us": round(avg, 2)}
+                    "bytes_per_launch": fb, "avg_us": round(avg, 2),
+                    "frac_of_ceiling": round(fb / avg / 1e3 / ceiling, 4)}
     else:
         d = stages[dom]
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, dom),
-                    "bytes_per_launch": d["bytes_per_launch"], "avg_us": round(d["avg_us"], 2)}
+                    "bytes_per_launch": d["bytes_per_launch"], "avg_us": round(d["avg_us"], 2),
+                    "frac_of_ceiling": round(d["gbs"] / ceiling, 4)}
 
     cpu = None
     if not args.no_cpu_baseline and from_zero and B == 1:
@@ -291,6 +343,9 @@ def main():
         "tokens_per_s": round(9 * B * fps, 1),
         "frame_roofline": {"bytes_per_frame": fb, "achieved_gbs": round(fb / (dt / K) / 1e9, 1),
                            "frac": round(fb / (dt / K) / 1e9 / HBM_PEAK_GBS, 4),
+                           "read_ceiling_gbs": round(ceiling, 1),
+                           "frac_of_ceiling": round(fb / (dt / K) / 1e9 / ceiling, 4),
+                           "kv_storage_surplus_bytes": kv_surplus,
                            "gpu_us_per_frame": round(gpu_us / gpu_n, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -290,6 +290,16 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
 moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, const float *W, const float *X,
                               float *Y, int32_t iters, float *avg_us);
 
+/*
+ * Measurement: the device's streaming-read rate, the ceiling the frame's weight streaming is
+ * compared with.  A kernel reads `bytes` of a fresh device allocation with 16-byte nontemporal
+ * loads (8 per lane in flight, 4 blocks of 256 threads per compute unit, each block a contiguous
+ * share), once untimed and then `iters` times between HIP events; *gbs receives bytes x iters /
+ * elapsed time in GB/s (10^9 bytes per second).  Errors: MOSHI_EINVAL (bytes outside
+ * [2^20, 2^31 - 16], iters < 1, gbs NULL), MOSHI_ENOMEM, MOSHI_EDEVICE.
+ */
+moshi_status moshi_debug_read_bw(int64_t bytes, int32_t iters, double *gbs);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,7 @@ _SIGS = {
     "moshi_gpu_time": (_i32, [_vp, _i32, _vp, _vp]),
     "moshi_phase_times": (_i32, [_vp, _i32, _vp, _i32, _vp]),
     "moshi_set_spin_limit": (_i32, [_vp, _i32]),
+    "moshi_debug_read_bw": (_i32, [_i64, _i32, _vp]),
 }
 
 STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv", "dep_out",
@@ -303,3 +304,13 @@ def debug_gemm(band: str, W: np.ndarray, X: np.ndarray, iters: int = 0):
     if st != MOSHI_OK:
         raise MoshiError(st, f"moshi_debug_gemm: {lib.moshi_status_string(st).decode()}")
     return Y, (us.value if iters > 0 else None)
+
+
+def debug_read_bw(nbytes: int = 1 << 30, iters: int = 20) -> float:
+    """Streaming-read rate of the device in GB/s (moshi_debug_read_bw)."""
+    lib = load_library()
+    g = ctypes.c_double(0)
+    st = lib.moshi_debug_read_bw(int(nbytes), int(iters), ctypes.byref(g))
+    if st != MOSHI_OK:
+        raise MoshiError(st, f"moshi_debug_read_bw: {lib.moshi_status_string(st).decode()}")
+    return g.value

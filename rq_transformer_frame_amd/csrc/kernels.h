@@ -722,10 +722,14 @@ static __global__ __launch_bounds__(BLOCK) void k_frame_end(Dims d, Bufs s, int 
   }
 }
 
-// [LM] state(): ring <- -2, offset <- 0 for conversations [b0, b0 + gridDim.x).
+// [LM] state(): ring <- -2, offset <- 0 for conversations [b0, b0 + gridDim.x).  The temporal
+// attention's per-head split counters are cleared too: a frame that was abandoned part-way (a
+// timed-out wait of the persistent kernel) can leave them raised, and a raised counter would make
+// a later frame merge a head's splits before all of them are written.
 static __global__ void k_reset(Dims d, Bufs s, int b0) {
   const int b = b0 + blockIdx.x;
   for (int i = threadIdx.x; i < d.NS * 3; i += blockDim.x) s.ring[(size_t)b * d.NS * 3 + i] = -2;
+  for (int h = threadIdx.x; h < d.H; h += blockDim.x) s.attn_cnt[(size_t)b * d.H + h] = 0u;
   if (threadIdx.x == 0) s.offset[b] = 0;
 }
 
@@ -734,6 +738,29 @@ static __global__ void k_force(Dims d, Bufs s, int b, Forced forced) {
   if (threadIdx.x != 0) return;
   const int p = (int)(s.offset[b] % 3);
   for (int st = 0; st <= d.Q; ++st) s.ring[((size_t)b * d.NS + st) * 3 + p] = forced.t[st];
+}
+
+// Streaming-read probe (measurement): block b reads its contiguous share of n16 16-byte vectors
+// with nontemporal buffer loads, 8 per lane in flight and no load under a branch (past the share's
+// end the buffer resource returns zeros), and folds them into one word; the word is stored only if
+// it equals a value no input here produces, which keeps the loads without a real store.
+static __global__ __launch_bounds__(BLOCK) void k_read_probe(const uint4 *__restrict__ p, int64_t n16,
+                                                          uint32_t *__restrict__ sink) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n16 ? lo + per : n16;
+  if (lo >= hi) return;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void *)(p + lo), (short)0, (int)((hi - lo) * 16), BUF_DWORD3);
+  uint32_t acc = 0;
+  for (int64_t i = threadIdx.x; i < hi - lo; i += 8 * BLOCK) {
+    u32x4b v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)((i + u * BLOCK) * 16), 0, BUF_NT);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
 // Per-row symmetric int8 quantisation (load time): s_r = max|w_r| / 127, q = round half away

@@ -1395,8 +1395,10 @@ static moshi_status run_frame(moshi_state *s, const int32_t *user, int32_t *out,
     s->gpu_frames += 1;
   }
   if (ho[(size_t)d.B * (1 + d.Q) + d.B] != 0) {  // a phase wait of the persistent kernel timed out
-    // the phase flags stay: later frames wait for larger tags
+    // the phase flags stay (later frames wait for larger tags); the attention split counters
+    // that blocks of the abandoned frame raised are cleared
     (void)hipMemsetAsync(s->d_err, 0, 4, s->stream);
+    (void)hipMemsetAsync(s->b.attn_cnt, 0, sizeof(uint32_t) * (size_t)d.B * d.H, s->stream);
     (void)hipStreamSynchronize(s->stream);
     return fail(s, MOSHI_EDEVICE, "persistent frame kernel: a phase wait timed out");
   }
@@ -1660,6 +1662,46 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
   if (ds) (void)hipFree(ds);
   if (dx) (void)hipFree(dx);
   if (dy) (void)hipFree(dy);
+  if (st) (void)hipStreamDestroy(st);
+  return rc;
+}
+
+moshi_status moshi_debug_read_bw(int64_t bytes, int32_t iters, double *gbs) {
+  if (bytes < (1 << 20) || bytes > 0x7FFFFFF0LL || iters < 1 || !gbs) return MOSHI_EINVAL;
+  const int64_t n16 = bytes / 16;
+  char *buf = nullptr;
+  uint32_t *sink = nullptr;
+  hipStream_t st = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  moshi_status rc = MOSHI_OK;
+  int dev = 0, cus = 0;
+  auto chk = [&](hipError_t e) {
+    if (e != hipSuccess && rc == MOSHI_OK) {
+      fprintf(stderr, "moshi_debug_read_bw: %s\n", hipGetErrorString(e));
+      rc = e == hipErrorOutOfMemory ? MOSHI_ENOMEM : MOSHI_EDEVICE;
+    }
+    return rc == MOSHI_OK;
+  };
+  const int blocks_per_cu = 4;
+  if (chk(hipGetDevice(&dev)) && chk(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) &&
+      chk(hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) && chk(hipMalloc(&buf, (size_t)n16 * 16)) &&
+      chk(hipMalloc(&sink, (size_t)cus * blocks_per_cu * 4)) && chk(hipMemsetAsync(buf, 0x5A, (size_t)n16 * 16, st))) {
+    const dim3 grid((unsigned)(cus * blocks_per_cu));
+    mk::k_read_probe<<<grid, mk::BLOCK, 0, st>>>(reinterpret_cast<const uint4 *>(buf), n16, sink);  // warm-up
+    if (chk(hipGetLastError()) && chk(hipEventCreate(&e0)) && chk(hipEventCreate(&e1)) && chk(hipEventRecord(e0, st))) {
+      for (int i = 0; i < iters; ++i)
+        mk::k_read_probe<<<grid, mk::BLOCK, 0, st>>>(reinterpret_cast<const uint4 *>(buf), n16, sink);
+      chk(hipGetLastError());
+      chk(hipEventRecord(e1, st));
+      chk(hipEventSynchronize(e1));
+      float ms = 0.f;
+      if (chk(hipEventElapsedTime(&ms, e0, e1))) *gbs = (double)n16 * 16.0 * iters / ((double)ms * 1e-3) / 1e9;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (buf) (void)hipFree(buf);
+  if (sink) (void)hipFree(sink);
   if (st) (void)hipStreamDestroy(st);
   return rc;
 }

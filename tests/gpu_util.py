@@ -33,3 +33,38 @@ def frame_agreement(tr, ref):
             break
         cos.append(cosine(tr["audio_logits"][c], ref["audio_logits"][c]))
     return min(cos), sum(int(a == b) for a, b in zip(got, want))
+
+
+class TraceStats:
+    """Running comparison of a GPU trace against a reference, frame by frame, under the judging
+    rule of frame_agreement: the text logits always, a codebook's logits while the tokens before it
+    agree.  Keeps the minimum cosine, the largest relative error (max |g - o| / max |o| per row)
+    and the token agreement."""
+
+    def __init__(self):
+        self.cos_min, self.rel_max, self.agree, self.total, self.frames = 1.0, 0.0, 0, 0, 0
+
+    def add(self, tr, ref):
+        got = [tr["text_token"]] + tr["audio_tokens"]
+        want = [ref["text_token"]] + ref["audio_tokens"]
+        rows = [(tr["text_logits"], ref["text_logits"])]
+        for c in range(len(want) - 1):
+            if got[: c + 1] != want[: c + 1]:
+                break
+            rows.append((tr["audio_logits"][c], ref["audio_logits"][c]))
+        for g, o in rows:
+            self.cos_min = min(self.cos_min, cosine(g, o))
+            self.rel_max = max(self.rel_max, rel_err(g, o))
+        a = sum(int(x == y) for x, y in zip(got, want))
+        self.agree += a
+        self.total += len(got)
+        self.frames += 1
+        return a
+
+    @property
+    def rate(self):
+        return self.agree / max(self.total, 1)
+
+    def __str__(self):
+        return (f"{self.frames} frames: min cosine {self.cos_min:.6f}, max rel logit err {self.rel_max:.2e}, "
+                f"tokens {self.agree}/{self.total}")

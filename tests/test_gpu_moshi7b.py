@@ -1,7 +1,10 @@
-"""Moshi-7B-shaped bfloat16 parity (B=1, seed-1 weights): the GPU frame step, teacher-forced onto
-the CPU oracle's greedy trajectory ([LM] force_generated), must keep every logits row at cosine
->= 0.999 and agree on >= 99% of the greedy tokens.  The oracle runs the same bf16 weights widened
-to float32.  Runs in the persistent configuration the bench times, and in the graph one."""
+"""Moshi-7B-shaped bfloat16 parity (B=1, seed-1 weights) over the whole 250-frame trace: the GPU
+frame step, teacher-forced onto the CPU oracle's greedy trajectory ([LM] force_generated), must keep
+every logits row at cosine >= 0.999 and agree on >= 99% of the greedy tokens.  The oracle runs the
+same bf16 weights widened to float32 and the GPU keeps a float32 KV cache, so only the order of
+the float32 sums differs: the largest relative logit error is asserted too.  The persistent
+executor (the one the bench times) and the graph executor step in lockstep with one oracle run;
+the bfloat16-KV instances of both run a shorter trace."""
 import time
 
 import numpy as np
@@ -10,12 +13,14 @@ import pytest
 import rq_transformer_frame_amd as rq
 import synth
 from oracle import OracleLM
-from tests.gpu_util import cosine, top2_margin
+from tests.gpu_util import TraceStats
 
 pytestmark = pytest.mark.gpu
 
 CFG = synth.MOSHI7B
-FRAMES = 4
+FRAMES = CFG.frames  # 250
+REL_F32KV = 1e-3     # bf16 weights on both sides, float32 KV: summation order only
+KV_BF16_FRAMES = 40
 
 
 @pytest.fixture(scope="module")
@@ -31,36 +36,57 @@ def oracle(weights):
     return OracleLM(CFG, weights)
 
 
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("exec_mode", ["persistent", "graph"])
-def test_moshi7b_bf16_teacher_forced_matches_oracle(weights, oracle, exec_mode):
-    users = synth.user_tokens(CFG, FRAMES)
-    with rq.Session(CFG, exec=exec_mode) as s:
-        t = time.time()
-        s.load_weights(weights)
-        print(f"loaded in {time.time() - t:.1f}s", flush=True)
-        lm = oracle
-        ost = lm.new_state()
-        agree = total = 0
-        cos_min = 1.0
-        for f in range(FRAMES):
-            t = time.time()
-            ref = lm.step(ost, users[f])
+def forced_run(sessions, lm, users, frames, label):
+    stats = {m: TraceStats() for m in sessions}
+    ost = lm.new_state()
+    t0 = time.time()
+    for f in range(frames):
+        ref = lm.step(ost, users[f])
+        for m, s in sessions.items():
             s.step(users[f])
             tr = s.read_trace(0)
-            assert tr["input_tokens"].tolist() == ref["input_tokens"].tolist()
-            rows = [(tr["text_logits"], ref["text_logits"])] + [
-                (tr["audio_logits"][c], ref["audio_logits"][c]) for c in range(CFG.dep_q)]
-            cs = [cosine(g, o) for g, o in rows]
-            cos_min = min(cos_min, *cs)
-            got = [tr["text_token"]] + tr["audio_tokens"]
-            want = [ref["text_token"]] + ref["audio_tokens"]
-            agree += sum(int(a == b) for a, b in zip(got, want))
-            total += len(got)
-            print(f"frame {f}: min cos {min(cs):.6f} tokens {sum(int(a == b) for a, b in zip(got, want))}/9 "
-                  f"text margin {top2_margin(ref['text_logits']):.2e} ({time.time() - t:.1f}s)", flush=True)
-            lm.force_generated(ost, ref["text_token"], ref["audio_tokens"])
+            assert tr["input_tokens"].tolist() == ref["input_tokens"].tolist(), (m, f)
+            stats[m].add(tr, ref)
             s.force_generated(0, ref["text_token"], ref["audio_tokens"])
-        print(f"7B bf16: min cosine {cos_min:.6f}, agreement {agree}/{total}", flush=True)
-        assert cos_min >= 0.999
-        assert agree / total >= 0.99
+        if f % 25 == 24 or f == frames - 1:
+            print(f"{label} frame {f}: " + "; ".join(f"{m} {st}" for m, st in stats.items()) +
+                  f" ({time.time() - t0:.1f}s)", flush=True)
+    return stats
+
+
+@pytest.mark.timeout(1200)
+def test_moshi7b_bf16_250_frames_match_oracle(weights, oracle):
+    users = synth.user_tokens(CFG, FRAMES)
+    sessions = {m: rq.Session(CFG, exec=m) for m in ("persistent", "graph")}
+    try:
+        for s in sessions.values():
+            s.load_weights(weights)
+        stats = forced_run(sessions, oracle, users, FRAMES, "7B bf16")
+    finally:
+        for s in sessions.values():
+            s.close()
+    for m, st in stats.items():
+        print(f"7B bf16 ({m}): {st}", flush=True)
+        assert st.frames == FRAMES
+        assert st.cos_min >= 0.999, m
+        assert st.rate >= 0.99, m
+        assert st.rel_max <= REL_F32KV, m
+
+
+@pytest.mark.timeout(900)
+def test_moshi7b_bf16_kv_bf16_instances_match_oracle(weights, oracle):
+    """The bfloat16 KV cache (an option: half the KV bytes, a storage loss that grows with the
+    context) on the persistent instance built for it and on the graph executor."""
+    users = synth.user_tokens(CFG, KV_BF16_FRAMES)
+    sessions = {m: rq.Session(CFG, exec=m, kv="bf16") for m in ("persistent", "graph")}
+    try:
+        for s in sessions.values():
+            s.load_weights(weights)
+        stats = forced_run(sessions, oracle, users, KV_BF16_FRAMES, "7B bf16, bf16 KV")
+    finally:
+        for s in sessions.values():
+            s.close()
+    for m, st in stats.items():
+        print(f"7B bf16, bf16 KV ({m}): {st}", flush=True)
+        assert st.cos_min >= 0.999, m
+        assert st.rate >= 0.99, m

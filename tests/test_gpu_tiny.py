@@ -401,3 +401,106 @@ def test_persistent_wait_timeout_exits_and_reset_recovers(weights, oracle):
         with pytest.raises(rq.MoshiError) as ei:
             g.set_spin_limit(10)
         assert ei.value.status == rq.MOSHI_ESTATE
+
+
+def test_persistent_timeout_with_attention_splits_then_reset_recovers():
+    """The timed-out frame of the test above, at a position where the temporal attention runs in
+    several position splits per head (16 heads, 200 cached positions): blocks that got past the
+    q|k|v wait raise their head's split counter before the next wait gives up.  After a reset and
+    a fresh prefill the frames must match the oracle, so the abandoned frame's counters must not
+    survive the reset."""
+    cfg = CFG.with_(name="tiny_f32_h16_long", d_model=1024, n_heads=16, context=1536)
+    T = 200
+    w = synth.gen_weights(cfg)
+    lm = OracleLM(cfg, w)
+    text, agent, user = synth.prefill_tokens(cfg, T, conv=3)
+    text %= cfg.text_card
+    users = synth.user_tokens(cfg, 4, conv=3, start_frame=T)
+    with rq.Session(cfg, exec="persistent") as s:
+        s.load_weights(w)
+        s.prefill_forced(0, text, agent, user)
+        s.step(users[0])
+        s.set_spin_limit(0)
+        with pytest.raises(rq.MoshiError) as ei:
+            s.step(users[1])
+        assert ei.value.status == rq.MOSHI_EDEVICE
+        s.set_spin_limit(1 << 20)
+        s.reset()
+        s.prefill_forced(0, text, agent, user)
+        ost = lm.new_state()
+        lm.prefill_forced(ost, text, agent, user)
+        for f in range(3):
+            ref = lm.step(ost, users[f])
+            s.step(users[f])
+            tr = s.read_trace(0)
+            assert rel_err(tr["transformer_out"], ref["transformer_out"]) <= TOL, f
+            assert rel_err(tr["text_logits"], ref["text_logits"]) <= TOL, f
+            assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], f
+
+
+def _contract_weights(weights, oracle):
+    """Text head: row 0 NaN, rows 17 and 990 both 4 x the oracle's frame-0 hidden (a tie far above
+    every other logit at frame 0), the rest as generated.  Codebook heads: row 0 NaN, rows 700 and
+    1900 one shared random vector, every other row zero, so the logits are NaN, 0 ... 0 and a tie
+    of two equal values: the token is 700 when that value is positive, else 1 (the first zero)."""
+    w = {k: v.copy() for k, v in weights.items()}
+    hid0 = oracle.step(oracle.new_state(), synth.user_tokens(CFG, 1)[0])["transformer_out"]
+    tl = w["text_linear.weight"]
+    tl[0] = np.nan
+    tl[17] = tl[990] = 4.0 * hid0
+    v = synth.normal(5, "contract/v", (CFG.dep_d_model,), 1.0)
+    for cb in range(CFG.dep_q):
+        lin = np.zeros((CFG.audio_card, CFG.dep_d_model), np.float32)
+        lin[0] = np.nan
+        lin[700] = lin[1900] = v
+        w[f"linears.{cb}.weight"] = lin
+    return w
+
+
+@pytest.mark.parametrize("exec_mode,batch", [("graph", 1), ("stream", 1), ("persistent", 1), ("graph", 3)])
+def test_greedy_contract_ties_first_wins_and_nan_never_chosen(weights, oracle, exec_mode, batch):
+    """[LM] argmax (a strict '>' scan from -inf): among equal maxima the first index wins and NaN
+    is never chosen.  Checked on the single-conversation heads (graph, stream, persistent) and on
+    the batched frame's row argmax, against the oracle and the closed-form expectation."""
+    w = _contract_weights(weights, oracle)
+    lm = OracleLM(CFG, w)
+    frames = 5
+    users = [synth.user_tokens(CFG, frames, conv=b) for b in range(batch)]
+    refs = []
+    for b in range(batch):
+        st = lm.new_state()
+        refs.append([lm.step(st, users[b][f]) for f in range(frames)])
+    assert refs[0][0]["text_token"] == 17
+    for r in (x for run in refs for x in run):
+        assert all(t in (700, 1) for t in r["audio_tokens"])
+    seen = {t for run in refs for x in run for t in x["audio_tokens"]}
+    print(f"audio tokens seen: {sorted(seen)}")
+    with rq.Session(CFG, exec=exec_mode, batch=batch) as s:
+        s.load_weights(w)
+        for f in range(frames):
+            s.step(np.stack([users[b][f] for b in range(batch)]))
+            for b in range(batch):
+                tr = s.read_trace(b)
+                ref = refs[b][f]
+                assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], (b, f)
+                ok = np.isfinite(ref["text_logits"])
+                assert rel_err(tr["text_logits"][ok], ref["text_logits"][ok]) <= TOL
+                assert np.isnan(tr["text_logits"][0]) and np.isnan(tr["audio_logits"][:, 0]).all()
+
+
+@pytest.mark.parametrize("exec_mode,batch", [("graph", 1), ("persistent", 1), ("graph", 3)])
+def test_greedy_contract_all_equal_logits_pick_index_zero(weights, oracle, exec_mode, batch):
+    """Every head zero: all logits are exactly 0 and every token is 0 (the first index)."""
+    w = {k: v.copy() for k, v in weights.items()}
+    w["text_linear.weight"][:] = 0
+    for cb in range(CFG.dep_q):
+        w[f"linears.{cb}.weight"][:] = 0
+    users = synth.user_tokens(CFG, 3)
+    with rq.Session(CFG, exec=exec_mode, batch=batch) as s:
+        s.load_weights(w)
+        for f in range(3):
+            s.step(np.stack([users[f]] * batch))
+            for b in range(batch):
+                tr = s.read_trace(b)
+                assert tr["tokens"].tolist() == [0] * (1 + CFG.dep_q), (b, f)
+                assert not tr["text_logits"].any() and not tr["audio_logits"].any()
