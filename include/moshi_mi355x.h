@@ -207,6 +207,35 @@ moshi_status moshi_read_trace(moshi_state *s, int32_t conv, const moshi_trace *t
 moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const int32_t *text,
                                   const int32_t *agent, const int32_t *user);
 
+/* ---- session snapshot ([LM] MoshiState::snapshot) --------------------------------------------- */
+
+/* A copy of one conversation's session state: the ring, the offset and the cached temporal KV
+ * positions (the last min(offset, context) positions, kept on the device in position order).  The
+ * depformer keeps no state across frames, and a sampler's random state (moshi_set_sampling) is
+ * not part of it, as on the page.  Opaque; owned by the caller until moshi_snapshot_free. */
+typedef struct moshi_snapshot moshi_snapshot;
+
+/* Copy conversation `conv` of `s` into a new snapshot (*out).  Allocates device memory of
+ * 2 x n_layers x positions x d_model KV elements on the session's device.  The session is not
+ * changed.  Errors: MOSHI_EINVAL, MOSHI_ESTATE (after a device error, before moshi_reset),
+ * MOSHI_ENOMEM, MOSHI_EDEVICE; *out is NULL on error. */
+moshi_status moshi_snapshot_take(moshi_state *s, int32_t conv, moshi_snapshot **out);
+
+/* Make conversation `conv` of `s` continue from the snapshot: its ring, offset and cached KV
+ * positions become the snapshot's (the cache slots are position % kv_capacity, so the destination
+ * may hold its conversations at another kv_capacity or batch).  The snapshot is unchanged and can
+ * be restored again, into any conversation of any session of the same model shape, band and KV
+ * storage on the same device.  Like moshi_reset it also clears a device-error state.  Errors:
+ * MOSHI_EINVAL (another shape, band, KV storage or device), MOSHI_ERANGE (kv_capacity below context
+ * and below the snapshot's offset), MOSHI_EDEVICE. */
+moshi_status moshi_snapshot_restore(moshi_state *s, int32_t conv, const moshi_snapshot *snap);
+
+/* The snapshot's offset, cached positions and device bytes (each optional). */
+moshi_status moshi_snapshot_info(const moshi_snapshot *snap, int64_t *offset, int64_t *positions, int64_t *bytes);
+
+/* Free a snapshot and its device memory.  NULL is ignored. */
+void moshi_snapshot_free(moshi_snapshot *snap);
+
 /* GPU time of frames: with enable >= 0 the per-frame HIP event pair around the frame's device
  * work (graph replay or persistent kernel, recorded on the session stream) is switched on (1)
  * or off (0) and the totals are cleared; with enable < 0 nothing changes.  *total_us and *frames

@@ -49,6 +49,7 @@ independent float64 implementation of the whole frame.
 """
 from __future__ import annotations
 
+import copy
 import math
 
 import numpy as np
@@ -169,6 +170,14 @@ def quantize_rows_int8(W):
 
 def dequantize_rows_int8(q, s):
     return q.astype(F32) * np.asarray(s, F32)[:, None]
+
+
+def round_bf16(x):
+    """float32 -> the nearest bfloat16 value (ties to even), returned as float32: keep the top 16
+    bits after adding 0x7FFF plus the lowest kept bit (finite inputs)."""
+    u = np.asarray(x, F32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(F32)
 
 
 def bf16_to_f32(b):
@@ -380,11 +389,15 @@ class OracleLM:
     `weights` maps the checkpoint names to arrays: float32, or uint16 bfloat16 bits (widened
     exactly to float32).  `band` picks the storage loss applied to every linear: 'f32' none,
     'i8sim' the per-row int8 band, 'q4sim' Q4_0 ([LM] load_q4sim), 'q8sim' q8_0 (float32 compute
-    throughout)."""
+    throughout).  `kv='bf16'` stores the temporal keys and values rounded to bfloat16 (the
+    storage loss of a bfloat16 cache; attention reads every position from the cache)."""
 
-    def __init__(self, cfg, weights: dict, band: str = "f32"):
+    def __init__(self, cfg, weights: dict, band: str = "f32", kv: str = "f32"):
         self.cfg = c = cfg
         self.band = band
+        if kv not in ("f32", "bf16"):
+            raise ValueError(kv)
+        self.kv_store = (lambda a: a) if kv == "f32" else round_bf16
         self.Q = c.dep_q
         self.NS = 2 * c.dep_q + 1
         self.delays = stream_delays(c.dep_q)
@@ -426,6 +439,14 @@ class OracleLM:
         # dep_layers[j][cb]: layer j's weights as step cb uses them (norms shared by the steps)
         self.dep_layers = [[layer(f"depformer.layers.{j}", s, f"gating.{s}") for s in range(c.dep_q)]
                            for j in range(c.dep_layers)]
+
+    def with_kv(self, kv: str) -> "OracleLM":
+        """The same model (weights shared, not copied) with another KV storage ('f32' or 'bf16')."""
+        other = copy.copy(self)
+        if kv not in ("f32", "bf16"):
+            raise ValueError(kv)
+        other.kv_store = (lambda a: a) if kv == "f32" else round_bf16
+        return other
 
     # -- session: the ring of the [LM] module doc ----------------------------------------------
     # Stream s holds RING slots; a token for step `offset` sits at slot (offset + delay[s]) % 3 and
@@ -483,9 +504,10 @@ class OracleLM:
         pos = st.offset
         rope = lambda r: rope_interleaved(r, pos, hd, c.rope_theta)  # noqa: E731
         x = np.asarray(x, F32).copy()
+        kvs = self.kv_store
         for l, ly in enumerate(self.layers):
             x = block(x, ly["norm1"], ly["norm2"], ly["w_in"], ly["w_out"], ly["w_gin"], ly["w_gout"], c.rms_eps,
-                      c.n_heads, hd, rope, lambda k, v, l=l: st.push_kv(l, k, v))
+                      c.n_heads, hd, rope, lambda k, v, l=l: st.push_kv(l, kvs(k), kvs(v)))
         return rms_norm(x, self.out_norm, c.rms_eps)
 
     def depformer_cycle(self, hidden, text_token: int, sampler=None):
@@ -580,8 +602,8 @@ class OracleLM:
             H = rms_norm_rows(X, ly["norm1"], c.rms_eps)
             QKV = H @ ly["w_in"].T
             Qm = np.stack([rope_interleaved(QKV[t, :D], pos[t], hd, c.rope_theta) for t in range(T)])
-            Km = np.stack([rope_interleaved(QKV[t, D:2 * D], pos[t], hd, c.rope_theta) for t in range(T)])
-            Vm = QKV[:, 2 * D:]
+            Km = self.kv_store(np.stack([rope_interleaved(QKV[t, D:2 * D], pos[t], hd, c.rope_theta) for t in range(T)]))
+            Vm = self.kv_store(QKV[:, 2 * D:])
             n0 = len(st.K[l])
             Kall = np.concatenate([st.K[l], Km])
             Vall = np.concatenate([st.V[l], Vm])

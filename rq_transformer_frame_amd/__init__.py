@@ -45,6 +45,10 @@ _SIGS = {
     "moshi_phase_times": (_i32, [_vp, _i32, _vp, _i32, _vp]),
     "moshi_set_spin_limit": (_i32, [_vp, _i32]),
     "moshi_debug_read_bw": (_i32, [_i64, _i32, _vp]),
+    "moshi_snapshot_take": (_i32, [_vp, _i32, _vp]),
+    "moshi_snapshot_restore": (_i32, [_vp, _i32, _vp]),
+    "moshi_snapshot_info": (_i32, [_vp, _vp, _vp, _vp]),
+    "moshi_snapshot_free": (None, [_vp]),
 }
 
 STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv", "dep_out",
@@ -101,6 +105,27 @@ _SHAPE_FIELDS = ("n_layers", "d_model", "n_heads", "ffn_hidden", "context", "tex
 
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
+
+
+class Snapshot:
+    """A moshi_snapshot (freed with free() or when collected)."""
+
+    def __init__(self, lib, h):
+        self.lib, self.h = lib, h
+
+    def info(self):
+        """(offset, cached positions, device bytes)."""
+        o, n, b = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        self.lib.moshi_snapshot_info(self.h, ctypes.byref(o), ctypes.byref(n), ctypes.byref(b))
+        return o.value, n.value, b.value
+
+    def free(self):
+        if getattr(self, "h", None):
+            self.lib.moshi_snapshot_free(self.h)
+            self.h = None
+
+    def __del__(self):
+        self.free()
 
 
 class Session:
@@ -190,6 +215,16 @@ class Session:
 
     def reset(self, conv: int = -1):
         self._check(self.lib.moshi_reset(self.h, conv), "moshi_reset")
+
+    def snapshot(self, conv: int = 0) -> "Snapshot":
+        """moshi_snapshot_take: a device copy of conversation `conv`'s ring, offset and KV."""
+        h = ctypes.c_void_p()
+        self._check(self.lib.moshi_snapshot_take(self.h, conv, ctypes.byref(h)), "moshi_snapshot_take")
+        return Snapshot(self.lib, h)
+
+    def restore(self, conv: int, snap: "Snapshot"):
+        """moshi_snapshot_restore: conversation `conv` continues from `snap`."""
+        self._check(self.lib.moshi_snapshot_restore(self.h, conv, snap.h), "moshi_snapshot_restore")
 
     def offset(self, conv: int = 0) -> int:
         v = ctypes.c_int64()

@@ -740,6 +740,25 @@ static __global__ void k_force(Dims d, Bufs s, int b, Forced forced) {
   for (int st = 0; st <= d.Q; ++st) s.ring[((size_t)b * d.NS + st) * 3 + p] = forced.t[st];
 }
 
+// Session snapshot ([LM] MoshiState::snapshot): copy the n cached positions p0 .. p0 + n - 1 of
+// conversation b's temporal KV (position p at slot p % cap) to (to_buf = 1) or from (0) a
+// position-ordered buffer [2][L][n][D] (keys, then values).  Grid (n, L).
+template <typename KT>
+__global__ __launch_bounds__(BLOCK) void k_kv_snapshot(Dims d, KV<KT> kv, KT *__restrict__ buf, int b, int64_t p0,
+                                                    int n, int to_buf) {
+  const int j = blockIdx.x, l = blockIdx.y;
+  const int slot = (int)((p0 + j) % d.cap);
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    KT *c = (which ? kv.v : kv.k) + kv_index(d, b, l, slot, 0, 0);
+    KT *o = buf + (((size_t)which * d.L + l) * n + j) * d.D;
+    if (to_buf)
+      for (int e = threadIdx.x; e < d.D; e += BLOCK) o[e] = c[e];
+    else
+      for (int e = threadIdx.x; e < d.D; e += BLOCK) c[e] = o[e];
+  }
+}
+
 // Streaming-read probe (measurement): block b reads its contiguous share of n16 16-byte vectors
 // with nontemporal buffer loads, 8 per lane in flight and no load under a branch (past the share's
 // end the buffer resource returns zeros), and folds them into one word; the word is stored only if

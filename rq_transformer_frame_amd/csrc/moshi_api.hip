@@ -134,6 +134,18 @@ struct moshi_state {
   }
 };
 
+// A conversation's session state copied out of a moshi_state: the ring and offset on the host,
+// the cached temporal KV positions on the device, in position order.
+struct moshi_snapshot {
+  moshi_config cfg{};         // shape, band and KV storage of the session it came from
+  int device = 0;
+  int64_t offset = 0;
+  int n = 0;                  // cached positions held: the last n before `offset`
+  size_t kv_bytes = 0;
+  void *kv = nullptr;         // [2][L][n][D] in the session's KV storage type
+  std::vector<int32_t> ring;  // [NS][3]
+};
+
 namespace {
 
 moshi_status fail(moshi_state *s, moshi_status code, const char *fmt, ...) {
@@ -1664,6 +1676,106 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
   if (dy) (void)hipFree(dy);
   if (st) (void)hipStreamDestroy(st);
   return rc;
+}
+
+static bool same_model(const moshi_config &a, const moshi_config &b) {
+  return a.n_layers == b.n_layers && a.d_model == b.d_model && a.n_heads == b.n_heads && a.ffn_hidden == b.ffn_hidden &&
+         a.context == b.context && a.text_card == b.text_card && a.audio_card == b.audio_card &&
+         a.dep_layers == b.dep_layers && a.dep_d_model == b.dep_d_model && a.dep_heads == b.dep_heads &&
+         a.dep_ffn_hidden == b.dep_ffn_hidden && a.dep_q == b.dep_q && a.rope_theta == b.rope_theta &&
+         a.rms_eps == b.rms_eps && a.band == b.band && a.kv_dtype == b.kv_dtype;
+}
+
+static size_t kv_elt(const moshi_config &c) { return c.kv_dtype == MOSHI_KV_BF16 ? 2 : 4; }
+
+// Launch the KV copy between conversation `conv`'s cache and a snapshot buffer.
+static void kv_snapshot_copy(moshi_state *s, void *buf, int conv, int64_t p0, int n, int to_buf) {
+  if (n <= 0) return;
+  const dim3 grid((unsigned)n, (unsigned)s->d.L);
+  if (s->cfg.kv_dtype == MOSHI_KV_BF16) {
+    const mk::KV<bf16_t> kv{reinterpret_cast<bf16_t *>(s->kc), reinterpret_cast<bf16_t *>(s->vc)};
+    mk::k_kv_snapshot<bf16_t><<<grid, mk::BLOCK, 0, s->stream>>>(s->d, kv, reinterpret_cast<bf16_t *>(buf), conv, p0,
+                                                               n, to_buf);
+  } else {
+    const mk::KV<float> kv{reinterpret_cast<float *>(s->kc), reinterpret_cast<float *>(s->vc)};
+    mk::k_kv_snapshot<float><<<grid, mk::BLOCK, 0, s->stream>>>(s->d, kv, reinterpret_cast<float *>(buf), conv, p0, n,
+                                                              to_buf);
+  }
+}
+
+moshi_status moshi_snapshot_take(moshi_state *s, int32_t conv, moshi_snapshot **out) {
+  if (!s) return MOSHI_EINVAL;
+  if (!out || conv < 0 || conv >= s->d.B) return fail(s, MOSHI_EINVAL, "bad conversation or NULL snapshot pointer");
+  *out = nullptr;
+  if (s->broken) return fail(s, MOSHI_ESTATE, "a device error occurred; call moshi_reset first");
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  const mk::Dims &d = s->d;
+  moshi_snapshot *snap = new moshi_snapshot();
+  snap->cfg = s->cfg;
+  snap->device = s->device;
+  snap->offset = s->h_offset[conv];
+  snap->n = (int)std::min<int64_t>(snap->offset, std::min(d.C, d.cap));
+  snap->kv_bytes = (size_t)2 * d.L * snap->n * d.D * kv_elt(s->cfg);
+  snap->ring.resize((size_t)d.NS * 3);
+  hipError_t e = hipStreamSynchronize(s->stream);
+  if (e == hipSuccess && snap->kv_bytes) e = hipMalloc(&snap->kv, snap->kv_bytes);
+  if (e == hipSuccess) {
+    kv_snapshot_copy(s, snap->kv, conv, snap->offset - snap->n, snap->n, 1);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(snap->ring.data(), s->b.ring + (size_t)conv * d.NS * 3, sizeof(int32_t) * d.NS * 3,
+                       hipMemcpyDeviceToHost, s->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
+  if (e != hipSuccess) {
+    moshi_snapshot_free(snap);
+    return fail(s, e == hipErrorOutOfMemory ? MOSHI_ENOMEM : MOSHI_EDEVICE, "snapshot: %s", hipGetErrorString(e));
+  }
+  *out = snap;
+  return MOSHI_OK;
+}
+
+moshi_status moshi_snapshot_restore(moshi_state *s, int32_t conv, const moshi_snapshot *snap) {
+  if (!s) return MOSHI_EINVAL;
+  if (!snap || conv < 0 || conv >= s->d.B) return fail(s, MOSHI_EINVAL, "bad conversation or NULL snapshot");
+  if (!same_model(s->cfg, snap->cfg))
+    return fail(s, MOSHI_EINVAL, "the snapshot comes from a session of another shape, band or KV storage");
+  if (snap->device != s->device) return fail(s, MOSHI_EINVAL, "the snapshot lives on another device");
+  const mk::Dims &d = s->d;
+  if (d.cap < d.C && snap->offset > d.cap)
+    return fail(s, MOSHI_ERANGE, "the snapshot is at offset %lld, kv_capacity is %d", (long long)snap->offset, d.cap);
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  HIP_TRY(s, hipStreamSynchronize(s->stream));
+  kv_snapshot_copy(s, snap->kv, conv, snap->offset - snap->n, snap->n, 0);
+  HIP_TRY(s, hipGetLastError());
+  HIP_TRY(s, hipMemcpyAsync(s->b.ring + (size_t)conv * d.NS * 3, snap->ring.data(), sizeof(int32_t) * d.NS * 3,
+                            hipMemcpyHostToDevice, s->stream));
+  HIP_TRY(s, hipMemcpyAsync(s->b.offset + conv, &snap->offset, sizeof(int64_t), hipMemcpyHostToDevice, s->stream));
+  HIP_TRY(s, hipMemsetAsync(s->b.attn_cnt + (size_t)conv * d.H, 0, sizeof(uint32_t) * d.H, s->stream));
+  HIP_TRY(s, hipStreamSynchronize(s->stream));
+  s->h_offset[conv] = snap->offset;
+  s->broken = false;
+  return MOSHI_OK;
+}
+
+moshi_status moshi_snapshot_info(const moshi_snapshot *snap, int64_t *offset, int64_t *positions, int64_t *bytes) {
+  if (!snap) return MOSHI_EINVAL;
+  if (offset) *offset = snap->offset;
+  if (positions) *positions = snap->n;
+  if (bytes) *bytes = (int64_t)snap->kv_bytes;
+  return MOSHI_OK;
+}
+
+void moshi_snapshot_free(moshi_snapshot *snap) {
+  if (!snap) return;
+  if (snap->kv) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(snap->device);
+    (void)hipFree(snap->kv);
+    (void)hipSetDevice(cur);
+  }
+  delete snap;
 }
 
 moshi_status moshi_debug_read_bw(int64_t bytes, int32_t iters, double *gbs) {

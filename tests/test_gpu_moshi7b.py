@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 CFG = synth.MOSHI7B
 FRAMES = CFG.frames  # 250
-REL_F32KV = 1e-3     # bf16 weights on both sides, float32 KV: summation order only
+REL_F32KV = 1e-4     # bf16 weights on both sides, float32 KV: summation order only
 KV_BF16_FRAMES = 40
 
 
@@ -75,18 +75,22 @@ def test_moshi7b_bf16_250_frames_match_oracle(weights, oracle):
 
 @pytest.mark.timeout(900)
 def test_moshi7b_bf16_kv_bf16_instances_match_oracle(weights, oracle):
-    """The bfloat16 KV cache (an option: half the KV bytes, a storage loss that grows with the
-    context) on the persistent instance built for it and on the graph executor."""
+    """The bfloat16 KV cache (an option: half the KV bytes at a storage loss) on the persistent
+    instance built for it and on the graph executor, against the oracle with the same storage
+    loss (keys and values rounded to bfloat16 in its cache); the float32-KV oracle's agreement on
+    the same trajectory is printed to separate the storage loss from kernel error."""
     users = synth.user_tokens(CFG, KV_BF16_FRAMES)
     sessions = {m: rq.Session(CFG, exec=m, kv="bf16") for m in ("persistent", "graph")}
+    lm16 = oracle.with_kv("bf16")
     try:
         for s in sessions.values():
             s.load_weights(weights)
-        stats = forced_run(sessions, oracle, users, KV_BF16_FRAMES, "7B bf16, bf16 KV")
+        stats = forced_run(sessions, lm16, users, KV_BF16_FRAMES, "7B bf16, bf16 KV")
     finally:
         for s in sessions.values():
             s.close()
     for m, st in stats.items():
-        print(f"7B bf16, bf16 KV ({m}): {st}", flush=True)
+        print(f"7B bf16, bf16 KV ({m}) vs the bf16-KV oracle: {st}", flush=True)
         assert st.cos_min >= 0.999, m
         assert st.rate >= 0.99, m
+        assert st.rel_max <= 1e-3, m

@@ -553,3 +553,35 @@ def test_temporal_step_ropes_q_and_k_at_the_absolute_position():
         x1 = x + o
         hid = x1 / np.sqrt(1e-8 + np.mean(x1 * x1))
         np.testing.assert_allclose(tr["text_logits"][:D], hid, rtol=1e-4, atol=1e-5)
+
+
+# ------------------------------------------------------------------ bf16 KV storage option
+
+def test_round_bf16_hand_values():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties to the even mantissa (1.0);
+    # 1 + 3 * 2^-8 ties upward to 1 + 2^-6; just above a tie rounds up; signs are kept
+    x = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -(1 + 2 ** -8 + 2 ** -20), 3.0, 0.0], F32)
+    np.testing.assert_array_equal(O.round_bf16(x), np.array([1.0, 1 + 2 ** -6, 1 + 2 ** -7, -(1 + 2 ** -7), 3.0, 0.0], F32))
+
+
+def test_bf16_kv_option_stores_rounded_keys_and_values():
+    """With kv='bf16' every cached key and value is the bfloat16 rounding of the float32 one (low
+    16 bits zero), in the decode step and in the batched prefill; the default keeps float32."""
+    cfg = MINI.with_(context=6)
+    w = mini_weights(cfg)
+    lm, lm16 = O.OracleLM(cfg, w), O.OracleLM(cfg, w, kv="bf16")
+    a, b = lm.new_state(), lm16.new_state()
+    text = synth.uniform_int(5, "pin/kvt", (4,), cfg.text_card)
+    agent = synth.uniform_int(5, "pin/kva", (4, 8), cfg.audio_card)
+    user = synth.uniform_int(5, "pin/kvu", (4, 8), cfg.audio_card)
+    lm16.prefill_forced(b, text, agent, user)
+    lm16.step(b, [2] * 8)
+    lm.step(a, [2] * 8)
+    for l in range(cfg.n_layers):
+        for arr in (b.K[l], b.V[l]):
+            assert not np.any(arr.view(np.uint32) & 0xFFFF)
+    assert np.any(a.K[0].view(np.uint32) & 0xFFFF)
+    # the first decode key of layer 0 is the rounded float32 key
+    c = lm16.new_state()
+    lm16.step(c, [2] * 8)
+    np.testing.assert_array_equal(c.K[0][0], O.round_bf16(a.K[0][0]))
