@@ -41,8 +41,10 @@ class TraceStats:
     agree.  Keeps the minimum cosine, the largest relative error (max |g - o| / max |o| per row)
     and the token agreement."""
 
-    def __init__(self):
+    def __init__(self, tie_tol: float = 0.0):
         self.cos_min, self.rel_max, self.agree, self.total, self.frames = 1.0, 0.0, 0, 0, 0
+        self.tie_tol = tie_tol
+        self.unexplained = 0  # differing tokens that are not near-ties of the reference's logits
 
     def add(self, tr, ref):
         got = [tr["text_token"]] + tr["audio_tokens"]
@@ -52,9 +54,14 @@ class TraceStats:
             if got[: c + 1] != want[: c + 1]:
                 break
             rows.append((tr["audio_logits"][c], ref["audio_logits"][c]))
-        for g, o in rows:
+        for i, (g, o) in enumerate(rows):
             self.cos_min = min(self.cos_min, cosine(g, o))
             self.rel_max = max(self.rel_max, rel_err(g, o))
+            # a differing pick on an agreeing conditioning: is it a near-tie of the reference?
+            if got[i] != want[i]:
+                o64 = np.asarray(o, np.float64)
+                margin = (o64[want[i]] - o64[got[i]]) / max(np.max(np.abs(o64)), 1e-30)
+                self.unexplained += int(not (margin <= self.tie_tol))
         a = sum(int(x == y) for x, y in zip(got, want))
         self.agree += a
         self.total += len(got)
@@ -67,4 +74,4 @@ class TraceStats:
 
     def __str__(self):
         return (f"{self.frames} frames: min cosine {self.cos_min:.6f}, max rel logit err {self.rel_max:.2e}, "
-                f"tokens {self.agree}/{self.total}")
+                f"tokens {self.agree}/{self.total}, differing picks that are not near-ties {self.unexplained}")
