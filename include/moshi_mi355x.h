@@ -207,6 +207,41 @@ moshi_status moshi_read_trace(moshi_state *s, int32_t conv, const moshi_trace *t
 moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const int32_t *text,
                                   const int32_t *agent, const int32_t *user);
 
+/* ---- sampled decoding ([LM] Sampling, MoshiLm::pick) ------------------------------------------ */
+
+typedef enum {
+  MOSHI_PICK_GREEDY = 0,  /* first-wins argmax ([LM] argmax), the default */
+  MOSHI_PICK_TOPK = 1,    /* [LM] topk_sample: the k largest logits, exp(double((l - max) / T)) weights
+                             summed in order of decreasing logit (equal logits by increasing index),
+                             normalised, one uniform, inverse-CDF walk */
+  MOSHI_PICK_GUMBEL = 2   /* [LM] gumbel_full_pick: argmax over the whole head of float32(l / T) +
+                             float32(-ln(-ln(max(u, 1e-300)))), one uniform per logit in index order */
+} moshi_pick;
+
+/* How a conversation picks its tokens.  The text head uses temp_text / top_k_text, the codebook
+ * heads temp / top_k ([LM] Sampling; LMGen defaults 0.8, 0.7, 250, 25).  Uniforms come from one
+ * 64-bit xorshift stream per conversation ([LM] xorshift_u01: shifts 13, 7, 17; u = top 53 bits /
+ * 2^53), drawn in pick order (text, then codebooks 0..dep_q-1), started at max(seed, 1). */
+typedef struct moshi_sampling {
+  int32_t mode;        /* moshi_pick */
+  float temp;          /* codebook temperature, > 0 */
+  float temp_text;     /* text temperature, > 0 */
+  int32_t top_k;       /* codebook k, in [1, 1024] (top-k mode) */
+  int32_t top_k_text;  /* text k, in [1, 1024] (top-k mode) */
+  uint64_t seed;       /* xorshift state; 0 means 1 */
+} moshi_sampling;
+
+/* Set conversation `conv`'s (or with conv == -1 every conversation's) token pick and restart its
+ * xorshift stream at max(seed, 1).  Later frames use it; moshi_reset and snapshots leave it alone
+ * (on the page the sampler belongs to the model, not to the session state).  The persistent
+ * executor samples with MOSHI_PICK_GUMBEL (folded into its heads' argmax) or greedy; top-k needs the
+ * graph or stream executor and heads of at most 36864 logits.  Errors: MOSHI_EINVAL (bad mode,
+ * temperature or k, or top-k on the persistent executor), MOSHI_EDEVICE. */
+moshi_status moshi_set_sampling(moshi_state *s, int32_t conv, const moshi_sampling *smp);
+
+/* The current xorshift state of conversation `conv`'s sampler (after the frames run so far). */
+moshi_status moshi_sampler_state(moshi_state *s, int32_t conv, uint64_t *state);
+
 /* ---- session snapshot ([LM] MoshiState::snapshot) --------------------------------------------- */
 
 /* A copy of one conversation's session state: the ring, the offset and the cached temporal KV

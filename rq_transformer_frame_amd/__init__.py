@@ -49,6 +49,8 @@ _SIGS = {
     "moshi_snapshot_restore": (_i32, [_vp, _i32, _vp]),
     "moshi_snapshot_info": (_i32, [_vp, _vp, _vp, _vp]),
     "moshi_snapshot_free": (None, [_vp]),
+    "moshi_set_sampling": (_i32, [_vp, _i32, _vp]),
+    "moshi_sampler_state": (_i32, [_vp, _i32, _vp]),
 }
 
 STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv", "dep_out",
@@ -91,6 +93,14 @@ class _Config(ctypes.Structure):
 class _Tensor(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
                 ("shape", ctypes.c_int64 * 2), ("data", ctypes.c_void_p)]
+
+
+class _Sampling(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("temp", ctypes.c_float), ("temp_text", ctypes.c_float),
+                ("top_k", ctypes.c_int32), ("top_k_text", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+PICK = {"greedy": 0, "topk": 1, "gumbel": 2}
 
 
 class _Trace(ctypes.Structure):
@@ -215,6 +225,17 @@ class Session:
 
     def reset(self, conv: int = -1):
         self._check(self.lib.moshi_reset(self.h, conv), "moshi_reset")
+
+    def set_sampling(self, conv: int = -1, mode: str = "topk", seed: int = 0, temp: float = 0.8,
+                     temp_text: float = 0.7, top_k: int = 250, top_k_text: int = 25):
+        """moshi_set_sampling: 'greedy', 'topk' or 'gumbel' picks for conversation `conv` (-1: all)."""
+        c = _Sampling(PICK[mode], temp, temp_text, top_k, top_k_text, seed)
+        self._check(self.lib.moshi_set_sampling(self.h, conv, ctypes.byref(c)), "moshi_set_sampling")
+
+    def sampler_state(self, conv: int = 0) -> int:
+        v = ctypes.c_uint64()
+        self._check(self.lib.moshi_sampler_state(self.h, conv, ctypes.byref(v)), "moshi_sampler_state")
+        return v.value
 
     def snapshot(self, conv: int = 0) -> "Snapshot":
         """moshi_snapshot_take: a device copy of conversation `conv`'s ring, offset and KV."""

@@ -13,7 +13,7 @@
 // readers poll (st_ll below).  Every wait is a bounded spin: on timeout the block raises the error
 // flag and the whole grid exits.
 #pragma once
-#include "kernels.h"
+#include "sample.h"
 
 namespace mk {
 
@@ -662,10 +662,24 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
     if (blockIdx.x == 0)
       for (int k = threadIdx.x; k < d.D; k += PBLOCK) s.hidden[k] = xs[k];
     ArgBest best = arg_none();
+    // full-vocabulary Gumbel-max sampling folded into the heads' argmax: each wave starts its
+    // rows' draws at the frame's stream state advanced to its first row ([LM] gumbel_full_pick
+    // draws one uniform per logit, text head first, then codebooks 0..Q-1); the sampler fields
+    // are read where they are used, so that nothing stays live across the frame
+    const bool gumbel = s.samp[0].mode == PICK_GUMBEL;
+    uint64_t gx = 0;
+    float gt = 1.f;
+    if (gumbel) {
+      int lo, hi;
+      wave_rows(gwave(), nwaves(), d.Vt, 1, lo, hi);
+      gx = wave_xs_jump(s.rng[0], (uint32_t)lo, s.jump);
+      gt = s.samp[0].temp_text;
+    }
     rs.run(xs, [&](int row, float v) {
+      const float sc = gumbel ? gumbel_score(v, gt, gx) : v;
       if (lane != 0) return;
       s.text_logits[row] = v;
-      best = arg_take(best, v, row);
+      best = arg_take(best, sc, row);
     });
     best = wave_arg(best);
     best = block_arg(best, wb);
@@ -891,10 +905,20 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
       }
       ArgBest best = arg_none();
       float *lg = s.audio_logits + (size_t)cb * d.Va;
+      const bool gumbel = s.samp[0].mode == PICK_GUMBEL;
+      uint64_t gx = 0;
+      float gt = 1.f;
+      if (gumbel) {
+        int lo, hi;
+        wave_rows(gwave(), nwaves(), d.Va, 1, lo, hi);
+        gx = wave_xs_jump(s.rng[0], (uint32_t)(d.Vt + cb * d.Va + lo), s.jump);
+        gt = s.samp[0].temp;
+      }
       rs.run(xs, [&](int row, float v) {
+        const float sc = gumbel ? gumbel_score(v, gt, gx) : v;
         if (lane != 0) return;
         lg[row] = v;
-        best = arg_take(best, v, row);
+        best = arg_take(best, sc, row);
       });
       best = wave_arg(best);
       best = block_arg(best, wb);
@@ -914,6 +938,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
   const int last = merge_head(s.am_part + (size_t)d.Q * AM_MAX_BLOCKS, gridDim.x, wb);
   if (threadIdx.x == 0) {
     s.tokens[d.Q] = last;
+    if (s.samp[0].mode == PICK_GUMBEL) s.rng[0] = xs_jump(s.rng[0], (uint32_t)(d.Vt + d.Q * d.Va), s.jump);
     const int64_t off = pos + 1;
     s.offset[0] = off;
     const int p = (int)(off % 3);

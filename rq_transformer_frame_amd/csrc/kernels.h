@@ -27,6 +27,15 @@ constexpr int ATTN_MAX_S = 32;       // temporal attention splits
 constexpr int ATTN_MIN_CHUNK = 64;   // positions per split before another split is used
 constexpr int DEP_MAX_POS = 16;      // depformer steps (dep_q) per frame
 
+// Token pick of a conversation ([LM] Sampling / MoshiLm::pick): greedy argmax, top-k temperature
+// sampling or full-vocabulary Gumbel-max, with the text stream's own temperature and k.
+enum { PICK_GREEDY = 0, PICK_TOPK = 1, PICK_GUMBEL = 2 };
+struct SampleCfg {
+  int32_t mode;
+  float temp, temp_text;
+  int32_t top_k, top_k_text, pad;
+};
+
 // Device-resident session state and activations.
 struct Bufs {
   int32_t *ring;        // [B][NS][3]  token ring ([LM] MoshiState cache)
@@ -52,6 +61,9 @@ struct Bufs {
   uint32_t *attn_cnt;   // [B][H]
   ArgBest *am_part;     // [B][1+Q][AM_MAX_BLOCKS] best row of each head block
   float *rope_freq;     // [hd/2]
+  SampleCfg *samp;      // [B]         token pick of each conversation
+  uint64_t *rng;        // [B]         xorshift state of each conversation's sampler
+  const uint64_t *jump; // [32][64]    columns of the xorshift step's 2^i-th power over GF(2)
 };
 
 // Element e of head h at cache slot `slot` of conversation b's layer: [B][L][cap][H][hd], so the

@@ -17,6 +17,7 @@
 
 #include "batch.h"
 #include "persistent_variants.h"
+#include "sample.h"
 #include "moshi_mi355x.h"
 
 using mk::bf16_t;
@@ -89,6 +90,8 @@ struct moshi_state {
   std::vector<int64_t> h_offset;
 
   hipGraphExec_t gexec = nullptr;
+  bool sampling = false;       // some conversation samples (a pick kernel follows every head)
+  std::vector<int32_t> pick_mode;  // per conversation (host copy)
   std::string err;
   bool broken = false;
 
@@ -309,6 +312,30 @@ void plan_weights(moshi_state *s) {
 
 // Session buffers in one arena.
 // Split-K partial tiles the scratch holds (splits x tiles never exceed it).
+// Columns of the xorshift step's powers M^(2^i), i < JUMP_POW, over GF(2)^64: column j of M is
+// the step applied to the unit vector e_j, and column j of A^2 is A applied to column j of A (the
+// XOR of A's columns picked by its bits).
+void xorshift_jump_table(uint64_t *tab) {
+  auto step = [](uint64_t x) {
+    x ^= x << 13;
+    x ^= x >> 7;
+    x ^= x << 17;
+    return x;
+  };
+  uint64_t cur[64], nxt[64];
+  for (int j = 0; j < 64; ++j) cur[j] = step(1ull << j);
+  for (int i = 0; i < mk::JUMP_POW; ++i) {
+    std::memcpy(tab + (size_t)i * 64, cur, sizeof cur);
+    for (int j = 0; j < 64; ++j) {
+      uint64_t y = 0;
+      for (int bit = 0; bit < 64; ++bit)
+        if ((cur[j] >> bit) & 1ull) y ^= cur[bit];
+      nxt[j] = y;
+    }
+    std::memcpy(cur, nxt, sizeof cur);
+  }
+}
+
 int gemm_part_tiles(int cus) { return 8 * cus; }
 size_t gemm_part_bytes(int cus) {
   return (size_t)gemm_part_tiles(cus) * (mk::GWAVES * 32 * mk::XNMAX) * mk::XM * sizeof(float);
@@ -349,6 +376,9 @@ moshi_status alloc_session(moshi_state *s) {
   req((void **)&b.attn_cnt, B * d.H * 4);
   req((void **)&b.am_part, B * (1 + d.Q) * mk::AM_MAX_BLOCKS * sizeof(mk::ArgBest));
   req((void **)&b.rope_freq, (size_t)(d.hd / 2) * 4);
+  req((void **)&b.samp, B * sizeof(mk::SampleCfg));
+  req((void **)&b.rng, B * 8);
+  req((void **)&b.jump, (size_t)mk::JUMP_POW * 64 * 8);
   const size_t nph = (size_t)5 * d.L + 1 + (size_t)d.Q * (4 * d.Ld + 1) + 1;
   req((void **)&s->sync, (size_t)std::max(s->cus, 64) * 4);  // one phase flag per persistent block
   // y0 [Q][Dd], then per (depformer layer, step) k | v | q | y1 | a | y2; zeroed below, so the tag
@@ -395,6 +425,14 @@ moshi_status alloc_session(moshi_state *s) {
     fr[i] = (float)std::exp((double)arg);
   }
   HIP_TRY(s, hipMemcpy(b.rope_freq, fr.data(), fr.size() * 4, hipMemcpyHostToDevice));
+  // samplers: greedy (zeroed SampleCfg), xorshift state 1 (seed 0), and the jump table
+  {
+    std::vector<uint64_t> tab((size_t)mk::JUMP_POW * 64), ones(B, 1ull);
+    xorshift_jump_table(tab.data());
+    HIP_TRY(s, hipMemcpy((void *)b.jump, tab.data(), tab.size() * 8, hipMemcpyHostToDevice));
+    HIP_TRY(s, hipMemcpy(b.rng, ones.data(), B * 8, hipMemcpyHostToDevice));
+    s->pick_mode.assign(B, mk::PICK_GREEDY);
+  }
   s->d_err = b.outpack + B * (1 + d.Q) + B;
   // per-layer weight pointers for the persistent kernel
   {
@@ -574,6 +612,11 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
       k_head<WT, MOSHI_STAGE_TEXT_HEAD><<<dim3(g_text, nb), BLOCK, d.D * f4, st>>>(
           W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, b.x, d.D, N(s->out_norm), d.eps, b.hidden,
           b.text_logits, d.Vt, b.am_part, AM, b0);
+      if (s->sampling) {  // the pick replaces the partials by the token
+        k_pick<<<nb, PICK_BLOCK, d.Vt * 4, st>>>(d, b, 0, b.text_logits + (size_t)b0 * d.Vt, d.Vt, d.Vt,
+                                                 b.am_part + (size_t)b0 * AM, AM, g_text, b0);
+        prev_parts = 1;
+      }
     });
     // depformer_in[cb] . hidden for every codebook at once
     run(MOSHI_STAGE_DEP_IN, [&] {
@@ -611,6 +654,14 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
         k_head<WT, MOSHI_STAGE_DEP_HEAD><<<dim3(g_dhead, nb), BLOCK, d.Dd * f4, st>>>(
             W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, b.y, d.Dd, nullptr, d.eps, nullptr,
             b.audio_logits + (size_t)cb * d.Va, d.Q * d.Va, b.am_part + (size_t)(1 + cb) * AM_MAX_BLOCKS, AM, b0);
+        if (s->sampling) {
+          k_pick<<<nb, PICK_BLOCK, d.Va * 4, st>>>(d, b, 1 + cb,
+                                                   b.audio_logits + (size_t)b0 * d.Q * d.Va + (size_t)cb * d.Va,
+                                                   d.Q * d.Va, d.Va,
+                                                   b.am_part + ((size_t)b0 * (1 + d.Q) + 1 + cb) * AM_MAX_BLOCKS, AM,
+                                                   g_dhead, b0);
+          prev_parts = 1;
+        }
       });
     }
   }
@@ -855,8 +906,12 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
     k_rows_cvt<XT><<<rows, BLOCK, d.D * f4, st>>>(x, d.D, N(s->out_norm), d.eps, d.D, X, P * d.D,
                                                   b.hidden + (size_t)b0 * d.D, d.D);
     gemm<WT, false, MOSHI_STAGE_TEXT_HEAD>(st, s->cus, s->gpart, W(s->text_lin), s->scale(s->text_lin), d.Vt, d.D, X, P * d.D, rows, b.text_logits + (size_t)b0 * d.Vt, d.Vt);
-    k_argmax_rows<<<rows, BLOCK, 0, st>>>(b.text_logits + (size_t)b0 * d.Vt, d.Vt, d.Vt,
-                                          b.am_part + (size_t)b0 * (1 + d.Q) * AM, (1 + d.Q) * AM);
+    if (s->sampling)
+      k_pick<<<rows, PICK_BLOCK, d.Vt * 4, st>>>(d, b, 0, b.text_logits + (size_t)b0 * d.Vt, d.Vt, d.Vt,
+                                                 b.am_part + (size_t)b0 * (1 + d.Q) * AM, (1 + d.Q) * AM, 0, b0);
+    else
+      k_argmax_rows<<<rows, BLOCK, 0, st>>>(b.text_logits + (size_t)b0 * d.Vt, d.Vt, d.Vt,
+                                            b.am_part + (size_t)b0 * (1 + d.Q) * AM, (1 + d.Q) * AM);
   });
   run(MOSHI_STAGE_DEP_IN, [&] {
     gemm<WT, false, MOSHI_STAGE_DEP_IN>(st, s->cus, s->gpart, W(s->din[0]), s->scale(s->din[0]), d.Q * d.Dd, d.D, X, P * d.D, rows, b.din + (size_t)b0 * d.Q * d.Dd, d.Q * d.Dd);
@@ -926,8 +981,13 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
       // X holds y (converted by the last gate_out projection)
       float *lg = b.audio_logits + (size_t)b0 * d.Q * d.Va + (size_t)cb * d.Va;
       gemm<WT, false, MOSHI_STAGE_DEP_HEAD>(st, s->cus, s->gpart, W(s->lin[cb]), s->scale(s->lin[cb]), d.Va, d.Dd, X, P * d.Dd, rows, lg, d.Q * d.Va);
-      k_argmax_rows<<<rows, BLOCK, 0, st>>>(lg, d.Q * d.Va, d.Va, b.am_part + ((size_t)b0 * (1 + d.Q) + 1 + cb) * AM,
-                                            (1 + d.Q) * AM);
+      if (s->sampling)
+        k_pick<<<rows, PICK_BLOCK, d.Va * 4, st>>>(d, b, 1 + cb, lg, d.Q * d.Va, d.Va,
+                                                   b.am_part + ((size_t)b0 * (1 + d.Q) + 1 + cb) * AM, (1 + d.Q) * AM,
+                                                   0, b0);
+      else
+        k_argmax_rows<<<rows, BLOCK, 0, st>>>(lg, d.Q * d.Va, d.Va,
+                                              b.am_part + ((size_t)b0 * (1 + d.Q) + 1 + cb) * AM, (1 + d.Q) * AM);
     });
   }
   run(MOSHI_STAGE_FRAME_END, [&] { k_frame_end<<<nb, BLOCK, 0, st>>>(d, b, b0, 0, mk::Forced{}, 1); });
@@ -1676,6 +1736,58 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
   if (dy) (void)hipFree(dy);
   if (st) (void)hipStreamDestroy(st);
   return rc;
+}
+
+moshi_status moshi_set_sampling(moshi_state *s, int32_t conv, const moshi_sampling *smp) {
+  if (!s) return MOSHI_EINVAL;
+  if (!smp || conv < -1 || conv >= s->d.B) return fail(s, MOSHI_EINVAL, "bad conversation or NULL sampling");
+  const int mode = smp->mode;
+  if (mode < MOSHI_PICK_GREEDY || mode > MOSHI_PICK_GUMBEL) return fail(s, MOSHI_EINVAL, "unknown pick mode %d", mode);
+  if (mode != MOSHI_PICK_GREEDY &&
+      !(smp->temp > 0.f && smp->temp_text > 0.f && std::isfinite(smp->temp) && std::isfinite(smp->temp_text)))
+    return fail(s, MOSHI_EINVAL, "temperatures must be positive and finite");
+  if (mode == MOSHI_PICK_TOPK) {
+    if (smp->top_k < 1 || smp->top_k > mk::TOPK_MAX || smp->top_k_text < 1 || smp->top_k_text > mk::TOPK_MAX)
+      return fail(s, MOSHI_EINVAL, "top-k must be in [1, %d]", mk::TOPK_MAX);
+    if ((size_t)std::max(s->d.Vt, s->d.Va) * 4 + sizeof(mk::PickScratch) > 160 * 1024)
+      return fail(s, MOSHI_EINVAL, "top-k sampling needs a head of at most 36864 logits");
+    if (s->cfg.exec == MOSHI_EXEC_PERSISTENT)
+      return fail(s, MOSHI_EINVAL, "the persistent executor samples by full-vocabulary Gumbel-max only");
+  }
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  HIP_TRY(s, hipStreamSynchronize(s->stream));
+  mk::SampleCfg c{};
+  c.mode = mode;
+  c.temp = smp->temp;
+  c.temp_text = smp->temp_text;
+  c.top_k = smp->top_k;
+  c.top_k_text = smp->top_k_text;
+  const uint64_t state = smp->seed ? smp->seed : 1ull;
+  const int b0 = conv < 0 ? 0 : conv, nb = conv < 0 ? s->d.B : 1;
+  for (int b = b0; b < b0 + nb; ++b) {
+    HIP_TRY(s, hipMemcpy(s->b.samp + b, &c, sizeof c, hipMemcpyHostToDevice));
+    HIP_TRY(s, hipMemcpy(s->b.rng + b, &state, 8, hipMemcpyHostToDevice));
+    s->pick_mode[b] = mode;
+  }
+  bool any = false;
+  for (int m : s->pick_mode) any = any || m != MOSHI_PICK_GREEDY;
+  if (any != s->sampling) {  // the frame's launches change: capture the graph again
+    s->sampling = any;
+    if (s->gexec) {
+      (void)hipGraphExecDestroy(s->gexec);
+      s->gexec = nullptr;
+    }
+  }
+  return MOSHI_OK;
+}
+
+moshi_status moshi_sampler_state(moshi_state *s, int32_t conv, uint64_t *state) {
+  if (!s) return MOSHI_EINVAL;
+  if (!state || conv < 0 || conv >= s->d.B) return fail(s, MOSHI_EINVAL, "bad conversation or NULL state");
+  if (bind_device(s) != MOSHI_OK) return MOSHI_EDEVICE;
+  HIP_TRY(s, hipStreamSynchronize(s->stream));
+  HIP_TRY(s, hipMemcpy(state, s->b.rng + conv, 8, hipMemcpyDeviceToHost));
+  return MOSHI_OK;
 }
 
 static bool same_model(const moshi_config &a, const moshi_config &b) {

@@ -27,7 +27,7 @@ from tests.gpu_util import TraceStats
 
 pytestmark = pytest.mark.gpu
 
-REL_F32KV = 1e-3
+REL_F32KV = 1e-4  # B=1 bf16 weights, float32 KV: summation order only
 
 
 def tick(msg, t0):
