@@ -364,6 +364,24 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
  */
 moshi_status moshi_debug_read_bw(int64_t bytes, int32_t iters, double *gbs);
 
+/*
+ * Y[M][N] = X[M][K] . W[N][K]^T (times the int8 row scales) with the matrix-core projection of
+ * moshi_debug_gemm, for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): it allocates nothing and only enqueues
+ * kernels on `hip_stream` (a hipStream_t, NULL for the null stream); the caller synchronises.
+ * All pointers are device memory owned by the caller: W row-major in the band's storage (float32,
+ * bfloat16 bits, or int8 with `scale` [N] float32 per-row scales; scale is ignored otherwise),
+ * X float32 [M][K], Y float32 [M][N] (written).  The bf16 and int8 bands round X to bf16 hi / lo
+ * parts as the batched frame does.  Its scratch (those activation planes and the split-K partial
+ * tiles) is a 32 MiB device array inside the library, one per device, held until the process
+ * ends and shared by every call on that device: calls that overlap on one device race, and each
+ * call overwrites what the previous one left there.  Limits: 1 <= M <= 256, K a multiple of 16 in
+ * [16, 16384], 4 M K <= 16 MiB for the bf16 and int8 bands.  Errors: MOSHI_EINVAL (bad argument),
+ * MOSHI_ERANGE (beyond the scratch), MOSHI_EDEVICE (HIP error at launch).
+ */
+moshi_status moshi_gemm_noalloc(int32_t band, int32_t M, int32_t N, int32_t K, const void *W, const float *scale,
+                                const float *X, float *Y, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,6 +51,7 @@ _SIGS = {
     "moshi_snapshot_free": (None, [_vp]),
     "moshi_set_sampling": (_i32, [_vp, _i32, _vp]),
     "moshi_sampler_state": (_i32, [_vp, _i32, _vp]),
+    "moshi_gemm_noalloc": (_i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
 }
 
 STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv", "dep_out",
@@ -370,3 +371,9 @@ def debug_read_bw(nbytes: int = 1 << 30, iters: int = 20) -> float:
     if st != MOSHI_OK:
         raise MoshiError(st, f"moshi_debug_read_bw: {lib.moshi_status_string(st).decode()}")
     return g.value
+
+
+def gemm_noalloc(band: str, M: int, N: int, K: int, W_ptr: int, scale_ptr, X_ptr: int, Y_ptr: int, stream=None) -> int:
+    """moshi_gemm_noalloc on device pointers (ints); enqueues only.  Returns the status."""
+    lib = load_library()
+    return lib.moshi_gemm_noalloc(BANDS[band], M, N, K, W_ptr, scale_ptr, X_ptr, Y_ptr, stream)

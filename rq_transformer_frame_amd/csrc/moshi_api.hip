@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <mutex>
 #include <type_traits>
 #include <string>
 #include <unordered_map>
@@ -701,9 +702,9 @@ void gemm_split(int N, int K, int M, int xn, int cus, int cap_tiles, int &S, int
 struct GemmPlan {
   int nt, S, kbs;
 };
-GemmPlan gemm_plan(int N, int K, int M, int cus) {
+GemmPlan gemm_plan(int N, int K, int M, int cus, int cap_tiles = -1) {
   GemmPlan g{(K >= 4096 && (N >= 8192 || M >= 256)) ? 2 : 1, 1, 1};
-  gemm_split(N, K, M, mk::GWAVES * 32 * g.nt, cus, gemm_part_tiles(cus), g.S, g.kbs);
+  gemm_split(N, K, M, mk::GWAVES * 32 * g.nt, cus, cap_tiles < 0 ? gemm_part_tiles(cus) : cap_tiles, g.S, g.kbs);
   return g;
 }
 
@@ -726,13 +727,13 @@ void gemm_x_launch(hipStream_t st, const GemmPlan &g, float *part, const WT *W, 
 // tiles.  X is in the XPut layout with row stride ldx.
 template <typename WT, bool ADD, int TAG>
 void gemm(hipStream_t st, int cus, float *part, const WT *W, const float *scale, int N, int K,
-          const typename mk::GemmX<WT>::type *X, int ldx, int M, float *Y, int ldy) {
+          const typename mk::GemmX<WT>::type *X, int ldx, int M, float *Y, int ldy, int cap_tiles = -1) {
   using namespace mk;
   if constexpr (std::is_same<WT, float>::value) {
     k_gemm<float, ADD, TAG><<<dim3((N + GN - 1) / GN, (M + GM - 1) / GM), GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M,
                                                                                           Y, ldy);
   } else {
-    const GemmPlan g = gemm_plan(N, K, M, cus);
+    const GemmPlan g = gemm_plan(N, K, M, cus, cap_tiles);
     gemm_x_launch<WT, ADD, TAG>(st, g, part, W, scale, N, K, X, ldx, M, Y, ldy);
     if (g.S > 1)
       k_gemm_reduce<ADD><<<dim3((N + 4 * BLOCK - 1) / (4 * BLOCK), M), BLOCK, 0, st>>>(part, g.S, M, N, scale, Y, ldy);
@@ -1115,6 +1116,37 @@ moshi_status bind_device(moshi_state *s) {
   return MOSHI_OK;
 }
 
+}  // namespace
+
+// ---------------------------------------------------------------------------------------------
+// Projection without allocation: its scratch (the bf16 hi / lo planes of the activations and the
+// split-K partial tiles) is this file-scope device array, one copy per device, held until the
+// process ends.  Host code never passes the array's name to a kernel: `scratch` names a host-side
+// stand-in there.  The device address is looked up once per device with hipGetSymbolAddress and
+// kept in scratch_dev.
+// ---------------------------------------------------------------------------------------------
+constexpr size_t NOALLOC_BYTES = (size_t)32 << 20;   // the whole scratch
+constexpr size_t NOALLOC_PLANES = (size_t)16 << 20;  // its first part: activation planes, 4 M K bytes
+constexpr int NOALLOC_MAX_DEVICES = 64;
+
+static __device__ __align__(256) char scratch[NOALLOC_BYTES];
+
+namespace {
+std::mutex scratch_mu;
+void *scratch_dev[NOALLOC_MAX_DEVICES] = {};
+
+// The device address of `scratch` on `dev` (the current device), looked up on first use.
+hipError_t scratch_on(int dev, char **out) {
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_dev[dev] = p;
+  }
+  *out = reinterpret_cast<char *>(scratch_dev[dev]);
+  return hipSuccess;
+}
 }  // namespace
 
 // =============================================================================================
@@ -1906,20 +1938,34 @@ moshi_status moshi_debug_read_bw(int64_t bytes, int32_t iters, double *gbs) {
     }
     return rc == MOSHI_OK;
   };
-  const int blocks_per_cu = 4;
+  // launch shapes tried: (blocks per compute unit, threads per block); the best rate is reported
+  const int shapes[][2] = {{1, 512}, {2, 512}, {1, 1024}, {4, 256}, {8, 256}};
+  const int max_bpc = 8;
+  *gbs = 0.0;
   if (chk(hipGetDevice(&dev)) && chk(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) &&
       chk(hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) && chk(hipMalloc(&buf, (size_t)n16 * 16)) &&
-      chk(hipMalloc(&sink, (size_t)cus * blocks_per_cu * 4)) && chk(hipMemsetAsync(buf, 0x5A, (size_t)n16 * 16, st))) {
-    const dim3 grid((unsigned)(cus * blocks_per_cu));
-    mk::k_read_probe<<<grid, mk::BLOCK, 0, st>>>(reinterpret_cast<const uint4 *>(buf), n16, sink);  // warm-up
-    if (chk(hipGetLastError()) && chk(hipEventCreate(&e0)) && chk(hipEventCreate(&e1)) && chk(hipEventRecord(e0, st))) {
-      for (int i = 0; i < iters; ++i)
-        mk::k_read_probe<<<grid, mk::BLOCK, 0, st>>>(reinterpret_cast<const uint4 *>(buf), n16, sink);
+      chk(hipMalloc(&sink, (size_t)cus * max_bpc * 4)) && chk(hipMemsetAsync(buf, 0x5A, (size_t)n16 * 16, st)) &&
+      chk(hipEventCreate(&e0)) && chk(hipEventCreate(&e1))) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(buf);
+    for (const auto &sh : shapes) {
+      const dim3 grid((unsigned)(cus * sh[0]));
+      auto launch = [&]() {
+        if (sh[1] == 256)
+          mk::k_read_probe<256><<<grid, 256, 0, st>>>(src, n16, sink);
+        else if (sh[1] == 512)
+          mk::k_read_probe<512><<<grid, 512, 0, st>>>(src, n16, sink);
+        else
+          mk::k_read_probe<1024><<<grid, 1024, 0, st>>>(src, n16, sink);
+      };
+      launch();  // warm-up
+      if (!chk(hipGetLastError()) || !chk(hipEventRecord(e0, st))) break;
+      for (int i = 0; i < iters; ++i) launch();
       chk(hipGetLastError());
       chk(hipEventRecord(e1, st));
       chk(hipEventSynchronize(e1));
       float ms = 0.f;
-      if (chk(hipEventElapsedTime(&ms, e0, e1))) *gbs = (double)n16 * 16.0 * iters / ((double)ms * 1e-3) / 1e9;
+      if (chk(hipEventElapsedTime(&ms, e0, e1)))
+        *gbs = std::max(*gbs, (double)n16 * 16.0 * iters / ((double)ms * 1e-3) / 1e9);
     }
   }
   if (e0) (void)hipEventDestroy(e0);
@@ -1928,6 +1974,57 @@ moshi_status moshi_debug_read_bw(int64_t bytes, int32_t iters, double *gbs) {
   if (sink) (void)hipFree(sink);
   if (st) (void)hipStreamDestroy(st);
   return rc;
+}
+
+moshi_status moshi_gemm_noalloc(int32_t band, int32_t M, int32_t N, int32_t K, const void *W, const float *scale,
+                                const float *X, float *Y, void *hip_stream) {
+  if (band < MOSHI_BAND_F32 || band > MOSHI_BAND_I8 || M < 1 || M > 256 || N < 1 || K < 16 || K % 16 || K > 16384 ||
+      !W || !X || !Y || (band == MOSHI_BAND_I8 && !scale)) {
+    fprintf(stderr, "moshi_gemm_noalloc: bad arguments (band %d, M %d, N %d, K %d)\n", band, M, N, K);
+    return MOSHI_EINVAL;
+  }
+  if (band != MOSHI_BAND_F32 && (size_t)4 * M * K > NOALLOC_PLANES) {
+    fprintf(stderr, "moshi_gemm_noalloc: 4 M K = %zu bytes of activation planes exceed the %zu-byte scratch share\n",
+            (size_t)4 * M * K, NOALLOC_PLANES);
+    return MOSHI_ERANGE;
+  }
+  if ((size_t)N * K * linear_elt(band) >= ((size_t)1 << 31)) {
+    fprintf(stderr, "moshi_gemm_noalloc: weights of 2^31 bytes or more\n");
+    return MOSHI_EINVAL;
+  }
+  int dev = 0, cus = 0;
+  char *scr = nullptr;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MOSHI_EDEVICE;
+  const hipError_t se = scratch_on(dev, &scr);
+  if (se != hipSuccess) {
+    fprintf(stderr, "moshi_gemm_noalloc: hipGetSymbolAddress(scratch): %s\n", hipGetErrorString(se));
+    return MOSHI_EDEVICE;
+  }
+  hipStream_t st = (hipStream_t)hip_stream;
+  // the partial tiles get the scratch after the planes: at most that many tiles per split plan
+  float *part = reinterpret_cast<float *>(scr + NOALLOC_PLANES);
+  const size_t tile_bytes = gemm_part_bytes(1) / gemm_part_tiles(1);
+  const int cap = (int)((NOALLOC_BYTES - NOALLOC_PLANES) / tile_bytes);
+  bf16_t *planes = reinterpret_cast<bf16_t *>(scr);
+  if (band == MOSHI_BAND_F32) {
+    gemm<float, false, MOSHI_N_STAGES>(st, cus, nullptr, reinterpret_cast<const float *>(W), nullptr, N, K, X, K, M, Y, N);
+  } else {
+    mk::k_rows_cvt<bf16_t><<<M, mk::BLOCK, K * 4, st>>>(X, K, nullptr, 0.f, K, planes, 2 * K, nullptr, 0);
+    if (band == MOSHI_BAND_BF16)
+      gemm<bf16_t, false, MOSHI_N_STAGES>(st, cus, part, reinterpret_cast<const bf16_t *>(W), nullptr, N, K, planes,
+                                          2 * K, M, Y, N, cap);
+    else
+      gemm<int8_t, false, MOSHI_N_STAGES>(st, cus, part, reinterpret_cast<const int8_t *>(W), scale, N, K, planes, 2 * K,
+                                          M, Y, N, cap);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    fprintf(stderr, "moshi_gemm_noalloc: %s\n", hipGetErrorString(e));
+    return MOSHI_EDEVICE;
+  }
+  return MOSHI_OK;
 }
 
 moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, const float *W, const float *X,
