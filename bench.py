@@ -176,11 +176,76 @@ def cpu_baseline(cfg, weights, users, budget_s: float, max_frames: int):
             "host": host_record(), "tiny_f32_16_frames": tiny_oracle_fps()}
 
 
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def prefill_flops(cfg, T: int, p0: int = 0):
+    """Algorithmic flops of a teacher-forced prefill of T positions from offset p0, as (projections,
+    attention): every temporal projection once per position (2 flops per weight), and per layer and
+    position the scores and the weighted sum over its min(pos + 1, context) cached positions
+    (2 x 2 x d_model flops each)."""
+    D, F, L = cfg.d_model, cfg.ffn_hidden, cfg.n_layers
+    params = L * (3 * D * D + D * D + 2 * F * D + D * F)
+    pos = np.arange(p0, p0 + T)
+    ctx = np.minimum(pos + 1, cfg.context).sum()
+    return 2.0 * params * T, 4.0 * D * L * float(ctx)
+
+
+def prefill_main(args, cfg):
+    """Prompt throughput: K teacher-forced prefills of cfg.prefill frames from offset 0 (each after a
+    reset), timed on the host around the synchronous moshi_prefill_forced calls."""
+    import rq_transformer_frame_amd as rq
+    import synth
+    T = cfg.prefill
+    K = args.steps if args.steps is not None else cfg.frames
+    W = max(1, args.warmup if args.warmup is not None else 1)
+    t = time.time()
+    weights = synth.gen_weights(cfg)
+    log(f"generated {cfg.name} weights (seed {cfg.seed}) in {time.time() - t:.1f}s")
+    text, agent, user = synth.prefill_tokens(cfg, T)
+    sess = rq.Session(cfg, exec="graph", kv=args.kv)
+    sess.load_weights(weights)
+    del weights
+    for _ in range(W):
+        sess.reset()
+        sess.prefill_forced(0, text, agent, user)
+    times = []
+    for _ in range(K):
+        sess.reset()
+        t0 = time.perf_counter()
+        sess.prefill_forced(0, text, agent, user)
+        times.append(time.perf_counter() - t0)
+    sess.close()
+    dt = float(np.sum(times))
+    per = dt / K
+    proj, attn = prefill_flops(cfg, T)
+    fl = proj + attn
+    tflops = fl / per / 1e12
+    log(f"{K} prefills of {T} frames: {per * 1e3:.1f} ms each, {T / per:.0f} prompt frames/s, {tflops:.1f} TFLOP/s")
+    return {
+        "metric": f"prompt frames/s (teacher-forced prefill of {T} frames), Moshi-7B shape bf16",
+        "value": round(T / per, 1), "unit": "prompt frames/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(1000 * per, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: teacher-forced prefill of {T} frames of uniform tokens from offset 0 "
+                               f"(seed {cfg.seed}), temporal layers only, row batches on the matrix cores",
+                   "batch": 1, "band": cfg.band, "kv": args.kv, "accumulate": "f32",
+                   "activations": "bf16 hi + lo parts (two products per step)"},
+        "roofline": {"bound": "mfma", "kernel": "whole prefill (matrix-core projections, attention, epilogues)",
+                     "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": fl, "avg_us": round(per * 1e6, 1),
+                     # the projections run two bf16 products per step (activation hi and lo parts)
+                     "mfma_issued_tflops": round(2 * proj / per / 1e12, 1)},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed frames (default: the workload's frame count)")
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 10; prefill 1)")
     ap.add_argument("--config", default="moshi7b_bf16_b1")
     ap.add_argument("--exec", default="persistent", choices=["graph", "persistent", "stream"])
     ap.add_argument("--profile-frames", type=int, default=10)
@@ -212,12 +277,15 @@ def main():
         del a, b
 
     cfg = synth.CONFIGS[args.config]
+    if cfg.name.endswith("_prefill"):
+        print(json.dumps(prefill_main(args, cfg)), flush=True)
+        return
     band = cfg.band
     B = cfg.batch
     t = time.time()
     weights = synth.gen_weights(cfg)
     log(f"generated {cfg.name} weights (seed {cfg.seed}) in {time.time() - t:.1f}s")
-    K, W = (args.steps if args.steps is not None else cfg.frames), args.warmup
+    K, W = (args.steps if args.steps is not None else cfg.frames), (args.warmup if args.warmup is not None else 10)
     nprof = args.profile_frames
     nframes = nprof + W + K
 

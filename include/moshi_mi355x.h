@@ -357,9 +357,10 @@ moshi_status moshi_debug_gemm(int32_t band, int32_t M, int32_t N, int32_t K, con
 /*
  * Measurement: the device's streaming-read rate, the ceiling the frame's weight streaming is
  * compared with.  A kernel reads `bytes` of a fresh device allocation with 16-byte nontemporal
- * loads (8 per lane in flight, 4 blocks of 256 threads per compute unit, each block a contiguous
- * share), once untimed and then `iters` times between HIP events; *gbs receives bytes x iters /
- * elapsed time in GB/s (10^9 bytes per second).  Errors: MOSHI_EINVAL (bytes outside
+ * loads (8 per lane in flight, each block a contiguous share), once untimed and then `iters`
+ * times between HIP events, for each of a few launch shapes (1 to 8 blocks of 256 to 1024
+ * threads per compute unit); *gbs receives the best bytes x iters / elapsed time in GB/s (10^9
+ * bytes per second).  Errors: MOSHI_EINVAL (bytes outside
  * [2^20, 2^31 - 16], iters < 1, gbs NULL), MOSHI_ENOMEM, MOSHI_EDEVICE.
  */
 moshi_status moshi_debug_read_bw(int64_t bytes, int32_t iters, double *gbs);

@@ -771,12 +771,12 @@ __global__ __launch_bounds__(BLOCK) void k_kv_snapshot(Dims d, KV<KT> kv, KT *__
   }
 }
 
-// Streaming-read probe (measurement): block b reads its contiguous share of n16 16-byte vectors
+// Streaming-read probe (measurement): block b of NT threads reads its contiguous share of n16 16-byte vectors
 // with nontemporal buffer loads, 8 per lane in flight and no load under a branch (past the share's
 // end the buffer resource returns zeros), and folds them into one word; the word is stored only if
 // it equals a value no input here produces, which keeps the loads without a real store.
-static __global__ __launch_bounds__(BLOCK) void k_read_probe(const uint4 *__restrict__ p, int64_t n16,
-                                                          uint32_t *__restrict__ sink) {
+template <int NT>
+__global__ __launch_bounds__(NT) void k_read_probe(const uint4 *__restrict__ p, int64_t n16, uint32_t *__restrict__ sink) {
   const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
   const int64_t lo = (int64_t)blockIdx.x * per;
   const int64_t hi = lo + per < n16 ? lo + per : n16;
@@ -784,10 +784,10 @@ static __global__ __launch_bounds__(BLOCK) void k_read_probe(const uint4 *__rest
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void *)(p + lo), (short)0, (int)((hi - lo) * 16), BUF_DWORD3);
   uint32_t acc = 0;
-  for (int64_t i = threadIdx.x; i < hi - lo; i += 8 * BLOCK) {
+  for (int64_t i = threadIdx.x; i < hi - lo; i += 8 * NT) {
     u32x4b v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)((i + u * BLOCK) * 16), 0, BUF_NT);
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (int)((i + u * NT) * 16), 0, BUF_NT);
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }

@@ -154,7 +154,10 @@ MOSHI7B_LONG = MOSHI7B.with_(name="moshi7b_bf16_long", seed=2, prefill=2900, fra
 MOSHI7B_B64 = MOSHI7B.with_(name="moshi7b_bf16_b64", seed=3, batch=64, frames=200, max_start_offset=1000)
 MOSHI7B_I8 = MOSHI7B.with_(name="moshi7b_i8_b1", seed=4, band="i8", frames=250)
 
-CONFIGS = {c.name: c for c in (TINY, MOSHI7B, MOSHI7B_LONG, MOSHI7B_B64, MOSHI7B_I8)}
+# teacher-forced priming as a workload of its own: prefill 2900 frames from offset 0, timed
+MOSHI7B_PREFILL = MOSHI7B.with_(name="moshi7b_bf16_prefill", seed=2, prefill=2900, frames=5)
+
+CONFIGS = {c.name: c for c in (TINY, MOSHI7B, MOSHI7B_LONG, MOSHI7B_B64, MOSHI7B_I8, MOSHI7B_PREFILL)}
 
 
 def weight_specs(cfg: Config):
