@@ -44,8 +44,14 @@ typedef enum {
 typedef enum {
   MOSHI_BAND_F32 = 0,  /* float32 linears and embeddings ([LM] Band::F32, the parity band) */
   MOSHI_BAND_BF16 = 1, /* bfloat16 linears and embeddings, float32 arithmetic */
-  MOSHI_BAND_I8 = 2    /* int8 linears with one float32 scale per output row ([LM] Band::I8);
+  MOSHI_BAND_I8 = 2,   /* int8 linears with one float32 scale per output row ([LM] Band::I8);
                           embeddings bfloat16.  Quantised at load, see moshi_load_weights. */
+  MOSHI_BAND_Q4 = 3,   /* Q4_0 linears ([LM] q4_roundtrip, load_q4sim): per row and 32-column block
+                          one float32 scale and 16 bytes of 4-bit codes; embeddings bfloat16.
+                          Quantised at load.  Batch 1 only (graph, stream, persistent executors). */
+  MOSHI_BAND_Q8 = 4    /* q8_0 linears ([LM] qn_roundtrip at 8 bits, group 32): per row and 32-column
+                          block one float32 scale and 32 int8 codes; embeddings bfloat16.
+                          Quantised at load.  Batch 1 only. */
 } moshi_band;
 
 /* Storage type of the temporal KV cache. */
@@ -84,7 +90,8 @@ typedef enum {
  *                            at offset >= kv_capacity returns MOSHI_ERANGE.
  *   exec                   : a moshi_exec value.
  *   kv_dtype               : a moshi_kv value (0 = float32).
- * Constraints (else MOSHI_EINVAL): d_model % n_heads == 0 with head_dim 64 or 128;
+ * Constraints (else MOSHI_EINVAL): d_model % n_heads == 0 with head_dim 64 or 128; the Q4 and Q8
+ * bands need batch 1 and d_model, ffn_hidden, dep_d_model and dep_ffn_hidden multiples of 32;
  * dep_d_model % dep_heads == 0; 1 <= dep_q <= 16 (Moshi uses 8); d_model, ffn_hidden,
  * dep_d_model and dep_ffn_hidden multiples of 16 and at most 16384; batch >= 1; kv_dtype
  * MOSHI_KV_BF16 only with the bf16 and int8 bands.
@@ -156,8 +163,12 @@ moshi_status moshi_create(const moshi_config *cfg, void *hip_stream, moshi_state
  * float32; MOSHI_BAND_BF16 rounds float32 input to bfloat16 (nearest-even); MOSHI_BAND_I8
  * quantises every linear per output row r: s_r = max_k |w_rk| / 127 (float32), q_rk =
  * round-half-away-from-zero(w_rk / s_r) clamped to [-127, 127], q = 0 when s_r = 0, and the
- * product is s_r * sum_k q_rk x_k.  Norm gains are always float32.  Errors: MOSHI_ESHAPE
- * (unknown name, wrong shape, bad dtype), MOSHI_EDEVICE.
+ * product is s_r * sum_k q_rk x_k.  MOSHI_BAND_Q4 and MOSHI_BAND_Q8 quantise every linear per row
+ * and 32-column block with [LM] qn_roundtrip's rule: d = (the block's value of largest magnitude,
+ * the first on ties) / -2^(b-1) with b = 4 or 8, q = clamp(round-half-away(w * (1 / d)),
+ * -2^(b-1), 2^(b-1) - 1), q = 0 where d = 0; the weight is q * d (float32 operations, IEEE
+ * round to nearest).  Norm gains are always float32.  Errors: MOSHI_ESHAPE (unknown name, wrong
+ * shape, bad dtype), MOSHI_EDEVICE.
  */
 moshi_status moshi_load_weights(moshi_state *s, const moshi_tensor *tensors, int32_t n);
 

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmoshi_mi355x.so")
 
 MOSHI_OK, MOSHI_NONE = 0, 1
 MOSHI_EINVAL, MOSHI_ESTATE, MOSHI_ESHAPE, MOSHI_ENOMEM, MOSHI_EDEVICE, MOSHI_ERANGE = -1, -2, -3, -4, -5, -6
-BANDS = {"f32": 0, "bf16": 1, "i8": 2}
+BANDS = {"f32": 0, "bf16": 1, "i8": 2, "q4": 3, "q8": 4}
 EXEC = {"graph": 0, "stream": 1, "persistent": 2}
 KV = {"f32": 0, "bf16": 1}
 DTYPE_F32, DTYPE_BF16 = 0, 1

@@ -12,7 +12,8 @@ CSRC = os.path.join(PKG, "csrc")
 # slow ones, split by head dim)
 SOURCES = [os.path.join(CSRC, f) for f in (
     "moshi_api.hip", "persistent_hd128_bf16_kvf32.hip", "persistent_hd128_bf16_kvbf16.hip",
-    "persistent_hd128_i8_kvf32.hip", "persistent_hd64.hip")]
+    "persistent_hd128_i8_kvf32.hip", "persistent_hd128_q4_kvf32.hip", "persistent_hd128_q8_kvf32.hip",
+    "persistent_hd64.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

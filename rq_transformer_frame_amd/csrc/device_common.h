@@ -416,6 +416,182 @@ struct PairStream {
 template <> struct RowStream<int8_t> : PairStream<int8_t> {};
 template <> struct RowStream<bf16_t> : PairStream<bf16_t> {};
 
+// ---- block-scaled weights (the Q4_0 and q8_0 bands) --------------------------------------------
+// A row of K weights is K / 32 blocks of 32 columns, each with one float32 scale; the scales of a
+// matrix are [rows][K / 32].  Q4_0: 16 bytes per block, byte i holding the code of column i in its
+// low nibble and of column i + 16 in its high nibble, each code stored + 8 (weight = (nibble - 8)
+// x scale).  q8_0: 32 int8 codes per block (weight = code x scale).
+struct q4_t {
+  uint8_t bits;  // two 4-bit codes
+};
+struct q8_t {
+  int8_t bits;  // one 8-bit code
+};
+
+template <typename QT> struct QVec;
+template <> struct QVec<q4_t> {
+  static constexpr int N = 32;    // weights per 16-byte vector: one whole block
+  static constexpr int VPB = 1;   // vectors per block
+  static constexpr int BPW2 = 1;  // bytes per two weights
+  // weights 16 h .. 16 h + 15 of the vector: the low nibbles (h = 0) or the high ones (h = 1)
+  __device__ __forceinline__ static void cvt16(const uint4 &u, int h, float *f) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t byte = (w[j] >> (8 * b)) & 0xFFu;
+        f[4 * j + b] = (float)((int)(h ? (byte >> 4) : (byte & 15u)) - 8);
+      }
+    }
+  }
+};
+template <> struct QVec<q8_t> {
+  static constexpr int N = 16;
+  static constexpr int VPB = 2;
+  static constexpr int BPW2 = 2;
+  __device__ __forceinline__ static void cvt16(const uint4 &u, int, float *f) { WVec<int8_t>::cvt(u, f); }
+};
+
+// The pair stream for block-scaled weights: rows walked in pairs as in PairStream (one input
+// fragment from LDS feeds both rows), each 16-byte vector's products scaled by its block's scale
+// before they join the row's sum.  Scales are loaded with the vectors (4 bytes per lane and
+// vector, past the row's end zero).  A pair-chunk holds SCH_B vectors per lane of each row: the
+// rows are short in vectors (Q4_0 packs 32 weights in one), and the converted weights of a vector
+// are what fill the registers.
+constexpr int SCH_B = 2;
+
+template <typename QT>
+struct BlockPairStream {
+  static constexpr int N = QVec<QT>::N;
+  static constexpr int VPB = QVec<QT>::VPB;
+  uint4 a0[SCH_B], b0[SCH_B], a1[SCH_B], b1[SCH_B];
+  float da0[SCH_B], db0[SCH_B], da1[SCH_B], db1[SCH_B];
+  const uint8_t *W;
+  const float *S;
+  int K, nv, nsc, rowb, nch, r0, r1, T;
+  int lp, lc;
+  int cp, cc;
+
+  __device__ __forceinline__ void load(uint4 (&A)[SCH_B], uint4 (&B)[SCH_B], float (&dA)[SCH_B], float (&dB)[SCH_B]) {
+    const int lane = threadIdx.x & 63;
+    const int ra = r0 + 2 * lp, rb = ra + 1;
+    const bool hasb = rb < r1;
+    const __amdgpu_buffer_rsrc_t rsa =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(W + (size_t)ra * rowb), (short)0, rowb, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rsb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(W + (size_t)rb * rowb), (short)0, hasb ? rowb : 0, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t ssa =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(S + (size_t)ra * nsc), (short)0, nsc * 4, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t ssb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(S + (size_t)rb * nsc), (short)0, hasb ? nsc * 4 : 0, BUF_DWORD3);
+    const int soff = lc * (SCH_B * WAVE * 16);
+#pragma unroll
+    for (int i = 0; i < SCH_B; ++i) {
+      const u32x4b va = __builtin_amdgcn_raw_buffer_load_b128(rsa, (i * WAVE + lane) * 16, soff, BUF_NT);
+      const u32x4b vb = __builtin_amdgcn_raw_buffer_load_b128(rsb, (i * WAVE + lane) * 16, soff, BUF_NT);
+      A[i] = uint4{va[0], va[1], va[2], va[3]};
+      B[i] = uint4{vb[0], vb[1], vb[2], vb[3]};
+      const int v = lc * (SCH_B * WAVE) + i * WAVE + lane;
+      dA[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ssa, (v / VPB) * 4, 0, BUF_NT));
+      dB[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ssb, (v / VPB) * 4, 0, BUF_NT));
+    }
+    if (++lc == nch) {
+      lc = 0;
+      ++lp;
+    }
+  }
+
+  __device__ __forceinline__ void begin(const QT *__restrict__ W_, const float *__restrict__ S_, int K_, int r0_,
+                                        int r1_) {
+    W = reinterpret_cast<const uint8_t *>(W_);
+    S = S_;
+    K = K_;
+    nv = K_ / N;
+    nsc = K_ / 32;
+    rowb = K_ * QVec<QT>::BPW2 / 2;
+    nch = (nv + SCH_B * WAVE - 1) / (SCH_B * WAVE);
+    r0 = r0_;
+    r1 = r1_ > r0_ ? r1_ : r0_;
+    T = ((r1 - r0 + 1) / 2) * nch;
+    lp = lc = 0;
+    if (T > 0) load(a0, b0, da0, db0);
+    if (T > 1) load(a1, b1, da1, db1);
+  }
+
+  template <typename Epi>
+  __device__ __forceinline__ void consume(const uint4 (&A)[SCH_B], const uint4 (&B)[SCH_B], const float (&dA)[SCH_B],
+                                          const float (&dB)[SCH_B], const float *__restrict__ xs, float &acca,
+                                          float &accb, Epi &epi) {
+    const int lane = threadIdx.x & 63;
+    const int left = nv - cc * (SCH_B * WAVE);
+    const float *xp = xs + (size_t)(cc * (SCH_B * WAVE) + lane) * N;
+#pragma unroll
+    for (int i = 0; i < SCH_B; ++i) {
+      if (left >= SCH_B * WAVE || i * WAVE + lane < left) {
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int h = 0; h < N / 16; ++h) {  // 16 weights of both rows per pass
+          float xv[16], wa[16], wb[16];
+#pragma unroll
+          for (int e = 0; e < 16; e += 4) {
+            const float4 q = *reinterpret_cast<const float4 *>(xp + i * WAVE * N + 16 * h + e);
+            xv[e] = q.x;
+            xv[e + 1] = q.y;
+            xv[e + 2] = q.z;
+            xv[e + 3] = q.w;
+          }
+          QVec<QT>::cvt16(A[i], h, wa);
+          QVec<QT>::cvt16(B[i], h, wb);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            sa = fmaf(wa[e], xv[e], sa);
+            sb = fmaf(wb[e], xv[e], sb);
+          }
+        }
+        acca = fmaf(dA[i], sa, acca);
+        accb = fmaf(dB[i], sb, accb);
+      }
+    }
+    if (cc == nch - 1) {
+      const int ra = r0 + 2 * cp, rb = ra + 1;
+      const float va = wave_sum(acca), vb = wave_sum(accb);
+      epi(ra, va);
+      if (rb < r1) epi(rb, vb);
+      acca = accb = 0.f;
+      cc = 0;
+      ++cp;
+    } else {
+      ++cc;
+    }
+  }
+
+  template <typename Epi>
+  __device__ __forceinline__ void run(const float *__restrict__ xs, Epi &&epi) {
+    float acca = 0.f, accb = 0.f;
+    cp = cc = 0;
+    int t = 0;
+    for (; t + 3 < T; t += 2) {
+      consume(a0, b0, da0, db0, xs, acca, accb, epi);
+      load(a0, b0, da0, db0);
+      consume(a1, b1, da1, db1, xs, acca, accb, epi);
+      load(a1, b1, da1, db1);
+    }
+    const int rem = T - t;
+    if (rem >= 1) consume(a0, b0, da0, db0, xs, acca, accb, epi);
+    if (rem == 3) load(a0, b0, da0, db0);
+    if (rem >= 2) consume(a1, b1, da1, db1, xs, acca, accb, epi);
+    if (rem == 3) consume(a0, b0, da0, db0, xs, acca, accb, epi);
+  }
+};
+
+template <> struct RowStream<q4_t> : BlockPairStream<q4_t> {};
+template <> struct RowStream<q8_t> : BlockPairStream<q8_t> {};
+
+template <typename WT> struct IsBlockBand : std::false_type {};
+template <> struct IsBlockBand<q4_t> : std::true_type {};
+template <> struct IsBlockBand<q8_t> : std::true_type {};
+
 // Index of the calling wave in its block, as a wave-uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

@@ -752,6 +752,46 @@ static __global__ void k_force(Dims d, Bufs s, int b, Forced forced) {
   for (int st = 0; st <= d.Q; ++st) s.ring[((size_t)b * d.NS + st) * 3 + p] = forced.t[st];
 }
 
+// Block quantisation at load time (the Q4_0 band with BITS = 4, q8_0 with BITS = 8), per row and
+// 32-column block: d = (the block's value of largest magnitude, the first on ties) / -2^(BITS-1),
+// code = clamp(round-half-away(x * (1 / d)), -2^(BITS-1), 2^(BITS-1) - 1), code 0 where d = 0; the
+// float32 operations are IEEE round-to-nearest (no contraction).  Q4_0 stores code + 8 as a nibble,
+// column i in the low and i + 16 in the high nibble of byte i of the block's 16; q8_0 stores the
+// int8 codes.  One block of threads per row, one thread per 32-column block.
+template <int BITS>
+static __global__ __launch_bounds__(BLOCK) void k_quant_blocks(const float *__restrict__ w, int K,
+                                                            uint8_t *__restrict__ codes, float *__restrict__ scale,
+                                                            int64_t row0) {
+  const int64_t r = row0 + blockIdx.x;
+  const float *wr = w + (size_t)blockIdx.x * K;
+  const int nb = K / 32;
+  const int qmin = -(1 << (BITS - 1)), qmax = (1 << (BITS - 1)) - 1;
+  for (int bk = threadIdx.x; bk < nb; bk += BLOCK) {
+    const float *x = wr + bk * 32;
+    float amax = 0.f, mx = 0.f;
+    for (int j = 0; j < 32; ++j)
+      if (fabsf(x[j]) > amax) {
+        amax = fabsf(x[j]);
+        mx = x[j];
+      }
+    const float d = __fdiv_rn(mx, (float)qmin);
+    const float id = d != 0.f ? __fdiv_rn(1.0f, d) : 0.f;
+    int q[32];
+    for (int j = 0; j < 32; ++j) {
+      const float v = roundf(__fmul_rn(x[j], id));
+      q[j] = (int)fminf(fmaxf(v, (float)qmin), (float)qmax);
+    }
+    scale[(size_t)r * nb + bk] = d;
+    if (BITS == 4) {
+      uint8_t *o = codes + (size_t)r * (K / 2) + bk * 16;
+      for (int i = 0; i < 16; ++i) o[i] = (uint8_t)((q[i] + 8) | ((q[i + 16] + 8) << 4));
+    } else {
+      int8_t *o = reinterpret_cast<int8_t *>(codes) + (size_t)r * K + bk * 32;
+      for (int j = 0; j < 32; ++j) o[j] = (int8_t)q[j];
+    }
+  }
+}
+
 // Session snapshot ([LM] MoshiState::snapshot): copy the n cached positions p0 .. p0 + n - 1 of
 // conversation b's temporal KV (position p at slot p % cap) to (to_buf = 1) or from (0) a
 // position-ordered buffer [2][L][n][D] (keys, then values).  Grid (n, L).

@@ -134,7 +134,7 @@ struct moshi_state {
   }
   const void *data(int slot) const { return warena + slots[slot].off; }
   const float *scale(int slot) const {
-    return cfg.band == MOSHI_BAND_I8 ? reinterpret_cast<const float *>(warena + slots[slot].soff) : nullptr;
+    return cfg.band >= MOSHI_BAND_I8 ? reinterpret_cast<const float *>(warena + slots[slot].soff) : nullptr;
   }
 };
 
@@ -171,6 +171,16 @@ moshi_status fail(moshi_state *s, moshi_status code, const char *fmt, ...) {
 
 size_t linear_elt(int band) { return band == MOSHI_BAND_F32 ? 4 : band == MOSHI_BAND_BF16 ? 2 : 1; }
 size_t embed_elt(int band) { return band == MOSHI_BAND_F32 ? 4 : 2; }
+// Bytes of a linear's weights and of its scales in a band.
+size_t linear_bytes(int band, int64_t rows, int64_t cols) {
+  const size_t n = (size_t)rows * (size_t)cols;
+  return band == MOSHI_BAND_Q4 ? n / 2 : n * linear_elt(band);
+}
+size_t scale_bytes(int band, int64_t rows, int64_t cols) {
+  if (band == MOSHI_BAND_I8) return (size_t)rows * 4;
+  if (band == MOSHI_BAND_Q4 || band == MOSHI_BAND_Q8) return (size_t)rows * (size_t)(cols / 32) * 4;
+  return 0;
+}
 
 // The storage types of a session: weights, embedding tables, KV cache.
 template <typename W, typename E, typename K>
@@ -188,6 +198,10 @@ void with_types(const moshi_config &c, F &&f) {
       return f(Types<float, float, float>{});
     case MOSHI_BAND_BF16:
       return kvb ? f(Types<bf16_t, bf16_t, bf16_t>{}) : f(Types<bf16_t, bf16_t, float>{});
+    case MOSHI_BAND_Q4:
+      return kvb ? f(Types<mk::q4_t, bf16_t, bf16_t>{}) : f(Types<mk::q4_t, bf16_t, float>{});
+    case MOSHI_BAND_Q8:
+      return kvb ? f(Types<mk::q8_t, bf16_t, bf16_t>{}) : f(Types<mk::q8_t, bf16_t, float>{});
     default:
       return kvb ? f(Types<int8_t, bf16_t, bf16_t>{}) : f(Types<int8_t, bf16_t, float>{});
   }
@@ -216,16 +230,18 @@ void plan_weights(moshi_state *s) {
   auto place = [&](int i) {
     Slot &sl = s->slots[i];
     const int64_t n = sl.rows * std::max<int64_t>(sl.cols, 1);
-    const size_t elt = sl.kind == K_LINEAR ? linear_elt(band) : sl.kind == K_EMBED ? embed_elt(band) : 4;
+    const size_t bytes = sl.kind == K_LINEAR ? linear_bytes(band, sl.rows, sl.cols)
+                                             : (size_t)n * (sl.kind == K_EMBED ? embed_elt(band) : 4);
     sl.off = off;
-    off += (size_t)n * elt;
-    if (sl.kind == K_LINEAR) s->linear_bytes += (int64_t)n * (int64_t)elt;
+    off += bytes;
+    if (sl.kind == K_LINEAR) s->linear_bytes += (int64_t)bytes;
   };
   auto place_scales = [&](int i) {
-    if (band != MOSHI_BAND_I8) return;
+    const size_t sb = scale_bytes(band, s->slots[i].rows, s->slots[i].cols);
+    if (!sb) return;
     s->slots[i].soff = off;
-    off += (size_t)s->slots[i].rows * 4;
-    s->linear_bytes += s->slots[i].rows * 4;
+    off += sb;
+    s->linear_bytes += (int64_t)sb;
   };
   // audio tables, contiguous [2Q][Va+1][D]
   for (int k = 0; k < 2 * Q; ++k) s->emb.push_back(add("emb." + std::to_string(k) + ".weight", Va + 1, D, K_EMBED));
@@ -501,9 +517,10 @@ const void *select_persistent(const moshi_config &c, int cus, size_t *lds, int *
   if ((D | F | Dd | Fd) & 3) return nullptr;  // inputs are staged 16 bytes per lane
   const int ud = stage_passes(D), uf = stage_passes(F), udd = stage_passes(Dd), ufd = stage_passes(Fd);
   int n = 0;
-  const PVariant hd128[] = {pvariant_hd128_bf16_kvf32(), pvariant_hd128_bf16_kvbf16(), pvariant_hd128_i8_kvf32()};
+  const PVariant hd128[] = {pvariant_hd128_bf16_kvf32(), pvariant_hd128_bf16_kvbf16(), pvariant_hd128_i8_kvf32(),
+                            pvariant_hd128_q4_kvf32(), pvariant_hd128_q8_kvf32()};
   const PVariant *v = hd128;
-  n = 3;
+  n = (int)(sizeof(hd128) / sizeof(hd128[0]));
   if (hd != 128) v = pvariants_hd64(&n);
   const PVariant *pick = nullptr;
   for (int i = 0; i < n; ++i) {
@@ -1015,11 +1032,13 @@ void enqueue_frame(moshi_state *s, int b0, int nb, bool temporal_only, const int
                    const mk::Forced &forced, Prof *prof = nullptr) {
   with_types(s->cfg, [&](auto t) {
     typedef decltype(t) T;
-    if (nb >= 2 && !temporal_only)  // several conversations: projections on the matrix cores
-      enqueue_frame_rows<typename T::WT, typename T::ET, typename T::KT>(s, b0, nb, user_dev, prof);
-    else
-      enqueue_frame_t<typename T::WT, typename T::ET, typename T::KT>(s, b0, nb, temporal_only, user_dev, forced,
-                                                                       prof);
+    if constexpr (!mk::IsBlockBand<typename T::WT>::value) {
+      if (nb >= 2 && !temporal_only) {  // several conversations: projections on the matrix cores
+        enqueue_frame_rows<typename T::WT, typename T::ET, typename T::KT>(s, b0, nb, user_dev, prof);
+        return;
+      }
+    }
+    enqueue_frame_t<typename T::WT, typename T::ET, typename T::KT>(s, b0, nb, temporal_only, user_dev, forced, prof);
   });
 }
 
@@ -1101,7 +1120,12 @@ moshi_status check_config(const moshi_config *c, std::string &why) {
   if (hdd != 16 && hdd != 32 && hdd != 64 && hdd != 128) return bad("depformer head_dim must be 16, 32, 64 or 128");
   for (int k : {c->d_model, c->ffn_hidden, c->dep_d_model, c->dep_ffn_hidden})
     if (k % 16 || k > 16384) return bad("linear input widths must be multiples of 16 and at most 16384");
-  if (c->band < MOSHI_BAND_F32 || c->band > MOSHI_BAND_I8) return bad("unknown band");
+  if (c->band < MOSHI_BAND_F32 || c->band > MOSHI_BAND_Q8) return bad("unknown band");
+  if (c->band == MOSHI_BAND_Q4 || c->band == MOSHI_BAND_Q8) {
+    if (c->batch != 1) return bad("the Q4 and Q8 bands run one conversation (batch 1)");
+    for (int k : {c->d_model, c->ffn_hidden, c->dep_d_model, c->dep_ffn_hidden})
+      if (k % 32) return bad("the Q4 and Q8 bands need linear input widths that are multiples of 32");
+  }
   if (c->batch < 1) return bad("batch must be >= 1");
   if (c->kv_capacity < 0 || c->kv_capacity > c->context) return bad("kv_capacity must be in [0, context]");
   if (c->exec < MOSHI_EXEC_GRAPH || c->exec > MOSHI_EXEC_PERSISTENT) return bad("unknown exec mode");
@@ -1344,7 +1368,7 @@ moshi_status moshi_load_weights(moshi_state *s, const moshi_tensor *t, int32_t n
       e = hipMemcpy(dst, lin_f32(), cnt * 4, hipMemcpyHostToDevice);
     } else if (sl.kind == K_EMBED || band == MOSHI_BAND_BF16) {
       e = hipMemcpy(dst, lin_bf16(), cnt * 2, hipMemcpyHostToDevice);
-    } else {  // int8 linear: quantise on the device
+    } else {  // int8, Q4_0 or q8_0 linear: quantise on the device
       if (staging_n < cnt) {
         if (staging) (void)hipFree(staging);
         staging = nullptr;
@@ -1358,8 +1382,16 @@ moshi_status moshi_load_weights(moshi_state *s, const moshi_tensor *t, int32_t n
       }
       e = hipMemcpy(staging, lin_f32(), cnt * 4, hipMemcpyHostToDevice);
       if (e == hipSuccess) {
-        mk::k_quant_rows<<<(unsigned)sl.rows, mk::BLOCK, 0, s->stream>>>(
-            staging, sl.cols, reinterpret_cast<int8_t *>(dst), reinterpret_cast<float *>(s->warena + sl.soff), 0);
+        float *sc = reinterpret_cast<float *>(s->warena + sl.soff);
+        if (band == MOSHI_BAND_Q4)
+          mk::k_quant_blocks<4><<<(unsigned)sl.rows, mk::BLOCK, 0, s->stream>>>(staging, (int)sl.cols,
+                                                                              reinterpret_cast<uint8_t *>(dst), sc, 0);
+        else if (band == MOSHI_BAND_Q8)
+          mk::k_quant_blocks<8><<<(unsigned)sl.rows, mk::BLOCK, 0, s->stream>>>(staging, (int)sl.cols,
+                                                                              reinterpret_cast<uint8_t *>(dst), sc, 0);
+        else
+          mk::k_quant_rows<<<(unsigned)sl.rows, mk::BLOCK, 0, s->stream>>>(staging, sl.cols,
+                                                                          reinterpret_cast<int8_t *>(dst), sc, 0);
         e = hipGetLastError();
         if (e == hipSuccess) e = hipStreamSynchronize(s->stream);
       }
@@ -1675,12 +1707,15 @@ moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const
   for (int t = 0; t < T && e == hipSuccess;) {
     const int64_t pos = s->h_offset[conv] + t;
     const int64_t room = limit - pos;
-    if (room >= 2 && T - t >= 2) {
+    // the block-scaled bands have no matrix-core projection: they prefill one frame at a time
+    const bool rows_ok = s->cfg.band != MOSHI_BAND_Q4 && s->cfg.band != MOSHI_BAND_Q8;
+    if (rows_ok && room >= 2 && T - t >= 2) {
       const int n = (int)std::min<int64_t>({room, (int64_t)PF_ROWS, (int64_t)(T - t)});
       with_types(s->cfg, [&](auto tt) {
         typedef decltype(tt) T;
-        enqueue_prefill_rows<typename T::WT, typename T::ET, typename T::KT>(
-            s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q, duser + (size_t)t * d.Q);
+        if constexpr (!mk::IsBlockBand<typename T::WT>::value)
+          enqueue_prefill_rows<typename T::WT, typename T::ET, typename T::KT>(
+              s, conv, n, pos, dtext + t, dagent + (size_t)t * d.Q, duser + (size_t)t * d.Q);
       });
       t += n;
     } else {
@@ -1701,9 +1736,10 @@ moshi_status moshi_prefill_forced(moshi_state *s, int32_t conv, int32_t T, const
 
 moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W, const float *x, float *y,
                               int32_t iters, float *avg_us) {
-  if (N < 1 || K < 16 || K % 16 || K > 16384 || !W || !x || !y || band < 0 || band > 2) return MOSHI_EINVAL;
+  if (N < 1 || K < 16 || K % 16 || K > 16384 || !W || !x || !y || band < 0 || band > MOSHI_BAND_Q8) return MOSHI_EINVAL;
+  const bool blocks = band == MOSHI_BAND_Q4 || band == MOSHI_BAND_Q8;
+  if (blocks && K % 32) return MOSHI_EINVAL;
   const size_t cnt = (size_t)N * K;
-  const size_t elt = linear_elt(band);
   char *dw = nullptr;
   float *ds = nullptr, *dx = nullptr, *dy = nullptr, *stg = nullptr;
   hipStream_t st = nullptr;
@@ -1716,9 +1752,9 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
     }
     return rc == MOSHI_OK;
   };
-  if (chk(hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) && chk(hipMalloc(&dw, cnt * elt)) &&
-      chk(hipMalloc(&ds, (size_t)N * 4)) && chk(hipMalloc(&dx, (size_t)K * 4)) && chk(hipMalloc(&dy, (size_t)N * 4)) &&
-      chk(hipMemcpy(dx, x, (size_t)K * 4, hipMemcpyHostToDevice))) {
+  if (chk(hipStreamCreateWithFlags(&st, hipStreamNonBlocking)) && chk(hipMalloc(&dw, linear_bytes(band, N, K))) &&
+      chk(hipMalloc(&ds, std::max<size_t>(scale_bytes(band, N, K), 4))) && chk(hipMalloc(&dx, (size_t)K * 4)) &&
+      chk(hipMalloc(&dy, (size_t)N * 4)) && chk(hipMemcpy(dx, x, (size_t)K * 4, hipMemcpyHostToDevice))) {
     if (band == MOSHI_BAND_F32) {
       chk(hipMemcpy(dw, W, cnt * 4, hipMemcpyHostToDevice));
     } else if (band == MOSHI_BAND_BF16) {
@@ -1726,22 +1762,33 @@ moshi_status moshi_debug_gemv(int32_t band, int32_t N, int32_t K, const float *W
       for (size_t k = 0; k < cnt; ++k) hb[k] = host_f2bf(W[k]);
       chk(hipMemcpy(dw, hb.data(), cnt * 2, hipMemcpyHostToDevice));
     } else if (chk(hipMalloc(&stg, cnt * 4)) && chk(hipMemcpy(stg, W, cnt * 4, hipMemcpyHostToDevice))) {
-      mk::k_quant_rows<<<(unsigned)N, mk::BLOCK, 0, st>>>(stg, K, reinterpret_cast<int8_t *>(dw), ds, 0);
+      if (band == MOSHI_BAND_Q4)
+        mk::k_quant_blocks<4><<<(unsigned)N, mk::BLOCK, 0, st>>>(stg, K, reinterpret_cast<uint8_t *>(dw), ds, 0);
+      else if (band == MOSHI_BAND_Q8)
+        mk::k_quant_blocks<8><<<(unsigned)N, mk::BLOCK, 0, st>>>(stg, K, reinterpret_cast<uint8_t *>(dw), ds, 0);
+      else
+        mk::k_quant_rows<<<(unsigned)N, mk::BLOCK, 0, st>>>(stg, K, reinterpret_cast<int8_t *>(dw), ds, 0);
       chk(hipGetLastError());
     }
   }
   auto launch = [&]() {
     const dim3 grid(proj_blocks(N, 1024));
-    const float *sc = band == MOSHI_BAND_I8 ? ds : nullptr;
+    const float *sc = band >= MOSHI_BAND_I8 ? ds : nullptr;
     if (band == MOSHI_BAND_F32)
       mk::k_gemv<float, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const float *>(dw), sc,
                                                                             N, K, dx, K, dy, N, 0);
     else if (band == MOSHI_BAND_BF16)
       mk::k_gemv<bf16_t, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const bf16_t *>(dw),
                                                                              sc, N, K, dx, K, dy, N, 0);
-    else
+    else if (band == MOSHI_BAND_I8)
       mk::k_gemv<int8_t, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(reinterpret_cast<const int8_t *>(dw),
                                                                              sc, N, K, dx, K, dy, N, 0);
+    else if (band == MOSHI_BAND_Q4)
+      mk::k_gemv<mk::q4_t, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(
+          reinterpret_cast<const mk::q4_t *>(dw), sc, N, K, dx, K, dy, N, 0);
+    else
+      mk::k_gemv<mk::q8_t, false, MOSHI_N_STAGES><<<grid, mk::BLOCK, K * 4, st>>>(
+          reinterpret_cast<const mk::q8_t *>(dw), sc, N, K, dx, K, dy, N, 0);
   };
   if (rc == MOSHI_OK) {
     launch();

@@ -1,0 +1,6 @@
+// Persistent frame kernel instance: temporal head dim 128, Q4_0 weights, float32 KV.
+#include "persistent_variants.h"
+
+using mk::bf16_t;
+
+PVariant pvariant_hd128_q4_kvf32() { return pvariant<mk::q4_t, bf16_t, float, 128, 4, 2, 6, 1, 2>(MOSHI_BAND_Q4); }

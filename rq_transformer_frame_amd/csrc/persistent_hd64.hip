@@ -8,6 +8,8 @@ const PVariant *pvariants_hd64(int *n) {
       pvariant<float, float, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_F32),
       pvariant<bf16_t, bf16_t, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_BF16),
       pvariant<int8_t, bf16_t, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_I8),
+      pvariant<mk::q4_t, bf16_t, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_Q4),
+      pvariant<mk::q8_t, bf16_t, float, 64, 4, 1, 1, 1, 1>(MOSHI_BAND_Q8),
   };
   *n = (int)(sizeof(v) / sizeof(v[0]));
   return v;

@@ -22,9 +22,11 @@ PVariant pvariant(int band) {
 }
 
 // Temporal head dim 128 (the Moshi-7B shape: d4096 / ffn 11264, depformer d1024 / ffn 2816), one
-// instance per translation unit: bf16 weights with float32 or bf16 KV, int8 weights.
+// instance per translation unit: bf16 weights with float32 or bf16 KV, int8, Q4_0 and q8_0 weights.
 PVariant pvariant_hd128_bf16_kvf32();
 PVariant pvariant_hd128_bf16_kvbf16();
 PVariant pvariant_hd128_i8_kvf32();
+PVariant pvariant_hd128_q4_kvf32();
+PVariant pvariant_hd128_q8_kvf32();
 // Temporal head dim 64 (small shapes, one staging pass per 2048-wide input).
 const PVariant *pvariants_hd64(int *n);

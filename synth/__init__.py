@@ -121,7 +121,7 @@ class Config:
     rope_theta: float = 10000.0
     rms_eps: float = 1e-8
     dtype: str = "bf16"  # storage of the generated weights: 'f32' or 'bf16'
-    band: str = "bf16"  # weight band on the device: 'f32', 'bf16' or 'i8'
+    band: str = "bf16"  # weight band on the device: 'f32', 'bf16', 'i8', 'q4' or 'q8'
     batch: int = 1
     seed: int = 0
     frames: int = 16
@@ -154,10 +154,15 @@ MOSHI7B_LONG = MOSHI7B.with_(name="moshi7b_bf16_long", seed=2, prefill=2900, fra
 MOSHI7B_B64 = MOSHI7B.with_(name="moshi7b_bf16_b64", seed=3, batch=64, frames=200, max_start_offset=1000)
 MOSHI7B_I8 = MOSHI7B.with_(name="moshi7b_i8_b1", seed=4, band="i8", frames=250)
 
+# the 4-bit and 8-bit block bands ([LM] load_q4sim's Q4_0, qn_roundtrip's q8_0 at group 32)
+MOSHI7B_Q4 = MOSHI7B.with_(name="moshi7b_q4_b1", seed=5, band="q4", frames=250)
+MOSHI7B_Q8 = MOSHI7B.with_(name="moshi7b_q8_b1", seed=6, band="q8", frames=250)
+
 # teacher-forced priming as a workload of its own: prefill 2900 frames from offset 0, timed
 MOSHI7B_PREFILL = MOSHI7B.with_(name="moshi7b_bf16_prefill", seed=2, prefill=2900, frames=5)
 
-CONFIGS = {c.name: c for c in (TINY, MOSHI7B, MOSHI7B_LONG, MOSHI7B_B64, MOSHI7B_I8, MOSHI7B_PREFILL)}
+CONFIGS = {c.name: c for c in (TINY, MOSHI7B, MOSHI7B_LONG, MOSHI7B_B64, MOSHI7B_I8, MOSHI7B_Q4, MOSHI7B_Q8,
+                               MOSHI7B_PREFILL)}
 
 
 def weight_specs(cfg: Config):

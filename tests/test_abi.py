@@ -56,8 +56,9 @@ def _cfg(**kw):
 
 @pytest.mark.parametrize("bad", [
     dict(n_heads=3), dict(d_model=512, n_heads=2), dict(ffn_hidden=700), dict(dep_q=17), dict(batch=0),
-    dict(kv_capacity=65), dict(band=3), dict(exec=3), dict(context=0), dict(dep_heads=3),
+    dict(kv_capacity=65), dict(band=5), dict(exec=3), dict(context=0), dict(dep_heads=3),
     dict(kv_dtype=2), dict(band=0, kv_dtype=1),
+    dict(band=3, batch=2), dict(band=4, ffn_hidden=720),  # block bands: batch 1, widths multiples of 32
 ])
 def test_create_rejects_bad_configs_before_touching_the_device(bad):
     lib = rq.load_library()

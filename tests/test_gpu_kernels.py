@@ -7,6 +7,7 @@ import pytest
 import rq_transformer_frame_amd as rq
 import synth
 from oracle import quantize_rows_int8
+from oracle.moshi_oracle import dequantize_blocks, quantize_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -17,12 +18,17 @@ def stored(band, W):
         return W.astype(np.float64), None
     if band == "bf16":
         return synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(W)).astype(np.float64), None
+    if band in ("q4", "q8"):
+        return dequantize_blocks(*quantize_blocks(W, 4 if band == "q4" else 8)).astype(np.float64), None
     q, s = quantize_rows_int8(W)
     return q.astype(np.float64), s.astype(np.float64)
 
 
-@pytest.mark.parametrize("band", ["f32", "bf16", "i8"])
-@pytest.mark.parametrize("N,K", [(1, 16), (37, 48), (130, 272), (1000, 256), (2048, 1024), (333, 2816)])
+BYTES_PER_WEIGHT = {"bf16": 2.0, "i8": 1.0, "q4": 0.5 + 4 / 32, "q8": 1.0 + 4 / 32}
+
+
+@pytest.mark.parametrize("band", ["f32", "bf16", "i8", "q4", "q8"])
+@pytest.mark.parametrize("N,K", [(1, 32), (37, 64), (130, 288), (1000, 256), (2048, 1024), (333, 2816)])
 def test_gemv_small_and_ragged(band, N, K):
     W = synth.normal(1, f"k/W{N}x{K}", (N, K), 0.02)
     x = synth.normal(1, f"k/x{K}", (K,), 1.0)
@@ -35,7 +41,7 @@ def test_gemv_small_and_ragged(band, N, K):
     assert err < 2e-6, err
 
 
-@pytest.mark.parametrize("band", ["bf16", "i8"])
+@pytest.mark.parametrize("band", ["bf16", "i8", "q4", "q8"])
 @pytest.mark.parametrize("N,K", [(12288, 4096), (22528, 4096), (4096, 11264), (32000, 4096), (8192, 4096)])
 def test_gemv_moshi7b_shapes_sampled_rows(band, N, K):
     W = synth.normal(2, f"k7/W{N}x{K}", (N, K), 0.02)
@@ -48,7 +54,7 @@ def test_gemv_moshi7b_shapes_sampled_rows(band, N, K):
     if s is not None:
         ref *= s
     err = np.max(np.abs(y[rows] - ref)) / np.max(np.abs(ref))
-    bytes_ = N * K * (2 if band == "bf16" else 1) + (N * 4 if band == "i8" else 0)
+    bytes_ = N * K * BYTES_PER_WEIGHT[band] + (N * 4 if band == "i8" else 0)
     print(f"gemv {band} {N}x{K}: {us:.1f} us, {bytes_ / us / 1e3:.0f} GB/s")
     assert err < 2e-6, err
 

@@ -199,3 +199,55 @@ def test_batch64_matches_single_conversations_and_oracle_subset():
     for x in (inv, sub_batch, sub_single):
         assert x.cos_min >= 0.999
         assert x.rate >= 0.99
+
+
+@pytest.mark.timeout(1500)
+@pytest.mark.parametrize("name,sim", [("moshi7b_q4_b1", "q4sim"), ("moshi7b_q8_b1", "q8sim")])
+def test_block_bands_250_frames_match_round_trip_oracle(name, sim):
+    """The Q4_0 and q8_0 bands ([LM] load_q4sim: storage loss only) over 250 frames on the
+    persistent executor (their instances) and the graph executor, teacher-forced onto the
+    round-trip oracle's greedy trajectory; the float32 oracle's agreement is printed as the
+    quantisation loss."""
+    cfg = synth.CONFIGS[name]
+    frames = cfg.frames
+    t0 = time.time()
+    w = synth.gen_weights(cfg)
+    users = synth.user_tokens(cfg, frames)
+    lm = OracleLM(cfg, w, band=sim)
+    t0 = tick(f"{name}: weights and the {sim} oracle", t0)
+    sessions = {m: rq.Session(cfg, exec=m) for m in ("persistent", "graph")}
+    stats = {m: TraceStats() for m in sessions}
+    kept, forced = [], []
+    try:
+        for s in sessions.values():
+            s.load_weights(w)
+        st = lm.new_state()
+        for f in range(frames):
+            ref = lm.step(st, users[f])
+            forced.append((ref["text_token"], ref["audio_tokens"]))
+            for m, s in sessions.items():
+                s.step(users[f])
+                tr = s.read_trace(0)
+                stats[m].add(tr, ref)
+                if m == "persistent" and f < 50:
+                    kept.append({k: tr[k] for k in ("text_token", "audio_tokens", "text_logits", "audio_logits")})
+                s.force_generated(0, ref["text_token"], ref["audio_tokens"])
+            if f % 50 == 49:
+                t0 = tick(f"frame {f}: " + "; ".join(f"{m} {x}" for m, x in stats.items()), t0)
+    finally:
+        for s in sessions.values():
+            s.close()
+    del lm
+    lm32 = OracleLM(cfg, w)
+    st = lm32.new_state()
+    loss = TraceStats()
+    for f in range(len(kept)):
+        loss.add(kept[f], lm32.step(st, users[f]))
+        lm32.force_generated(st, *forced[f])
+    for m, x in stats.items():
+        print(f"{name} ({m}) vs the {sim} oracle: {x}", flush=True)
+    print(f"{name} (persistent) vs the float32 oracle, first {len(kept)} frames (quantisation loss): {loss}", flush=True)
+    for m, x in stats.items():
+        assert x.frames == frames
+        assert x.cos_min >= 0.999, m
+        assert x.rate >= 0.99, m

@@ -250,13 +250,17 @@ def test_batch_of_three_conversations_matches_single_runs(weights, oracle):
         assert [s.offset(b) for b in range(B)] == [6, 0, 6]
 
 
+SIM = {"bf16": "f32", "i8": "i8sim", "q4": "q4sim", "q8": "q8sim"}
+
+
 @pytest.mark.parametrize("exec_mode", ["graph", "persistent"])
-@pytest.mark.parametrize("band", ["bf16", "i8"])
+@pytest.mark.parametrize("band", ["bf16", "i8", "q4", "q8"])
 def test_low_precision_bands_on_the_tiny_model(weights, band, exec_mode):
-    """bf16 band vs the oracle on the same bf16-rounded weights; int8 band vs the int8-dequantised
-    oracle (storage loss only).  Teacher-forced onto the oracle's tokens."""
+    """bf16 band vs the oracle on the same bf16-rounded weights; int8, Q4_0 and q8_0 bands vs the
+    oracle on the same quantise-dequantise round trip (storage loss only, [LM] load_q4sim).
+    Teacher-forced onto the oracle's tokens."""
     w16 = {k: (synth.f32_to_bf16_bits(v) if v.ndim == 2 else v) for k, v in weights.items()}
-    ref_lm = OracleLM(CFG, w16, band="i8sim" if band == "i8" else "f32")
+    ref_lm = OracleLM(CFG, w16, band=SIM[band])
     users = synth.user_tokens(CFG, 8)
     ost = ref_lm.new_state()
     agree, total, cos_min = 0, 0, 1.0
@@ -504,3 +508,36 @@ def test_greedy_contract_all_equal_logits_pick_index_zero(weights, oracle, exec_
                 tr = s.read_trace(b)
                 assert tr["tokens"].tolist() == [0] * (1 + CFG.dep_q), (b, f)
                 assert not tr["text_logits"].any() and not tr["audio_logits"].any()
+
+
+@pytest.mark.parametrize("band", ["q4", "q8"])
+def test_block_bands_free_running_and_prefill(weights, band):
+    """Q4_0 and q8_0 from float32 weights on the stream executor, free-running against the
+    round-trip oracle with a prefill first (the block bands prefill one frame at a time):
+    logits within 1e-4, tokens and outputs exact."""
+    lm = OracleLM(CFG, weights, band=SIM[band])
+    T = 5
+    text, agent, user = synth.prefill_tokens(CFG, T, conv=6)
+    text %= CFG.text_card
+    users = synth.user_tokens(CFG, 6, conv=6, start_frame=T)
+    ost = lm.new_state()
+    lm.prefill_forced(ost, text, agent, user)
+    with rq.Session(CFG, band=band, exec="stream") as s:
+        s.load_weights(weights)
+        s.prefill_forced(0, text, agent, user)
+        for f in range(6):
+            ref = lm.step(ost, users[f])
+            st, out, has = s.step(users[f])
+            tr = s.read_trace(0)
+            assert rel_err(tr["text_logits"], ref["text_logits"]) <= TOL, f
+            for cb in range(CFG.dep_q):
+                assert rel_err(tr["audio_logits"][cb], ref["audio_logits"][cb]) <= TOL, (f, cb)
+            assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], f
+            assert out[0].tolist() == ref["out"], f
+
+
+def test_block_bands_refuse_batches(weights):
+    for band in ("q4", "q8"):
+        with pytest.raises(rq.MoshiError) as ei:
+            rq.Session(CFG, band=band, batch=2)
+        assert ei.value.status == rq.MOSHI_EINVAL
