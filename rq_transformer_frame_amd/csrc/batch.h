@@ -406,35 +406,60 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv_attn(Dims d, Bufs s, const fl
   }
 }
 
-// a11 bookkeeping of a teacher-forced prefill of T frames of conversation `conv`, one thread:
-// for each frame, the user write and the gather of the 17 model inputs (into rows[t]), then the
-// forced ring write and the offset step, exactly as the frame kernels do them one frame at a time.
-static __global__ void k_prefill_ring(Dims d, Bufs s, int conv, int T, const int32_t *__restrict__ text,
-                               const int32_t *__restrict__ agent, const int32_t *__restrict__ user,
-                               int32_t *__restrict__ rows) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
-  int32_t *rg = s.ring + (size_t)conv * d.NS * 3;
-  int64_t off = s.offset[conv];
-  for (int t = 0; t < T; ++t) {
-    const int32_t *u = user + (size_t)t * d.Q;
-    for (int st = 0; st < d.NS; ++st) {
-      const int delay = stream_delay(st, d.Q);
-      int v;
-      if (off <= delay)
-        v = (st == 0) ? d.Vt : d.Va;
-      else if (st >= d.Q + 1 && delay == 0)
-        v = u[st - d.Q - 1];
-      else
-        v = rg[st * 3 + (int)(off % 3)];
-      rows[(size_t)t * d.NS + st] = v;
+// a11 bookkeeping of a teacher-forced prefill of T frames of conversation `conv`: for each frame,
+// the user write and the gather of the 17 model inputs (into rows[t]), then the forced ring write
+// and the offset step, exactly as the frame kernels do them one frame at a time.  Every step
+// touches only its own stream's three ring slots, so thread st carries stream st through all T
+// frames with its slots in registers, reading its forced tokens 32 frames at a time.  One block of
+// 64 threads.
+static __global__ __launch_bounds__(64) void k_prefill_ring(Dims d, Bufs s, int conv, int T,
+                                                            const int32_t *__restrict__ text,
+                                                            const int32_t *__restrict__ agent,
+                                                            const int32_t *__restrict__ user,
+                                                            int32_t *__restrict__ rows) {
+  constexpr int U = 32;
+  const int st = threadIdx.x;
+  const bool on = blockIdx.x == 0 && st < d.NS;
+  const int64_t off0 = s.offset[conv];
+  if (on) {
+    int32_t *rg = s.ring + ((size_t)conv * d.NS + st) * 3;
+    int r0 = rg[0], r1 = rg[1], r2 = rg[2];
+    const int delay = stream_delay(st, d.Q);
+    const bool ust = st >= d.Q + 1;  // a user stream: written from the user tokens
+    // this stream's forced token of frame t: text, agent codebook st - 1, or user codebook
+    const int32_t *src = st == 0 ? text : ust ? user + (st - d.Q - 1) : agent + (st - 1);
+    const int stride = st == 0 ? 1 : d.Q;
+    for (int t0 = 0; t0 < T; t0 += U) {
+      int tk[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i) tk[i] = t0 + i < T ? src[(size_t)(t0 + i) * stride] : 0;
+#pragma unroll
+      for (int i = 0; i < U; ++i) {
+        if (t0 + i >= T) break;
+        const int64_t off = off0 + t0 + i;
+        const int slot = (int)(off % 3);
+        int v;
+        if (off <= delay)
+          v = st == 0 ? d.Vt : d.Va;
+        else if (ust && delay == 0)
+          v = tk[i];
+        else
+          v = slot == 0 ? r0 : slot == 1 ? r1 : r2;
+        rows[(size_t)(t0 + i) * d.NS + st] = v;
+        // user streams: this frame's user token at (off + delay) % 3; generated streams: the
+        // forced token at the next offset's slot
+        const int w = ust ? (int)((off + delay) % 3) : (int)((off + 1) % 3);
+        if (w == 0) r0 = tk[i];
+        if (w == 1) r1 = tk[i];
+        if (w == 2) r2 = tk[i];
+      }
     }
-    for (int st = d.Q + 1; st < d.NS; ++st) rg[st * 3 + (int)((off + stream_delay(st, d.Q)) % 3)] = u[st - d.Q - 1];
-    off += 1;
-    const int p = (int)(off % 3);
-    rg[p] = text[t];
-    for (int k = 0; k < d.Q; ++k) rg[(1 + k) * 3 + p] = agent[(size_t)t * d.Q + k];
+    rg[0] = r0;
+    rg[1] = r1;
+    rg[2] = r2;
   }
-  s.offset[conv] = off;
+  __syncthreads();  // every thread has read the offset before it moves
+  if (blockIdx.x == 0 && st == 0) s.offset[conv] = off0 + T;
 }
 
 // a3 for prefill rows: x[t] = the 17-row embedding sum of rows[t] (audio tables in stream order,

@@ -16,6 +16,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "attn_pf.h"
 #include "batch.h"
 #include "persistent_variants.h"
 #include "sample.h"
@@ -27,7 +28,7 @@ namespace {
 
 enum Kind { K_LINEAR = 0, K_EMBED = 1, K_NORM = 2 };
 
-constexpr int PF_ROWS = 256;  // prefill positions per row-batched chunk
+constexpr int PF_ROWS = 1024;  // prefill positions per row-batched chunk
 
 struct Slot {
   std::string name;
@@ -852,7 +853,13 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
       bf16_t *xo = nullptr;
       if constexpr (std::is_same<XT, bf16_t>::value) xo = X;
       const AttnQ aq{q_rows, o_rows, rm.conv, rm.pos0, xo, P * d.D};
-      if (d.hd == 128)
+      // a prefill chunk: key tiles shared by 128 query rows on the matrix cores
+      const dim3 pfg(d.H, (rows + PFA_ROWS - 1) / PFA_ROWS);
+      if (rm.conv >= 0 && d.hd == 128)
+        k_attn_pf<KT, 128><<<pfg, PFA_WAVES * 64, 0, st>>>(d, kv, l, aq, rows);
+      else if (rm.conv >= 0 && d.hd == 64)
+        k_attn_pf<KT, 64><<<pfg, PFA_WAVES * 64, 0, st>>>(d, kv, l, aq, rows);
+      else if (d.hd == 128)
         k_attn<KT, 128><<<dim3(d.H, attn_splits, rows), BLOCK, chunk * 4, st>>>(d, b, kv, l, rm.b0, aq);
       else
         k_attn<KT, 64><<<dim3(d.H, attn_splits, rows), BLOCK, chunk * 4, st>>>(d, b, kv, l, rm.b0, aq);

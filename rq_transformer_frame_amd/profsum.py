@@ -3,13 +3,18 @@
     python -m rq_transformer_frame_amd.profsum stats <kernel_stats.csv> [bench.json]
     python -m rq_transformer_frame_amd.profsum traffic <fetch counter_collection.csv> <write ...csv> <copy MiB>
     python -m rq_transformer_frame_amd.profsum steps <kernel_trace.csv> <marker kernel> <steps>
+    python -m rq_transformer_frame_amd.profsum counters <counter_collection.csv> [marker kernel]
 
 `stats` prints a markdown table of the per-kernel averages (stage names recovered from the kernels'
 stage tags; algorithmic GB/s when the bench JSON line of the same run is given).  `traffic` prints
 per-kernel HBM bytes per dispatch from a FETCH_SIZE run and a WRITE_SIZE run, each scaled by what
 the same counter reads for the first device-to-device copy of `copy MiB` in that run.  `steps`
 keeps the dispatches after the last one whose name contains `marker` (e.g. the end of a prefill)
-and prints per-stage averages and microseconds per step over `steps` steps.
+and prints per-stage averages and microseconds per step over `steps` steps.  `counters` prints, per
+stage, the mean of every counter of a --pmc run per dispatch (after the last `marker` dispatch when
+given) and, where the run holds them, the matrix-core figures: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
+bf16 flops per dispatch over the dispatch's duration, and SQ_VALU_MFMA_BUSY_CYCLES over
+SQ_BUSY_CYCLES.
 """
 from __future__ import annotations
 
@@ -109,11 +114,52 @@ def steps(path: str, marker: str, nsteps: int) -> str:
     return "\n".join(out)
 
 
+def counters(path: str, after: str | None = None) -> str:
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    last = max((int(r["Dispatch_Id"]) for r in rows if after and after in r["Kernel_Name"]), default=-1)
+    # one row per (dispatch, counter)
+    disp = collections.defaultdict(dict)
+    meta = {}
+    for r in rows:
+        i = int(r["Dispatch_Id"])
+        if i <= last or "rocclr" in r["Kernel_Name"]:
+            continue
+        disp[i][r["Counter_Name"]] = float(r["Counter_Value"])
+        meta[i] = (stage_of(r["Kernel_Name"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3,
+                   int(r["Grid_Size"]))
+    names = sorted({c for d in disp.values() for c in d})
+    agg = collections.defaultdict(list)
+    for i, d in disp.items():
+        agg[meta[i][0]].append((d, meta[i][1]))
+    head = "| stage (kernel) | dispatches | avg us | " + " | ".join(names)
+    mf = "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names
+    bz = "SQ_VALU_MFMA_BUSY_CYCLES" in names and "SQ_BUSY_CYCLES" in names
+    if mf:
+        head += " | bf16 MFMA TFLOP/s (MOPS x 512 / duration)"
+    if bz:
+        head += " | MFMA busy / SQ busy"
+    out = [head + " |", "|" + "---|" * (head.count("|") )]
+    tot = lambda v, c: sum(d.get(c, 0.0) for d, _ in v)
+    for st, v in sorted(agg.items(), key=lambda x: -sum(t for _, t in x[1])):
+        us = sum(t for _, t in v) / len(v)
+        cells = [f"{tot(v, c) / len(v):.4g}" for c in names]
+        if mf:
+            cells.append(f"{512.0 * tot(v, 'SQ_INSTS_VALU_MFMA_MOPS_BF16') / (sum(t for _, t in v) * 1e6):.1f}")
+        if bz:
+            b = tot(v, "SQ_BUSY_CYCLES")
+            cells.append(f"{tot(v, 'SQ_VALU_MFMA_BUSY_CYCLES') / b:.3f}" if b else "")
+        out.append(f"| {st} | {len(v)} | {us:.2f} | " + " | ".join(cells) + " |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 3 and sys.argv[1] == "stats":
         print(stats(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else None))
     elif len(sys.argv) in (5, 6) and sys.argv[1] == "traffic":
         print(traffic(sys.argv[2], sys.argv[3], float(sys.argv[4]), sys.argv[5] if len(sys.argv) == 6 else None))
+    elif len(sys.argv) in (3, 4) and sys.argv[1] == "counters":
+        print(counters(sys.argv[2], sys.argv[3] if len(sys.argv) == 4 else None))
     elif len(sys.argv) == 5 and sys.argv[1] == "steps":
         print(steps(sys.argv[2], sys.argv[3], int(sys.argv[4])))
     else:
