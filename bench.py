@@ -32,11 +32,11 @@ METRIC = "frames/s (80 ms) at B=1, Moshi-7B shape bf16; % of HBM roofline"
 # B=1 frame kernels and the attention are compiled from, and the launch code): the bench reports
 # traffic null when their hash differs.
 TRAFFIC = {
-    "sources_sha256": "a776bc3644a2afd3205f3cea2d8ec0c4cbbd323c9089653a3140518e0a562afc",
-    "per_dispatch": {
-        "moshi7b_bf16_b1/frame_persistent": 14875870583,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
-        "moshi7b_bf16_b1/gate_in": 185062986,
-        "moshi7b_bf16_b64/attn": 1035621601,  # profiles/frame_moshi7b_bf16_b64_hbm_traffic.md
+    "sources_sha256": "ca9e39cafc9c7f4a57f523ef30066fea861ebae5efc5f5a9737483d503c47ec9",
+    "per_dispatch": {  # config/KV storage/kernel
+        "moshi7b_bf16_b1/f32/frame_persistent": 14874322718,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
+        "moshi7b_bf16_b1/f32/gate_in": 185063133,
+        "moshi7b_bf16_b64/bf16/attn": 517755393,  # profiles/frame_moshi7b_bf16_b64_hbm_traffic.md
     },
 }
 
@@ -56,10 +56,10 @@ def sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(config: str, kernel: str):
+def measured_traffic(config: str, kv: str, kernel: str):
     if TRAFFIC["sources_sha256"] != sources_sha256():
         return None
-    return TRAFFIC["per_dispatch"].get(f"{config}/{kernel}")
+    return TRAFFIC["per_dispatch"].get(f"{config}/{kv}/{kernel}")
 
 
 def log(msg):
@@ -251,7 +251,8 @@ def main():
     ap.add_argument("--profile-frames", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--kv", default="f32", choices=["f32", "bf16"], help="KV cache storage")
+    ap.add_argument("--kv", default=None, choices=["f32", "bf16"],
+                    help="KV cache storage (default: bf16 for batched conversations, else f32)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first copy this many MiB device to device (a kernel of known traffic, for "
                          "scaling hardware byte counters)")
@@ -277,6 +278,8 @@ def main():
         del a, b
 
     cfg = synth.CONFIGS[args.config]
+    if args.kv is None:
+        args.kv = "bf16" if cfg.batch > 1 else "f32"
     if cfg.name.endswith("_prefill"):
         print(json.dumps(prefill_main(args, cfg)), flush=True)
         return
@@ -373,13 +376,13 @@ def main():
         roofline = {"bound": "hbm", "kernel": "k_frame_persistent (one launch per frame)",
                     "achieved": round(fb / avg / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(fb / avg / 1e3 / HBM_PEAK_GBS, 4),
-                    "traffic": measured_traffic(cfg.name, "frame_persistent"),
+                    "traffic": measured_traffic(cfg.name, kv, "frame_persistent"),
                     "bytes_per_launch": fb, "avg_us": round(avg, 2),
                     "frac_of_ceiling": round(fb / avg / 1e3 / ceiling, 4)}
     else:
         d = stages[dom]
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(d["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, dom),
+                    "frac": round(d["gbs"] / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name, kv, dom),
                     "bytes_per_launch": d["bytes_per_launch"], "avg_us": round(d["avg_us"], 2),
                     "frac_of_ceiling": round(d["gbs"] / ceiling, 4)}
 

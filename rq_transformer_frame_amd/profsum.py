@@ -12,9 +12,11 @@ the same counter reads for the first device-to-device copy of `copy MiB` in that
 keeps the dispatches after the last one whose name contains `marker` (e.g. the end of a prefill)
 and prints per-stage averages and microseconds per step over `steps` steps.  `counters` prints, per
 stage, the mean of every counter of a --pmc run per dispatch (after the last `marker` dispatch when
-given) and, where the run holds them, the matrix-core figures: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512
-bf16 flops per dispatch over the dispatch's duration, and SQ_VALU_MFMA_BUSY_CYCLES over
-SQ_BUSY_CYCLES.
+given) and, where the run holds them, the matrix-core figures: SQ_INSTS_VALU_MFMA_MOPS_BF16 (and _F32)
+x 512 flops per dispatch over the dispatch's duration, and the matrix-core busy fraction
+SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDS x SIMDS): the busy counter sums the cycles of
+every SIMD, and GRBM_GUI_ACTIVE sums the active cycles of every XCD (MI355X: 8 XCDs, 256 CUs of 4
+SIMDs).
 """
 from __future__ import annotations
 
@@ -23,6 +25,8 @@ import csv
 import json
 import re
 import sys
+
+XCDS, SIMDS = 8, 256 * 4  # MI355X
 
 STAGES = ["embed", "qkv", "attn", "out_proj", "gate_in", "gate_out", "text_head", "dep_in", "dep_qkv",
           "dep_out", "dep_gate_in", "dep_gate_out", "dep_head", "frame_end"]
@@ -133,22 +137,22 @@ def counters(path: str, after: str | None = None) -> str:
     for i, d in disp.items():
         agg[meta[i][0]].append((d, meta[i][1]))
     head = "| stage (kernel) | dispatches | avg us | " + " | ".join(names)
-    mf = "SQ_INSTS_VALU_MFMA_MOPS_BF16" in names
-    bz = "SQ_VALU_MFMA_BUSY_CYCLES" in names and "SQ_BUSY_CYCLES" in names
-    if mf:
-        head += " | bf16 MFMA TFLOP/s (MOPS x 512 / duration)"
+    mops = [c for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32") if c in names]
+    bz = "SQ_VALU_MFMA_BUSY_CYCLES" in names and "GRBM_GUI_ACTIVE" in names
+    for c in mops:
+        head += f" | {c[-4:].lstrip('_').lower()} MFMA TFLOP/s (MOPS x 512 / duration)"
     if bz:
-        head += " | MFMA busy / SQ busy"
+        head += " | MFMA busy"
     out = [head + " |", "|" + "---|" * (head.count("|") )]
     tot = lambda v, c: sum(d.get(c, 0.0) for d, _ in v)
     for st, v in sorted(agg.items(), key=lambda x: -sum(t for _, t in x[1])):
         us = sum(t for _, t in v) / len(v)
         cells = [f"{tot(v, c) / len(v):.4g}" for c in names]
-        if mf:
-            cells.append(f"{512.0 * tot(v, 'SQ_INSTS_VALU_MFMA_MOPS_BF16') / (sum(t for _, t in v) * 1e6):.1f}")
+        for c in mops:
+            cells.append(f"{512.0 * tot(v, c) / (sum(t for _, t in v) * 1e6):.1f}")
         if bz:
-            b = tot(v, "SQ_BUSY_CYCLES")
-            cells.append(f"{tot(v, 'SQ_VALU_MFMA_BUSY_CYCLES') / b:.3f}" if b else "")
+            a = tot(v, "GRBM_GUI_ACTIVE")
+            cells.append(f"{tot(v, 'SQ_VALU_MFMA_BUSY_CYCLES') / (a / XCDS * SIMDS):.3f}" if a else "")
         out.append(f"| {st} | {len(v)} | {us:.2f} | " + " | ".join(cells) + " |")
     return "\n".join(out)
 
