@@ -77,11 +77,14 @@ def stage_bytes(cfg, band: str, n_kv: float, rows: int = 1, kve: int = KV_ALG) -
     conversations."""
     D, F, Dd, Fd, Q = cfg.d_model, cfg.ffn_hidden, cfg.dep_d_model, cfg.dep_ffn_hidden, cfg.dep_q
     Vt, Va, L = cfg.text_card, cfg.audio_card, cfg.n_layers
-    we = {"f32": 4, "bf16": 2, "i8": 1}[band]
-    sc = 4 if band == "i8" else 0  # per-row scales
+    # bytes per weight (Q4_0 packs two per byte) and per weight row of the band's float32 scales:
+    # one per row (int8), one per 32-column block (Q4_0, q8_0)
+    we = {"f32": 4, "bf16": 2, "i8": 1, "q4": 0.5, "q8": 1}[band]
+    sc_row = 4 if band == "i8" else 0
+    sc_blk = 4 / 32 if band in ("q4", "q8") else 0
 
     def lin(n, k):
-        return n * k * we + n * sc
+        return int(n * k * we + n * sc_row + n * k * sc_blk)
 
     f = 4 * rows  # float32 activations, one row per conversation
     return {
@@ -394,6 +397,9 @@ def main():
     metric, unit, value, what = METRIC, "frames/s", fps, "greedy frames from offset 0"
     if band == "i8":
         metric = "frames/s (80 ms) at B=1, Moshi-7B shape int8 per-row weights; % of HBM roofline"
+    if band in ("q4", "q8"):
+        metric = (f"frames/s (80 ms) at B=1, Moshi-7B shape {'Q4_0' if band == 'q4' else 'q8_0'} block-scaled "
+                  "weights; % of HBM roofline")
     if cfg.prefill:
         metric = f"frames/s (80 ms) at B=1 after a {cfg.prefill}-frame prefill, Moshi-7B shape bf16; % of HBM roofline"
         what = f"greedy frames at positions {int(tpos.min())}..{int(tpos.max())} after a teacher-forced prefill"
