@@ -250,9 +250,8 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm(const WT *__restrict__ W, const
 // feeds the products of its NT 32-row weight tiles (two tiles halve the LDS reads per product but
 // halve the number of blocks: the host takes them for wide projections).  Each 1 KB load fills whole 128-byte row segments (8 rows of a 64-column bf16 block, or
 // 16 rows of int8), so every cache line is fetched by one instruction; within a row the 16-byte
-// pieces are stored XOR-swizzled by the row (piece p of row r at slot p ^ (r % slots)), so the
-// matrix-core fragment reads (lane l: row l % 32, pieces of columns 32 (l / 32) ..) hit distinct
-// banks.
+// pieces are stored XOR-swizzled by the row (xswz), so the matrix-core fragment reads (lane l:
+// row l % 32, pieces of columns 32 (l / 32) ..) hit distinct banks.
 // A grid z dimension splits K: every split writes its partial tile to `part` ([split][M][N]
 // floats) and k_gemm_reduce adds the splits in order, so the result does not depend on timing.
 constexpr int XNMAX = 2;                // most 32-row weight tiles per wave
@@ -265,6 +264,12 @@ constexpr int XLDS = 160 * 1024;        // the LDS of a CU: the ring takes as ma
 template <typename WT> struct XWC;
 template <> struct XWC<bf16_t> { static constexpr int N = 4, ELT = 2, PER = 8, PPR = 8, RPC = 8; };
 template <> struct XWC<int8_t> { static constexpr int N = 2, ELT = 1, PER = 16, PPR = 4, RPC = 16; };
+
+// The LDS serves a 16-byte read of 16 lanes per cycle from 64 banks (256 bytes), so the 16 rows a
+// fragment read touches must land on 16 distinct 16-byte slots of the 256-byte bank window.  A row
+// of PPR pieces spans 16 PPR bytes: 16 / PPR rows share a window position, and piece p of row r is
+// stored at slot p ^ ((r / (16 / PPR)) % PPR).
+template <int PPR> __device__ __forceinline__ int xswz(int r) { return (r / (16 / PPR)) % PPR; }
 
 // s_waitcnt immediate that waits until at most n vector memory operations are outstanding
 // (expcnt and lgkmcnt left at their maxima: no wait on them).
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
     const int c = GWAVES * wave + i;
     const int pl = c >> 3, r = 8 * (c & 7) + (lane >> 3);
     const int m = m0 + r;
-    xcol[i] = 8 * ((lane & 7) ^ (r & 7));
+    xcol[i] = 8 * ((lane & 7) ^ xswz<8>(r));
     xo[i] = m < M ? (int)(((size_t)m * ldx + (size_t)pl * K + xcol[i]) * 2) : -1;
   }
   // this wave's weight chunks c: rows RPC c .. + RPC of its 32 XNT; lane l fills slot l % PPR of
@@ -330,7 +335,7 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
   for (int c = 0; c < WC; ++c) {
     const int rr = RPC * c + lane / PPR;
     const int nr = nw + rr;
-    wcol[c] = PER * ((lane % PPR) ^ (rr % PPR));
+    wcol[c] = PER * ((lane % PPR) ^ xswz<PPR>(rr));
     wo[c] = nr < N ? (int)(((size_t)nr * K + wcol[c]) * WE) : -1;
   }
   // K block kb into a stage (past kb1 or K: out-of-range loads, which read zero and move no data,
@@ -362,14 +367,14 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
 #pragma unroll
       for (int c = 0; c < WCT; ++c) {
         const int pi = WCT * g + c, r = 32 * t + ln;
-        wq[t][c] = wst[(r / RPC) * WAVE + (r % RPC) * PPR + (pi ^ (r % PPR))];
+        wq[t][c] = wst[(r / RPC) * WAVE + (r % RPC) * PPR + (pi ^ xswz<PPR>(r))];
       }
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {  // j: (plane, m tile) = (j / 2, j % 2)
         const int pl = j >> 1, r = 32 * (j & 1) + ln;
-        xf[4 * stp + j] = stg[(pl * 8 + (r >> 3)) * WAVE + (r & 7) * 8 + ((4 * g + stp) ^ (r & 7))];
+        xf[4 * stp + j] = stg[(pl * 8 + (r >> 3)) * WAVE + (r & 7) * 8 + ((4 * g + stp) ^ xswz<8>(r))];
       }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the multiplies
 #pragma unroll
