@@ -445,6 +445,163 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
   }
 }
 
+// ---- many activation rows (the prefill's chunks): 128 x 256 tiles ------------------------------
+// The same product for M > XM.  With 64-row activation tiles every weight tile is read once per
+// 64 rows, and the re-reads bound the projection (at M = 1024 gate_in moves 4.4 GB for 189 GFLOP).
+// Here a block owns 128 activation rows and 256 weight rows and its four waves split both (2 x 2:
+// 64 rows x 128 weight rows each, 8 accumulator tiles); a K block is 32 columns, so that a stage
+// (the activation tile's hi and lo planes, 16 KB, and the weight tile, 16 KB for bf16 or 8 KB for
+// int8) leaves room for 5 (6) stages in LDS.  Loads, the LDS-direct ring and the waits are those of
+// k_gemm_x.  A row segment of a stage is 64 bytes (bf16: 4 pieces of 8 columns; int8 weights: 32
+// bytes, 2 pieces of 16) and its pieces are swizzled with xswz.  MFMA step s of a K block takes, in
+// lane half g, columns 16 g + 8 s .. + 7 of both operands.  The grid walks the activation tiles
+// fastest, so the blocks that read one weight tile run together.
+constexpr int XLM = 128;  // activation rows per block
+constexpr int XLN = 256;  // weight rows per block
+constexpr int XLK = 32;   // K block
+
+template <typename WT> struct XLW;
+template <> struct XLW<bf16_t> { static constexpr int ELT = 2, PPR = 4, RPC = 16, PER = 8, CH = 16; };
+template <> struct XLW<int8_t> { static constexpr int ELT = 1, PPR = 2, RPC = 32, PER = 16, CH = 8; };
+
+template <typename WT, bool ADD, int TAG>
+__global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, const float *__restrict__ wscale, int N,
+                                                    int K, const bf16_t *__restrict__ X, int ldx, int M,
+                                                    float *__restrict__ Y, int ldy, float *__restrict__ part, int kbs) {
+  constexpr int WE = XLW<WT>::ELT, PPR = XLW<WT>::PPR, RPC = XLW<WT>::RPC, PER = XLW<WT>::PER;
+  constexpr int WCH = XLW<WT>::CH;   // weight chunks per stage
+  constexpr int XCH = 16;            // activation chunks per stage: [plane][16-row group]
+  constexpr int NCH = XCH + WCH;
+  constexpr int NL = NCH / GWAVES;   // loads each wave issues per K block
+  constexpr int XST = XLDS / (NCH * WAVE * 16);
+  static_assert(NCH % GWAVES == 0 && XST >= 3, "stage shape");
+  __shared__ __align__(16) uint4 ring[XST][NCH * WAVE];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm = wave & 1, wn = wave >> 1;
+  const int m0 = blockIdx.x * XLM, n0 = blockIdx.y * XLN;
+  const int ln = lane & 31, g = lane >> 5;
+  const i32x4 rw = raw_desc(W, (int)((size_t)N * K * WE));
+  const i32x4 rx = raw_desc(X, (int)((size_t)M * ldx * 2));
+  const int nkb = (K + XLK - 1) / XLK;
+  const int kb0 = blockIdx.z * kbs, kb1 = min(nkb, kb0 + kbs);
+  // the NL chunks this wave loads: chunk c = wave + GWAVES i (activations first, then weights)
+  int off0[NL], col0[NL];
+  bool isx[NL];
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int c = wave + GWAVES * i;
+    if (c < XCH) {  // activations: plane c / 8, rows 16 (c % 8) + lane / 4, 4 pieces of 8 columns
+      const int pl = c >> 3, r = 16 * (c & 7) + (lane >> 2);
+      const int m = m0 + r;
+      col0[i] = 8 * ((lane & 3) ^ xswz<4>(r));
+      off0[i] = m < M ? (int)(((size_t)m * ldx + (size_t)pl * K + col0[i]) * 2) : -1;
+      isx[i] = true;
+    } else {  // weights: rows RPC (c - XCH) + lane / PPR
+      const int r = RPC * (c - XCH) + lane / PPR;
+      const int n = n0 + r;
+      col0[i] = PER * ((lane % PPR) ^ xswz<PPR>(r));
+      off0[i] = n < N ? (int)(((size_t)n * K + col0[i]) * WE) : -1;
+      isx[i] = false;
+    }
+  }
+  auto issue = [&](uint4 *stg, int kb) {
+    const int k = kb * XLK;
+    const bool in = kb < kb1;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const int c = wave + GWAVES * i;
+      const int off = (in && off0[i] >= 0 && k + col0[i] < K) ? off0[i] + k * (isx[i] ? 2 : WE) : BUF_OOB;
+      lds_load16(isx[i] ? rx : rw, stg + c * WAVE, off);
+    }
+  };
+  f32x16 acc[2][4] = {};  // [m tile][n tile] of this wave
+  auto compute = [&](const uint4 *stg) {
+    uint4 xf[2][2][2];  // [m tile][plane][step]
+    uint4 wq[4][2];     // [n tile][step] (int8: [n tile][0] holds both steps' 32 weights)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int r = 64 * wm + 32 * mt + ln;  // block row
+          xf[mt][pl][st] = stg[(pl * 8 + (r >> 4)) * WAVE + (r & 15) * 4 + ((2 * g + st) ^ xswz<4>(r))];
+        }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 128 * wn + 32 * t + ln;  // block weight row
+      const uint4 *wst = stg + XCH * WAVE;
+      if constexpr (PPR == 4) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          wq[t][st] = wst[(r / RPC) * WAVE + (r % RPC) * PPR + ((2 * g + st) ^ xswz<PPR>(r))];
+      } else {
+        wq[t][0] = wst[(r / RPC) * WAVE + (r % RPC) * PPR + (g ^ xswz<PPR>(r))];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint4 wv;
+        if constexpr (PPR == 4) {
+          wv = wq[t][st];
+        } else {
+          const uint4 &q = wq[t][0];
+          wv = st ? i8_to_bf16x8(q.z, q.w) : i8_to_bf16x8(q.x, q.y);
+        }
+        const bf16x8 wb = as_bf16x8(wv);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[mt][0][st]), wb, acc[mt][t], 0, 0, 0);
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[mt][1][st]), wb, acc[mt][t], 0, 0, 0);
+        }
+      }
+  };
+  auto sync = [&] {
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm((XST - 2) * NL));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+#pragma unroll
+  for (int i = 0; i < XST - 1; ++i) issue(ring[i], kb0 + i);
+  int cur = 0;
+  for (int kb = kb0; kb < kb1; ++kb) {
+    sync();
+    issue(ring[cur == 0 ? XST - 1 : cur - 1], kb + XST - 1);
+    compute(ring[cur]);
+    cur = cur == XST - 1 ? 0 : cur + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // no copy may still be writing LDS at exit
+  // element i of lane l in acc[mt][t]: activation row 64 wm + 32 mt + (i / 4) * 8 + g * 4 + (i % 4),
+  // weight row 128 wn + 32 t + l % 32
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int n = n0 + 128 * wn + 32 * t + ln;
+    if (n >= N) continue;
+    const float sc = (wscale && gridDim.z == 1) ? wscale[n] : 1.f;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + 64 * wm + 32 * mt + (i >> 2) * 8 + g * 4 + (i & 3);
+        if (m >= M) continue;
+        const float v = acc[mt][t][i];
+        if (gridDim.z > 1) {
+          part[((size_t)blockIdx.z * M + m) * N + n] = v;
+        } else {
+          float *yp = Y + (size_t)m * ldy + n;
+          if (ADD)
+            *yp += v * sc;
+          else
+            *yp = v * sc;
+        }
+      }
+  }
+}
+
 // Sum over the splits, in order, of part[s][m][c .. c + 4) (the loads of up to 8 splits in flight).
 __device__ __forceinline__ float4 split_sum4(const float *__restrict__ part, int S, int M, int N, int m, int c) {
   float4 v = {0.f, 0.f, 0.f, 0.f};

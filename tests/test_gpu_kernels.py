@@ -72,7 +72,8 @@ def rounded_x(band, X):
 
 @pytest.mark.parametrize("band", ["f32", "bf16", "i8"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 37, 48), (5, 64, 352), (64, 96, 256), (70, 1000, 704),
-                                   (3, 130, 1040), (64, 2048, 1024)])
+                                   (3, 130, 1040), (64, 2048, 1024), (200, 300, 48), (257, 520, 1040),
+                                   (129, 257, 4112)])
 def test_gemm_small_and_ragged(band, M, N, K):
     W = synth.normal(3, f"g/W{N}x{K}", (N, K), 0.02)
     X = synth.normal(3, f"g/X{M}x{K}", (M, K), 1.0)
@@ -82,6 +83,27 @@ def test_gemm_small_and_ragged(band, M, N, K):
     if s is not None:
         ref *= s[None, :]
     err = np.max(np.abs(Y - ref)) / np.max(np.abs(ref))
+    assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("band", ["bf16", "i8"])
+@pytest.mark.parametrize("N,K", [(12288, 4096), (4096, 4096), (22528, 4096), (4096, 11264)])
+def test_gemm_moshi7b_shapes_prefill_chunk(band, N, K):
+    """The prefill's 1024-row chunks (128 x 256 tiles, K split where the tiles alone do not cover
+    the CUs), checked on sampled output columns and every row."""
+    M = 1024
+    W = synth.normal(5, f"g8/W{N}x{K}", (N, K), 0.02)
+    X = synth.normal(5, f"g8/X{K}", (M, K), 1.0)
+    Y, us = rq.debug_gemm(band, W, X, iters=5)
+    rows = np.unique(synth.uniform_int(5, f"g8/rows{N}", (96,), N))
+    rows = np.concatenate([[0, N - 1], rows])
+    Ws, s = stored(band, W[rows])
+    ref = rounded_x(band, X) @ Ws.T
+    if s is not None:
+        ref *= s[None, :]
+    err = np.max(np.abs(Y[:, rows] - ref)) / np.max(np.abs(ref))
+    print(f"gemm M=1024 {band} {N}x{K}: {us:.1f} us, {2 * M * N * K / us / 1e6:.1f} TFLOP/s "
+          f"({4 * M * N * K / us / 1e6:.1f} issued)")
     assert err < 1e-5, err
 
 

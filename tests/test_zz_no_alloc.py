@@ -1,6 +1,6 @@
 """moshi_gemm_noalloc (the projection that allocates nothing, for callers that cannot allocate)
-against the entry point it varies, moshi_debug_gemm, through the C ABI: two calls in a row, the
-second with a smaller input, for every band.  Device buffers come from torch (plumbing only)."""
+against the entry point it varies, moshi_debug_gemm, through the C ABI: calls in a row, the second
+with a smaller input and the third with more than one 64-row activation tile, for every band.  Device buffers come from torch (plumbing only)."""
 import ctypes
 
 import numpy as np
@@ -29,7 +29,7 @@ def device_weights(band, W):
 def test_noalloc_gemm_matches_debug_gemm_on_two_calls(band):
     lib = rq.load_library()
     stream = torch.cuda.current_stream().cuda_stream
-    for call, (M, N, K) in enumerate([(64, 4096, 4096), (5, 1000, 352)]):
+    for call, (M, N, K) in enumerate([(64, 4096, 4096), (5, 1000, 352), (200, 1000, 1040)]):
         W = synth.normal(21 + call, "noalloc/w", (N, K), 0.02)
         X = synth.normal(21 + call, "noalloc/x", (M, K), 1.0)
         ref, _ = rq.debug_gemm(band, W, X)
