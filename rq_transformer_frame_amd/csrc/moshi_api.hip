@@ -881,9 +881,12 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
       bf16_t *xo = nullptr;
       if constexpr (std::is_same<XT, bf16_t>::value) xo = X;
       const AttnQ aq{q_rows, o_rows, rm.conv, rm.pos0, xo, P * d.D};
-      // a prefill chunk: key tiles shared by 128 query rows on the matrix cores
+      // a prefill chunk: key tiles shared by 128 query rows on the matrix cores (bf16 hi / lo
+      // products with the bf16 hi / lo projection inputs, float32 products otherwise)
       const dim3 pfg(d.H, (rows + PFA_ROWS - 1) / PFA_ROWS);
-      if (rm.conv >= 0 && d.hd == 128)
+      if (rm.conv >= 0 && d.hd == 128 && std::is_same<XT, bf16_t>::value)
+        k_attn_pf3<KT><<<pfg, PFA_WAVES * 64, 0, st>>>(d, kv, l, aq, rows);
+      else if (rm.conv >= 0 && d.hd == 128)
         k_attn_pf<KT, 128><<<pfg, PFA_WAVES * 64, 0, st>>>(d, kv, l, aq, rows);
       else if (rm.conv >= 0 && d.hd == 64)
         k_attn_pf<KT, 64><<<pfg, PFA_WAVES * 64, 0, st>>>(d, kv, l, aq, rows);

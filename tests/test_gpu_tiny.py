@@ -380,6 +380,37 @@ def test_long_prefill_many_attention_splits_matches_oracle(exec_mode):
             assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], f
 
 
+def test_long_prefill_bf16_head_dim_128_matches_oracle():
+    """The bf16 band with 128-dim heads (the 7B head shape): the prefill's causal attention on the
+    matrix cores and its projections on the 128 x 256 tiles over a full 1024-position chunk and a
+    ragged one of 76, then 3 frames (graph executor: the prefill is the same row-batched path on
+    every executor, and no persistent instance serves this shape).  Against the oracle holding the
+    same bf16 weights."""
+    exec_mode = "graph"
+    cfg = CFG.with_(name="tiny_bf16_h8_long", d_model=1024, n_heads=8, context=1536, band="bf16", dtype="bf16")
+    T = 1100
+    w = synth.gen_weights(cfg)
+    lm = OracleLM(cfg, w)
+    text, agent, user = synth.prefill_tokens(cfg, T, conv=4)
+    text %= cfg.text_card
+    ost = lm.new_state()
+    lm.prefill_forced(ost, text, agent, user)
+    users = synth.user_tokens(cfg, 3, conv=4, start_frame=T)
+    with rq.Session(cfg, exec=exec_mode) as s:
+        s.load_weights(w)
+        s.prefill_forced(0, text, agent, user)
+        for f in range(3):
+            ref = lm.step(ost, users[f])
+            s.step(users[f])
+            tr = s.read_trace(0)
+            assert tr["input_tokens"].tolist() == ref["input_tokens"].tolist(), f
+            assert rel_err(tr["transformer_out"], ref["transformer_out"]) <= TOL, f
+            assert rel_err(tr["text_logits"], ref["text_logits"]) <= TOL, f
+            for cb in range(cfg.dep_q):
+                assert rel_err(tr["audio_logits"][cb], ref["audio_logits"][cb]) <= TOL, (f, cb)
+            assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], f
+
+
 def test_persistent_wait_timeout_exits_and_reset_recovers(weights, oracle):
     """A wait of the persistent frame kernel that gives up (forced from the host: zero polls
     allowed) raises the error flag, every block leaves the kernel, and the step returns
