@@ -288,6 +288,11 @@ __device__ __forceinline__ i32x4 raw_desc(const void *base, int bytes) {
 // (lds wave-uniform).  Issued from inline assembly so that the compiler does not track it: it
 // would otherwise wait for every such load before the next LDS read.  The caller waits for it with
 // an explicit s_waitcnt (a wave's vector memory operations complete in issue order).
+// The same copy to the LDS byte address `lds` (wave-uniform).
+__device__ __forceinline__ void lds_load16_at(i32x4 desc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(desc)
+               : "memory", "m0");
+}
 __device__ __forceinline__ void lds_load16(i32x4 desc, const void *lds, int voff) {
   const int a = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)lds);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(desc)
@@ -448,10 +453,11 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
 // ---- many activation rows (the prefill's chunks): 128 x 256 tiles ------------------------------
 // The same product for M > XM.  With 64-row activation tiles every weight tile is read once per
 // 64 rows, and the re-reads bound the projection (at M = 1024 gate_in moves 4.4 GB for 189 GFLOP).
-// Here a block owns 128 activation rows and 256 weight rows and its four waves split both (2 x 2:
-// 64 rows x 128 weight rows each, 8 accumulator tiles); a K block is 32 columns, so that a stage
-// (the activation tile's hi and lo planes, 16 KB, and the weight tile, 16 KB for bf16 or 8 KB for
-// int8) leaves room for 5 (6) stages in LDS.  Loads, the LDS-direct ring and the waits are those of
+// Here a block owns BM = 128 activation rows and 256 weight rows and its four waves split both
+// (2 x 2: 64 rows x 128 weight rows each, 8 accumulator tiles); a K block is 32 columns, so that a
+// stage (the activation tile's hi and lo planes, 16 KB, and the weight tile, 16 KB for bf16 or 8 KB
+// for int8) leaves room for 5 (6) stages in LDS.  (A block of 256 rows halves the weight re-reads
+// but leaves 3 stages and 1.4 rounds of blocks over the CUs at 1024 rows: slower.)  Loads, the LDS-direct ring and the waits are those of
 // k_gemm_x.  A row segment of a stage is 64 bytes (bf16: 4 pieces of 8 columns; int8 weights: 32
 // bytes, 2 pieces of 16) and its pieces are swizzled with xswz.  MFMA step s of a K block takes, in
 // lane half g, columns 16 g + 8 s .. + 7 of both operands.  The grid walks the activation tiles
@@ -464,13 +470,31 @@ template <typename WT> struct XLW;
 template <> struct XLW<bf16_t> { static constexpr int ELT = 2, PPR = 4, RPC = 16, PER = 8, CH = 16; };
 template <> struct XLW<int8_t> { static constexpr int ELT = 1, PPR = 2, RPC = 32, PER = 16, CH = 8; };
 
+// The dispatcher hands workgroups to the 8 XCDs in turn (linear block b to XCD b % 8), and each XCD
+// has its own L2.  Renumbered so that each XCD runs one contiguous range of tiles, M fastest, the
+// blocks that run together on an XCD share weight and activation tiles in its L2 instead of each
+// fetching its own weight tile through the fabric.
+constexpr int XCDS = 8;
+__device__ __forceinline__ void xcd_tile(int &bx, int &by, int &bz) {
+  const int nx = gridDim.x, ny = gridDim.y, n = nx * ny * gridDim.z;
+  const int b = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int per = n / XCDS, rem = n % XCDS, x = b % XCDS, i = b / XCDS;
+  const int l = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
+  bx = l % nx;
+  by = (l / nx) % ny;
+  bz = l / (nx * ny);
+}
+
 template <typename WT, bool ADD, int TAG>
 __global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, const float *__restrict__ wscale, int N,
                                                     int K, const bf16_t *__restrict__ X, int ldx, int M,
                                                     float *__restrict__ Y, int ldy, float *__restrict__ part, int kbs) {
   constexpr int WE = XLW<WT>::ELT, PPR = XLW<WT>::PPR, RPC = XLW<WT>::RPC, PER = XLW<WT>::PER;
   constexpr int WCH = XLW<WT>::CH;   // weight chunks per stage
-  constexpr int XCH = 16;            // activation chunks per stage: [plane][16-row group]
+  constexpr int BM = XLM;
+  constexpr int XG = BM / 16;        // 16-row groups of the activation tile
+  constexpr int XCH = 2 * XG;        // activation chunks per stage: [plane][16-row group]
+  constexpr int MT = BM / 64;        // 32-row activation tiles per wave
   constexpr int NCH = XCH + WCH;
   constexpr int NL = NCH / GWAVES;   // loads each wave issues per K block
   constexpr int XST = XLDS / (NCH * WAVE * 16);
@@ -478,20 +502,22 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, co
   __shared__ __align__(16) uint4 ring[XST][NCH * WAVE];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave & 1, wn = wave >> 1;
-  const int m0 = blockIdx.x * XLM, n0 = blockIdx.y * XLN;
+  int bx, by, bz;
+  xcd_tile(bx, by, bz);
+  const int m0 = bx * BM, n0 = by * XLN;
   const int ln = lane & 31, g = lane >> 5;
   const i32x4 rw = raw_desc(W, (int)((size_t)N * K * WE));
   const i32x4 rx = raw_desc(X, (int)((size_t)M * ldx * 2));
   const int nkb = (K + XLK - 1) / XLK;
-  const int kb0 = blockIdx.z * kbs, kb1 = min(nkb, kb0 + kbs);
+  const int kb0 = bz * kbs, kb1 = min(nkb, kb0 + kbs);
   // the NL chunks this wave loads: chunk c = wave + GWAVES i (activations first, then weights)
   int off0[NL], col0[NL];
   bool isx[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int c = wave + GWAVES * i;
-    if (c < XCH) {  // activations: plane c / 8, rows 16 (c % 8) + lane / 4, 4 pieces of 8 columns
-      const int pl = c >> 3, r = 16 * (c & 7) + (lane >> 2);
+    if (c < XCH) {  // activations: plane c / XG, rows 16 (c % XG) + lane / 4, 4 pieces of 8 columns
+      const int pl = c / XG, r = 16 * (c % XG) + (lane >> 2);
       const int m = m0 + r;
       col0[i] = 8 * ((lane & 3) ^ xswz<4>(r));
       off0[i] = m < M ? (int)(((size_t)m * ldx + (size_t)pl * K + col0[i]) * 2) : -1;
@@ -514,83 +540,100 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, co
       lds_load16(isx[i] ? rx : rw, stg + c * WAVE, off);
     }
   };
-  f32x16 acc[2][4] = {};  // [m tile][n tile] of this wave
-  auto compute = [&](const uint4 *stg) {
-    uint4 xf[2][2][2];  // [m tile][plane][step]
-    uint4 wq[4][2];     // [n tile][step] (int8: [n tile][0] holds both steps' 32 weights)
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int pl = 0; pl < 2; ++pl)
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int r = 64 * wm + 32 * mt + ln;  // block row
-          xf[mt][pl][st] = stg[(pl * 8 + (r >> 4)) * WAVE + (r & 15) * 4 + ((2 * g + st) ^ xswz<4>(r))];
-        }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
+  // A K block is two MFMA steps of 16 columns, and the loop is pipelined by steps: a step's
+  // fragments are read from LDS while the previous step's products run, and the barrier that
+  // publishes the next stage sits between the two steps, where the step-1 fragments are already in
+  // registers.  Each phase interleaves its memory instructions one by one with the products.
+  f32x16 acc[MT][4] = {};  // [m tile][n tile] of this wave
+  constexpr int NRD = 2 * MT + 4;  // fragment reads per step
+  uint4 fr[2][NRD];                // [step][activation (m tile, plane) ..., weights (n tile) ...]
+  auto rd = [&](const uint4 *stg, int st, int j) {  // fragment read j of step st
+    if (j < 2 * MT) {
+      const int mt = j >> 1, pl = j & 1;
+      const int r = (BM / 2) * wm + 32 * mt + ln;  // block row
+      fr[st][j] = stg[(pl * XG + (r >> 4)) * WAVE + (r & 15) * 4 + ((2 * g + st) ^ xswz<4>(r))];
+    } else {
+      const int t = j - 2 * MT;
       const int r = 128 * wn + 32 * t + ln;  // block weight row
       const uint4 *wst = stg + XCH * WAVE;
-      if constexpr (PPR == 4) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-          wq[t][st] = wst[(r / RPC) * WAVE + (r % RPC) * PPR + ((2 * g + st) ^ xswz<PPR>(r))];
-      } else {
-        wq[t][0] = wst[(r / RPC) * WAVE + (r % RPC) * PPR + (g ^ xswz<PPR>(r))];
-      }
+      // int8: one piece holds the 32 weights of both steps; each step reads it for itself
+      const int pc = PPR == 4 ? 2 * g + st : g;
+      fr[st][j] = wst[(r / RPC) * WAVE + (r % RPC) * PPR + (pc ^ xswz<PPR>(r))];
     }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint4 wv;
-        if constexpr (PPR == 4) {
-          wv = wq[t][st];
-        } else {
-          const uint4 &q = wq[t][0];
-          wv = st ? i8_to_bf16x8(q.z, q.w) : i8_to_bf16x8(q.x, q.y);
-        }
-        const bf16x8 wb = as_bf16x8(wv);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[mt][0][st]), wb, acc[mt][t], 0, 0, 0);
-          acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(xf[mt][1][st]), wb, acc[mt][t], 0, 0, 0);
-        }
-      }
   };
-  auto sync = [&] {
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm((XST - 2) * NL));
+  // product j of a step: plane j / (4 MT) (hi products first, then lo), n tile (j / MT) % 4, m tile j % MT
+  auto mma = [&](int st, int j) {
+    const int pl = j / (4 * MT), t = (j / MT) % 4, mt = j % MT;
+    uint4 wv = fr[st][2 * MT + t];
+    if constexpr (PPR != 4) wv = st ? i8_to_bf16x8(wv.z, wv.w) : i8_to_bf16x8(wv.x, wv.y);
+    acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fr[st][2 * mt + pl]), as_bf16x8(wv), acc[mt][t], 0, 0, 0);
+  };
+  constexpr int NMM = 8 * MT;  // products per step
+  static_assert(NMM >= NRD && NMM >= NRD + NL, "a phase spreads its memory instructions over its products");
+  // LDS byte address of the ring; stage s, chunk c sits at ring0 + ((s NCH + c) WAVE) 16
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)&ring[0][0]);
+  auto issue1 = [&](int stage, int kb, int i) {
+    const int c = wave + GWAVES * i;
+    const int k = kb * XLK;
+    const int off = (kb < kb1 && off0[i] >= 0 && k + col0[i] < K) ? off0[i] + k * (isx[i] ? 2 : WE) : BUF_OOB;
+    lds_load16_at(isx[i] ? rx : rw, ring0 + (uint32_t)((stage * NCH + c) * WAVE * 16), off);
+  };
+  auto barrier = [] {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  // prologue: stages for the first XST - 1 K blocks in flight, then the first block's step-0 reads
 #pragma unroll
-  for (int i = 0; i < XST - 1; ++i) issue(ring[i], kb0 + i);
+  for (int i = 0; i < XST - 1; ++i)
+#pragma unroll
+    for (int l = 0; l < NL; ++l) issue1(i, kb0 + i, l);
+  __builtin_amdgcn_s_waitcnt(vm_wait_imm((XST - 2) * NL));
+  barrier();
+#pragma unroll
+  for (int j = 0; j < NRD; ++j) rd(ring[0], 0, j);
   int cur = 0;
   for (int kb = kb0; kb < kb1; ++kb) {
-    sync();
-    issue(ring[cur == 0 ? XST - 1 : cur - 1], kb + XST - 1);
-    compute(ring[cur]);
-    cur = cur == XST - 1 ? 0 : cur + 1;
+    const int nxt = cur == XST - 1 ? 0 : cur + 1, prv = cur == 0 ? XST - 1 : cur - 1;
+    // phase A: step-0 products, step-1 reads of this block
+#pragma unroll
+    for (int j = 0; j < NMM; ++j) {
+      mma(0, j);
+      if (j < NRD) rd(ring[cur], 1, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the next block's stage has landed (the loads of the XST - 3 blocks after it may still be in
+    // flight), and every wave is done with the previous block's stage, which the loads below refill
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm((XST - 3) * NL));
+    barrier();
+    // phase B: step-1 products; the loads of block kb + XST - 1 and the next block's step-0 reads
+#pragma unroll
+    for (int j = 0; j < NMM; ++j) {
+      mma(1, j);
+      if (j < NL) issue1(prv, kb + XST - 1, j);
+      else if (j < NL + NRD) rd(ring[nxt], 0, j - NL);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    cur = nxt;
   }
   __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // no copy may still be writing LDS at exit
-  // element i of lane l in acc[mt][t]: activation row 64 wm + 32 mt + (i / 4) * 8 + g * 4 + (i % 4),
-  // weight row 128 wn + 32 t + l % 32
+  // element i of lane l in acc[mt][t]: activation row (BM / 2) wm + 32 mt + (i / 4) * 8 + g * 4 +
+  // (i % 4), weight row 128 wn + 32 t + l % 32
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int n = n0 + 128 * wn + 32 * t + ln;
     if (n >= N) continue;
     const float sc = (wscale && gridDim.z == 1) ? wscale[n] : 1.f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = m0 + 64 * wm + 32 * mt + (i >> 2) * 8 + g * 4 + (i & 3);
+        const int m = m0 + (BM / 2) * wm + 32 * mt + (i >> 2) * 8 + g * 4 + (i & 3);
         if (m >= M) continue;
         const float v = acc[mt][t][i];
         if (gridDim.z > 1) {
-          part[((size_t)blockIdx.z * M + m) * N + n] = v;
+          part[((size_t)bz * M + m) * N + n] = v;
         } else {
           float *yp = Y + (size_t)m * ldy + n;
           if (ADD)

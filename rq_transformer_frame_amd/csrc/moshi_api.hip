@@ -717,7 +717,7 @@ void gemm_split(int N, int K, int M, int xn, int cus, int cap_tiles, int &S, int
 // Launch plan of a wide-tile projection: weight tiles per wave (two for the long-K projections
 // with many output rows or many activation rows, where they measured faster; narrow or short-K
 // ones keep one, since two would halve their block count) and the K split.  More than one
-// activation tile of rows (the prefill's chunks) takes the 128 x 256 tiles of k_gemm_xl (nt = 0),
+// activation tile of rows (the prefill's chunks) takes the 128 x 256 tiles of k_gemm_xl (nt = -1),
 // its K split (in 32-column K blocks) chosen as for k_gemm_x: fewest rounds of one block per CU
 // times K blocks per split, plus the partial tiles' traffic, as far as they fit the scratch.
 struct GemmPlan {
@@ -729,7 +729,7 @@ GemmPlan gemm_plan(int N, int K, int M, int cus, int cap_tiles = -1) {
     const int nb = ((M + mk::XLM - 1) / mk::XLM) * ((N + mk::XLN - 1) / mk::XLN);
     const int nkb = (K + mk::XLK - 1) / mk::XLK;
     const size_t cap_floats = (size_t)cap * (mk::GWAVES * 32 * mk::XNMAX) * mk::XM;
-    GemmPlan g{0, 1, nkb};
+    GemmPlan g{-1, 1, nkb};
     const double step_bytes = (double)cus * (mk::XLM * 4 + mk::XLN * 2) * mk::XLK;  // one K block per CU
     double best = 1e30;
     for (int want = 1; want <= std::min(nkb, 8); ++want) {
@@ -754,7 +754,7 @@ template <typename WT, bool ADD, int TAG>
 void gemm_x_launch(hipStream_t st, const GemmPlan &g, float *part, const WT *W, const float *scale, int N, int K,
                    const bf16_t *X, int ldx, int M, float *Y, int ldy) {
   using namespace mk;
-  if (g.nt == 0) {  // activation tiles of 128 rows, walked fastest
+  if (g.nt < 0) {  // activation tiles of 128 rows
     const dim3 grid((M + XLM - 1) / XLM, (N + XLN - 1) / XLN, g.S);
     k_gemm_xl<WT, ADD, TAG><<<grid, GBLOCK, 0, st>>>(W, scale, N, K, X, ldx, M, Y, ldy, part, g.kbs);
     return;

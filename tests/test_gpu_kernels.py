@@ -73,7 +73,7 @@ def rounded_x(band, X):
 @pytest.mark.parametrize("band", ["f32", "bf16", "i8"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 16), (2, 37, 48), (5, 64, 352), (64, 96, 256), (70, 1000, 704),
                                    (3, 130, 1040), (64, 2048, 1024), (200, 300, 48), (257, 520, 1040),
-                                   (129, 257, 4112)])
+                                   (129, 257, 4112), (513, 300, 64), (700, 520, 1040)])
 def test_gemm_small_and_ragged(band, M, N, K):
     W = synth.normal(3, f"g/W{N}x{K}", (N, K), 0.02)
     X = synth.normal(3, f"g/X{M}x{K}", (M, K), 1.0)
@@ -89,7 +89,7 @@ def test_gemm_small_and_ragged(band, M, N, K):
 @pytest.mark.parametrize("band", ["bf16", "i8"])
 @pytest.mark.parametrize("N,K", [(12288, 4096), (4096, 4096), (22528, 4096), (4096, 11264)])
 def test_gemm_moshi7b_shapes_prefill_chunk(band, N, K):
-    """The prefill's 1024-row chunks (128 x 256 tiles, K split where the tiles alone do not cover
+    """The prefill's 1024-row chunks (256 x 256 tiles, K split where the tiles alone do not cover
     the CUs), checked on sampled output columns and every row."""
     M = 1024
     W = synth.normal(5, f"g8/W{N}x{K}", (N, K), 0.02)
