@@ -49,7 +49,7 @@ __global__ __launch_bounds__(PFA_WAVES * 64) void k_attn_pf(Dims d, KV<KT> kv, i
   const int nkeys = (int)(aq.pos0 + rb1);  // keys of the block's last row: slots 0 .. pos0 + rb1 - 1
   const int ntiles = (nkeys + PFA_KT - 1) / PFA_KT;
   const size_t base = kv_index(d, aq.conv, layer, 0, h, 0);
-  const int PS = d.H * HD;  // elements from one cached position to the next
+  constexpr int PS = HD;  // elements from one cached position of the head to the next
   const float scale = 1.0f / sqrtf((float)HD);
 
   // this lane's query: row qw0 + l32 (zero past the chunk), dims QH g .. QH g + QH - 1
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(PFA_WAVES * 64) void k_attn_pf3(Dims d, KV<KT> kv, 
   const int nkeys = (int)(aq.pos0 + rb1);
   const int ntiles = (nkeys + PFA_KT - 1) / PFA_KT;
   const size_t base = kv_index(d, aq.conv, layer, 0, h, 0);
-  const int PS = d.H * HD;
+  constexpr int PS = HD;
   const float scale = 1.0f / sqrtf((float)HD);
 
   // this lane's query (row qw0 + l32, zero past the chunk): step s holds dims 16 s + 8 g .. + 7

@@ -282,10 +282,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_attn(Dims d, Bufs s, int layer, i
 #pragma unroll
         for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
       }
-      dot += __shfl_xor(dot, 8, WAVE);
-      dot += __shfl_xor(dot, 4, WAVE);
-      dot += __shfl_xor(dot, 2, WAVE);
-      dot += __shfl_xor(dot, 1, WAVE);
+      dot = row16_sum(dot);
       dot = __shfl(dot, lane & 48, WAVE);
       sc[p] = dot * scale;
       if (p < npos) mx = fmaxf(mx, sc[p]);
@@ -376,10 +373,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv_attn(Dims d, Bufs s, const fl
 #pragma unroll
         for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
       }
-      dot += __shfl_xor(dot, 8, WAVE);
-      dot += __shfl_xor(dot, 4, WAVE);
-      dot += __shfl_xor(dot, 2, WAVE);
-      dot += __shfl_xor(dot, 1, WAVE);
+      dot = row16_sum(dot);
       dot = __shfl(dot, lane & 48, WAVE);
       sc[p] = dot * scale;
       if (p < npos) mx = fmaxf(mx, sc[p]);

@@ -31,20 +31,42 @@ template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
 
-// Sum over the 64 lanes; the result is taken from lane 0 by callers that need one value.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+// Cross-lane reductions on DPP moves (VALU, no LDS round trip per step).  A DPP move with full row
+// and bank masks and bound_ctrl reads lane CTRL-selected within its row of 16.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over each row of 16 lanes: the two quad swaps (quad_perm [1,0,3,2], [2,3,0,1]), then the
+// half-row mirror and the row mirror.  Each step adds two partial sums that are equal in both
+// lanes of a pair (float addition commutes), so every lane of the row ends with identical bits.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);
+  v += dpp_f<0x4E>(v);
+  v += dpp_f<0x141>(v);
+  v += dpp_f<0x140>(v);
   return v;
 }
 
-// Sum over 64 lanes, lane 0's value broadcast so every lane holds identical bits.
-__device__ __forceinline__ float wave_sum_bcast(float v) { return __shfl(wave_sum(v), 0, WAVE); }
+// Sum over the 64 lanes: row sums, then (row 0 + row 1) + (row 2 + row 3) from lanes 0, 16, 32, 48;
+// every lane holds identical bits.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+// Sum over 64 lanes with identical bits in every lane.
+__device__ __forceinline__ float wave_sum_bcast(float v) { return wave_sum(v); }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, WAVE));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 
 // Block-wide sum: each wave's lane-0 sum goes to LDS, then every thread adds the wave sums in

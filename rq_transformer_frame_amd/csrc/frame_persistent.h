@@ -502,7 +502,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
         }
         const float scale = 1.0f / sqrtf((float)HD);
         const size_t base = kv_index(d, 0, l, 0, h, 0);
-        const int PS = d.H * HD;  // elements from one cached position to the next
+        constexpr int PS = HD;  // elements from one cached position of the head to the next
         const KT *kb = kc + base, *vb = vc + base;
         // a wave takes positions jb + g, jb stepping by PWAVES * 4; the loads of ATTN_U steps are
         // issued together (indexes past the split clamp to its last position, results discarded)
@@ -519,10 +519,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
             float dot = 0.f;
 #pragma unroll
             for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kr[u][i], dot);
-            dot += __shfl_xor(dot, 8, WAVE);
-            dot += __shfl_xor(dot, 4, WAVE);
-            dot += __shfl_xor(dot, 2, WAVE);
-            dot += __shfl_xor(dot, 1, WAVE);
+            dot = row16_sum(dot);
             if (j < j1 && sub == 0) sc[j - j0] = dot * scale;
           }
         }
@@ -815,10 +812,7 @@ __global__ __launch_bounds__(PBLOCK) void k_frame_persistent(const PArgs *__rest
 #pragma unroll
               for (int i = 0; i < DEPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
             }
-            dot += __shfl_xor(dot, 8, WAVE);
-            dot += __shfl_xor(dot, 4, WAVE);
-            dot += __shfl_xor(dot, 2, WAVE);
-            dot += __shfl_xor(dot, 1, WAVE);
+            dot = row16_sum(dot);
             dot = __shfl(dot, lane & 48, WAVE);
             sc[p] = dot * scale;
             if (p < npos) m = fmaxf(m, sc[p]);

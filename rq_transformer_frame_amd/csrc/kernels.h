@@ -66,16 +66,17 @@ struct Bufs {
   const uint64_t *jump; // [32][64]    columns of the xorshift step's 2^i-th power over GF(2)
 };
 
-// Element e of head h at cache slot `slot` of conversation b's layer: [B][L][cap][H][hd], so the
-// cached positions of one conversation's layer are one contiguous run (every head of a position
-// together), and a head's positions are H * hd elements apart.
+// Element e of head h at cache slot `slot` of conversation b's layer: [B][L][H][cap][hd], head-major,
+// so that the positions one head's attention reads are one contiguous run of hd-element rows (an
+// attention block streams whole DRAM pages instead of one 2 * hd-byte piece of every position's
+// row of all heads).
 __device__ __forceinline__ size_t kv_index(const Dims &d, int b, int layer, int slot, int h, int e) {
-  return ((((size_t)b * d.L + layer) * d.cap + slot) * d.H + h) * d.hd + e;
+  return ((((size_t)b * d.L + layer) * d.H + h) * d.cap + slot) * d.hd + e;
 }
 
 template <typename KT>
 struct KV {
-  KT *k, *v;  // [B][L][cap][H][hd]
+  KT *k, *v;  // [B][L][H][cap][hd]
 };
 
 // ---- argmax partials --------------------------------------------------------------------------
@@ -254,6 +255,39 @@ template <int N> __device__ __forceinline__ void ld_row(const bf16_t *p, float *
   }
 }
 
+// N consecutive cache elements as floats through a buffer resource, from byte offset `off` (16-byte
+// aligned for N * sizeof(KT) >= 16, else 8-byte); an offset past the resource's extent reads zeros
+// and makes no memory request.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+template <typename KT, int N>
+__device__ __forceinline__ void ld_row_rsrc(__amdgpu_buffer_rsrc_t r, int off, float *o) {
+  constexpr int BYTES = N * (int)sizeof(KT);
+  uint32_t w[BYTES / 4];
+  if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+    for (int c = 0; c < BYTES / 16; ++c) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * c, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[4 * c + i] = v[i];
+    }
+  } else {
+    static_assert(BYTES == 8, "8 or a multiple of 16 bytes");
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  }
+  if constexpr (sizeof(KT) == 4) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) o[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      o[2 * i] = __uint_as_float(w[i] << 16);
+      o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+}
+
 // k_attn: a wave takes positions jb + g with jb stepping by NWAVES * 4 and issues the cache loads
 // of ATTN_KU steps at once (one split of ATTN_MIN_CHUNK positions is one batch of loads).
 constexpr int ATTN_KU = ATTN_MIN_CHUNK / (NWAVES * 4);
@@ -286,19 +320,28 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   for (int i = 0; i < EPL; ++i) qv[i] = qp[i];
   const float scale = 1.0f / sqrtf((float)HD);
   const size_t base = kv_index(d, b, layer, 0, h, 0);
-  const int PS = d.H * HD;  // elements from one cached position to the next
+  constexpr int PS = HD;  // elements from one cached position of the head to the next
   const KT *kb = kv.k + base, *vb = kv.v + base;
 
-  // indexes past the split clamp to its last position (results discarded), so the loads of a
-  // batch carry no branch; the next batch's loads are issued before the current batch is used
-  // (two batches in flight per wave; the one past the end reads the last position again)
+  // the next batch's loads are issued before the current batch is used (two batches in flight per
+  // wave), through buffer resources over the head's cache region: a step wholly past the split
+  // takes an offset past the region, which reads zeros without a memory request (results
+  // discarded), so the prefetch past the end costs no traffic and the loads carry no branch;
+  // within a step that starts inside the split, indexes past its end clamp to its last position.
   constexpr int STEP = ATTN_KU * NWAVES * 4;
   const int jl = j1 > j0 ? j1 - 1 : 0;
   const int jf = j0 + wave * 4;
-  auto load_batch = [&](const KT *src, int jb0, float(&r)[ATTN_KU][EPL]) {
+  const int region = d.cap * HD * (int)sizeof(KT);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)kb, (short)0, region, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)vb, (short)0, region, BUF_DWORD3);
+  auto load_batch = [&](__amdgpu_buffer_rsrc_t src, int jb0, float(&r)[ATTN_KU][EPL]) {
 #pragma unroll
-    for (int u = 0; u < ATTN_KU; ++u)
-      ld_row<EPL>(src + (size_t)min(jb0 + u * NWAVES * 4 + g, jl) * PS + sub * EPL, r[u]);
+    for (int u = 0; u < ATTN_KU; ++u) {
+      const int off = jb0 + u * NWAVES * 4 < j1
+                          ? (min(jb0 + u * NWAVES * 4 + g, jl) * PS + sub * EPL) * (int)sizeof(KT)
+                          : BUF_OOB;
+      ld_row_rsrc<KT, EPL>(src, off, r[u]);
+    }
   };
   auto scores = [&](int jb0, const float(&kr)[ATTN_KU][EPL]) {
 #pragma unroll
@@ -307,20 +350,17 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
       float dot = 0.f;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kr[u][i], dot);
-      dot += __shfl_xor(dot, 8, WAVE);
-      dot += __shfl_xor(dot, 4, WAVE);
-      dot += __shfl_xor(dot, 2, WAVE);
-      dot += __shfl_xor(dot, 1, WAVE);
+      dot = row16_sum(dot);
       if (j < j1 && sub == 0) sc[j - j0] = dot * scale;
     }
   };
   {
     float ka[ATTN_KU][EPL], kb2[ATTN_KU][EPL];
-    load_batch(kb, jf, ka);
+    load_batch(rk, jf, ka);
     for (int jb0 = jf; jb0 < j1; jb0 += 2 * STEP) {
-      load_batch(kb, jb0 + STEP, kb2);
+      load_batch(rk, jb0 + STEP, kb2);
       scores(jb0, ka);
-      load_batch(kb, jb0 + 2 * STEP, ka);
+      load_batch(rk, jb0 + 2 * STEP, ka);
       scores(jb0 + STEP, kb2);
     }
   }
@@ -350,11 +390,11 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   };
   {
     float va[ATTN_KU][EPL], vb2[ATTN_KU][EPL];
-    load_batch(vb, jf, va);
+    load_batch(rv, jf, va);
     for (int jb0 = jf; jb0 < j1; jb0 += 2 * STEP) {
-      load_batch(vb, jb0 + STEP, vb2);
+      load_batch(rv, jb0 + STEP, vb2);
       accum(jb0, va);
-      load_batch(vb, jb0 + 2 * STEP, va);
+      load_batch(rv, jb0 + 2 * STEP, va);
       accum(jb0 + STEP, vb2);
     }
   }
@@ -658,10 +698,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_out(Dims d, Bufs s, const WT *__r
 #pragma unroll
         for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
       }
-      dot += __shfl_xor(dot, 8, WAVE);
-      dot += __shfl_xor(dot, 4, WAVE);
-      dot += __shfl_xor(dot, 2, WAVE);
-      dot += __shfl_xor(dot, 1, WAVE);
+      dot = row16_sum(dot);
       dot = __shfl(dot, lane & 48, WAVE);  // the group's first lane: identical bits in the group
       sc[p] = dot * scale;
       if (p < npos) m = fmaxf(m, sc[p]);
@@ -802,12 +839,15 @@ __global__ __launch_bounds__(BLOCK) void k_kv_snapshot(Dims d, KV<KT> kv, KT *__
   const int slot = (int)((p0 + j) % d.cap);
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    KT *c = (which ? kv.v : kv.k) + kv_index(d, b, l, slot, 0, 0);
+    KT *c = which ? kv.v : kv.k;
     KT *o = buf + (((size_t)which * d.L + l) * n + j) * d.D;
-    if (to_buf)
-      for (int e = threadIdx.x; e < d.D; e += BLOCK) o[e] = c[e];
-    else
-      for (int e = threadIdx.x; e < d.D; e += BLOCK) c[e] = o[e];
+    for (int e = threadIdx.x; e < d.D; e += BLOCK) {
+      const size_t ci = kv_index(d, b, l, slot, e / d.hd, e % d.hd);
+      if (to_buf)
+        o[e] = c[ci];
+      else
+        c[ci] = o[e];
+    }
   }
 }
 
