@@ -284,18 +284,13 @@ __device__ __forceinline__ i32x4 raw_desc(const void *base, int bytes) {
                __builtin_amdgcn_readfirstlane(bytes), BUF_DWORD3};
 }
 
-// LDS-direct load: lane l's 16 bytes at byte offset voff of the buffer go to LDS at lds + 16 l
-// (lds wave-uniform).  Issued from inline assembly so that the compiler does not track it: it
-// would otherwise wait for every such load before the next LDS read.  The caller waits for it with
-// an explicit s_waitcnt (a wave's vector memory operations complete in issue order).
-// The same copy to the LDS byte address `lds` (wave-uniform).
+// LDS-direct load: lane l's 16 bytes at byte offset voff of the buffer go to the LDS byte address
+// lds + 16 l (lds wave-uniform, a scalar).  Issued from inline assembly so that the compiler does
+// not track it: it would otherwise wait for every such load before the next LDS read.  The caller
+// waits for it with an explicit s_waitcnt (a wave's vector memory operations complete in issue
+// order).
 __device__ __forceinline__ void lds_load16_at(i32x4 desc, uint32_t lds, int voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voff), "s"(desc)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_load16(i32x4 desc, const void *lds, int voff) {
-  const int a = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(a), "v"(voff), "s"(desc)
                : "memory", "m0");
 }
 
@@ -345,18 +340,22 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
   }
   // K block kb into a stage (past kb1 or K: out-of-range loads, which read zero and move no data,
   // so every wave issues the same count and the waits below stay exact)
-  auto issue = [&](uint4 *stg, int kb) {
+  // LDS byte address of the ring: stage s, chunk c at ring0 + ((s NCH + c) WAVE) 16
+  const uint32_t ring0 = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void *)&ring[0][0]);
+  auto issue = [&](int stage, int kb) {
     const int k = kb * XKB;
     const bool in = kb < kb1;
+    const uint32_t sb = ring0 + (uint32_t)(stage * NCH * WAVE * 16);
 #pragma unroll
     for (int i = 0; i < XCH / GWAVES; ++i) {
       const int off = (in && xo[i] >= 0 && k + xcol[i] < K) ? xo[i] + k * 2 : BUF_OOB;
-      lds_load16(rx, stg + (GWAVES * wave + i) * WAVE, off);
+      lds_load16_at(rx, sb + (uint32_t)((GWAVES * wave + i) * WAVE * 16), off);
     }
 #pragma unroll
     for (int c = 0; c < WC; ++c) {
       const int off = (in && wo[c] >= 0 && k + wcol[c] < K) ? wo[c] + k * WE : BUF_OOB;
-      lds_load16(rw, stg + (XCH + wave * WC + c) * WAVE, off);
+      lds_load16_at(rw, sb + (uint32_t)((XCH + wave * WC + c) * WAVE * 16), off);
     }
   };
   f32x16 acc[XNT][2] = {};  // [weight tile][activation tile]
@@ -412,11 +411,11 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_x(const WT *__restrict__ W, con
     asm volatile("" ::: "memory");
   };
 #pragma unroll
-  for (int i = 0; i < XST - 1; ++i) issue(ring[i], kb0 + i);
+  for (int i = 0; i < XST - 1; ++i) issue(i, kb0 + i);
   int cur = 0;  // stage of K block kb
   for (int kb = kb0; kb < kb1; ++kb) {
     sync();
-    issue(ring[cur == 0 ? XST - 1 : cur - 1], kb + XST - 1);
+    issue(cur == 0 ? XST - 1 : cur - 1, kb + XST - 1);
     compute(ring[cur]);
     cur = cur == XST - 1 ? 0 : cur + 1;
   }
@@ -530,16 +529,6 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, co
       isx[i] = false;
     }
   }
-  auto issue = [&](uint4 *stg, int kb) {
-    const int k = kb * XLK;
-    const bool in = kb < kb1;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int c = wave + GWAVES * i;
-      const int off = (in && off0[i] >= 0 && k + col0[i] < K) ? off0[i] + k * (isx[i] ? 2 : WE) : BUF_OOB;
-      lds_load16(isx[i] ? rx : rw, stg + c * WAVE, off);
-    }
-  };
   // A K block is two MFMA steps of 16 columns, and the loop is pipelined by steps: a step's
   // fragments are read from LDS while the previous step's products run, and the barrier that
   // publishes the next stage sits between the two steps, where the step-1 fragments are already in
