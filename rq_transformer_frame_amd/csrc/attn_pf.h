@@ -135,7 +135,7 @@ __global__ __launch_bounds__(PFA_WAVES * 64) void k_attn_pf(Dims d, KV<KT> kv, i
         p[i] = (int64_t)key <= qpos ? sacc[i] * scale : -INFINITY;
         mx = fmaxf(mx, p[i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = xor32_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float corr = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
       float rs = 0.f;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(PFA_WAVES * 64) void k_attn_pf(Dims d, KV<KT> kv, i
         p[i] = p[i] == -INFINITY ? 0.f : expf(p[i] - m_new);
         rs += p[i];
       }
-      rs += __shfl_xor(rs, 32, 64);
+      rs = xor32_sum(rs);
       l_run = l_run * corr + rs;
       m_run = m_new;
 #pragma unroll
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(PFA_WAVES * 64) void k_attn_pf3(Dims d, KV<KT> kv, 
         p[i] = (int64_t)key <= qpos ? sacc[i] * scale : -INFINITY;
         mx = fmaxf(mx, p[i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = xor32_max(mx);
       const float m_new = fmaxf(m_run, mx);
       const float corr = m_run == -INFINITY ? 0.f : expf(m_run - m_new);
       float rs = 0.f;
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(PFA_WAVES * 64) void k_attn_pf3(Dims d, KV<KT> kv, 
         p[i] = p[i] == -INFINITY ? 0.f : expf(p[i] - m_new);
         rs += p[i];
       }
-      rs += __shfl_xor(rs, 32, 64);
+      rs = xor32_sum(rs);
       l_run = l_run * corr + rs;
       m_run = m_new;
 #pragma unroll

@@ -58,6 +58,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 
+// Lane l's value combined with lane l ^ 32's (l ^ 16's) through the gfx950 lane swaps (VALU): with
+// both operands v, the two results hold, in every lane, the two values of the pair, so their sum
+// (max) has identical bits in both lanes -- the same value a shuffle-and-add gives.
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Sum over 64 lanes with identical bits in every lane.
 __device__ __forceinline__ float wave_sum_bcast(float v) { return wave_sum(v); }
 

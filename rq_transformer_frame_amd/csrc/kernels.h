@@ -400,8 +400,7 @@ __global__ __launch_bounds__(BLOCK) void k_attn(Dims d, Bufs s, KV<KT> kv, int l
   }
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
-    op[i] += __shfl_xor(op[i], 16, WAVE);
-    op[i] += __shfl_xor(op[i], 32, WAVE);
+    op[i] = xor32_sum(xor16_sum(op[i]));
   }
   if (g == 0) {
 #pragma unroll
