@@ -487,4 +487,175 @@ __global__ __launch_bounds__(BLOCK) void k_embed_rows(Dims d, const int32_t *__r
   }
 }
 
+// NW consecutive 32-bit words through a buffer resource from byte offset `off` (16-byte aligned
+// for NW >= 4, else 8-byte); an offset past the resource's extent reads zeros and makes no request.
+template <int NW>
+__device__ __forceinline__ void ld_words_rsrc(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&w)[NW]) {
+  if constexpr (NW % 4 == 0) {
+#pragma unroll
+    for (int c = 0; c < NW / 4; ++c) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * c, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[4 * c + i] = v[i];
+    }
+  } else {
+    static_assert(NW == 2, "8 bytes or a multiple of 16");
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+  }
+}
+
+// a4.2 for many conversation rows at once (one decode step each): one block per (head h, row z)
+// and no split of the positions.  A single pass over the n cached positions loads each step's
+// keys and values together (two batches of KU steps in flight per wave, through buffer resources
+// over the head's cache region: positions past n read zeros without a memory request), and every
+// 16-lane group keeps an online softmax over the positions it takes (jw + g + 16 t, jw = 4 wave),
+// rescaling its running sum and output when the running max grows.  The 4 groups of a wave then
+// merge through the lane swaps (each swap returns the even-row or lower-half value and the
+// odd-row or upper-half value in fixed slots, so both lanes of a pair compute identical bits),
+// and the 4 waves through LDS in wave order: m = max, weights exp(m_w - m), out = sum w o_w /
+// sum w l_w ([LM] attend: softmax(q k^T / sqrt(hd)) v over the cached positions).
+template <typename KT, int HD>
+__global__ __launch_bounds__(BLOCK) void k_attn_dec(Dims d, Bufs s, KV<KT> kv, int layer, int b0, AttnQ aq) {
+  constexpr int EPL = HD / 16;  // elements per lane; 16 lanes cover one position's head slice
+  constexpr int KU = 2;         // steps per batch
+  constexpr int STEP = KU * NWAVES * 4;
+  __shared__ float wm[NWAVES], wl[NWAVES];
+  __shared__ float wo[NWAVES][HD];
+  const int h = blockIdx.x, z = blockIdx.y, b = b0 + z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
+  const int64_t pos = s.offset[b];
+  const int n = (int)(pos + 1 < (int64_t)d.C ? pos + 1 : (int64_t)d.C);
+  float qv[EPL];
+  const float *qp = s.q + (size_t)b * d.D + h * HD + sub * EPL;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) qv[i] = qp[i];
+  const float scale = 1.0f / sqrtf((float)HD);
+  const size_t base = kv_index(d, b, layer, 0, h, 0);
+  const int region = d.cap * HD * (int)sizeof(KT);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)(kv.k + base), (short)0, region, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void *)(kv.v + base), (short)0, region, BUF_DWORD3);
+  // loaded rows stay in their storage words until used (bf16: half the registers of floats)
+  constexpr int NW = EPL * (int)sizeof(KT) / 4;
+  auto load = [&](int jb, uint32_t(&kr)[KU][NW], uint32_t(&vr)[KU][NW]) {
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int j = jb + g + u * NWAVES * 4;
+      const int off = j < n ? (j * HD + sub * EPL) * (int)sizeof(KT) : BUF_OOB;
+      ld_words_rsrc<NW>(rk, off, kr[u]);
+      ld_words_rsrc<NW>(rv, off, vr[u]);
+    }
+  };
+  auto elt = [](const uint32_t(&w)[NW], int i) {
+    if constexpr (sizeof(KT) == 4)
+      return __uint_as_float(w[i]);
+    else
+      return __uint_as_float((i & 1) ? (w[i >> 1] & 0xffff0000u) : (w[i >> 1] << 16));
+  };
+  float m = -INFINITY, l = 0.f, o[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) o[i] = 0.f;
+  auto consume = [&](int jb, const uint32_t(&kr)[KU][NW], const uint32_t(&vr)[KU][NW]) {
+    float sc[KU];
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], elt(kr[u], i), dot);
+      dot = row16_sum(dot) * scale;
+      sc[u] = jb + g + u * NWAVES * 4 < n ? dot : -INFINITY;
+      mx = fmaxf(mx, sc[u]);
+    }
+    if (mx == -INFINITY) return;  // no position of this group yet
+    const float corr = expf(m - mx);  // 0 while m is -inf
+    l *= corr;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] *= corr;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const float p = expf(sc[u] - mx);  // 0 for a position past n
+      l += p;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) o[i] = fmaf(p, elt(vr[u], i), o[i]);
+    }
+    m = mx;
+  };
+  {
+    const int jw = wave * 4;
+    uint32_t ka[KU][NW], va[KU][NW], kb2[KU][NW], vb2[KU][NW];
+    load(jw, ka, va);
+    for (int jb = jw; jb < n; jb += 2 * STEP) {
+      load(jb + STEP, kb2, vb2);
+      consume(jb, ka, va);
+      load(jb + 2 * STEP, ka, va);
+      consume(jb + STEP, kb2, vb2);
+    }
+  }
+  // merge two (m, l, o) states; a and b are the same two states in both lanes of a pair
+  auto merge = [&](float ma, float la, const float *oa, float mb, float lb, const float *ob) {
+    const float mm = fmaxf(ma, mb);
+    const float wa = ma == -INFINITY ? 0.f : expf(ma - mm), wb = mb == -INFINITY ? 0.f : expf(mb - mm);
+    m = mm;
+    l = la * wa + lb * wb;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) o[i] = oa[i] * wa + ob[i] * wb;
+  };
+  {
+    float oa[EPL], ob[EPL];
+    const auto rm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    const auto rl = __builtin_amdgcn_permlane16_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(o[i]), __float_as_uint(o[i]), false, false);
+      oa[i] = __uint_as_float(r[0]);
+      ob[i] = __uint_as_float(r[1]);
+    }
+    merge(__uint_as_float(rm[0]), __uint_as_float(rl[0]), oa, __uint_as_float(rm[1]), __uint_as_float(rl[1]), ob);
+  }
+  {
+    float oa[EPL], ob[EPL];
+    const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    const auto rl = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l), false, false);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(o[i]), __float_as_uint(o[i]), false, false);
+      oa[i] = __uint_as_float(r[0]);
+      ob[i] = __uint_as_float(r[1]);
+    }
+    merge(__uint_as_float(rm[0]), __uint_as_float(rl[0]), oa, __uint_as_float(rm[1]), __uint_as_float(rl[1]), ob);
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) wo[wave][sub * EPL + i] = o[i];
+    if (sub == 0) {
+      wm[wave] = m;
+      wl[wave] = l;
+    }
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < HD; t += BLOCK) {
+    float mm = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) mm = fmaxf(mm, wm[w]);
+    float lsum = 0.f, acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) {
+      const float ww = wm[w] == -INFINITY ? 0.f : expf(wm[w] - mm);
+      lsum += wl[w] * ww;
+      acc += wo[w][t] * ww;
+    }
+    const float v = acc / lsum;
+    if (aq.xo) {
+      bf16_t *row = aq.xo + (size_t)z * aq.ldxo + h * HD;
+      const bf16_t hi = f2bf(v);
+      row[t] = hi;
+      row[d.D + t] = f2bf(v - bf2f(hi));
+    } else {
+      s.o[(size_t)b * d.D + h * HD + t] = v;
+    }
+  }
+}
+
 }  // namespace mk

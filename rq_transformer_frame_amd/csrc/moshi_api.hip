@@ -890,6 +890,11 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
         k_attn_pf<KT, 128><<<pfg, PFA_WAVES * 64, 0, st>>>(d, kv, l, aq, rows);
       else if (rm.conv >= 0 && d.hd == 64)
         k_attn_pf<KT, 64><<<pfg, PFA_WAVES * 64, 0, st>>>(d, kv, l, aq, rows);
+      // decode rows with one split per (head, row): the single-pass online-softmax kernel
+      else if (attn_splits == 1 && d.hd == 128)
+        k_attn_dec<KT, 128><<<dim3(d.H, rows), BLOCK, 0, st>>>(d, b, kv, l, rm.b0, aq);
+      else if (attn_splits == 1 && d.hd == 64)
+        k_attn_dec<KT, 64><<<dim3(d.H, rows), BLOCK, 0, st>>>(d, b, kv, l, rm.b0, aq);
       else if (d.hd == 128)
         k_attn<KT, 128><<<dim3(d.H, attn_splits, rows), BLOCK, chunk * 4, st>>>(d, b, kv, l, rm.b0, aq);
       else

@@ -250,6 +250,35 @@ def test_batch_of_three_conversations_matches_single_runs(weights, oracle):
         assert [s.offset(b) for b in range(B)] == [6, 0, 6]
 
 
+def test_batch_of_256_after_prefixes_matches_oracle(weights, oracle):
+    """256 conversations with prefixes of 0..61 positions, then 6 greedy frames (some caches pass
+    the 64-position window).  With 4 heads and 256 rows the attention takes one block per (head,
+    conversation) on a 256-CU part: the single-pass online-softmax kernel.  Tokens equal the
+    oracle's; logits within TOL."""
+    B, F = 256, 6
+    starts = synth.uniform_int(11, "b256/start", (B,), 62).astype(int)
+    pre = [synth.prefill_tokens(CFG, int(starts[b]), conv=b) for b in range(B)]
+    users = np.stack([synth.user_tokens(CFG, F, conv=b, start_frame=int(starts[b])) for b in range(B)], axis=1)
+    refs = []
+    for b in range(B):
+        ost = oracle.new_state()
+        if starts[b]:
+            oracle.prefill_forced(ost, *pre[b])
+        refs.append([oracle.step(ost, users[f, b]) for f in range(F)])
+    with rq.Session(CFG, batch=B) as s:
+        s.load_weights(weights)
+        for b in range(B):
+            if starts[b]:
+                s.prefill_forced(b, *pre[b])
+        for f in range(F):
+            st, out, has = s.step(users[f])
+            for b in range(B):
+                tr = s.read_trace(b)
+                ref = refs[b][f]
+                assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], (f, b, int(starts[b]))
+                assert rel_err(tr["text_logits"], ref["text_logits"]) <= TOL, (f, b)
+
+
 SIM = {"bf16": "f32", "i8": "i8sim", "q4": "q4sim", "q8": "q8sim"}
 
 
