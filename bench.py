@@ -29,19 +29,19 @@ METRIC = "frames/s (80 ms) at B=1, Moshi-7B shape bf16; % of HBM roofline"
 # HBM bytes per dispatch of the dominant kernels, from two rocprofv3 --pmc runs (FETCH_SIZE,
 # WRITE_SIZE) scaled by a 256 MiB device-to-device copy in the same runs (profiles/ holds the
 # summaries and commands).  Valid only for the kernel sources they were taken on (the files the
-# B=1 frame kernels and the attention are compiled from, and the launch code): the bench reports
+# B=1 frame kernels and the attentions are compiled from, and the launch code): the bench reports
 # traffic null when their hash differs.
 TRAFFIC = {
-    "sources_sha256": "46e01cfd69e2a8e8157ebf9014237330a8674c87eb20a49c43af2a29297645c3",
+    "sources_sha256": "9532a687e959108824060ed17c8b8abee76bdf5a40709fc582af3e5db19b4b8e",
     "per_dispatch": {  # config/KV storage/kernel
-        "moshi7b_bf16_b1/f32/frame_persistent": 14875271591,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
-        "moshi7b_bf16_b1/f32/gate_in": 185052852,
-        "moshi7b_bf16_b64/bf16/attn": 517720171,  # profiles/frame_moshi7b_bf16_b64_hbm_traffic.md
+        "moshi7b_bf16_b1/f32/frame_persistent": 14875755841,  # profiles/frame_moshi7b_bf16_b1_hbm_traffic.md
+        "moshi7b_bf16_b1/f32/gate_in": 185060304,
+        "moshi7b_bf16_b64/bf16/attn": 517958289,  # profiles/frame_moshi7b_bf16_b64_hbm_traffic.md
     },
 }
 
 
-TRAFFIC_SOURCES = ("device_common.h", "kernels.h", "frame_persistent.h", "persistent_variants.h",
+TRAFFIC_SOURCES = ("device_common.h", "kernels.h", "batch.h", "frame_persistent.h", "persistent_variants.h",
                    "persistent_hd128_bf16_kvf32.hip", "moshi_api.hip")
 
 
