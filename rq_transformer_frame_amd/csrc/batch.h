@@ -58,6 +58,8 @@ __global__ __launch_bounds__(ADD_BLOCK) void k_add_rows_cvt(const float *__restr
   const int m = blockIdx.x;
   float ss = 0.f;
   for (int c = 4 * threadIdx.x; c < N; c += 4 * ADD_BLOCK) {
+    float *yp = Y + (size_t)m * ldy + c;
+    const float4 y = *reinterpret_cast<const float4 *>(yp);  // in flight with the partials below
     float4 v = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < S; s0 += 8) {
       float4 p[8];
@@ -73,8 +75,6 @@ __global__ __launch_bounds__(ADD_BLOCK) void k_add_rows_cvt(const float *__restr
         v.w += p[u].w;
       }
     }
-    float *yp = Y + (size_t)m * ldy + c;
-    const float4 y = *reinterpret_cast<const float4 *>(yp);
     float xn[4] = {v.x, v.y, v.z, v.w};
     const float yv[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
@@ -523,8 +523,25 @@ __global__ __launch_bounds__(BLOCK) void k_attn_dec(Dims d, Bufs s, KV<KT> kv, i
   constexpr int STEP = KU * NWAVES * 4;
   __shared__ float wm[NWAVES], wl[NWAVES];
   __shared__ float wo[NWAVES][HD];
-  const int h = blockIdx.x, z = blockIdx.y, b = b0 + z;
+  const int h = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
+  // rows in order of decreasing cached length (ties by row): block y takes the y-th longest, so
+  // the longest conversations are dispatched first and none is left streaming alone at the end.
+  // With up to 64 rows every wave ranks them itself (lane l holds row l); more rows keep the
+  // grid's order.
+  int z = blockIdx.y;
+  if (gridDim.y <= WAVE) {
+    const int rows = gridDim.y;
+    const int nl = lane < rows ? (int)min(s.offset[b0 + lane] + 1, (int64_t)d.C) : -1;
+    int rank = 0;
+    for (int k = 0; k < rows; ++k) {
+      const int nk = __builtin_amdgcn_readlane(nl, k);
+      rank += (nk > nl || (nk == nl && k < lane)) ? 1 : 0;
+    }
+    const unsigned long long hit = __ballot(lane < rows && rank == (int)blockIdx.y);
+    z = __builtin_ctzll(hit);
+  }
+  const int b = b0 + z;
   const int64_t pos = s.offset[b];
   const int n = (int)(pos + 1 < (int64_t)d.C ? pos + 1 : (int64_t)d.C);
   float qv[EPL];
