@@ -353,11 +353,12 @@ def test_prefill_row_batches_then_single_frames(weights, oracle):
             compare_step(s.read_trace(0), ref, st, out, has, T + f)
 
 
-@pytest.mark.parametrize("batch", [1, 3])
+@pytest.mark.parametrize("batch", [1, 3, 256])
 def test_bf16_kv_cache_on_the_tiny_model(weights, batch):
     """The opt-in bfloat16 KV cache (bf16 band), single-conversation and batched paths, against the
     oracle on the same bf16-rounded weights (the KV storage loss stays within the bar at this
-    context length)."""
+    context length).  With 256 conversations the attention takes one block per (head,
+    conversation): the single-pass kernel on the bfloat16 cache."""
     w16 = {k: (synth.f32_to_bf16_bits(v) if v.ndim == 2 else v) for k, v in weights.items()}
     ref_lm = OracleLM(CFG, w16)
     users = np.stack([synth.user_tokens(CFG, 8, conv=b) for b in range(batch)], axis=1)
