@@ -314,22 +314,35 @@ __global__ __launch_bounds__(BLOCK) void k_dep_attn(Dims d, Bufs s, int layer, i
 // 3 Dd), times the int8 row scales when wscale is set (S = 1 and no scales: `part` is the product
 // itself); k and v become the per-frame cache entry (layer, cb); then the attention of q over the
 // cb + 1 entries exactly as k_dep_attn, this step's entry taken from registers; o goes to X[m]
-// (XPut layout).  EPL (head dims per lane) a multiple of 4.
+// (XPut layout).  EPL (head dims per lane) a multiple of 4.  Grid (rows, ceil(Hd / 4)) of one wave:
+// each 16-lane group takes one head, and the earlier entries' loads are issued with the split
+// partials', one memory round trip.
 template <typename XT, int EPL>
-__global__ __launch_bounds__(BLOCK) void k_dep_qkv_attn(Dims d, Bufs s, const float *__restrict__ part, int S, int M,
+__global__ __launch_bounds__(WAVE) void k_dep_qkv_attn(Dims d, Bufs s, const float *__restrict__ part, int S, int M,
                                                         const float *__restrict__ wscale, int layer, int cb,
                                                         XT *__restrict__ X, int ldx, int b0) {
   static_assert(EPL % 4 == 0, "columns are summed four at a time");
   const int m = blockIdx.x, b = b0 + m;
   const int Dd = d.Dd, hdd = d.hdd, N = 3 * Dd;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, sub = lane & 15;
+  const int lane = threadIdx.x & 63, g = lane >> 4, sub = lane & 15;
   float *kv0 = s.dkv + ((((size_t)b * d.Ld + layer) * d.Q) * 2) * Dd;
   float *kvc = kv0 + (size_t)cb * 2 * Dd;
   const float scale = 1.0f / sqrtf((float)hdd);
   const int npos = cb + 1;
-  for (int hh = wave * 4 + g; hh < d.Hd; hh += NWAVES * 4) {
+  const int hh = blockIdx.y * 4 + g;
+  if (hh < d.Hd) {  // a whole 16-lane group (the lanes its row sums read) or none
     const int e0 = hh * hdd + sub * EPL;
     float qv[EPL], kk[DEP_MAX_POS][EPL], vv[DEP_MAX_POS][EPL], kc[EPL], vc[EPL];
+#pragma unroll
+    for (int p = 0; p < DEP_MAX_POS; ++p) {  // the earlier entries first: they do not wait for the sums
+      if (p < cb) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+          kk[p][i] = kv0[(size_t)p * 2 * Dd + e0 + i];
+          vv[p][i] = kv0[(size_t)p * 2 * Dd + Dd + e0 + i];
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < EPL; i += 4) {
       const float4 a4 = split_sum4(part, S, M, N, m, e0 + i);
@@ -350,13 +363,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv_attn(Dims d, Bufs s, const fl
     }
 #pragma unroll
     for (int p = 0; p < DEP_MAX_POS; ++p) {
-      if (p < cb) {
-#pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-          kk[p][i] = kv0[(size_t)p * 2 * Dd + e0 + i];
-          vv[p][i] = kv0[(size_t)p * 2 * Dd + Dd + e0 + i];
-        }
-      } else if (p == cb) {
+      if (p == cb) {
 #pragma unroll
         for (int i = 0; i < EPL; ++i) {
           kk[p][i] = kc[i];
@@ -373,8 +380,7 @@ __global__ __launch_bounds__(BLOCK) void k_dep_qkv_attn(Dims d, Bufs s, const fl
 #pragma unroll
         for (int i = 0; i < EPL; ++i) dot = fmaf(qv[i], kk[p][i], dot);
       }
-      dot = row16_sum(dot);
-      dot = __shfl(dot, lane & 48, WAVE);
+      dot = row16_sum(dot);  // identical bits in the group's 16 lanes
       sc[p] = dot * scale;
       if (p < npos) mx = fmaxf(mx, sc[p]);
     }

@@ -1009,8 +1009,8 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
                                                  P * d.Dd, rows, Y, 3 * d.Dd);
           with_epl(d.hdd, [&](auto e) {
             if constexpr (decltype(e)::value % 4 == 0)
-              k_dep_qkv_attn<XT, decltype(e)::value><<<rows, BLOCK, 0, st>>>(d, b, src, S, rows, sc, j, cb, X,
-                                                                             P * d.Dd, b0);
+              k_dep_qkv_attn<XT, decltype(e)::value><<<dim3(rows, (d.Hd + 3) / 4), WAVE, 0, st>>>(
+                  d, b, src, S, rows, sc, j, cb, X, P * d.Dd, b0);
           });
         } else {
           gemm<WT, false, MOSHI_STAGE_DEP_QKV>(st, s->cus, s->gpart, W(lw.in), s->scale(lw.in), 3 * d.Dd, d.Dd, X,
