@@ -694,6 +694,10 @@ void enqueue_frame_t(moshi_state *s, int b0, int nb, bool temporal_only, const i
 // split minimises rounds x K blocks per split, plus the partial tiles' write and read (counted in
 // the same unit: one K block of every CU's weight rows) and a reduction launch; the partials must
 // fit `cap_tiles` tiles of the scratch.
+// Each round of blocks also pays a block's start-up (its first stages' loads, the partial-tile
+// stores at its end), about XPRO K blocks' worth: without it the model preferred 1.7 rounds of
+// 440 blocks for gate_in at 64 rows (55.0 us with the reduction) over one round of 176 (47.8 us).
+constexpr int XPRO = 6;
 void gemm_split(int N, int K, int M, int xn, int cus, int cap_tiles, int &S, int &kbs) {
   const int nb = ((N + xn - 1) / xn) * ((M + mk::XM - 1) / mk::XM);
   const int nkb = (K + mk::XKB - 1) / mk::XKB;
@@ -705,7 +709,7 @@ void gemm_split(int N, int K, int M, int xn, int cus, int cap_tiles, int &S, int
     const int kb = (nkb + want - 1) / want, sp = (nkb + kb - 1) / kb;
     if (sp > 1 && sp * nb > cap_tiles) break;
     const double rounds = (double)((sp * nb + cus - 1) / cus);
-    const double cost = rounds * kb + (sp > 1 ? 2.0 * sp * M * N * 4 / step_bytes + 4.0 : 0.0);
+    const double cost = rounds * (kb + XPRO) + (sp > 1 ? 2.0 * sp * M * N * 4 / step_bytes + 4.0 : 0.0);
     if (cost < best) {
       best = cost;
       S = sp;
