@@ -484,10 +484,15 @@ __device__ __forceinline__ void xcd_tile(int &bx, int &by, int &bz) {
   bz = l / (nx * ny);
 }
 
-template <typename WT, bool ADD, int TAG>
+// GATE (the gated unit's first product, one split): the epilogue writes
+// gx[m][j] = silu(y[m][2j]) * y[m][2j + 1] in the XPut layout (row stride ldg, F = N / 2 columns)
+// in place of Y.  The block's product tile goes through the LDS of the ring (free once the K loop
+// is done), so the pairs are read as float2 and the outputs stored row by row.
+template <typename WT, bool ADD, int TAG, bool GATE = false>
 __global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, const float *__restrict__ wscale, int N,
                                                     int K, const bf16_t *__restrict__ X, int ldx, int M,
-                                                    float *__restrict__ Y, int ldy, float *__restrict__ part, int kbs) {
+                                                    float *__restrict__ Y, int ldy, float *__restrict__ part, int kbs,
+                                                    bf16_t *__restrict__ gx = nullptr, int ldg = 0) {
   constexpr int WE = XLW<WT>::ELT, PPR = XLW<WT>::PPR, RPC = XLW<WT>::RPC, PER = XLW<WT>::PER;
   constexpr int WCH = XLW<WT>::CH;   // weight chunks per stage
   constexpr int BM = XLM;
@@ -607,6 +612,9 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, co
     cur = nxt;
   }
   __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));  // no copy may still be writing LDS at exit
+  static_assert(!GATE || sizeof(ring) >= (size_t)BM * XLN * 4, "the product tile fits the ring");
+  float *gtile = reinterpret_cast<float *>(&ring[0][0]);  // GATE: [BM][XLN] products
+  if (GATE) __syncthreads();  // every wave's fragment reads of the last stage are done
   // element i of lane l in acc[mt][t]: activation row (BM / 2) wm + 32 mt + (i / 4) * 8 + g * 4 +
   // (i % 4), weight row 128 wn + 32 t + l % 32
 #pragma unroll
@@ -621,7 +629,9 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, co
         const int m = m0 + (BM / 2) * wm + 32 * mt + (i >> 2) * 8 + g * 4 + (i & 3);
         if (m >= M) continue;
         const float v = acc[mt][t][i];
-        if (gridDim.z > 1) {
+        if (GATE) {
+          gtile[(m - m0) * XLN + (n - n0)] = v * sc;
+        } else if (gridDim.z > 1) {
           part[((size_t)bz * M + m) * N + n] = v;
         } else {
           float *yp = Y + (size_t)m * ldy + n;
@@ -631,6 +641,18 @@ __global__ __launch_bounds__(GBLOCK) void k_gemm_xl(const WT *__restrict__ W, co
             *yp = v * sc;
         }
       }
+  }
+  if (GATE) {
+    __syncthreads();
+    const float2 *t2 = reinterpret_cast<const float2 *>(gtile);
+    for (int e = threadIdx.x; e < BM * (XLN / 2); e += GBLOCK) {
+      const int r = e / (XLN / 2), jj = e - r * (XLN / 2);
+      const int m = m0 + r, n = n0 + 2 * jj;
+      if (m < M && n < N) {
+        const float2 gm = t2[e];
+        XPut<bf16_t>::put(gx + (size_t)m * ldg, N >> 1, n >> 1, silu(gm.x) * gm.y);
+      }
+    }
   }
 }
 

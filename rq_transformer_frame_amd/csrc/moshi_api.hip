@@ -792,7 +792,23 @@ void gemm(hipStream_t st, int cus, float *part, const WT *W, const float *scale,
 
 // Gated unit's first projection: Y = X W^T over the 2 F interleaved gate / mult rows, then
 // Xo[m][j] = silu(Y[m][2j]) * Y[m][2j + 1] in the XPut layout.  With a K split the split reduction
-// and the epilogue are one kernel (k_reduce_gate); without one, k_gate_post reads Y.
+// and the epilogue are one kernel (k_reduce_gate); without one, k_gate_post reads Y.  On the
+// unsplit 128-row tiles (gate_fused) the product forms the output itself; Xo may be X, which
+// other blocks are still reading then, so the output goes to Y's storage (row stride 2 F) instead.
+template <typename WT>
+bool gate_fused(int F, int K, int M, int cus) {
+  if constexpr (std::is_same<WT, float>::value) {
+    return false;
+  } else {
+    const GemmPlan g = gemm_plan(2 * F, K, M, cus);
+    return g.nt < 0 && g.S == 1;
+  }
+}
+template <typename WT>
+const typename mk::GemmX<WT>::type *gate_out_input(int F, int K, int M, int cus, const float *Y,
+                                                   const typename mk::GemmX<WT>::type *Xo) {
+  return gate_fused<WT>(F, K, M, cus) ? reinterpret_cast<const typename mk::GemmX<WT>::type *>(Y) : Xo;
+}
 template <typename WT, int TAG>
 void gemm_gate(hipStream_t st, int cus, float *part, const WT *W, const float *scale, int F, int K,
                const typename mk::GemmX<WT>::type *X, int ldx, int M, float *Y, typename mk::GemmX<WT>::type *Xo,
@@ -804,6 +820,11 @@ void gemm_gate(hipStream_t st, int cus, float *part, const WT *W, const float *s
     if (g.S > 1 && F % 2 == 0 && ldxo % 2 == 0) {
       gemm_x_launch<WT, false, TAG>(st, g, part, W, scale, 2 * F, K, X, ldx, M, Y, 2 * F);
       k_reduce_gate<XT><<<dim3((F + 2 * BLOCK - 1) / (2 * BLOCK), M), BLOCK, 0, st>>>(part, g.S, M, F, scale, Xo, ldxo);
+      return;
+    }
+    if (g.nt < 0 && g.S == 1) {  // 128-row tiles, one split: the product's epilogue forms the output
+      k_gemm_xl<WT, false, TAG, true><<<dim3((M + XLM - 1) / XLM, (2 * F + XLN - 1) / XLN, 1), GBLOCK, 0, st>>>(
+          W, scale, 2 * F, K, X, ldx, M, Y, 2 * F, part, g.kbs, reinterpret_cast<XT *>(Y), 2 * F);
       return;
     }
   }
@@ -917,11 +938,12 @@ void enqueue_temporal_rows(moshi_state *s, int rows, float *x, float *q_rows, fl
     });
     run(MOSHI_STAGE_GATE_OUT, [&] {
       if (l + 1 < d.L)  // x += a . W_gout^T, then X = rms_norm(x; next layer's norm1)
-        gemm_add_cvt<WT, MOSHI_STAGE_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.D, d.F, X,
-                                               P * d.F, rows, x, d.D, N(s->layers[l + 1].norm1), d.eps, X, P * d.D);
+        gemm_add_cvt<WT, MOSHI_STAGE_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.D, d.F,
+                                               gate_out_input<WT>(d.F, d.D, rows, s->cus, Y, X), P * d.F, rows, x,
+                                               d.D, N(s->layers[l + 1].norm1), d.eps, X, P * d.D);
       else
-        gemm<WT, true, MOSHI_STAGE_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.D, d.F, X,
-                                             P * d.F, rows, x, d.D);
+        gemm<WT, true, MOSHI_STAGE_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.D, d.F,
+                                             gate_out_input<WT>(d.F, d.D, rows, s->cus, Y, X), P * d.F, rows, x, d.D);
     });
   }
 }
@@ -1039,7 +1061,8 @@ void enqueue_frame_rows(moshi_state *s, int b0, int nb, const int32_t *user_dev,
         // y += a . W_gout^T, then X = rms_norm(y; next layer's norm1), or y as is for the head
         const float *next = j + 1 < d.Ld ? N(s->dlayers[j + 1][cb].norm1) : nullptr;
         gemm_add_cvt<WT, MOSHI_STAGE_DEP_GATE_OUT>(st, s->cus, s->gpart, W(lw.gout), s->scale(lw.gout), d.Dd, d.Fd,
-                                                   X, P * d.Fd, rows, y, d.Dd, next, d.eps, X, P * d.Dd);
+                                                   gate_out_input<WT>(d.Fd, d.Dd, rows, s->cus, Y, X), P * d.Fd, rows,
+                                                   y, d.Dd, next, d.eps, X, P * d.Dd);
       });
     }
     run(MOSHI_STAGE_DEP_HEAD, [&] {

@@ -441,6 +441,37 @@ def test_long_prefill_bf16_head_dim_128_matches_oracle():
             assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], f
 
 
+def test_long_prefill_int8_band_matches_dequantised_oracle():
+    """The int8 band's prefill on the 128 x 256 tiles (int8 weights widened in registers), with the
+    gated unit's silu(gate) * mult formed in the first product's epilogue: a full 1024-position
+    chunk and a ragged one of 76, then 3 frames, against the oracle on the same int8
+    quantise-dequantise round trip of the bf16-rounded weights ([LM] load_q4sim's storage-loss
+    reading, int8 per-row scales)."""
+    cfg = CFG.with_(name="tiny_i8_h8_long", d_model=1024, n_heads=8, context=1536)
+    T = 1100
+    w = synth.gen_weights(cfg)
+    w16 = {k: (synth.f32_to_bf16_bits(v) if v.ndim == 2 else v) for k, v in w.items()}
+    lm = OracleLM(cfg, w16, band="i8sim")
+    text, agent, user = synth.prefill_tokens(cfg, T, conv=5)
+    text %= cfg.text_card
+    ost = lm.new_state()
+    lm.prefill_forced(ost, text, agent, user)
+    users = synth.user_tokens(cfg, 3, conv=5, start_frame=T)
+    with rq.Session(cfg, band="i8", exec="graph") as s:
+        s.load_weights(w16)
+        s.prefill_forced(0, text, agent, user)
+        for f in range(3):
+            ref = lm.step(ost, users[f])
+            s.step(users[f])
+            tr = s.read_trace(0)
+            assert tr["input_tokens"].tolist() == ref["input_tokens"].tolist(), f
+            assert rel_err(tr["transformer_out"], ref["transformer_out"]) <= TOL, f
+            assert rel_err(tr["text_logits"], ref["text_logits"]) <= TOL, f
+            for cb in range(cfg.dep_q):
+                assert rel_err(tr["audio_logits"][cb], ref["audio_logits"][cb]) <= TOL, (f, cb)
+            assert tr["tokens"].tolist() == [ref["text_token"]] + ref["audio_tokens"], f
+
+
 def test_persistent_wait_timeout_exits_and_reset_recovers(weights, oracle):
     """A wait of the persistent frame kernel that gives up (forced from the host: zero polls
     allowed) raises the error flag, every block leaves the kernel, and the step returns
