@@ -260,19 +260,27 @@ __global__ __launch_bounds__(PFA_WAVES * 64) void k_attn_pf3(Dims d, KV<KT> kv, 
   const int64_t wlast = aq.pos0 + min(qw0 + 31, rows - 1);
   const bool wactive = qw0 < rows;
 
-  float4 kreg[PPT], vreg[PPT];
+  // keys: four dims of one key per piece; values: thread t takes dim t % HD of VK keys, so that
+  // its transposed-tile writes are 8-byte runs of four keys and a wave's lanes write consecutive
+  // rows (the stride the reads use: no bank conflicts)
+  constexpr int VK = PFA_KT * HD / NT;
+  static_assert(NT % HD == 0 && VK % 4 == 0, "value tile shape");
+  const int vd = threadIdx.x % HD, vk0 = VK * (threadIdx.x / HD);
+  float4 kreg[PPT];
+  float vreg[VK];
   auto load_tile = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
       const int p = threadIdx.x + NT * i;
       const int key = tile * PFA_KT + p / LPR, c = 4 * (p % LPR);
-      float kf[4] = {0.f, 0.f, 0.f, 0.f}, vf[4] = {0.f, 0.f, 0.f, 0.f};
-      if (key < nkeys) {
-        ld_row<4>(kv.k + base + (size_t)key * PS + c, kf);
-        ld_row<4>(kv.v + base + (size_t)key * PS + c, vf);
-      }
+      float kf[4] = {0.f, 0.f, 0.f, 0.f};
+      if (key < nkeys) ld_row<4>(kv.k + base + (size_t)key * PS + c, kf);
       kreg[i] = float4{kf[0], kf[1], kf[2], kf[3]};
-      vreg[i] = float4{vf[0], vf[1], vf[2], vf[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < VK; ++j) {
+      const int key = tile * PFA_KT + vk0 + j;
+      vreg[j] = key < nkeys ? to_f(kv.v[base + (size_t)key * PS + vd]) : 0.f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -285,16 +293,14 @@ __global__ __launch_bounds__(PFA_WAVES * 64) void k_attn_pf3(Dims d, KV<KT> kv, 
       pfa_split2(kreg[i].z, kreg[i].w, h1, l1);
       *reinterpret_cast<uint2 *>(&kh[buf][key][c]) = uint2{h0, h1};
       *reinterpret_cast<uint2 *>(&kl[buf][key][c]) = uint2{l0, l1};
-      pfa_split2(vreg[i].x, vreg[i].y, h0, l0);
-      pfa_split2(vreg[i].z, vreg[i].w, h1, l1);
-      vh[buf][c][key] = (bf16_t)h0;
-      vh[buf][c + 1][key] = (bf16_t)(h0 >> 16);
-      vh[buf][c + 2][key] = (bf16_t)h1;
-      vh[buf][c + 3][key] = (bf16_t)(h1 >> 16);
-      vl[buf][c][key] = (bf16_t)l0;
-      vl[buf][c + 1][key] = (bf16_t)(l0 >> 16);
-      vl[buf][c + 2][key] = (bf16_t)l1;
-      vl[buf][c + 3][key] = (bf16_t)(l1 >> 16);
+    }
+#pragma unroll
+    for (int q = 0; q < VK / 4; ++q) {
+      uint32_t h0, l0, h1, l1;
+      pfa_split2(vreg[4 * q], vreg[4 * q + 1], h0, l0);
+      pfa_split2(vreg[4 * q + 2], vreg[4 * q + 3], h1, l1);
+      *reinterpret_cast<uint2 *>(&vh[buf][vd][vk0 + 4 * q]) = uint2{h0, h1};
+      *reinterpret_cast<uint2 *>(&vl[buf][vd][vk0 + 4 * q]) = uint2{l0, l1};
     }
   };
 
